@@ -1,0 +1,164 @@
+"""CPU oracle for batched gapped seed extension -- TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product library never does, and this package never
+imports the product.  The arithmetic lives in ``fz_oracle.c`` (plain C,
+int64, anti-diagonal order, value-based traceback); this module only builds
+that file with gcc and marshals numpy arrays through ctypes.
+
+See the header of ``fz_oracle.c`` for the passages of the FastZ paper (SC'21)
+each part follows.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fz_oracle.c")
+_LIB = os.path.join(_HERE, "libfz_oracle.so")
+
+YDROP_INF = 2147483647
+
+STATUS_ESEED, STATUS_EBASE, STATUS_ERANGE, STATUS_ENOMEM = 1, 2, 4, 8
+
+HIT_FIELDS = ["score", "t_begin", "t_end", "q_begin", "q_end",
+              "score_l", "i_l", "j_l", "score_r", "i_r", "j_r",
+              "cells_l", "cells_r", "dend_l", "dend_r", "n_runs", "status"]
+HIT_DTYPE = np.dtype([(f, np.int64) for f in HIT_FIELDS])
+SEED_FIELDS = ["t_pos", "q_pos", "seed_len", "t_lo", "t_hi", "q_lo", "q_hi"]
+
+
+def build(force=True):
+    """Compile the oracle with gcc (plain -O2, pthreads)."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared",
+                           "-pthread", _SRC, "-o", tmp])
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        lib.fzo_run.restype = P
+        lib.fzo_run.argtypes = [P, i64, P, i64, P, i64, P, i64, i64, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_int, P]
+        lib.fzo_copy_cigars.restype = None
+        lib.fzo_copy_cigars.argtypes = [P, P, P]
+        lib.fzo_free.restype = None
+        lib.fzo_free.argtypes = [P]
+        lib.fzo_side_matrix.restype = i64
+        lib.fzo_side_matrix.argtypes = [P, i64, P, i64, P, i64, P, P, P, P, P, P]
+        _lib = lib
+    return _lib
+
+
+def _scoring_arr(scoring):
+    return np.array([scoring["match"], scoring["transition"], scoring["transversion"],
+                     scoring["gap_open"], scoring["gap_extend"]], dtype=np.int64)
+
+
+def _as_bytes(seq):
+    if isinstance(seq, (bytes, bytearray)):
+        return np.frombuffer(bytes(seq), dtype=np.uint8).copy()
+    if isinstance(seq, str):
+        return np.frombuffer(seq.encode(), dtype=np.uint8).copy()
+    return np.ascontiguousarray(seq, dtype=np.uint8)
+
+
+def seeds_array(seeds):
+    """Seeds as an (n, 7) int64 array in SEED_FIELDS order."""
+    if isinstance(seeds, np.ndarray) and seeds.dtype.names:
+        return np.stack([seeds[f].astype(np.int64) for f in SEED_FIELDS], axis=1).copy()
+    a = np.ascontiguousarray(seeds, dtype=np.int64)
+    return a.reshape(-1, 7)
+
+
+def run(target, query, seeds, scoring, ydrop, min_tb=None, traceback=True, local=False,
+        threads=None):
+    """Run the oracle on a batch.
+
+    Returns (hits, cigar_words, cigar_offsets): hits is a structured array with
+    HIT_FIELDS, cigar_words the concatenated BAM-style run words (len << 4 | op,
+    op 0=M 1=I 2=D) of every seed that was traced, cigar_offsets[k] the start of
+    seed k's runs (n_runs of them).
+    """
+    lib = _load()
+    T = _as_bytes(target)
+    Q = _as_bytes(query)
+    S = seeds_array(seeds)
+    n = S.shape[0]
+    sc = _scoring_arr(scoring)
+    hits = np.zeros(n, dtype=HIT_DTYPE)
+    if threads is None:
+        threads = os.cpu_count() or 1
+    if min_tb is None:
+        min_tb = -(1 << 62)
+    h = lib.fzo_run(T.ctypes.data, T.size, Q.ctypes.data, Q.size, S.ctypes.data, n, sc.ctypes.data,
+                    int(ydrop), int(min_tb), int(bool(traceback)), int(bool(local)), int(threads),
+                    hits.ctypes.data)
+    if not h:
+        raise MemoryError("oracle batch allocation failed")
+    try:
+        total = int(hits["n_runs"].sum())
+        words = np.zeros(max(total, 1), dtype=np.uint32)
+        lib.fzo_copy_cigars(h, hits.ctypes.data, words.ctypes.data)
+    finally:
+        lib.fzo_free(h)
+    offs = np.zeros(n, dtype=np.int64)
+    if n:
+        offs[1:] = np.cumsum(hits["n_runs"])[:-1]
+    return hits, words[:total], offs
+
+
+def side(a, b, scoring, ydrop, matrices=False, traceback=True):
+    """One side on explicit sequences a (rows, length m) and b (columns, n).
+
+    Returns dict(score, ie, je, cells, dend, ops[, S, I, D]); ops end-first
+    ('M', 'I', 'D'); matrices hold None for cells never evaluated or dead.
+    """
+    lib = _load()
+    A = _as_bytes(a)
+    B = _as_bytes(b)
+    m, n = A.size, B.size
+    sc = _scoring_arr(scoring)
+    out5 = np.zeros(5, dtype=np.int64)
+    Sm = Im = Dm = None
+    if matrices:
+        Sm = np.zeros((m + 1, n + 1), dtype=np.int64)
+        Im = np.zeros_like(Sm)
+        Dm = np.zeros_like(Sm)
+    ops = ctypes.create_string_buffer(m + n + 2) if traceback else None
+    nops = ctypes.c_int64(0)
+    Ap = A.ctypes.data if m else ctypes.c_void_p(ctypes.addressof(ctypes.c_char()))
+    Bp = B.ctypes.data if n else ctypes.c_void_p(ctypes.addressof(ctypes.c_char()))
+    st = lib.fzo_side_matrix(Ap, m, Bp, n, sc.ctypes.data, int(ydrop), out5.ctypes.data,
+                             Sm.ctypes.data if matrices else None,
+                             Im.ctypes.data if matrices else None,
+                             Dm.ctypes.data if matrices else None,
+                             ops, ctypes.byref(nops) if traceback else None)
+    res = dict(score=int(out5[0]), ie=int(out5[1]), je=int(out5[2]), cells=int(out5[3]),
+               dend=int(out5[4]), status=int(st))
+    if traceback:
+        res["ops"] = ops.raw[:nops.value].decode()
+    if matrices:
+        NEG = np.iinfo(np.int64).min
+        res["S"], res["I"], res["D"] = [np.where(x == NEG, None, x).astype(object) for x in (Sm, Im, Dm)]
+    return res
+
+
+def cigar_string(words):
+    """BAM-style run words -> text CIGAR."""
+    return "".join("%d%s" % (w >> 4, "MID"[w & 15]) for w in np.asarray(words, dtype=np.uint32).tolist())

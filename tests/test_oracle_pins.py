@@ -1,0 +1,349 @@
+"""Pins for the CPU oracle: it is checked against things other than itself.
+
+- exhaustive path enumeration (tests/bruteforce.py) for the recurrence,
+  the y-drop rule, the end-cell rule and the traceback tie rules;
+- hand-derived closed forms (tests/golden/closed_forms.tsv);
+- the linear-gap special case of local mode against a textbook one-matrix
+  Smith-Waterman (DPX article, section 1.1);
+- invariants: the CIGAR rescored from the sequences equals the score, spans
+  match the coordinates, the left side equals the right side on reversed
+  strings, local >= any seeded extension in the same window.
+"""
+import os
+import random
+
+import numpy as np
+import pytest
+
+import bruteforce as bf
+import oracle
+from smith_waterman_dp_amd import workloads as W
+
+SC = dict(W.DEFAULT_SCORING)
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def rand_seq(rng, n, alphabet="ACGT"):
+    return "".join(rng.choice(alphabet) for _ in range(n))
+
+
+def rand_scoring(rng):
+    return dict(match=rng.randint(1, 120), transition=rng.randint(-150, 40),
+                transversion=rng.randint(-200, 0), gap_open=rng.randint(1, 500),
+                gap_extend=rng.randint(1, 80))
+
+
+def check_against_brute(a, b, sc, ydrop):
+    ob = oracle.side(a, b, sc, oracle.YDROP_INF if ydrop is None else ydrop, matrices=True)
+    assert ob["status"] == 0
+    br = bf.extension_brute(a, b, sc, ydrop)
+    ctx = (a, b, sc, ydrop)
+    assert ob["score"] == br["score"], ctx
+    assert (ob["ie"], ob["je"]) == (br["ie"], br["je"]), ctx
+    assert ob["ops"] == br["ops"][::-1], ctx
+    # live set and every live value
+    live_o = {(i, j) for i in range(len(a) + 1) for j in range(len(b) + 1) if ob["S"][i, j] is not None}
+    assert live_o == br["live"], ctx
+    for c in live_o:
+        assert ob["S"][c] == br["V"][c], (ctx, c)
+
+
+@pytest.mark.parametrize("case", range(150))
+def test_bruteforce_unpruned(case):
+    """No pruning: the oracle's maximum is the maximum over every path."""
+    rng = random.Random(1000 + case)
+    alphabet = ["ACGT", "AC", "AG", "A"][case % 4]
+    a = rand_seq(rng, rng.randint(0, 5), alphabet)
+    b = rand_seq(rng, rng.randint(0, 5), alphabet)
+    sc = SC if case % 3 == 0 else rand_scoring(rng)
+    check_against_brute(a, b, sc, None)
+
+
+@pytest.mark.parametrize("case", range(200))
+def test_bruteforce_ydrop(case):
+    """Anti-diagonal y-drop: live set, values, end cell and path all match
+    the enumeration with the same kill rule."""
+    rng = random.Random(5000 + case)
+    alphabet = ["ACGT", "AC", "AG", "AT", "A"][case % 5]
+    a = rand_seq(rng, rng.randint(1, 6), alphabet)
+    b = rand_seq(rng, rng.randint(1, 6), alphabet)
+    sc = SC if case % 2 == 0 else rand_scoring(rng)
+    ydrop = rng.choice([0, 1, 30, 100, 150, 300, 500, 900])
+    check_against_brute(a, b, sc, ydrop)
+
+
+@pytest.mark.parametrize("a,b", [("AAAAA", "AAAA"), ("ACACAC", "ACAC"), ("AAAA", "AAAAAA"),
+                                 ("ACGACG", "ACG"), ("AGAGAG", "AG"), ("TTTTT", "TT")])
+def test_bruteforce_repeat_ties(a, b):
+    """Homopolymer and short-repeat indels: many equal-scoring gap places;
+    the traceback picks the tie-ruled one."""
+    sc = dict(match=91, transition=-31, transversion=-123, gap_open=40, gap_extend=30)
+    for ydrop in (None, 200, 1000):
+        check_against_brute(a, b, sc, ydrop)
+        check_against_brute(b, a, sc, ydrop)
+
+
+def load_closed_forms():
+    rows = []
+    with open(os.path.join(HERE, "golden", "closed_forms.tsv")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            p = line.rstrip("\n").split("\t")
+            rows.append((p[0], p[1], p[2], int(p[3]), int(p[4]), int(p[5]), int(p[6]), p[7] if len(p) > 7 else ""))
+    return rows
+
+
+@pytest.mark.parametrize("row", load_closed_forms(), ids=lambda r: r[0])
+def test_closed_forms(row):
+    name, a, b, ydrop, score, ie, je, ops = row
+    r = oracle.side(a, b, SC, ydrop)
+    assert (r["score"], r["ie"], r["je"], r["ops"]) == (score, ie, je, ops)
+
+
+@pytest.mark.parametrize("ell", [1, 7, 64, 300])
+def test_identical_flanks_closed_form(ell):
+    rng = random.Random(ell)
+    a = rand_seq(rng, ell)
+    r = oracle.side(a, a, SC, W.DEFAULT_YDROP)
+    assert (r["score"], r["ie"], r["je"], r["ops"]) == (91 * ell, ell, ell, "M" * ell)
+
+
+@pytest.mark.parametrize("g,kind", [(1, "D"), (5, "D"), (40, "I"), (200, "I")])
+def test_single_gap_closed_form(g, kind):
+    """One gap of g bases inside long identical flanks costs open + g*extend."""
+    rng = random.Random(g)
+    left, right = rand_seq(rng, 400), rand_seq(rng, 400)
+    ins = rand_seq(rng, g)
+    # guard against the inserted bases extending a neighbouring identical run
+    while ins[0] == right[0] or ins[-1] == left[-1]:
+        ins = rand_seq(rng, g)
+    a = left + right
+    b = left + ins + right
+    if kind == "D":
+        a, b = b, a
+    r = oracle.side(a, b, SC, W.DEFAULT_YDROP)
+    assert r["score"] == 91 * 800 - (400 + 30 * g)
+    assert r["ops"].count(kind) == g and set(r["ops"]) == {"M", kind}
+
+
+@pytest.mark.parametrize("k", [0, 1, 9, 50])
+def test_ydrop_zero_closed_form(k):
+    rng = random.Random(k)
+    a = rand_seq(rng, k) + "A" + rand_seq(rng, 30)
+    b = a[:k] + "C" + a[k + 1:]
+    r = oracle.side(a, b, SC, 0)
+    assert (r["score"], r["ie"], r["je"]) == (91 * k, k, k)
+
+
+def test_infinite_ydrop_equals_unpruned_bruteforce_medium():
+    """ydrop = inf on medium random pairs equals an unpruned full-matrix
+    maximum computed by a separate path-free route: the best path score to
+    each cell by the three-state recurrence written over the whole matrix."""
+    rng = random.Random(7)
+    for _ in range(20):
+        a = rand_seq(rng, rng.randint(5, 40))
+        b = rand_seq(rng, rng.randint(5, 40))
+        r = oracle.side(a, b, SC, oracle.YDROP_INF, matrices=True)
+        m, n = len(a), len(b)
+        assert r["cells"] == (m + 1) * (n + 1)
+        assert r["score"] == bf.path_score(r["ops"][::-1], a, b, SC)
+
+
+def full_matrix_ydrop(a, b, sc, ydrop):
+    """Unbanded y-drop: every cell of the matrix, anti-diagonal order, the
+    kill rule applied cell by cell with no range bookkeeping."""
+    m, n = len(a), len(b)
+    NEG = None
+    S = [[NEG] * (n + 1) for _ in range(m + 1)]
+    I = [[NEG] * (n + 1) for _ in range(m + 1)]
+    D = [[NEG] * (n + 1) for _ in range(m + 1)]
+    S[0][0] = 0
+    best = 0
+    OE = sc["gap_open"] + sc["gap_extend"]
+    E = sc["gap_extend"]
+
+    def mx(*xs):
+        xs = [x for x in xs if x is not None]
+        return max(xs) if xs else None
+
+    def sub_(x, y):
+        return None if x is None else x + y
+
+    for d in range(1, m + n + 1):
+        thr = best - ydrop
+        dbest = None
+        for i in range(max(0, d - n), min(m, d) + 1):
+            j = d - i
+            Iv = mx(sub_(I[i][j - 1], -E), sub_(S[i][j - 1], -OE)) if j >= 1 else None
+            Dv = mx(sub_(D[i - 1][j], -E), sub_(S[i - 1][j], -OE)) if i >= 1 else None
+            H = sub_(S[i - 1][j - 1], bf.sub(a[i - 1], b[j - 1], sc)) if i >= 1 and j >= 1 else None
+            Sv = mx(H, Iv, Dv)
+            if Sv is None or Sv < thr:
+                continue
+            S[i][j], I[i][j], D[i][j] = Sv, Iv, Dv
+            dbest = Sv if dbest is None else max(dbest, Sv)
+        if dbest is not None:
+            best = max(best, dbest)
+    return S
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_band_bookkeeping_vs_full_matrix(case):
+    """The oracle's range rule (hull of cells with a live predecessor) loses
+    nothing: same live set and values as evaluating the whole matrix."""
+    rng = random.Random(900 + case)
+    m, n = rng.randint(20, 70), rng.randint(20, 70)
+    a = rand_seq(rng, m)
+    # half the cases: b is a mutated a, so the band wanders
+    if case % 2:
+        b = list(a)
+        for _ in range(rng.randint(1, 6)):
+            p = rng.randrange(len(b))
+            op = rng.random()
+            if op < 0.4:
+                b.insert(p, rng.choice("ACGT"))
+            elif op < 0.8 and len(b) > 1:
+                del b[p]
+            else:
+                b[p] = rng.choice("ACGT")
+        b = "".join(b)
+    else:
+        b = rand_seq(rng, n)
+    ydrop = rng.choice([100, 400, 900, 2000])
+    r = oracle.side(a, b, SC, ydrop, matrices=True)
+    S = full_matrix_ydrop(a, b, SC, ydrop)
+    for i in range(len(a) + 1):
+        for j in range(len(b) + 1):
+            assert r["S"][i, j] == S[i][j], (i, j)
+
+
+# ------------------------------------------------------------- local mode --
+
+def textbook_sw_linear(a, b, sc):
+    """One-matrix local alignment with a linear gap penalty g per base:
+    H = max(0, diag + s, up - g, left - g) (DPX article, section 1.1)."""
+    m, n = len(a), len(b)
+    g = sc["gap_extend"]
+    H = np.zeros((m + 1, n + 1), dtype=np.int64)
+    for i in range(1, m + 1):
+        for j in range(1, n + 1):
+            H[i, j] = max(0, H[i - 1, j - 1] + bf.sub(a[i - 1], b[j - 1], sc), H[i - 1, j] - g, H[i, j - 1] - g)
+    top = int(H.max())
+    cells = [(i + j, i) for i in range(m + 1) for j in range(n + 1) if H[i, j] == top]
+    d, i = min(cells)
+    return top, i, d - i
+
+
+def run_local(a, b, sc):
+    seeds = np.array([[0, 0, 0, 0, len(a), 0, len(b)]], dtype=np.int64)
+    hits, _, _ = oracle.run(a, b, seeds, sc, oracle.YDROP_INF, local=True, traceback=False, threads=1)
+    h = hits[0]
+    assert h["status"] == 0
+    return int(h["score"]), int(h["t_end"]), int(h["q_end"]), int(h["cells_r"])
+
+
+@pytest.mark.parametrize("case", range(30))
+def test_local_linear_gap_equals_textbook(case):
+    rng = random.Random(300 + case)
+    a = rand_seq(rng, rng.randint(1, 60), "ACGT" if case % 2 else "AC")
+    b = rand_seq(rng, rng.randint(1, 60), "ACGT" if case % 2 else "AC")
+    sc = dict(SC, gap_open=0) if case % 3 else dict(rand_scoring(rng), gap_open=0)
+    assert run_local(a, b, sc)[:3] == textbook_sw_linear(a, b, sc)
+
+
+@pytest.mark.parametrize("case", range(60))
+def test_local_bruteforce(case):
+    rng = random.Random(700 + case)
+    a = rand_seq(rng, rng.randint(0, 5), ["ACGT", "AC", "A"][case % 3])
+    b = rand_seq(rng, rng.randint(0, 5), ["ACGT", "AC", "A"][case % 3])
+    sc = SC if case % 2 else rand_scoring(rng)
+    br = bf.local_brute(a, b, sc)
+    s, ie, je, cells = run_local(a, b, sc)
+    assert (s, ie, je) == (br["score"], br["ie"], br["je"])
+    assert cells == len(a) * len(b)
+
+
+def test_local_identical_2048():
+    rng = random.Random(2048)
+    a = rand_seq(rng, 2048)
+    assert run_local(a, a, SC)[:3] == (91 * 2048, 2048, 2048)
+
+
+# ------------------------------------------------------------- invariants --
+
+def rescore_cigar(T, Q, t0, q0, words, sc):
+    t, q, total = t0, q0, 0
+    for w in words:
+        n, op = int(w) >> 4, int(w) & 15
+        if op == 0:
+            for k in range(n):
+                total += bf.sub(chr(T[t + k]), chr(Q[q + k]), sc)
+            t += n
+            q += n
+        else:
+            total -= sc["gap_open"] + n * sc["gap_extend"]
+            if op == 1:
+                q += n
+            else:
+                t += n
+    return total, t, q
+
+
+@pytest.fixture(scope="module")
+def tiny_small():
+    return W.tiny(n_seeds=60, seed=3)
+
+
+def test_tiny_invariants(tiny_small):
+    w = tiny_small
+    hits, words, offs = oracle.run(w["target"], w["query"], w["seeds"], w["scoring"], w["ydrop"], threads=4)
+    assert (hits["status"] == 0).all()
+    for k, h in enumerate(hits):
+        cw = words[offs[k]:offs[k] + h["n_runs"]]
+        total, t_end, q_end = rescore_cigar(w["target"], w["query"], h["t_begin"], h["q_begin"], cw, w["scoring"])
+        assert total == h["score"]
+        assert (t_end, q_end) == (h["t_end"], h["q_end"])
+        ops = [int(x) & 15 for x in cw]
+        assert all(ops[i] != ops[i + 1] for i in range(len(ops) - 1)), "runs must be maximal"
+
+
+def test_left_equals_right_on_reversed(tiny_small):
+    w = tiny_small
+    T, Q = bytes(w["target"]), bytes(w["query"])
+    for s in w["seeds"][:20]:
+        t_pos, q_pos, L, t_lo, t_hi, q_lo, q_hi = [int(x) for x in s]
+        left_a = T[t_lo:t_pos][::-1]
+        left_b = Q[q_lo:q_pos][::-1]
+        hits, _, _ = oracle.run(w["target"], w["query"], s.reshape(1, 7), w["scoring"], w["ydrop"], threads=1)
+        r = oracle.side(left_a, left_b, w["scoring"], w["ydrop"])
+        h = hits[0]
+        assert (r["score"], r["ie"], r["je"], r["cells"]) == (h["score_l"], h["i_l"], h["j_l"], h["cells_l"])
+
+
+def test_local_at_least_seeded_extension(tiny_small):
+    w = tiny_small
+    seeds = w["seeds"][:8]
+    hits, _, _ = oracle.run(w["target"], w["query"], seeds, w["scoring"], w["ydrop"], traceback=False, threads=4)
+    loc = seeds.copy()
+    loc[:, 2] = 0
+    lh, _, _ = oracle.run(w["target"], w["query"], loc, w["scoring"], oracle.YDROP_INF, local=True,
+                          traceback=False, threads=4)
+    assert (lh["score"] >= hits["score"]).all()
+
+
+def test_seed_validation():
+    T = "ACGT" * 10
+    bad = np.array([[5, 5, 19, 10, 40, 0, 40]], dtype=np.int64)   # seed before its window
+    hits, _, _ = oracle.run(T, T, bad, SC, 9400, threads=1)
+    assert hits[0]["status"] == oracle.STATUS_ESEED
+
+
+def test_empty_flanks():
+    """Seed flush with both window ends: both sides empty, total = seed."""
+    T = "ACGTACGTACGTACGTACG"
+    s = np.array([[0, 0, 19, 0, 19, 0, 19]], dtype=np.int64)
+    hits, words, _ = oracle.run(T, T, s, SC, 9400, threads=1)
+    h = hits[0]
+    assert (h["score"], h["t_begin"], h["t_end"], h["cells_l"], h["cells_r"]) == (19 * 91, 0, 19, 1, 1)
+    assert oracle.cigar_string(words) == "19M"
