@@ -1,0 +1,165 @@
+"""Benchmark of the batched gapped-extension hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one whole fz_extend_batch call (every phase of the path) over the
+workload's batch, inputs already resident in device memory.  Prints one JSON
+line: GCUPS (canonical cells / step time), seed extensions per second, the
+roofline of the dominant kernel (integer VALU bound), and the CPU oracle
+timed on a bounded sample of the same batch on this host's cores.
+
+Workloads (seeded, synthetic; see smith_waterman_dp_amd/workloads.py):
+  skewed          one million 19-mer seeds on a 10 Mbp pair
+  local           4,096 full-matrix local alignments of 2048 x 2048 (default
+                  while the extension path is off the GPU)
+  tiny, executor_heavy, chromosome
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GCUPS and seed extensions/sec on 1M-seed skewed batch, 1 MI355X"
+
+# Integer VALU peak of MI355X: 256 CUs x 4 SIMD x 16 lanes (64 lane-ops per
+# clock per CU) x 2.4 GHz peak engine clock.
+N_CU, LANE_OPS_PER_CLK_PER_CU, CLOCK_HZ = 256, 64, 2.4e9
+VALU_PEAK_OPS = N_CU * LANE_OPS_PER_CLK_PER_CU * CLOCK_HZ
+
+# Algorithmic integer operations per cell (fixed, independent of the code):
+#   extension: 5 adds + 4 compares of the three-state cell (FastZ section 2.2,
+#   observation (1)), 1 substitution lookup, 2 for the y-drop test and kill,
+#   1 running maximum = 13;
+#   local: 5 adds + 5 max (zero clamp included), 1 substitution, 1 running
+#   maximum = 12.
+OPS_PER_CELL = {"extend": 13, "local": 12}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=1)
+    # default: local until the extension path is back on the GPU
+    ap.add_argument("--workload", default="local",
+                    choices=["skewed", "local", "tiny", "executor_heavy", "chromosome"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def make_workload(name):
+    from smith_waterman_dp_amd import workloads as W
+    return W.WORKLOADS[name]()
+
+
+def cpu_baseline(w, target_seconds, local):
+    """The oracle, as it stands, on a seeded sample of the batch, all host cores."""
+    import numpy as np
+
+    import oracle
+    threads = os.cpu_count() or 1
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    rng = np.random.default_rng(123)
+    seeds = w["seeds"]
+    n = seeds.shape[0]
+    order = rng.permutation(n)
+    done_cells = 0
+    done = 0
+    t0 = time.time()
+    chunk = max(threads, 8)
+    while done < n and time.time() - t0 < target_seconds:
+        idx = order[done:done + chunk]
+        hits, _, _ = oracle.run(w["target"], w["query"], seeds[idx], w["scoring"],
+                                oracle.YDROP_INF if local else w["ydrop"], min_tb=w.get("min_tb"),
+                                traceback=not local and w.get("traceback", True), local=local, threads=threads)
+        done_cells += int(hits["cells_r"].sum() + (0 if local else hits["cells_l"].sum()))
+        done += len(idx)
+        chunk = min(chunk * 2, 4096)
+    dt = time.time() - t0
+    return {"value": round(done_cells / dt / 1e9, 4), "unit": "GCUPS", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d records (seeded draw), %.1f s, %.3g cells, extensions/s %.1f"
+                      % (done, n, dt, done_cells, done / dt)}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d refused)" % a.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from smith_waterman_dp_amd import fz
+
+    local = a.workload == "local"
+    steps = a.steps if a.steps is not None else (20 if local else 5)
+    print("[bench] generating workload %s" % a.workload, file=sys.stderr, flush=True)
+    t = time.time()
+    w = make_workload(a.workload)
+    print("[bench] generated in %.1fs: %d records" % (time.time() - t, len(w["seeds"])), file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    T = torch.from_numpy(w["target"]).to(dev)
+    Q = torch.from_numpy(w["query"]).to(dev)
+    S = torch.from_numpy(w["seeds"]).to(dev)
+    ctx = fz.Context(0)
+    min_tb = w.get("min_tb")
+    min_tb = -(1 << 62) if min_tb is None else min_tb
+
+    def step():
+        if local:
+            return ctx.local(T, Q, S, w["scoring"], want_stats=True)
+        return ctx.extend(T, Q, S, w["scoring"], w["ydrop"], min_tb, traceback=w.get("traceback", True),
+                          want_stats=True)
+
+    for k in range(a.warmup):
+        step()
+        print("[bench] warmup %d done" % k, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    main_ms = []
+    t0 = time.perf_counter()
+    hits = None
+    for k in range(steps):
+        hits, cig, st = step()
+        main_ms.append(st["ms_main"])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    h = hits.cpu().numpy()
+    cells = int(h[:, 8].sum())
+    n = len(w["seeds"])
+    ms_per_step = dt / steps * 1e3
+    gcups = cells / (ms_per_step / 1e3) / 1e9
+    ops = OPS_PER_CELL["local" if local else "extend"]
+    kern_s = float(np.mean(main_ms)) / 1e3
+    achieved = ops * cells / kern_s / 1e12
+    peak = VALU_PEAK_OPS / 1e12
+    cfg = {"workload": a.workload, "records": n, "target_bp": int(w["target"].size), "query_bp": int(w["query"].size),
+           "cells_per_step": cells, "scoring": w["scoring"], "ydrop": None if local else w["ydrop"],
+           "min_traceback_score": w.get("min_tb"), "main_kernel_ms": round(kern_s * 1e3, 3)}
+    if not local:
+        cfg["extensions_per_sec"] = round(n / (ms_per_step / 1e3), 1)
+    out = {"metric": METRIC if a.workload == "skewed" else "GCUPS on the %s batch, 1 MI355X" % a.workload,
+           "value": round(gcups, 3), "unit": "GCUPS", "n_gpus": 1, "steps": steps, "warmup": a.warmup,
+           "ms_per_step": round(ms_per_step, 3), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "int32", "data": "synthetic", "config": cfg,
+           "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(peak, 3), "unit": "TOP/s",
+                        "frac": round(achieved / peak, 4), "traffic": None,
+                        "kernel": "local_kernel" if local else "extend_kernel (inspector)",
+                        "ops_per_cell": ops}}
+    if not a.no_cpu:
+        print("[bench] CPU oracle sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds, local)
+    ctx.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+/*
+ * fz.h -- C ABI of libfz: batched gapped seed extension on one MI355X (gfx950).
+ *
+ * The operation follows "FastZ: Accelerating Gapped Whole Genome Alignment on
+ * GPUs" (Gundabolu, Vijaykumar, Thottethodi, SC'21).  FastZ is a drop-in
+ * replacement for the gapped-extension stage of LASTZ: the host picks 19-bp
+ * seeds, sequences and seeds go in, alignments come out (section 1 and
+ * section 3.4 "implementation").  Each seed is extended on both sides
+ * separately (section 3.1.2) with affine-gap Smith-Waterman (section 1,
+ * Fig. 1) pruned by y-drop (section 2.1, Fig. 3a, in the "previously
+ * completed scores" form of section 3.4), then traced back from the best cell
+ * (section 2.1, Fig. 3b).
+ *
+ * Exact definition computed for one side (a_1..a_m from the target, b_1..b_n
+ * from the query, both read outward from the seed):
+ *   I(i,j) = max(I(i,j-1) - E, S(i,j-1) - O - E)   gap in the target (CIGAR 'I')
+ *   D(i,j) = max(D(i-1,j) - E, S(i-1,j) - O - E)   gap in the query  (CIGAR 'D')
+ *   S(i,j) = max(S(i-1,j-1) + sub(a_i, b_j), I(i,j), D(i,j)),  S(0,0) = 0
+ *   anti-diagonals d = i + j are settled in order; T_d = (best S over live
+ *   cells of diagonals < d) - ydrop; a cell with S < T_d is dead (S=I=D=-inf);
+ *   the run ends when no cell of the next diagonal can have a live predecessor.
+ *   The side's result is the best live S, ties to the smallest d then the
+ *   smallest i.  Traceback prefers the diagonal move, then I, then D; inside
+ *   a gap it prefers "opened here" over "extended".
+ * A gap of g bases costs O + g*E.  sub() is `match` for equal bases,
+ * `transition` for A<->G and C<->T, `transversion` otherwise.  The seed's own
+ * columns are scored with sub() and added to the two sides' scores.
+ *
+ * Local mode (FZ_LOCAL): each record's windows are one pair; the whole
+ * window is scored with S = max(0, H, I, D), no y-drop, and the result is
+ * the best S and its cell (same tie rule).  No traceback in local mode.
+ *
+ * Memory: every pointer marked "device" must be device memory of the
+ * context's GPU (e.g. a torch tensor's data_ptr()); the library never frees
+ * caller memory.  All work is enqueued on `stream` (a hipStream_t, NULL = the
+ * null stream); fz_extend_batch synchronises that stream before it returns
+ * because it reads sizes back between its phases, so outputs are complete on
+ * return.
+ *
+ * Errors: call-level problems return a negative FZ_E* code and set a message
+ * readable with fz_last_error(); per-seed problems set bits in
+ * fz_hit.status and leave the rest of the batch valid.
+ */
+#ifndef FZ_H
+#define FZ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct fz_ctx fz_ctx;
+
+/* Scores (signed) and gap costs (>= 0).  A gap of g bases costs
+ * gap_open + g * gap_extend. */
+typedef struct {
+    int32_t match, transition, transversion;
+    int32_t gap_open, gap_extend;
+} fz_scoring;
+
+/* One seed: an exact match of seed_len bases at target[t_pos..] and
+ * query[q_pos..], plus half-open windows that bound the extension (the
+ * extension treats a window edge as a sequence end).  Requires
+ * t_lo <= t_pos, t_pos + seed_len <= t_hi <= target_len (same for q).
+ * In FZ_LOCAL mode only the windows are read.  56 bytes, int64 fields, so a
+ * (n, 7) int64 array in this field order is an array of fz_seed. */
+typedef struct {
+    int64_t t_pos, q_pos, seed_len;
+    int64_t t_lo, t_hi, q_lo, q_hi;
+} fz_seed;
+
+/* Result per seed.  Coordinates are 0-based half-open on the forward
+ * strand.  cigar_off / cigar_len index the CIGAR word array returned by the
+ * call (cigar_len 0 when the seed was not traced).  96 bytes, int64 fields. */
+typedef struct {
+    int64_t score;                 /* left + seed columns + right (local: best S) */
+    int64_t status;                /* FZ_HIT_* bits */
+    int64_t t_begin, t_end, q_begin, q_end;
+    int64_t cigar_off, cigar_len;
+    int64_t cells;                 /* canonical cells evaluated, both sides */
+    int64_t score_left, score_right;
+    int64_t bin;                   /* executor length bin of the longer side, -1 if none */
+} fz_hit;
+
+/* Statistics of one call (host struct, optional). */
+typedef struct {
+    uint64_t cells;                /* canonical cells, all seeds, both sides */
+    uint64_t executor_cells;       /* cells recomputed by the executor */
+    uint64_t pointer_bytes;        /* traceback pointer bytes written */
+    uint64_t n_sides, n_eager, n_executor, n_overflow;
+    uint64_t bin_hist[8];
+    uint64_t n_batches;
+    float ms_pack, ms_inspect, ms_bin, ms_exec, ms_walk, ms_gather;
+    float ms_main;                 /* the dominant kernel alone (inspector, or the local kernel) */
+} fz_stats;
+
+enum {
+    FZ_TRACEBACK = 1u << 0,        /* CIGAR for every seed whose score > min_traceback_score */
+    FZ_LOCAL = 1u << 1,            /* full-window local alignment, score and end cell only */
+    FZ_STATS = 1u << 2             /* fill *stats (adds stream syncs for phase timings) */
+};
+
+enum {
+    FZ_OK = 0,
+    FZ_EINVAL = -1,                /* bad argument, or a byte other than ACGTacgt */
+    FZ_ENOMEM = -2,                /* device allocation failed */
+    FZ_EDEVICE = -3,               /* HIP runtime error */
+    FZ_EBAND = -4                  /* (reserved) */
+};
+
+enum {
+    FZ_HIT_TRACED = 1,             /* CIGAR present */
+    FZ_HIT_EAGER_LEFT = 2,         /* left side traced inside the inspector (<= 16x16) */
+    FZ_HIT_EAGER_RIGHT = 4,
+    FZ_HIT_BELOW_MIN = 8,          /* score <= min_traceback_score: no CIGAR by request */
+    FZ_HIT_EBAND = 16,             /* a side's band outgrew the widest kernel: result invalid */
+    FZ_HIT_ESEED = 32,             /* seed outside its window or window outside the sequences */
+    FZ_HIT_ERANGE = 64             /* window too long for int32 scores with these parameters */
+};
+
+#define FZ_YDROP_INF 2147483647    /* ydrop >= this: no pruning */
+
+/* Create a context on HIP device `device`.  The context owns its device
+ * workspace (grown on demand, reused across calls) and the CIGAR buffer.
+ * Returns FZ_OK or a negative code; *out is NULL on failure. */
+int fz_create(fz_ctx **out, int device);
+
+/* Free the context and every device buffer it owns.  NULL is ignored. */
+void fz_destroy(fz_ctx *ctx);
+
+/* Message of the last failed call on ctx ("" if none).  Valid until the
+ * next call on ctx.  Not thread-safe per context. */
+const char *fz_last_error(const fz_ctx *ctx);
+
+/* Cap (bytes) of the traceback-pointer workspace; the executor works in
+ * batches that fit.  0 restores the default (1/4 of free device memory,
+ * at most 32 GiB). */
+int fz_set_pointer_workspace(fz_ctx *ctx, uint64_t bytes);
+
+/*
+ * Extend a batch of seeds (or, with FZ_LOCAL, align a batch of windows).
+ *   target, query   device, ASCII bases (A/C/G/T in either case; any other
+ *                   byte makes the call fail with FZ_EINVAL), lengths in bytes
+ *   seeds           device, n_seeds records
+ *   scoring         host; costs must be >= 0
+ *   ydrop           >= 0; FZ_YDROP_INF disables pruning (ignored in local mode)
+ *   min_traceback_score   with FZ_TRACEBACK, seeds whose score is strictly
+ *                   greater get a CIGAR; others get FZ_HIT_BELOW_MIN
+ *   flags           FZ_TRACEBACK | FZ_LOCAL | FZ_STATS
+ *   hits            device, n_seeds records, written by the call
+ *   cigar           out (may be NULL): device pointer to the CIGAR words,
+ *                   BAM-style (length << 4 | op, op 0 = M, 1 = I, 2 = D),
+ *                   owned by ctx, valid until the next call or fz_destroy
+ *   cigar_words     out (may be NULL): number of words at *cigar
+ *   stats           host, optional
+ *   stream          hipStream_t or NULL
+ * Returns FZ_OK or a negative FZ_E* code.
+ */
+int fz_extend_batch(fz_ctx *ctx,
+                    const uint8_t *target, uint64_t target_len,
+                    const uint8_t *query, uint64_t query_len,
+                    const fz_seed *seeds, uint64_t n_seeds,
+                    const fz_scoring *scoring, int32_t ydrop,
+                    int64_t min_traceback_score, uint32_t flags,
+                    fz_hit *hits, const uint32_t **cigar, uint64_t *cigar_words,
+                    fz_stats *stats, void *stream);
+
+/* Copy the first `words` CIGAR words of the last successful fz_extend_batch
+ * on ctx into caller device memory `dst` (enqueued on `stream`, which is
+ * synchronised before return).  words must not exceed the count that call
+ * returned.  Returns FZ_OK or a negative code. */
+int fz_copy_cigar(fz_ctx *ctx, uint32_t *dst, uint64_t words, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FZ_H */

@@ -1,0 +1,133 @@
+// fz_device.hpp -- records and wave64 helpers shared by the libfz kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fz {
+
+// "Minus infinity" for scores.  Live scores stay above T_FLOOR (the library
+// rejects windows whose worst-case score could reach it), so anything built
+// from NEG stays below every threshold and never wraps.
+constexpr int32_t NEG = -(1 << 30);
+constexpr int32_t T_FLOOR = -(1 << 29);
+constexpr int64_t SCORE_LIMIT = (int64_t)1 << 29;
+
+// Padding (bases) around the packed sequences: kernels read whole window
+// rows that may run past a window edge.
+constexpr int64_t PAD = 4096;
+
+// Eager traceback block of FastZ section 3.1.2: extensions whose best cell
+// has i, j <= 16 are traced inside the inspector.
+constexpr int EAGER_EDGE = 16;
+constexpr int EAGER_ROWS = 2 * EAGER_EDGE + 1;   // anti-diagonals 0..32
+constexpr int EAGER_OPS = 2 * EAGER_EDGE;
+
+// Length bins of FastZ section 3.3: 512, 2048, 8192, 32768, then x4.
+constexpr int NBINS = 8;
+
+struct Scoring {
+    int32_t match, ts, tv;      // substitution scores
+    int32_t oe, e;              // open + extend, extend
+    uint32_t lut;               // int8 score per xor code (A=0,C=1,G=2,T=3): [match, tv, ts, tv]
+    int32_t ydrop;              // >= 0; values >= SCORE_LIMIT act as "no pruning"
+    int32_t small;              // lut usable (all three scores fit int8)
+};
+
+// One side of one seed.  a_i = A[abase + i], b_j = B[bbase - j] for
+// i = 1..m, j = 1..n.  A and B are padded code arrays (0..3), so every
+// index a kernel forms for cells near the window stays inside them.
+struct SideTask {
+    const uint8_t *A;
+    const uint8_t *B;
+    int64_t abase, bbase;
+    int32_t m, n;               // m < 0: skip (invalid seed)
+    int32_t seed, side;         // side 0 = left, 1 = right
+};
+
+enum : int32_t { SO_OVERFLOW = 1, SO_EAGER = 2, SO_SKIPPED = 4, SO_EXEC_MISMATCH = 8, SO_WIDE_FLAG = 16 };
+
+struct SideOut {
+    int32_t score, ie, je, dend;
+    int64_t cells;
+    int64_t ptr_bytes;          // executor pointer bytes through the best anti-diagonal
+    int32_t flags, eager_len;
+};
+
+// One side queued for the executor / walker.
+struct ExecItem {
+    int32_t side;               // index into tasks / side outputs
+    int32_t dstar;              // anti-diagonal of the best cell
+    int64_t ptr_off;            // byte offset of its pointer rows (whole list; a batch subtracts its base)
+    int64_t ptr_bytes;
+    int64_t batch;
+};
+
+// Row header of the executor's pointer store, one per anti-diagonal.
+struct RowHdr {
+    uint32_t off;               // dword offset of the row inside the side's row area
+    int32_t ibase;              // i of slot 0 of the row's first lane
+};
+
+// ----------------------------------------------------------- wave helpers --
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+// Lane l receives lane l+1's value; lane 63 receives `fill`.
+__device__ __forceinline__ int from_next_lane(int v, int fill)
+{
+    return __builtin_amdgcn_update_dpp(fill, v, 0x130 /* wave_shl:1 */, 0xF, 0xF, false);
+}
+
+// Lane l receives lane l-1's value; lane 0 receives `fill`.
+__device__ __forceinline__ int from_prev_lane(int v, int fill)
+{
+    return __builtin_amdgcn_update_dpp(fill, v, 0x138 /* wave_shr:1 */, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ int wave_max(int v)
+{
+    for (int off = 32; off >= 1; off >>= 1) {
+        int o = __shfl_xor(v, off);
+        v = v > o ? v : o;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ int ctz64(uint64_t x) { return __builtin_ctzll(x); }
+__device__ __forceinline__ int hibit64(uint64_t x) { return 63 - __builtin_clzll(x); }
+
+// Lanes [lo, hi] as a mask (empty when hi < lo); lo, hi clamped to 0..63.
+__device__ __forceinline__ uint64_t lane_range(int lo, int hi)
+{
+    lo = lo < 0 ? 0 : lo;
+    hi = hi > 63 ? 63 : hi;
+    if (hi < lo) return 0ull;
+    return (~0ull >> (63 - hi)) & (~0ull << lo);
+}
+
+__device__ __forceinline__ int floordiv(int a, int b)
+{
+    int q = a / b;
+    return (q * b > a) ? q - 1 : q;
+}
+
+// NW little-endian dwords holding bytes p[x], p[x+1], ... built from
+// dword-aligned loads (p itself is 256-byte aligned).
+template <int NW>
+__device__ __forceinline__ void load_bytes(const uint8_t *p, int64_t x, uint32_t (&out)[NW])
+{
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(p + (x & ~(int64_t)3));
+    const uint32_t sh = (uint32_t)(x & 3);
+    uint32_t raw[NW + 1];
+#pragma unroll
+    for (int k = 0; k <= NW; ++k) raw[k] = w[k];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) out[k] = __builtin_amdgcn_alignbyte(raw[k + 1], raw[k], sh);
+}
+
+}  // namespace fz

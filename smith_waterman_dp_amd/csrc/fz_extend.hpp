@@ -1,0 +1,430 @@
+// fz_extend.hpp -- one-sided y-drop extension, one wave64 per side (gfx950).
+//
+// Used twice, as in the inspector-executor scheme of FastZ (SC'21, section 3):
+//   inspector (EXEC = false): score only; finds the best cell, the canonical
+//     cell count, the executor's pointer-memory size, and traces sides whose
+//     best cell lies in the 16 x 16 corner at once (section 3.1.2);
+//   executor  (EXEC = true):  recomputes the same band up to the best cell's
+//     anti-diagonal and stores a 4-bit pointer per cell (section 3.1.3).
+//
+// Layout.  The wave works one anti-diagonal d = i + j at a time (FastZ
+// section 2.2, observations (2) and (3)).  Cells of the current band sit at
+// "positions" p = i - o_d, o_d = (d + K) >> 1, of a window of W = 64 * C
+// positions: lane l holds positions l*C .. l*C + C - 1 in registers.  A
+// position keeps its k = i - j from one diagonal to the next-but-one, so the
+// diagonal predecessor (i-1, j-1) is the same register; the up and left
+// predecessors are the same or the adjacent position, and only one value per
+// diagonal crosses a lane boundary (one DPP move).  Three diagonals live in
+// registers (S of d-1 and d-2, plus the gap states handed on from d-1): the
+// circular use-and-discard buffer of section 3.2.  K is even, so
+// o_d - o_(d-1) is 1 on even d and 0 on odd d; the loop is unrolled by two
+// to make that a compile-time fact.  When the band nears a window edge the
+// window slides by whole lanes; a band wider than the window sets
+// SO_OVERFLOW and the side is redone by a wider instantiation.
+//
+// Per cell (positions are lane-private): H = S(d-2) + sub; S = max3(H, I, D);
+// live iff S >= T_d; U = S - (O + E); the I handed right is max(I - E, U),
+// the D handed down is max(D - E, U).  A dead cell only keeps S = -inf: its
+// handed-on gap values are below T_d <= T_(d+1) and cannot revive a cell or
+// tie a live one, so live values and traceback choices equal the definition
+// where dead cells hold -inf in all three states.
+#pragma once
+
+#include "fz_device.hpp"
+
+namespace fz {
+
+struct ExtendArgs {
+    const SideTask *tasks;
+    const int32_t *list;        // inspector: side ids (NULL = identity); executor: unused
+    int32_t nlist;
+    const ExecItem *exec;       // executor items (EXEC only)
+    int64_t exec_begin;         // executor batch [begin, begin + nlist) into exec
+    uint8_t *ptr_ws;            // executor pointer workspace
+    int64_t ptr_base_off;       // list offset that maps to ptr_ws[0] for this batch
+    SideOut *out;
+    uint8_t *eager_ops;         // EAGER_OPS bytes per side (op codes 0 M, 1 I, 2 D; end-first)
+    uint32_t *queue;            // work counter
+    int32_t *overflow_list;     // sides that outgrew the window
+    uint32_t *overflow_count;
+    int64_t *exec_cells;        // executor: cells recomputed (stats)
+    int32_t result_flags;       // OR'ed into every inspector result (SO_WIDE_FLAG for the wide pass)
+    Scoring sc;
+};
+
+template <int C, bool EXEC, bool SMALL>
+struct SideDP {
+    static constexpr int W = 64 * C;
+    static constexpr int NDW = (C + 3) / 4;             // dwords of bases per lane
+    static constexpr int P0 = 32 * C;                   // position of (0,0): lane 32, slot 0
+    static constexpr int EL0 = 32 - (8 + C - 1) / C;    // lanes holding the eager block
+    static constexpr int EL1 = 32 + 8 / C;
+    static constexpr int NEL = EL1 - EL0 + 1;
+
+    // registers
+    int SA[C], SB[C], R[C], Dn[C];
+    // wave-uniform state
+    int K;
+    int lo1, hi1, lo2, hi2;     // live hulls (positions) of d-1 and d-2
+    int best, bi, bj, dend;
+    int64_t cells, cum_bytes, ptr_at_best;
+    bool overflow;
+    // executor
+    uint32_t rowoff, rowcap;    // rows written / rows the inspector sized
+    RowHdr *hdr;
+    uint32_t *rows;
+
+    const SideTask &t;
+    const Scoring &sc;
+    const int lane;
+
+    __device__ SideDP(const SideTask &task, const Scoring &s) : t(task), sc(s), lane(lane_id()) {}
+
+    __device__ __forceinline__ int sub_of(uint32_t X, uint32_t P, int c) const
+    {
+        if (SMALL) {
+            return (int)(int8_t)((P >> (8 * (c & 3))) & 0xFF);
+        } else {
+            const uint32_t x = (X >> (8 * (c & 3))) & 3u;
+            return x == 0 ? sc.match : (x == 2 ? sc.ts : sc.tv);
+        }
+    }
+
+    // Evaluate diagonal d.  DELTA = o_d - o_(d-1); S of d-2 is in SN (and
+    // is replaced by S of d), S of d-1 is in SP.  Returns the packed
+    // pointer word (PTR) of this lane's C cells.
+    template <int DELTA, bool PTR>
+    __device__ __forceinline__ uint32_t cells_of(int (&SN)[C], int od, int d, int T, bool masked, int rlo,
+                                                 int rhi, uint64_t (&live)[C], int &dmax)
+    {
+        // bases: a_i for i = i0 + c, b_j for j = d - i0 - c
+        const int i0 = lane * C + od;
+        uint32_t TA[NDW], QB[NDW], X[NDW], P[NDW];
+        load_bytes<NDW>(t.A, t.abase + i0, TA);
+        load_bytes<NDW>(t.B, t.bbase - d + i0, QB);
+#pragma unroll
+        for (int k = 0; k < NDW; ++k) {
+            X[k] = TA[k] ^ QB[k];
+            P[k] = SMALL ? __builtin_amdgcn_perm(0u, sc.lut, X[k]) : 0u;
+        }
+        // the one value that crosses a lane boundary
+        int cross;
+        if (DELTA == 1) cross = from_next_lane(R[0], NEG);       // left of slot C-1 is next lane's slot 0
+        else cross = from_prev_lane(Dn[C - 1], NEG);            // up of slot 0 is previous lane's slot C-1
+
+        uint32_t word = 0;
+        dmax = NEG;
+        int Rn[C], Dnn[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int Iv = DELTA == 1 ? (c < C - 1 ? R[c + 1] : cross) : R[c];
+            const int Dv = DELTA == 1 ? Dn[c] : (c > 0 ? Dn[c - 1] : cross);
+            const int H = SN[c] + sub_of(X[c / 4], P[c / 4], c);
+            int S = max(max(H, Iv), Dv);
+            bool ok = S >= T;
+            if (masked) {
+                const int pos = lane * C + c;
+                ok = ok && pos >= rlo && pos <= rhi;
+            }
+            live[c] = ballot(ok);
+            const int Sk = ok ? S : NEG;
+            const int U = Sk - sc.oe;
+            const int Ie = Iv - sc.e, De = Dv - sc.e;
+            Rn[c] = max(Ie, U);
+            Dnn[c] = max(De, U);
+            if (PTR) {
+                const uint32_t src = (S == H) ? 0u : (S == Iv ? 1u : 2u);
+                const uint32_t nib = src | (Ie > U ? 4u : 0u) | (De > U ? 8u : 0u);
+                word |= nib << (4 * c);
+            }
+            SN[c] = Sk;
+            dmax = max(dmax, Sk);
+        }
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            R[c] = Rn[c];
+            Dn[c] = Dnn[c];
+        }
+        return word;
+    }
+
+    __device__ __forceinline__ void slide(int s)
+    {
+        // s > 0: lane l takes lane l+s's registers (window moves to larger i - j)
+        while (s > 0) {
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                SA[c] = from_next_lane(SA[c], NEG);
+                SB[c] = from_next_lane(SB[c], NEG);
+                R[c] = from_next_lane(R[c], NEG);
+                Dn[c] = from_next_lane(Dn[c], NEG);
+            }
+            --s;
+        }
+        while (s < 0) {
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                SA[c] = from_prev_lane(SA[c], NEG);
+                SB[c] = from_prev_lane(SB[c], NEG);
+                R[c] = from_prev_lane(R[c], NEG);
+                Dn[c] = from_prev_lane(Dn[c], NEG);
+            }
+            ++s;
+        }
+    }
+
+    // One anti-diagonal.  Returns false when the extension is over.
+    template <int DELTA, bool PTR>
+    __device__ __forceinline__ bool step(int d, int dstop, uint32_t *eager_lds)
+    {
+        int od = (d + K) >> 1;
+        // R_d: cells with a possibly live predecessor, clipped to the matrix
+        int rlo = 0x7fffffff, rhi = -0x7fffffff;
+        if (lo1 <= hi1) {
+            rlo = lo1 - DELTA;
+            rhi = hi1 - DELTA + 1;
+        }
+        if (lo2 <= hi2) {
+            rlo = min(rlo, lo2);
+            rhi = max(rhi, hi2);
+        }
+        const int vlo = max(0, d - t.n) - od, vhi = min(t.m, d) - od;
+        rlo = max(rlo, vlo);
+        rhi = min(rhi, vhi);
+        if (rlo > rhi) return false;
+        if (EXEC && d > dstop) return false;
+        if (rlo < 0 || rhi > W - 1) {
+            // slide by s lanes so that [rlo, rhi] fits, near the centre
+            const int smin = floordiv(rhi - (W - 1) + C - 1, C), smax = floordiv(rlo, C);
+            if (smin > smax) {
+                overflow = true;
+                return false;
+            }
+            int s = floordiv((rlo + rhi + 1) / 2 - W / 2, C);
+            s = s < smin ? smin : (s > smax ? smax : s);
+            slide(s);
+            const int sh = s * C;
+            K += 2 * sh;
+            od += sh;
+            lo1 -= sh; hi1 -= sh; lo2 -= sh; hi2 -= sh;
+            rlo -= sh; rhi -= sh;
+        }
+        // positions with i > m or j > n are the only ones that can pick up a
+        // live value without being in R_d; mask explicitly only when the
+        // window reaches them (cells with i < 0 or j < 0 only ever see -inf)
+        const bool masked = (W - 1 + od > t.m) || (d - od > t.n);
+        const int64_t tw = (int64_t)best - (int64_t)sc.ydrop;
+        const int T = tw < (int64_t)T_FLOOR ? T_FLOOR : (int)tw;
+
+        uint64_t live[C];
+        int dmax;
+        uint32_t word;
+        if (DELTA == 1) word = cells_of<DELTA, PTR>(SA, od, d, T, masked, rlo, rhi, live, dmax);   // even d
+        else word = cells_of<DELTA, PTR>(SB, od, d, T, masked, rlo, rhi, live, dmax);             // odd d
+
+        // live hull of d
+        uint64_t any = 0;
+#pragma unroll
+        for (int c = 0; c < C; ++c) any |= live[c];
+        int lo = 1, hi = 0, llo = 0, lhi = -1;
+        if (any) {
+            llo = ctz64(any);
+            lhi = hibit64(any);
+            int slo = C, shi = -1;
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                if (slo == C && ((live[c] >> llo) & 1ull)) slo = c;
+                if ((live[c] >> lhi) & 1ull) shi = c;
+            }
+            lo = llo * C + slo;
+            hi = lhi * C + shi;
+        }
+        cells += rhi - rlo + 1;
+        const int nl = lhi - llo + 1;
+        cum_bytes += 8 + 4 * (int64_t)nl;
+
+        if (ballot(dmax > best)) {
+            const int nb = wave_max(dmax);
+            int pbest = 0x7fffffff;
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                // recover this diagonal's S from the register it was written to
+                const int Sv = DELTA == 1 ? SA[c] : SB[c];
+                const uint64_t m = ballot(Sv == nb);
+                if (m) pbest = min(pbest, ctz64(m) * C + c);
+            }
+            best = nb;
+            bi = pbest + od;
+            bj = d - bi;
+            ptr_at_best = cum_bytes;
+        }
+
+        if (EXEC) {
+            if (rowoff + (uint32_t)nl > rowcap) {
+                // the recompute disagrees with the inspector's sizing
+                overflow = true;
+                return false;
+            }
+            if (lane == 0) {
+                RowHdr h;
+                h.off = rowoff;
+                h.ibase = llo * C + od;
+                hdr[d] = h;
+            }
+            if (lane >= llo && lane <= lhi) rows[rowoff + (lane - llo)] = word;
+            rowoff += (uint32_t)nl;
+        } else if (PTR) {
+            if (lane >= EL0 && lane <= EL1) eager_lds[d * NEL + (lane - EL0)] = word;
+        }
+
+        lo2 = lo1; hi2 = hi1;
+        lo1 = lo; hi1 = hi;
+        dend = d;
+        return true;
+    }
+
+    __device__ void run(int dstop, uint32_t *eager_lds, uint8_t *ptr_base, int64_t ptr_bytes = 0)
+    {
+#pragma unroll
+        for (int c = 0; c < C; ++c) { SA[c] = NEG; SB[c] = NEG; R[c] = NEG; Dn[c] = NEG; }
+        K = -W;
+        // d = 0: the single cell (0,0), S = 0, I = D = -inf
+        if (lane == P0 / C) {
+            SA[0] = 0;
+            R[0] = -sc.oe;
+            Dn[0] = -sc.oe;
+        }
+        lo1 = P0; hi1 = P0; lo2 = 1; hi2 = 0;
+        best = 0; bi = 0; bj = 0; dend = 0;
+        cells = 1;
+        cum_bytes = 8 + 4;
+        ptr_at_best = cum_bytes;
+        overflow = false;
+        rowoff = 0;
+        if (EXEC) {
+            hdr = reinterpret_cast<RowHdr *>(ptr_base);
+            rows = reinterpret_cast<uint32_t *>(ptr_base + 8 * ((int64_t)dstop + 1));
+            if (lane == 0) {
+                RowHdr h;
+                h.off = 0;
+                h.ibase = 0;         // lane 32 slot 0 is i = 0
+                hdr[0] = h;
+            }
+            if (lane == P0 / C) rows[0] = 0u;   // (0,0): source 0, gaps opened
+            rowoff = 1;
+            rowcap = (uint32_t)((ptr_bytes - 8 * ((int64_t)dstop + 1)) / 4);
+        } else {
+            if (lane >= EL0 && lane <= EL1) eager_lds[lane - EL0] = 0u;
+        }
+        int d = 1;
+        if (!EXEC) {
+            // diagonals 1..32 keep pointers for the eager block
+            bool go = true;
+            for (; d <= EAGER_ROWS - 1 && go; d += 2) {
+                go = step<0, true>(d, dstop, eager_lds);
+                if (go) go = step<1, true>(d + 1, dstop, eager_lds);
+            }
+            if (!go) return;
+        }
+        for (;; d += 2) {
+            if (!step<0, EXEC>(d, dstop, eager_lds)) break;
+            if (!step<1, EXEC>(d + 1, dstop, eager_lds)) break;
+        }
+    }
+
+    // Walk the eager block from (bi, bj) (lane 0 only).  Ops end-first.
+    __device__ int eager_walk(const uint32_t *eager_lds, uint8_t *ops) const
+    {
+        int i = bi, j = bj, st = 0, n = 0;
+        auto nib = [&](int ii, int jj) -> uint32_t {
+            const int dd = ii + jj;
+            const int od0 = (dd - W) >> 1;     // no slide happens before diagonal 33
+            const int p = ii - od0;
+            const int l = p / C, c = p % C;
+            return (eager_lds[dd * NEL + (l - EL0)] >> (4 * c)) & 0xFu;
+        };
+        while (!(st == 0 && i == 0 && j == 0) && n < EAGER_OPS && i >= 0 && j >= 0) {
+            if (st == 0) {
+                const uint32_t src = nib(i, j) & 3u;
+                if (src == 0) { ops[n++] = 0; --i; --j; }
+                else st = (int)src;
+            } else if (st == 1) {
+                ops[n++] = 1;
+                if (--j < 0) break;
+                st = (nib(i, j) & 4u) ? 1 : 0;
+            } else {
+                ops[n++] = 2;
+                if (--i < 0) break;
+                st = (nib(i, j) & 8u) ? 2 : 0;
+            }
+        }
+        return (st == 0 && i == 0 && j == 0) ? n : -1;
+    }
+};
+
+template <int C, bool EXEC, bool SMALL, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void extend_kernel(ExtendArgs a)
+{
+    using DP = SideDP<C, EXEC, SMALL>;
+    __shared__ uint32_t eager_lds_all[WAVES][EAGER_ROWS * DP::NEL];
+    uint32_t *eager_lds = eager_lds_all[threadIdx.x / 64];
+    const int lane = lane_id();
+    for (;;) {
+        int idx = 0;
+        if (lane == 0) idx = (int)atomicAdd(a.queue, 1u);
+        idx = uniform(idx);
+        int64_t item;
+        if (EXEC) {
+            item = a.exec_begin + idx;
+            if (idx >= a.nlist) break;
+        } else {
+            if (idx >= a.nlist) break;
+            item = idx;
+        }
+        const int sid = EXEC ? a.exec[item].side : (a.list ? a.list[item] : (int)item);
+        const SideTask task = a.tasks[sid];
+        SideOut *o = &a.out[sid];
+        if (task.m < 0) {
+            if (!EXEC && lane == 0) {
+                SideOut r = {};
+                r.flags = SO_SKIPPED;
+                *o = r;
+            }
+            continue;
+        }
+        DP dp(task, a.sc);
+        if (EXEC) {
+            const ExecItem it = a.exec[item];
+            dp.run(it.dstar, nullptr, a.ptr_ws + (it.ptr_off - a.ptr_base_off), it.ptr_bytes);
+            if (lane == 0) {
+                atomicAdd((unsigned long long *)a.exec_cells, (unsigned long long)dp.cells);
+                if (dp.overflow || dp.best != o->score || dp.bi != o->ie) atomicOr(&o->flags, SO_EXEC_MISMATCH);
+            }
+        } else {
+            dp.run(0x7fffffff, eager_lds, nullptr);
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            SideOut r;
+            r.score = dp.best;
+            r.ie = dp.bi;
+            r.je = dp.bj;
+            r.dend = dp.dend;
+            r.cells = dp.cells;
+            r.ptr_bytes = dp.ptr_at_best;
+            r.flags = (dp.overflow ? SO_OVERFLOW : 0) | a.result_flags;
+            r.eager_len = 0;
+            if (!dp.overflow && dp.bi <= EAGER_EDGE && dp.bj <= EAGER_EDGE) {
+                r.flags |= SO_EAGER;
+                if (lane == 0) r.eager_len = dp.eager_walk(eager_lds, a.eager_ops + (int64_t)sid * EAGER_OPS);
+            }
+            if (lane == 0) {
+                *o = r;
+                if (dp.overflow) {
+                    const uint32_t k = atomicAdd(a.overflow_count, 1u);
+                    a.overflow_list[k] = sid;
+                }
+            }
+        }
+    }
+}
+
+}  // namespace fz

@@ -1,0 +1,646 @@
+// fz_lib.hip -- C ABI of libfz: batched gapped seed extension on gfx950.
+//
+// Phases of one fz_extend_batch call (FastZ, SC'21, section 3 and Fig. 8):
+//   pack      ASCII -> codes, forward and reversed copies, with validation
+//   setup     seeds -> two side tasks each, seed-column scores
+//   inspect   score-only y-drop extension of every side (one wave per side,
+//             persistent waves pulling sides from an atomic queue, which
+//             takes the place of the paper's 32 CUDA streams, section 3.4);
+//             sides whose best cell is in the 16 x 16 corner are traced here
+//   widen     sides whose band outgrew the window are redone with a wider one
+//   bin       per seed totals; executor sides counted and scattered by length
+//             bin, longest bins first (section 3.3)
+//   execute   in batches that fit the pointer workspace: pruned recompute
+//             with 4-bit pointers, then one lane per side walks them back
+//   gather    left ops + seed + reversed right ops, merged into CIGAR words
+// Local mode runs pack and one full-window kernel.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/fz.h"
+#include "fz_aux.hpp"
+#include "fz_device.hpp"
+#include "fz_extend.hpp"
+#include "fz_local.hpp"
+
+using namespace fz;
+
+namespace {
+
+struct DevBuf {
+    void *p = nullptr;
+    size_t cap = 0;
+};
+
+// Scalars the kernels update, one allocation.
+struct Counters {
+    uint32_t err;               // bit 0: non-ACGT byte; bit 1: broken traceback
+    uint32_t queue[4];
+    uint32_t overflow_count[2];
+    uint32_t bin_count[2 * NBINS];
+    uint32_t bin_base[2 * NBINS];
+    uint32_t bin_fill[2 * NBINS];
+    int64_t max_ptr;
+    int64_t exec_cells;
+    int64_t totals[4];
+};
+
+constexpr int WAVES = 4;                // waves per block for the wave-per-side kernels
+constexpr int C_STD = 6;                // window 384 positions
+constexpr int C_WIDE = 16;              // window 1024 positions
+constexpr int LOCAL_RL = 32;            // rows per lane in local mode
+
+}  // namespace
+
+struct fz_ctx {
+    int device = 0;
+    int n_cu = 256;
+    std::string err;
+    uint64_t ptr_cap = 0;               // 0 = default
+    uint64_t last_words = 0;            // CIGAR words of the last successful call
+    DevBuf Tf, Tr, Qf, Qr;
+    DevBuf tasks, info, out, eager, side_trace, run_cap, run_off, run_len, runs;
+    DevBuf items, batch_first, scan_tmp, cig, cigar, ptr_ws, counters, ovl0, ovl1, bnd;
+    hipEvent_t ev[8] = {};
+    hipEvent_t kev[2] = {};             // brackets the dominant kernel
+};
+
+namespace {
+
+int fail(fz_ctx *ctx, int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    ctx->err = buf;
+    return code;
+}
+
+#define HIP_OK(call)                                                                                   \
+    do {                                                                                               \
+        hipError_t e_ = (call);                                                                        \
+        if (e_ != hipSuccess) return fail(ctx, FZ_EDEVICE, "%s: %s", #call, hipGetErrorString(e_));    \
+    } while (0)
+
+int ensure(fz_ctx *ctx, DevBuf &b, size_t bytes)
+{
+    if (bytes == 0) bytes = 256;
+    if (b.cap >= bytes) return FZ_OK;
+    if (b.p) {
+        (void)hipFree(b.p);
+        b.p = nullptr;
+        b.cap = 0;
+    }
+    size_t want = bytes + bytes / 8;
+    if (hipMalloc(&b.p, want) != hipSuccess) {
+        (void)hipGetLastError();
+        if (hipMalloc(&b.p, bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            b.p = nullptr;
+            return fail(ctx, FZ_ENOMEM, "device allocation of %zu bytes failed", bytes);
+        }
+        want = bytes;
+    }
+    b.cap = want;
+    return FZ_OK;
+}
+
+#define ENSURE(buf, bytes)                                   \
+    do {                                                     \
+        int r_ = ensure(ctx, (buf), (size_t)(bytes));        \
+        if (r_ != FZ_OK) return r_;                          \
+    } while (0)
+
+template <class T>
+T *as(DevBuf &b) { return reinterpret_cast<T *>(b.p); }
+
+inline unsigned blocks_for(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
+
+__global__ void zero_kernel(uint32_t *p, int64_t nwords)
+{
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < nwords; k += (int64_t)gridDim.x * blockDim.x)
+        p[k] = 0u;
+}
+
+int zero(fz_ctx *ctx, void *p, size_t bytes, hipStream_t st)
+{
+    const int64_t w = (int64_t)((bytes + 3) / 4);
+    zero_kernel<<<std::min<int64_t>(blocks_for(w, 256), 4096), 256, 0, st>>>((uint32_t *)p, w);
+    HIP_OK(hipGetLastError());
+    return FZ_OK;
+}
+
+// Exclusive scan of n int64 values read at vals[k * stride] into
+// out[k * ostride]; the total lands in *d_total (device).
+int scan(fz_ctx *ctx, const int64_t *vals, int64_t stride, int64_t n, int64_t *outv, int64_t ostride,
+         int64_t *d_total, hipStream_t st)
+{
+    const int64_t nb = std::max<int64_t>(1, (n + SCAN_TILE - 1) / SCAN_TILE);
+    ENSURE(ctx->scan_tmp, (size_t)nb * sizeof(int64_t));
+    int64_t *bs = as<int64_t>(ctx->scan_tmp);
+    if (n > 0) {
+        scan_reduce_kernel<<<(unsigned)nb, SCAN_BLOCK, 0, st>>>(vals, stride, n, bs);
+        HIP_OK(hipGetLastError());
+    }
+    scan_top_kernel<<<1, SCAN_BLOCK, 0, st>>>(bs, n > 0 ? nb : 0, d_total);
+    HIP_OK(hipGetLastError());
+    if (n > 0) {
+        scan_apply_kernel<<<(unsigned)nb, SCAN_BLOCK, 0, st>>>(vals, stride, n, bs, outv, ostride);
+        HIP_OK(hipGetLastError());
+    }
+    return FZ_OK;
+}
+
+Scoring make_scoring(const fz_scoring *s, int32_t ydrop)
+{
+    Scoring sc;
+    sc.match = s->match;
+    sc.ts = s->transition;
+    sc.tv = s->transversion;
+    sc.oe = s->gap_open + s->gap_extend;
+    sc.e = s->gap_extend;
+    auto fits = [](int v) { return v >= -128 && v <= 127; };
+    sc.small = fits(sc.match) && fits(sc.ts) && fits(sc.tv);
+    // xor code of two base codes: 0 equal, 2 transition, 1 or 3 transversion
+    sc.lut = ((uint32_t)(sc.match & 0xFF)) | ((uint32_t)(sc.tv & 0xFF) << 8) | ((uint32_t)(sc.ts & 0xFF) << 16) |
+             ((uint32_t)(sc.tv & 0xFF) << 24);
+    sc.ydrop = (int64_t)ydrop >= SCORE_LIMIT ? (int32_t)SCORE_LIMIT : ydrop;
+    return sc;
+}
+
+template <int C, bool EXEC>
+int launch_extend(fz_ctx *ctx, const ExtendArgs &a, int64_t nwork, hipStream_t st)
+{
+    if (nwork <= 0) return FZ_OK;
+    const int64_t max_blocks = (int64_t)ctx->n_cu * 8;
+    const unsigned blocks = (unsigned)std::min<int64_t>((nwork + WAVES - 1) / WAVES, max_blocks);
+    if (a.sc.small) extend_kernel<C, EXEC, true, WAVES><<<blocks, 64 * WAVES, 0, st>>>(a);
+    else extend_kernel<C, EXEC, false, WAVES><<<blocks, 64 * WAVES, 0, st>>>(a);
+    HIP_OK(hipGetLastError());
+    return FZ_OK;
+}
+
+int check_args(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const uint8_t *query, uint64_t qlen,
+               const fz_seed *seeds, uint64_t n, const fz_scoring *sc, int32_t ydrop, uint32_t flags, fz_hit *hits)
+{
+    if (!sc) return fail(ctx, FZ_EINVAL, "scoring is NULL");
+    if (n > 0 && (!seeds || !hits)) return fail(ctx, FZ_EINVAL, "seeds or hits is NULL");
+    if ((tlen > 0 && !target) || (qlen > 0 && !query)) return fail(ctx, FZ_EINVAL, "sequence pointer is NULL");
+    if (tlen >= ((uint64_t)1 << 40) || qlen >= ((uint64_t)1 << 40)) return fail(ctx, FZ_EINVAL, "sequence too long");
+    if (n >= ((uint64_t)1 << 30)) return fail(ctx, FZ_EINVAL, "too many seeds (max 2^30 - 1 per call)");
+    if (sc->gap_open < 0 || sc->gap_extend < 0) return fail(ctx, FZ_EINVAL, "gap costs must be >= 0");
+    const int64_t lim = (int64_t)1 << 24;
+    if (sc->gap_open > lim || sc->gap_extend > lim || sc->match > lim || sc->match < -lim || sc->transition > lim ||
+        sc->transition < -lim || sc->transversion > lim || sc->transversion < -lim)
+        return fail(ctx, FZ_EINVAL, "scoring values must lie in [-2^24, 2^24]");
+    if (!(flags & FZ_LOCAL) && ydrop < 0) return fail(ctx, FZ_EINVAL, "ydrop must be >= 0");
+    if (flags & ~(uint32_t)(FZ_TRACEBACK | FZ_LOCAL | FZ_STATS)) return fail(ctx, FZ_EINVAL, "unknown flag bits");
+    if ((flags & FZ_LOCAL) && (flags & FZ_TRACEBACK)) return fail(ctx, FZ_EINVAL, "local mode has no traceback");
+    return FZ_OK;
+}
+
+struct Timer {
+    fz_ctx *ctx;
+    hipStream_t st;
+    bool on;
+    int k = 0;
+    void mark()
+    {
+        if (on && k < 8) (void)hipEventRecord(ctx->ev[k++], st);
+    }
+    float ms(int a, int b)
+    {
+        if (!on || b >= k) return 0.f;
+        float v = 0.f;
+        (void)hipEventElapsedTime(&v, ctx->ev[a], ctx->ev[b]);
+        return v;
+    }
+};
+
+int run_local(fz_ctx *ctx, const fz_seed *seeds, uint64_t n, uint64_t tlen, uint64_t qlen, const Scoring &sc,
+              fz_hit *hits, int64_t *d_max2, hipStream_t st)
+{
+    // windows taller than one strip spill their strip's last row; size that
+    // buffer by the largest windows (read back once)
+    window_max_kernel<<<blocks_for((int64_t)n, 256), 256, 0, st>>>(seeds, (int64_t)n, d_max2);
+    HIP_OK(hipGetLastError());
+    int64_t mx[2] = {0, 0};
+    HIP_OK(hipMemcpyAsync(mx, d_max2, sizeof mx, hipMemcpyDeviceToHost, st));
+    HIP_OK(hipStreamSynchronize(st));
+    int64_t stride = 0;
+    if (mx[0] > 64 * LOCAL_RL) stride = 2 * (std::max<int64_t>(mx[1], 0) + 1);
+    ENSURE(ctx->bnd, (size_t)std::max<int64_t>(stride, 1) * sizeof(int32_t) * (stride ? (size_t)n : 1));
+    LocalArgs a;
+    a.seeds = seeds;
+    a.n = (int64_t)n;
+    a.tlen = (int64_t)tlen;
+    a.qlen = (int64_t)qlen;
+    a.Tf = as<uint8_t>(ctx->Tf);
+    a.Qf = as<uint8_t>(ctx->Qf);
+    a.sc = sc;
+    a.hits = hits;
+    a.bnd = as<int32_t>(ctx->bnd);
+    a.bnd_stride = stride;
+    const unsigned blocks = blocks_for((int64_t)n, WAVES);
+    HIP_OK(hipEventRecord(ctx->kev[0], st));
+    if (sc.small) local_kernel<LOCAL_RL, true, WAVES><<<blocks, 64 * WAVES, 0, st>>>(a);
+    else local_kernel<LOCAL_RL, false, WAVES><<<blocks, 64 * WAVES, 0, st>>>(a);
+    HIP_OK(hipGetLastError());
+    HIP_OK(hipEventRecord(ctx->kev[1], st));
+    return FZ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fz_create(fz_ctx **out, int device)
+{
+    if (!out) return FZ_EINVAL;
+    *out = nullptr;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) {
+        (void)hipGetLastError();
+        return FZ_EDEVICE;
+    }
+    fz_ctx *ctx = new fz_ctx;
+    ctx->device = device;
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    if (hipSetDevice(device) != hipSuccess) {
+        delete ctx;
+        return FZ_EDEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) == hipSuccess && prop.multiProcessorCount > 0)
+        ctx->n_cu = prop.multiProcessorCount;
+    for (auto &e : ctx->kev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            (void)hipSetDevice(prev);
+            fz_destroy(ctx);
+            return FZ_EDEVICE;
+        }
+    }
+    for (auto &e : ctx->ev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            (void)hipSetDevice(prev);
+            fz_destroy(ctx);
+            return FZ_EDEVICE;
+        }
+    }
+    (void)hipSetDevice(prev);
+    *out = ctx;
+    return FZ_OK;
+}
+
+void fz_destroy(fz_ctx *ctx)
+{
+    if (!ctx) return;
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    (void)hipSetDevice(ctx->device);
+    DevBuf *bufs[] = {&ctx->Tf, &ctx->Tr, &ctx->Qf, &ctx->Qr, &ctx->tasks, &ctx->info, &ctx->out,
+                      &ctx->eager, &ctx->side_trace, &ctx->run_cap, &ctx->run_off, &ctx->run_len, &ctx->runs,
+                      &ctx->items, &ctx->batch_first, &ctx->scan_tmp, &ctx->cig, &ctx->cigar, &ctx->ptr_ws,
+                      &ctx->counters, &ctx->ovl0, &ctx->ovl1, &ctx->bnd};
+    for (DevBuf *b : bufs)
+        if (b->p) (void)hipFree(b->p);
+    for (auto &e : ctx->ev)
+        if (e) (void)hipEventDestroy(e);
+    for (auto &e : ctx->kev)
+        if (e) (void)hipEventDestroy(e);
+    (void)hipSetDevice(prev);
+    delete ctx;
+}
+
+const char *fz_last_error(const fz_ctx *ctx) { return ctx ? ctx->err.c_str() : "null context"; }
+
+int fz_set_pointer_workspace(fz_ctx *ctx, uint64_t bytes)
+{
+    if (!ctx) return FZ_EINVAL;
+    ctx->ptr_cap = bytes;
+    return FZ_OK;
+}
+
+static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const uint8_t *query, uint64_t qlen,
+                       const fz_seed *seeds, uint64_t n_seeds, const fz_scoring *scoring, int32_t ydrop,
+                       int64_t min_tb, uint32_t flags, fz_hit *hits, const uint32_t **cigar, uint64_t *cigar_words,
+                       fz_stats *stats, hipStream_t st)
+{
+    int rc = check_args(ctx, target, tlen, query, qlen, seeds, n_seeds, scoring, ydrop, flags, hits);
+    if (rc != FZ_OK) return rc;
+    if (cigar) *cigar = nullptr;
+    if (cigar_words) *cigar_words = 0;
+    fz_stats S;
+    memset(&S, 0, sizeof S);
+    Timer tm{ctx, st, (flags & FZ_STATS) != 0};
+    const int64_t n = (int64_t)n_seeds;
+    if (n == 0) {
+        if (stats) *stats = S;
+        return FZ_OK;
+    }
+    const Scoring sc = make_scoring(scoring, ydrop);
+    const int64_t NT = (int64_t)tlen + 2 * PAD, NQ = (int64_t)qlen + 2 * PAD;
+
+    ENSURE(ctx->counters, sizeof(Counters));
+    Counters *dc = as<Counters>(ctx->counters);
+    rc = zero(ctx, dc, sizeof(Counters), st);
+    if (rc) return rc;
+
+    tm.mark();
+    // ---- pack
+    ENSURE(ctx->Tf, NT + 64);
+    ENSURE(ctx->Tr, NT + 64);
+    ENSURE(ctx->Qf, NQ + 64);
+    ENSURE(ctx->Qr, NQ + 64);
+    {
+        const unsigned bt = std::min<int64_t>(blocks_for(NT, 256), 8192);
+        pack_kernel<<<bt, 256, 0, st>>>(target, (int64_t)tlen, as<uint8_t>(ctx->Tf), as<uint8_t>(ctx->Tr), NT,
+                                        &dc->err);
+        HIP_OK(hipGetLastError());
+        const unsigned bq = std::min<int64_t>(blocks_for(NQ, 256), 8192);
+        pack_kernel<<<bq, 256, 0, st>>>(query, (int64_t)qlen, as<uint8_t>(ctx->Qf), as<uint8_t>(ctx->Qr), NQ,
+                                        &dc->err);
+        HIP_OK(hipGetLastError());
+    }
+    Counters hc;
+    auto read_counters = [&]() -> int {
+        HIP_OK(hipMemcpyAsync(&hc, dc, sizeof(Counters), hipMemcpyDeviceToHost, st));
+        HIP_OK(hipStreamSynchronize(st));
+        return FZ_OK;
+    };
+
+    if (flags & FZ_LOCAL) {
+        rc = run_local(ctx, seeds, n_seeds, tlen, qlen, sc, hits, &dc->totals[0], st);
+        if (rc) return rc;
+        tm.mark();
+        if ((rc = read_counters())) return rc;
+        if (hc.err & 1u) return fail(ctx, FZ_EINVAL, "sequence holds a byte other than A, C, G, T");
+        if (stats) {
+            S.ms_inspect = tm.ms(0, 1);
+            (void)hipEventElapsedTime(&S.ms_main, ctx->kev[0], ctx->kev[1]);
+            *stats = S;
+        }
+        return FZ_OK;
+    }
+
+    // ---- setup
+    const int64_t nsides = 2 * n;
+    ENSURE(ctx->tasks, nsides * sizeof(SideTask));
+    ENSURE(ctx->info, n * sizeof(SeedInfo));
+    ENSURE(ctx->out, nsides * sizeof(SideOut));
+    ENSURE(ctx->eager, nsides * EAGER_OPS);
+    setup_kernel<<<blocks_for(n, 256), 256, 0, st>>>(seeds, n, (int64_t)tlen, (int64_t)qlen, as<uint8_t>(ctx->Tf),
+                                                      as<uint8_t>(ctx->Tr), as<uint8_t>(ctx->Qf),
+                                                      as<uint8_t>(ctx->Qr), NT, NQ, sc, as<SideTask>(ctx->tasks),
+                                                      as<SeedInfo>(ctx->info));
+    HIP_OK(hipGetLastError());
+    tm.mark();
+
+    // ---- inspect
+    ENSURE(ctx->ovl0, nsides * sizeof(int32_t));
+    ENSURE(ctx->ovl1, nsides * sizeof(int32_t));
+    ExtendArgs ea = {};
+    ea.tasks = as<SideTask>(ctx->tasks);
+    ea.list = nullptr;
+    ea.nlist = (int32_t)nsides;
+    ea.out = as<SideOut>(ctx->out);
+    ea.eager_ops = as<uint8_t>(ctx->eager);
+    ea.queue = &dc->queue[0];
+    ea.overflow_list = as<int32_t>(ctx->ovl0);
+    ea.overflow_count = &dc->overflow_count[0];
+    ea.exec_cells = &dc->exec_cells;
+    ea.result_flags = 0;
+    ea.sc = sc;
+    HIP_OK(hipEventRecord(ctx->kev[0], st));
+    rc = launch_extend<C_STD, false>(ctx, ea, nsides, st);
+    if (rc) return rc;
+    HIP_OK(hipEventRecord(ctx->kev[1], st));
+    if ((rc = read_counters())) return rc;
+    if (hc.err & 1u) return fail(ctx, FZ_EINVAL, "sequence holds a byte other than A, C, G, T");
+    S.n_overflow = hc.overflow_count[0];
+    if (hc.overflow_count[0] > 0) {
+        ExtendArgs wa = ea;
+        wa.list = as<int32_t>(ctx->ovl0);
+        wa.nlist = (int32_t)hc.overflow_count[0];
+        wa.queue = &dc->queue[1];
+        wa.overflow_list = as<int32_t>(ctx->ovl1);
+        wa.overflow_count = &dc->overflow_count[1];
+        wa.result_flags = SO_WIDE_FLAG;
+        rc = launch_extend<C_WIDE, false>(ctx, wa, wa.nlist, st);
+        if (rc) return rc;
+    }
+    tm.mark();
+
+    // ---- combine + bin
+    ENSURE(ctx->side_trace, nsides * sizeof(int32_t));
+    ENSURE(ctx->run_cap, nsides * sizeof(int64_t));
+    ENSURE(ctx->run_off, nsides * sizeof(int64_t));
+    ENSURE(ctx->run_len, nsides * sizeof(int64_t));
+    CombineArgs ca;
+    ca.seeds = seeds;
+    ca.n = n;
+    ca.out = as<SideOut>(ctx->out);
+    ca.info = as<SeedInfo>(ctx->info);
+    ca.min_tb = min_tb;
+    ca.traceback = (flags & FZ_TRACEBACK) ? 1 : 0;
+    ca.hits = hits;
+    ca.side_trace = as<int32_t>(ctx->side_trace);
+    ca.run_cap = as<int64_t>(ctx->run_cap);
+    ca.bin_count = dc->bin_count;
+    ca.max_ptr = &dc->max_ptr;
+    ca.cells_total = &dc->totals[3];
+    combine_kernel<<<blocks_for(n, 256), 256, 0, st>>>(ca);
+    HIP_OK(hipGetLastError());
+    // run slots of traced sides
+    rc = scan(ctx, as<int64_t>(ctx->run_cap), 1, nsides, as<int64_t>(ctx->run_off), 1, &dc->totals[0], st);
+    if (rc) return rc;
+    if ((rc = read_counters())) return rc;
+    const int64_t total_runs = hc.totals[0];
+    uint32_t base[2 * NBINS];
+    int64_t n_exec = 0, n_exec0 = 0;
+    for (int cls = 0; cls < 2; ++cls)
+        for (int b = NBINS - 1; b >= 0; --b) {
+            base[cls * NBINS + b] = (uint32_t)n_exec;
+            n_exec += hc.bin_count[cls * NBINS + b];
+            if (cls == 0) n_exec0 = n_exec;
+            S.bin_hist[b] += hc.bin_count[cls * NBINS + b];
+        }
+    S.n_executor = (uint64_t)n_exec;
+    ENSURE(ctx->runs, std::max<int64_t>(total_runs, 1) * sizeof(uint32_t));
+    if (n_exec > 0) {
+        HIP_OK(hipMemcpyAsync(dc->bin_base, base, sizeof base, hipMemcpyHostToDevice, st));
+        ENSURE(ctx->items, n_exec * sizeof(ExecItem));
+        bin_scatter_kernel<<<blocks_for(nsides, 256), 256, 0, st>>>(nsides, as<int32_t>(ctx->side_trace),
+                                                                    as<SideOut>(ctx->out), dc->bin_base,
+                                                                    dc->bin_fill, as<ExecItem>(ctx->items));
+        HIP_OK(hipGetLastError());
+        const int64_t stride = sizeof(ExecItem) / sizeof(int64_t);
+        ExecItem *it = as<ExecItem>(ctx->items);
+        rc = scan(ctx, reinterpret_cast<const int64_t *>(&it->ptr_bytes), stride, n_exec,
+                  reinterpret_cast<int64_t *>(&it->ptr_off), stride, &dc->totals[1], st);
+        if (rc) return rc;
+    }
+    eager_runs_kernel<<<blocks_for(nsides, 256), 256, 0, st>>>(nsides, as<int32_t>(ctx->side_trace),
+                                                               as<SideOut>(ctx->out), as<uint8_t>(ctx->eager),
+                                                               as<int64_t>(ctx->run_off), as<uint32_t>(ctx->runs),
+                                                               as<int64_t>(ctx->run_len));
+    HIP_OK(hipGetLastError());
+    tm.mark();
+
+    // ---- execute + walk, in batches
+    if (n_exec > 0) {
+        if ((rc = read_counters())) return rc;
+        const int64_t total_ptr = hc.totals[1], max_item = hc.max_ptr;
+        S.pointer_bytes = (uint64_t)total_ptr;
+        uint64_t cap = ctx->ptr_cap;
+        if (cap == 0) {
+            size_t fr = 0, tot = 0;
+            HIP_OK(hipMemGetInfo(&fr, &tot));
+            cap = std::min<uint64_t>((uint64_t)fr / 4, (uint64_t)32 << 30);
+        }
+        cap = std::max<uint64_t>(cap, (uint64_t)2 * (uint64_t)max_item + 4096);
+        const int64_t ws = std::min<int64_t>((int64_t)cap, total_ptr + 256);
+        const int64_t step = std::max<int64_t>(1, ws - max_item);
+        ENSURE(ctx->ptr_ws, ws);
+        const int64_t nb = (total_ptr + step - 1) / step;
+        ENSURE(ctx->batch_first, (nb + 1) * sizeof(int64_t));
+        fill_i64_kernel<<<blocks_for(nb + 1, 256), 256, 0, st>>>(as<int64_t>(ctx->batch_first), nb + 1, n_exec);
+        HIP_OK(hipGetLastError());
+        batch_assign_kernel<<<blocks_for(n_exec, 256), 256, 0, st>>>(as<ExecItem>(ctx->items), n_exec, step,
+                                                                     as<int64_t>(ctx->batch_first));
+        HIP_OK(hipGetLastError());
+        std::vector<int64_t> first((size_t)nb + 1);
+        HIP_OK(hipMemcpyAsync(first.data(), ctx->batch_first.p, nb * sizeof(int64_t), hipMemcpyDeviceToHost, st));
+        HIP_OK(hipStreamSynchronize(st));
+        first[(size_t)nb] = n_exec;
+        // batches that own no item start where the next one does
+        for (int64_t b = nb - 1; b >= 0; --b)
+            if (first[(size_t)b] > first[(size_t)b + 1]) first[(size_t)b] = first[(size_t)b + 1];
+        S.n_batches = (uint64_t)nb;
+        int qslot = 2;
+        for (int64_t b = 0; b < nb; ++b) {
+            const int64_t lo = first[(size_t)b], hi = first[(size_t)b + 1];
+            if (hi <= lo) continue;
+            const int64_t segs[2][2] = {{lo, std::min(hi, n_exec0)}, {std::max(lo, n_exec0), hi}};
+            for (int cls = 0; cls < 2; ++cls) {
+                const int64_t s0 = segs[cls][0], s1 = segs[cls][1];
+                if (s1 <= s0) continue;
+                rc = zero(ctx, &dc->queue[qslot], sizeof(uint32_t), st);
+                if (rc) return rc;
+                ExtendArgs xa = ea;
+                xa.exec = as<ExecItem>(ctx->items);
+                xa.exec_begin = s0;
+                xa.nlist = (int32_t)(s1 - s0);
+                xa.ptr_ws = as<uint8_t>(ctx->ptr_ws);
+                xa.ptr_base_off = b * step;
+                xa.queue = &dc->queue[qslot];
+                rc = cls == 0 ? launch_extend<C_STD, true>(ctx, xa, s1 - s0, st)
+                              : launch_extend<C_WIDE, true>(ctx, xa, s1 - s0, st);
+                if (rc) return rc;
+                WalkArgs wk;
+                wk.items = as<ExecItem>(ctx->items);
+                wk.begin = s0;
+                wk.end = s1;
+                wk.ptr_ws = as<uint8_t>(ctx->ptr_ws);
+                wk.ptr_base_off = b * step;
+                wk.C = cls == 0 ? C_STD : C_WIDE;
+                wk.out = as<SideOut>(ctx->out);
+                wk.run_off = as<int64_t>(ctx->run_off);
+                wk.runs = as<uint32_t>(ctx->runs);
+                wk.run_len = as<int64_t>(ctx->run_len);
+                walk_kernel<<<blocks_for(s1 - s0, 64), 64, 0, st>>>(wk);
+                HIP_OK(hipGetLastError());
+            }
+        }
+    }
+    tm.mark();
+
+    // ---- gather CIGARs
+    ENSURE(ctx->cig, n * sizeof(int64_t));
+    AssembleArgs aa;
+    aa.seeds = seeds;
+    aa.n = n;
+    aa.run_off = as<int64_t>(ctx->run_off);
+    aa.run_len = as<int64_t>(ctx->run_len);
+    aa.runs = as<uint32_t>(ctx->runs);
+    aa.hits = hits;
+    aa.cig_len = as<int64_t>(ctx->cig);
+    aa.cigar = nullptr;
+    aa.err = &dc->err;
+    assemble_kernel<false><<<blocks_for(n, 256), 256, 0, st>>>(aa);
+    HIP_OK(hipGetLastError());
+    rc = scan(ctx, as<int64_t>(ctx->cig), 1, n, as<int64_t>(ctx->cig), 1, &dc->totals[2], st);
+    if (rc) return rc;
+    if ((rc = read_counters())) return rc;
+    const int64_t total_words = hc.totals[2];
+    ENSURE(ctx->cigar, std::max<int64_t>(total_words, 1) * sizeof(uint32_t));
+    aa.cigar = as<uint32_t>(ctx->cigar);
+    assemble_kernel<true><<<blocks_for(n, 256), 256, 0, st>>>(aa);
+    HIP_OK(hipGetLastError());
+    tm.mark();
+    if ((rc = read_counters())) return rc;
+    if (hc.err & 2u) return fail(ctx, FZ_EDEVICE, "internal error: a traceback walk did not reach the origin");
+    if (cigar) *cigar = as<uint32_t>(ctx->cigar);
+    if (cigar_words) *cigar_words = (uint64_t)total_words;
+    ctx->last_words = (uint64_t)total_words;
+    if (stats) {
+        S.n_sides = (uint64_t)nsides;
+        S.cells = (uint64_t)hc.totals[3];
+        S.executor_cells = (uint64_t)hc.exec_cells;
+        S.ms_pack = tm.ms(0, 1);
+        S.ms_inspect = tm.ms(1, 2);
+        S.ms_bin = tm.ms(2, 3);
+        S.ms_exec = tm.ms(3, 4);
+        S.ms_gather = tm.ms(4, 5);
+        (void)hipEventElapsedTime(&S.ms_main, ctx->kev[0], ctx->kev[1]);
+        *stats = S;
+    }
+    return FZ_OK;
+}
+
+int fz_extend_batch(fz_ctx *ctx, const uint8_t *target, uint64_t target_len, const uint8_t *query, uint64_t query_len,
+                    const fz_seed *seeds, uint64_t n_seeds, const fz_scoring *scoring, int32_t ydrop,
+                    int64_t min_traceback_score, uint32_t flags, fz_hit *hits, const uint32_t **cigar,
+                    uint64_t *cigar_words, fz_stats *stats, void *stream)
+{
+    if (!ctx) return FZ_EINVAL;
+    ctx->err.clear();
+    ctx->last_words = 0;
+    int prev = 0;
+    if (hipGetDevice(&prev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ctx, FZ_EDEVICE, "hipGetDevice failed");
+    }
+    if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ctx, FZ_EDEVICE, "hipSetDevice(%d) failed", ctx->device);
+    }
+    const int rc = extend_impl(ctx, target, target_len, query, query_len, seeds, n_seeds, scoring, ydrop,
+                               min_traceback_score, flags, hits, cigar, cigar_words, stats, (hipStream_t)stream);
+    if (prev != ctx->device) (void)hipSetDevice(prev);
+    return rc;
+}
+
+int fz_copy_cigar(fz_ctx *ctx, uint32_t *dst, uint64_t words, void *stream)
+{
+    if (!ctx) return FZ_EINVAL;
+    if (words > ctx->last_words) return fail(ctx, FZ_EINVAL, "asked for %llu CIGAR words, last call made %llu",
+                                             (unsigned long long)words, (unsigned long long)ctx->last_words);
+    if (words == 0) return FZ_OK;
+    if (!dst) return fail(ctx, FZ_EINVAL, "dst is NULL");
+    hipStream_t st = (hipStream_t)stream;
+    HIP_OK(hipMemcpyAsync(dst, ctx->cigar.p, words * sizeof(uint32_t), hipMemcpyDeviceToDevice, st));
+    HIP_OK(hipStreamSynchronize(st));
+    return FZ_OK;
+}
+
+}  // extern "C"

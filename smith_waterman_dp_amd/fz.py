@@ -1,0 +1,188 @@
+"""Thin ctypes binding of libfz (include/fz.h), same names as the C ABI.
+
+Argument marshalling only: torch tensors supply device memory and the
+stream; every step of the computation runs in the HIP library.  If
+``libfz.so`` is missing, or no GPU is present, the calls raise -- there is no
+other implementation behind them.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfz.so")
+
+FZ_TRACEBACK, FZ_LOCAL, FZ_STATS = 1, 2, 4
+FZ_OK, FZ_EINVAL, FZ_ENOMEM, FZ_EDEVICE, FZ_EBAND = 0, -1, -2, -3, -4
+FZ_HIT_TRACED, FZ_HIT_EAGER_LEFT, FZ_HIT_EAGER_RIGHT = 1, 2, 4
+FZ_HIT_BELOW_MIN, FZ_HIT_EBAND, FZ_HIT_ESEED, FZ_HIT_ERANGE = 8, 16, 32, 64
+FZ_YDROP_INF = 2147483647
+
+HIT_FIELDS = ["score", "status", "t_begin", "t_end", "q_begin", "q_end", "cigar_off", "cigar_len",
+              "cells", "score_left", "score_right", "bin"]
+SEED_FIELDS = ["t_pos", "q_pos", "seed_len", "t_lo", "t_hi", "q_lo", "q_hi"]
+
+# every symbol include/fz.h declares
+EXPORTS = ["fz_create", "fz_destroy", "fz_last_error", "fz_set_pointer_workspace", "fz_extend_batch",
+           "fz_copy_cigar"]
+
+
+class fz_scoring(ctypes.Structure):
+    _fields_ = [("match", ctypes.c_int32), ("transition", ctypes.c_int32), ("transversion", ctypes.c_int32),
+                ("gap_open", ctypes.c_int32), ("gap_extend", ctypes.c_int32)]
+
+
+class fz_stats(ctypes.Structure):
+    _fields_ = [("cells", ctypes.c_uint64), ("executor_cells", ctypes.c_uint64),
+                ("pointer_bytes", ctypes.c_uint64), ("n_sides", ctypes.c_uint64), ("n_eager", ctypes.c_uint64),
+                ("n_executor", ctypes.c_uint64), ("n_overflow", ctypes.c_uint64),
+                ("bin_hist", ctypes.c_uint64 * 8), ("n_batches", ctypes.c_uint64),
+                ("ms_pack", ctypes.c_float), ("ms_inspect", ctypes.c_float), ("ms_bin", ctypes.c_float),
+                ("ms_exec", ctypes.c_float), ("ms_walk", ctypes.c_float), ("ms_gather", ctypes.c_float),
+                ("ms_main", ctypes.c_float)]
+
+    def as_dict(self):
+        d = {f: getattr(self, f) for f, _ in self._fields_}
+        d["bin_hist"] = list(self.bin_hist)
+        return d
+
+
+class FzError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("libfz error %d: %s" % (code, msg))
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libfz.so and declare its signatures (no device call)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libfz.so is not built (%s); run `python -m smith_waterman_dp_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    P, u64, i32, i64 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int64
+    lib.fz_create.restype = ctypes.c_int
+    lib.fz_create.argtypes = [ctypes.POINTER(P), ctypes.c_int]
+    lib.fz_destroy.restype = None
+    lib.fz_destroy.argtypes = [P]
+    lib.fz_last_error.restype = ctypes.c_char_p
+    lib.fz_last_error.argtypes = [P]
+    lib.fz_set_pointer_workspace.restype = ctypes.c_int
+    lib.fz_set_pointer_workspace.argtypes = [P, u64]
+    lib.fz_extend_batch.restype = ctypes.c_int
+    lib.fz_extend_batch.argtypes = [P, P, u64, P, u64, P, u64, ctypes.POINTER(fz_scoring), i32, i64,
+                                    ctypes.c_uint32, P, ctypes.POINTER(P), ctypes.POINTER(u64),
+                                    ctypes.POINTER(fz_stats), P]
+    lib.fz_copy_cigar.restype = ctypes.c_int
+    lib.fz_copy_cigar.argtypes = [P, P, u64, P]
+    _lib = lib
+    return lib
+
+
+def _check(ctx, rc):
+    if rc != FZ_OK:
+        msg = load_library().fz_last_error(ctx).decode(errors="replace") if ctx else ""
+        raise FzError(rc, msg)
+
+
+def fz_create(device=0):
+    lib = load_library()
+    h = ctypes.c_void_p()
+    rc = lib.fz_create(ctypes.byref(h), int(device))
+    if rc != FZ_OK:
+        raise FzError(rc, "fz_create(%d) failed" % device)
+    return h
+
+
+def fz_destroy(ctx):
+    load_library().fz_destroy(ctx)
+
+
+def fz_last_error(ctx):
+    return load_library().fz_last_error(ctx).decode(errors="replace")
+
+
+def fz_set_pointer_workspace(ctx, nbytes):
+    _check(ctx, load_library().fz_set_pointer_workspace(ctx, int(nbytes)))
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def fz_extend_batch(ctx, target, query, seeds, scoring, ydrop, min_traceback_score=-(1 << 62),
+                    flags=FZ_TRACEBACK, stream=None, want_stats=False):
+    """Run one batch.
+
+    target, query: uint8 CUDA tensors of ASCII bases.  seeds: int64 CUDA
+    tensor (n, 7) in SEED_FIELDS order.  scoring: dict with match,
+    transition, transversion, gap_open, gap_extend.
+    Returns (hits, cigar, stats): hits an int64 (n, 12) CUDA tensor in
+    HIT_FIELDS order, cigar an int32 CUDA tensor of BAM-style words
+    (len << 4 | op), stats a dict or None.
+    """
+    import torch
+    lib = load_library()
+    for name, t, dt in (("target", target, torch.uint8), ("query", query, torch.uint8), ("seeds", seeds, torch.int64)):
+        if not t.is_cuda or t.dtype != dt or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous %s CUDA tensor" % (name, dt))
+    if seeds.dim() != 2 or seeds.shape[1] != 7:
+        raise ValueError("seeds must have shape (n, 7)")
+    n = seeds.shape[0]
+    hits = torch.empty((n, len(HIT_FIELDS)), dtype=torch.int64, device=seeds.device)
+    sc = fz_scoring(int(scoring["match"]), int(scoring["transition"]), int(scoring["transversion"]),
+                    int(scoring["gap_open"]), int(scoring["gap_extend"]))
+    cig_ptr = ctypes.c_void_p()
+    words = ctypes.c_uint64(0)
+    st = fz_stats()
+    if want_stats:
+        flags |= FZ_STATS
+    strm = _stream_handle(stream)
+    rc = lib.fz_extend_batch(ctx, target.data_ptr(), target.numel(), query.data_ptr(), query.numel(),
+                             seeds.data_ptr(), n, ctypes.byref(sc), int(min(int(ydrop), FZ_YDROP_INF)),
+                             int(min_traceback_score), int(flags), hits.data_ptr() if n else None,
+                             ctypes.byref(cig_ptr), ctypes.byref(words),
+                             ctypes.byref(st), strm)
+    _check(ctx, rc)
+    cigar = torch.empty(max(words.value, 0), dtype=torch.int32, device=seeds.device)
+    if words.value:
+        _check(ctx, lib.fz_copy_cigar(ctx, cigar.data_ptr(), words.value, strm))
+    return hits, cigar, (st.as_dict() if want_stats else None)
+
+
+def fz_copy_cigar(ctx, dst, words, stream=None):
+    _check(ctx, load_library().fz_copy_cigar(ctx, dst.data_ptr(), int(words), _stream_handle(stream)))
+
+
+class Context:
+    """Owns one fz_ctx; `extend` and `local` wrap fz_extend_batch."""
+
+    def __init__(self, device=0):
+        self.device = device
+        self.h = fz_create(device)
+
+    def close(self):
+        if self.h:
+            fz_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def extend(self, target, query, seeds, scoring, ydrop, min_traceback_score=-(1 << 62), traceback=True,
+               stream=None, want_stats=False):
+        flags = FZ_TRACEBACK if traceback else 0
+        return fz_extend_batch(self.h, target, query, seeds, scoring, ydrop, min_traceback_score, flags,
+                               stream, want_stats)
+
+    def local(self, target, query, seeds, scoring, stream=None, want_stats=False):
+        return fz_extend_batch(self.h, target, query, seeds, scoring, 0, 0, FZ_LOCAL, stream, want_stats)

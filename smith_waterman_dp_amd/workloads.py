@@ -103,6 +103,10 @@ def shared_kmers(t_codes, q_codes, k=SEED_LEN, t_mask=None, q_mask=None):
         kq = kq[qpos]
     order = np.argsort(kt, kind="stable")
     st = kt[order]
+    # sorted queries make the merge walk memory in order
+    qorder = np.argsort(kq, kind="stable")
+    kq = kq[qorder]
+    qpos = qpos[qorder]
     lo = np.searchsorted(st, kq, "left")
     hi = np.searchsorted(st, kq, "right")
     cnt = hi - lo
@@ -110,7 +114,8 @@ def shared_kmers(t_codes, q_codes, k=SEED_LEN, t_mask=None, q_mask=None):
     qi = np.repeat(qpos, cnt)
     within = np.arange(tot, dtype=np.int64) - np.repeat(np.cumsum(cnt) - cnt, cnt)
     ti = tpos[order[np.repeat(lo, cnt) + within]]
-    return ti, qi
+    o = np.lexsort((ti, qi))
+    return ti[o], qi[o]
 
 
 def _windows(t_pos, q_pos, tlen, qlen, flank=WINDOW_FLANK, L=SEED_LEN):
@@ -192,21 +197,24 @@ def _homology_with_blocks(rng, src_len, unrelated_frac, run_min, run_max):
     return runs, block
 
 
-def skewed(target_len=10_000_000, n_seeds=1_000_000, family_frac=0.97, n_families=200,
-           copies=32, sub_rate=0.15, indel_rate=0.015, p_geom=0.4, unrelated_frac=0.10,
-           flank=WINDOW_FLANK, min_tb=3000, seed=0):
+def skewed(target_len=10_000_000, n_seeds=1_000_000, short_frac=0.78, long_frac=0.19,
+           n_short=150, n_long=50, copies=32, sub_rate=0.15, indel_rate=0.015, p_geom=0.4,
+           unrelated_frac=0.10, flank=WINDOW_FLANK, min_tb=3000, seed=0):
     """Skewed seed batch (one million seeds by default).
 
     Target: uniform random.  Query: a mutated copy of the target (15%
     substitutions 2:1, 1.5% indels of Geom(0.4) length) in which about 10% is
     replaced by unrelated blocks placed between homologous runs of
-    log-uniform length 128 bp .. 64 kb.  Repeat families: `n_families`
-    random strings of U{19..128} bases, each planted as `copies` exact copies
-    at random non-overlapping places in target and in query (after the
-    mutation).  Seeds are shared 19-mers: `family_frac` of them drawn
-    uniformly from family hits (their alignments stop within 128 bp), the
-    rest from the other shared 19-mers (homologous hits that run long).
-    Windows reach `flank` bases past each side of the seed."""
+    log-uniform length 128 bp .. 64 kb.  Repeat families: random strings
+    planted as `copies` exact copies at random non-overlapping places in
+    target and in query (after the mutation); `n_short` families of
+    U{19..34} bases and `n_long` of U{35..100}.  Seeds are shared 19-mers
+    drawn uniformly from the hits of each group: `short_frac` from short
+    families (both extensions end within 16 bases, the eager-traceback
+    class of FastZ Table 2), `long_frac` from long families (alignments of
+    at most about 128 bp), the rest from the other shared 19-mers
+    (homologous hits that run to tens of kb).  Windows reach `flank` bases
+    past each side of the seed."""
     rng = np.random.default_rng(seed)
     T = random_codes(rng, target_len)
     # query: homologous runs separated by unrelated blocks
@@ -222,14 +230,16 @@ def skewed(target_len=10_000_000, n_seeds=1_000_000, family_frac=0.97, n_familie
         parts.append(random_codes(rng, block))
     Q = np.concatenate(parts)
     # repeat families, planted in non-overlapping slots
-    fam_len = rng.integers(SEED_LEN, 129, size=n_families)
+    n_families = n_short + n_long
+    fam_len = np.concatenate([rng.integers(SEED_LEN, 35, size=n_short),
+                              rng.integers(35, 101, size=n_long)])
     fams = [random_codes(rng, L) for L in fam_len]
-    slot = 160
+    slot = 128
 
     def plant(seq):
         nslots = seq.size // slot
         picks = rng.choice(nslots, size=n_families * copies, replace=False)
-        starts = picks.reshape(n_families, copies) * slot + rng.integers(0, slot - 128, size=(n_families, copies))
+        starts = picks.reshape(n_families, copies) * slot + rng.integers(0, slot - 100, size=(n_families, copies))
         for f in range(n_families):
             for c in range(copies):
                 s = starts[f, c]
@@ -238,15 +248,21 @@ def skewed(target_len=10_000_000, n_seeds=1_000_000, family_frac=0.97, n_familie
 
     t_starts = plant(T)
     q_starts = plant(Q)
+
     # family hits: family f, offset o, target copy a, query copy b
-    n_fam = int(round(n_seeds * family_frac))
-    w = (fam_len - SEED_LEN + 1).astype(np.float64)
-    f = rng.choice(n_families, size=n_fam, p=w / w.sum())
-    o = (rng.random(n_fam) * (fam_len[f] - SEED_LEN + 1)).astype(np.int64)
-    a = rng.integers(0, copies, size=n_fam)
-    b = rng.integers(0, copies, size=n_fam)
-    ft = t_starts[f, a] + o
-    fq = q_starts[f, b] + o
+    def family_hits(fam_ids, count):
+        w = (fam_len[fam_ids] - SEED_LEN + 1).astype(np.float64)
+        f = fam_ids[rng.choice(fam_ids.size, size=count, p=w / w.sum())]
+        o = (rng.random(count) * (fam_len[f] - SEED_LEN + 1)).astype(np.int64)
+        a = rng.integers(0, copies, size=count)
+        b = rng.integers(0, copies, size=count)
+        return t_starts[f, a] + o, q_starts[f, b] + o
+
+    n_sh = int(round(n_seeds * short_frac))
+    n_lg = int(round(n_seeds * long_frac))
+    st_, sq_ = family_hits(np.arange(n_short), n_sh)
+    lt_, lq_ = family_hits(np.arange(n_short, n_families), n_lg)
+
     # other hits: shared 19-mers whose positions touch no family copy
     def fam_mask(seq_len, starts):
         cover = np.zeros(seq_len + 1, dtype=np.int64)
@@ -257,16 +273,17 @@ def skewed(target_len=10_000_000, n_seeds=1_000_000, family_frac=0.97, n_familie
         return np.cumsum(cover[:seq_len]) == 0
 
     ht, hq = shared_kmers(T, Q, t_mask=fam_mask(T.size, t_starts), q_mask=fam_mask(Q.size, q_starts))
-    n_hom = n_seeds - n_fam
+    n_hom = n_seeds - n_sh - n_lg
     pick = rng.choice(ht.size, size=min(n_hom, ht.size), replace=False)
-    t_pos = np.concatenate([ft, ht[pick]])
-    q_pos = np.concatenate([fq, hq[pick]])
+    t_pos = np.concatenate([st_, lt_, ht[pick]])
+    q_pos = np.concatenate([sq_, lq_, hq[pick]])
     perm = rng.permutation(t_pos.size)
     t_pos, q_pos = t_pos[perm], q_pos[perm]
     t_lo, t_hi, q_lo, q_hi = _windows(t_pos, q_pos, T.size, Q.size, flank)
     seeds = _pack(t_pos, q_pos, SEED_LEN, t_lo, t_hi, q_lo, q_hi)
-    return _workload("skewed", T, Q, seeds, min_tb=min_tb, n_family_seeds=n_fam,
-                     n_other_seeds=int(pick.size), n_other_hits=int(ht.size), query_len=int(Q.size))
+    return _workload("skewed", T, Q, seeds, min_tb=min_tb, n_short_family_seeds=n_sh,
+                     n_long_family_seeds=n_lg, n_other_seeds=int(pick.size),
+                     n_other_hits=int(ht.size), query_len=int(Q.size))
 
 
 def executor_heavy(n_pairs=100_000, len_min=1000, len_max=20000, unrelated=2048, seed=0):

@@ -1,0 +1,52 @@
+"""Host-only checks of the C-ABI boundary: the library loads, exports every
+symbol include/fz.h declares, and rejects bad calls without touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from smith_waterman_dp_amd import fz
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "fz.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fz_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(fz.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fz.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_struct_sizes_match_header():
+    # fz_seed is 7 int64, fz_hit is 12 int64 (the binding's tensor views rely on it)
+    assert len(fz.SEED_FIELDS) == 7
+    assert len(fz.HIT_FIELDS) == 12
+    assert ctypes.sizeof(fz.fz_scoring) == 20
+
+
+def test_null_context_is_rejected():
+    lib = fz.load_library()
+    sc = fz.fz_scoring(91, -31, -123, 400, 30)
+    rc = lib.fz_extend_batch(None, None, 0, None, 0, None, 0, ctypes.byref(sc), 9400, 0, 0, None,
+                             None, None, None, None)
+    assert rc == fz.FZ_EINVAL
+    assert lib.fz_set_pointer_workspace(None, 0) == fz.FZ_EINVAL
+    assert lib.fz_copy_cigar(None, None, 0, None) == fz.FZ_EINVAL
+    lib.fz_destroy(None)
+
+
+def test_create_bad_device_fails_cleanly():
+    lib = fz.load_library()
+    h = ctypes.c_void_p()
+    assert lib.fz_create(ctypes.byref(h), 10_000) != fz.FZ_OK
+    assert not h.value
