@@ -357,11 +357,13 @@ __global__ void walk_kernel(WalkArgs a)
         const RowHdr h = hdr[d];
         const uint32_t row_end = d < it.dstar ? hdr[d + 1].off : total_rows;
         const int p = i - h.ibase;
-        if (p < 0 || h.off + (uint32_t)(p / C) >= row_end) {
+        const int nword = (C + 7) / 8;
+        const uint32_t wi = h.off + (uint32_t)((p / C) * nword + (p % C) / 8);
+        if (p < 0 || wi >= row_end) {
             bad = true;
             return 0u;
         }
-        return (rows[h.off + p / C] >> (4 * (p % C))) & 0xFu;
+        return (rows[wi] >> (4 * ((p % C) % 8))) & 0xFu;
     };
     int64_t n = 0;
     uint32_t cop = 0, clen = 0;

@@ -44,7 +44,6 @@ struct ExtendArgs {
     int64_t ptr_base_off;       // list offset that maps to ptr_ws[0] for this batch
     SideOut *out;
     uint8_t *eager_ops;         // EAGER_OPS bytes per side (op codes 0 M, 1 I, 2 D; end-first)
-    uint32_t *queue;            // work counter
     int32_t *overflow_list;     // sides that outgrew the window
     uint32_t *overflow_count;
     int64_t *exec_cells;        // executor: cells recomputed (stats)
@@ -60,6 +59,7 @@ struct SideDP {
     static constexpr int EL0 = 32 - (8 + C - 1) / C;    // lanes holding the eager block
     static constexpr int EL1 = 32 + 8 / C;
     static constexpr int NEL = EL1 - EL0 + 1;
+    static constexpr int NWORD = (C + 7) / 8;           // pointer words per lane per row (8 nibbles each)
 
     // registers
     int SA[C], SB[C], R[C], Dn[C];
@@ -91,11 +91,11 @@ struct SideDP {
     }
 
     // Evaluate diagonal d.  DELTA = o_d - o_(d-1); S of d-2 is in SN (and
-    // is replaced by S of d), S of d-1 is in SP.  Returns the packed
-    // pointer word (PTR) of this lane's C cells.
+    // is replaced by S of d).  With PTR, word[] receives this lane's C
+    // pointer nibbles, eight per word.
     template <int DELTA, bool PTR>
-    __device__ __forceinline__ uint32_t cells_of(int (&SN)[C], int od, int d, int T, bool masked, int rlo,
-                                                 int rhi, uint64_t (&live)[C], int &dmax)
+    __device__ __forceinline__ void cells_of(int (&SN)[C], int od, int d, int T, bool masked, int rlo, int rhi,
+                                             uint64_t (&live)[C], int &dmax, uint32_t (&word)[NWORD])
     {
         // bases: a_i for i = i0 + c, b_j for j = d - i0 - c
         const int i0 = lane * C + od;
@@ -112,7 +112,8 @@ struct SideDP {
         if (DELTA == 1) cross = from_next_lane(R[0], NEG);       // left of slot C-1 is next lane's slot 0
         else cross = from_prev_lane(Dn[C - 1], NEG);            // up of slot 0 is previous lane's slot C-1
 
-        uint32_t word = 0;
+#pragma unroll
+        for (int k = 0; k < NWORD; ++k) word[k] = 0;
         dmax = NEG;
         int Rn[C], Dnn[C];
 #pragma unroll
@@ -135,7 +136,7 @@ struct SideDP {
             if (PTR) {
                 const uint32_t src = (S == H) ? 0u : (S == Iv ? 1u : 2u);
                 const uint32_t nib = src | (Ie > U ? 4u : 0u) | (De > U ? 8u : 0u);
-                word |= nib << (4 * c);
+                word[c / 8] |= nib << (4 * (c % 8));
             }
             SN[c] = Sk;
             dmax = max(dmax, Sk);
@@ -145,7 +146,6 @@ struct SideDP {
             R[c] = Rn[c];
             Dn[c] = Dnn[c];
         }
-        return word;
     }
 
     __device__ __forceinline__ void slide(int s)
@@ -218,9 +218,9 @@ struct SideDP {
 
         uint64_t live[C];
         int dmax;
-        uint32_t word;
-        if (DELTA == 1) word = cells_of<DELTA, PTR>(SA, od, d, T, masked, rlo, rhi, live, dmax);   // even d
-        else word = cells_of<DELTA, PTR>(SB, od, d, T, masked, rlo, rhi, live, dmax);             // odd d
+        uint32_t word[NWORD];
+        if (DELTA == 1) cells_of<DELTA, PTR>(SA, od, d, T, masked, rlo, rhi, live, dmax, word);   // even d
+        else cells_of<DELTA, PTR>(SB, od, d, T, masked, rlo, rhi, live, dmax, word);             // odd d
 
         // live hull of d
         uint64_t any = 0;
@@ -241,7 +241,7 @@ struct SideDP {
         }
         cells += rhi - rlo + 1;
         const int nl = lhi - llo + 1;
-        cum_bytes += 8 + 4 * (int64_t)nl;
+        cum_bytes += 8 + 4 * (int64_t)nl * NWORD;
 
         if (ballot(dmax > best)) {
             const int nb = wave_max(dmax);
@@ -260,7 +260,7 @@ struct SideDP {
         }
 
         if (EXEC) {
-            if (rowoff + (uint32_t)nl > rowcap) {
+            if (rowoff + (uint32_t)(nl * NWORD) > rowcap) {
                 // the recompute disagrees with the inspector's sizing
                 overflow = true;
                 return false;
@@ -271,10 +271,16 @@ struct SideDP {
                 h.ibase = llo * C + od;
                 hdr[d] = h;
             }
-            if (lane >= llo && lane <= lhi) rows[rowoff + (lane - llo)] = word;
-            rowoff += (uint32_t)nl;
+            if (lane >= llo && lane <= lhi) {
+#pragma unroll
+                for (int k = 0; k < NWORD; ++k) rows[rowoff + (lane - llo) * NWORD + k] = word[k];
+            }
+            rowoff += (uint32_t)(nl * NWORD);
         } else if (PTR) {
-            if (lane >= EL0 && lane <= EL1) eager_lds[d * NEL + (lane - EL0)] = word;
+            if (lane >= EL0 && lane <= EL1) {
+#pragma unroll
+                for (int k = 0; k < NWORD; ++k) eager_lds[(d * NEL + (lane - EL0)) * NWORD + k] = word[k];
+            }
         }
 
         lo2 = lo1; hi2 = hi1;
@@ -297,7 +303,7 @@ struct SideDP {
         lo1 = P0; hi1 = P0; lo2 = 1; hi2 = 0;
         best = 0; bi = 0; bj = 0; dend = 0;
         cells = 1;
-        cum_bytes = 8 + 4;
+        cum_bytes = 8 + 4 * NWORD;
         ptr_at_best = cum_bytes;
         overflow = false;
         rowoff = 0;
@@ -310,11 +316,17 @@ struct SideDP {
                 h.ibase = 0;         // lane 32 slot 0 is i = 0
                 hdr[0] = h;
             }
-            if (lane == P0 / C) rows[0] = 0u;   // (0,0): source 0, gaps opened
-            rowoff = 1;
+            if (lane == P0 / C) {
+#pragma unroll
+                for (int k = 0; k < NWORD; ++k) rows[k] = 0u;   // (0,0): source 0, gaps opened
+            }
+            rowoff = NWORD;
             rowcap = (uint32_t)((ptr_bytes - 8 * ((int64_t)dstop + 1)) / 4);
         } else {
-            if (lane >= EL0 && lane <= EL1) eager_lds[lane - EL0] = 0u;
+            if (lane >= EL0 && lane <= EL1) {
+#pragma unroll
+                for (int k = 0; k < NWORD; ++k) eager_lds[(lane - EL0) * NWORD + k] = 0u;
+            }
         }
         int d = 1;
         if (!EXEC) {
@@ -332,7 +344,9 @@ struct SideDP {
         }
     }
 
-    // Walk the eager block from (bi, bj) (lane 0 only).  Ops end-first.
+    // Walk the eager block from (bi, bj).  The whole wave walks in step (the
+    // nibble read from LDS is broadcast to a scalar), so the walk is plain
+    // uniform control flow; lane 0 stores the ops, end-first.
     __device__ int eager_walk(const uint32_t *eager_lds, uint8_t *ops) const
     {
         int i = bi, j = bj, st = 0, n = 0;
@@ -341,19 +355,29 @@ struct SideDP {
             const int od0 = (dd - W) >> 1;     // no slide happens before diagonal 33
             const int p = ii - od0;
             const int l = p / C, c = p % C;
-            return (eager_lds[dd * NEL + (l - EL0)] >> (4 * c)) & 0xFu;
+            const uint32_t wd = (uint32_t)uniform((int)eager_lds[(dd * NEL + (l - EL0)) * NWORD + c / 8]);
+            return (wd >> (4 * (c % 8))) & 0xFu;
         };
-        while (!(st == 0 && i == 0 && j == 0) && n < EAGER_OPS && i >= 0 && j >= 0) {
+        for (int guard = 0; guard < 2 * EAGER_OPS + 2; ++guard) {
+            if ((st == 0 && i == 0 && j == 0) || n >= EAGER_OPS || i < 0 || j < 0) break;
             if (st == 0) {
                 const uint32_t src = nib(i, j) & 3u;
-                if (src == 0) { ops[n++] = 0; --i; --j; }
-                else st = (int)src;
+                if (src == 0) {
+                    if (lane == 0) ops[n] = 0;
+                    ++n;
+                    --i;
+                    --j;
+                } else {
+                    st = (int)src;
+                }
             } else if (st == 1) {
-                ops[n++] = 1;
+                if (lane == 0) ops[n] = 1;
+                ++n;
                 if (--j < 0) break;
                 st = (nib(i, j) & 4u) ? 1 : 0;
             } else {
-                ops[n++] = 2;
+                if (lane == 0) ops[n] = 2;
+                ++n;
                 if (--i < 0) break;
                 st = (nib(i, j) & 8u) ? 2 : 0;
             }
@@ -362,67 +386,61 @@ struct SideDP {
     }
 };
 
+// One wave per side; the grid covers the work list (the hardware dispatcher
+// hands waves to CUs as others retire, which balances sides of very
+// different lengths).
 template <int C, bool EXEC, bool SMALL, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void extend_kernel(ExtendArgs a)
 {
     using DP = SideDP<C, EXEC, SMALL>;
-    __shared__ uint32_t eager_lds_all[WAVES][EAGER_ROWS * DP::NEL];
-    uint32_t *eager_lds = eager_lds_all[threadIdx.x / 64];
+    __shared__ uint32_t eager_lds_all[WAVES][EAGER_ROWS * DP::NEL * DP::NWORD];
+    const int wv = uniform((int)(threadIdx.x / 64));
+    uint32_t *eager_lds = eager_lds_all[wv];
     const int lane = lane_id();
-    for (;;) {
-        int idx = 0;
-        if (lane == 0) idx = (int)atomicAdd(a.queue, 1u);
-        idx = uniform(idx);
-        int64_t item;
-        if (EXEC) {
-            item = a.exec_begin + idx;
-            if (idx >= a.nlist) break;
-        } else {
-            if (idx >= a.nlist) break;
-            item = idx;
+    const int idx = (int)blockIdx.x * WAVES + wv;
+    if (idx >= a.nlist) return;
+    const int64_t item = EXEC ? a.exec_begin + idx : (int64_t)idx;
+    const int sid = EXEC ? a.exec[item].side : (a.list ? a.list[item] : (int)item);
+    const SideTask task = a.tasks[sid];
+    SideOut *o = &a.out[sid];
+    if (task.m < 0) {
+        if (!EXEC && lane == 0) {
+            SideOut r = {};
+            r.flags = SO_SKIPPED;
+            *o = r;
         }
-        const int sid = EXEC ? a.exec[item].side : (a.list ? a.list[item] : (int)item);
-        const SideTask task = a.tasks[sid];
-        SideOut *o = &a.out[sid];
-        if (task.m < 0) {
-            if (!EXEC && lane == 0) {
-                SideOut r = {};
-                r.flags = SO_SKIPPED;
-                *o = r;
-            }
-            continue;
+        return;
+    }
+    DP dp(task, a.sc);
+    if (EXEC) {
+        const ExecItem it = a.exec[item];
+        dp.run(it.dstar, nullptr, a.ptr_ws + (it.ptr_off - a.ptr_base_off), it.ptr_bytes);
+        if (lane == 0) {
+            atomicAdd((unsigned long long *)a.exec_cells, (unsigned long long)dp.cells);
+            if (dp.overflow || dp.best != o->score || dp.bi != o->ie) atomicOr(&o->flags, SO_EXEC_MISMATCH);
         }
-        DP dp(task, a.sc);
-        if (EXEC) {
-            const ExecItem it = a.exec[item];
-            dp.run(it.dstar, nullptr, a.ptr_ws + (it.ptr_off - a.ptr_base_off), it.ptr_bytes);
-            if (lane == 0) {
-                atomicAdd((unsigned long long *)a.exec_cells, (unsigned long long)dp.cells);
-                if (dp.overflow || dp.best != o->score || dp.bi != o->ie) atomicOr(&o->flags, SO_EXEC_MISMATCH);
-            }
-        } else {
-            dp.run(0x7fffffff, eager_lds, nullptr);
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            SideOut r;
-            r.score = dp.best;
-            r.ie = dp.bi;
-            r.je = dp.bj;
-            r.dend = dp.dend;
-            r.cells = dp.cells;
-            r.ptr_bytes = dp.ptr_at_best;
-            r.flags = (dp.overflow ? SO_OVERFLOW : 0) | a.result_flags;
-            r.eager_len = 0;
-            if (!dp.overflow && dp.bi <= EAGER_EDGE && dp.bj <= EAGER_EDGE) {
-                r.flags |= SO_EAGER;
-                if (lane == 0) r.eager_len = dp.eager_walk(eager_lds, a.eager_ops + (int64_t)sid * EAGER_OPS);
-            }
-            if (lane == 0) {
-                *o = r;
-                if (dp.overflow) {
-                    const uint32_t k = atomicAdd(a.overflow_count, 1u);
-                    a.overflow_list[k] = sid;
-                }
-            }
+        return;
+    }
+    dp.run(0x7fffffff, eager_lds, nullptr);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    SideOut r;
+    r.score = dp.best;
+    r.ie = dp.bi;
+    r.je = dp.bj;
+    r.dend = dp.dend;
+    r.cells = dp.cells;
+    r.ptr_bytes = dp.ptr_at_best;
+    r.flags = (dp.overflow ? SO_OVERFLOW : 0) | a.result_flags;
+    r.eager_len = 0;
+    if (!dp.overflow && dp.bi <= EAGER_EDGE && dp.bj <= EAGER_EDGE) {
+        r.flags |= SO_EAGER;
+        r.eager_len = dp.eager_walk(eager_lds, a.eager_ops + (int64_t)sid * EAGER_OPS);
+    }
+    if (lane == 0) {
+        *o = r;
+        if (dp.overflow) {
+            const uint32_t k = atomicAdd(a.overflow_count, 1u);
+            a.overflow_list[k] = sid;
         }
     }
 }

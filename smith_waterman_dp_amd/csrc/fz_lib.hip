@@ -3,10 +3,11 @@
 // Phases of one fz_extend_batch call (FastZ, SC'21, section 3 and Fig. 8):
 //   pack      ASCII -> codes, forward and reversed copies, with validation
 //   setup     seeds -> two side tasks each, seed-column scores
-//   inspect   score-only y-drop extension of every side (one wave per side,
-//             persistent waves pulling sides from an atomic queue, which
-//             takes the place of the paper's 32 CUDA streams, section 3.4);
-//             sides whose best cell is in the 16 x 16 corner are traced here
+//   inspect   score-only y-drop extension of every side, one wave per side;
+//             the hardware dispatcher starts a new wave wherever one retires,
+//             which takes the place of the paper's 32 CUDA streams against
+//             load imbalance (section 3.4); sides whose best cell is in the
+//             16 x 16 corner are traced here
 //   widen     sides whose band outgrew the window are redone with a wider one
 //   bin       per seed totals; executor sides counted and scattered by length
 //             bin, longest bins first (section 3.3)
@@ -41,7 +42,6 @@ struct DevBuf {
 // Scalars the kernels update, one allocation.
 struct Counters {
     uint32_t err;               // bit 0: non-ACGT byte; bit 1: broken traceback
-    uint32_t queue[4];
     uint32_t overflow_count[2];
     uint32_t bin_count[2 * NBINS];
     uint32_t bin_base[2 * NBINS];
@@ -180,8 +180,7 @@ template <int C, bool EXEC>
 int launch_extend(fz_ctx *ctx, const ExtendArgs &a, int64_t nwork, hipStream_t st)
 {
     if (nwork <= 0) return FZ_OK;
-    const int64_t max_blocks = (int64_t)ctx->n_cu * 8;
-    const unsigned blocks = (unsigned)std::min<int64_t>((nwork + WAVES - 1) / WAVES, max_blocks);
+    const unsigned blocks = (unsigned)((nwork + WAVES - 1) / WAVES);
     if (a.sc.small) extend_kernel<C, EXEC, true, WAVES><<<blocks, 64 * WAVES, 0, st>>>(a);
     else extend_kernel<C, EXEC, false, WAVES><<<blocks, 64 * WAVES, 0, st>>>(a);
     HIP_OK(hipGetLastError());
@@ -414,7 +413,6 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     ea.nlist = (int32_t)nsides;
     ea.out = as<SideOut>(ctx->out);
     ea.eager_ops = as<uint8_t>(ctx->eager);
-    ea.queue = &dc->queue[0];
     ea.overflow_list = as<int32_t>(ctx->ovl0);
     ea.overflow_count = &dc->overflow_count[0];
     ea.exec_cells = &dc->exec_cells;
@@ -431,7 +429,6 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         ExtendArgs wa = ea;
         wa.list = as<int32_t>(ctx->ovl0);
         wa.nlist = (int32_t)hc.overflow_count[0];
-        wa.queue = &dc->queue[1];
         wa.overflow_list = as<int32_t>(ctx->ovl1);
         wa.overflow_count = &dc->overflow_count[1];
         wa.result_flags = SO_WIDE_FLAG;
@@ -526,7 +523,6 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         for (int64_t b = nb - 1; b >= 0; --b)
             if (first[(size_t)b] > first[(size_t)b + 1]) first[(size_t)b] = first[(size_t)b + 1];
         S.n_batches = (uint64_t)nb;
-        int qslot = 2;
         for (int64_t b = 0; b < nb; ++b) {
             const int64_t lo = first[(size_t)b], hi = first[(size_t)b + 1];
             if (hi <= lo) continue;
@@ -534,15 +530,12 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
             for (int cls = 0; cls < 2; ++cls) {
                 const int64_t s0 = segs[cls][0], s1 = segs[cls][1];
                 if (s1 <= s0) continue;
-                rc = zero(ctx, &dc->queue[qslot], sizeof(uint32_t), st);
-                if (rc) return rc;
                 ExtendArgs xa = ea;
                 xa.exec = as<ExecItem>(ctx->items);
                 xa.exec_begin = s0;
                 xa.nlist = (int32_t)(s1 - s0);
                 xa.ptr_ws = as<uint8_t>(ctx->ptr_ws);
                 xa.ptr_base_off = b * step;
-                xa.queue = &dc->queue[qslot];
                 rc = cls == 0 ? launch_extend<C_STD, true>(ctx, xa, s1 - s0, st)
                               : launch_extend<C_WIDE, true>(ctx, xa, s1 - s0, st);
                 if (rc) return rc;
