@@ -9,9 +9,8 @@ roofline of the dominant kernel (integer VALU bound), and the CPU oracle
 timed on a bounded sample of the same batch on this host's cores.
 
 Workloads (seeded, synthetic; see smith_waterman_dp_amd/workloads.py):
-  skewed          one million 19-mer seeds on a 10 Mbp pair
-  local           4,096 full-matrix local alignments of 2048 x 2048 (default
-                  while the extension path is off the GPU)
+  skewed          one million 19-mer seeds on a 10 Mbp pair (default)
+  local           4,096 full-matrix local alignments of 2048 x 2048
   tiny, executor_heavy, chromosome
 """
 import argparse
@@ -44,8 +43,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=1)
-    # default: local until the extension path is back on the GPU
-    ap.add_argument("--workload", default="local",
+    ap.add_argument("--workload", default="skewed",
                     choices=["skewed", "local", "tiny", "executor_heavy", "chromosome"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     ap.add_argument("--no-cpu", action="store_true")
