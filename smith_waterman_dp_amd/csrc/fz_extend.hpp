@@ -93,8 +93,8 @@ struct SideDP {
     // Evaluate diagonal d.  DELTA = o_d - o_(d-1); S of d-2 is in SN (and
     // is replaced by S of d).  With PTR, word[] receives this lane's C
     // pointer nibbles, eight per word.
-    template <int DELTA, bool PTR>
-    __device__ __forceinline__ void cells_of(int (&SN)[C], int od, int d, int T, bool masked, int rlo, int rhi,
+    template <int DELTA, bool PTR, bool MASKED>
+    __device__ __forceinline__ void cells_of(int (&SN)[C], int od, int d, int T, int rlo, int rhi,
                                              uint64_t (&live)[C], int &dmax, uint32_t (&word)[NWORD])
     {
         // bases: a_i for i = i0 + c, b_j for j = d - i0 - c
@@ -123,7 +123,7 @@ struct SideDP {
             const int H = SN[c] + sub_of(X[c / 4], P[c / 4], c);
             int S = max(max(H, Iv), Dv);
             bool ok = S >= T;
-            if (masked) {
+            if (MASKED) {
                 const int pos = lane * C + c;
                 ok = ok && pos >= rlo && pos <= rhi;
             }
@@ -219,8 +219,14 @@ struct SideDP {
         uint64_t live[C];
         int dmax;
         uint32_t word[NWORD];
-        if (DELTA == 1) cells_of<DELTA, PTR>(SA, od, d, T, masked, rlo, rhi, live, dmax, word);   // even d
-        else cells_of<DELTA, PTR>(SB, od, d, T, masked, rlo, rhi, live, dmax, word);             // odd d
+        // (the uniform branch keeps the range test out of the common path)
+        if (masked) {
+            if (DELTA == 1) cells_of<DELTA, PTR, true>(SA, od, d, T, rlo, rhi, live, dmax, word);   // even d
+            else cells_of<DELTA, PTR, true>(SB, od, d, T, rlo, rhi, live, dmax, word);             // odd d
+        } else {
+            if (DELTA == 1) cells_of<DELTA, PTR, false>(SA, od, d, T, rlo, rhi, live, dmax, word);
+            else cells_of<DELTA, PTR, false>(SB, od, d, T, rlo, rhi, live, dmax, word);
+        }
 
         // live hull of d
         uint64_t any = 0;

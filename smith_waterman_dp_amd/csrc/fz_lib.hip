@@ -51,7 +51,12 @@ struct Counters {
     int64_t totals[4];
 };
 
-constexpr int WAVES = 4;                // waves per block for the wave-per-side kernels
+// One wave per workgroup for the wave-per-side kernels: sides differ in
+// length by orders of magnitude, and a workgroup's slot on the CU is held
+// until its longest wave ends, so larger groups strand short waves' slots
+// (measured: about half the occupancy with four waves per group).
+constexpr int EXT_WAVES = 1;
+constexpr int LOCAL_WAVES = 4;          // local mode: every wave does the same work
 constexpr int C_STD = 6;                // window 384 positions
 constexpr int C_WIDE = 16;              // window 1024 positions
 constexpr int LOCAL_RL = 32;            // rows per lane in local mode
@@ -180,9 +185,9 @@ template <int C, bool EXEC>
 int launch_extend(fz_ctx *ctx, const ExtendArgs &a, int64_t nwork, hipStream_t st)
 {
     if (nwork <= 0) return FZ_OK;
-    const unsigned blocks = (unsigned)((nwork + WAVES - 1) / WAVES);
-    if (a.sc.small) extend_kernel<C, EXEC, true, WAVES><<<blocks, 64 * WAVES, 0, st>>>(a);
-    else extend_kernel<C, EXEC, false, WAVES><<<blocks, 64 * WAVES, 0, st>>>(a);
+    const unsigned blocks = (unsigned)((nwork + EXT_WAVES - 1) / EXT_WAVES);
+    if (a.sc.small) extend_kernel<C, EXEC, true, EXT_WAVES><<<blocks, 64 * EXT_WAVES, 0, st>>>(a);
+    else extend_kernel<C, EXEC, false, EXT_WAVES><<<blocks, 64 * EXT_WAVES, 0, st>>>(a);
     HIP_OK(hipGetLastError());
     return FZ_OK;
 }
@@ -248,10 +253,10 @@ int run_local(fz_ctx *ctx, const fz_seed *seeds, uint64_t n, uint64_t tlen, uint
     a.hits = hits;
     a.bnd = as<int32_t>(ctx->bnd);
     a.bnd_stride = stride;
-    const unsigned blocks = blocks_for((int64_t)n, WAVES);
+    const unsigned blocks = blocks_for((int64_t)n, LOCAL_WAVES);
     HIP_OK(hipEventRecord(ctx->kev[0], st));
-    if (sc.small) local_kernel<LOCAL_RL, true, WAVES><<<blocks, 64 * WAVES, 0, st>>>(a);
-    else local_kernel<LOCAL_RL, false, WAVES><<<blocks, 64 * WAVES, 0, st>>>(a);
+    if (sc.small) local_kernel<LOCAL_RL, true, LOCAL_WAVES><<<blocks, 64 * LOCAL_WAVES, 0, st>>>(a);
+    else local_kernel<LOCAL_RL, false, LOCAL_WAVES><<<blocks, 64 * LOCAL_WAVES, 0, st>>>(a);
     HIP_OK(hipGetLastError());
     HIP_OK(hipEventRecord(ctx->kev[1], st));
     return FZ_OK;
