@@ -71,6 +71,10 @@ struct RowHdr {
 
 // ----------------------------------------------------------- wave helpers --
 
+// A dword in the global address space (device memory): loads through it are
+// global_load instructions, which return in order.
+typedef __attribute__((address_space(1))) const uint32_t GlobalU32;
+
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
 // Lane l receives lane l+1's value; lane 63 receives `fill`.

@@ -60,11 +60,18 @@ struct SideDP {
     static constexpr int EL1 = 32 + 8 / C;
     static constexpr int NEL = EL1 - EL0 + 1;
     static constexpr int NWORD = (C + 7) / 8;           // pointer words per lane per row (8 nibbles each)
+    // an empty live hull: far outside every window, so that the range of the
+    // next diagonal comes out empty or from the other hull alone
+    static constexpr int NONE_LO = 1 << 29, NONE_HI = -(1 << 29);
 
     // registers
     int SA[C], SB[C], R[C], Dn[C];
+    uint32_t TA[NDW], QB[NDW];          // bases under this lane's slots on the current diagonal
+    uint32_t TAn[NDW + 1], QBn[NDW + 1];// dwords fetched ahead for the next update of each sequence
+    uint32_t shA, shB;                  // byte offset of those dwords
+    const uint8_t *pa, *pb;             // this lane's slot 0 at o_d = 0 (target) / o_d - d = 0 (query)
     // wave-uniform state
-    int K;
+    int K, dmask;               // dmask: first d whose window reaches i > m or j > n
     int lo1, hi1, lo2, hi2;     // live hulls (positions) of d-1 and d-2
     int best, bi, bj, dend;
     int64_t cells, cum_bytes, ptr_at_best;
@@ -90,18 +97,54 @@ struct SideDP {
         }
     }
 
-    // Evaluate diagonal d.  DELTA = o_d - o_(d-1); S of d-2 is in SN (and
-    // is replaced by S of d).  With PTR, word[] receives this lane's C
-    // pointer nibbles, eight per word.
-    template <int DELTA, bool PTR, bool MASKED>
-    __device__ __forceinline__ void cells_of(int (&SN)[C], int od, int d, int T, int rlo, int rhi,
-                                             uint64_t (&live)[C], int &dmax, uint32_t (&word)[NWORD])
+    // Sequence bytes.  Along the diagonals the target bytes under a lane move
+    // by one every even d and the query bytes by one every odd d, so each
+    // diagonal updates one sequence from dwords fetched two diagonals ahead.
+    __device__ __forceinline__ static void fetch(const uint8_t *p, uint32_t (&raw)[NDW + 1], uint32_t &sh)
     {
-        // bases: a_i for i = i0 + c, b_j for j = d - i0 - c
-        const int i0 = lane * C + od;
-        uint32_t TA[NDW], QB[NDW], X[NDW], P[NDW];
-        load_bytes<NDW>(t.A, t.abase + i0, TA);
-        load_bytes<NDW>(t.B, t.bbase - d + i0, QB);
+        const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+        // global (not flat) loads: they complete in order, so the wait for a
+        // fetch does not also wait for the one issued after it
+        const GlobalU32 *w = reinterpret_cast<const GlobalU32 *>(a & ~(uintptr_t)3);
+        sh = (uint32_t)(a & 3);
+#pragma unroll
+        for (int k = 0; k <= NDW; ++k) raw[k] = w[k];
+    }
+
+    __device__ __forceinline__ static void align(const uint32_t (&raw)[NDW + 1], uint32_t sh, uint32_t (&out)[NDW])
+    {
+#pragma unroll
+        for (int k = 0; k < NDW; ++k) out[k] = __builtin_amdgcn_alignbyte(raw[k + 1], raw[k], sh);
+    }
+
+    // After a slide: this diagonal's bases at the new offset, and the
+    // fetches for the next update of each sequence.
+    __device__ __forceinline__ void reload(int d, int od)
+    {
+        uint32_t raw[NDW + 1], sh;
+        fetch(pa + od, raw, sh);
+        align(raw, sh, TA);
+        fetch(pb + (od - d), raw, sh);
+        align(raw, sh, QB);
+        fetch(pa + (od + 1), TAn, shA);         // next even diagonal
+        fetch(pb + (od - d - 1), QBn, shB);     // next odd diagonal
+    }
+
+    __device__ __forceinline__ void set_dmask()
+    {
+        // o_d = (d + K) >> 1 reaches m - W + 2 at d = 2(m - W + 2) - K;
+        // d - o_d reaches n + 1 at d = 2n + 1 + K
+        dmask = min(2 * (t.m - W + 2) - K, 2 * t.n + 1 + K);
+    }
+
+    // Evaluate diagonal d.  DELTA = o_d - o_(d-1); S of d-2 is in SN (and
+    // is replaced by S of d).  Returns this lane's live slots as a bit mask.
+    // With PTR, word[] receives this lane's C pointer nibbles, eight per word.
+    template <int DELTA, bool PTR, bool MASKED>
+    __device__ __forceinline__ int cells_of(int (&SN)[C], int T, int rlo, int rhi, int &dmax,
+                                            uint32_t (&word)[NWORD])
+    {
+        uint32_t X[NDW], P[NDW];
 #pragma unroll
         for (int k = 0; k < NDW; ++k) {
             X[k] = TA[k] ^ QB[k];
@@ -115,6 +158,7 @@ struct SideDP {
 #pragma unroll
         for (int k = 0; k < NWORD; ++k) word[k] = 0;
         dmax = NEG;
+        int lm = 0;
         int Rn[C], Dnn[C];
 #pragma unroll
         for (int c = 0; c < C; ++c) {
@@ -127,7 +171,7 @@ struct SideDP {
                 const int pos = lane * C + c;
                 ok = ok && pos >= rlo && pos <= rhi;
             }
-            live[c] = ballot(ok);
+            lm |= ok ? (1 << c) : 0;
             const int Sk = ok ? S : NEG;
             const int U = Sk - sc.oe;
             const int Ie = Iv - sc.e, De = Dv - sc.e;
@@ -146,6 +190,7 @@ struct SideDP {
             R[c] = Rn[c];
             Dn[c] = Dnn[c];
         }
+        return lm;
     }
 
     __device__ __forceinline__ void slide(int s)
@@ -177,80 +222,86 @@ struct SideDP {
     template <int DELTA, bool PTR>
     __device__ __forceinline__ bool step(int d, int dstop, uint32_t *eager_lds)
     {
-        int od = (d + K) >> 1;
-        // R_d: cells with a possibly live predecessor, clipped to the matrix
-        int rlo = 0x7fffffff, rhi = -0x7fffffff;
-        if (lo1 <= hi1) {
-            rlo = lo1 - DELTA;
-            rhi = hi1 - DELTA + 1;
-        }
-        if (lo2 <= hi2) {
-            rlo = min(rlo, lo2);
-            rhi = max(rhi, hi2);
-        }
-        const int vlo = max(0, d - t.n) - od, vhi = min(t.m, d) - od;
-        rlo = max(rlo, vlo);
-        rhi = min(rhi, vhi);
-        if (rlo > rhi) return false;
         if (EXEC && d > dstop) return false;
-        if (rlo < 0 || rhi > W - 1) {
-            // slide by s lanes so that [rlo, rhi] fits, near the centre
-            const int smin = floordiv(rhi - (W - 1) + C - 1, C), smax = floordiv(rlo, C);
-            if (smin > smax) {
-                overflow = true;
-                return false;
-            }
-            int s = floordiv((rlo + rhi + 1) / 2 - W / 2, C);
-            s = s < smin ? smin : (s > smax ? smax : s);
-            slide(s);
-            const int sh = s * C;
-            K += 2 * sh;
-            od += sh;
-            lo1 -= sh; hi1 -= sh; lo2 -= sh; hi2 -= sh;
-            rlo -= sh; rhi -= sh;
+        int od = (d + K) >> 1;
+        // This diagonal's bases, fetched two diagonals ago, and at once the
+        // fetch for the next update of the same sequence; a full step of
+        // work separates each fetch from its first use.  (A slide below
+        // refetches everything.)
+        if (DELTA == 1) {
+            align(TAn, shA, TA);
+            fetch(pa + (od + 1), TAn, shA);
+        } else {
+            align(QBn, shB, QB);
+            fetch(pb + (od - d - 1), QBn, shB);
         }
-        // positions with i > m or j > n are the only ones that can pick up a
-        // live value without being in R_d; mask explicitly only when the
-        // window reaches them (cells with i < 0 or j < 0 only ever see -inf)
-        const bool masked = (W - 1 + od > t.m) || (d - od > t.n);
-        const int64_t tw = (int64_t)best - (int64_t)sc.ydrop;
-        const int T = tw < (int64_t)T_FLOOR ? T_FLOOR : (int)tw;
+        // R_d: cells with a possibly live predecessor (hulls of d-1 and d-2)
+        int rlo = min(lo1 - DELTA, lo2);
+        int rhi = max(hi1 - DELTA + 1, hi2);
+        bool masked = false;
+        if (!(d < dmask && rlo >= 0 && rhi <= W - 1 && rlo <= rhi)) {
+            // Near a matrix edge, an empty range, or the band at a window
+            // edge.  (Elsewhere R_d needs no clipping: its cells have
+            // 0 <= i <= d by construction and the window lies inside
+            // d - n <= i <= m.)
+            const int vlo = max(0, d - t.n) - od, vhi = min(t.m, d) - od;
+            rlo = max(rlo, vlo);
+            rhi = min(rhi, vhi);
+            if (rlo > rhi) return false;
+            if (rlo < 0 || rhi > W - 1) {
+                // slide by s lanes so that [rlo, rhi] fits, near the centre
+                const int smin = floordiv(rhi - (W - 1) + C - 1, C), smax = floordiv(rlo, C);
+                if (smin > smax) {
+                    overflow = true;
+                    return false;
+                }
+                int s = floordiv((rlo + rhi + 1) / 2 - W / 2, C);
+                s = s < smin ? smin : (s > smax ? smax : s);
+                slide(s);
+                const int sh = s * C;
+                K += 2 * sh;
+                od += sh;
+                lo1 -= sh; hi1 -= sh; lo2 -= sh; hi2 -= sh;
+                rlo -= sh; rhi -= sh;
+                set_dmask();
+                reload(d, od);
+            }
+            // positions with i > m or j > n are the only ones that can pick
+            // up a live value without being in R_d; mask explicitly only when
+            // the window reaches them (cells with i < 0 or j < 0 only ever
+            // see -inf)
+            masked = (W - 1 + od > t.m) || (d - od > t.n);
+        }
+        const int T = max(best - sc.ydrop, T_FLOOR);
 
-        uint64_t live[C];
-        int dmax;
+        int lm, dmax;
         uint32_t word[NWORD];
         // (the uniform branch keeps the range test out of the common path)
         if (masked) {
-            if (DELTA == 1) cells_of<DELTA, PTR, true>(SA, od, d, T, rlo, rhi, live, dmax, word);   // even d
-            else cells_of<DELTA, PTR, true>(SB, od, d, T, rlo, rhi, live, dmax, word);             // odd d
+            if (DELTA == 1) lm = cells_of<DELTA, PTR, true>(SA, T, rlo, rhi, dmax, word);   // even d
+            else lm = cells_of<DELTA, PTR, true>(SB, T, rlo, rhi, dmax, word);             // odd d
         } else {
-            if (DELTA == 1) cells_of<DELTA, PTR, false>(SA, od, d, T, rlo, rhi, live, dmax, word);
-            else cells_of<DELTA, PTR, false>(SB, od, d, T, rlo, rhi, live, dmax, word);
+            if (DELTA == 1) lm = cells_of<DELTA, PTR, false>(SA, T, rlo, rhi, dmax, word);
+            else lm = cells_of<DELTA, PTR, false>(SB, T, rlo, rhi, dmax, word);
         }
 
-        // live hull of d
-        uint64_t any = 0;
-#pragma unroll
-        for (int c = 0; c < C; ++c) any |= live[c];
-        int lo = 1, hi = 0, llo = 0, lhi = -1;
-        if (any) {
-            llo = ctz64(any);
-            lhi = hibit64(any);
-            int slo = C, shi = -1;
-#pragma unroll
-            for (int c = 0; c < C; ++c) {
-                if (slo == C && ((live[c] >> llo) & 1ull)) slo = c;
-                if ((live[c] >> lhi) & 1ull) shi = c;
-            }
-            lo = llo * C + slo;
-            hi = lhi * C + shi;
+        // live hull of d: lanes from the ballot, slots from the two edge lanes
+        const uint64_t anyl = ballot(lm != 0);
+        int lo = NONE_LO, hi = NONE_HI, llo = 0, lhi = -1;
+        if (anyl) {
+            llo = ctz64(anyl);
+            lhi = hibit64(anyl);
+            const uint32_t mlo = (uint32_t)__builtin_amdgcn_readlane(lm, llo);
+            const uint32_t mhi = (uint32_t)__builtin_amdgcn_readlane(lm, lhi);
+            lo = llo * C + __builtin_ctz(mlo);
+            hi = lhi * C + (31 - __builtin_clz(mhi));
         }
         cells += rhi - rlo + 1;
         const int nl = lhi - llo + 1;
         cum_bytes += 8 + 4 * (int64_t)nl * NWORD;
 
         if (ballot(dmax > best)) {
-            const int nb = wave_max(dmax);
+            const int nb = uniform(wave_max(dmax));
             int pbest = 0x7fffffff;
 #pragma unroll
             for (int c = 0; c < C; ++c) {
@@ -300,19 +351,32 @@ struct SideDP {
 #pragma unroll
         for (int c = 0; c < C; ++c) { SA[c] = NEG; SB[c] = NEG; R[c] = NEG; Dn[c] = NEG; }
         K = -W;
+        set_dmask();
+        pa = t.A + (t.abase + lane * C);
+        pb = t.B + (t.bbase + lane * C);
         // d = 0: the single cell (0,0), S = 0, I = D = -inf
         if (lane == P0 / C) {
             SA[0] = 0;
             R[0] = -sc.oe;
             Dn[0] = -sc.oe;
         }
-        lo1 = P0; hi1 = P0; lo2 = 1; hi2 = 0;
+        lo1 = P0; hi1 = P0; lo2 = NONE_LO; hi2 = NONE_HI;
         best = 0; bi = 0; bj = 0; dend = 0;
         cells = 1;
         cum_bytes = 8 + 4 * NWORD;
         ptr_at_best = cum_bytes;
         overflow = false;
         rowoff = 0;
+        {
+            // diagonal 1 is odd: it takes its query bytes from QBn and keeps
+            // the target bytes set here; diagonal 2 takes TAn
+            const int od1 = (1 + K) >> 1;
+            uint32_t raw[NDW + 1], sh;
+            fetch(pa + od1, raw, sh);
+            align(raw, sh, TA);
+            fetch(pb + (od1 - 1), QBn, shB);
+            fetch(pa + (od1 + 1), TAn, shA);
+        }
         if (EXEC) {
             hdr = reinterpret_cast<RowHdr *>(ptr_base);
             rows = reinterpret_cast<uint32_t *>(ptr_base + 8 * ((int64_t)dstop + 1));
@@ -337,12 +401,10 @@ struct SideDP {
         int d = 1;
         if (!EXEC) {
             // diagonals 1..32 keep pointers for the eager block
-            bool go = true;
-            for (; d <= EAGER_ROWS - 1 && go; d += 2) {
-                go = step<0, true>(d, dstop, eager_lds);
-                if (go) go = step<1, true>(d + 1, dstop, eager_lds);
+            for (; d <= EAGER_ROWS - 1; d += 2) {
+                if (!step<0, true>(d, dstop, eager_lds)) return;
+                if (!step<1, true>(d + 1, dstop, eager_lds)) return;
             }
-            if (!go) return;
         }
         for (;; d += 2) {
             if (!step<0, EXEC>(d, dstop, eager_lds)) break;
