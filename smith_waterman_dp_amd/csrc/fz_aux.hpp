@@ -304,11 +304,9 @@ __global__ void window_max_kernel(const fz_seed *seeds, int64_t n, int64_t *out2
 }
 
 // ---------------------------------------------------------------- walker --
-// One lane per traced side: follow the executor's 4-bit pointers from the
-// best cell back to (0,0) (FastZ section 3.1.3: the walk has no parallelism
-// inside one extension, so it runs one thread per extension), emitting
-// run-length words end-first.  Pointer nibble: bits 0-1 source of S
-// (0 diagonal, 1 I, 2 D), bit 2 "the I entering the right neighbour
+// Follow the executor's 4-bit pointers from the best cell back to (0,0),
+// emitting run-length words end-first.  Pointer nibble: bits 0-1 source of
+// S (0 diagonal, 1 I, 2 D), bit 2 "the I entering the right neighbour
 // extends", bit 3 "the D entering the lower neighbour extends".
 struct WalkArgs {
     const ExecItem *items;
@@ -333,9 +331,28 @@ __device__ __forceinline__ void rle_push(uint32_t *runs, int64_t &n, uint32_t &c
     cur_len = 1;
 }
 
-__global__ void walk_kernel(WalkArgs a)
+// Traceback walk (FastZ section 2.1, Fig. 3b; section 3.1.3) over the
+// executor's pointer rows, one wave per side, 64 anti-diagonals at a time.
+// The walk has no parallelism inside one extension (FastZ runs it one thread
+// per extension), and a lane per side would pay two dependent memory round
+// trips (row header, then pointer word) per step.  Here, for each
+// chunk of anti-diagonals d - 63 .. d below the walk's current cell (i, j),
+// lane r loads row d - 63 + r's header and the pointer words the walk can
+// reach on it (i never grows, and falls by at most one per anti-diagonal)
+// into LDS; the wave then walks the chunk from LDS in uniform control flow.
+constexpr int WALK_CHUNK = 64;
+
+template <int C>
+__global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
 {
-    const int64_t k = a.begin + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    constexpr int NW = (C + 7) / 8;                      // pointer words per lane per row
+    constexpr int WPR = (WALK_CHUNK / C + 2) * NW;       // words staged per row
+    __shared__ uint32_t wl[WALK_CHUNK][WPR];
+    __shared__ int32_t w0l[WALK_CHUNK];                  // first staged word (relative to the row)
+    __shared__ int32_t ibl[WALK_CHUNK];                  // i of the row's first stored position
+    __shared__ int32_t nwl[WALK_CHUNK];                  // words stored in the row
+    const int lane = lane_id();
+    const int64_t k = a.begin + (int64_t)blockIdx.x;
     if (k >= a.end) return;
     const ExecItem it = a.items[k];
     const SideOut o = a.out[it.side];
@@ -343,59 +360,98 @@ __global__ void walk_kernel(WalkArgs a)
     const RowHdr *hdr = reinterpret_cast<const RowHdr *>(base);
     const uint32_t *rows = reinterpret_cast<const uint32_t *>(base + 8 * ((int64_t)it.dstar + 1));
     uint32_t *runs = a.runs + a.run_off[it.side];
-    const int C = a.C;
     const uint32_t total_rows = (uint32_t)((it.ptr_bytes - 8 * ((int64_t)it.dstar + 1)) / 4);
-    bool bad = false;
-    // nibble of cell (i, j); marks the walk bad instead of reading outside
-    // the side's stored rows
-    auto nib = [&](int i, int j) -> uint32_t {
-        const int d = i + j;
-        if (i < 0 || j < 0 || d > it.dstar) {
-            bad = true;
-            return 0u;
-        }
-        const RowHdr h = hdr[d];
-        const uint32_t row_end = d < it.dstar ? hdr[d + 1].off : total_rows;
-        const int p = i - h.ibase;
-        const int nword = (C + 7) / 8;
-        const uint32_t wi = h.off + (uint32_t)((p / C) * nword + (p % C) / 8);
-        if (p < 0 || wi >= row_end) {
-            bad = true;
-            return 0u;
-        }
-        return (rows[wi] >> (4 * ((p % C) % 8))) & 0xFu;
-    };
-    int64_t n = 0;
-    uint32_t cop = 0, clen = 0;
+
+    // states: 0 = S; 1 = arrived in I (continue if the cell's bit 2 says
+    // the gap extends); 2 = arrived in D (bit 3)
     int i = o.ie, j = o.je, st = 0;
+    bool bad = i < 0 || j < 0 || i + j > it.dstar;
+    int64_t n = 0, moves = 0;
+    uint32_t cop = 0, clen = 0;
     const int64_t limit = (int64_t)o.ie + o.je;
-    int64_t steps = 0;
-    while (!(st == 0 && i == 0 && j == 0) && steps <= limit && !bad) {
-        if (st == 0) {
-            const uint32_t src = nib(i, j) & 3u;
-            if (src == 0) {
-                rle_push(runs, n, cop, clen, 0);
-                --i;
-                --j;
-                ++steps;
-            } else {
-                st = (int)src;
-            }
-        } else if (st == 1) {
-            rle_push(runs, n, cop, clen, 1);
-            --j;
-            ++steps;
-            st = (nib(i, j) & 4u) ? 1 : 0;
-        } else {
-            rle_push(runs, n, cop, clen, 2);
-            --i;
-            ++steps;
-            st = (nib(i, j) & 8u) ? 2 : 0;
+    auto emit = [&](uint32_t op) {
+        if (clen && op == cop) {
+            ++clen;
+            return;
         }
-        if (i < 0 || j < 0) break;
+        if (clen && lane == 0) runs[n] = (clen << 4) | cop;
+        if (clen) ++n;
+        cop = op;
+        clen = 1;
+    };
+    while (!bad && !(st == 0 && i == 0 && j == 0)) {
+        const int d = i + j;
+        const int dlo = max(0, d - (WALK_CHUNK - 1));
+        {
+            const int dr = dlo + lane;
+            if (dr <= d) {
+                const RowHdr h = hdr[dr];
+                // (clamped to the side's rows, so that no header value can
+                // send a read outside them)
+                const uint32_t row_end = min(dr < it.dstar ? hdr[dr + 1].off : total_rows, total_rows);
+                const int plo = max(0, i - (d - dr)) - h.ibase;
+                const int w0 = plo <= 0 ? 0 : (plo / C) * NW;
+                const int nw = row_end > h.off ? (int)(row_end - h.off) : 0;
+#pragma unroll
+                for (int q = 0; q < WPR; ++q) {
+                    const int w = w0 + q;
+                    wl[lane][q] = w < nw ? rows[h.off + (uint32_t)w] : 0u;
+                }
+                w0l[lane] = w0;
+                ibl[lane] = h.ibase;
+                nwl[lane] = nw;
+            }
+        }
+        __syncthreads();
+        // walk down to anti-diagonal dlo
+        while (!(st == 0 && i == 0 && j == 0)) {
+            const int dd = i + j;
+            if (dd < dlo) break;
+            const int r = dd - dlo;
+            const int p = i - ibl[r];
+            const int w = p < 0 ? -1 : (p / C) * NW + (p % C) / 8;
+            const int q = w - w0l[r];
+            if (p < 0 || w >= nwl[r] || q < 0 || q >= WPR || moves > limit) {
+                bad = true;
+                break;
+            }
+            const uint32_t x = (wl[r][q] >> (4 * ((p % C) % 8))) & 0xFu;
+            if (st == 1 && (x & 4u)) {
+                emit(1);
+                --j;
+            } else if (st == 2 && (x & 8u)) {
+                emit(2);
+                --i;
+            } else {
+                // the gap (if any) ends here: this cell is taken in S
+                st = 0;
+                if (i == 0 && j == 0) break;
+                const uint32_t src = x & 3u;
+                if (src == 0) {
+                    emit(0);
+                    --i;
+                    --j;
+                } else if (src == 1) {
+                    emit(1);
+                    --j;
+                    st = 1;
+                } else {
+                    emit(2);
+                    --i;
+                    st = 2;
+                }
+            }
+            ++moves;
+            if (i < 0 || j < 0) {
+                bad = true;
+                break;
+            }
+        }
+        __syncthreads();
     }
-    if (clen) runs[n++] = (clen << 4) | cop;
-    a.run_len[it.side] = (!bad && i == 0 && j == 0 && st == 0) ? n : -1;
+    if (clen && lane == 0) runs[n] = (clen << 4) | cop;
+    if (clen) ++n;
+    if (lane == 0) a.run_len[it.side] = (!bad && i == 0 && j == 0 && st == 0) ? n : -1;
 }
 
 // Eager sides: op bytes (end-first) -> run words (end-first).

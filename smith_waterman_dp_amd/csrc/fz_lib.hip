@@ -555,7 +555,8 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
                 wk.run_off = as<int64_t>(ctx->run_off);
                 wk.runs = as<uint32_t>(ctx->runs);
                 wk.run_len = as<int64_t>(ctx->run_len);
-                walk_kernel<<<blocks_for(s1 - s0, 64), 64, 0, st>>>(wk);
+                if (cls == 0) walk_wave_kernel<C_STD><<<(unsigned)(s1 - s0), 64, 0, st>>>(wk);
+                else walk_wave_kernel<C_WIDE><<<(unsigned)(s1 - s0), 64, 0, st>>>(wk);
                 HIP_OK(hipGetLastError());
             }
         }
