@@ -125,6 +125,7 @@ def main():
     main_ms = []
     t0 = time.perf_counter()
     hits = None
+    st = None
     for k in range(steps):
         hits, cig, st = step()
         main_ms.append(st["ms_main"])
@@ -144,6 +145,14 @@ def main():
            "min_traceback_score": w.get("min_tb"), "main_kernel_ms": round(kern_s * 1e3, 3)}
     if not local:
         cfg["extensions_per_sec"] = round(n / (ms_per_step / 1e3), 1)
+        # last step's statistics (phase times are stream-event spans; "exec"
+        # covers the executor batches with their walks)
+        cfg["executor_cells"] = int(st["executor_cells"])
+        cfg["pointer_bytes"] = int(st["pointer_bytes"])
+        cfg["executor_sides"] = int(st["n_executor"])
+        cfg["executor_batches"] = int(st["n_batches"])
+        cfg["phase_ms"] = {k[3:]: round(float(st[k]), 1) for k in
+                           ("ms_pack", "ms_inspect", "ms_bin", "ms_exec", "ms_gather")}
     out = {"metric": METRIC if a.workload == "skewed" else "GCUPS on the %s batch, 1 MI355X" % a.workload,
            "value": round(gcups, 3), "unit": "GCUPS", "n_gpus": 1, "steps": steps, "warmup": a.warmup,
            "ms_per_step": round(ms_per_step, 3), "higher_is_better": True, "scaling": "weak",

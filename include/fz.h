@@ -93,6 +93,9 @@ typedef struct {
     uint64_t bin_hist[8];
     uint64_t n_batches;
     float ms_pack, ms_inspect, ms_bin, ms_exec, ms_walk, ms_gather;
+                                   /* phase spans; the walks run interleaved with the
+                                    * executor batches and are part of ms_exec (ms_walk
+                                    * stays 0) */
     float ms_main;                 /* the dominant kernel alone (inspector, or the local kernel) */
 } fz_stats;
 
@@ -134,9 +137,10 @@ void fz_destroy(fz_ctx *ctx);
  * next call on ctx.  Not thread-safe per context. */
 const char *fz_last_error(const fz_ctx *ctx);
 
-/* Cap (bytes) of the traceback-pointer workspace; the executor works in
- * batches that fit.  0 restores the default (1/4 of free device memory,
- * at most 32 GiB). */
+/* Cap (bytes) of the traceback-pointer workspace, shared by the executor's
+ * streams (three workspaces of a third each, each at least twice the
+ * largest side's pointer rows); the executor works in batches that fit.
+ * 0 restores the default (1/4 of free device memory, at most 48 GiB). */
 int fz_set_pointer_workspace(fz_ctx *ctx, uint64_t bytes);
 
 /*

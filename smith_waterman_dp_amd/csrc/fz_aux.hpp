@@ -304,10 +304,8 @@ __global__ void window_max_kernel(const fz_seed *seeds, int64_t n, int64_t *out2
 }
 
 // ---------------------------------------------------------------- walker --
-// Follow the executor's 4-bit pointers from the best cell back to (0,0),
-// emitting run-length words end-first.  Pointer nibble: bits 0-1 source of
-// S (0 diagonal, 1 I, 2 D), bit 2 "the I entering the right neighbour
-// extends", bit 3 "the D entering the lower neighbour extends".
+// Follow the executor's 4-bit pointers (PTR_* in fz_device.hpp) from the
+// best cell back to (0,0), emitting run-length words end-first.
 struct WalkArgs {
     const ExecItem *items;
     int64_t begin, end;
@@ -332,15 +330,18 @@ __device__ __forceinline__ void rle_push(uint32_t *runs, int64_t &n, uint32_t &c
 }
 
 // Traceback walk (FastZ section 2.1, Fig. 3b; section 3.1.3) over the
-// executor's pointer rows, one wave per side, 64 anti-diagonals at a time.
+// executor's pointer rows, one wave per side, 128 anti-diagonals at a time.
 // The walk has no parallelism inside one extension (FastZ runs it one thread
 // per extension), and a lane per side would pay two dependent memory round
-// trips (row header, then pointer word) per step.  Here, for each
-// chunk of anti-diagonals d - 63 .. d below the walk's current cell (i, j),
-// lane r loads row d - 63 + r's header and the pointer words the walk can
-// reach on it (i never grows, and falls by at most one per anti-diagonal)
-// into LDS; the wave then walks the chunk from LDS in uniform control flow.
-constexpr int WALK_CHUNK = 64;
+// trips (row header, then pointer word) per step.  Here, for each chunk of
+// anti-diagonals d - 127 .. d below the walk's current cell (i, j), lane l
+// loads rows d - 127 + l and d - 63 + l: header, and the pointer words the
+// walk can reach on the row (i never grows, and falls by at most one per
+// anti-diagonal), all loads in flight at once, into LDS.  The wave then
+// walks the chunk from LDS in uniform control flow; a run of diagonal moves
+// is taken in one round, lane l testing the l-th cell down the diagonal.
+constexpr int WALK_LANES = 64;
+constexpr int WALK_CHUNK = 2 * WALK_LANES;
 
 template <int C>
 __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
@@ -348,9 +349,6 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
     constexpr int NW = (C + 7) / 8;                      // pointer words per lane per row
     constexpr int WPR = (WALK_CHUNK / C + 2) * NW;       // words staged per row
     __shared__ uint32_t wl[WALK_CHUNK][WPR];
-    __shared__ int32_t w0l[WALK_CHUNK];                  // first staged word (relative to the row)
-    __shared__ int32_t ibl[WALK_CHUNK];                  // i of the row's first stored position
-    __shared__ int32_t nwl[WALK_CHUNK];                  // words stored in the row
     const int lane = lane_id();
     const int64_t k = a.begin + (int64_t)blockIdx.x;
     if (k >= a.end) return;
@@ -362,86 +360,145 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
     uint32_t *runs = a.runs + a.run_off[it.side];
     const uint32_t total_rows = (uint32_t)((it.ptr_bytes - 8 * ((int64_t)it.dstar + 1)) / 4);
 
-    // states: 0 = S; 1 = arrived in I (continue if the cell's bit 2 says
-    // the gap extends); 2 = arrived in D (bit 3)
+    // states: 0 = S; 1 = arrived in I (continue if the cell's PTR_EXT_I
+    // says the gap extends); 2 = arrived in D (PTR_EXT_D)
     int i = o.ie, j = o.je, st = 0;
-    bool bad = i < 0 || j < 0 || i + j > it.dstar;
+    bool bad = i < 0 || j < 0 || i + j > it.dstar || total_rows == 0;
     int64_t n = 0, moves = 0;
     uint32_t cop = 0, clen = 0;
     const int64_t limit = (int64_t)o.ie + o.je;
-    auto emit = [&](uint32_t op) {
+    auto emit = [&](uint32_t op, uint32_t cnt) {
         if (clen && op == cop) {
-            ++clen;
+            clen += cnt;
             return;
         }
         if (clen && lane == 0) runs[n] = (clen << 4) | cop;
         if (clen) ++n;
         cop = op;
-        clen = 1;
+        clen = cnt;
+    };
+    // the staged pointer nibble of cell (ii, dd - ii) on chunk row r, or 16
+    // when the row does not hold it (fields of row r live in lane r % 64)
+    auto nib_at = [&](int r, int ii, int ib, int w0, int nw) -> uint32_t {
+        const int p = ii - ib;
+        if (p < 0) return 16u;
+        const int w = (p / C) * NW + (p % C) / 8;
+        const int q = w - w0;
+        if (w >= nw || q < 0 || q >= WPR) return 16u;
+        return (wl[r][q] >> ptr_shift<C>(p % C)) & 0xFu;
     };
     while (!bad && !(st == 0 && i == 0 && j == 0)) {
         const int d = i + j;
         const int dlo = max(0, d - (WALK_CHUNK - 1));
+        int rib[2] = {0, 0}, rw0[2] = {0, 0}, rnw[2] = {0, 0};
         {
-            const int dr = dlo + lane;
-            if (dr <= d) {
-                const RowHdr h = hdr[dr];
+            // both rows' headers, then every word load of both rows, then
+            // the LDS stores: two memory round trips per chunk
+            RowHdr h[2];
+            uint32_t rend[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                // rows past d are not needed: they read row d's header,
+                // unconditionally (no divergent branch between the loads)
+                const int dr = min(dlo + h2 * WALK_LANES + lane, d);
+                h[h2] = hdr[dr];
                 // (clamped to the side's rows, so that no header value can
                 // send a read outside them)
-                const uint32_t row_end = min(dr < it.dstar ? hdr[dr + 1].off : total_rows, total_rows);
-                const int plo = max(0, i - (d - dr)) - h.ibase;
-                const int w0 = plo <= 0 ? 0 : (plo / C) * NW;
-                const int nw = row_end > h.off ? (int)(row_end - h.off) : 0;
+                const uint32_t next_off = hdr[min(dr + 1, it.dstar)].off;
+                rend[h2] = min(dr < it.dstar ? next_off : total_rows, total_rows);
+            }
+            uint32_t v[2][WPR];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int dr = dlo + h2 * WALK_LANES + lane;
+                const int plo = max(0, i - (d - dr)) - h[h2].ibase;
+                rw0[h2] = plo <= 0 ? 0 : (plo / C) * NW;
+                rnw[h2] = (dr <= d && rend[h2] > h[h2].off) ? (int)(rend[h2] - h[h2].off) : 0;
+                rib[h2] = h[h2].ibase;
 #pragma unroll
                 for (int q = 0; q < WPR; ++q) {
-                    const int w = w0 + q;
-                    wl[lane][q] = w < nw ? rows[h.off + (uint32_t)w] : 0u;
+                    // every load in bounds (the side's first word when the
+                    // row is empty), all issued before any is used
+                    const int w = min(rw0[h2] + q, rnw[h2] - 1);
+                    v[h2][q] = rows[rnw[h2] > 0 ? h[h2].off + (uint32_t)w : 0u];
                 }
-                w0l[lane] = w0;
-                ibl[lane] = h.ibase;
-                nwl[lane] = nw;
             }
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                for (int q = 0; q < WPR; ++q)
+                    wl[h2 * WALK_LANES + lane][q] = rw0[h2] + q < rnw[h2] ? v[h2][q] : 0u;
         }
         __syncthreads();
-        // walk down to anti-diagonal dlo
         while (!(st == 0 && i == 0 && j == 0)) {
             const int dd = i + j;
             if (dd < dlo) break;
             const int r = dd - dlo;
-            const int p = i - ibl[r];
-            const int w = p < 0 ? -1 : (p / C) * NW + (p % C) / 8;
-            const int q = w - w0l[r];
-            if (p < 0 || w >= nwl[r] || q < 0 || q >= WPR || moves > limit) {
+            const int hr = r / WALK_LANES, lr = r % WALK_LANES;
+            const int ib = __builtin_amdgcn_readlane(hr ? rib[1] : rib[0], lr);
+            const int w0 = __builtin_amdgcn_readlane(hr ? rw0[1] : rw0[0], lr);
+            const int nw = __builtin_amdgcn_readlane(hr ? rnw[1] : rnw[0], lr);
+            const uint32_t x = (uint32_t)uniform((int)nib_at(r, i, ib, w0, nw));
+            if (x > 15u || moves > limit) {
                 bad = true;
                 break;
             }
-            const uint32_t x = (wl[r][q] >> (4 * ((p % C) % 8))) & 0xFu;
-            if (st == 1 && (x & 4u)) {
-                emit(1);
+            if (st == 1 && (x & PTR_EXT_I)) {
+                emit(1, 1);
                 --j;
-            } else if (st == 2 && (x & 8u)) {
-                emit(2);
+                ++moves;
+            } else if (st == 2 && (x & PTR_EXT_D)) {
+                emit(2, 1);
                 --i;
+                ++moves;
             } else {
                 // the gap (if any) ends here: this cell is taken in S
                 st = 0;
                 if (i == 0 && j == 0) break;
-                const uint32_t src = x & 3u;
+                const uint32_t src = ptr_src(x);
                 if (src == 0) {
-                    emit(0);
-                    --i;
-                    --j;
+                    // diagonal moves from here: lane l tests cell
+                    // (i - l, j - l) on row r - 2l; the run ends at the
+                    // first cell that is not a diagonal move, at the
+                    // origin, or at the chunk's end
+                    const int rl = r - 2 * lane;
+                    const int sl = rl < 0 ? 0 : rl;
+                    // row sl's fields: fetch both of lane sl % 64's rows,
+                    // pick here
+                    const int src_lane = sl % WALK_LANES;
+                    const int ib0 = __shfl(rib[0], src_lane), ib1 = __shfl(rib[1], src_lane);
+                    const int w00 = __shfl(rw0[0], src_lane), w01 = __shfl(rw0[1], src_lane);
+                    const int nw0 = __shfl(rnw[0], src_lane), nw1 = __shfl(rnw[1], src_lane);
+                    const bool lo_half = sl < WALK_LANES;
+                    const int lib = lo_half ? ib0 : ib1, lw0 = lo_half ? w00 : w01, lnw = lo_half ? nw0 : nw1;
+                    const int il = i - lane, jl = j - lane;
+                    bool m = rl >= 0 && il >= 0 && jl >= 0 && !(il == 0 && jl == 0);
+                    if (m) {
+                        const uint32_t xl = nib_at(rl, il, lib, lw0, lnw);
+                        m = xl <= 15u && (xl & PTR_DIAG);
+                    }
+                    const uint64_t stop = ~ballot(m);
+                    const int f = stop ? ctz64(stop) : WALK_LANES;   // >= 1: lane 0 is this cell
+                    if (f == 0) {
+                        bad = true;     // cannot happen; never loop without progress
+                        break;
+                    }
+                    emit(0, (uint32_t)f);
+                    i -= f;
+                    j -= f;
+                    moves += f;
                 } else if (src == 1) {
-                    emit(1);
+                    emit(1, 1);
                     --j;
                     st = 1;
+                    ++moves;
                 } else {
-                    emit(2);
+                    emit(2, 1);
                     --i;
                     st = 2;
+                    ++moves;
                 }
             }
-            ++moves;
             if (i < 0 || j < 0) {
                 bad = true;
                 break;

@@ -91,6 +91,41 @@ __device__ __forceinline__ int from_prev_lane(int v, int fill)
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
+// ------------------------------------------------------ traceback pointers --
+// One 4-bit pointer per cell (FastZ section 3.1.3), built by shifting bits
+// into a dword, most significant first:
+//   PTR_DIAG (bit 3)  S came by the diagonal move (H)
+//   PTR_FROM_I (2)    S came from I (taken when not PTR_DIAG)
+//   PTR_EXT_I (1)     the I handed to the right neighbour extends this I
+//   PTR_EXT_D (0)     the D handed to the lower neighbour extends this D
+// A lane's C cells fill ceil(C/8) dwords, eight cells each; the first cell
+// of a dword ends up in its highest nibble.
+enum : uint32_t { PTR_DIAG = 8, PTR_FROM_I = 4, PTR_EXT_I = 2, PTR_EXT_D = 1 };
+
+// w * 2 + bit, with the bit taken from the lane mask of a comparison (one
+// v_addc: the comparison's mask is the carry-in).
+__device__ __forceinline__ uint32_t shift_in(uint32_t w, bool bit)
+{
+    const uint64_t m = ballot(bit);
+    uint32_t r;
+    asm("v_addc_co_u32_e64 %0, vcc, %1, %1, %2" : "=v"(r) : "v"(w), "s"(m) : "vcc");
+    return r;
+}
+
+// Bit offset of the nibble of slot c (0 .. C-1) inside its dword.
+template <int C>
+__device__ __forceinline__ int ptr_shift(int c)
+{
+    const int n = (C - (c / 8) * 8) < 8 ? (C - (c / 8) * 8) : 8;    // cells in c's dword
+    return 4 * (n - 1 - c % 8);
+}
+
+// Source of S from a pointer: 0 diagonal, 1 I, 2 D.
+__device__ __forceinline__ uint32_t ptr_src(uint32_t nib)
+{
+    return (nib & PTR_DIAG) ? 0u : ((nib & PTR_FROM_I) ? 1u : 2u);
+}
+
 __device__ __forceinline__ int wave_max(int v)
 {
     for (int off = 32; off >= 1; off >>= 1) {

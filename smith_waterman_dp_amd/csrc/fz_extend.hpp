@@ -178,9 +178,11 @@ struct SideDP {
             Rn[c] = max(Ie, U);
             Dnn[c] = max(De, U);
             if (PTR) {
-                const uint32_t src = (S == H) ? 0u : (S == Iv ? 1u : 2u);
-                const uint32_t nib = src | (Ie > U ? 4u : 0u) | (De > U ? 8u : 0u);
-                word[c / 8] |= nib << (4 * (c % 8));
+                uint32_t &wd = word[c / 8];
+                wd = shift_in(wd, S == H);      // PTR_DIAG
+                wd = shift_in(wd, S == Iv);     // PTR_FROM_I
+                wd = shift_in(wd, Ie > U);      // PTR_EXT_I
+                wd = shift_in(wd, De > U);      // PTR_EXT_D
             }
             SN[c] = Sk;
             dmax = max(dmax, Sk);
@@ -388,7 +390,7 @@ struct SideDP {
             }
             if (lane == P0 / C) {
 #pragma unroll
-                for (int k = 0; k < NWORD; ++k) rows[k] = 0u;   // (0,0): source 0, gaps opened
+                for (int k = 0; k < NWORD; ++k) rows[k] = 0u;   // (0,0): no gap extends through it
             }
             rowoff = NWORD;
             rowcap = (uint32_t)((ptr_bytes - 8 * ((int64_t)dstop + 1)) / 4);
@@ -424,12 +426,12 @@ struct SideDP {
             const int p = ii - od0;
             const int l = p / C, c = p % C;
             const uint32_t wd = (uint32_t)uniform((int)eager_lds[(dd * NEL + (l - EL0)) * NWORD + c / 8]);
-            return (wd >> (4 * (c % 8))) & 0xFu;
+            return (wd >> ptr_shift<C>(c)) & 0xFu;
         };
         for (int guard = 0; guard < 2 * EAGER_OPS + 2; ++guard) {
             if ((st == 0 && i == 0 && j == 0) || n >= EAGER_OPS || i < 0 || j < 0) break;
             if (st == 0) {
-                const uint32_t src = nib(i, j) & 3u;
+                const uint32_t src = ptr_src(nib(i, j));
                 if (src == 0) {
                     if (lane == 0) ops[n] = 0;
                     ++n;
@@ -442,12 +444,12 @@ struct SideDP {
                 if (lane == 0) ops[n] = 1;
                 ++n;
                 if (--j < 0) break;
-                st = (nib(i, j) & 4u) ? 1 : 0;
+                st = (nib(i, j) & PTR_EXT_I) ? 1 : 0;
             } else {
                 if (lane == 0) ops[n] = 2;
                 ++n;
                 if (--i < 0) break;
-                st = (nib(i, j) & 8u) ? 2 : 0;
+                st = (nib(i, j) & PTR_EXT_D) ? 2 : 0;
             }
         }
         return (st == 0 && i == 0 && j == 0) ? n : -1;

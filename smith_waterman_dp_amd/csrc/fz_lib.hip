@@ -57,6 +57,11 @@ struct Counters {
 // (measured: about half the occupancy with four waves per group).
 constexpr int EXT_WAVES = 1;
 constexpr int LOCAL_WAVES = 4;          // local mode: every wave does the same work
+// Executor batches go round-robin to this many streams, each with its own
+// pointer workspace, so that a batch's last long sides overlap the next
+// batches instead of leaving the machine idle (a batch holds only a few
+// thousand sides, about one round of resident waves).
+constexpr int EXEC_STREAMS = 3;
 constexpr int C_STD = 6;                // window 384 positions
 constexpr int C_WIDE = 16;              // window 1024 positions
 constexpr int LOCAL_RL = 32;            // rows per lane in local mode
@@ -71,7 +76,10 @@ struct fz_ctx {
     uint64_t last_words = 0;            // CIGAR words of the last successful call
     DevBuf Tf, Tr, Qf, Qr;
     DevBuf tasks, info, out, eager, side_trace, run_cap, run_off, run_len, runs;
-    DevBuf items, batch_first, scan_tmp, cig, cigar, ptr_ws, counters, ovl0, ovl1, bnd;
+    DevBuf items, batch_first, scan_tmp, cig, cigar, counters, ovl0, ovl1, bnd;
+    DevBuf ptr_ws[EXEC_STREAMS];        // one pointer workspace per executor stream
+    hipStream_t xs[EXEC_STREAMS - 1] = {};   // executor streams besides the caller's
+    hipEvent_t fork_ev = nullptr, join_ev[EXEC_STREAMS - 1] = {};
     hipEvent_t ev[8] = {};
     hipEvent_t kev[2] = {};             // brackets the dominant kernel
 };
@@ -300,6 +308,15 @@ int fz_create(fz_ctx **out, int device)
             return FZ_EDEVICE;
         }
     }
+    bool ok = hipEventCreateWithFlags(&ctx->fork_ev, hipEventDisableTiming) == hipSuccess;
+    for (auto &e : ctx->join_ev) ok = ok && hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
+    // default priority, no implicit ordering with the null stream
+    for (auto &x : ctx->xs) ok = ok && hipStreamCreateWithFlags(&x, hipStreamNonBlocking) == hipSuccess;
+    if (!ok) {
+        (void)hipSetDevice(prev);
+        fz_destroy(ctx);
+        return FZ_EDEVICE;
+    }
     (void)hipSetDevice(prev);
     *out = ctx;
     return FZ_OK;
@@ -313,10 +330,19 @@ void fz_destroy(fz_ctx *ctx)
     (void)hipSetDevice(ctx->device);
     DevBuf *bufs[] = {&ctx->Tf, &ctx->Tr, &ctx->Qf, &ctx->Qr, &ctx->tasks, &ctx->info, &ctx->out,
                       &ctx->eager, &ctx->side_trace, &ctx->run_cap, &ctx->run_off, &ctx->run_len, &ctx->runs,
-                      &ctx->items, &ctx->batch_first, &ctx->scan_tmp, &ctx->cig, &ctx->cigar, &ctx->ptr_ws,
+                      &ctx->items, &ctx->batch_first, &ctx->scan_tmp, &ctx->cig, &ctx->cigar,
                       &ctx->counters, &ctx->ovl0, &ctx->ovl1, &ctx->bnd};
+    for (auto &x : ctx->xs)
+        if (x) (void)hipStreamSynchronize(x);
     for (DevBuf *b : bufs)
         if (b->p) (void)hipFree(b->p);
+    for (auto &b : ctx->ptr_ws)
+        if (b.p) (void)hipFree(b.p);
+    for (auto &x : ctx->xs)
+        if (x) (void)hipStreamDestroy(x);
+    if (ctx->fork_ev) (void)hipEventDestroy(ctx->fork_ev);
+    for (auto &e : ctx->join_ev)
+        if (e) (void)hipEventDestroy(e);
     for (auto &e : ctx->ev)
         if (e) (void)hipEventDestroy(e);
     for (auto &e : ctx->kev)
@@ -468,12 +494,15 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     if ((rc = read_counters())) return rc;
     const int64_t total_runs = hc.totals[0];
     uint32_t base[2 * NBINS];
-    int64_t n_exec = 0, n_exec0 = 0;
-    for (int cls = 0; cls < 2; ++cls)
+    // executor order: wide-window sides first (they are few and slow, so
+    // they overlap everything after them), then the standard ones, each
+    // class longest bins first
+    int64_t n_exec = 0, n_wide = 0;
+    for (int cls = 1; cls >= 0; --cls)
         for (int b = NBINS - 1; b >= 0; --b) {
             base[cls * NBINS + b] = (uint32_t)n_exec;
             n_exec += hc.bin_count[cls * NBINS + b];
-            if (cls == 0) n_exec0 = n_exec;
+            if (cls == 1) n_wide = n_exec;
             S.bin_hist[b] += hc.bin_count[cls * NBINS + b];
         }
     S.n_executor = (uint64_t)n_exec;
@@ -507,13 +536,16 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         if (cap == 0) {
             size_t fr = 0, tot = 0;
             HIP_OK(hipMemGetInfo(&fr, &tot));
-            cap = std::min<uint64_t>((uint64_t)fr / 4, (uint64_t)32 << 30);
+            cap = std::min<uint64_t>((uint64_t)fr / 4, (uint64_t)48 << 30);
         }
-        cap = std::max<uint64_t>(cap, (uint64_t)2 * (uint64_t)max_item + 4096);
-        const int64_t ws = std::min<int64_t>((int64_t)cap, total_ptr + 256);
+        // the cap covers all workspaces; each holds at least two of the
+        // largest sides
+        uint64_t cap1 = std::max<uint64_t>(cap / EXEC_STREAMS, (uint64_t)2 * (uint64_t)max_item + 4096);
+        const int64_t ws = std::min<int64_t>((int64_t)cap1, total_ptr + 256);
         const int64_t step = std::max<int64_t>(1, ws - max_item);
-        ENSURE(ctx->ptr_ws, ws);
         const int64_t nb = (total_ptr + step - 1) / step;
+        const int nbuf = (int)std::min<int64_t>(nb, EXEC_STREAMS);
+        for (int k = 0; k < nbuf; ++k) ENSURE(ctx->ptr_ws[k], ws);
         ENSURE(ctx->batch_first, (nb + 1) * sizeof(int64_t));
         fill_i64_kernel<<<blocks_for(nb + 1, 256), 256, 0, st>>>(as<int64_t>(ctx->batch_first), nb + 1, n_exec);
         HIP_OK(hipGetLastError());
@@ -528,37 +560,51 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         for (int64_t b = nb - 1; b >= 0; --b)
             if (first[(size_t)b] > first[(size_t)b + 1]) first[(size_t)b] = first[(size_t)b + 1];
         S.n_batches = (uint64_t)nb;
+        // batch b runs on stream b % nbuf with workspace b % nbuf; a
+        // workspace is reused only by later batches of its own stream
+        if (nbuf > 1) {
+            HIP_OK(hipEventRecord(ctx->fork_ev, st));
+            for (int k = 1; k < nbuf; ++k) HIP_OK(hipStreamWaitEvent(ctx->xs[k - 1], ctx->fork_ev, 0));
+        }
         for (int64_t b = 0; b < nb; ++b) {
             const int64_t lo = first[(size_t)b], hi = first[(size_t)b + 1];
             if (hi <= lo) continue;
-            const int64_t segs[2][2] = {{lo, std::min(hi, n_exec0)}, {std::max(lo, n_exec0), hi}};
-            for (int cls = 0; cls < 2; ++cls) {
+            const int kb = (int)(b % nbuf);
+            hipStream_t xst = kb == 0 ? st : ctx->xs[kb - 1];
+            uint8_t *wsp = as<uint8_t>(ctx->ptr_ws[kb]);
+            // class 1 (wide window) items come first in the list
+            const int64_t segs[2][2] = {{std::max(lo, n_wide), hi}, {lo, std::min(hi, n_wide)}};
+            for (int cls = 1; cls >= 0; --cls) {
                 const int64_t s0 = segs[cls][0], s1 = segs[cls][1];
                 if (s1 <= s0) continue;
                 ExtendArgs xa = ea;
                 xa.exec = as<ExecItem>(ctx->items);
                 xa.exec_begin = s0;
                 xa.nlist = (int32_t)(s1 - s0);
-                xa.ptr_ws = as<uint8_t>(ctx->ptr_ws);
+                xa.ptr_ws = wsp;
                 xa.ptr_base_off = b * step;
-                rc = cls == 0 ? launch_extend<C_STD, true>(ctx, xa, s1 - s0, st)
-                              : launch_extend<C_WIDE, true>(ctx, xa, s1 - s0, st);
+                rc = cls == 0 ? launch_extend<C_STD, true>(ctx, xa, s1 - s0, xst)
+                              : launch_extend<C_WIDE, true>(ctx, xa, s1 - s0, xst);
                 if (rc) return rc;
                 WalkArgs wk;
                 wk.items = as<ExecItem>(ctx->items);
                 wk.begin = s0;
                 wk.end = s1;
-                wk.ptr_ws = as<uint8_t>(ctx->ptr_ws);
+                wk.ptr_ws = wsp;
                 wk.ptr_base_off = b * step;
                 wk.C = cls == 0 ? C_STD : C_WIDE;
                 wk.out = as<SideOut>(ctx->out);
                 wk.run_off = as<int64_t>(ctx->run_off);
                 wk.runs = as<uint32_t>(ctx->runs);
                 wk.run_len = as<int64_t>(ctx->run_len);
-                if (cls == 0) walk_wave_kernel<C_STD><<<(unsigned)(s1 - s0), 64, 0, st>>>(wk);
-                else walk_wave_kernel<C_WIDE><<<(unsigned)(s1 - s0), 64, 0, st>>>(wk);
+                if (cls == 0) walk_wave_kernel<C_STD><<<(unsigned)(s1 - s0), 64, 0, xst>>>(wk);
+                else walk_wave_kernel<C_WIDE><<<(unsigned)(s1 - s0), 64, 0, xst>>>(wk);
                 HIP_OK(hipGetLastError());
             }
+        }
+        for (int k = 1; k < nbuf; ++k) {
+            HIP_OK(hipEventRecord(ctx->join_ev[k - 1], ctx->xs[k - 1]));
+            HIP_OK(hipStreamWaitEvent(st, ctx->join_ev[k - 1], 0));
         }
     }
     tm.mark();
