@@ -74,6 +74,7 @@ struct RowHdr {
 // A dword in the global address space (device memory): loads through it are
 // global_load instructions, which return in order.
 typedef __attribute__((address_space(1))) const uint32_t GlobalU32;
+typedef __attribute__((address_space(1))) const uint8_t GlobalU8;
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
@@ -126,13 +127,19 @@ __device__ __forceinline__ uint32_t ptr_src(uint32_t nib)
     return (nib & PTR_DIAG) ? 0u : ((nib & PTR_FROM_I) ? 1u : 2u);
 }
 
+// Maximum over the wave (every lane active), by DPP moves only: within
+// quads, then 8-lane halves, then 16-lane rows; then the row broadcasts
+// fold rows 0-1 into row 1, rows 2-3 into row 3 and rows 0-1 into rows
+// 2-3, leaving the wave's maximum in lane 63.
 __device__ __forceinline__ int wave_max(int v)
 {
-    for (int off = 32; off >= 1; off >>= 1) {
-        int o = __shfl_xor(v, off);
-        v = v > o ? v : o;
-    }
-    return v;
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false));   // row_mirror
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x142, 0xA, 0xF, false));   // row_bcast:15 -> rows 1, 3
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x143, 0xC, 0xF, false));   // row_bcast:31 -> rows 2, 3
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }

@@ -69,7 +69,8 @@ struct SideDP {
     uint32_t TA[NDW], QB[NDW];          // bases under this lane's slots on the current diagonal
     uint32_t TAn[NDW + 1], QBn[NDW + 1];// dwords fetched ahead for the next update of each sequence
     uint32_t shA, shB;                  // byte offset of those dwords
-    const uint8_t *pa, *pb;             // this lane's slot 0 at o_d = 0 (target) / o_d - d = 0 (query)
+    const GlobalU8 *ba, *bb;            // wave-uniform bases, below every byte a window can touch
+    uint32_t la, lb;                    // this lane's slot 0 from ba at o_d = 0 / from bb at o_d - d = 0
     // wave-uniform state
     int K, dmask;               // dmask: first d whose window reaches i > m or j > n
     int lo1, hi1, lo2, hi2;     // live hulls (positions) of d-1 and d-2
@@ -100,13 +101,14 @@ struct SideDP {
     // Sequence bytes.  Along the diagonals the target bytes under a lane move
     // by one every even d and the query bytes by one every odd d, so each
     // diagonal updates one sequence from dwords fetched two diagonals ahead.
-    __device__ __forceinline__ static void fetch(const uint8_t *p, uint32_t (&raw)[NDW + 1], uint32_t &sh)
+    // NDW + 1 dwords from base + (off rounded down to 4); sh = off % 4.
+    // base is wave-uniform and 4-aligned, off a per-lane 32-bit offset.
+    __device__ __forceinline__ static void fetch(const GlobalU8 *base, uint32_t off, uint32_t (&raw)[NDW + 1],
+                                                 uint32_t &sh)
     {
-        const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-        // global (not flat) loads: they complete in order, so the wait for a
-        // fetch does not also wait for the one issued after it
-        const GlobalU32 *w = reinterpret_cast<const GlobalU32 *>(a & ~(uintptr_t)3);
-        sh = (uint32_t)(a & 3);
+        // global (not flat) loads: they complete in order
+        const GlobalU32 *w = reinterpret_cast<const GlobalU32 *>(base + (off & ~3u));
+        sh = off & 3u;
 #pragma unroll
         for (int k = 0; k <= NDW; ++k) raw[k] = w[k];
     }
@@ -122,12 +124,12 @@ struct SideDP {
     __device__ __forceinline__ void reload(int d, int od)
     {
         uint32_t raw[NDW + 1], sh;
-        fetch(pa + od, raw, sh);
+        fetch(ba, la + od, raw, sh);
         align(raw, sh, TA);
-        fetch(pb + (od - d), raw, sh);
+        fetch(bb, lb + (od - d), raw, sh);
         align(raw, sh, QB);
-        fetch(pa + (od + 1), TAn, shA);         // next even diagonal
-        fetch(pb + (od - d - 1), QBn, shB);     // next odd diagonal
+        fetch(ba, la + (od + 1), TAn, shA);         // next even diagonal
+        fetch(bb, lb + (od - d - 1), QBn, shB);     // next odd diagonal
     }
 
     __device__ __forceinline__ void set_dmask()
@@ -159,6 +161,7 @@ struct SideDP {
         for (int k = 0; k < NWORD; ++k) word[k] = 0;
         dmax = NEG;
         int lm = 0;
+        const int mbase = MASKED ? lane * C - rlo : 0;
         int Rn[C], Dnn[C];
 #pragma unroll
         for (int c = 0; c < C; ++c) {
@@ -168,8 +171,9 @@ struct SideDP {
             int S = max(max(H, Iv), Dv);
             bool ok = S >= T;
             if (MASKED) {
-                const int pos = lane * C + c;
-                ok = ok && pos >= rlo && pos <= rhi;
+                // rlo <= lane*C + c <= rhi, from a per-diagonal base (no
+                // per-slot constants held across the loop)
+                ok = ok && (uint32_t)(mbase + c) <= (uint32_t)(rhi - rlo);
             }
             lm |= ok ? (1 << c) : 0;
             const int Sk = ok ? S : NEG;
@@ -232,10 +236,10 @@ struct SideDP {
         // refetches everything.)
         if (DELTA == 1) {
             align(TAn, shA, TA);
-            fetch(pa + (od + 1), TAn, shA);
+            fetch(ba, la + (od + 1), TAn, shA);
         } else {
             align(QBn, shB, QB);
-            fetch(pb + (od - d - 1), QBn, shB);
+            fetch(bb, lb + (od - d - 1), QBn, shB);
         }
         // R_d: cells with a possibly live predecessor (hulls of d-1 and d-2)
         int rlo = min(lo1 - DELTA, lo2);
@@ -354,8 +358,19 @@ struct SideDP {
         for (int c = 0; c < C; ++c) { SA[c] = NEG; SB[c] = NEG; R[c] = NEG; Dn[c] = NEG; }
         K = -W;
         set_dmask();
-        pa = t.A + (t.abase + lane * C);
-        pb = t.B + (t.bbase + lane * C);
+        // Window positions reach i = o_d + p with o_d >= -W and p < W, and
+        // j <= n + W, so every byte read lies at or above abase - W - 4 in
+        // A and bbase - n - W - 4 in B; the bases sit 4-aligned below that
+        // (inside the padding of the sequence arrays), and the per-lane
+        // offsets stay positive.
+        {
+            const int64_t aoff = (t.abase - W - 8) & ~(int64_t)3;
+            const int64_t boff = (t.bbase - (int64_t)t.n - W - 8) & ~(int64_t)3;
+            ba = reinterpret_cast<const GlobalU8 *>(reinterpret_cast<uintptr_t>(t.A + aoff));
+            bb = reinterpret_cast<const GlobalU8 *>(reinterpret_cast<uintptr_t>(t.B + boff));
+            la = (uint32_t)(t.abase - aoff) + (uint32_t)(lane * C);
+            lb = (uint32_t)(t.bbase - boff) + (uint32_t)(lane * C);
+        }
         // d = 0: the single cell (0,0), S = 0, I = D = -inf
         if (lane == P0 / C) {
             SA[0] = 0;
@@ -374,10 +389,10 @@ struct SideDP {
             // the target bytes set here; diagonal 2 takes TAn
             const int od1 = (1 + K) >> 1;
             uint32_t raw[NDW + 1], sh;
-            fetch(pa + od1, raw, sh);
+            fetch(ba, la + od1, raw, sh);
             align(raw, sh, TA);
-            fetch(pb + (od1 - 1), QBn, shB);
-            fetch(pa + (od1 + 1), TAn, shA);
+            fetch(bb, lb + (od1 - 1), QBn, shB);
+            fetch(ba, la + (od1 + 1), TAn, shA);
         }
         if (EXEC) {
             hdr = reinterpret_cast<RowHdr *>(ptr_base);
@@ -460,7 +475,7 @@ struct SideDP {
 // hands waves to CUs as others retire, which balances sides of very
 // different lengths).
 template <int C, bool EXEC, bool SMALL, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void extend_kernel(ExtendArgs a)
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <= 8 ? 6 : 1))) void extend_kernel(ExtendArgs a)
 {
     using DP = SideDP<C, EXEC, SMALL>;
     __shared__ uint32_t eager_lds_all[WAVES][EAGER_ROWS * DP::NEL * DP::NWORD];
