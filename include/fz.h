@@ -140,7 +140,8 @@ const char *fz_last_error(const fz_ctx *ctx);
 /* Cap (bytes) of the traceback-pointer workspace, shared by the executor's
  * streams (three workspaces of a third each, each at least twice the
  * largest side's pointer rows); the executor works in batches that fit.
- * 0 restores the default (1/4 of free device memory, at most 48 GiB). */
+ * 0 restores the default: 70% of the device memory free at the call, at
+ * most 200 GiB (allocated on first need and kept by the context). */
 int fz_set_pointer_workspace(fz_ctx *ctx, uint64_t bytes);
 
 /*

@@ -112,7 +112,7 @@ int ensure(fz_ctx *ctx, DevBuf &b, size_t bytes)
         b.p = nullptr;
         b.cap = 0;
     }
-    size_t want = bytes + bytes / 8;
+    size_t want = bytes + std::min<size_t>(bytes / 8, (size_t)1 << 30);   // room to grow, at most 1 GiB
     if (hipMalloc(&b.p, want) != hipSuccess) {
         (void)hipGetLastError();
         if (hipMalloc(&b.p, bytes) != hipSuccess) {
@@ -536,7 +536,12 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         if (cap == 0) {
             size_t fr = 0, tot = 0;
             HIP_OK(hipMemGetInfo(&fr, &tot));
-            cap = std::min<uint64_t>((uint64_t)fr / 4, (uint64_t)48 << 30);
+            // the context's own workspaces count as available
+            uint64_t avail = (uint64_t)fr;
+            for (const auto &b : ctx->ptr_ws) avail += b.cap;
+            // most of what is available: a batch lasts at least as long as
+            // its longest side, so fewer, larger batches finish sooner
+            cap = std::min<uint64_t>(avail / 10 * 7, (uint64_t)200 << 30);
         }
         // the cap covers all workspaces; each holds at least two of the
         // largest sides
