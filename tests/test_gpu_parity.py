@@ -436,3 +436,36 @@ def test_skewed_full_size_sampled(ctx):
     compare(gh, gc, oh, ow, oo, idx=idx, label="skewed full")
     assert not (gh[:, 1] & (fz.FZ_HIT_EBAND | fz.FZ_HIT_ERANGE | fz.FZ_HIT_ESEED)).any()
     check_invariants(w, gh, gc, "skewed full")
+
+
+def _full_size_sampled(ctx, w, n_sample, n_longest, label):
+    log("%s: %d records, target %d bp" % (label, len(w["seeds"]), w["target"].size))
+    gh, gc, st = run_gpu(ctx, w, min_tb=w.get("min_tb"))
+    log("%s: %d executor sides, %d batches, %.3g pointer bytes" % (label, st["n_executor"], st["n_batches"],
+                                                                   st["pointer_bytes"]))
+    rng = np.random.default_rng(0)
+    n = len(w["seeds"])
+    idx = rng.choice(n, min(n_sample, n), replace=False)
+    span = gh[:, 3] - gh[:, 2]
+    idx = np.unique(np.concatenate([idx, np.argsort(span)[-n_longest:]]))
+    oh, ow, oo = run_oracle(w, seeds=w["seeds"][idx], min_tb=w.get("min_tb"))
+    log("%s: oracle done on %d records" % (label, len(idx)))
+    compare(gh, gc, oh, ow, oo, idx=idx, label=label)
+    assert not (gh[:, 1] & (fz.FZ_HIT_EBAND | fz.FZ_HIT_ERANGE | fz.FZ_HIT_ESEED)).any(), label
+    check_invariants(w, gh, gc, label)
+
+
+@pytest.mark.skipif(os.environ.get("FZ_FULL_SIZE", "1") == "0", reason="full-size runs disabled")
+def test_executor_heavy_full_size_sampled(ctx):
+    """100,000 pairs of 1-20 kb homology, every seed traced: a seeded sample
+    and the longest alignments against the oracle, invariants on the rest."""
+    log("generating the executor-heavy batch")
+    _full_size_sampled(ctx, W.executor_heavy(), 40, 4, "executor heavy full")
+
+
+@pytest.mark.skipif(os.environ.get("FZ_FULL_SIZE", "1") == "0", reason="full-size runs disabled")
+def test_chromosome_full_size_sampled(ctx):
+    """Two 20 Mbp chromosomes, all forward shared 19-mers after diagonal
+    dedup: a seeded sample and the longest alignments against the oracle."""
+    log("generating the chromosome pair")
+    _full_size_sampled(ctx, W.chromosome(), 24, 4, "chromosome full")
