@@ -38,6 +38,26 @@ VALU_PEAK_OPS = N_CU * LANE_OPS_PER_CLK_PER_CU * CLOCK_HZ
 OPS_PER_CELL = {"extend": 13, "local": 12}
 
 
+# HBM traffic of one inspector launch on the 1M-seed skewed batch, from two
+# rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) scaled by what the same
+# counters read for a plain 1 GiB device copy in the same run (FETCH_SIZE
+# reads 0.5 GiB for it, WRITE_SIZE 1.0 GiB).  Valid only for the kernel
+# sources it was taken on (hash of fz_extend.hpp + fz_device.hpp); reported
+# as null otherwise.
+TRAFFIC_SRC_HASH = "8dedc7c554ff351e"
+TRAFFIC_FETCH_BYTES = 2.407e6 * 1024 / 0.5
+TRAFFIC_WRITE_BYTES = 4.10e5 * 1024 / 1.0
+
+
+def kernel_src_hash():
+    """sha256 over the two files' sha256 hex digests, first 16 hex digits."""
+    import hashlib
+    d = os.path.join(ROOT, "smith_waterman_dp_amd", "csrc")
+    digests = "".join(hashlib.sha256(open(os.path.join(d, f), "rb").read()).hexdigest()
+                      for f in ("fz_extend.hpp", "fz_device.hpp"))
+    return hashlib.sha256(digests.encode()).hexdigest()[:16]
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -47,6 +67,9 @@ def parse():
                     choices=["skewed", "local", "tiny", "executor_heavy", "chromosome"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="after the timed steps, one plain device-to-device copy of this many MiB "
+                         "(a known-size reference for HBM traffic counters)")
     return ap.parse_args()
 
 
@@ -131,6 +154,14 @@ def main():
         main_ms.append(st["ms_main"])
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    if a.copy_probe > 0:
+        src = torch.empty(a.copy_probe << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     h = hits.cpu().numpy()
     cells = int(h[:, 8].sum())
     n = len(w["seeds"])
@@ -140,6 +171,12 @@ def main():
     kern_s = float(np.mean(main_ms)) / 1e3
     achieved = ops * cells / kern_s / 1e12
     peak = VALU_PEAK_OPS / 1e12
+    traffic = None
+    if a.workload == "skewed" and kernel_src_hash() == TRAFFIC_SRC_HASH:
+        traffic = {"bytes_per_launch": int(TRAFFIC_FETCH_BYTES + TRAFFIC_WRITE_BYTES),
+                   "fetch_bytes": int(TRAFFIC_FETCH_BYTES), "write_bytes": int(TRAFFIC_WRITE_BYTES),
+                   "gb_per_s": round((TRAFFIC_FETCH_BYTES + TRAFFIC_WRITE_BYTES) / kern_s / 1e9, 2),
+                   "hbm_frac": round((TRAFFIC_FETCH_BYTES + TRAFFIC_WRITE_BYTES) / kern_s / 8e12, 5)}
     cfg = {"workload": a.workload, "records": n, "target_bp": int(w["target"].size), "query_bp": int(w["query"].size),
            "cells_per_step": cells, "scoring": w["scoring"], "ydrop": None if local else w["ydrop"],
            "min_traceback_score": w.get("min_tb"), "main_kernel_ms": round(kern_s * 1e3, 3)}
@@ -158,7 +195,7 @@ def main():
            "ms_per_step": round(ms_per_step, 3), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "int32", "data": "synthetic", "config": cfg,
            "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(peak, 3), "unit": "TOP/s",
-                        "frac": round(achieved / peak, 4), "traffic": None,
+                        "frac": round(achieved / peak, 4), "traffic": traffic,
                         "kernel": "local_kernel" if local else "extend_kernel (inspector)",
                         "ops_per_cell": ops}}
     if not a.no_cpu:
