@@ -76,6 +76,27 @@ struct RowHdr {
 typedef __attribute__((address_space(1))) const uint32_t GlobalU32;
 typedef __attribute__((address_space(1))) const uint8_t GlobalU8;
 
+// N dwords at any byte address in device memory, as one global load
+// (gfx9 and later serve unaligned global loads; the compiler emits a single
+// global_load_dword{,x2,x4} for these types).
+template <int N> struct Unaligned;
+template <> struct Unaligned<1> { typedef uint32_t T __attribute__((aligned(1))); };
+template <> struct Unaligned<2> { typedef uint32_t T __attribute__((ext_vector_type(2), aligned(1))); };
+template <> struct Unaligned<4> { typedef uint32_t T __attribute__((ext_vector_type(4), aligned(1))); };
+
+template <int N>
+__device__ __forceinline__ void load_unaligned(const GlobalU8 *p, uint32_t (&out)[N])
+{
+    typedef typename Unaligned<N>::T V;
+    const V v = *reinterpret_cast<const __attribute__((address_space(1))) V *>(p);
+    if constexpr (N == 1) {
+        out[0] = v;
+    } else {
+#pragma unroll
+        for (int k = 0; k < N; ++k) out[k] = v[k];
+    }
+}
+
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
 // Lane l receives lane l+1's value; lane 63 receives `fill`.

@@ -60,6 +60,7 @@ struct SideDP {
     static constexpr int EL1 = 32 + 8 / C;
     static constexpr int NEL = EL1 - EL0 + 1;
     static constexpr int NWORD = (C + 7) / 8;           // pointer words per lane per row (8 nibbles each)
+    static constexpr bool PAIRED = C == 3;              // narrow layout: two lanes per pointer dword
     // an empty live hull: far outside every window, so that the range of the
     // next diagonal comes out empty or from the other hull alone
     static constexpr int NONE_LO = 1 << 29, NONE_HI = -(1 << 29);
@@ -67,15 +68,17 @@ struct SideDP {
     // registers
     int SA[C], SB[C], R[C], Dn[C];
     uint32_t TA[NDW], QB[NDW];          // bases under this lane's slots on the current diagonal
-    uint32_t TAn[NDW + 1], QBn[NDW + 1];// dwords fetched ahead for the next update of each sequence
-    uint32_t shA, shB;                  // byte offset of those dwords
+    uint32_t TAn[NDW], QBn[NDW];        // fetched ahead for the next update of each sequence
     const GlobalU8 *ba, *bb;            // wave-uniform bases, below every byte a window can touch
     uint32_t la, lb;                    // this lane's slot 0 from ba at o_d = 0 / from bb at o_d - d = 0
     // wave-uniform state
     int K, dmask;               // dmask: first d whose window reaches i > m or j > n
     int lo1, hi1, lo2, hi2;     // live hulls (positions) of d-1 and d-2
     int best, bi, bj, dend;
-    int64_t cells, cum_bytes, ptr_at_best;
+    int T;                      // y-drop threshold of the next diagonal
+    int64_t cells, cum_bytes, ptr_at_best;  // totals up to diagonal dflush
+    int dflush;
+    int32_t acc_cells, acc_words;   // since dflush: sum of (|R_d| - 1), of (row words - NWORD)
     bool overflow;
     // executor
     uint32_t rowoff, rowcap;    // rows written / rows the inspector sized
@@ -84,7 +87,7 @@ struct SideDP {
 
     const SideTask &t;
     const Scoring &sc;
-    const int lane;
+    int lane;
 
     __device__ SideDP(const SideTask &task, const Scoring &s) : t(task), sc(s), lane(lane_id()) {}
 
@@ -101,35 +104,22 @@ struct SideDP {
     // Sequence bytes.  Along the diagonals the target bytes under a lane move
     // by one every even d and the query bytes by one every odd d, so each
     // diagonal updates one sequence from dwords fetched two diagonals ahead.
-    // NDW + 1 dwords from base + (off rounded down to 4); sh = off % 4.
-    // base is wave-uniform and 4-aligned, off a per-lane 32-bit offset.
-    __device__ __forceinline__ static void fetch(const GlobalU8 *base, uint32_t off, uint32_t (&raw)[NDW + 1],
-                                                 uint32_t &sh)
+    // NDW dwords from base + off (any byte offset: one unaligned global
+    // load, which also completes in order); base is wave-uniform, off a
+    // per-lane 32-bit offset.
+    __device__ __forceinline__ static void fetch(const GlobalU8 *base, uint32_t off, uint32_t (&out)[NDW])
     {
-        // global (not flat) loads: they complete in order
-        const GlobalU32 *w = reinterpret_cast<const GlobalU32 *>(base + (off & ~3u));
-        sh = off & 3u;
-#pragma unroll
-        for (int k = 0; k <= NDW; ++k) raw[k] = w[k];
-    }
-
-    __device__ __forceinline__ static void align(const uint32_t (&raw)[NDW + 1], uint32_t sh, uint32_t (&out)[NDW])
-    {
-#pragma unroll
-        for (int k = 0; k < NDW; ++k) out[k] = __builtin_amdgcn_alignbyte(raw[k + 1], raw[k], sh);
+        load_unaligned<NDW>(base + off, out);
     }
 
     // After a slide: this diagonal's bases at the new offset, and the
     // fetches for the next update of each sequence.
     __device__ __forceinline__ void reload(int d, int od)
     {
-        uint32_t raw[NDW + 1], sh;
-        fetch(ba, la + od, raw, sh);
-        align(raw, sh, TA);
-        fetch(bb, lb + (od - d), raw, sh);
-        align(raw, sh, QB);
-        fetch(ba, la + (od + 1), TAn, shA);         // next even diagonal
-        fetch(bb, lb + (od - d - 1), QBn, shB);     // next odd diagonal
+        fetch(ba, la + od, TA);
+        fetch(bb, lb + (od - d), QB);
+        fetch(ba, la + (od + 1), TAn);          // next even diagonal
+        fetch(bb, lb + (od - d - 1), QBn);      // next odd diagonal
     }
 
     __device__ __forceinline__ void set_dmask()
@@ -235,17 +225,21 @@ struct SideDP {
         // work separates each fetch from its first use.  (A slide below
         // refetches everything.)
         if (DELTA == 1) {
-            align(TAn, shA, TA);
-            fetch(ba, la + (od + 1), TAn, shA);
+#pragma unroll
+            for (int k = 0; k < NDW; ++k) TA[k] = TAn[k];
+            fetch(ba, la + (od + 1), TAn);
         } else {
-            align(QBn, shB, QB);
-            fetch(bb, lb + (od - d - 1), QBn, shB);
+#pragma unroll
+            for (int k = 0; k < NDW; ++k) QB[k] = QBn[k];
+            fetch(bb, lb + (od - d - 1), QBn);
         }
         // R_d: cells with a possibly live predecessor (hulls of d-1 and d-2)
         int rlo = min(lo1 - DELTA, lo2);
         int rhi = max(hi1 - DELTA + 1, hi2);
         bool masked = false;
-        if (!(d < dmask && rlo >= 0 && rhi <= W - 1 && rlo <= rhi)) {
+        // fast path: d < dmask and 0 <= rlo <= rhi <= W - 1, i.e. four
+        // terms that are all non-negative (one sign test)
+        if (((dmask - 1 - d) | rlo | (W - 1 - rhi) | (rhi - rlo)) < 0) {
             // Near a matrix edge, an empty range, or the band at a window
             // edge.  (Elsewhere R_d needs no clipping: its cells have
             // 0 <= i <= d by construction and the window lies inside
@@ -278,8 +272,6 @@ struct SideDP {
             // see -inf)
             masked = (W - 1 + od > t.m) || (d - od > t.n);
         }
-        const int T = max(best - sc.ydrop, T_FLOOR);
-
         int lm, dmax;
         uint32_t word[NWORD];
         // (the uniform branch keeps the range test out of the common path)
@@ -302,9 +294,15 @@ struct SideDP {
             lo = llo * C + __builtin_ctz(mlo);
             hi = lhi * C + (31 - __builtin_clz(mhi));
         }
-        cells += rhi - rlo + 1;
-        const int nl = lhi - llo + 1;
-        cum_bytes += 8 + 4 * (int64_t)nl * NWORD;
+        // Σ|R_d| and the pointer-row sizes, as 32-bit sums that flush()
+        // folds into the totals (the per-diagonal constants are added there)
+        acc_cells += rhi - rlo;
+        // pointer row: the lanes of the live hull; with C = 3, lane pairs
+        // share a dword so that rows keep the six-cells-per-dword format
+        const int rlane0 = PAIRED ? (llo & ~1) : llo;
+        const int nl1 = PAIRED ? (lhi >> 1) - (llo >> 1) : lhi - llo;     // row words / NWORD - 1
+        const int nl = (nl1 + 1) * NWORD;
+        if (!EXEC) acc_words += nl1;
 
         if (ballot(dmax > best)) {
             const int nb = uniform(wave_max(dmax));
@@ -317,13 +315,15 @@ struct SideDP {
                 if (m) pbest = min(pbest, ctz64(m) * C + c);
             }
             best = nb;
+            T = max(best - sc.ydrop, T_FLOOR);
             bi = pbest + od;
             bj = d - bi;
-            ptr_at_best = cum_bytes;
+            const int n = d - dflush;
+            ptr_at_best = cum_bytes + 8 * (int64_t)n + 4 * NWORD * ((int64_t)acc_words + n);
         }
 
         if (EXEC) {
-            if (rowoff + (uint32_t)(nl * NWORD) > rowcap) {
+            if (rowoff + (uint32_t)nl > rowcap) {
                 // the recompute disagrees with the inspector's sizing
                 overflow = true;
                 return false;
@@ -331,14 +331,19 @@ struct SideDP {
             if (lane == 0) {
                 RowHdr h;
                 h.off = rowoff;
-                h.ibase = llo * C + od;
+                h.ibase = rlane0 * C + od;
                 hdr[d] = h;
             }
-            if (lane >= llo && lane <= lhi) {
+            if (PAIRED) {
+                // the odd lane's three nibbles go under the even lane's
+                const uint32_t odd = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word[0], 0xB1, 0xF, 0xF, false);
+                if (!(lane & 1) && lane >= rlane0 && lane <= lhi)
+                    rows[rowoff + ((lane - rlane0) >> 1)] = (word[0] << 12) | odd;
+            } else if (lane >= llo && lane <= lhi) {
 #pragma unroll
                 for (int k = 0; k < NWORD; ++k) rows[rowoff + (lane - llo) * NWORD + k] = word[k];
             }
-            rowoff += (uint32_t)(nl * NWORD);
+            rowoff += (uint32_t)nl;
         } else if (PTR) {
             if (lane >= EL0 && lane <= EL1) {
 #pragma unroll
@@ -352,25 +357,45 @@ struct SideDP {
         return true;
     }
 
-    __device__ void run(int dstop, uint32_t *eager_lds, uint8_t *ptr_base, int64_t ptr_bytes = 0)
+    // Fold the 32-bit sums of the diagonals after dflush, up to dend, into
+    // the totals.
+    __device__ __forceinline__ void flush()
+    {
+        const int n = dend - dflush;
+        cells += (int64_t)acc_cells + n;
+        cum_bytes += 8 * (int64_t)n + 4 * NWORD * ((int64_t)acc_words + n);
+        acc_cells = 0;
+        acc_words = 0;
+        dflush = dend;
+    }
+
+    // Bases of the sequence arrays for this layout.  Window positions reach
+    // i = o_d + p with o_d >= -W and p < W, and j <= n + W, so every byte
+    // read lies at or above abase - W - 4 in A and bbase - n - W - 4 in B;
+    // the bases sit 4-aligned below that (inside the padding of the
+    // sequence arrays), and the per-lane offsets stay positive.
+    __device__ __forceinline__ void init_bases()
+    {
+        const int64_t aoff = (t.abase - W - 8) & ~(int64_t)3;
+        const int64_t boff = (t.bbase - (int64_t)t.n - W - 8) & ~(int64_t)3;
+        ba = reinterpret_cast<const GlobalU8 *>(reinterpret_cast<uintptr_t>(t.A + aoff));
+        bb = reinterpret_cast<const GlobalU8 *>(reinterpret_cast<uintptr_t>(t.B + boff));
+        la = (uint32_t)(t.abase - aoff) + (uint32_t)(lane * C);
+        lb = (uint32_t)(t.bbase - boff) + (uint32_t)(lane * C);
+        // computed afresh at every change of layout, not held in registers
+        // (or spilled) while the other layout runs
+        asm volatile("" : "+v"(la), "+v"(lb));
+    }
+
+    // d = 0 and, in the inspector, the eager diagonals 1..32.  Returns the
+    // next diagonal, or -1 when the extension is over.
+    __device__ int start(int dstop, uint32_t *eager_lds, uint8_t *ptr_base, int64_t ptr_bytes)
     {
 #pragma unroll
         for (int c = 0; c < C; ++c) { SA[c] = NEG; SB[c] = NEG; R[c] = NEG; Dn[c] = NEG; }
         K = -W;
         set_dmask();
-        // Window positions reach i = o_d + p with o_d >= -W and p < W, and
-        // j <= n + W, so every byte read lies at or above abase - W - 4 in
-        // A and bbase - n - W - 4 in B; the bases sit 4-aligned below that
-        // (inside the padding of the sequence arrays), and the per-lane
-        // offsets stay positive.
-        {
-            const int64_t aoff = (t.abase - W - 8) & ~(int64_t)3;
-            const int64_t boff = (t.bbase - (int64_t)t.n - W - 8) & ~(int64_t)3;
-            ba = reinterpret_cast<const GlobalU8 *>(reinterpret_cast<uintptr_t>(t.A + aoff));
-            bb = reinterpret_cast<const GlobalU8 *>(reinterpret_cast<uintptr_t>(t.B + boff));
-            la = (uint32_t)(t.abase - aoff) + (uint32_t)(lane * C);
-            lb = (uint32_t)(t.bbase - boff) + (uint32_t)(lane * C);
-        }
+        init_bases();
         // d = 0: the single cell (0,0), S = 0, I = D = -inf
         if (lane == P0 / C) {
             SA[0] = 0;
@@ -379,20 +404,20 @@ struct SideDP {
         }
         lo1 = P0; hi1 = P0; lo2 = NONE_LO; hi2 = NONE_HI;
         best = 0; bi = 0; bj = 0; dend = 0;
+        T = max(-sc.ydrop, T_FLOOR);
         cells = 1;
         cum_bytes = 8 + 4 * NWORD;
         ptr_at_best = cum_bytes;
+        dflush = 0; acc_cells = 0; acc_words = 0;
         overflow = false;
         rowoff = 0;
         {
             // diagonal 1 is odd: it takes its query bytes from QBn and keeps
             // the target bytes set here; diagonal 2 takes TAn
             const int od1 = (1 + K) >> 1;
-            uint32_t raw[NDW + 1], sh;
-            fetch(ba, la + od1, raw, sh);
-            align(raw, sh, TA);
-            fetch(bb, lb + (od1 - 1), QBn, shB);
-            fetch(ba, la + (od1 + 1), TAn, shA);
+            fetch(ba, la + od1, TA);
+            fetch(bb, lb + (od1 - 1), QBn);
+            fetch(ba, la + (od1 + 1), TAn);
         }
         if (EXEC) {
             hdr = reinterpret_cast<RowHdr *>(ptr_base);
@@ -409,24 +434,128 @@ struct SideDP {
             }
             rowoff = NWORD;
             rowcap = (uint32_t)((ptr_bytes - 8 * ((int64_t)dstop + 1)) / 4);
-        } else {
-            if (lane >= EL0 && lane <= EL1) {
-#pragma unroll
-                for (int k = 0; k < NWORD; ++k) eager_lds[(lane - EL0) * NWORD + k] = 0u;
-            }
+            return 1;
         }
+        if (lane >= EL0 && lane <= EL1) {
+#pragma unroll
+            for (int k = 0; k < NWORD; ++k) eager_lds[(lane - EL0) * NWORD + k] = 0u;
+        }
+        // diagonals 1..32 keep pointers for the eager block
         int d = 1;
-        if (!EXEC) {
-            // diagonals 1..32 keep pointers for the eager block
-            for (; d <= EAGER_ROWS - 1; d += 2) {
-                if (!step<0, true>(d, dstop, eager_lds)) return;
-                if (!step<1, true>(d + 1, dstop, eager_lds)) return;
-            }
+        for (; d <= EAGER_ROWS - 1; d += 2) {
+            if (!step<0, true>(d, dstop, eager_lds)) return -1;
+            if (!step<1, true>(d + 1, dstop, eager_lds)) return -1;
+        }
+        return d;
+    }
+
+    // Width of the union of the live hulls of the last two diagonals (the
+    // next range is at most 3 wider), or -1 when both are empty.
+    __device__ __forceinline__ int hull_width() const
+    {
+        const int ul = min(lo1, lo2), uh = max(hi1, hi2);
+        return ul <= uh ? uh - ul : -1;
+    }
+
+    // Layout switches (standard kernel only): a side whose band has
+    // narrowed moves to the 192-position layout, and back when it widens.
+    // The test runs every 8 diagonals.  Each diagonal widens the union by at
+    // most 2, so a band that passed the test at width <= 172 keeps every
+    // range within 172 + 2*8 = 188 <= W - C positions until the next test,
+    // which always fits the 192-position window (slides go by whole lanes).
+    static constexpr int SWITCH_EVERY = 8;
+    static constexpr int NARROW_FROM_D = 256;
+    static constexpr int NARROW_ENTER = 157;     // union hull width to enter the narrow layout
+    static constexpr int NARROW_LEAVE = 172;     // ... and to leave it
+
+    template <bool SWITCHABLE>
+    __device__ __forceinline__ bool want_switch(int d) const
+    {
+        if (!SWITCHABLE) return false;
+        const int w = hull_width();
+        if (C == 6) return d >= NARROW_FROM_D && w >= 0 && w <= NARROW_ENTER;
+        return w > NARROW_LEAVE;
+    }
+
+    // Diagonals from d on until the extension ends (returns -1) or, with
+    // SWITCHABLE, the band calls for the other layout (returns the next d).
+    template <bool SWITCHABLE>
+    __device__ int advance(int d, int dstop, uint32_t *eager_lds)
+    {
+        if (SWITCHABLE) {
+            // lane-derived constants of this layout are formed here, inside
+            // the layout's own run, not once for the whole side (where both
+            // layouts' sets would occupy registers at the same time)
+            asm volatile("" : "+v"(lane));
+        }
+        if (d & 1) {
+            if (!step<0, EXEC>(d, dstop, eager_lds)) return -1;
+            ++d;
         }
         for (;; d += 2) {
-            if (!step<0, EXEC>(d, dstop, eager_lds)) break;
-            if (!step<1, EXEC>(d + 1, dstop, eager_lds)) break;
+            if (!step<1, EXEC>(d, dstop, eager_lds)) return -1;
+            if (!step<0, EXEC>(d + 1, dstop, eager_lds)) return -1;
+            if (((d + 1) & (SWITCH_EVERY - 1)) == SWITCH_EVERY - 1) {
+                flush();
+                if (want_switch<SWITCHABLE>(d + 1)) return d + 2;
+            }
         }
+    }
+
+    // Lane registers by position, for a change of layout.  Only the union
+    // [ul, uh] of the last two live hulls is handed over: elsewhere S is
+    // -inf, and the handed-on gap values come from dead cells, which lie
+    // below the threshold and act as -inf (see the top of this file).  x
+    // holds four arrays of XFER_W entries, indexed by position - ul.
+    static constexpr int XFER_W = 192;
+    __device__ __forceinline__ void export_regs(uint32_t *x, int ul, int uh) const
+    {
+        // (an opaque base keeps per-slot position constants from being
+        // computed once and held in registers through the whole side)
+        int q0 = lane * C - ul;
+        asm volatile("" : "+v"(q0));
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int q = q0 + c;
+            if ((uint32_t)q <= (uint32_t)(uh - ul)) {
+                x[q] = (uint32_t)SA[c];
+                x[XFER_W + q] = (uint32_t)SB[c];
+                x[2 * XFER_W + q] = (uint32_t)R[c];
+                x[3 * XFER_W + q] = (uint32_t)Dn[c];
+            }
+        }
+    }
+
+    // Take over from a side run in another layout after its diagonal dlast:
+    // position q here is position q + s there (o_d grows by s for every d,
+    // which keeps K even).
+    template <class O>
+    __device__ __forceinline__ void adopt(const O &o, int s, const uint32_t *x, int ul, int uh, int dlast)
+    {
+        int q0 = lane * C + s - ul;
+        asm volatile("" : "+v"(q0));
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const bool in = (uint32_t)(q0 + c) <= (uint32_t)(uh - ul);
+            const int q = in ? q0 + c : 0;
+            SA[c] = in ? (int)x[q] : NEG;
+            SB[c] = in ? (int)x[XFER_W + q] : NEG;
+            R[c] = in ? (int)x[2 * XFER_W + q] : NEG;
+            Dn[c] = in ? (int)x[3 * XFER_W + q] : NEG;
+        }
+        auto mlo = [&](int v) { return v == NONE_LO ? v : v - s; };
+        auto mhi = [&](int v) { return v == NONE_HI ? v : v - s; };
+        K = o.K + 2 * s;
+        lo1 = mlo(o.lo1); hi1 = mhi(o.hi1);
+        lo2 = mlo(o.lo2); hi2 = mhi(o.hi2);
+        best = o.best; bi = o.bi; bj = o.bj; dend = o.dend; T = o.T;
+        cells = o.cells; cum_bytes = o.cum_bytes; ptr_at_best = o.ptr_at_best;
+        dflush = o.dflush; acc_cells = 0; acc_words = 0;        // (the other side flushed)
+        overflow = o.overflow;
+        rowoff = o.rowoff; rowcap = o.rowcap; hdr = o.hdr; rows = o.rows;
+        set_dmask();
+        init_bases();
+        reload(dlast, (dlast + K) >> 1);
     }
 
     // Walk the eager block from (bi, bj).  The whole wave walks in step (the
@@ -471,6 +600,76 @@ struct SideDP {
     }
 };
 
+// What a side's extension reports, from whichever layout finished it.
+struct SideResult {
+    int best, bi, bj, dend;
+    int64_t cells, ptr_at_best;
+    bool overflow;
+    template <class DP>
+    __device__ __forceinline__ void take(DP &dp)
+    {
+        dp.flush();
+        best = dp.best; bi = dp.bi; bj = dp.bj; dend = dp.dend;
+        cells = dp.cells; ptr_at_best = dp.ptr_at_best;
+        overflow = dp.overflow;
+    }
+};
+
+// Move a side between layouts after diagonal d - 1: the union of its last
+// two hulls is centred in the new window.
+template <class TO, class FROM>
+__device__ __forceinline__ void switch_layout(TO &to, FROM &from, uint32_t *x, int d)
+{
+    from.flush();
+    const int ul = min(from.lo1, from.lo2), uh = max(from.hi1, from.hi2);
+    const int s = ((ul + uh) >> 1) - TO::W / 2;
+    from.export_regs(x, ul, uh);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    to.adopt(from, s, x, ul, uh, d - 1);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// One side, start to end.  In the 384-position layout a side whose band has
+// narrowed continues in a 192-position layout (three cells per lane, about
+// half the work per diagonal) and returns when the band widens again; the
+// executor makes the same moves as the inspector, since they depend only on
+// the hulls.
+template <int C, bool EXEC, bool SMALL>
+__device__ __forceinline__ SideResult run_side(const SideTask &task, const Scoring &sc, int dstop, uint32_t *eager_lds,
+                                               uint32_t *xfer, uint8_t *ptr_base, int64_t ptr_bytes,
+                                               SideDP<C, EXEC, SMALL> &dp)
+{
+    SideResult r;
+    int d = dp.start(dstop, eager_lds, ptr_base, ptr_bytes);
+    if (C != 6) {
+        if (d >= 0) dp.template advance<false>(d, dstop, eager_lds);
+        r.take(dp);
+        return r;
+    }
+    using DN = SideDP<3, EXEC, SMALL>;
+    DN dn(task, sc);
+    if (d < 0) {
+        r.take(dp);
+        return r;
+    }
+    for (;;) {
+        d = dp.template advance<true>(d, dstop, eager_lds);
+        if (d < 0) {
+            r.take(dp);
+            return r;
+        }
+        switch_layout(dn, dp, xfer, d);
+        d = dn.template advance<true>(d, dstop, eager_lds);
+        if (d < 0) {
+            r.take(dn);
+            return r;
+        }
+        switch_layout(dp, dn, xfer, d);
+    }
+}
+
 // One wave per side; the grid covers the work list (the hardware dispatcher
 // hands waves to CUs as others retire, which balances sides of very
 // different lengths).
@@ -479,8 +678,10 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <=
 {
     using DP = SideDP<C, EXEC, SMALL>;
     __shared__ uint32_t eager_lds_all[WAVES][EAGER_ROWS * DP::NEL * DP::NWORD];
+    __shared__ uint32_t xfer_all[WAVES][C == 6 ? 4 * DP::XFER_W : 1];
     const int wv = uniform((int)(threadIdx.x / 64));
     uint32_t *eager_lds = eager_lds_all[wv];
+    uint32_t *xfer = xfer_all[wv];
     const int lane = lane_id();
     const int idx = (int)blockIdx.x * WAVES + wv;
     if (idx >= a.nlist) return;
@@ -499,31 +700,36 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <=
     DP dp(task, a.sc);
     if (EXEC) {
         const ExecItem it = a.exec[item];
-        dp.run(it.dstar, nullptr, a.ptr_ws + (it.ptr_off - a.ptr_base_off), it.ptr_bytes);
+        const SideResult x = run_side<C, EXEC, SMALL>(task, a.sc, it.dstar, nullptr, xfer,
+                                                      a.ptr_ws + (it.ptr_off - a.ptr_base_off), it.ptr_bytes, dp);
         if (lane == 0) {
-            atomicAdd((unsigned long long *)a.exec_cells, (unsigned long long)dp.cells);
-            if (dp.overflow || dp.best != o->score || dp.bi != o->ie) atomicOr(&o->flags, SO_EXEC_MISMATCH);
+            atomicAdd((unsigned long long *)a.exec_cells, (unsigned long long)x.cells);
+            if (x.overflow || x.best != o->score || x.bi != o->ie) atomicOr(&o->flags, SO_EXEC_MISMATCH);
         }
         return;
     }
-    dp.run(0x7fffffff, eager_lds, nullptr);
+    const SideResult x = run_side<C, EXEC, SMALL>(task, a.sc, 0x7fffffff, eager_lds, xfer, nullptr, 0, dp);
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     SideOut r;
-    r.score = dp.best;
-    r.ie = dp.bi;
-    r.je = dp.bj;
-    r.dend = dp.dend;
-    r.cells = dp.cells;
-    r.ptr_bytes = dp.ptr_at_best;
-    r.flags = (dp.overflow ? SO_OVERFLOW : 0) | a.result_flags;
+    r.score = x.best;
+    r.ie = x.bi;
+    r.je = x.bj;
+    r.dend = x.dend;
+    r.cells = x.cells;
+    r.ptr_bytes = x.ptr_at_best;
+    r.flags = (x.overflow ? SO_OVERFLOW : 0) | a.result_flags;
     r.eager_len = 0;
-    if (!dp.overflow && dp.bi <= EAGER_EDGE && dp.bj <= EAGER_EDGE) {
+    if (!x.overflow && x.bi <= EAGER_EDGE && x.bj <= EAGER_EDGE) {
+        // the best cell lies in the eager block, which the 384-position
+        // layout kept (no layout change happens before diagonal 33)
+        dp.bi = x.bi;
+        dp.bj = x.bj;
         r.flags |= SO_EAGER;
         r.eager_len = dp.eager_walk(eager_lds, a.eager_ops + (int64_t)sid * EAGER_OPS);
     }
     if (lane == 0) {
         *o = r;
-        if (dp.overflow) {
+        if (x.overflow) {
             const uint32_t k = atomicAdd(a.overflow_count, 1u);
             a.overflow_list[k] = sid;
         }
