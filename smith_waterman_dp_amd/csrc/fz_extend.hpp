@@ -70,7 +70,7 @@ struct SideDP {
     uint32_t TA[NDW], QB[NDW];          // bases under this lane's slots on the current diagonal
     uint32_t TAn[NDW], QBn[NDW];        // fetched ahead for the next update of each sequence
     const GlobalU8 *ba, *bb;            // wave-uniform bases, below every byte a window can touch
-    uint32_t la, lb;                    // this lane's slot 0 from ba at o_d = 0 / from bb at o_d - d = 0
+    uint32_t ua, ub;                    // offset of slot 0 of lane 0 from ba at o_d = 0 / from bb at o_d - d = 0
     // wave-uniform state
     int K, dmask;               // dmask: first d whose window reaches i > m or j > n
     int lo1, hi1, lo2, hi2;     // live hulls (positions) of d-1 and d-2
@@ -104,22 +104,22 @@ struct SideDP {
     // Sequence bytes.  Along the diagonals the target bytes under a lane move
     // by one every even d and the query bytes by one every odd d, so each
     // diagonal updates one sequence from dwords fetched two diagonals ahead.
-    // NDW dwords from base + off (any byte offset: one unaligned global
-    // load, which also completes in order); base is wave-uniform, off a
-    // per-lane 32-bit offset.
-    __device__ __forceinline__ static void fetch(const GlobalU8 *base, uint32_t off, uint32_t (&out)[NDW])
+    // NDW dwords from base + off + this lane's first slot (any byte offset:
+    // one unaligned global load, which also completes in order); base and
+    // off are wave-uniform.
+    __device__ __forceinline__ void fetch(const GlobalU8 *base, uint32_t off, uint32_t (&out)[NDW]) const
     {
-        load_unaligned<NDW>(base + off, out);
+        load_unaligned<NDW>(base + (off + (uint32_t)(lane * C)), out);
     }
 
     // After a slide: this diagonal's bases at the new offset, and the
     // fetches for the next update of each sequence.
     __device__ __forceinline__ void reload(int d, int od)
     {
-        fetch(ba, la + od, TA);
-        fetch(bb, lb + (od - d), QB);
-        fetch(ba, la + (od + 1), TAn);          // next even diagonal
-        fetch(bb, lb + (od - d - 1), QBn);      // next odd diagonal
+        fetch(ba, ua + od, TA);
+        fetch(bb, ub + (od - d), QB);
+        fetch(ba, ua + (od + 1), TAn);          // next even diagonal
+        fetch(bb, ub + (od - d - 1), QBn);      // next odd diagonal
     }
 
     __device__ __forceinline__ void set_dmask()
@@ -227,11 +227,11 @@ struct SideDP {
         if (DELTA == 1) {
 #pragma unroll
             for (int k = 0; k < NDW; ++k) TA[k] = TAn[k];
-            fetch(ba, la + (od + 1), TAn);
+            fetch(ba, ua + (od + 1), TAn);
         } else {
 #pragma unroll
             for (int k = 0; k < NDW; ++k) QB[k] = QBn[k];
-            fetch(bb, lb + (od - d - 1), QBn);
+            fetch(bb, ub + (od - d - 1), QBn);
         }
         // R_d: cells with a possibly live predecessor (hulls of d-1 and d-2)
         int rlo = min(lo1 - DELTA, lo2);
@@ -380,15 +380,13 @@ struct SideDP {
         const int64_t boff = (t.bbase - (int64_t)t.n - W - 8) & ~(int64_t)3;
         ba = reinterpret_cast<const GlobalU8 *>(reinterpret_cast<uintptr_t>(t.A + aoff));
         bb = reinterpret_cast<const GlobalU8 *>(reinterpret_cast<uintptr_t>(t.B + boff));
-        la = (uint32_t)(t.abase - aoff) + (uint32_t)(lane * C);
-        lb = (uint32_t)(t.bbase - boff) + (uint32_t)(lane * C);
-        // computed afresh at every change of layout, not held in registers
-        // (or spilled) while the other layout runs
-        asm volatile("" : "+v"(la), "+v"(lb));
+        ua = (uint32_t)(t.abase - aoff);
+        ub = (uint32_t)(t.bbase - boff);
     }
 
-    // d = 0 and, in the inspector, the eager diagonals 1..32.  Returns the
-    // next diagonal, or -1 when the extension is over.
+    // d = 0 and diagonal 1 (the executor), or diagonals 0..33 with the eager
+    // pointers of 1..32 (the inspector).  Returns the next diagonal, which is
+    // even, or -1 when the extension is over.
     __device__ int start(int dstop, uint32_t *eager_lds, uint8_t *ptr_base, int64_t ptr_bytes)
     {
 #pragma unroll
@@ -415,9 +413,9 @@ struct SideDP {
             // diagonal 1 is odd: it takes its query bytes from QBn and keeps
             // the target bytes set here; diagonal 2 takes TAn
             const int od1 = (1 + K) >> 1;
-            fetch(ba, la + od1, TA);
-            fetch(bb, lb + (od1 - 1), QBn);
-            fetch(ba, la + (od1 + 1), TAn);
+            fetch(ba, ua + od1, TA);
+            fetch(bb, ub + (od1 - 1), QBn);
+            fetch(ba, ua + (od1 + 1), TAn);
         }
         if (EXEC) {
             hdr = reinterpret_cast<RowHdr *>(ptr_base);
@@ -434,7 +432,7 @@ struct SideDP {
             }
             rowoff = NWORD;
             rowcap = (uint32_t)((ptr_bytes - 8 * ((int64_t)dstop + 1)) / 4);
-            return 1;
+            return step<0, EXEC>(1, dstop, eager_lds) ? 2 : -1;
         }
         if (lane >= EL0 && lane <= EL1) {
 #pragma unroll
@@ -446,7 +444,7 @@ struct SideDP {
             if (!step<0, true>(d, dstop, eager_lds)) return -1;
             if (!step<1, true>(d + 1, dstop, eager_lds)) return -1;
         }
-        return d;
+        return step<0, false>(d, dstop, eager_lds) ? d + 1 : -1;
     }
 
     // Width of the union of the live hulls of the last two diagonals (the
@@ -457,8 +455,9 @@ struct SideDP {
         return ul <= uh ? uh - ul : -1;
     }
 
-    // Layout switches (standard kernel only): a side whose band has
-    // narrowed moves to the 192-position layout, and back when it widens.
+    // Layout switches (standard kernel only): a side in the 192-position
+    // layout moves to the 384-position one when its band widens, and back
+    // when it narrows again.
     // The test runs every 8 diagonals.  Each diagonal widens the union by at
     // most 2, so a band that passed the test at width <= 172 keeps every
     // range within 172 + 2*8 = 188 <= W - C positions until the next test,
@@ -477,8 +476,9 @@ struct SideDP {
         return w > NARROW_LEAVE;
     }
 
-    // Diagonals from d on until the extension ends (returns -1) or, with
-    // SWITCHABLE, the band calls for the other layout (returns the next d).
+    // Diagonals from d (even) on until the extension ends (returns -1) or,
+    // with SWITCHABLE, the band calls for the other layout (returns the next
+    // d, again even).
     template <bool SWITCHABLE>
     __device__ int advance(int d, int dstop, uint32_t *eager_lds)
     {
@@ -487,10 +487,6 @@ struct SideDP {
             // the layout's own run, not once for the whole side (where both
             // layouts' sets would occupy registers at the same time)
             asm volatile("" : "+v"(lane));
-        }
-        if (d & 1) {
-            if (!step<0, EXEC>(d, dstop, eager_lds)) return -1;
-            ++d;
         }
         for (;; d += 2) {
             if (!step<1, EXEC>(d, dstop, eager_lds)) return -1;
@@ -631,42 +627,54 @@ __device__ __forceinline__ void switch_layout(TO &to, FROM &from, uint32_t *x, i
     __builtin_amdgcn_wave_barrier();
 }
 
-// One side, start to end.  In the 384-position layout a side whose band has
-// narrowed continues in a 192-position layout (three cells per lane, about
-// half the work per diagonal) and returns when the band widens again; the
-// executor makes the same moves as the inspector, since they depend only on
-// the hulls.
+// The layout a side starts in: in the standard kernel the 192-position one
+// (every band starts as the single cell (0,0), and the eager block of
+// diagonals 0..32 is at most 17 positions wide); a wide retry starts and
+// stays in its own.
+template <int C>
+struct StartLayout {
+    static constexpr int value = C == 6 ? 3 : C;
+};
+
+// One side, start to end.  In the standard kernel a side runs three cells
+// per lane (192 positions) while its band is narrow and six per lane (384)
+// while it is wide: it moves up when the band passes 172 positions and back
+// down, from diagonal 256 on, when it narrows to 157 (the narrow layout
+// does about half the work per diagonal).  The executor makes the same
+// moves as the inspector, since they depend only on the hulls.
 template <int C, bool EXEC, bool SMALL>
 __device__ __forceinline__ SideResult run_side(const SideTask &task, const Scoring &sc, int dstop, uint32_t *eager_lds,
-                                               uint32_t *xfer, uint8_t *ptr_base, int64_t ptr_bytes,
-                                               SideDP<C, EXEC, SMALL> &dp)
+                                               uint32_t *xfer, uint8_t *ptr_base, int64_t ptr_bytes)
 {
     SideResult r;
-    int d = dp.start(dstop, eager_lds, ptr_base, ptr_bytes);
-    if (C != 6) {
+    if constexpr (C != 6) {
+        SideDP<C, EXEC, SMALL> dp(task, sc);
+        const int d = dp.start(dstop, eager_lds, ptr_base, ptr_bytes);
         if (d >= 0) dp.template advance<false>(d, dstop, eager_lds);
         r.take(dp);
         return r;
-    }
-    using DN = SideDP<3, EXEC, SMALL>;
-    DN dn(task, sc);
-    if (d < 0) {
-        r.take(dp);
-        return r;
-    }
-    for (;;) {
-        d = dp.template advance<true>(d, dstop, eager_lds);
-        if (d < 0) {
-            r.take(dp);
-            return r;
-        }
-        switch_layout(dn, dp, xfer, d);
-        d = dn.template advance<true>(d, dstop, eager_lds);
+    } else {
+        SideDP<3, EXEC, SMALL> dn(task, sc);
+        SideDP<6, EXEC, SMALL> dw(task, sc);
+        int d = dn.start(dstop, eager_lds, ptr_base, ptr_bytes);
         if (d < 0) {
             r.take(dn);
             return r;
         }
-        switch_layout(dp, dn, xfer, d);
+        for (;;) {
+            d = dn.template advance<true>(d, dstop, eager_lds);
+            if (d < 0) {
+                r.take(dn);
+                return r;
+            }
+            switch_layout(dw, dn, xfer, d);
+            d = dw.template advance<true>(d, dstop, eager_lds);
+            if (d < 0) {
+                r.take(dw);
+                return r;
+            }
+            switch_layout(dn, dw, xfer, d);
+        }
     }
 }
 
@@ -677,7 +685,8 @@ template <int C, bool EXEC, bool SMALL, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <= 8 ? 6 : 1))) void extend_kernel(ExtendArgs a)
 {
     using DP = SideDP<C, EXEC, SMALL>;
-    __shared__ uint32_t eager_lds_all[WAVES][EAGER_ROWS * DP::NEL * DP::NWORD];
+    using EDP = SideDP<StartLayout<C>::value, EXEC, SMALL>;     // holds the eager block
+    __shared__ uint32_t eager_lds_all[WAVES][EAGER_ROWS * EDP::NEL * EDP::NWORD];
     __shared__ uint32_t xfer_all[WAVES][C == 6 ? 4 * DP::XFER_W : 1];
     const int wv = uniform((int)(threadIdx.x / 64));
     uint32_t *eager_lds = eager_lds_all[wv];
@@ -697,18 +706,17 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <=
         }
         return;
     }
-    DP dp(task, a.sc);
     if (EXEC) {
         const ExecItem it = a.exec[item];
         const SideResult x = run_side<C, EXEC, SMALL>(task, a.sc, it.dstar, nullptr, xfer,
-                                                      a.ptr_ws + (it.ptr_off - a.ptr_base_off), it.ptr_bytes, dp);
+                                                      a.ptr_ws + (it.ptr_off - a.ptr_base_off), it.ptr_bytes);
         if (lane == 0) {
             atomicAdd((unsigned long long *)a.exec_cells, (unsigned long long)x.cells);
             if (x.overflow || x.best != o->score || x.bi != o->ie) atomicOr(&o->flags, SO_EXEC_MISMATCH);
         }
         return;
     }
-    const SideResult x = run_side<C, EXEC, SMALL>(task, a.sc, 0x7fffffff, eager_lds, xfer, nullptr, 0, dp);
+    const SideResult x = run_side<C, EXEC, SMALL>(task, a.sc, 0x7fffffff, eager_lds, xfer, nullptr, 0);
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     SideOut r;
     r.score = x.best;
@@ -720,12 +728,13 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <=
     r.flags = (x.overflow ? SO_OVERFLOW : 0) | a.result_flags;
     r.eager_len = 0;
     if (!x.overflow && x.bi <= EAGER_EDGE && x.bj <= EAGER_EDGE) {
-        // the best cell lies in the eager block, which the 384-position
-        // layout kept (no layout change happens before diagonal 33)
-        dp.bi = x.bi;
-        dp.bj = x.bj;
+        // the best cell lies in the eager block, which the start layout
+        // kept (no layout change happens before diagonal 34)
+        EDP e(task, a.sc);
+        e.bi = x.bi;
+        e.bj = x.bj;
         r.flags |= SO_EAGER;
-        r.eager_len = dp.eager_walk(eager_lds, a.eager_ops + (int64_t)sid * EAGER_OPS);
+        r.eager_len = e.eager_walk(eager_lds, a.eager_ops + (int64_t)sid * EAGER_OPS);
     }
     if (lane == 0) {
         *o = r;
