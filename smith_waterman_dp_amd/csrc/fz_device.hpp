@@ -99,6 +99,16 @@ __device__ __forceinline__ void load_unaligned(const GlobalU8 *p, uint32_t (&out
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
+// The lane id computed afresh where it is used (two VALU instructions the
+// compiler cannot merge with other computations of it), so that it need not
+// stay in a register, or be spilled, across a long loop that does not use it.
+__device__ __forceinline__ int fresh_lane_id()
+{
+    int r;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(r));
+    return r;
+}
+
 // Lane l receives lane l+1's value; lane 63 receives `fill`.
 __device__ __forceinline__ int from_next_lane(int v, int fill)
 {

@@ -89,7 +89,7 @@ struct SideDP {
     const Scoring &sc;
     int lane;
 
-    __device__ SideDP(const SideTask &task, const Scoring &s) : t(task), sc(s), lane(lane_id()) {}
+    __device__ SideDP(const SideTask &task, const Scoring &s) : t(task), sc(s), lane(fresh_lane_id()) {}
 
     __device__ __forceinline__ int sub_of(uint32_t X, uint32_t P, int c) const
     {
@@ -486,7 +486,7 @@ struct SideDP {
             // lane-derived constants of this layout are formed here, inside
             // the layout's own run, not once for the whole side (where both
             // layouts' sets would occupy registers at the same time)
-            asm volatile("" : "+v"(lane));
+            lane = fresh_lane_id();
         }
         for (;; d += 2) {
             if (!step<1, EXEC>(d, dstop, eager_lds)) return -1;
@@ -508,8 +508,7 @@ struct SideDP {
     {
         // (an opaque base keeps per-slot position constants from being
         // computed once and held in registers through the whole side)
-        int q0 = lane * C - ul;
-        asm volatile("" : "+v"(q0));
+        const int q0 = fresh_lane_id() * C - ul;
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             const int q = q0 + c;
@@ -528,8 +527,7 @@ struct SideDP {
     template <class O>
     __device__ __forceinline__ void adopt(const O &o, int s, const uint32_t *x, int ul, int uh, int dlast)
     {
-        int q0 = lane * C + s - ul;
-        asm volatile("" : "+v"(q0));
+        const int q0 = fresh_lane_id() * C + s - ul;
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             const bool in = (uint32_t)(q0 + c) <= (uint32_t)(uh - ul);
@@ -549,6 +547,7 @@ struct SideDP {
         dflush = o.dflush; acc_cells = 0; acc_words = 0;        // (the other side flushed)
         overflow = o.overflow;
         rowoff = o.rowoff; rowcap = o.rowcap; hdr = o.hdr; rows = o.rows;
+        lane = fresh_lane_id();
         set_dmask();
         init_bases();
         reload(dlast, (dlast + K) >> 1);
@@ -680,9 +679,12 @@ __device__ __forceinline__ SideResult run_side(const SideTask &task, const Scori
 
 // One wave per side; the grid covers the work list (the hardware dispatcher
 // hands waves to CUs as others retire, which balances sides of very
-// different lengths).
+// different lengths).  Register budgets of the standard kernels: the
+// inspector fits 64 VGPRs (8 waves per SIMD), the executor 72 (7 waves)
+// with byte substitution scores and 80 (6) without; more waves let a SIMD
+// pair one wave's VALU instruction with another's SALU instruction.
 template <int C, bool EXEC, bool SMALL, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <= 8 ? 6 : 1))) void extend_kernel(ExtendArgs a)
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <= 8 ? (EXEC ? (SMALL ? 7 : 6) : 8) : 1))) void extend_kernel(ExtendArgs a)
 {
     using DP = SideDP<C, EXEC, SMALL>;
     using EDP = SideDP<StartLayout<C>::value, EXEC, SMALL>;     // holds the eager block
@@ -691,7 +693,6 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <=
     const int wv = uniform((int)(threadIdx.x / 64));
     uint32_t *eager_lds = eager_lds_all[wv];
     uint32_t *xfer = xfer_all[wv];
-    const int lane = lane_id();
     const int idx = (int)blockIdx.x * WAVES + wv;
     if (idx >= a.nlist) return;
     const int64_t item = EXEC ? a.exec_begin + idx : (int64_t)idx;
@@ -699,7 +700,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <=
     const SideTask task = a.tasks[sid];
     SideOut *o = &a.out[sid];
     if (task.m < 0) {
-        if (!EXEC && lane == 0) {
+        if (!EXEC && fresh_lane_id() == 0) {
             SideOut r = {};
             r.flags = SO_SKIPPED;
             *o = r;
@@ -710,7 +711,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <=
         const ExecItem it = a.exec[item];
         const SideResult x = run_side<C, EXEC, SMALL>(task, a.sc, it.dstar, nullptr, xfer,
                                                       a.ptr_ws + (it.ptr_off - a.ptr_base_off), it.ptr_bytes);
-        if (lane == 0) {
+        if (fresh_lane_id() == 0) {
             atomicAdd((unsigned long long *)a.exec_cells, (unsigned long long)x.cells);
             if (x.overflow || x.best != o->score || x.bi != o->ie) atomicOr(&o->flags, SO_EXEC_MISMATCH);
         }
@@ -736,7 +737,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <=
         r.flags |= SO_EAGER;
         r.eager_len = e.eager_walk(eager_lds, a.eager_ops + (int64_t)sid * EAGER_OPS);
     }
-    if (lane == 0) {
+    if (fresh_lane_id() == 0) {
         *o = r;
         if (x.overflow) {
             const uint32_t k = atomicAdd(a.overflow_count, 1u);
