@@ -306,14 +306,17 @@ struct SideDP {
 
         if (ballot(dmax > best)) {
             const int nb = uniform(wave_max(dmax));
-            int pbest = 0x7fffffff;
+            // first position holding it: each lane finds its first slot (this
+            // diagonal's S is in the register it was written to), the ballot
+            // the first lane
+            int slot = C;
 #pragma unroll
-            for (int c = 0; c < C; ++c) {
-                // recover this diagonal's S from the register it was written to
+            for (int c = C - 1; c >= 0; --c) {
                 const int Sv = DELTA == 1 ? SA[c] : SB[c];
-                const uint64_t m = ballot(Sv == nb);
-                if (m) pbest = min(pbest, ctz64(m) * C + c);
+                slot = Sv == nb ? c : slot;
             }
+            const int fl = ctz64(ballot(slot < C));
+            const int pbest = fl * C + __builtin_amdgcn_readlane(slot, fl);
             best = nb;
             T = max(best - sc.ydrop, T_FLOOR);
             bi = pbest + od;
