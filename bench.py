@@ -12,6 +12,7 @@ Workloads (seeded, synthetic; see smith_waterman_dp_amd/workloads.py):
   skewed          one million 19-mer seeds on a 10 Mbp pair (default)
   local           4,096 full-matrix local alignments of 2048 x 2048
   tiny, executor_heavy, chromosome
+  chromosome_rc   the chromosome pair searched on the query's reverse strand
 """
 import argparse
 import json
@@ -64,7 +65,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="skewed",
-                    choices=["skewed", "local", "tiny", "executor_heavy", "chromosome"])
+                    choices=["skewed", "local", "tiny", "executor_heavy", "chromosome", "chromosome_rc"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -90,6 +91,7 @@ def cpu_baseline(w, target_seconds, local):
         pass
     rng = np.random.default_rng(123)
     seeds = w["seeds"]
+    query = oracle.revcomp(w["query"]) if w.get("query_rc") else w["query"]
     n = seeds.shape[0]
     order = rng.permutation(n)
     done_cells = 0
@@ -98,7 +100,7 @@ def cpu_baseline(w, target_seconds, local):
     chunk = max(threads, 8)
     while done < n and time.time() - t0 < target_seconds:
         idx = order[done:done + chunk]
-        hits, _, _ = oracle.run(w["target"], w["query"], seeds[idx], w["scoring"],
+        hits, _, _ = oracle.run(w["target"], query, seeds[idx], w["scoring"],
                                 oracle.YDROP_INF if local else w["ydrop"], min_tb=w.get("min_tb"),
                                 traceback=not local and w.get("traceback", True), local=local, threads=threads)
         done_cells += int(hits["cells_r"].sum() + (0 if local else hits["cells_l"].sum()))
@@ -136,10 +138,11 @@ def main():
     min_tb = -(1 << 62) if min_tb is None else min_tb
 
     def step():
+        rc = bool(w.get("query_rc"))
         if local:
-            return ctx.local(T, Q, S, w["scoring"], want_stats=True)
+            return ctx.local(T, Q, S, w["scoring"], want_stats=True, query_rc=rc)
         return ctx.extend(T, Q, S, w["scoring"], w["ydrop"], min_tb, traceback=w.get("traceback", True),
-                          want_stats=True)
+                          want_stats=True, query_rc=rc)
 
     for k in range(a.warmup):
         step()

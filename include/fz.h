@@ -102,8 +102,18 @@ typedef struct {
 enum {
     FZ_TRACEBACK = 1u << 0,        /* CIGAR for every seed whose score > min_traceback_score */
     FZ_LOCAL = 1u << 1,            /* full-window local alignment, score and end cell only */
-    FZ_STATS = 1u << 2             /* fill *stats (adds stream syncs for phase timings) */
+    FZ_STATS = 1u << 2,            /* fill *stats (adds stream syncs for phase timings) */
+    FZ_QUERY_RC = 1u << 3          /* seeds lie on the query's reverse complement (see below) */
 };
+
+/* FZ_QUERY_RC: the call aligns the target against the reverse complement
+ * of `query` (base j of it is the complement of query[query_len - 1 - j];
+ * A<->T, C<->G).  Seed positions, windows and the q_begin / q_end of the
+ * results are coordinates on that reverse complement; the forward-strand
+ * span of a hit is [query_len - q_end, query_len - q_begin).  The query
+ * buffer itself is read, never written.  Works with and without FZ_LOCAL.
+ * (FastZ and LASTZ search both strands; the reverse strand is this
+ * transform of the input, the kernels are the same.) */
 
 enum {
     FZ_OK = 0,
@@ -153,7 +163,7 @@ int fz_set_pointer_workspace(fz_ctx *ctx, uint64_t bytes);
  *   ydrop           >= 0; FZ_YDROP_INF disables pruning (ignored in local mode)
  *   min_traceback_score   with FZ_TRACEBACK, seeds whose score is strictly
  *                   greater get a CIGAR; others get FZ_HIT_BELOW_MIN
- *   flags           FZ_TRACEBACK | FZ_LOCAL | FZ_STATS
+ *   flags           FZ_TRACEBACK | FZ_LOCAL | FZ_STATS | FZ_QUERY_RC
  *   hits            device, n_seeds records, written by the call
  *   cigar           out (may be NULL): device pointer to the CIGAR words,
  *                   BAM-style (length << 4 | op, op 0 = M, 1 = I, 2 = D),

@@ -78,6 +78,26 @@ def _as_bytes(seq):
     return np.ascontiguousarray(seq, dtype=np.uint8)
 
 
+# Complement of each ASCII base: A<->T, C<->G in either case; any other byte
+# maps to itself, so the batch still rejects it as a non-ACGT input.
+_COMPLEMENT = np.arange(256, dtype=np.uint8)
+for _a, _b in ("AT", "TA", "CG", "GC", "at", "ta", "cg", "gc"):
+    _COMPLEMENT[ord(_a)] = ord(_b)
+
+
+def revcomp(seq):
+    """Reverse complement of an ASCII sequence: the other strand read in its
+    own direction, base j being the complement of base len-1-j.
+
+    FastZ (SC'21), section 2, places the extension inside whole-genome
+    alignment, which searches both strands of the query; the pages do not
+    spell out the reverse strand, so this is the textbook definition, and an
+    extension on the reverse strand is the forward extension against this
+    sequence (seeds and windows in its coordinates).
+    """
+    return _COMPLEMENT[_as_bytes(seq)[::-1]]
+
+
 def seeds_array(seeds):
     """Seeds as an (n, 7) int64 array in SEED_FIELDS order."""
     if isinstance(seeds, np.ndarray) and seeds.dtype.names:

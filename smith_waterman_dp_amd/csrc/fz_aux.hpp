@@ -10,7 +10,7 @@ namespace fz {
 // ASCII -> 2-bit codes (A0 C1 G2 T3) one per byte, forward and reversed,
 // with PAD code-0 bases on both ends.  Any other byte raises *err.
 __global__ void pack_kernel(const uint8_t *__restrict__ ascii, int64_t len, uint8_t *__restrict__ fwd,
-                            uint8_t *__restrict__ rev, int64_t padded, uint32_t *err)
+                            uint8_t *__restrict__ rev, int64_t padded, uint32_t *err, int revcomp)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     bool bad = false;
@@ -18,11 +18,15 @@ __global__ void pack_kernel(const uint8_t *__restrict__ ascii, int64_t len, uint
         const int64_t s = x - PAD;
         uint8_t code = 0;
         if (s >= 0 && s < len) {
-            const uint8_t c = ascii[s] & 0xDF;   // upper-case
+            // revcomp: base s of the reverse complement is the complement of
+            // base len-1-s; with A=0, C=1, G=2, T=3 the complement is code ^ 3
+            const uint8_t c = ascii[revcomp ? len - 1 - s : s] & 0xDF;   // upper-case
             code = c == 'A' ? 0 : c == 'C' ? 1 : c == 'G' ? 2 : c == 'T' ? 3 : 255;
             if (code == 255) {
                 bad = true;
                 code = 0;
+            } else if (revcomp) {
+                code ^= 3;
             }
         }
         fwd[x] = code;

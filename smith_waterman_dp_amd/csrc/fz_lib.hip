@@ -214,7 +214,8 @@ int check_args(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const uint8_t 
         sc->transition < -lim || sc->transversion > lim || sc->transversion < -lim)
         return fail(ctx, FZ_EINVAL, "scoring values must lie in [-2^24, 2^24]");
     if (!(flags & FZ_LOCAL) && ydrop < 0) return fail(ctx, FZ_EINVAL, "ydrop must be >= 0");
-    if (flags & ~(uint32_t)(FZ_TRACEBACK | FZ_LOCAL | FZ_STATS)) return fail(ctx, FZ_EINVAL, "unknown flag bits");
+    if (flags & ~(uint32_t)(FZ_TRACEBACK | FZ_LOCAL | FZ_STATS | FZ_QUERY_RC))
+        return fail(ctx, FZ_EINVAL, "unknown flag bits");
     if ((flags & FZ_LOCAL) && (flags & FZ_TRACEBACK)) return fail(ctx, FZ_EINVAL, "local mode has no traceback");
     return FZ_OK;
 }
@@ -394,11 +395,13 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     {
         const unsigned bt = std::min<int64_t>(blocks_for(NT, 256), 8192);
         pack_kernel<<<bt, 256, 0, st>>>(target, (int64_t)tlen, as<uint8_t>(ctx->Tf), as<uint8_t>(ctx->Tr), NT,
-                                        &dc->err);
+                                        &dc->err, 0);
         HIP_OK(hipGetLastError());
         const unsigned bq = std::min<int64_t>(blocks_for(NQ, 256), 8192);
+        // with FZ_QUERY_RC every later step sees the query's reverse
+        // complement: seeds, windows and results are in its coordinates
         pack_kernel<<<bq, 256, 0, st>>>(query, (int64_t)qlen, as<uint8_t>(ctx->Qf), as<uint8_t>(ctx->Qr), NQ,
-                                        &dc->err);
+                                        &dc->err, (flags & FZ_QUERY_RC) ? 1 : 0);
         HIP_OK(hipGetLastError());
     }
     Counters hc;

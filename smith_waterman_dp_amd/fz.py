@@ -11,7 +11,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfz.so")
 
-FZ_TRACEBACK, FZ_LOCAL, FZ_STATS = 1, 2, 4
+FZ_TRACEBACK, FZ_LOCAL, FZ_STATS, FZ_QUERY_RC = 1, 2, 4, 8
 FZ_OK, FZ_EINVAL, FZ_ENOMEM, FZ_EDEVICE, FZ_EBAND = 0, -1, -2, -3, -4
 FZ_HIT_TRACED, FZ_HIT_EAGER_LEFT, FZ_HIT_EAGER_RIGHT = 1, 2, 4
 FZ_HIT_BELOW_MIN, FZ_HIT_EBAND, FZ_HIT_ESEED, FZ_HIT_ERANGE = 8, 16, 32, 64
@@ -179,10 +179,12 @@ class Context:
             pass
 
     def extend(self, target, query, seeds, scoring, ydrop, min_traceback_score=-(1 << 62), traceback=True,
-               stream=None, want_stats=False):
-        flags = FZ_TRACEBACK if traceback else 0
+               stream=None, want_stats=False, query_rc=False):
+        """query_rc: seeds lie on the query's reverse complement (FZ_QUERY_RC)."""
+        flags = (FZ_TRACEBACK if traceback else 0) | (FZ_QUERY_RC if query_rc else 0)
         return fz_extend_batch(self.h, target, query, seeds, scoring, ydrop, min_traceback_score, flags,
                                stream, want_stats)
 
-    def local(self, target, query, seeds, scoring, stream=None, want_stats=False):
-        return fz_extend_batch(self.h, target, query, seeds, scoring, 0, 0, FZ_LOCAL, stream, want_stats)
+    def local(self, target, query, seeds, scoring, stream=None, want_stats=False, query_rc=False):
+        flags = FZ_LOCAL | (FZ_QUERY_RC if query_rc else 0)
+        return fz_extend_batch(self.h, target, query, seeds, scoring, 0, 0, flags, stream, want_stats)

@@ -34,6 +34,12 @@ def random_codes(rng, n):
     return rng.integers(0, 4, size=int(n), dtype=np.int8)
 
 
+def revcomp_codes(codes):
+    """Reverse complement in base codes (A=0, C=1, G=2, T=3, so the
+    complement of c is 3 - c)."""
+    return (3 - np.asarray(codes, dtype=np.int8))[::-1].copy()
+
+
 def mutate(rng, src, sub_rate, indel_rate, p_geom, ts_frac=2.0 / 3.0):
     """Mutated copy of a code array (0..3 = A, C, G, T).
 
@@ -139,10 +145,12 @@ def _pack(t_pos, q_pos, L, t_lo, t_hi, q_lo, q_hi):
     return s
 
 
-def _workload(name, t_codes, q_codes, seeds, local=False, min_tb=None, **info):
+def _workload(name, t_codes, q_codes, seeds, local=False, min_tb=None, query_rc=False, **info):
+    """query_rc: the seeds lie on the reverse complement of `query` (the
+    library is called with FZ_QUERY_RC; `query` is the forward strand)."""
     return dict(name=name, target=to_ascii(t_codes), query=to_ascii(q_codes), seeds=seeds,
                 scoring=dict(DEFAULT_SCORING), ydrop=DEFAULT_YDROP, local=local,
-                traceback=not local, min_tb=min_tb, info=info)
+                traceback=not local, min_tb=min_tb, query_rc=query_rc, info=info)
 
 
 def tiny(n_seeds=1000, flank=256, seed=0):
@@ -314,14 +322,7 @@ def executor_heavy(n_pairs=100_000, len_min=1000, len_max=20000, unrelated=2048,
                      n_pairs=n_pairs, mean_len=float(L.mean()))
 
 
-def chromosome(length=20_000_000, sub_rate=0.12, indel_rate=0.01, p_geom=0.3, n_inversions=5,
-               inv_min=50_000, inv_max=500_000, unrelated_frac=0.20, flank=WINDOW_FLANK, seed=0):
-    """Chromosome-scale pair: C2 = mut(C1) (12% substitutions 2:1, 1% indels of
-    Geom(0.3)), then `n_inversions` non-overlapping reverse-complement
-    inversions of U(50 kb, 500 kb), then one contiguous unrelated block of
-    20% of the length.  Seeds are all forward-strand shared 19-mers after
-    diagonal dedup: each run of hits on consecutive positions of one
-    diagonal (t - q) becomes one seed at the run start."""
+def _chromosome_pair(length, sub_rate, indel_rate, p_geom, n_inversions, inv_min, inv_max, unrelated_frac, seed):
     rng = np.random.default_rng(seed)
     C1 = random_codes(rng, length)
     C2 = mutate(rng, C1, sub_rate, indel_rate, p_geom)
@@ -331,21 +332,54 @@ def chromosome(length=20_000_000, sub_rate=0.12, indel_rate=0.01, p_geom=0.3, n_
     for k in range(n_inversions):
         L = int(rng.integers(inv_min, inv_max + 1))
         s = k * span + int(rng.integers(0, max(span - L, 1)))
-        seg = C2[s:s + L]
-        C2[s:s + L] = (3 - seg)[::-1]
+        C2[s:s + L] = revcomp_codes(C2[s:s + L])
     ub = int(unrelated_frac * n2)
     us = int(rng.integers(0, n2 - ub))
     C2[us:us + ub] = random_codes(rng, ub)
-    t, q = shared_kmers(C1, C2)
+    return C1, C2
+
+
+def _diagonal_dedup_seeds(t, q, tlen, qlen, flank):
+    """Each run of hits on consecutive positions of one diagonal (t - q)
+    becomes one seed at the run start; windows +-flank."""
     diag = t - q
     order = np.lexsort((t, diag))
     t, q, diag = t[order], q[order], diag[order]
     start = np.ones(t.size, dtype=bool)
     start[1:] = ~((diag[1:] == diag[:-1]) & (t[1:] == t[:-1] + 1))
     t, q = t[start], q[start]
-    t_lo, t_hi, q_lo, q_hi = _windows(t, q, C1.size, C2.size, flank)
-    seeds = _pack(t, q, SEED_LEN, t_lo, t_hi, q_lo, q_hi)
-    return _workload("chromosome", C1, C2, seeds, n_seeds=int(t.size))
+    t_lo, t_hi, q_lo, q_hi = _windows(t, q, tlen, qlen, flank)
+    return _pack(t, q, SEED_LEN, t_lo, t_hi, q_lo, q_hi)
+
+
+def chromosome(length=20_000_000, sub_rate=0.12, indel_rate=0.01, p_geom=0.3, n_inversions=5,
+               inv_min=50_000, inv_max=500_000, unrelated_frac=0.20, flank=WINDOW_FLANK, seed=0):
+    """Chromosome-scale pair: C2 = mut(C1) (12% substitutions 2:1, 1% indels of
+    Geom(0.3)), then `n_inversions` non-overlapping reverse-complement
+    inversions of U(50 kb, 500 kb), then one contiguous unrelated block of
+    20% of the length.  Seeds are all forward-strand shared 19-mers after
+    diagonal dedup: each run of hits on consecutive positions of one
+    diagonal (t - q) becomes one seed at the run start."""
+    C1, C2 = _chromosome_pair(length, sub_rate, indel_rate, p_geom, n_inversions, inv_min, inv_max,
+                              unrelated_frac, seed)
+    t, q = shared_kmers(C1, C2)
+    seeds = _diagonal_dedup_seeds(t, q, C1.size, C2.size, flank)
+    return _workload("chromosome", C1, C2, seeds, n_seeds=len(seeds))
+
+
+def chromosome_rc(length=20_000_000, sub_rate=0.12, indel_rate=0.01, p_geom=0.3, n_inversions=5,
+                  inv_min=50_000, inv_max=500_000, unrelated_frac=0.20, flank=WINDOW_FLANK, seed=0):
+    """The pair of `chromosome` (same parameters, same draw) searched on the
+    other strand: seeds are the shared 19-mers of C1 and the reverse
+    complement of C2 (mostly inside the inversions), diagonal-deduplicated,
+    in the coordinates of that reverse complement.  The query passed is C2
+    itself, with query_rc set."""
+    C1, C2 = _chromosome_pair(length, sub_rate, indel_rate, p_geom, n_inversions, inv_min, inv_max,
+                              unrelated_frac, seed)
+    R2 = revcomp_codes(C2)
+    t, q = shared_kmers(C1, R2)
+    seeds = _diagonal_dedup_seeds(t, q, C1.size, R2.size, flank)
+    return _workload("chromosome_rc", C1, C2, seeds, query_rc=True, n_seeds=len(seeds))
 
 
 WORKLOADS = {
@@ -354,4 +388,5 @@ WORKLOADS = {
     "skewed": skewed,
     "executor_heavy": executor_heavy,
     "chromosome": chromosome,
+    "chromosome_rc": chromosome_rc,
 }

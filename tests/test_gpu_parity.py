@@ -60,21 +60,27 @@ def run_gpu(ctx, w, seeds=None, local=False, ydrop=None, min_tb=None, traceback=
     T, Q, S = dev(w["target"]), dev(w["query"]), dev(seeds)
     log("call %s: %d records, target %d, query %d" % ("local" if local else "extend", len(seeds),
                                                       T.numel(), Q.numel()))
+    rc = bool(w.get("query_rc"))
     if local:
-        hits, cig, st = ctx.local(T, Q, S, sc, want_stats=True)
+        hits, cig, st = ctx.local(T, Q, S, sc, want_stats=True, query_rc=rc)
     else:
         yd = w["ydrop"] if ydrop is None else ydrop
         mt = -(1 << 62) if min_tb is None else min_tb
-        hits, cig, st = ctx.extend(T, Q, S, sc, yd, mt, traceback=traceback, want_stats=True)
+        hits, cig, st = ctx.extend(T, Q, S, sc, yd, mt, traceback=traceback, want_stats=True, query_rc=rc)
     torch.cuda.synchronize()
     log("call done")
     return hits.cpu().numpy(), cig.cpu().numpy().view(np.uint32), st
 
 
+def oracle_query(w):
+    """The query as the oracle sees it: with query_rc, its reverse complement."""
+    return oracle.revcomp(w["query"]) if w.get("query_rc") else w["query"]
+
+
 def run_oracle(w, seeds=None, local=False, ydrop=None, min_tb=None, traceback=True, scoring=None):
     seeds = w["seeds"] if seeds is None else seeds
     yd = w["ydrop"] if ydrop is None else ydrop
-    return oracle.run(w["target"], w["query"], seeds, scoring or w["scoring"], yd, min_tb=min_tb,
+    return oracle.run(w["target"], oracle_query(w), seeds, scoring or w["scoring"], yd, min_tb=min_tb,
                       traceback=traceback, local=local)
 
 
@@ -357,7 +363,7 @@ def test_local_full_size_sampled(ctx):
 def check_invariants(w, gh, gc, label, limit=1500):
     """Rescore CIGARs from the sequences and check spans (any size); at most
     `limit` traced seeds, chosen by a seeded draw."""
-    T, Q = w["target"], w["query"]
+    T, Q = w["target"], oracle_query(w)
     code = np.full(256, -1, dtype=np.int64)
     for k, c in enumerate(b"ACGT"):
         code[c] = k
@@ -469,3 +475,52 @@ def test_chromosome_full_size_sampled(ctx):
     dedup: a seeded sample and the longest alignments against the oracle."""
     log("generating the chromosome pair")
     _full_size_sampled(ctx, W.chromosome(), 24, 4, "chromosome full")
+
+
+# ------------------------------------------------------ reverse strand --
+
+def on_reverse_strand(w):
+    """The same alignments asked on the other strand: the query handed in is
+    the reverse complement of w's query (built by the input generator), so
+    with query_rc the library must see w's query again."""
+    r = dict(w)
+    r["query"] = W.to_ascii(W.revcomp_codes(np.searchsorted(np.frombuffer(b"ACGT", np.uint8),
+                                                              np.asarray(w["query"], np.uint8))))
+    r["query_rc"] = True
+    return r
+
+
+def test_query_rc_tiny_full(ctx):
+    """A 200-seed tiny batch through FZ_QUERY_RC: every field against the
+    oracle on the reverse complement, and identical to the forward call."""
+    w = W.tiny(n_seeds=200, seed=21)
+    r = on_reverse_strand(w)
+    gh, gc, st = run_gpu(ctx, r)
+    oh, ow, oo = run_oracle(r)
+    compare(gh, gc, oh, ow, oo, label="query_rc tiny")
+    fh, fc, _ = run_gpu(ctx, w)
+    assert np.array_equal(fh, gh) and np.array_equal(fc, gc)
+
+
+def test_query_rc_local(ctx):
+    w = W.local_pairs(n_pairs=24, length=300, seed=22)
+    r = on_reverse_strand(w)
+    gh, gc, st = run_gpu(ctx, r, local=True)
+    oh, ow, oo = run_oracle(r, local=True)
+    compare(gh, gc, oh, ow, oo, local=True, label="query_rc local")
+
+
+def test_chromosome_rc_reduced(ctx):
+    """Reverse-strand seeds of a 600 kb chromosome pair (the inversions)."""
+    w = W.chromosome_rc(length=600_000, inv_min=5_000, inv_max=20_000, seed=3)
+    gh, gc, st = sample_compare(ctx, w, 40, "chromosome rc reduced")
+    check_invariants(w, gh, gc, "chromosome rc reduced", limit=200)
+
+
+@pytest.mark.skipif(os.environ.get("FZ_FULL_SIZE", "1") == "0", reason="full-size runs disabled")
+def test_chromosome_rc_full_size_sampled(ctx):
+    """The 20 Mbp chromosome pair searched on the reverse strand (seeds in
+    the five inversions and chance hits): a seeded sample and the longest
+    alignments against the oracle, invariants on the rest."""
+    log("generating the chromosome pair, reverse-strand seeds")
+    _full_size_sampled(ctx, W.chromosome_rc(), 24, 4, "chromosome rc full")

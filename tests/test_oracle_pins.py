@@ -347,3 +347,72 @@ def test_empty_flanks():
     h = hits[0]
     assert (h["score"], h["t_begin"], h["t_end"], h["cells_l"], h["cells_r"]) == (19 * 91, 0, 19, 1, 1)
     assert oracle.cigar_string(words) == "19M"
+
+
+# ------------------------------------------------------ reverse strand --
+
+def test_revcomp_hand_examples():
+    """Complement A<->T, C<->G (either case), then reverse; other bytes kept."""
+    assert oracle.revcomp(b"AACGTTTGCA").tobytes() == b"TGCAAACGTT"
+    assert oracle.revcomp(b"acgT").tobytes() == b"Acgt"
+    assert oracle.revcomp(b"ANC").tobytes() == b"GNT"
+    assert oracle.revcomp(b"").tobytes() == b""
+
+
+def test_revcomp_involution():
+    rng = np.random.default_rng(5)
+    for n in (1, 2, 19, 1000):
+        s = W.to_ascii(W.random_codes(rng, n))
+        r = oracle.revcomp(s)
+        assert r.size == n
+        assert np.array_equal(oracle.revcomp(r), s)
+        # no base is its own complement, so every position changes
+        assert (oracle.revcomp(s)[::-1] != s).all()
+
+
+def _strand_case(seed):
+    """T random; R = mut(T) holds the homology; the query handed in is the
+    reverse complement of R, so the seeds (shared 19-mers of T and R) lie on
+    the query's reverse strand."""
+    rng = np.random.default_rng(seed)
+    T = W.random_codes(rng, 1500)
+    R = W.mutate(rng, T, 0.08, 0.01, 0.5)
+    t, q = W.shared_kmers(T, R)
+    keep = np.unique(t - q, return_index=True)[1][:12]
+    t, q = t[keep], q[keep]
+    lo_t = np.maximum(t - 400, 0)
+    hi_t = np.minimum(t + 19 + 400, T.size)
+    lo_q = np.maximum(q - 300, 0)
+    hi_q = np.minimum(q + 19 + 500, R.size)
+    seeds = np.stack([t, q, np.full_like(t, 19), lo_t, hi_t, lo_q, hi_q], axis=1).astype(np.int64)
+    return W.to_ascii(T), W.to_ascii(W.revcomp_codes(R)), seeds
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_strand_symmetry(seed):
+    """Extending T against revcomp(Q) is extending revcomp(T) against Q with
+    the seed mirrored: complementing both sequences keeps every
+    substitution's class (transitions stay transitions), so each side's
+    matrix is the same, the left and right sides trade places and the CIGAR
+    runs come out in reverse order."""
+    T, Q, s1 = _strand_case(seed)
+    nT, nQ = T.size, Q.size
+    h1, w1, o1 = oracle.run(T, oracle.revcomp(Q), s1, SC, 9400, threads=4)
+    s2 = s1.copy()
+    s2[:, 0] = nT - s1[:, 0] - s1[:, 2]
+    s2[:, 1] = nQ - s1[:, 1] - s1[:, 2]
+    s2[:, 3], s2[:, 4] = nT - s1[:, 4], nT - s1[:, 3]
+    s2[:, 5], s2[:, 6] = nQ - s1[:, 6], nQ - s1[:, 5]
+    h2, w2, o2 = oracle.run(oracle.revcomp(T), Q, s2, SC, 9400, threads=4)
+    assert (h1["status"] == 0).all() and (h2["status"] == 0).all()
+    assert (h1["score"] > 19 * 91).any()            # some seeds do extend
+    for k in range(len(s1)):
+        a, b = h1[k], h2[k]
+        assert a["score"] == b["score"]
+        assert (a["score_l"], a["score_r"]) == (b["score_r"], b["score_l"])
+        assert (a["cells_l"], a["cells_r"]) == (b["cells_r"], b["cells_l"])
+        assert (b["t_begin"], b["t_end"]) == (nT - a["t_end"], nT - a["t_begin"])
+        assert (b["q_begin"], b["q_end"]) == (nQ - a["q_end"], nQ - a["q_begin"])
+        c1 = w1[o1[k]:o1[k] + a["n_runs"]]
+        c2 = w2[o2[k]:o2[k] + b["n_runs"]]
+        assert np.array_equal(c1[::-1], c2)
