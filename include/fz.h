@@ -103,7 +103,8 @@ enum {
     FZ_TRACEBACK = 1u << 0,        /* CIGAR for every seed whose score > min_traceback_score */
     FZ_LOCAL = 1u << 1,            /* full-window local alignment, score and end cell only */
     FZ_STATS = 1u << 2,            /* fill *stats (adds stream syncs for phase timings) */
-    FZ_QUERY_RC = 1u << 3          /* seeds lie on the query's reverse complement (see below) */
+    FZ_QUERY_RC = 1u << 3,         /* seeds lie on the query's reverse complement (see below) */
+    FZ_SEEDS_ALL = 1u << 4         /* fz_find_seeds: every shared k-mer, no diagonal dedup */
 };
 
 /* FZ_QUERY_RC: the call aligns the target against the reverse complement
@@ -181,6 +182,44 @@ int fz_extend_batch(fz_ctx *ctx,
                     int64_t min_traceback_score, uint32_t flags,
                     fz_hit *hits, const uint32_t **cigar, uint64_t *cigar_words,
                     fz_stats *stats, void *stream);
+
+/*
+ * Seed stage (FastZ, SC'21, section 2: whole-genome alignment first finds
+ * short exact matches between the two sequences as seed sites, then filters
+ * them, then runs the gapped extension).  Finds every pair (t, q) with
+ * target[t .. t+k) == query[q .. q+k) (with FZ_QUERY_RC: equal to the
+ * query's reverse complement, q counted on it) and, unless FZ_SEEDS_ALL,
+ * keeps one seed per run of hits on consecutive positions of one diagonal
+ * t - q (the run's first hit).  Seeds come out ordered by diagonal t - q,
+ * then by t, with seed_len = k and windows [t - flank, t + k + flank) and
+ * [q - flank, q + k + flank) clipped to the sequences: an fz_seed array
+ * fz_extend_batch takes as it is (with the same FZ_QUERY_RC).
+ *   target, query   device, ASCII bases as for fz_extend_batch; each
+ *                   shorter than 2^31 bases
+ *   k               1..32
+ *   flank           >= 0
+ *   flags           FZ_QUERY_RC | FZ_SEEDS_ALL
+ *   seeds           out (may be NULL): device pointer to *n_seeds records,
+ *                   owned by ctx, valid until the next fz_find_seeds or
+ *                   fz_destroy (fz_copy_seeds copies them out)
+ *   n_seeds         out: number of seeds
+ *   n_hits          out (may be NULL): shared k-mer hits before the dedup
+ *   stream          hipStream_t or NULL
+ * Every hit is materialized (16 bytes each in device memory, plus sort
+ * scratch); more than 2^31 hits fail with FZ_ENOMEM.  The call reads counts
+ * back, so it returns after the stream has finished it.  Returns FZ_OK or a
+ * negative FZ_E* code (FZ_EINVAL for bad arguments or a non-ACGT byte).
+ */
+int fz_find_seeds(fz_ctx *ctx,
+                  const uint8_t *target, uint64_t target_len,
+                  const uint8_t *query, uint64_t query_len,
+                  uint32_t k, int64_t flank, uint32_t flags,
+                  const fz_seed **seeds, uint64_t *n_seeds, uint64_t *n_hits,
+                  void *stream);
+
+/* Copy the first n seeds of the last successful fz_find_seeds to dst
+ * (device, n records). */
+int fz_copy_seeds(fz_ctx *ctx, fz_seed *dst, uint64_t n, void *stream);
 
 /* Copy the first `words` CIGAR words of the last successful fz_extend_batch
  * on ctx into caller device memory `dst` (enqueued on `stream`, which is

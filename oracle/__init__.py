@@ -98,6 +98,70 @@ def revcomp(seq):
     return _COMPLEMENT[_as_bytes(seq)[::-1]]
 
 
+_CODE = np.full(256, -1, dtype=np.int64)
+for _k, _c in enumerate("ACGT"):
+    _CODE[ord(_c)] = _k
+    _CODE[ord(_c.lower())] = _k
+
+
+def find_seeds(target, query, k=19, flank=32768, dedup=True, query_rc=False):
+    """The seed stage: every (t, q) with target[t:t+k] == query[q:q+k] (with
+    query_rc, q indexes the query's reverse complement).
+
+    FastZ (SC'21), section 2: whole-genome alignment first finds short exact
+    matches (19 bases) between the two sequences as seed sites and then
+    filters them before the gapped extension.  The filter here is the
+    plainest one: with dedup, of each run of hits on consecutive positions of
+    one diagonal t - q only the first is kept.  Seeds are ordered by diagonal
+    t - q, then t; windows are [x - flank, x + k + flank) clipped to each
+    sequence.  Returns (seeds, n_hits): an (n, 7) int64 array in
+    SEED_FIELDS order and the number of hits before the dedup.
+    """
+    T = _as_bytes(target)
+    Q = revcomp(query) if query_rc else _as_bytes(query)
+    tc, qc = _CODE[T], _CODE[Q]
+    if (tc < 0).any() or (qc < 0).any():
+        raise ValueError("sequence holds a byte other than A, C, G, T")
+    if not 1 <= k <= 32:
+        raise ValueError("k must be 1..32")
+    nt, nq = T.size - k + 1, Q.size - k + 1
+    if nt <= 0 or nq <= 0:
+        return np.zeros((0, 7), dtype=np.int64), 0
+
+    def kmers(c, n):
+        # the k codes from each start as a base-4 number, first base most significant
+        v = np.zeros(n, dtype=np.uint64)
+        for i in range(k):
+            v = v * np.uint64(4) + c[i:i + n].astype(np.uint64)
+        return v
+
+    tk, qk = kmers(tc, nt), kmers(qc, nq)
+    order = np.argsort(tk, kind="stable")
+    st = tk[order]
+    lo = np.searchsorted(st, qk, "left")
+    hi = np.searchsorted(st, qk, "right")
+    cnt = hi - lo
+    n_hits = int(cnt.sum())
+    q = np.repeat(np.arange(nq, dtype=np.int64), cnt)
+    first = np.repeat(lo, cnt)
+    nth = np.arange(n_hits, dtype=np.int64) - np.repeat(np.cumsum(cnt) - cnt, cnt)
+    t = order[first + nth].astype(np.int64)
+    diag = t - q
+    o = np.lexsort((t, diag))
+    t, q, diag = t[o], q[o], diag[o]
+    if dedup and n_hits:
+        keep = np.ones(n_hits, dtype=bool)
+        keep[1:] = ~((diag[1:] == diag[:-1]) & (t[1:] == t[:-1] + 1))
+        t, q = t[keep], q[keep]
+    out = np.empty((t.size, 7), dtype=np.int64)
+    out[:, 0], out[:, 1], out[:, 2] = t, q, k
+    out[:, 3] = np.maximum(t - flank, 0)
+    out[:, 4] = np.minimum(t + k + flank, T.size)
+    out[:, 5] = np.maximum(q - flank, 0)
+    out[:, 6] = np.minimum(q + k + flank, Q.size)
+    return out, n_hits
+
+
 def seeds_array(seeds):
     """Seeds as an (n, 7) int64 array in SEED_FIELDS order."""
     if isinstance(seeds, np.ndarray) and seeds.dtype.names:

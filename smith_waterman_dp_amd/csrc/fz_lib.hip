@@ -14,8 +14,10 @@
 //   execute   in batches that fit the pointer workspace: pruned recompute
 //             with 4-bit pointers, then one lane per side walks them back
 //   gather    left ops + seed + reversed right ops, merged into CIGAR words
-// Local mode runs pack and one full-window kernel.
+// Local mode runs pack and one full-window kernel.  fz_find_seeds is the seed
+// stage before all this (fz_seeds.hpp).
 #include <hip/hip_runtime.h>
+#include <hipcub/hipcub.hpp>
 
 #include <algorithm>
 #include <cstdarg>
@@ -29,6 +31,7 @@
 #include "fz_device.hpp"
 #include "fz_extend.hpp"
 #include "fz_local.hpp"
+#include "fz_seeds.hpp"
 
 using namespace fz;
 
@@ -78,6 +81,11 @@ struct fz_ctx {
     DevBuf tasks, info, out, eager, side_trace, run_cap, run_off, run_len, runs;
     DevBuf items, batch_first, scan_tmp, cig, cigar, counters, ovl0, ovl1, bnd;
     DevBuf ptr_ws[EXEC_STREAMS];        // one pointer workspace per executor stream
+    // seed stage: target keys and positions (two of each for the sort), query
+    // keys, join ranges and counts, hits (two for the sort), run flags and
+    // ranks, library scratch, and the seeds of the last fz_find_seeds
+    DevBuf sk_tk, sk_tk2, sk_tp, sk_tp2, sk_qk, sk_lo, sk_cnt, sk_off, sk_hit, sk_hit2, sk_flag, sk_rank, sk_tmp, sk_out;
+    uint64_t last_seeds = 0;
     hipStream_t xs[EXEC_STREAMS - 1] = {};   // executor streams besides the caller's
     hipEvent_t fork_ev = nullptr, join_ev[EXEC_STREAMS - 1] = {};
     hipEvent_t ev[8] = {};
@@ -271,6 +279,129 @@ int run_local(fz_ctx *ctx, const fz_seed *seeds, uint64_t n, uint64_t tlen, uint
     return FZ_OK;
 }
 
+// The seed stage (fz_seeds.hpp), on `st`; synchronous at its two read-backs
+// and at the end.
+static int seeds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const uint8_t *query, uint64_t qlen,
+                      uint32_t k, int64_t flank, uint32_t flags, const fz_seed **seeds, uint64_t *n_seeds,
+                      uint64_t *n_hits, hipStream_t st)
+{
+    if (!n_seeds) return fail(ctx, FZ_EINVAL, "n_seeds is NULL");
+    *n_seeds = 0;
+    if (n_hits) *n_hits = 0;
+    if (seeds) *seeds = nullptr;
+    ctx->last_seeds = 0;
+    if (k < 1 || k > 32) return fail(ctx, FZ_EINVAL, "k must be 1..32 (got %u)", k);
+    if (flank < 0) return fail(ctx, FZ_EINVAL, "flank must be >= 0");
+    if (flags & ~(uint32_t)(FZ_QUERY_RC | FZ_SEEDS_ALL)) return fail(ctx, FZ_EINVAL, "unknown flag bits");
+    if ((tlen && !target) || (qlen && !query)) return fail(ctx, FZ_EINVAL, "NULL sequence");
+    if (tlen >= (1ull << 31) || qlen >= (1ull << 31))
+        return fail(ctx, FZ_EINVAL, "sequences must be shorter than 2^31 bases for the seed stage");
+    if (tlen < k || qlen < k) return FZ_OK;
+    const int64_t nt = (int64_t)(tlen - k + 1), nq = (int64_t)(qlen - k + 1);
+    const int64_t NT = (int64_t)tlen + 2 * PAD, NQ = (int64_t)qlen + 2 * PAD;
+
+    // codes, validated (the extension's own staging)
+    ENSURE(ctx->counters, sizeof(Counters));
+    Counters *dc = as<Counters>(ctx->counters);
+    int rc = zero(ctx, dc, sizeof(Counters), st);
+    if (rc) return rc;
+    ENSURE(ctx->Tf, NT + 64);
+    ENSURE(ctx->Tr, NT + 64);
+    ENSURE(ctx->Qf, NQ + 64);
+    ENSURE(ctx->Qr, NQ + 64);
+    pack_kernel<<<std::min<int64_t>(blocks_for(NT, 256), 8192), 256, 0, st>>>(
+        target, (int64_t)tlen, as<uint8_t>(ctx->Tf), as<uint8_t>(ctx->Tr), NT, &dc->err, 0);
+    pack_kernel<<<std::min<int64_t>(blocks_for(NQ, 256), 8192), 256, 0, st>>>(
+        query, (int64_t)qlen, as<uint8_t>(ctx->Qf), as<uint8_t>(ctx->Qr), NQ, &dc->err, (flags & FZ_QUERY_RC) ? 1 : 0);
+    HIP_OK(hipGetLastError());
+
+    // target keys, sorted with their positions
+    ENSURE(ctx->sk_tk, nt * sizeof(uint64_t));
+    ENSURE(ctx->sk_tk2, nt * sizeof(uint64_t));
+    ENSURE(ctx->sk_tp, nt * sizeof(uint32_t));
+    ENSURE(ctx->sk_tp2, nt * sizeof(uint32_t));
+    ENSURE(ctx->sk_qk, nq * sizeof(uint64_t));
+    const unsigned gb = 4 * (unsigned)ctx->n_cu * 4;
+    kmer_keys_kernel<<<gb, 256, 0, st>>>(as<uint8_t>(ctx->Tf) + PAD, nt, (int)k, as<uint64_t>(ctx->sk_tk),
+                                         as<uint32_t>(ctx->sk_tp));
+    kmer_keys_kernel<<<gb, 256, 0, st>>>(as<uint8_t>(ctx->Qf) + PAD, nq, (int)k, as<uint64_t>(ctx->sk_qk), nullptr);
+    HIP_OK(hipGetLastError());
+    size_t tmp_sort = 0, tmp_scan = 0, tmp_sort2 = 0;
+    HIP_OK(hipcub::DeviceRadixSort::SortPairs(nullptr, tmp_sort, as<uint64_t>(ctx->sk_tk), as<uint64_t>(ctx->sk_tk2),
+                                              as<uint32_t>(ctx->sk_tp), as<uint32_t>(ctx->sk_tp2), (int)nt, 0,
+                                              (int)(2 * k), st));
+    HIP_OK(hipcub::DeviceScan::ExclusiveSum(nullptr, tmp_scan, as<uint64_t>(ctx->sk_cnt), as<uint64_t>(ctx->sk_off),
+                                            (int)nq, st));
+    ENSURE(ctx->sk_tmp, std::max(tmp_sort, tmp_scan));
+    HIP_OK(hipcub::DeviceRadixSort::SortPairs(ctx->sk_tmp.p, tmp_sort, as<uint64_t>(ctx->sk_tk),
+                                              as<uint64_t>(ctx->sk_tk2), as<uint32_t>(ctx->sk_tp),
+                                              as<uint32_t>(ctx->sk_tp2), (int)nt, 0, (int)(2 * k), st));
+
+    // join: per query position, the range of equal target keys
+    ENSURE(ctx->sk_lo, nq * sizeof(uint32_t));
+    ENSURE(ctx->sk_cnt, nq * sizeof(uint64_t));
+    ENSURE(ctx->sk_off, nq * sizeof(uint64_t));
+    join_count_kernel<<<gb, 256, 0, st>>>(as<uint64_t>(ctx->sk_tk2), nt, as<uint64_t>(ctx->sk_qk), nq,
+                                          as<uint32_t>(ctx->sk_lo), as<uint64_t>(ctx->sk_cnt));
+    HIP_OK(hipGetLastError());
+    tmp_scan = ctx->sk_tmp.cap;
+    HIP_OK(hipcub::DeviceScan::ExclusiveSum(ctx->sk_tmp.p, tmp_scan, as<uint64_t>(ctx->sk_cnt),
+                                            as<uint64_t>(ctx->sk_off), (int)nq, st));
+    uint64_t last[2] = {0, 0};
+    HIP_OK(hipMemcpyAsync(&last[0], as<uint64_t>(ctx->sk_off) + (nq - 1), sizeof(uint64_t), hipMemcpyDeviceToHost, st));
+    HIP_OK(hipMemcpyAsync(&last[1], as<uint64_t>(ctx->sk_cnt) + (nq - 1), sizeof(uint64_t), hipMemcpyDeviceToHost, st));
+    Counters hc;
+    HIP_OK(hipMemcpyAsync(&hc, dc, sizeof(Counters), hipMemcpyDeviceToHost, st));
+    HIP_OK(hipStreamSynchronize(st));
+    if (hc.err & 1u) return fail(ctx, FZ_EINVAL, "sequence holds a byte other than A, C, G, T");
+    const uint64_t H = last[0] + last[1];
+    if (n_hits) *n_hits = H;
+    if (H == 0) return FZ_OK;
+    if (H >= (1ull << 31)) return fail(ctx, FZ_ENOMEM, "%llu shared k-mer hits: more than the stage handles (2^31)",
+                                       (unsigned long long)H);
+
+    // hits, sorted by diagonal then t; run starts; their ranks
+    ENSURE(ctx->sk_hit, H * sizeof(uint64_t));
+    ENSURE(ctx->sk_hit2, H * sizeof(uint64_t));
+    ENSURE(ctx->sk_flag, H * sizeof(uint64_t));
+    ENSURE(ctx->sk_rank, H * sizeof(uint64_t));
+    emit_hits_kernel<<<gb, 256, 0, st>>>(as<uint32_t>(ctx->sk_tp2), as<uint32_t>(ctx->sk_lo),
+                                         as<uint64_t>(ctx->sk_cnt), as<uint64_t>(ctx->sk_off), nq, (int64_t)qlen,
+                                         as<uint64_t>(ctx->sk_hit));
+    HIP_OK(hipGetLastError());
+    HIP_OK(hipcub::DeviceRadixSort::SortKeys(nullptr, tmp_sort2, as<uint64_t>(ctx->sk_hit),
+                                             as<uint64_t>(ctx->sk_hit2), (int)H, 0, 64, st));
+    size_t tmp_scan2 = 0;
+    HIP_OK(hipcub::DeviceScan::ExclusiveSum(nullptr, tmp_scan2, as<uint64_t>(ctx->sk_flag),
+                                            as<uint64_t>(ctx->sk_rank), (int)H, st));
+    ENSURE(ctx->sk_tmp, std::max(tmp_sort2, tmp_scan2));
+    size_t t2 = ctx->sk_tmp.cap;
+    HIP_OK(hipcub::DeviceRadixSort::SortKeys(ctx->sk_tmp.p, t2, as<uint64_t>(ctx->sk_hit), as<uint64_t>(ctx->sk_hit2),
+                                             (int)H, 0, 64, st));
+    run_start_kernel<<<gb, 256, 0, st>>>(as<uint64_t>(ctx->sk_hit2), (int64_t)H, (flags & FZ_SEEDS_ALL) ? 0 : 1,
+                                         as<uint64_t>(ctx->sk_flag));
+    HIP_OK(hipGetLastError());
+    t2 = ctx->sk_tmp.cap;
+    HIP_OK(hipcub::DeviceScan::ExclusiveSum(ctx->sk_tmp.p, t2, as<uint64_t>(ctx->sk_flag), as<uint64_t>(ctx->sk_rank),
+                                            (int)H, st));
+    HIP_OK(hipMemcpyAsync(&last[0], as<uint64_t>(ctx->sk_rank) + (H - 1), sizeof(uint64_t), hipMemcpyDeviceToHost, st));
+    HIP_OK(hipMemcpyAsync(&last[1], as<uint64_t>(ctx->sk_flag) + (H - 1), sizeof(uint64_t), hipMemcpyDeviceToHost, st));
+    HIP_OK(hipStreamSynchronize(st));
+    const uint64_t n = last[0] + last[1];
+
+    // the seed records
+    ENSURE(ctx->sk_out, n * sizeof(fz_seed));
+    write_seeds_kernel<<<gb, 256, 0, st>>>(as<uint64_t>(ctx->sk_hit2), as<uint64_t>(ctx->sk_flag),
+                                           as<uint64_t>(ctx->sk_rank), (int64_t)H, (int)k, flank, (int64_t)tlen,
+                                           (int64_t)qlen, as<fz_seed>(ctx->sk_out));
+    HIP_OK(hipGetLastError());
+    HIP_OK(hipStreamSynchronize(st));
+    ctx->last_seeds = n;
+    *n_seeds = n;
+    if (seeds) *seeds = as<fz_seed>(ctx->sk_out);
+    return FZ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -332,7 +463,10 @@ void fz_destroy(fz_ctx *ctx)
     DevBuf *bufs[] = {&ctx->Tf, &ctx->Tr, &ctx->Qf, &ctx->Qr, &ctx->tasks, &ctx->info, &ctx->out,
                       &ctx->eager, &ctx->side_trace, &ctx->run_cap, &ctx->run_off, &ctx->run_len, &ctx->runs,
                       &ctx->items, &ctx->batch_first, &ctx->scan_tmp, &ctx->cig, &ctx->cigar,
-                      &ctx->counters, &ctx->ovl0, &ctx->ovl1, &ctx->bnd};
+                      &ctx->counters, &ctx->ovl0, &ctx->ovl1, &ctx->bnd,
+                      &ctx->sk_tk, &ctx->sk_tk2, &ctx->sk_tp, &ctx->sk_tp2, &ctx->sk_qk, &ctx->sk_lo, &ctx->sk_cnt,
+                      &ctx->sk_off, &ctx->sk_hit, &ctx->sk_hit2, &ctx->sk_flag, &ctx->sk_rank, &ctx->sk_tmp,
+                      &ctx->sk_out};
     for (auto &x : ctx->xs)
         if (x) (void)hipStreamSynchronize(x);
     for (DevBuf *b : bufs)
@@ -681,6 +815,40 @@ int fz_extend_batch(fz_ctx *ctx, const uint8_t *target, uint64_t target_len, con
                                min_traceback_score, flags, hits, cigar, cigar_words, stats, (hipStream_t)stream);
     if (prev != ctx->device) (void)hipSetDevice(prev);
     return rc;
+}
+
+int fz_find_seeds(fz_ctx *ctx, const uint8_t *target, uint64_t target_len, const uint8_t *query, uint64_t query_len,
+                  uint32_t k, int64_t flank, uint32_t flags, const fz_seed **seeds, uint64_t *n_seeds,
+                  uint64_t *n_hits, void *stream)
+{
+    if (!ctx) return FZ_EINVAL;
+    ctx->err.clear();
+    int prev = 0;
+    if (hipGetDevice(&prev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ctx, FZ_EDEVICE, "hipGetDevice failed");
+    }
+    if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ctx, FZ_EDEVICE, "hipSetDevice(%d) failed", ctx->device);
+    }
+    const int rc = seeds_impl(ctx, target, target_len, query, query_len, k, flank, flags, seeds, n_seeds, n_hits,
+                              (hipStream_t)stream);
+    if (prev != ctx->device) (void)hipSetDevice(prev);
+    return rc;
+}
+
+int fz_copy_seeds(fz_ctx *ctx, fz_seed *dst, uint64_t n, void *stream)
+{
+    if (!ctx) return FZ_EINVAL;
+    if (n > ctx->last_seeds) return fail(ctx, FZ_EINVAL, "asked for %llu seeds, the last seed stage found %llu",
+                                         (unsigned long long)n, (unsigned long long)ctx->last_seeds);
+    if (n == 0) return FZ_OK;
+    if (!dst) return fail(ctx, FZ_EINVAL, "dst is NULL");
+    hipStream_t st = (hipStream_t)stream;
+    HIP_OK(hipMemcpyAsync(dst, ctx->sk_out.p, n * sizeof(fz_seed), hipMemcpyDeviceToDevice, st));
+    HIP_OK(hipStreamSynchronize(st));
+    return FZ_OK;
 }
 
 int fz_copy_cigar(fz_ctx *ctx, uint32_t *dst, uint64_t words, void *stream)

@@ -1,0 +1,115 @@
+// fz_seeds.hpp -- the seed stage on gfx950: shared k-mers of target and query
+// and their diagonal dedup.
+//
+// FastZ (SC'21), section 2: whole-genome alignment first finds short exact
+// matches (19 bases) between the two sequences as seed sites, then filters
+// them, then extends the survivors with the gapped DP.  This file is the
+// first step plus the plainest filter, one seed per run of hits on one
+// diagonal:
+//   keys    the k codes at every start position as one base-4 number
+//   sort    the target's (key, position) pairs by key (device radix sort)
+//   join    per query position, the range of equal target keys by binary
+//           search; counts, their exclusive scan, then every hit written as
+//           one 64-bit word ((t - q + query_len) << 32 | t)
+//   sort    the hit words, which orders hits by diagonal and then by t
+//   runs    a hit starts a run unless its word is the previous word + 1
+//           (same diagonal, t one further): one seed per run
+// The stage is bound by memory traffic (keys and hits through the sorts);
+// nothing here is arithmetic-heavy.
+#pragma once
+
+#include <stdint.h>
+
+#include "fz_device.hpp"
+
+namespace fz {
+
+// key of every start position p < nkeys: codes[p .. p+k-1], first base most
+// significant (k <= 32, two bits per base)
+__global__ void kmer_keys_kernel(const uint8_t *__restrict__ codes, int64_t nkeys, int k, uint64_t *__restrict__ keys,
+                                 uint32_t *__restrict__ pos)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < nkeys; p += stride) {
+        uint64_t key = 0;
+        for (int i = 0; i < k; ++i) key = (key << 2) | (uint64_t)codes[p + i];
+        keys[p] = key;
+        if (pos) pos[p] = (uint32_t)p;
+    }
+}
+
+// For every query position: where its key's run starts in the sorted target
+// keys, and how long it is.
+__global__ void join_count_kernel(const uint64_t *__restrict__ tkeys, int64_t nt, const uint64_t *__restrict__ qkeys,
+                                  int64_t nq, uint32_t *__restrict__ lo_out, uint64_t *__restrict__ cnt)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nq; q += stride) {
+        const uint64_t key = qkeys[q];
+        int64_t a = 0, b = nt;              // first index with tkeys >= key
+        while (a < b) {
+            const int64_t m = (a + b) >> 1;
+            if (tkeys[m] < key) a = m + 1;
+            else b = m;
+        }
+        int64_t c = a, e = nt;              // first index with tkeys > key
+        while (c < e) {
+            const int64_t m = (c + e) >> 1;
+            if (tkeys[m] <= key) c = m + 1;
+            else e = m;
+        }
+        lo_out[q] = (uint32_t)a;
+        cnt[q] = (uint64_t)(c - a);
+    }
+}
+
+// Every hit of query position q as ((t - q + qlen) << 32) | t.
+__global__ void emit_hits_kernel(const uint32_t *__restrict__ tpos, const uint32_t *__restrict__ lo,
+                                 const uint64_t *__restrict__ cnt, const uint64_t *__restrict__ off, int64_t nq,
+                                 int64_t qlen, uint64_t *__restrict__ hits)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nq; q += stride) {
+        const uint64_t c = cnt[q];
+        const uint64_t base = off[q];
+        const uint32_t l = lo[q];
+        for (uint64_t i = 0; i < c; ++i) {
+            const uint64_t t = tpos[l + i];
+            hits[base + i] = ((t - (uint64_t)q + (uint64_t)qlen) << 32) | t;
+        }
+    }
+}
+
+// 1 where a hit starts a run on its diagonal (or every hit, without dedup).
+__global__ void run_start_kernel(const uint64_t *__restrict__ hits, int64_t n, int dedup, uint64_t *__restrict__ flag)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        flag[i] = (!dedup || i == 0 || hits[i] != hits[i - 1] + 1) ? 1u : 0u;
+}
+
+// The selected hits as seed records, in hit order, windows +-flank clipped
+// to the sequences.
+__global__ void write_seeds_kernel(const uint64_t *__restrict__ hits, const uint64_t *__restrict__ flag,
+                                   const uint64_t *__restrict__ rank, int64_t n, int k, int64_t flank, int64_t tlen,
+                                   int64_t qlen, fz_seed *__restrict__ out)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        if (!flag[i]) continue;
+        const int64_t t = (int64_t)(hits[i] & 0xffffffffull);
+        const int64_t diag = (int64_t)(hits[i] >> 32) - qlen;
+        const int64_t q = t - diag;
+        fz_seed s;
+        s.t_pos = t;
+        s.q_pos = q;
+        s.seed_len = k;
+        s.t_lo = t - flank > 0 ? t - flank : 0;
+        s.t_hi = t + k + flank < tlen ? t + k + flank : tlen;
+        s.q_lo = q - flank > 0 ? q - flank : 0;
+        s.q_hi = q + k + flank < qlen ? q + k + flank : qlen;
+        out[rank[i]] = s;
+    }
+}
+
+}  // namespace fz

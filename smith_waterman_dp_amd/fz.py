@@ -11,7 +11,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfz.so")
 
-FZ_TRACEBACK, FZ_LOCAL, FZ_STATS, FZ_QUERY_RC = 1, 2, 4, 8
+FZ_TRACEBACK, FZ_LOCAL, FZ_STATS, FZ_QUERY_RC, FZ_SEEDS_ALL = 1, 2, 4, 8, 16
 FZ_OK, FZ_EINVAL, FZ_ENOMEM, FZ_EDEVICE, FZ_EBAND = 0, -1, -2, -3, -4
 FZ_HIT_TRACED, FZ_HIT_EAGER_LEFT, FZ_HIT_EAGER_RIGHT = 1, 2, 4
 FZ_HIT_BELOW_MIN, FZ_HIT_EBAND, FZ_HIT_ESEED, FZ_HIT_ERANGE = 8, 16, 32, 64
@@ -23,7 +23,7 @@ SEED_FIELDS = ["t_pos", "q_pos", "seed_len", "t_lo", "t_hi", "q_lo", "q_hi"]
 
 # every symbol include/fz.h declares
 EXPORTS = ["fz_create", "fz_destroy", "fz_last_error", "fz_set_pointer_workspace", "fz_extend_batch",
-           "fz_copy_cigar"]
+           "fz_find_seeds", "fz_copy_seeds", "fz_copy_cigar"]
 
 
 class fz_scoring(ctypes.Structure):
@@ -78,6 +78,11 @@ def load_library(path=LIB_PATH):
                                     ctypes.POINTER(fz_stats), P]
     lib.fz_copy_cigar.restype = ctypes.c_int
     lib.fz_copy_cigar.argtypes = [P, P, u64, P]
+    lib.fz_find_seeds.restype = ctypes.c_int
+    lib.fz_find_seeds.argtypes = [P, P, u64, P, u64, ctypes.c_uint32, i64, ctypes.c_uint32, ctypes.POINTER(P),
+                                  ctypes.POINTER(u64), ctypes.POINTER(u64), P]
+    lib.fz_copy_seeds.restype = ctypes.c_int
+    lib.fz_copy_seeds.argtypes = [P, P, u64, P]
     _lib = lib
     return lib
 
@@ -156,6 +161,34 @@ def fz_extend_batch(ctx, target, query, seeds, scoring, ydrop, min_traceback_sco
     return hits, cigar, (st.as_dict() if want_stats else None)
 
 
+def fz_find_seeds(ctx, target, query, k=19, flank=32768, flags=0, stream=None):
+    """The seed stage: shared k-mers of target and query (of the query's
+    reverse complement with FZ_QUERY_RC), one per diagonal run unless
+    FZ_SEEDS_ALL.  target, query: uint8 CUDA tensors of ASCII bases.
+    Returns (seeds, n_hits): seeds an int64 (n, 7) CUDA tensor in
+    SEED_FIELDS order, ordered by diagonal t - q then t."""
+    import torch
+    lib = load_library()
+    for name, t in (("target", target), ("query", query)):
+        if not t.is_cuda or t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous uint8 CUDA tensor" % name)
+    ptr = ctypes.c_void_p()
+    n = ctypes.c_uint64(0)
+    hits = ctypes.c_uint64(0)
+    strm = _stream_handle(stream)
+    _check(ctx, lib.fz_find_seeds(ctx, target.data_ptr(), target.numel(), query.data_ptr(), query.numel(), int(k),
+                                  int(flank), int(flags), ctypes.byref(ptr), ctypes.byref(n), ctypes.byref(hits),
+                                  strm))
+    seeds = torch.empty((n.value, len(SEED_FIELDS)), dtype=torch.int64, device=target.device)
+    if n.value:
+        _check(ctx, lib.fz_copy_seeds(ctx, seeds.data_ptr(), n.value, strm))
+    return seeds, hits.value
+
+
+def fz_copy_seeds(ctx, dst, n, stream=None):
+    _check(ctx, load_library().fz_copy_seeds(ctx, dst.data_ptr(), int(n), _stream_handle(stream)))
+
+
 def fz_copy_cigar(ctx, dst, words, stream=None):
     _check(ctx, load_library().fz_copy_cigar(ctx, dst.data_ptr(), int(words), _stream_handle(stream)))
 
@@ -184,6 +217,13 @@ class Context:
         flags = (FZ_TRACEBACK if traceback else 0) | (FZ_QUERY_RC if query_rc else 0)
         return fz_extend_batch(self.h, target, query, seeds, scoring, ydrop, min_traceback_score, flags,
                                stream, want_stats)
+
+    def find_seeds(self, target, query, k=19, flank=32768, dedup=True, query_rc=False, stream=None):
+        """Seeds from shared k-mers (FZ_QUERY_RC: on the query's reverse
+        complement); returns (seeds (n, 7) int64 CUDA tensor, hits before the
+        diagonal dedup)."""
+        flags = (0 if dedup else FZ_SEEDS_ALL) | (FZ_QUERY_RC if query_rc else 0)
+        return fz_find_seeds(self.h, target, query, k, flank, flags, stream)
 
     def local(self, target, query, seeds, scoring, stream=None, want_stats=False, query_rc=False):
         flags = FZ_LOCAL | (FZ_QUERY_RC if query_rc else 0)

@@ -1,0 +1,111 @@
+"""GPU parity of the seed stage (fz_find_seeds) against the oracle's
+find_seeds: the same seed records in the same order, bit for bit, and the
+same hit count, on random pairs with repeats, both strands, with and
+without the diagonal dedup, and on the chromosome pair at reduced and full
+size; plus the error paths."""
+import random
+
+import numpy as np
+import pytest
+
+import oracle
+from smith_waterman_dp_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+from smith_waterman_dp_amd import fz  # noqa: E402
+
+
+def log(msg):
+    print("[gpu] " + msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.zeros(1, device="cuda:0").add_(1)
+    torch.cuda.synchronize()
+    c = fz.Context(0)
+    yield c
+    c.close()
+
+
+def dev(a):
+    if isinstance(a, str):
+        a = np.frombuffer(a.encode(), dtype=np.uint8)
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def check(ctx, T, Q, k, flank, dedup, rc, label):
+    log("%s: target %d, query %d, k %d, dedup %d, rc %d" % (label, len(T), len(Q), k, dedup, rc))
+    got, hits = ctx.find_seeds(dev(T), dev(Q), k=k, flank=flank, dedup=dedup, query_rc=rc)
+    exp, ehits = oracle.find_seeds(T, Q, k=k, flank=flank, dedup=dedup, query_rc=rc)
+    got = got.cpu().numpy()
+    assert hits == ehits, "%s: %d hits, oracle %d" % (label, hits, ehits)
+    assert got.shape == exp.shape, "%s: %s seeds, oracle %s" % (label, got.shape, exp.shape)
+    assert np.array_equal(got, exp), "%s: first difference at %s" % (
+        label, int(np.nonzero((got != exp).any(axis=1))[0][0]))
+    return got
+
+
+def repeat_pair(seed, n=4000):
+    rng = random.Random(seed)
+    T = "".join(rng.choice("ACGT") for _ in range(n))
+    reps = ["".join(rng.choice("ACGT") for _ in range(rng.randint(20, 60))) for _ in range(6)]
+    T = list(T)
+    for r in reps:
+        for _ in range(8):
+            p = rng.randrange(0, n - len(r))
+            T[p:p + len(r)] = r
+    T = "".join(T)
+    Q = list(T[500:3500])
+    for _ in range(150):
+        Q[rng.randrange(len(Q))] = rng.choice("ACGT")
+    Q = "".join(Q) + oracle.revcomp(T[100:900]).tobytes().decode() + "A" * 40
+    return T, Q
+
+
+@pytest.mark.parametrize("k", [3, 8, 19, 32])
+def test_seeds_repeat_pairs(ctx, k):
+    T, Q = repeat_pair(k)
+    for dedup in (True, False):
+        for rc in (False, True):
+            check(ctx, T, Q, k, 500, dedup, rc, "repeats k=%d" % k)
+
+
+def test_seeds_chromosome_reduced(ctx):
+    w = W.chromosome(length=600_000, inv_min=5_000, inv_max=20_000, seed=3)
+    fwd = check(ctx, w["target"], w["query"], 19, 32768, True, False, "chromosome 600 kb")
+    # the generator's own join gives the same seeds (a second, independent join)
+    assert np.array_equal(fwd, w["seeds"])
+    rc = check(ctx, w["target"], w["query"], 19, 32768, True, True, "chromosome 600 kb rc")
+    wr = W.chromosome_rc(length=600_000, inv_min=5_000, inv_max=20_000, seed=3)
+    assert np.array_equal(rc, wr["seeds"])
+
+
+def test_seeds_chromosome_full_size(ctx):
+    """Two 20 Mbp chromosomes, both strands, every seed compared."""
+    log("generating the chromosome pair")
+    w = W.chromosome()
+    check(ctx, w["target"], w["query"], 19, 32768, True, False, "chromosome 20 Mbp")
+    check(ctx, w["target"], w["query"], 19, 32768, True, True, "chromosome 20 Mbp rc")
+
+
+def test_seeds_edges_and_errors(ctx):
+    T, Q = "ACGTACGTAC", "CGTACG"
+    check(ctx, T, Q, 3, 2, True, False, "tiny")
+    check(ctx, T, Q, 6, 0, False, False, "tiny k=6")
+    s, h = ctx.find_seeds(dev("ACG"), dev("ACGTT"), k=4)          # target shorter than k
+    assert s.shape == (0, 7) and h == 0
+    s, h = ctx.find_seeds(dev("AAAA"), dev("CCCC"), k=2)          # no shared k-mer
+    assert s.shape == (0, 7) and h == 0
+    for k in (0, 33):
+        with pytest.raises(fz.FzError) as e:
+            ctx.find_seeds(dev(T), dev(Q), k=k)
+        assert e.value.code == fz.FZ_EINVAL
+    with pytest.raises(fz.FzError) as e:
+        ctx.find_seeds(dev("ACGTNACGT"), dev(Q), k=3)
+    assert e.value.code == fz.FZ_EINVAL
+    # the context stays usable after an error
+    check(ctx, T, Q, 3, 2, True, True, "after errors")

@@ -416,3 +416,67 @@ def test_strand_symmetry(seed):
         c1 = w1[o1[k]:o1[k] + a["n_runs"]]
         c2 = w2[o2[k]:o2[k] + b["n_runs"]]
         assert np.array_equal(c1[::-1], c2)
+
+
+# ---------------------------------------------------------- seed stage --
+
+def test_find_seeds_hand_example():
+    """T = ACGTACGT, Q = CGTA, k = 3: CGT at t 1 and 5 matches q 0, GTA at
+    t 2 matches q 1.  Diagonal 1 holds (1, 0) and (2, 1), one run, so the
+    dedup keeps (1, 0); (5, 0) is alone on diagonal 5."""
+    s, n = oracle.find_seeds("ACGTACGT", "CGTA", k=3, flank=2, dedup=False)
+    assert n == 3
+    assert s[:, :2].tolist() == [[1, 0], [2, 1], [5, 0]]
+    s, n = oracle.find_seeds("ACGTACGT", "CGTA", k=3, flank=2, dedup=True)
+    assert s.tolist() == [[1, 0, 3, 0, 6, 0, 4], [5, 0, 3, 3, 8, 0, 4]]
+
+
+def _seeds_by_enumeration(T, Q, k, flank, dedup):
+    """Every start pair compared as strings, ordered by (t - q, t), runs cut
+    by a walk: the definition written out with loops."""
+    T, Q = T.upper(), Q.upper()
+    hits = []
+    for t in range(len(T) - k + 1):
+        for q in range(len(Q) - k + 1):
+            if T[t:t + k] == Q[q:q + k]:
+                hits.append((t - q, t, q))
+    hits.sort()
+    out = []
+    prev = None
+    for dg, t, q in hits:
+        if not (dedup and prev is not None and prev[0] == dg and prev[1] == t - 1):
+            out.append([t, q, k, max(t - flank, 0), min(t + k + flank, len(T)), max(q - flank, 0),
+                        min(q + k + flank, len(Q))])
+        prev = (dg, t)
+    return out, len(hits)
+
+
+@pytest.mark.parametrize("seed,k", [(0, 3), (1, 5), (2, 8), (3, 4)])
+def test_find_seeds_enumeration(seed, k):
+    """Random pairs with planted repeats and mutated copies, against the
+    enumeration of all start pairs."""
+    rng = random.Random(seed)
+    T = "".join(rng.choice("ACGT") for _ in range(150))
+    rep = "".join(rng.choice("ACGT") for _ in range(12))
+    T = T[:30] + rep + T[42:90] + rep + T[102:]
+    Q = list(T[20:140])
+    for _ in range(10):
+        Q[rng.randrange(len(Q))] = rng.choice("ACGT")
+    Q = "".join(Q) + rep.lower()
+    for dedup in (False, True):
+        got, n = oracle.find_seeds(T, Q, k=k, flank=7, dedup=dedup)
+        exp, ne = _seeds_by_enumeration(T, Q, k, 7, dedup)
+        assert n == ne
+        assert got.tolist() == exp
+
+
+def test_find_seeds_reverse_strand_and_edges():
+    rng = random.Random(9)
+    T = "".join(rng.choice("ACGT") for _ in range(200))
+    Q = "".join(rng.choice("ACGT") for _ in range(180))
+    a, na = oracle.find_seeds(T, Q, k=4, flank=5, query_rc=True)
+    b, nb = oracle.find_seeds(T, oracle.revcomp(Q).tobytes(), k=4, flank=5)
+    assert na == nb and np.array_equal(a, b)
+    assert oracle.find_seeds("ACG", "ACGT", k=4)[0].shape == (0, 7)        # target shorter than k
+    with pytest.raises(ValueError):
+        oracle.find_seeds("ACGN", "ACGT", k=2)
