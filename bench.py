@@ -13,6 +13,8 @@ Workloads (seeded, synthetic; see smith_waterman_dp_amd/workloads.py):
   local           4,096 full-matrix local alignments of 2048 x 2048
   tiny, executor_heavy, chromosome
   chromosome_rc   the chromosome pair searched on the query's reverse strand
+  seeds           the seed stage (fz_find_seeds) on the 20 Mbp chromosome pair,
+                  both strands per step; reported in Mbp/s of target + query
 """
 import argparse
 import json
@@ -50,13 +52,27 @@ TRAFFIC_FETCH_BYTES = 2.121e6 * 1024 / 0.5
 TRAFFIC_WRITE_BYTES = 1.704e5 * 1024 / 1.0
 
 
-def kernel_src_hash():
-    """sha256 over the two files' sha256 hex digests, first 16 hex digits."""
+# The same for one join_count_kernel launch of the seed stage on the 20 Mbp
+# chromosome pair (mean of the forward and reverse-strand launches), valid
+# for the sources hashed from fz_seeds.hpp.
+SEED_TRAFFIC_SRC_HASH = "e1ff44293a6376ae"
+SEED_TRAFFIC_FETCH_BYTES = 1.910e6 * 1024 / 0.5
+SEED_TRAFFIC_WRITE_BYTES = 2.344e5 * 1024 / 1.0
+
+
+def kernel_src_hash(files=("fz_extend.hpp", "fz_device.hpp")):
+    """sha256 over the files' sha256 hex digests, first 16 hex digits."""
     import hashlib
     d = os.path.join(ROOT, "smith_waterman_dp_amd", "csrc")
     digests = "".join(hashlib.sha256(open(os.path.join(d, f), "rb").read()).hexdigest()
-                      for f in ("fz_extend.hpp", "fz_device.hpp"))
+                      for f in files)
     return hashlib.sha256(digests.encode()).hexdigest()[:16]
+
+
+def measured_traffic(fetch, write, seconds):
+    tot = fetch + write
+    return {"bytes_per_launch": int(tot), "fetch_bytes": int(fetch), "write_bytes": int(write),
+            "gb_per_s": round(tot / seconds / 1e9, 2), "hbm_frac": round(tot / seconds / 8e12, 5)}
 
 
 def parse():
@@ -65,7 +81,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="skewed",
-                    choices=["skewed", "local", "tiny", "executor_heavy", "chromosome", "chromosome_rc"])
+                    choices=["skewed", "local", "tiny", "executor_heavy", "chromosome", "chromosome_rc", "seeds"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -112,12 +128,126 @@ def cpu_baseline(w, target_seconds, local):
                       % (done, n, dt, done_cells, done / dt)}
 
 
+def copy_probe(mib, dev):
+    """One plain device-to-device copy of `mib` MiB (a known-size reference
+    for the HBM traffic counters), or nothing for 0."""
+    if mib <= 0:
+        return
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+SEED_PHASES = ("pack", "keys", "sort_keys", "index", "join", "scan", "emit", "sort_hits", "runs", "write")
+
+
+def cpu_seed_baseline(w, target_seconds):
+    """The oracle's seed stage, as it stands, on growing prefixes of the pair
+    (both strands each), until one run passes half the target time."""
+    import oracle
+    L = 1 << 20
+    full = min(w["target"].size, w["query"].size)
+    while True:
+        L = min(L, full)
+        t0 = time.time()
+        for rc in (False, True):
+            oracle.find_seeds(w["target"][:L], w["query"][:L], w["k"], w["flank"], query_rc=rc)
+        dt = time.time() - t0
+        if dt > target_seconds / 2 or L == full:
+            break
+        L *= 2
+    return {"value": round(2 * L / dt / 1e6, 3), "unit": "Mbp/s", "cores": 1, "kind": "oracle",
+            "sample": "first %d bases of target and query, both strands, %.1f s (numpy, one thread)" % (L, dt)}
+
+
+def bench_seeds(a):
+    import numpy as np
+    import torch
+
+    from smith_waterman_dp_amd import fz
+    from smith_waterman_dp_amd import workloads as W
+
+    steps = a.steps if a.steps is not None else 10
+    print("[bench] generating the 20 Mbp chromosome pair", file=sys.stderr, flush=True)
+    w = W.chromosome_seed_stage()
+    dev = torch.device("cuda:0")
+    T = torch.from_numpy(w["target"]).to(dev)
+    Q = torch.from_numpy(w["query"]).to(dev)
+    ctx = fz.Context(0)
+
+    def step():
+        # the reverse strand reuses the target index the forward call built
+        out = []
+        for rc in (False, True):
+            out.append(ctx.find_seeds(T, Q, w["k"], w["flank"], query_rc=rc, want_stats=True, reuse_index=rc))
+        return out
+
+    for k in range(a.warmup):
+        step()
+        print("[bench] warmup %d done" % k, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    phases = {p: [] for p in SEED_PHASES}
+    t0 = time.perf_counter()
+    res = None
+    for k in range(steps):
+        res = step()
+        for _, _, st in res:
+            for p in SEED_PHASES:
+                phases[p].append(st["ms_" + p])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    copy_probe(a.copy_probe, dev)
+    ms_per_step = dt / steps * 1e3
+    bases = int(w["target"].size + w["query"].size)
+    nt = w["target"].size - w["k"] + 1
+    nq = w["query"].size - w["k"] + 1
+    hits = [h for _, h, _ in res]
+    n_seeds = [int(s.shape[0]) for s, _, _ in res]
+    mean = {p: float(np.mean(v)) for p, v in phases.items()}
+    # HBM roofline of the join kernel, the longest single launch of the
+    # stage: per query position it reads the position's code (1 B; its k-1
+    # neighbours are shared with the next positions) and writes the range
+    # start (4 B) and the count (8 B); the bucket table (4 B per bucket) and
+    # the sorted target keys (8 B each) are counted once, the least any
+    # lookup of every query key must read.
+    nb_bits = 1
+    while nb_bits < 30 and (1 << nb_bits) < nt:
+        nb_bits += 1
+    nb = 1 << min(nb_bits, 2 * w["k"])
+    join_bytes = 13 * nq + 4 * (nb + 1) + 8 * nt
+    achieved = join_bytes / (mean["join"] / 1e3) / 1e9
+    traffic = None
+    if kernel_src_hash(("fz_seeds.hpp",)) == SEED_TRAFFIC_SRC_HASH:
+        traffic = measured_traffic(SEED_TRAFFIC_FETCH_BYTES, SEED_TRAFFIC_WRITE_BYTES, mean["join"] / 1e3)
+    cfg = {"workload": "chromosome_seed_stage", "target_bp": int(w["target"].size), "query_bp": int(w["query"].size),
+           "k": w["k"], "flank": w["flank"], "strands": 2, "hits": hits, "seeds": n_seeds,
+           "phase_ms": {p: round(v, 3) for p, v in mean.items()}}
+    out = {"metric": "seed stage throughput on a 20 Mbp chromosome pair, both strands, 1 MI355X",
+           "value": round(bases / (ms_per_step / 1e3) / 1e6, 3), "unit": "Mbp/s", "n_gpus": 1, "steps": steps,
+           "warmup": a.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "u64", "data": "synthetic", "config": cfg,
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": 8000.0, "unit": "GB/s",
+                        "frac": round(achieved / 8000.0, 4), "traffic": traffic, "kernel": "join_count_kernel",
+                        "bytes_per_launch": join_bytes}}
+    if not a.no_cpu:
+        print("[bench] CPU oracle sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_seed_baseline(w, a.cpu_seconds)
+    ctx.close()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d refused)" % a.gpus,
               file=sys.stderr)
         sys.exit(2)
+    if a.workload == "seeds":
+        return bench_seeds(a)
     import numpy as np
     import torch
 
@@ -157,14 +287,7 @@ def main():
         main_ms.append(st["ms_main"])
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    if a.copy_probe > 0:
-        src = torch.empty(a.copy_probe << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_probe(a.copy_probe, dev)
     h = hits.cpu().numpy()
     cells = int(h[:, 8].sum())
     n = len(w["seeds"])
@@ -176,10 +299,7 @@ def main():
     peak = VALU_PEAK_OPS / 1e12
     traffic = None
     if a.workload == "skewed" and kernel_src_hash() == TRAFFIC_SRC_HASH:
-        traffic = {"bytes_per_launch": int(TRAFFIC_FETCH_BYTES + TRAFFIC_WRITE_BYTES),
-                   "fetch_bytes": int(TRAFFIC_FETCH_BYTES), "write_bytes": int(TRAFFIC_WRITE_BYTES),
-                   "gb_per_s": round((TRAFFIC_FETCH_BYTES + TRAFFIC_WRITE_BYTES) / kern_s / 1e9, 2),
-                   "hbm_frac": round((TRAFFIC_FETCH_BYTES + TRAFFIC_WRITE_BYTES) / kern_s / 8e12, 5)}
+        traffic = measured_traffic(TRAFFIC_FETCH_BYTES, TRAFFIC_WRITE_BYTES, kern_s)
     cfg = {"workload": a.workload, "records": n, "target_bp": int(w["target"].size), "query_bp": int(w["query"].size),
            "cells_per_step": cells, "scoring": w["scoring"], "ydrop": None if local else w["ydrop"],
            "min_traceback_score": w.get("min_tb"), "main_kernel_ms": round(kern_s * 1e3, 3)}

@@ -99,12 +99,29 @@ typedef struct {
     float ms_main;                 /* the dominant kernel alone (inspector, or the local kernel) */
 } fz_stats;
 
+/* Phase times of one fz_find_seeds call, milliseconds between HIP events on
+ * the call's stream.  A phase that did not run (no hits) reads 0. */
+typedef struct {
+    float ms_pack;                 /* ASCII -> codes, both sequences, validation */
+    float ms_keys;                 /* k-mer key of every target start position */
+    float ms_sort_keys;            /* radix sort of the target's (key, position) pairs */
+    float ms_index;                /* bucket table over the sorted keys' top bits */
+    float ms_join;                 /* per query position, its key and range of equal target keys */
+    float ms_scan;                 /* exclusive scan of the per-position hit counts */
+    float ms_emit;                 /* every hit written as one 64-bit word */
+    float ms_sort_hits;            /* radix sort of the hit words (diagonal, then t) */
+    float ms_runs;                 /* run starts on each diagonal and their ranks */
+    float ms_write;                /* the seed records */
+    float ms_total;                /* first to last event, the count read-back included */
+} fz_seed_stats;
+
 enum {
     FZ_TRACEBACK = 1u << 0,        /* CIGAR for every seed whose score > min_traceback_score */
     FZ_LOCAL = 1u << 1,            /* full-window local alignment, score and end cell only */
     FZ_STATS = 1u << 2,            /* fill *stats (adds stream syncs for phase timings) */
     FZ_QUERY_RC = 1u << 3,         /* seeds lie on the query's reverse complement (see below) */
-    FZ_SEEDS_ALL = 1u << 4         /* fz_find_seeds: every shared k-mer, no diagonal dedup */
+    FZ_SEEDS_ALL = 1u << 4,        /* fz_find_seeds: every shared k-mer, no diagonal dedup */
+    FZ_SEEDS_REUSE_INDEX = 1u << 5 /* fz_find_seeds: reuse the target index of an earlier call */
 };
 
 /* FZ_QUERY_RC: the call aligns the target against the reverse complement
@@ -198,12 +215,14 @@ int fz_extend_batch(fz_ctx *ctx,
  *                   shorter than 2^31 bases
  *   k               1..32
  *   flank           >= 0
- *   flags           FZ_QUERY_RC | FZ_SEEDS_ALL
+ *   flags           FZ_QUERY_RC | FZ_SEEDS_ALL | FZ_SEEDS_REUSE_INDEX
  *   seeds           out (may be NULL): device pointer to *n_seeds records,
  *                   owned by ctx, valid until the next fz_find_seeds or
  *                   fz_destroy (fz_copy_seeds copies them out)
  *   n_seeds         out: number of seeds
  *   n_hits          out (may be NULL): shared k-mer hits before the dedup
+ *   stats           out (may be NULL): phase times from HIP events on
+ *                   `stream` (recording them costs a little)
  *   stream          hipStream_t or NULL
  * Every hit is materialized (16 bytes each in device memory, plus sort
  * scratch); more than 2^31 hits fail with FZ_ENOMEM.  The call reads counts
@@ -215,7 +234,16 @@ int fz_find_seeds(fz_ctx *ctx,
                   const uint8_t *query, uint64_t query_len,
                   uint32_t k, int64_t flank, uint32_t flags,
                   const fz_seed **seeds, uint64_t *n_seeds, uint64_t *n_hits,
-                  void *stream);
+                  fz_seed_stats *stats, void *stream);
+
+/* FZ_SEEDS_REUSE_INDEX: every call without this flag builds an index of the
+ * target (its k-mers sorted, and a bucket table over them) and keeps it on
+ * ctx once the call has succeeded.  A call with the flag skips that build
+ * and uses the kept index; the target pointer, target_len and k must equal
+ * those of the call that built it (else FZ_EINVAL), and the caller
+ * guarantees the target bytes have not changed since.  Searching both
+ * strands of one query, or many queries against one target, builds the
+ * index once.  fz_extend_batch does not touch the index. */
 
 /* Copy the first n seeds of the last successful fz_find_seeds to dst
  * (device, n records). */

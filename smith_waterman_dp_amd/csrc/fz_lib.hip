@@ -84,11 +84,16 @@ struct fz_ctx {
     // seed stage: target keys and positions (two of each for the sort), query
     // keys, join ranges and counts, hits (two for the sort), run flags and
     // ranks, library scratch, and the seeds of the last fz_find_seeds
-    DevBuf sk_tk, sk_tk2, sk_tp, sk_tp2, sk_qk, sk_lo, sk_cnt, sk_off, sk_hit, sk_hit2, sk_flag, sk_rank, sk_tmp, sk_out;
+    DevBuf sk_tk, sk_tk2, sk_tp, sk_tp2, sk_bend, sk_boff, sk_lo, sk_cnt, sk_off, sk_hit, sk_hit2, sk_flag, sk_rank, sk_tmp, sk_out;
     uint64_t last_seeds = 0;
+    // the target index held in sk_tk2 / sk_tp2 / sk_boff (FZ_SEEDS_REUSE_INDEX)
+    bool idx_valid = false;
+    const uint8_t *idx_target = nullptr;
+    uint64_t idx_tlen = 0;
+    uint32_t idx_k = 0;
     hipStream_t xs[EXEC_STREAMS - 1] = {};   // executor streams besides the caller's
     hipEvent_t fork_ev = nullptr, join_ev[EXEC_STREAMS - 1] = {};
-    hipEvent_t ev[8] = {};
+    hipEvent_t ev[12] = {};
     hipEvent_t kev[2] = {};             // brackets the dominant kernel
 };
 
@@ -235,7 +240,7 @@ struct Timer {
     int k = 0;
     void mark()
     {
-        if (on && k < 8) (void)hipEventRecord(ctx->ev[k++], st);
+        if (on && k < 12) (void)hipEventRecord(ctx->ev[k++], st);
     }
     float ms(int a, int b)
     {
@@ -283,19 +288,26 @@ int run_local(fz_ctx *ctx, const fz_seed *seeds, uint64_t n, uint64_t tlen, uint
 // and at the end.
 static int seeds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const uint8_t *query, uint64_t qlen,
                       uint32_t k, int64_t flank, uint32_t flags, const fz_seed **seeds, uint64_t *n_seeds,
-                      uint64_t *n_hits, hipStream_t st)
+                      uint64_t *n_hits, fz_seed_stats *stats, hipStream_t st)
 {
     if (!n_seeds) return fail(ctx, FZ_EINVAL, "n_seeds is NULL");
     *n_seeds = 0;
     if (n_hits) *n_hits = 0;
+    if (stats) *stats = fz_seed_stats{};
+    Timer tm{ctx, st, stats != nullptr};
     if (seeds) *seeds = nullptr;
     ctx->last_seeds = 0;
     if (k < 1 || k > 32) return fail(ctx, FZ_EINVAL, "k must be 1..32 (got %u)", k);
     if (flank < 0) return fail(ctx, FZ_EINVAL, "flank must be >= 0");
-    if (flags & ~(uint32_t)(FZ_QUERY_RC | FZ_SEEDS_ALL)) return fail(ctx, FZ_EINVAL, "unknown flag bits");
+    if (flags & ~(uint32_t)(FZ_QUERY_RC | FZ_SEEDS_ALL | FZ_SEEDS_REUSE_INDEX))
+        return fail(ctx, FZ_EINVAL, "unknown flag bits");
     if ((tlen && !target) || (qlen && !query)) return fail(ctx, FZ_EINVAL, "NULL sequence");
     if (tlen >= (1ull << 31) || qlen >= (1ull << 31))
         return fail(ctx, FZ_EINVAL, "sequences must be shorter than 2^31 bases for the seed stage");
+    const bool reuse = (flags & FZ_SEEDS_REUSE_INDEX) != 0;
+    if (reuse && !(ctx->idx_valid && ctx->idx_target == target && ctx->idx_tlen == tlen && ctx->idx_k == k))
+        return fail(ctx, FZ_EINVAL, "FZ_SEEDS_REUSE_INDEX: no index of this target (pointer, length, k) on ctx");
+    if (!reuse) ctx->idx_valid = false;
     if (tlen < k || qlen < k) return FZ_OK;
     const int64_t nt = (int64_t)(tlen - k + 1), nq = (int64_t)(qlen - k + 1);
     const int64_t NT = (int64_t)tlen + 2 * PAD, NQ = (int64_t)qlen + 2 * PAD;
@@ -309,44 +321,78 @@ static int seeds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const u
     ENSURE(ctx->Tr, NT + 64);
     ENSURE(ctx->Qf, NQ + 64);
     ENSURE(ctx->Qr, NQ + 64);
-    pack_kernel<<<std::min<int64_t>(blocks_for(NT, 256), 8192), 256, 0, st>>>(
-        target, (int64_t)tlen, as<uint8_t>(ctx->Tf), as<uint8_t>(ctx->Tr), NT, &dc->err, 0);
+    tm.mark();
+    if (!reuse)
+        pack_kernel<<<std::min<int64_t>(blocks_for(NT, 256), 8192), 256, 0, st>>>(
+            target, (int64_t)tlen, as<uint8_t>(ctx->Tf), as<uint8_t>(ctx->Tr), NT, &dc->err, 0);
     pack_kernel<<<std::min<int64_t>(blocks_for(NQ, 256), 8192), 256, 0, st>>>(
         query, (int64_t)qlen, as<uint8_t>(ctx->Qf), as<uint8_t>(ctx->Qr), NQ, &dc->err, (flags & FZ_QUERY_RC) ? 1 : 0);
     HIP_OK(hipGetLastError());
+    tm.mark();
 
-    // target keys, sorted with their positions
-    ENSURE(ctx->sk_tk, nt * sizeof(uint64_t));
-    ENSURE(ctx->sk_tk2, nt * sizeof(uint64_t));
-    ENSURE(ctx->sk_tp, nt * sizeof(uint32_t));
-    ENSURE(ctx->sk_tp2, nt * sizeof(uint32_t));
-    ENSURE(ctx->sk_qk, nq * sizeof(uint64_t));
+    // target keys, sorted with their positions, and a bucket table over the
+    // top bits of the key: about as many buckets as target keys (at most
+    // 2^30), all 2k bits when that is fewer
     const unsigned gb = 4 * (unsigned)ctx->n_cu * 4;
-    kmer_keys_kernel<<<gb, 256, 0, st>>>(as<uint8_t>(ctx->Tf) + PAD, nt, (int)k, as<uint64_t>(ctx->sk_tk),
-                                         as<uint32_t>(ctx->sk_tp));
-    kmer_keys_kernel<<<gb, 256, 0, st>>>(as<uint8_t>(ctx->Qf) + PAD, nq, (int)k, as<uint64_t>(ctx->sk_qk), nullptr);
-    HIP_OK(hipGetLastError());
-    size_t tmp_sort = 0, tmp_scan = 0, tmp_sort2 = 0;
-    HIP_OK(hipcub::DeviceRadixSort::SortPairs(nullptr, tmp_sort, as<uint64_t>(ctx->sk_tk), as<uint64_t>(ctx->sk_tk2),
-                                              as<uint32_t>(ctx->sk_tp), as<uint32_t>(ctx->sk_tp2), (int)nt, 0,
-                                              (int)(2 * k), st));
+    int nb_bits = 1;
+    while (nb_bits < 30 && (1ll << nb_bits) < nt) ++nb_bits;
+    nb_bits = std::min(nb_bits, (int)(2 * k));
+    const int shift = (int)(2 * k) - nb_bits;
+    const int64_t NB = 1ll << nb_bits;
+    size_t tmp_sort = 0, tmp_scan = 0, tmp_max = 0, tmp_sort2 = 0;
     HIP_OK(hipcub::DeviceScan::ExclusiveSum(nullptr, tmp_scan, as<uint64_t>(ctx->sk_cnt), as<uint64_t>(ctx->sk_off),
                                             (int)nq, st));
-    ENSURE(ctx->sk_tmp, std::max(tmp_sort, tmp_scan));
-    HIP_OK(hipcub::DeviceRadixSort::SortPairs(ctx->sk_tmp.p, tmp_sort, as<uint64_t>(ctx->sk_tk),
-                                              as<uint64_t>(ctx->sk_tk2), as<uint32_t>(ctx->sk_tp),
-                                              as<uint32_t>(ctx->sk_tp2), (int)nt, 0, (int)(2 * k), st));
+    if (reuse) {
+        ENSURE(ctx->sk_tmp, tmp_scan);
+        tm.mark();
+        tm.mark();
+        tm.mark();
+    } else {
+        ENSURE(ctx->sk_tk, nt * sizeof(uint64_t));
+        ENSURE(ctx->sk_tk2, nt * sizeof(uint64_t));
+        ENSURE(ctx->sk_tp, nt * sizeof(uint32_t));
+        ENSURE(ctx->sk_tp2, nt * sizeof(uint32_t));
+        kmer_keys_kernel<<<gb, 256, 0, st>>>(as<uint8_t>(ctx->Tf) + PAD, nt, (int)k, as<uint64_t>(ctx->sk_tk),
+                                             as<uint32_t>(ctx->sk_tp));
+        HIP_OK(hipGetLastError());
+        tm.mark();
+        HIP_OK(hipcub::DeviceRadixSort::SortPairs(nullptr, tmp_sort, as<uint64_t>(ctx->sk_tk),
+                                                  as<uint64_t>(ctx->sk_tk2), as<uint32_t>(ctx->sk_tp),
+                                                  as<uint32_t>(ctx->sk_tp2), (int)nt, 0, (int)(2 * k), st));
+        HIP_OK(hipcub::DeviceScan::InclusiveScan(nullptr, tmp_max, as<uint32_t>(ctx->sk_bend),
+                                                 as<uint32_t>(ctx->sk_boff) + 1, hipcub::Max(), (int)NB, st));
+        ENSURE(ctx->sk_tmp, std::max(std::max(tmp_sort, tmp_scan), tmp_max));
+        HIP_OK(hipcub::DeviceRadixSort::SortPairs(ctx->sk_tmp.p, tmp_sort, as<uint64_t>(ctx->sk_tk),
+                                                  as<uint64_t>(ctx->sk_tk2), as<uint32_t>(ctx->sk_tp),
+                                                  as<uint32_t>(ctx->sk_tp2), (int)nt, 0, (int)(2 * k), st));
+        tm.mark();
+        ENSURE(ctx->sk_bend, NB * sizeof(uint32_t));
+        ENSURE(ctx->sk_boff, (NB + 1) * sizeof(uint32_t));
+        rc = zero(ctx, ctx->sk_bend.p, NB * sizeof(uint32_t), st);
+        if (rc) return rc;
+        rc = zero(ctx, ctx->sk_boff.p, sizeof(uint32_t), st);
+        if (rc) return rc;
+        bucket_end_kernel<<<gb, 256, 0, st>>>(as<uint64_t>(ctx->sk_tk2), nt, shift, as<uint32_t>(ctx->sk_bend));
+        HIP_OK(hipGetLastError());
+        tmp_max = ctx->sk_tmp.cap;
+        HIP_OK(hipcub::DeviceScan::InclusiveScan(ctx->sk_tmp.p, tmp_max, as<uint32_t>(ctx->sk_bend),
+                                                 as<uint32_t>(ctx->sk_boff) + 1, hipcub::Max(), (int)NB, st));
+        tm.mark();
+    }
 
     // join: per query position, the range of equal target keys
     ENSURE(ctx->sk_lo, nq * sizeof(uint32_t));
     ENSURE(ctx->sk_cnt, nq * sizeof(uint64_t));
     ENSURE(ctx->sk_off, nq * sizeof(uint64_t));
-    join_count_kernel<<<gb, 256, 0, st>>>(as<uint64_t>(ctx->sk_tk2), nt, as<uint64_t>(ctx->sk_qk), nq,
-                                          as<uint32_t>(ctx->sk_lo), as<uint64_t>(ctx->sk_cnt));
+    join_count_kernel<<<gb, 256, 0, st>>>(as<uint64_t>(ctx->sk_tk2), as<uint32_t>(ctx->sk_boff), shift,
+                                          as<uint8_t>(ctx->Qf) + PAD, nq, (int)k, as<uint32_t>(ctx->sk_lo),
+                                          as<uint64_t>(ctx->sk_cnt));
     HIP_OK(hipGetLastError());
+    tm.mark();
     tmp_scan = ctx->sk_tmp.cap;
     HIP_OK(hipcub::DeviceScan::ExclusiveSum(ctx->sk_tmp.p, tmp_scan, as<uint64_t>(ctx->sk_cnt),
                                             as<uint64_t>(ctx->sk_off), (int)nq, st));
+    tm.mark();
     uint64_t last[2] = {0, 0};
     HIP_OK(hipMemcpyAsync(&last[0], as<uint64_t>(ctx->sk_off) + (nq - 1), sizeof(uint64_t), hipMemcpyDeviceToHost, st));
     HIP_OK(hipMemcpyAsync(&last[1], as<uint64_t>(ctx->sk_cnt) + (nq - 1), sizeof(uint64_t), hipMemcpyDeviceToHost, st));
@@ -354,9 +400,31 @@ static int seeds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const u
     HIP_OK(hipMemcpyAsync(&hc, dc, sizeof(Counters), hipMemcpyDeviceToHost, st));
     HIP_OK(hipStreamSynchronize(st));
     if (hc.err & 1u) return fail(ctx, FZ_EINVAL, "sequence holds a byte other than A, C, G, T");
+    if (!reuse) {
+        ctx->idx_valid = true;
+        ctx->idx_target = target;
+        ctx->idx_tlen = tlen;
+        ctx->idx_k = k;
+    }
     const uint64_t H = last[0] + last[1];
     if (n_hits) *n_hits = H;
-    if (H == 0) return FZ_OK;
+    auto finish = [&]() -> int {
+        if (!stats) return FZ_OK;
+        HIP_OK(hipStreamSynchronize(st));
+        stats->ms_pack = tm.ms(0, 1);
+        stats->ms_keys = tm.ms(1, 2);
+        stats->ms_sort_keys = tm.ms(2, 3);
+        stats->ms_index = tm.ms(3, 4);
+        stats->ms_join = tm.ms(4, 5);
+        stats->ms_scan = tm.ms(5, 6);
+        stats->ms_emit = tm.ms(6, 7);
+        stats->ms_sort_hits = tm.ms(7, 8);
+        stats->ms_runs = tm.ms(8, 9);
+        stats->ms_write = tm.ms(9, 10);
+        stats->ms_total = tm.ms(0, tm.k - 1);
+        return FZ_OK;
+    };
+    if (H == 0) return finish();
     if (H >= (1ull << 31)) return fail(ctx, FZ_ENOMEM, "%llu shared k-mer hits: more than the stage handles (2^31)",
                                        (unsigned long long)H);
 
@@ -369,6 +437,7 @@ static int seeds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const u
                                          as<uint64_t>(ctx->sk_cnt), as<uint64_t>(ctx->sk_off), nq, (int64_t)qlen,
                                          as<uint64_t>(ctx->sk_hit));
     HIP_OK(hipGetLastError());
+    tm.mark();
     HIP_OK(hipcub::DeviceRadixSort::SortKeys(nullptr, tmp_sort2, as<uint64_t>(ctx->sk_hit),
                                              as<uint64_t>(ctx->sk_hit2), (int)H, 0, 64, st));
     size_t tmp_scan2 = 0;
@@ -378,12 +447,14 @@ static int seeds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const u
     size_t t2 = ctx->sk_tmp.cap;
     HIP_OK(hipcub::DeviceRadixSort::SortKeys(ctx->sk_tmp.p, t2, as<uint64_t>(ctx->sk_hit), as<uint64_t>(ctx->sk_hit2),
                                              (int)H, 0, 64, st));
+    tm.mark();
     run_start_kernel<<<gb, 256, 0, st>>>(as<uint64_t>(ctx->sk_hit2), (int64_t)H, (flags & FZ_SEEDS_ALL) ? 0 : 1,
                                          as<uint64_t>(ctx->sk_flag));
     HIP_OK(hipGetLastError());
     t2 = ctx->sk_tmp.cap;
     HIP_OK(hipcub::DeviceScan::ExclusiveSum(ctx->sk_tmp.p, t2, as<uint64_t>(ctx->sk_flag), as<uint64_t>(ctx->sk_rank),
                                             (int)H, st));
+    tm.mark();
     HIP_OK(hipMemcpyAsync(&last[0], as<uint64_t>(ctx->sk_rank) + (H - 1), sizeof(uint64_t), hipMemcpyDeviceToHost, st));
     HIP_OK(hipMemcpyAsync(&last[1], as<uint64_t>(ctx->sk_flag) + (H - 1), sizeof(uint64_t), hipMemcpyDeviceToHost, st));
     HIP_OK(hipStreamSynchronize(st));
@@ -395,11 +466,12 @@ static int seeds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const u
                                            as<uint64_t>(ctx->sk_rank), (int64_t)H, (int)k, flank, (int64_t)tlen,
                                            (int64_t)qlen, as<fz_seed>(ctx->sk_out));
     HIP_OK(hipGetLastError());
+    tm.mark();
     HIP_OK(hipStreamSynchronize(st));
     ctx->last_seeds = n;
     *n_seeds = n;
     if (seeds) *seeds = as<fz_seed>(ctx->sk_out);
-    return FZ_OK;
+    return finish();
 }
 
 }  // namespace
@@ -464,7 +536,7 @@ void fz_destroy(fz_ctx *ctx)
                       &ctx->eager, &ctx->side_trace, &ctx->run_cap, &ctx->run_off, &ctx->run_len, &ctx->runs,
                       &ctx->items, &ctx->batch_first, &ctx->scan_tmp, &ctx->cig, &ctx->cigar,
                       &ctx->counters, &ctx->ovl0, &ctx->ovl1, &ctx->bnd,
-                      &ctx->sk_tk, &ctx->sk_tk2, &ctx->sk_tp, &ctx->sk_tp2, &ctx->sk_qk, &ctx->sk_lo, &ctx->sk_cnt,
+                      &ctx->sk_tk, &ctx->sk_tk2, &ctx->sk_tp, &ctx->sk_tp2, &ctx->sk_bend, &ctx->sk_boff, &ctx->sk_lo, &ctx->sk_cnt,
                       &ctx->sk_off, &ctx->sk_hit, &ctx->sk_hit2, &ctx->sk_flag, &ctx->sk_rank, &ctx->sk_tmp,
                       &ctx->sk_out};
     for (auto &x : ctx->xs)
@@ -819,7 +891,7 @@ int fz_extend_batch(fz_ctx *ctx, const uint8_t *target, uint64_t target_len, con
 
 int fz_find_seeds(fz_ctx *ctx, const uint8_t *target, uint64_t target_len, const uint8_t *query, uint64_t query_len,
                   uint32_t k, int64_t flank, uint32_t flags, const fz_seed **seeds, uint64_t *n_seeds,
-                  uint64_t *n_hits, void *stream)
+                  uint64_t *n_hits, fz_seed_stats *stats, void *stream)
 {
     if (!ctx) return FZ_EINVAL;
     ctx->err.clear();
@@ -833,7 +905,7 @@ int fz_find_seeds(fz_ctx *ctx, const uint8_t *target, uint64_t target_len, const
         return fail(ctx, FZ_EDEVICE, "hipSetDevice(%d) failed", ctx->device);
     }
     const int rc = seeds_impl(ctx, target, target_len, query, query_len, k, flank, flags, seeds, n_seeds, n_hits,
-                              (hipStream_t)stream);
+                              stats, (hipStream_t)stream);
     if (prev != ctx->device) (void)hipSetDevice(prev);
     return rc;
 }

@@ -6,11 +6,16 @@
 // them, then extends the survivors with the gapped DP.  This file is the
 // first step plus the plainest filter, one seed per run of hits on one
 // diagonal:
-//   keys    the k codes at every start position as one base-4 number
+//   keys    the k codes at every target start position as one base-4
+//           number
 //   sort    the target's (key, position) pairs by key (device radix sort)
-//   join    per query position, the range of equal target keys by binary
-//           search; counts, their exclusive scan, then every hit written as
-//           one 64-bit word ((t - q + query_len) << 32 | t)
+//   index   a direct-address table over the top bits of the key: for each
+//           bucket, where its keys start in the sorted array (about one key
+//           per bucket, so a lookup is two table reads and a short search)
+//   join    per query position, its key from the codes, then the range of
+//           equal target keys through the table; counts, their exclusive
+//           scan, then every hit written as one 64-bit word
+//           ((t - q + query_len) << 32 | t)
 //   sort    the hit words, which orders hits by diagonal and then by t
 //   runs    a hit starts a run unless its word is the previous word + 1
 //           (same diagonal, t one further): one seed per run
@@ -38,28 +43,49 @@ __global__ void kmer_keys_kernel(const uint8_t *__restrict__ codes, int64_t nkey
     }
 }
 
-// For every query position: where its key's run starts in the sorted target
-// keys, and how long it is.
-__global__ void join_count_kernel(const uint64_t *__restrict__ tkeys, int64_t nt, const uint64_t *__restrict__ qkeys,
-                                  int64_t nq, uint32_t *__restrict__ lo_out, uint64_t *__restrict__ cnt)
+// Bucket table, step 1: for each non-empty bucket b (key >> shift), one past
+// the last index of its keys in the sorted array.  bend[] starts at zero.
+__global__ void bucket_end_kernel(const uint64_t *__restrict__ tkeys, int64_t nt, int shift, uint32_t *__restrict__ bend)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nt; i += stride) {
+        const uint64_t b = tkeys[i] >> shift;
+        if (i == nt - 1 || (tkeys[i + 1] >> shift) != b) bend[b] = (uint32_t)(i + 1);
+    }
+}
+// Step 2 (host side): off[0] = 0 and off[b + 1] = the running maximum of
+// bend[0..b], so bucket b's keys are sorted[off[b] .. off[b + 1]).
+
+// For every query position: its key (read from the codes), then where that
+// key's run starts in the sorted target keys, and how long it is.
+__global__ void join_count_kernel(const uint64_t *__restrict__ tkeys, const uint32_t *__restrict__ off, int shift,
+                                  const uint8_t *__restrict__ qcodes, int64_t nq, int k, uint32_t *__restrict__ lo_out,
+                                  uint64_t *__restrict__ cnt)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nq; q += stride) {
-        const uint64_t key = qkeys[q];
-        int64_t a = 0, b = nt;              // first index with tkeys >= key
-        while (a < b) {
-            const int64_t m = (a + b) >> 1;
-            if (tkeys[m] < key) a = m + 1;
-            else b = m;
+        uint64_t key = 0;
+        for (int i = 0; i < k; ++i) key = (key << 2) | (uint64_t)qcodes[q + i];
+        const uint64_t b = key >> shift;
+        uint32_t a = off[b], e = off[b + 1];
+        if (shift) {                        // the bucket holds other keys too
+            uint32_t x = a, y = e;          // first index with tkeys >= key
+            while (x < y) {
+                const uint32_t m = x + ((y - x) >> 1);
+                if (tkeys[m] < key) x = m + 1;
+                else y = m;
+            }
+            uint32_t u = x, v = e;          // first index with tkeys > key
+            while (u < v) {
+                const uint32_t m = u + ((v - u) >> 1);
+                if (tkeys[m] <= key) u = m + 1;
+                else v = m;
+            }
+            a = x;
+            e = u;
         }
-        int64_t c = a, e = nt;              // first index with tkeys > key
-        while (c < e) {
-            const int64_t m = (c + e) >> 1;
-            if (tkeys[m] <= key) c = m + 1;
-            else e = m;
-        }
-        lo_out[q] = (uint32_t)a;
-        cnt[q] = (uint64_t)(c - a);
+        lo_out[q] = a;
+        cnt[q] = (uint64_t)(e - a);
     }
 }
 

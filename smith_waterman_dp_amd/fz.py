@@ -11,7 +11,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfz.so")
 
-FZ_TRACEBACK, FZ_LOCAL, FZ_STATS, FZ_QUERY_RC, FZ_SEEDS_ALL = 1, 2, 4, 8, 16
+FZ_TRACEBACK, FZ_LOCAL, FZ_STATS, FZ_QUERY_RC, FZ_SEEDS_ALL, FZ_SEEDS_REUSE_INDEX = 1, 2, 4, 8, 16, 32
 FZ_OK, FZ_EINVAL, FZ_ENOMEM, FZ_EDEVICE, FZ_EBAND = 0, -1, -2, -3, -4
 FZ_HIT_TRACED, FZ_HIT_EAGER_LEFT, FZ_HIT_EAGER_RIGHT = 1, 2, 4
 FZ_HIT_BELOW_MIN, FZ_HIT_EBAND, FZ_HIT_ESEED, FZ_HIT_ERANGE = 8, 16, 32, 64
@@ -44,6 +44,14 @@ class fz_stats(ctypes.Structure):
         d = {f: getattr(self, f) for f, _ in self._fields_}
         d["bin_hist"] = list(self.bin_hist)
         return d
+
+
+class fz_seed_stats(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_float) for f in ("ms_pack", "ms_keys", "ms_sort_keys", "ms_index", "ms_join", "ms_scan",
+                                              "ms_emit", "ms_sort_hits", "ms_runs", "ms_write", "ms_total")]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
 
 
 class FzError(RuntimeError):
@@ -80,7 +88,7 @@ def load_library(path=LIB_PATH):
     lib.fz_copy_cigar.argtypes = [P, P, u64, P]
     lib.fz_find_seeds.restype = ctypes.c_int
     lib.fz_find_seeds.argtypes = [P, P, u64, P, u64, ctypes.c_uint32, i64, ctypes.c_uint32, ctypes.POINTER(P),
-                                  ctypes.POINTER(u64), ctypes.POINTER(u64), P]
+                                  ctypes.POINTER(u64), ctypes.POINTER(u64), ctypes.POINTER(fz_seed_stats), P]
     lib.fz_copy_seeds.restype = ctypes.c_int
     lib.fz_copy_seeds.argtypes = [P, P, u64, P]
     _lib = lib
@@ -161,12 +169,13 @@ def fz_extend_batch(ctx, target, query, seeds, scoring, ydrop, min_traceback_sco
     return hits, cigar, (st.as_dict() if want_stats else None)
 
 
-def fz_find_seeds(ctx, target, query, k=19, flank=32768, flags=0, stream=None):
+def fz_find_seeds(ctx, target, query, k=19, flank=32768, flags=0, stream=None, want_stats=False):
     """The seed stage: shared k-mers of target and query (of the query's
     reverse complement with FZ_QUERY_RC), one per diagonal run unless
     FZ_SEEDS_ALL.  target, query: uint8 CUDA tensors of ASCII bases.
     Returns (seeds, n_hits): seeds an int64 (n, 7) CUDA tensor in
-    SEED_FIELDS order, ordered by diagonal t - q then t."""
+    SEED_FIELDS order, ordered by diagonal t - q then t; with want_stats,
+    (seeds, n_hits, phase times as a dict)."""
     import torch
     lib = load_library()
     for name, t in (("target", target), ("query", query)):
@@ -176,12 +185,15 @@ def fz_find_seeds(ctx, target, query, k=19, flank=32768, flags=0, stream=None):
     n = ctypes.c_uint64(0)
     hits = ctypes.c_uint64(0)
     strm = _stream_handle(stream)
+    st = fz_seed_stats()
     _check(ctx, lib.fz_find_seeds(ctx, target.data_ptr(), target.numel(), query.data_ptr(), query.numel(), int(k),
                                   int(flank), int(flags), ctypes.byref(ptr), ctypes.byref(n), ctypes.byref(hits),
-                                  strm))
+                                  ctypes.byref(st) if want_stats else None, strm))
     seeds = torch.empty((n.value, len(SEED_FIELDS)), dtype=torch.int64, device=target.device)
     if n.value:
         _check(ctx, lib.fz_copy_seeds(ctx, seeds.data_ptr(), n.value, strm))
+    if want_stats:
+        return seeds, hits.value, st.as_dict()
     return seeds, hits.value
 
 
@@ -218,12 +230,16 @@ class Context:
         return fz_extend_batch(self.h, target, query, seeds, scoring, ydrop, min_traceback_score, flags,
                                stream, want_stats)
 
-    def find_seeds(self, target, query, k=19, flank=32768, dedup=True, query_rc=False, stream=None):
+    def find_seeds(self, target, query, k=19, flank=32768, dedup=True, query_rc=False, stream=None,
+                   want_stats=False, reuse_index=False):
         """Seeds from shared k-mers (FZ_QUERY_RC: on the query's reverse
         complement); returns (seeds (n, 7) int64 CUDA tensor, hits before the
-        diagonal dedup)."""
-        flags = (0 if dedup else FZ_SEEDS_ALL) | (FZ_QUERY_RC if query_rc else 0)
-        return fz_find_seeds(self.h, target, query, k, flank, flags, stream)
+        diagonal dedup), plus the phase times with want_stats.  reuse_index:
+        the same target tensor and k as the last call that built the index
+        (FZ_SEEDS_REUSE_INDEX)."""
+        flags = ((0 if dedup else FZ_SEEDS_ALL) | (FZ_QUERY_RC if query_rc else 0)
+                 | (FZ_SEEDS_REUSE_INDEX if reuse_index else 0))
+        return fz_find_seeds(self.h, target, query, k, flank, flags, stream, want_stats)
 
     def local(self, target, query, seeds, scoring, stream=None, want_stats=False, query_rc=False):
         flags = FZ_LOCAL | (FZ_QUERY_RC if query_rc else 0)

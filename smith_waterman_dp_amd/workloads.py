@@ -382,6 +382,17 @@ def chromosome_rc(length=20_000_000, sub_rate=0.12, indel_rate=0.01, p_geom=0.3,
     return _workload("chromosome_rc", C1, C2, seeds, query_rc=True, n_seeds=len(seeds))
 
 
+def chromosome_seed_stage(length=20_000_000, sub_rate=0.12, indel_rate=0.01, p_geom=0.3, n_inversions=5,
+                          inv_min=50_000, inv_max=500_000, unrelated_frac=0.20, flank=WINDOW_FLANK, seed=0):
+    """Input of the seed stage itself: the pair of `chromosome` (same
+    parameters, same draw) as ASCII, with the seed length and window flank.
+    The stage runs on both strands of the query."""
+    C1, C2 = _chromosome_pair(length, sub_rate, indel_rate, p_geom, n_inversions, inv_min, inv_max,
+                              unrelated_frac, seed)
+    return {"name": "chromosome_seed_stage", "target": to_ascii(C1), "query": to_ascii(C2), "k": SEED_LEN,
+            "flank": flank}
+
+
 WORKLOADS = {
     "tiny": tiny,
     "local": local_pairs,

@@ -109,3 +109,49 @@ def test_seeds_edges_and_errors(ctx):
     assert e.value.code == fz.FZ_EINVAL
     # the context stays usable after an error
     check(ctx, T, Q, 3, 2, True, True, "after errors")
+
+
+def test_seeds_phase_stats(ctx):
+    """With stats the call returns the same seeds plus phase times that are
+    non-negative and fit inside the total."""
+    rng = np.random.default_rng(5)
+    T = W.to_ascii(W.random_codes(rng, 50_000))
+    Q = T.copy()
+    Q[::97] = ord("A")
+    ref, h_ref = ctx.find_seeds(dev(T), dev(Q), k=12, flank=100)
+    s, h, st = ctx.find_seeds(dev(T), dev(Q), k=12, flank=100, want_stats=True)
+    assert h == h_ref and torch.equal(s, ref)
+    phases = [v for key, v in st.items() if key != "ms_total"]
+    assert all(v >= 0 for v in phases)
+    assert st["ms_total"] > 0 and sum(phases) <= st["ms_total"] * 1.01 + 1e-3
+
+
+def test_seeds_reuse_index(ctx):
+    """A call that reuses the target index gives the seeds of a full call;
+    reuse is refused for another target, length or k, and after a call that
+    failed."""
+    rng = np.random.default_rng(8)
+    base = W.random_codes(rng, 30_000)
+    T = dev(W.to_ascii(base))
+    Q = dev(W.to_ascii(W.mutate(rng, base, 0.05, 0.005, 0.5)))
+    Q2 = dev(W.to_ascii(W.revcomp_codes(W.mutate(rng, base, 0.08, 0.005, 0.5))))
+    want = [ctx.find_seeds(T, q, k=11, flank=50, query_rc=rc) for q in (Q, Q2) for rc in (False, True)]
+    ctx.find_seeds(T, Q, k=11, flank=50)                                  # builds the index
+    got = [ctx.find_seeds(T, q, k=11, flank=50, query_rc=rc, reuse_index=True) for q in (Q, Q2)
+           for rc in (False, True)]
+    for (ws, wh), (gs, gh) in zip(want, got):
+        assert wh == gh and torch.equal(ws, gs)
+    with pytest.raises(fz.FzError):
+        ctx.find_seeds(T, Q, k=12, flank=50, reuse_index=True)            # other k
+    with pytest.raises(fz.FzError):
+        ctx.find_seeds(T[:-1], Q, k=11, flank=50, reuse_index=True)       # other length
+    with pytest.raises(fz.FzError):
+        ctx.find_seeds(Q, Q, k=11, flank=50, reuse_index=True)            # other target
+    bad = T.clone()
+    bad[5] = ord("N")
+    with pytest.raises(fz.FzError):
+        ctx.find_seeds(bad, Q, k=11, flank=50)                            # failed build drops the index
+    with pytest.raises(fz.FzError):
+        ctx.find_seeds(T, Q, k=11, flank=50, reuse_index=True)
+    s, h = ctx.find_seeds(T, Q, k=11, flank=50)
+    assert h == want[0][1] and torch.equal(s, want[0][0])
