@@ -66,8 +66,17 @@ def _load():
 
 
 def _scoring_arr(scoring):
-    return np.array([scoring["match"], scoring["transition"], scoring["transversion"],
-                     scoring["gap_open"], scoring["gap_extend"]], dtype=np.int64)
+    """The C struct's fields in order.  A scoring dict with a "matrix" (4x4,
+    rows = target base, columns = query base, order A, C, G, T) and an
+    "n_score" (a pair with N) uses them instead of match / transition /
+    transversion, and then accepts N in the sequences."""
+    mat = scoring.get("matrix")
+    use = mat is not None
+    sub = np.asarray(mat, dtype=np.int64).reshape(16) if use else np.zeros(16, dtype=np.int64)
+    head = [scoring.get("match", 0), scoring.get("transition", 0), scoring.get("transversion", 0),
+            scoring["gap_open"], scoring["gap_extend"], int(use)]
+    return np.concatenate([np.array(head, dtype=np.int64), sub,
+                           np.array([scoring.get("n_score", 0) if use else 0], dtype=np.int64)])
 
 
 def _as_bytes(seq):

@@ -27,7 +27,10 @@
  *
  * Readings where the pages are silent (each listed in the design notes):
  *   gap of length g costs open + g*extend; substitution is match /
- *   transition (A<->G, C<->T) / transversion; a cell is dead when S < T_d
+ *   transition (A<->G, C<->T) / transversion, or, when a 4x4 matrix is
+ *   given, its entry for (target base, query base), with N (either case)
+ *   against anything, N included, scoring a separate n_score (N is an
+ *   invalid base without a matrix); a cell is dead when S < T_d
  *   (strict), T_d = best score over live cells of diagonals < d minus ydrop,
  *   and a dead cell has S = I = D = -inf; the end cell is the highest S, ties
  *   to the smallest anti-diagonal then the smallest i; traceback prefers the
@@ -50,6 +53,9 @@ enum { FZO_OK = 0, FZO_ESEED = 1, FZO_EBASE = 2, FZO_ERANGE = 4, FZO_ENOMEM = 8 
 
 typedef struct {
     int64_t match, transition, transversion, gap_open, gap_extend;
+    int64_t use_matrix;                  /* nonzero: sub[][] and n_score replace the three scores */
+    int64_t sub[4][4];                   /* [target base][query base], order A, C, G, T */
+    int64_t n_score;                     /* a pair with N on either side */
 } fzo_scoring;
 
 typedef struct {
@@ -69,22 +75,26 @@ typedef struct {
 
 /* ---------------------------------------------------------------- bases -- */
 
-/* 0..3 for A, C, G, T (either case); -1 otherwise. */
-static int base_code(uint8_t c)
+/* 0..3 for A, C, G, T (either case); 4 for N (either case) when a matrix
+ * is in use; -1 otherwise. */
+static int base_code(uint8_t c, const fzo_scoring *sc)
 {
     switch (c) {
     case 'A': case 'a': return 0;
     case 'C': case 'c': return 1;
     case 'G': case 'g': return 2;
     case 'T': case 't': return 3;
+    case 'N': case 'n': return sc->use_matrix ? 4 : -1;
     default: return -1;
     }
 }
 
-/* Substitution score.  Transitions are purine<->purine (A,G) and
+/* Substitution score.  With a matrix: its entry, or n_score for a pair with
+ * N.  Otherwise transitions are purine<->purine (A,G) and
  * pyrimidine<->pyrimidine (C,T); every other mismatch is a transversion. */
 static int64_t sub_score(int a, int b, const fzo_scoring *sc)
 {
+    if (sc->use_matrix) return (a == 4 || b == 4) ? sc->n_score : sc->sub[a][b];
     if (a == b) return sc->match;
     int a_purine = (a == 0 || a == 2), b_purine = (b == 0 || b == 2);
     if (a_purine == b_purine) return sc->transition;
@@ -164,9 +174,9 @@ typedef struct {
     int64_t m, n;
 } side_seq;
 
-static int side_base(const uint8_t *p, int64_t dir, int64_t idx, int *err)
+static int side_base(const uint8_t *p, int64_t dir, int64_t idx, const fzo_scoring *sc, int *err)
 {
-    int c = base_code(p[dir * idx]);
+    int c = base_code(p[dir * idx], sc);
     if (c < 0) { *err |= FZO_EBASE; c = 0; }
     return c;
 }
@@ -232,7 +242,7 @@ static void extend_side(const side_seq *s, const fzo_scoring *sc, int64_t ydrop,
                 int64_t H = NEG;
                 if (i >= 1 && j >= 1) {
                     int e = 0;
-                    int ca = side_base(s->t, s->tdir, i, &e), cb = side_base(s->q, s->qdir, j, &e);
+                    int ca = side_base(s->t, s->tdir, i, sc, &e), cb = side_base(s->q, s->qdir, j, sc, &e);
                     b->err |= e;
                     H = add(load(b, b->S, i - 1, j - 1), sub_score(ca, cb, sc));
                 }
@@ -270,7 +280,7 @@ static int64_t traceback(const side_seq *s, const fzo_scoring *sc, const band *b
             if (i >= 1 && j >= 1) {
                 int e = 0;
                 H = add(load(b, b->S, i - 1, j - 1),
-                        sub_score(side_base(s->t, s->tdir, i, &e), side_base(s->q, s->qdir, j, &e), sc));
+                        sub_score(side_base(s->t, s->tdir, i, sc, &e), side_base(s->q, s->qdir, j, sc, &e), sc));
             }
             if (Sv != NEG && Sv == H) { ops[n++] = 'M'; i--; j--; }
             else if (Sv != NEG && Sv == load(b, b->I, i, j)) st = ST_I;
@@ -343,7 +353,7 @@ static int64_t extend_seed(const uint8_t *T, int64_t tlen, const uint8_t *Q, int
 
     int64_t seed_score = 0;
     for (int64_t k = 0; k < L; k++) {
-        int ca = base_code(T[sd->t_pos + k]), cb = base_code(Q[sd->q_pos + k]);
+        int ca = base_code(T[sd->t_pos + k], sc), cb = base_code(Q[sd->q_pos + k], sc);
         if (ca < 0 || cb < 0) { err |= FZO_EBASE; continue; }
         seed_score += sub_score(ca, cb, sc);
     }
@@ -401,13 +411,13 @@ static int64_t local_pair(const uint8_t *a, int64_t m, const uint8_t *bq, int64_
     }
     int err = 0;
     for (int64_t j = 1; j <= n; j++) {
-        cb[j] = base_code(bq[j - 1]);
+        cb[j] = base_code(bq[j - 1], sc);
         if (cb[j] < 0) { err |= FZO_EBASE; cb[j] = 0; }
     }
     for (int64_t j = 0; j <= n; j++) { Sp[j] = 0; Dp[j] = NEG; }
     int64_t best = 0, bi = 0, bj = 0;
     for (int64_t i = 1; i <= m; i++) {
-        int ca = base_code(a[i - 1]);
+        int ca = base_code(a[i - 1], sc);
         if (ca < 0) { err |= FZO_EBASE; ca = 0; }
         Sc[0] = 0; Dc[0] = NEG;
         int64_t I = NEG;                 /* I(i, j-1) */

@@ -16,6 +16,12 @@ NEG = None
 
 
 def sub(x, y, sc):
+    """x from the target, y from the query."""
+    x, y = x.upper(), y.upper()
+    if "matrix" in sc:
+        if x == "N" or y == "N":
+            return sc["n_score"]
+        return sc["matrix"]["ACGT".index(x)]["ACGT".index(y)]
     if x == y:
         return sc["match"]
     purine = set("AG")

@@ -8,7 +8,8 @@
 # right; end-cell tie to the largest i; traceback prefers D over I; transition
 # and transversion swapped; matrix clip one cell too low; local mode without
 # the D term; gap state prefers "extended" over "opened here"; no revival of a
-# diagonal from d-2.
+# diagonal from d-2; the matrix read transposed; N scored as the matrix's A
+# entry instead of n_score.
 set -u
 SRC=$(cd "$(dirname "$0")/.." && pwd)
 W=${TMPDIR:-/tmp}/fz_oracle_mut
@@ -24,6 +25,8 @@ declare -a MUTS=(
  's/int64_t S = max2(0, max2(H, max2(I, D)));/int64_t S = max2(0, max2(H, I));/'
  's/if (Iv != NEG \&\& Iv == add(load(b, b->S, i, j - 1), -OE)) st = ST_S;/if (Iv != NEG \&\& Iv == add(load(b, b->I, i, j - 1), -E)) {} else st = ST_S;/'
  's/for (int64_t back = 1; back <= 2 \&\& d - back >= 0; back++)/for (int64_t back = 1; back <= 1 \&\& d - back >= 0; back++)/'
+ 's/? sc->n_score : sc->sub\[a\]\[b\];/? sc->n_score : sc->sub[b][a];/'
+ 's/return (a == 4 || b == 4) ? sc->n_score : sc->sub\[a\]\[b\];/return sc->sub[a \& 3][b \& 3];/'
 )
 for k in "${!MUTS[@]}"; do
   rm -rf $W && mkdir -p $W && cp -r $SRC/oracle $SRC/tests $SRC/smith_waterman_dp_amd $W/

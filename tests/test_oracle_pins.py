@@ -480,3 +480,84 @@ def test_find_seeds_reverse_strand_and_edges():
     assert oracle.find_seeds("ACG", "ACGT", k=4)[0].shape == (0, 7)        # target shorter than k
     with pytest.raises(ValueError):
         oracle.find_seeds("ACGN", "ACGT", k=2)
+
+
+# ---- 4x4 substitution matrix and N -------------------------------------
+
+def rand_matrix_scoring(rng):
+    """An asymmetric int8 matrix (rows = target base) and an N score."""
+    return dict(matrix=[[rng.randint(-128, 127) for _ in range(4)] for _ in range(4)],
+                n_score=rng.randint(-128, 127), gap_open=rng.randint(1, 400), gap_extend=rng.randint(1, 60))
+
+
+@pytest.mark.parametrize("case", range(120))
+def test_bruteforce_matrix(case):
+    """Random asymmetric matrices, N in either sequence (either case), with
+    and without pruning, against path enumeration."""
+    rng = random.Random(7000 + case)
+    alphabet = ["ACGTN", "ACGTn", "AN", "CGT"][case % 4]
+    a = rand_seq(rng, rng.randint(0, 5), alphabet)
+    b = rand_seq(rng, rng.randint(0, 5), alphabet)
+    sc = rand_matrix_scoring(rng)
+    check_against_brute(a, b, sc, None if case % 2 else rng.randint(0, 300))
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_local_bruteforce_matrix(case):
+    rng = random.Random(7500 + case)
+    a = rand_seq(rng, rng.randint(0, 5), "ACGTN")
+    b = rand_seq(rng, rng.randint(0, 5), "ACGTN")
+    sc = rand_matrix_scoring(rng)
+    hits, _, _ = oracle.run(a, b, np.array([[0, 0, 0, 0, len(a), 0, len(b)]], dtype=np.int64), sc, 0,
+                            local=True, threads=1)
+    br = bf.local_brute(a, b, sc)
+    assert hits["status"][0] == 0
+    assert hits["score"][0] == br["score"]
+
+
+def matrix_of(sc):
+    """The triple written as a matrix: equal bases score match, A<->G and
+    C<->T score transition, every other pair transversion."""
+    cls = {0: "match", 2: "transition"}
+    return [[sc[cls.get(x ^ y, "transversion")] for y in range(4)] for x in range(4)]
+
+
+def test_matrix_of_triple_equals_triple(tiny_small):
+    """The matrix mode with the triple's matrix gives the triple's results,
+    CIGARs included, on the tiny batch."""
+    w = tiny_small
+    sc_m = dict(matrix=matrix_of(w["scoring"]), n_score=-100, gap_open=w["scoring"]["gap_open"],
+                gap_extend=w["scoring"]["gap_extend"])
+    h1, c1, o1 = oracle.run(w["target"], w["query"], w["seeds"], w["scoring"], w["ydrop"], threads=4)
+    h2, c2, o2 = oracle.run(w["target"], w["query"], w["seeds"], sc_m, w["ydrop"], threads=4)
+    assert np.array_equal(h1, h2) and np.array_equal(c1, c2) and np.array_equal(o1, o2)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_matrix_transpose_symmetry(seed):
+    """Swapping target and query with the matrix transposed keeps the score
+    (an alignment read the other way has the same columns), with pruning."""
+    rng = random.Random(7900 + seed)
+    sc = rand_matrix_scoring(rng)
+    sc["matrix"] = [[rng.randint(-60, 100) if x == y else rng.randint(-128, -20) for y in range(4)]
+                    for x in range(4)]
+    a = rand_seq(rng, 300, "ACGT")
+    b = list(a)
+    for _ in range(30):
+        b[rng.randrange(len(b))] = rng.choice("ACGTN")
+    b = "".join(b)
+    scT = dict(sc, matrix=[list(r) for r in zip(*sc["matrix"])])
+    for ydrop in (oracle.YDROP_INF, 500):
+        x = oracle.side(a, b, sc, ydrop)
+        y = oracle.side(b, a, scT, ydrop)
+        assert x["status"] == 0 and y["status"] == 0
+        assert x["score"] == y["score"]
+
+
+def test_n_needs_a_matrix():
+    """Without a matrix N is an invalid base; with one it scores n_score."""
+    r = oracle.side("ACNT", "ACGT", SC, oracle.YDROP_INF)
+    assert r["status"] != 0
+    sc = dict(matrix=matrix_of(SC), n_score=-7, gap_open=SC["gap_open"], gap_extend=SC["gap_extend"])
+    r = oracle.side("ACNT", "ACGT", sc, oracle.YDROP_INF)
+    assert r["status"] == 0 and r["score"] == 3 * SC["match"] - 7 and (r["ie"], r["je"]) == (4, 4)
