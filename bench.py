@@ -13,6 +13,7 @@ Workloads (seeded, synthetic; see smith_waterman_dp_amd/workloads.py):
   local           4,096 full-matrix local alignments of 2048 x 2048
   tiny, executor_heavy, chromosome
   chromosome_rc   the chromosome pair searched on the query's reverse strand
+  skewed_matrix   the skewed batch scored with a 4x4 matrix, runs of N planted
   seeds           the seed stage (fz_find_seeds) on the 20 Mbp chromosome pair,
                   both strands per step; reported in Mbp/s of target + query
 """
@@ -81,7 +82,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="skewed",
-                    choices=["skewed", "local", "tiny", "executor_heavy", "chromosome", "chromosome_rc", "seeds"])
+                    choices=["skewed", "local", "tiny", "executor_heavy", "chromosome", "chromosome_rc",
+                             "skewed_matrix", "seeds"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",

@@ -60,6 +60,19 @@ typedef struct {
     int32_t gap_open, gap_extend;
 } fz_scoring;
 
+/* A full substitution matrix, used instead of the three scores of
+ * fz_scoring when passed to fz_extend_batch.  sub[a][b] scores target base
+ * a against query base b, bases in the order A, C, G, T (the matrix need
+ * not be symmetric).  With a matrix the sequences may also hold N (either
+ * case), the unknown base: a pair with N on either side, N against N
+ * included, scores n_score.  Every entry and n_score must lie in
+ * -128..127.  (FastZ fixes no scoring; LASTZ, whose extension it
+ * accelerates, scores with such a matrix.) */
+typedef struct {
+    int32_t sub[4][4];
+    int32_t n_score;
+} fz_matrix;
+
 /* One seed: an exact match of seed_len bases at target[t_pos..] and
  * query[q_pos..], plus half-open windows that bound the extension (the
  * extension treats a window edge as a sequence end).  Requires
@@ -174,10 +187,15 @@ int fz_set_pointer_workspace(fz_ctx *ctx, uint64_t bytes);
 
 /*
  * Extend a batch of seeds (or, with FZ_LOCAL, align a batch of windows).
- *   target, query   device, ASCII bases (A/C/G/T in either case; any other
- *                   byte makes the call fail with FZ_EINVAL), lengths in bytes
+ *   target, query   device, ASCII bases (A/C/G/T in either case, and N
+ *                   when a matrix is given; any other byte makes the call
+ *                   fail with FZ_EINVAL), lengths in bytes
  *   seeds           device, n_seeds records
  *   scoring         host; costs must be >= 0
+ *   matrix          host or NULL: a substitution matrix replacing
+ *                   scoring's match / transition / transversion (its gap
+ *                   costs still apply); FZ_EINVAL for an entry outside
+ *                   -128..127
  *   ydrop           >= 0; FZ_YDROP_INF disables pruning (ignored in local mode)
  *   min_traceback_score   with FZ_TRACEBACK, seeds whose score is strictly
  *                   greater get a CIGAR; others get FZ_HIT_BELOW_MIN
@@ -195,7 +213,7 @@ int fz_extend_batch(fz_ctx *ctx,
                     const uint8_t *target, uint64_t target_len,
                     const uint8_t *query, uint64_t query_len,
                     const fz_seed *seeds, uint64_t n_seeds,
-                    const fz_scoring *scoring, int32_t ydrop,
+                    const fz_scoring *scoring, const fz_matrix *matrix, int32_t ydrop,
                     int64_t min_traceback_score, uint32_t flags,
                     fz_hit *hits, const uint32_t **cigar, uint64_t *cigar_words,
                     fz_stats *stats, void *stream);

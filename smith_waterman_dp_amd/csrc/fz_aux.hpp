@@ -9,37 +9,37 @@ namespace fz {
 // ------------------------------------------------------------------ pack --
 // ASCII -> 2-bit codes (A0 C1 G2 T3) one per byte, forward and reversed,
 // with PAD code-0 bases on both ends.  Any other byte raises *err.
+// ASCII -> byte codes, forward and reversed, with PAD zero bytes on each
+// side.  role 0: codes 0..3 for A, C, G, T (N is an error); role 1 / 2: the
+// matrix mode's target / query codes (mx_target_code, the base itself),
+// with N (either case) accepted as MX_N.  revcomp: the reverse complement
+// is coded instead (complement = base ^ 3 with A=0, C=1, G=2, T=3; N stays
+// N).  Any other byte sets bit 0 of *err and is coded as A.
 __global__ void pack_kernel(const uint8_t *__restrict__ ascii, int64_t len, uint8_t *__restrict__ fwd,
-                            uint8_t *__restrict__ rev, int64_t padded, uint32_t *err, int revcomp)
+                            uint8_t *__restrict__ rev, int64_t padded, uint32_t *err, int revcomp, int role)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     bool bad = false;
     for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < padded; x += stride) {
         const int64_t s = x - PAD;
-        uint8_t code = 0;
+        uint32_t code = 0;
         if (s >= 0 && s < len) {
-            // revcomp: base s of the reverse complement is the complement of
-            // base len-1-s; with A=0, C=1, G=2, T=3 the complement is code ^ 3
             const uint8_t c = ascii[revcomp ? len - 1 - s : s] & 0xDF;   // upper-case
-            code = c == 'A' ? 0 : c == 'C' ? 1 : c == 'G' ? 2 : c == 'T' ? 3 : 255;
+            code = c == 'A' ? 0 : c == 'C' ? 1 : c == 'G' ? 2 : c == 'T' ? 3 : (c == 'N' && role) ? MX_N : 255;
             if (code == 255) {
                 bad = true;
                 code = 0;
-            } else if (revcomp) {
-                code ^= 3;
+            } else if (code != MX_N) {
+                if (revcomp) code ^= 3;
+                if (role == 1) code = mx_target_code(code);
             }
         }
-        fwd[x] = code;
-        rev[padded - 1 - x] = code;
+        fwd[x] = (uint8_t)code;
+        rev[padded - 1 - x] = (uint8_t)code;
     }
     if (__ballot(bad) && lane_id() == 0) atomicOr(err, 1u);
 }
 
-__device__ __forceinline__ int sub_codes(int a, int b, const Scoring &sc)
-{
-    const int x = a ^ b;
-    return x == 0 ? sc.match : (x == 2 ? sc.ts : sc.tv);
-}
 
 // ----------------------------------------------------------------- setup --
 struct SeedInfo {
@@ -71,15 +71,13 @@ __global__ void setup_kernel(const fz_seed *__restrict__ seeds, int64_t n, int64
         const int64_t mr = s.t_hi - s.t_pos - Ls, nr = s.q_hi - s.q_pos - Ls;
         // worst case of any score reachable inside the windows must stay
         // far from the int32 sentinels
-        int64_t msub = sc.match;
-        msub = max(msub, (int64_t)(sc.ts < 0 ? -sc.ts : sc.ts));
-        msub = max(msub, (int64_t)(sc.tv < 0 ? -sc.tv : sc.tv));
+        const int64_t msub = sc.msub;
         const int64_t span = (s.t_hi - s.t_lo) + (s.q_hi - s.q_lo) + 2;
         if ((msub + sc.e) * span + sc.oe >= SCORE_LIMIT / 2) {
             in.status = FZ_HIT_ERANGE;
         } else {
             int64_t ss = 0;
-            for (int64_t c = 0; c < Ls; ++c) ss += sub_codes(Tf[PAD + s.t_pos + c], Qf[PAD + s.q_pos + c], sc);
+            for (int64_t c = 0; c < Ls; ++c) ss += sub_pair(Tf[PAD + s.t_pos + c], Qf[PAD + s.q_pos + c], sc);
             in.seed_score = ss;
             L.A = Tr;
             L.abase = NT - 1 - PAD - s.t_pos;

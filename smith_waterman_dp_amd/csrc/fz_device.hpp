@@ -26,13 +26,66 @@ constexpr int EAGER_OPS = 2 * EAGER_EDGE;
 // Length bins of FastZ section 3.3: 512, 2048, 8192, 32768, then x4.
 constexpr int NBINS = 8;
 
+// How a kernel scores a base pair (its template argument):
+//   SUB_WIDE    match / transition / transversion from the xor of the codes,
+//               any int32 scores;
+//   SUB_LUT     the same three scores as int8, one byte permute per four
+//               cells (the xor of two codes, 0..3, selects the byte);
+//   SUB_MATRIX  a 4x4 int8 matrix plus an N score (see matrix_scores).
+enum : int { SUB_WIDE = 0, SUB_LUT = 1, SUB_MATRIX = 2 };
+
+// Byte codes in the matrix mode.  Codes of the other modes are the bases
+// 0..3 (A, C, G, T) in both sequences.  Here the target and the query are
+// coded differently, so that OR-ing a target byte with a query byte gives a
+// byte-permute selector into the matrix: the query byte is its base (bits
+// 0-1), the target byte has its base's low bit at bit 2 and its high bit at
+// bit 6, and N is bit 7 in either.
+constexpr uint32_t MX_N = 0x80u;
+__host__ __device__ constexpr uint32_t mx_target_code(uint32_t base) { return ((base & 1u) << 2) | ((base >> 1) << 6); }
+
 struct Scoring {
-    int32_t match, ts, tv;      // substitution scores
+    int32_t match, ts, tv;      // substitution scores (SUB_WIDE, SUB_LUT)
     int32_t oe, e;              // open + extend, extend
     uint32_t lut;               // int8 score per xor code (A=0,C=1,G=2,T=3): [match, tv, ts, tv]
     int32_t ydrop;              // >= 0; values >= SCORE_LIMIT act as "no pruning"
     int32_t small;              // lut usable (all three scores fit int8)
+    int32_t mode;               // SUB_* the kernels are launched with
+    uint32_t mrow[4];           // SUB_MATRIX: row a (target A, C, G, T), byte b = score against query base b
+    uint32_t nrep;              // SUB_MATRIX: the N score in all four bytes
+    int32_t nsc;                // SUB_MATRIX: the N score
+    int32_t msub;               // largest |substitution score| (range checks)
 };
+
+// SUB_MATRIX: the four int8 scores of four cells from sel = target bytes |
+// query bytes.  A selector byte 0..7 picks from rows A and C (one permute),
+// 0x40..0x47 from rows G and T (a second permute after flipping bit 6); the
+// permute returns 0xFF for any selector byte of 13 or more, so each byte is
+// right in one permute and all ones in the other, and AND keeps the right
+// one.  Bit 7 (N) makes both all ones; a third permute spreads each byte's
+// bit 7 over the byte (selectors 8..11 copy the top bit of bytes 1, 3, 5, 7
+// of the pair (sel, sel << 8), which are sel's bytes 0, 2, 1, 3), and that
+// mask puts the N score in those bytes.
+__device__ __forceinline__ uint32_t matrix_scores(uint32_t sel, const Scoring &sc)
+{
+    const uint32_t lo = __builtin_amdgcn_perm(sc.mrow[1], sc.mrow[0], sel);
+    const uint32_t hi = __builtin_amdgcn_perm(sc.mrow[3], sc.mrow[2], sel ^ 0x40404040u);
+    const uint32_t nmask = __builtin_amdgcn_perm(sel, sel << 8, 0x0B090A08u);
+    return ((lo & hi) & ~nmask) | (sc.nrep & nmask);
+}
+
+// Score of one target code against one query code, any mode (setup and
+// per-row profiles; not the per-cell path).
+__host__ __device__ inline int sub_pair(uint32_t ta, uint32_t qb, const Scoring &sc)
+{
+    if (sc.mode == SUB_MATRIX) {
+        if ((ta | qb) & MX_N) return sc.nsc;
+        const uint32_t a = ((ta >> 2) & 1u) | ((ta >> 5) & 2u);
+        const uint32_t row = a == 0 ? sc.mrow[0] : a == 1 ? sc.mrow[1] : a == 2 ? sc.mrow[2] : sc.mrow[3];
+        return (int)(int8_t)((row >> (8 * (qb & 3u))) & 0xFFu);
+    }
+    const uint32_t x = ta ^ qb;
+    return x == 0 ? sc.match : (x == 2 ? sc.ts : sc.tv);
+}
 
 // One side of one seed.  a_i = A[abase + i], b_j = B[bbase - j] for
 // i = 1..m, j = 1..n.  A and B are padded code arrays (0..3), so every

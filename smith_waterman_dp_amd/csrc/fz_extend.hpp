@@ -51,8 +51,9 @@ struct ExtendArgs {
     Scoring sc;
 };
 
-template <int C, bool EXEC, bool SMALL>
+template <int C, bool EXEC, int SUB>
 struct SideDP {
+    static constexpr bool SMALL = SUB != SUB_WIDE;       // one byte per substitution score
     static constexpr int W = 64 * C;
     static constexpr int NDW = (C + 3) / 4;             // dwords of bases per lane
     static constexpr int P0 = 32 * C;                   // position of (0,0): lane 32, slot 0
@@ -139,8 +140,13 @@ struct SideDP {
         uint32_t X[NDW], P[NDW];
 #pragma unroll
         for (int k = 0; k < NDW; ++k) {
-            X[k] = TA[k] ^ QB[k];
-            P[k] = SMALL ? __builtin_amdgcn_perm(0u, sc.lut, X[k]) : 0u;
+            if (SUB == SUB_MATRIX) {
+                X[k] = 0u;
+                P[k] = matrix_scores(TA[k] | QB[k], sc);
+            } else {
+                X[k] = TA[k] ^ QB[k];
+                P[k] = SMALL ? __builtin_amdgcn_perm(0u, sc.lut, X[k]) : 0u;
+            }
         }
         // the one value that crosses a lane boundary
         int cross;
@@ -644,20 +650,20 @@ struct StartLayout {
 // down, from diagonal 256 on, when it narrows to 157 (the narrow layout
 // does about half the work per diagonal).  The executor makes the same
 // moves as the inspector, since they depend only on the hulls.
-template <int C, bool EXEC, bool SMALL>
+template <int C, bool EXEC, int SUB>
 __device__ __forceinline__ SideResult run_side(const SideTask &task, const Scoring &sc, int dstop, uint32_t *eager_lds,
                                                uint32_t *xfer, uint8_t *ptr_base, int64_t ptr_bytes)
 {
     SideResult r;
     if constexpr (C != 6) {
-        SideDP<C, EXEC, SMALL> dp(task, sc);
+        SideDP<C, EXEC, SUB> dp(task, sc);
         const int d = dp.start(dstop, eager_lds, ptr_base, ptr_bytes);
         if (d >= 0) dp.template advance<false>(d, dstop, eager_lds);
         r.take(dp);
         return r;
     } else {
-        SideDP<3, EXEC, SMALL> dn(task, sc);
-        SideDP<6, EXEC, SMALL> dw(task, sc);
+        SideDP<3, EXEC, SUB> dn(task, sc);
+        SideDP<6, EXEC, SUB> dw(task, sc);
         int d = dn.start(dstop, eager_lds, ptr_base, ptr_bytes);
         if (d < 0) {
             r.take(dn);
@@ -686,11 +692,11 @@ __device__ __forceinline__ SideResult run_side(const SideTask &task, const Scori
 // inspector fits 64 VGPRs (8 waves per SIMD), the executor 72 (7 waves)
 // with byte substitution scores and 80 (6) without; more waves let a SIMD
 // pair one wave's VALU instruction with another's SALU instruction.
-template <int C, bool EXEC, bool SMALL, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <= 8 ? (EXEC ? (SMALL ? 7 : 6) : 8) : 1))) void extend_kernel(ExtendArgs a)
+template <int C, bool EXEC, int SUB, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <= 8 ? (EXEC ? (SUB != SUB_WIDE ? 7 : 6) : 8) : 1))) void extend_kernel(ExtendArgs a)
 {
-    using DP = SideDP<C, EXEC, SMALL>;
-    using EDP = SideDP<StartLayout<C>::value, EXEC, SMALL>;     // holds the eager block
+    using DP = SideDP<C, EXEC, SUB>;
+    using EDP = SideDP<StartLayout<C>::value, EXEC, SUB>;     // holds the eager block
     __shared__ uint32_t eager_lds_all[WAVES][EAGER_ROWS * EDP::NEL * EDP::NWORD];
     __shared__ uint32_t xfer_all[WAVES][C == 6 ? 4 * DP::XFER_W : 1];
     const int wv = uniform((int)(threadIdx.x / 64));
@@ -712,7 +718,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <=
     }
     if (EXEC) {
         const ExecItem it = a.exec[item];
-        const SideResult x = run_side<C, EXEC, SMALL>(task, a.sc, it.dstar, nullptr, xfer,
+        const SideResult x = run_side<C, EXEC, SUB>(task, a.sc, it.dstar, nullptr, xfer,
                                                       a.ptr_ws + (it.ptr_off - a.ptr_base_off), it.ptr_bytes);
         if (fresh_lane_id() == 0) {
             atomicAdd((unsigned long long *)a.exec_cells, (unsigned long long)x.cells);
@@ -720,7 +726,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <=
         }
         return;
     }
-    const SideResult x = run_side<C, EXEC, SMALL>(task, a.sc, 0x7fffffff, eager_lds, xfer, nullptr, 0);
+    const SideResult x = run_side<C, EXEC, SUB>(task, a.sc, 0x7fffffff, eager_lds, xfer, nullptr, 0);
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     SideOut r;
     r.score = x.best;

@@ -185,20 +185,44 @@ int scan(fz_ctx *ctx, const int64_t *vals, int64_t stride, int64_t n, int64_t *o
     return FZ_OK;
 }
 
-Scoring make_scoring(const fz_scoring *s, int32_t ydrop)
+const char *bad_byte_msg(const Scoring &sc)
 {
-    Scoring sc;
+    return sc.mode == SUB_MATRIX ? "sequence holds a byte other than A, C, G, T, N"
+                                 : "sequence holds a byte other than A, C, G, T (N needs a substitution matrix)";
+}
+
+Scoring make_scoring(const fz_scoring *s, const fz_matrix *mx, int32_t ydrop)
+{
+    Scoring sc = {};
     sc.match = s->match;
     sc.ts = s->transition;
     sc.tv = s->transversion;
     sc.oe = s->gap_open + s->gap_extend;
     sc.e = s->gap_extend;
     auto fits = [](int v) { return v >= -128 && v <= 127; };
+    auto mag = [](int v) { return v < 0 ? -v : v; };
     sc.small = fits(sc.match) && fits(sc.ts) && fits(sc.tv);
     // xor code of two base codes: 0 equal, 2 transition, 1 or 3 transversion
     sc.lut = ((uint32_t)(sc.match & 0xFF)) | ((uint32_t)(sc.tv & 0xFF) << 8) | ((uint32_t)(sc.ts & 0xFF) << 16) |
              ((uint32_t)(sc.tv & 0xFF) << 24);
     sc.ydrop = (int64_t)ydrop >= SCORE_LIMIT ? (int32_t)SCORE_LIMIT : ydrop;
+    if (mx) {
+        sc.mode = SUB_MATRIX;
+        sc.small = 1;
+        sc.nsc = mx->n_score;
+        sc.nrep = 0x01010101u * ((uint32_t)mx->n_score & 0xFFu);
+        sc.msub = mag(mx->n_score);
+        for (int a = 0; a < 4; ++a) {
+            sc.mrow[a] = 0;
+            for (int b = 0; b < 4; ++b) {
+                sc.mrow[a] |= ((uint32_t)mx->sub[a][b] & 0xFFu) << (8 * b);
+                sc.msub = std::max(sc.msub, mag(mx->sub[a][b]));
+            }
+        }
+    } else {
+        sc.mode = sc.small ? SUB_LUT : SUB_WIDE;
+        sc.msub = std::max(mag(sc.match), std::max(mag(sc.ts), mag(sc.tv)));
+    }
     return sc;
 }
 
@@ -207,16 +231,24 @@ int launch_extend(fz_ctx *ctx, const ExtendArgs &a, int64_t nwork, hipStream_t s
 {
     if (nwork <= 0) return FZ_OK;
     const unsigned blocks = (unsigned)((nwork + EXT_WAVES - 1) / EXT_WAVES);
-    if (a.sc.small) extend_kernel<C, EXEC, true, EXT_WAVES><<<blocks, 64 * EXT_WAVES, 0, st>>>(a);
-    else extend_kernel<C, EXEC, false, EXT_WAVES><<<blocks, 64 * EXT_WAVES, 0, st>>>(a);
+    if (a.sc.mode == SUB_MATRIX) extend_kernel<C, EXEC, SUB_MATRIX, EXT_WAVES><<<blocks, 64 * EXT_WAVES, 0, st>>>(a);
+    else if (a.sc.mode == SUB_LUT) extend_kernel<C, EXEC, SUB_LUT, EXT_WAVES><<<blocks, 64 * EXT_WAVES, 0, st>>>(a);
+    else extend_kernel<C, EXEC, SUB_WIDE, EXT_WAVES><<<blocks, 64 * EXT_WAVES, 0, st>>>(a);
     HIP_OK(hipGetLastError());
     return FZ_OK;
 }
 
 int check_args(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const uint8_t *query, uint64_t qlen,
-               const fz_seed *seeds, uint64_t n, const fz_scoring *sc, int32_t ydrop, uint32_t flags, fz_hit *hits)
+               const fz_seed *seeds, uint64_t n, const fz_scoring *sc, const fz_matrix *mx, int32_t ydrop,
+               uint32_t flags, fz_hit *hits)
 {
     if (!sc) return fail(ctx, FZ_EINVAL, "scoring is NULL");
+    if (mx) {
+        bool ok = mx->n_score >= -128 && mx->n_score <= 127;
+        for (int a = 0; a < 4; ++a)
+            for (int b = 0; b < 4; ++b) ok = ok && mx->sub[a][b] >= -128 && mx->sub[a][b] <= 127;
+        if (!ok) return fail(ctx, FZ_EINVAL, "matrix entries and n_score must lie in -128..127");
+    }
     if (n > 0 && (!seeds || !hits)) return fail(ctx, FZ_EINVAL, "seeds or hits is NULL");
     if ((tlen > 0 && !target) || (qlen > 0 && !query)) return fail(ctx, FZ_EINVAL, "sequence pointer is NULL");
     if (tlen >= ((uint64_t)1 << 40) || qlen >= ((uint64_t)1 << 40)) return fail(ctx, FZ_EINVAL, "sequence too long");
@@ -277,8 +309,9 @@ int run_local(fz_ctx *ctx, const fz_seed *seeds, uint64_t n, uint64_t tlen, uint
     a.bnd_stride = stride;
     const unsigned blocks = blocks_for((int64_t)n, LOCAL_WAVES);
     HIP_OK(hipEventRecord(ctx->kev[0], st));
-    if (sc.small) local_kernel<LOCAL_RL, true, LOCAL_WAVES><<<blocks, 64 * LOCAL_WAVES, 0, st>>>(a);
-    else local_kernel<LOCAL_RL, false, LOCAL_WAVES><<<blocks, 64 * LOCAL_WAVES, 0, st>>>(a);
+    if (sc.mode == SUB_MATRIX) local_kernel<LOCAL_RL, SUB_MATRIX, LOCAL_WAVES><<<blocks, 64 * LOCAL_WAVES, 0, st>>>(a);
+    else if (sc.mode == SUB_LUT) local_kernel<LOCAL_RL, SUB_LUT, LOCAL_WAVES><<<blocks, 64 * LOCAL_WAVES, 0, st>>>(a);
+    else local_kernel<LOCAL_RL, SUB_WIDE, LOCAL_WAVES><<<blocks, 64 * LOCAL_WAVES, 0, st>>>(a);
     HIP_OK(hipGetLastError());
     HIP_OK(hipEventRecord(ctx->kev[1], st));
     return FZ_OK;
@@ -324,9 +357,10 @@ static int seeds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const u
     tm.mark();
     if (!reuse)
         pack_kernel<<<std::min<int64_t>(blocks_for(NT, 256), 8192), 256, 0, st>>>(
-            target, (int64_t)tlen, as<uint8_t>(ctx->Tf), as<uint8_t>(ctx->Tr), NT, &dc->err, 0);
+            target, (int64_t)tlen, as<uint8_t>(ctx->Tf), as<uint8_t>(ctx->Tr), NT, &dc->err, 0, 0);
     pack_kernel<<<std::min<int64_t>(blocks_for(NQ, 256), 8192), 256, 0, st>>>(
-        query, (int64_t)qlen, as<uint8_t>(ctx->Qf), as<uint8_t>(ctx->Qr), NQ, &dc->err, (flags & FZ_QUERY_RC) ? 1 : 0);
+        query, (int64_t)qlen, as<uint8_t>(ctx->Qf), as<uint8_t>(ctx->Qr), NQ, &dc->err, (flags & FZ_QUERY_RC) ? 1 : 0,
+        0);
     HIP_OK(hipGetLastError());
     tm.mark();
 
@@ -568,11 +602,11 @@ int fz_set_pointer_workspace(fz_ctx *ctx, uint64_t bytes)
 }
 
 static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const uint8_t *query, uint64_t qlen,
-                       const fz_seed *seeds, uint64_t n_seeds, const fz_scoring *scoring, int32_t ydrop,
-                       int64_t min_tb, uint32_t flags, fz_hit *hits, const uint32_t **cigar, uint64_t *cigar_words,
-                       fz_stats *stats, hipStream_t st)
+                       const fz_seed *seeds, uint64_t n_seeds, const fz_scoring *scoring, const fz_matrix *matrix,
+                       int32_t ydrop, int64_t min_tb, uint32_t flags, fz_hit *hits, const uint32_t **cigar,
+                       uint64_t *cigar_words, fz_stats *stats, hipStream_t st)
 {
-    int rc = check_args(ctx, target, tlen, query, qlen, seeds, n_seeds, scoring, ydrop, flags, hits);
+    int rc = check_args(ctx, target, tlen, query, qlen, seeds, n_seeds, scoring, matrix, ydrop, flags, hits);
     if (rc != FZ_OK) return rc;
     if (cigar) *cigar = nullptr;
     if (cigar_words) *cigar_words = 0;
@@ -584,7 +618,7 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         if (stats) *stats = S;
         return FZ_OK;
     }
-    const Scoring sc = make_scoring(scoring, ydrop);
+    const Scoring sc = make_scoring(scoring, matrix, ydrop);
     const int64_t NT = (int64_t)tlen + 2 * PAD, NQ = (int64_t)qlen + 2 * PAD;
 
     ENSURE(ctx->counters, sizeof(Counters));
@@ -600,14 +634,15 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     ENSURE(ctx->Qr, NQ + 64);
     {
         const unsigned bt = std::min<int64_t>(blocks_for(NT, 256), 8192);
+        const int mxr = sc.mode == SUB_MATRIX ? 1 : 0;     // matrix mode: role codes, N accepted
         pack_kernel<<<bt, 256, 0, st>>>(target, (int64_t)tlen, as<uint8_t>(ctx->Tf), as<uint8_t>(ctx->Tr), NT,
-                                        &dc->err, 0);
+                                        &dc->err, 0, mxr);
         HIP_OK(hipGetLastError());
         const unsigned bq = std::min<int64_t>(blocks_for(NQ, 256), 8192);
         // with FZ_QUERY_RC every later step sees the query's reverse
         // complement: seeds, windows and results are in its coordinates
         pack_kernel<<<bq, 256, 0, st>>>(query, (int64_t)qlen, as<uint8_t>(ctx->Qf), as<uint8_t>(ctx->Qr), NQ,
-                                        &dc->err, (flags & FZ_QUERY_RC) ? 1 : 0);
+                                        &dc->err, (flags & FZ_QUERY_RC) ? 1 : 0, 2 * mxr);
         HIP_OK(hipGetLastError());
     }
     Counters hc;
@@ -622,7 +657,7 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         if (rc) return rc;
         tm.mark();
         if ((rc = read_counters())) return rc;
-        if (hc.err & 1u) return fail(ctx, FZ_EINVAL, "sequence holds a byte other than A, C, G, T");
+        if (hc.err & 1u) return fail(ctx, FZ_EINVAL, "%s", bad_byte_msg(sc));
         if (stats) {
             S.ms_inspect = tm.ms(0, 1);
             (void)hipEventElapsedTime(&S.ms_main, ctx->kev[0], ctx->kev[1]);
@@ -663,7 +698,7 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     if (rc) return rc;
     HIP_OK(hipEventRecord(ctx->kev[1], st));
     if ((rc = read_counters())) return rc;
-    if (hc.err & 1u) return fail(ctx, FZ_EINVAL, "sequence holds a byte other than A, C, G, T");
+    if (hc.err & 1u) return fail(ctx, FZ_EINVAL, "%s", bad_byte_msg(sc));
     S.n_overflow = hc.overflow_count[0];
     if (hc.overflow_count[0] > 0) {
         ExtendArgs wa = ea;
@@ -867,7 +902,8 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
 }
 
 int fz_extend_batch(fz_ctx *ctx, const uint8_t *target, uint64_t target_len, const uint8_t *query, uint64_t query_len,
-                    const fz_seed *seeds, uint64_t n_seeds, const fz_scoring *scoring, int32_t ydrop,
+                    const fz_seed *seeds, uint64_t n_seeds, const fz_scoring *scoring, const fz_matrix *matrix,
+                    int32_t ydrop,
                     int64_t min_traceback_score, uint32_t flags, fz_hit *hits, const uint32_t **cigar,
                     uint64_t *cigar_words, fz_stats *stats, void *stream)
 {
@@ -883,7 +919,7 @@ int fz_extend_batch(fz_ctx *ctx, const uint8_t *target, uint64_t target_len, con
         (void)hipGetLastError();
         return fail(ctx, FZ_EDEVICE, "hipSetDevice(%d) failed", ctx->device);
     }
-    const int rc = extend_impl(ctx, target, target_len, query, query_len, seeds, n_seeds, scoring, ydrop,
+    const int rc = extend_impl(ctx, target, target_len, query, query_len, seeds, n_seeds, scoring, matrix, ydrop,
                                min_traceback_score, flags, hits, cigar, cigar_words, stats, (hipStream_t)stream);
     if (prev != ctx->device) (void)hipSetDevice(prev);
     return rc;

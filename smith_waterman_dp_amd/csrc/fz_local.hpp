@@ -13,7 +13,9 @@
 // move per step.  The strip's last row is spilled to memory for the next
 // strip (FastZ section 3.2's strip-boundary spill).  The substitution score
 // comes from a per-row profile: four int8 scores (one per query base) packed
-// in one register, so a cell's score is one signed byte extract.
+// in one register, so a cell's score is one signed byte extract.  With a
+// substitution matrix the profile is the matrix row of the row's target base
+// (the N score in every byte for N), and a query N takes the N score.
 //
 // End cell: largest S, ties to the smallest anti-diagonal d = i + j, then
 // the smallest i; (0,0) when nothing scores above 0.
@@ -35,9 +37,10 @@ struct LocalArgs {
     int64_t bnd_stride;
 };
 
-template <int RL, bool SMALL, int WAVES>
+template <int RL, int SUB, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void local_kernel(LocalArgs a)
 {
+    constexpr bool SMALL = SUB != SUB_WIDE;
     const int lane = lane_id();
     const int64_t wave = (int64_t)blockIdx.x * WAVES + threadIdx.x / 64;
     if (wave >= a.n) return;
@@ -55,9 +58,7 @@ __global__ __launch_bounds__(64 * WAVES) void local_kernel(LocalArgs a)
     }
     const int m = (int)(s.t_hi - s.t_lo), n = (int)(s.q_hi - s.q_lo);
     const Scoring &sc = a.sc;
-    int64_t msub = sc.match;
-    msub = max(msub, (int64_t)(sc.ts < 0 ? -sc.ts : sc.ts));
-    msub = max(msub, (int64_t)(sc.tv < 0 ? -sc.tv : sc.tv));
+    const int64_t msub = sc.msub;
     if ((msub + sc.e) * ((int64_t)m + n + 2) + sc.oe >= SCORE_LIMIT / 2) {
         if (lane == 0) {
             h.status = FZ_HIT_ERANGE;
@@ -82,7 +83,13 @@ __global__ __launch_bounds__(64 * WAVES) void local_kernel(LocalArgs a)
             const int ca = i <= m ? A[i - 1] : 0;
             // byte b of prof: score of a_i against query base b
             uint32_t p = 0;
-            if (SMALL) {
+            if (SUB == SUB_MATRIX) {
+                // the matrix row of a_i (the N score throughout for N)
+                const uint32_t ua = (uint32_t)ca;
+                const uint32_t ra = ((ua >> 2) & 1u) | ((ua >> 5) & 2u);
+                p = (ua & MX_N) ? sc.nrep
+                                : ra == 0 ? sc.mrow[0] : ra == 1 ? sc.mrow[1] : ra == 2 ? sc.mrow[2] : sc.mrow[3];
+            } else if (SMALL) {
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     const int x = ca ^ b;
@@ -116,12 +123,15 @@ __global__ __launch_bounds__(64 * WAVES) void local_kernel(LocalArgs a)
             int colmax = 0;
             if (active) {
                 const int bj = B[j - 1];
-                const uint32_t sh = 8u * (uint32_t)bj;
+                const uint32_t sh = 8u * ((uint32_t)bj & 3u);
+                const bool colN = SUB == SUB_MATRIX && ((uint32_t)bj & MX_N);   // query base N
                 int diag = diag0, uS = upS0, uD = upD0;
 #pragma unroll
                 for (int r = 0; r < RL; ++r) {
                     int sub;
-                    if (SMALL) {
+                    if (SUB == SUB_MATRIX) {
+                        sub = colN ? sc.nsc : (int)(int8_t)((prof[r] >> sh) & 0xFFu);
+                    } else if (SMALL) {
                         sub = (int)(int8_t)((prof[r] >> sh) & 0xFFu);
                     } else {
                         const int x = (int)prof[r] ^ bj;

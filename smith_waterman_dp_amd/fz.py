@@ -31,6 +31,24 @@ class fz_scoring(ctypes.Structure):
                 ("gap_open", ctypes.c_int32), ("gap_extend", ctypes.c_int32)]
 
 
+class fz_matrix(ctypes.Structure):
+    _fields_ = [("sub", (ctypes.c_int32 * 4) * 4), ("n_score", ctypes.c_int32)]
+
+
+def _matrix_of(scoring):
+    """fz_matrix from a scoring dict's "matrix" (4x4, rows = target base,
+    columns = query base, order A, C, G, T) and "n_score", or None."""
+    mat = scoring.get("matrix")
+    if mat is None:
+        return None
+    m = fz_matrix()
+    for a in range(4):
+        for b in range(4):
+            m.sub[a][b] = int(mat[a][b])
+    m.n_score = int(scoring.get("n_score", 0))
+    return m
+
+
 class fz_stats(ctypes.Structure):
     _fields_ = [("cells", ctypes.c_uint64), ("executor_cells", ctypes.c_uint64),
                 ("pointer_bytes", ctypes.c_uint64), ("n_sides", ctypes.c_uint64), ("n_eager", ctypes.c_uint64),
@@ -81,7 +99,8 @@ def load_library(path=LIB_PATH):
     lib.fz_set_pointer_workspace.restype = ctypes.c_int
     lib.fz_set_pointer_workspace.argtypes = [P, u64]
     lib.fz_extend_batch.restype = ctypes.c_int
-    lib.fz_extend_batch.argtypes = [P, P, u64, P, u64, P, u64, ctypes.POINTER(fz_scoring), i32, i64,
+    lib.fz_extend_batch.argtypes = [P, P, u64, P, u64, P, u64, ctypes.POINTER(fz_scoring), ctypes.POINTER(fz_matrix),
+                                    i32, i64,
                                     ctypes.c_uint32, P, ctypes.POINTER(P), ctypes.POINTER(u64),
                                     ctypes.POINTER(fz_stats), P]
     lib.fz_copy_cigar.restype = ctypes.c_int
@@ -135,7 +154,9 @@ def fz_extend_batch(ctx, target, query, seeds, scoring, ydrop, min_traceback_sco
 
     target, query: uint8 CUDA tensors of ASCII bases.  seeds: int64 CUDA
     tensor (n, 7) in SEED_FIELDS order.  scoring: dict with match,
-    transition, transversion, gap_open, gap_extend.
+    transition, transversion, gap_open, gap_extend; or with "matrix" (4x4,
+    rows = target base) and "n_score" in place of the three scores, which
+    also lets the sequences hold N.
     Returns (hits, cigar, stats): hits an int64 (n, 12) CUDA tensor in
     HIT_FIELDS order, cigar an int32 CUDA tensor of BAM-style words
     (len << 4 | op), stats a dict or None.
@@ -149,8 +170,9 @@ def fz_extend_batch(ctx, target, query, seeds, scoring, ydrop, min_traceback_sco
         raise ValueError("seeds must have shape (n, 7)")
     n = seeds.shape[0]
     hits = torch.empty((n, len(HIT_FIELDS)), dtype=torch.int64, device=seeds.device)
-    sc = fz_scoring(int(scoring["match"]), int(scoring["transition"]), int(scoring["transversion"]),
-                    int(scoring["gap_open"]), int(scoring["gap_extend"]))
+    sc = fz_scoring(int(scoring.get("match", 0)), int(scoring.get("transition", 0)),
+                    int(scoring.get("transversion", 0)), int(scoring["gap_open"]), int(scoring["gap_extend"]))
+    mx = _matrix_of(scoring)
     cig_ptr = ctypes.c_void_p()
     words = ctypes.c_uint64(0)
     st = fz_stats()
@@ -158,7 +180,8 @@ def fz_extend_batch(ctx, target, query, seeds, scoring, ydrop, min_traceback_sco
         flags |= FZ_STATS
     strm = _stream_handle(stream)
     rc = lib.fz_extend_batch(ctx, target.data_ptr(), target.numel(), query.data_ptr(), query.numel(),
-                             seeds.data_ptr(), n, ctypes.byref(sc), int(min(int(ydrop), FZ_YDROP_INF)),
+                             seeds.data_ptr(), n, ctypes.byref(sc), ctypes.byref(mx) if mx is not None else None,
+                             int(min(int(ydrop), FZ_YDROP_INF)),
                              int(min_traceback_score), int(flags), hits.data_ptr() if n else None,
                              ctypes.byref(cig_ptr), ctypes.byref(words),
                              ctypes.byref(st), strm)

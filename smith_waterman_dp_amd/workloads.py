@@ -13,7 +13,8 @@ sequences, 19-bp exact seeds, and the skewed alignment-length mix of the
 paper's section 1 (most seed sites give alignments of at most 128 bp, a few
 run to tens of kb) and Table 2.
 
-Bases are ASCII bytes 'A', 'C', 'G', 'T'.  A seed record is seven int64s:
+Bases are ASCII bytes 'A', 'C', 'G', 'T' (and 'N', the unknown base, in the
+matrix workloads).  A seed record is seven int64s:
 (t_pos, q_pos, seed_len, t_lo, t_hi, q_lo, q_hi); the windows are half-open.
 """
 import numpy as np
@@ -24,6 +25,71 @@ WINDOW_FLANK = 32768          # largest length bin of FastZ section 3.3
 
 DEFAULT_SCORING = dict(match=91, transition=-31, transversion=-123, gap_open=400, gap_extend=30)
 DEFAULT_YDROP = 9400
+
+# A synthetic asymmetric 4x4 substitution matrix (rows = target base,
+# columns = query base, order A, C, G, T) of the same magnitudes as the
+# default triple: matches 92..100, transitions about -30, transversions
+# about -120; and a score for any pair with the unknown base N.
+DEFAULT_MATRIX = [[95, -120, -30, -125],
+                  [-115, 100, -120, -35],
+                  [-32, -118, 98, -110],
+                  [-122, -28, -116, 92]]
+DEFAULT_N_SCORE = -100
+
+
+def matrix_scoring(matrix=None, n_score=DEFAULT_N_SCORE, gap_open=400, gap_extend=30):
+    return dict(matrix=[list(r) for r in (DEFAULT_MATRIX if matrix is None else matrix)], n_score=n_score,
+                gap_open=gap_open, gap_extend=gap_extend)
+
+
+def plant_n_runs(rng, ascii_seq, n_runs, len_min, len_max, keep=None):
+    """A copy of an ASCII sequence with `n_runs` runs of 'N' (lengths
+    U{len_min..len_max}, uniform start positions); positions where `keep`
+    is true keep their bases."""
+    out = np.array(ascii_seq, dtype=np.uint8, copy=True)
+    if out.size == 0 or n_runs <= 0:
+        return out
+    starts = rng.integers(0, out.size, size=n_runs)
+    lens = rng.integers(len_min, len_max + 1, size=n_runs)
+    cover = np.zeros(out.size + 1, dtype=np.int64)
+    np.add.at(cover, starts, 1)
+    np.add.at(cover, np.minimum(starts + lens, out.size), -1)
+    mask = np.cumsum(cover[:-1]) > 0
+    if keep is not None:
+        mask &= ~keep
+    out[mask] = ord("N")
+    return out
+
+
+def seed_span_mask(seeds, length, col_pos, col_len=2):
+    """True on every base covered by a seed's exact-match columns."""
+    cover = np.zeros(length + 1, dtype=np.int64)
+    if len(seeds):
+        s = seeds[:, col_pos]
+        np.add.at(cover, s, 1)
+        np.add.at(cover, np.minimum(s + seeds[:, col_len], length), -1)
+    return np.cumsum(cover[:-1]) > 0
+
+
+def with_matrix_and_n(w, n_runs, len_min, len_max, seed):
+    """The workload scored with DEFAULT_MATRIX, with runs of N planted in
+    both sequences outside every seed's exact columns."""
+    rng = np.random.default_rng(seed)
+    out = dict(w)
+    out["name"] = w["name"] + "_matrix"
+    out["scoring"] = matrix_scoring(gap_open=w["scoring"]["gap_open"], gap_extend=w["scoring"]["gap_extend"])
+    S = w["seeds"]
+    out["target"] = plant_n_runs(rng, w["target"], n_runs, len_min, len_max,
+                                 keep=seed_span_mask(S, w["target"].size, 0))
+    if w.get("query_rc"):
+        # seed columns are on the reverse complement: mirror them
+        L = w["query"].size
+        m = seed_span_mask(S, L, 1)[::-1]
+    else:
+        m = seed_span_mask(S, w["query"].size, 1)
+    out["query"] = plant_n_runs(rng, w["query"], n_runs, len_min, len_max, keep=m)
+    out["info"] = dict(w.get("info", {}), n_runs=n_runs)
+    return out
 
 
 def to_ascii(codes):
@@ -393,6 +459,13 @@ def chromosome_seed_stage(length=20_000_000, sub_rate=0.12, indel_rate=0.01, p_g
             "flank": flank}
 
 
+def skewed_matrix(seed=0, **kw):
+    """The skewed batch scored with the 4x4 matrix, with 400 runs of N of
+    10..1000 bases planted in each sequence (about 2% of it) outside the
+    seeds' exact columns."""
+    return with_matrix_and_n(skewed(seed=seed, **kw), 400, 10, 1000, seed=100 + seed)
+
+
 WORKLOADS = {
     "tiny": tiny,
     "local": local_pairs,
@@ -400,4 +473,5 @@ WORKLOADS = {
     "executor_heavy": executor_heavy,
     "chromosome": chromosome,
     "chromosome_rc": chromosome_rc,
+    "skewed_matrix": skewed_matrix,
 }

@@ -37,7 +37,7 @@ def test_struct_sizes_match_header():
 def test_null_context_is_rejected():
     lib = fz.load_library()
     sc = fz.fz_scoring(91, -31, -123, 400, 30)
-    rc = lib.fz_extend_batch(None, None, 0, None, 0, None, 0, ctypes.byref(sc), 9400, 0, 0, None,
+    rc = lib.fz_extend_batch(None, None, 0, None, 0, None, 0, ctypes.byref(sc), None, 9400, 0, 0, None,
                              None, None, None, None)
     assert rc == fz.FZ_EINVAL
     assert lib.fz_set_pointer_workspace(None, 0) == fz.FZ_EINVAL

@@ -365,11 +365,20 @@ def check_invariants(w, gh, gc, label, limit=1500):
     `limit` traced seeds, chosen by a seeded draw."""
     T, Q = w["target"], oracle_query(w)
     code = np.full(256, -1, dtype=np.int64)
-    for k, c in enumerate(b"ACGT"):
+    for k, c in enumerate(b"ACGTN"):
         code[c] = k
         code[c + 32] = k
     sc = w["scoring"]
-    lut = np.array([sc["match"], sc["transversion"], sc["transition"], sc["transversion"]], dtype=np.int64)
+    # score of (target code, query code), N = 4
+    table = np.zeros((5, 5), dtype=np.int64)
+    if "matrix" in sc:
+        table[:4, :4] = np.asarray(sc["matrix"], dtype=np.int64)
+        table[4, :] = table[:, 4] = sc["n_score"]
+    else:
+        cls = [sc["match"], sc["transversion"], sc["transition"], sc["transversion"]]
+        for x in range(4):
+            for y in range(4):
+                table[x, y] = cls[x ^ y]
     traced = np.nonzero(gh[:, 1] & fz.FZ_HIT_TRACED)[0]
     if traced.size > limit:
         traced = np.sort(np.random.default_rng(1).choice(traced, limit, replace=False))
@@ -382,7 +391,7 @@ def check_invariants(w, gh, gc, label, limit=1500):
             if op == 0:
                 a = code[T[t:t + n]]
                 b = code[Q[q:q + n]]
-                total += int(lut[a ^ b].sum())
+                total += int(table[a, b].sum())
                 t += n
                 q += n
             else:
@@ -524,3 +533,109 @@ def test_chromosome_rc_full_size_sampled(ctx):
     alignments against the oracle, invariants on the rest."""
     log("generating the chromosome pair, reverse-strand seeds")
     _full_size_sampled(ctx, W.chromosome_rc(), 24, 4, "chromosome rc full")
+
+
+# ------------------------------------------------ 4x4 matrix and N ---
+
+def sprinkle_n(rng, seq, rate):
+    a = np.array(seq, dtype=np.uint8, copy=True)
+    hit = np.array([rng.random() < rate for _ in range(a.size)], dtype=bool)
+    a[hit] = ord("N") if rng.random() < 0.5 else ord("n")
+    return a
+
+
+def rand_matrix(rng):
+    return [[rng.randint(-128, 127) for _ in range(4)] for _ in range(4)]
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_matrix_random_small_batches(ctx, case):
+    """Random cases, random asymmetric int8 matrices and N scores, N in
+    both sequences (seed columns included), every field against the
+    oracle at several y-drops."""
+    rng = random.Random(90 + case)
+    w = random_case_workload(rng, 100)
+    w["target"] = sprinkle_n(rng, w["target"], 0.03)
+    w["query"] = sprinkle_n(rng, w["query"], 0.03)
+    mat = rand_matrix(rng)
+    for a in range(4):       # matches positive so extensions run
+        mat[a][a] = rng.randint(20, 127)
+    w["scoring"] = dict(matrix=mat, n_score=rng.randint(-128, 127), gap_open=rng.randint(0, 400),
+                        gap_extend=rng.randint(1, 60))
+    for ydrop in (0, 150, 1000, fz.FZ_YDROP_INF):
+        gh, gc, _ = run_gpu(ctx, w, ydrop=ydrop)
+        oh, ow, oo = run_oracle(w, ydrop=ydrop)
+        compare(gh, gc, oh, ow, oo, label="matrix case %d ydrop %d" % (case, ydrop))
+
+
+def test_matrix_of_triple_equals_triple(ctx):
+    """The triple written as a matrix runs the matrix kernels and gives the
+    triple kernels' results bit for bit."""
+    w = W.tiny(n_seeds=400, seed=31)
+    sc = w["scoring"]
+    cls = {0: "match", 2: "transition"}
+    mat = [[sc[cls.get(x ^ y, "transversion")] for y in range(4)] for x in range(4)]
+    wm = dict(w, scoring=dict(matrix=mat, n_score=-128, gap_open=sc["gap_open"], gap_extend=sc["gap_extend"]))
+    h1, c1, _ = run_gpu(ctx, w)
+    h2, c2, _ = run_gpu(ctx, wm)
+    assert np.array_equal(h1, h2) and np.array_equal(c1, c2)
+
+
+def test_matrix_tiny_with_n(ctx):
+    rng = np.random.default_rng(4)
+    w = W.with_matrix_and_n(W.tiny(n_seeds=500, seed=32), 60, 1, 40, seed=5)
+    assert (w["target"] == ord("N")).any() and (w["query"] == ord("N")).any()
+    gh, gc, _ = run_gpu(ctx, w)
+    oh, ow, oo = run_oracle(w)
+    compare(gh, gc, oh, ow, oo, label="matrix tiny with N")
+    check_invariants(w, gh, gc, "matrix tiny with N")
+
+
+def test_matrix_reverse_strand(ctx):
+    w = W.with_matrix_and_n(W.chromosome_rc(length=300_000, inv_min=5_000, inv_max=20_000, seed=6), 30, 5, 200,
+                            seed=7)
+    gh, gc, st = sample_compare(ctx, w, 60, "matrix chromosome rc reduced")
+    check_invariants(w, gh, gc, "matrix chromosome rc reduced", limit=200)
+
+
+def test_matrix_local(ctx):
+    rng = random.Random(12)
+    w = W.local_pairs(n_pairs=48, length=300, seed=8)
+    w["target"] = sprinkle_n(rng, w["target"], 0.02)
+    w["query"] = sprinkle_n(rng, w["query"], 0.02)
+    w["scoring"] = W.matrix_scoring()
+    gh, gc, _ = run_gpu(ctx, w, local=True)
+    oh, ow, oo = run_oracle(w, local=True)
+    compare(gh, gc, oh, ow, oo, local=True, label="matrix local")
+
+
+def test_matrix_skewed_reduced(ctx):
+    w = W.with_matrix_and_n(W.skewed(target_len=1_000_000, n_seeds=20_000, n_short=30, n_long=10, seed=1),
+                            60, 10, 1000, seed=9)
+    gh, gc, st = sample_compare(ctx, w, 300, "matrix skewed reduced")
+    check_invariants(w, gh, gc, "matrix skewed reduced")
+
+
+def test_matrix_errors(ctx):
+    w = W.tiny(n_seeds=4, seed=33)
+    T = w["target"].copy()
+    T[300] = ord("N")
+    with pytest.raises(fz.FzError):                       # N without a matrix
+        run_gpu(ctx, dict(w, target=T))
+    bad = W.matrix_scoring()
+    bad["matrix"][1][2] = 128
+    with pytest.raises(fz.FzError):                       # entry outside int8
+        run_gpu(ctx, dict(w, scoring=bad))
+    bad = W.matrix_scoring(n_score=-129)
+    with pytest.raises(fz.FzError):
+        run_gpu(ctx, dict(w, scoring=bad))
+    T[300] = ord("R")                                      # other letters stay invalid
+    with pytest.raises(fz.FzError):
+        run_gpu(ctx, dict(w, target=T, scoring=W.matrix_scoring()))
+
+
+@pytest.mark.skipif(os.environ.get("FZ_FULL_SIZE", "1") == "0", reason="full-size runs disabled")
+def test_skewed_matrix_full_size_sampled(ctx):
+    """The matrix benchmark batch (one million seeds, runs of N), sampled."""
+    w = W.skewed_matrix()
+    _full_size_sampled(ctx, w, 120, 4, "skewed matrix full")
