@@ -48,8 +48,8 @@ OPS_PER_CELL = {"extend": 13, "local": 12}
 # reads 0.5 GiB for it, WRITE_SIZE 1.0 GiB).  Valid only for the kernel
 # sources it was taken on (hash of fz_extend.hpp + fz_device.hpp); reported
 # as null otherwise.
-TRAFFIC_SRC_HASH = "66a8a73eb5258606"
-TRAFFIC_FETCH_BYTES = 2.121e6 * 1024 / 0.5
+TRAFFIC_SRC_HASH = "c5d4c1d4c1b1f087"
+TRAFFIC_FETCH_BYTES = 2.120e6 * 1024 / 0.5
 TRAFFIC_WRITE_BYTES = 1.704e5 * 1024 / 1.0
 
 
