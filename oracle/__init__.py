@@ -22,6 +22,7 @@ _LIB = os.path.join(_HERE, "libfz_oracle.so")
 YDROP_INF = 2147483647
 
 STATUS_ESEED, STATUS_EBASE, STATUS_ERANGE, STATUS_ENOMEM = 1, 2, 4, 8
+STATUS_COVERED = 128          # extend_rounds: the seed lies on an earlier round's alignment
 
 HIT_FIELDS = ["score", "t_begin", "t_end", "q_begin", "q_end",
               "score_l", "i_l", "j_l", "score_r", "i_r", "j_r",
@@ -250,6 +251,80 @@ def side(a, b, scoring, ydrop, matrices=False, traceback=True):
         NEG = np.iinfo(np.int64).min
         res["S"], res["I"], res["D"] = [np.where(x == NEG, None, x).astype(object) for x in (Sm, Im, Dm)]
     return res
+
+
+def aligned_segments(hits, words, offs):
+    """The aligned (M) columns of every traced alignment, as segments on
+    diagonals: (t - q, t_first, t_last + 1) for each M run, walking each
+    CIGAR from (t_begin, q_begin) (I consumes query, D consumes target)."""
+    segs = []
+    for k in range(len(hits)):
+        n = int(hits["n_runs"][k])
+        if n == 0:
+            continue
+        t, q = int(hits["t_begin"][k]), int(hits["q_begin"][k])
+        for w in words[offs[k]:offs[k] + n].tolist():
+            ln, op = w >> 4, w & 15
+            if op == 0:
+                segs.append((t - q, t, t + ln))
+                t += ln
+                q += ln
+            elif op == 1:
+                q += ln
+            else:
+                t += ln
+    return segs
+
+
+def extend_rounds(target, query, seeds, scoring, ydrop, min_tb, round_size, threads=None):
+    """Covered-seed suppression by rounds.
+
+    FastZ (SC'21) section 2.1 describes LASTZ ending a seed extension that
+    runs into an alignment it found before (joining the two would not pay),
+    and section 3.4 why FastZ drops that rule: it depends on the order of
+    the extensions.  Reading taken here, the data-parallel form of the rule:
+    seeds are taken in the given order in rounds of `round_size`; a seed of
+    round r whose exact-match columns (t_pos + k, q_pos + k), k < seed_len,
+    share a cell with the aligned (M) columns of an alignment traced (given
+    a CIGAR) in rounds before r is not extended and gets status
+    STATUS_COVERED with every other field zero; every other seed of round r
+    is extended on its own, as run() extends it.  Seeds of one round never
+    suppress each other.
+
+    Returns (hits, words, offsets) as run(); a seed's CIGAR words are those
+    run() gives it, concatenated in seed order.
+    """
+    S = seeds_array(seeds)
+    n = S.shape[0]
+    if round_size < 1:
+        raise ValueError("round_size must be >= 1")
+    hits = np.zeros(n, dtype=HIT_DTYPE)
+    cig = [np.zeros(0, dtype=np.uint32) for _ in range(n)]
+    by_diag = {}                       # diagonal -> list of (t_first, t_end) of earlier rounds
+    for r0 in range(0, n, round_size):
+        idx = np.arange(r0, min(r0 + round_size, n))
+        keep = []
+        for k in idx:
+            t, q, L = int(S[k, 0]), int(S[k, 1]), int(S[k, 2])
+            covered = any(a < t + L and b > t for a, b in by_diag.get(t - q, ()))
+            if covered:
+                hits["status"][k] = STATUS_COVERED
+            else:
+                keep.append(k)
+        if not keep:
+            continue
+        keep = np.array(keep)
+        h, w, o = run(target, query, S[keep], scoring, ydrop, min_tb=min_tb, threads=threads)
+        hits[keep] = h
+        for j, k in enumerate(keep):
+            cig[k] = w[o[j]:o[j] + h["n_runs"][j]]
+        for dg, a, b in aligned_segments(h, w, o):
+            by_diag.setdefault(dg, []).append((a, b))
+    words = np.concatenate(cig) if n else np.zeros(0, dtype=np.uint32)
+    offs = np.zeros(n, dtype=np.int64)
+    if n:
+        offs[1:] = np.cumsum(hits["n_runs"])[:-1]
+    return hits, words.astype(np.uint32), offs
 
 
 def cigar_string(words):

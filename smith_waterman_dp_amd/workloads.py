@@ -459,6 +459,35 @@ def chromosome_seed_stage(length=20_000_000, sub_rate=0.12, indel_rate=0.01, p_g
             "flank": flank}
 
 
+def homolog_rounds(length=40_000, sub_rate=0.12, indel_rate=0.01, p_geom=0.3, block=6000, gap=2000, flank=3000,
+                   min_tb=3000, seed=0):
+    """Input for covered-seed suppression: a homologous pair (C2 = mut(C1),
+    12% substitutions 2:1, 1% indels of Geom(0.3)) in which every `block`
+    bases of C2 end with `gap` unrelated ones, so that it holds several
+    alignments; seeds = the shared 19-mers after diagonal dedup (many seeds
+    per alignment: every indel starts a new diagonal), windows +-flank, in
+    a seeded random order."""
+    rng = np.random.default_rng(seed)
+    C1 = random_codes(rng, length)
+    C2 = mutate(rng, C1, sub_rate, indel_rate, p_geom)
+    for s0 in range(block - gap, C2.size, block):
+        C2[s0:s0 + gap] = random_codes(rng, min(gap, C2.size - s0))
+    t, q = shared_kmers(C1, C2)
+    seeds = _diagonal_dedup_seeds(t, q, C1.size, C2.size, flank)
+    seeds = seeds[rng.permutation(len(seeds))]
+    return _workload("homolog_rounds", C1, C2, seeds, min_tb=min_tb, n_seeds=len(seeds))
+
+
+def chromosome_rounds(length=20_000_000, seed=0, **kw):
+    """The chromosome pair's forward seeds (144,179 at full size) in a seeded
+    random order, for covered-seed suppression."""
+    w = chromosome(length=length, seed=seed, **kw)
+    rng = np.random.default_rng(1000 + seed)
+    w = dict(w, seeds=w["seeds"][rng.permutation(len(w["seeds"]))], min_tb=3000)
+    w["name"] = "chromosome_rounds"
+    return w
+
+
 def skewed_matrix(seed=0, **kw):
     """The skewed batch scored with the 4x4 matrix, with 400 runs of N of
     10..1000 bases planted in each sequence (about 2% of it) outside the
@@ -474,4 +503,5 @@ WORKLOADS = {
     "chromosome": chromosome,
     "chromosome_rc": chromosome_rc,
     "skewed_matrix": skewed_matrix,
+    "chromosome_rounds": chromosome_rounds,
 }

@@ -561,3 +561,88 @@ def test_n_needs_a_matrix():
     sc = dict(matrix=matrix_of(SC), n_score=-7, gap_open=SC["gap_open"], gap_extend=SC["gap_extend"])
     r = oracle.side("ACNT", "ACGT", sc, oracle.YDROP_INF)
     assert r["status"] == 0 and r["score"] == 3 * SC["match"] - 7 and (r["ie"], r["je"]) == (4, 4)
+
+
+# ---- covered-seed suppression by rounds --------------------------------
+
+def test_rounds_single_round_equals_run():
+    """With one round nothing is suppressed: the results are run()'s."""
+    w = W.homolog_rounds(length=12_000, seed=2)
+    n = len(w["seeds"])
+    a = oracle.run(w["target"], w["query"], w["seeds"], w["scoring"], w["ydrop"], min_tb=w["min_tb"])
+    b = oracle.extend_rounds(w["target"], w["query"], w["seeds"], w["scoring"], w["ydrop"], w["min_tb"], n)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_rounds_hand_example():
+    """Identical 400-base sequences: the seed at 50 aligns the whole main
+    diagonal, so the seed at 200 on it is covered when it comes in a later
+    round, not when both share a round.  A seed on another diagonal is
+    never covered by it."""
+    rng = random.Random(3)
+    T = rand_seq(rng, 400)
+    Q = T
+    seeds = np.array([[50, 50, 19, 0, 400, 0, 400],
+                      [200, 200, 19, 0, 400, 0, 400],
+                      [10, 300, 5, 0, 400, 0, 400]], dtype=np.int64)
+    h, w, o = oracle.extend_rounds(T, Q, seeds, SC, 9400, 0, 1)
+    assert h["n_runs"][0] > 0 and oracle.cigar_string(w[o[0]:o[0] + h["n_runs"][0]]) == "400M"
+    assert h["status"][1] == oracle.STATUS_COVERED and h["score"][1] == 0 and h["n_runs"][1] == 0
+    assert h["status"][2] == 0
+    h2, _, _ = oracle.extend_rounds(T, Q, seeds, SC, 9400, 0, 2)
+    assert h2["status"][1] == 0 and h2["score"][1] == h["score"][0]
+    # untraced alignments (score not above min_tb) cover nothing
+    h3, _, _ = oracle.extend_rounds(T, Q, seeds, SC, 9400, 10 ** 9, 1)
+    assert not (h3["status"] & oracle.STATUS_COVERED).any()
+
+
+def _cells_of(T, Q, hit, words):
+    """Every aligned (t, q) cell of one alignment, read from its text CIGAR
+    one column at a time."""
+    import re
+    t, q = int(hit["t_begin"]), int(hit["q_begin"])
+    cells = set()
+    for ln, op in re.findall(r"(\d+)([MID])", oracle.cigar_string(words)):
+        for _ in range(int(ln)):
+            if op == "M":
+                cells.add((t, q))
+                t += 1
+                q += 1
+            elif op == "I":
+                q += 1
+            else:
+                t += 1
+    assert (t, q) == (int(hit["t_end"]), int(hit["q_end"]))
+    return cells
+
+
+@pytest.mark.parametrize("round_size", [3, 10, 40])
+def test_rounds_coverage_by_cells(round_size):
+    """Coverage recomputed from explicit cell sets: a seed is covered exactly
+    when one of its columns is an aligned cell of an alignment traced in an
+    earlier round; every extended seed has run()'s result."""
+    w = W.homolog_rounds(length=16_000, seed=4)
+    S = w["seeds"]
+    h, words, offs = oracle.extend_rounds(w["target"], w["query"], S, w["scoring"], w["ydrop"], w["min_tb"],
+                                          round_size)
+    ref, rw, ro = oracle.run(w["target"], w["query"], S, w["scoring"], w["ydrop"], min_tb=w["min_tb"])
+    earlier = set()
+    n_cov = 0
+    for r0 in range(0, len(S), round_size):
+        this_round = set()
+        for k in range(r0, min(r0 + round_size, len(S))):
+            t, q, L = (int(x) for x in S[k, :3])
+            cov = any((t + i, q + i) in earlier for i in range(L))
+            assert bool(h["status"][k] & oracle.STATUS_COVERED) == cov, k
+            if cov:
+                n_cov += 1
+                assert h["score"][k] == 0 and h["n_runs"][k] == 0
+                continue
+            assert h[k] == ref[k]
+            got = words[offs[k]:offs[k] + h["n_runs"][k]]
+            assert np.array_equal(got, rw[ro[k]:ro[k] + ref["n_runs"][k]])
+            if h["n_runs"][k]:
+                this_round |= _cells_of(w["target"], w["query"], h[k], got)
+        earlier |= this_round
+    assert 0 < n_cov < len(S)
