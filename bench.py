@@ -14,6 +14,8 @@ Workloads (seeded, synthetic; see smith_waterman_dp_amd/workloads.py):
   tiny, executor_heavy, chromosome
   chromosome_rc   the chromosome pair searched on the query's reverse strand
   skewed_matrix   the skewed batch scored with a 4x4 matrix, runs of N planted
+  chromosome_rounds  the chromosome pair's seeds in random order through
+                  fz_extend_rounds (covered-seed suppression, --round-size)
   seeds           the seed stage (fz_find_seeds) on the 20 Mbp chromosome pair,
                   both strands per step; reported in Mbp/s of target + query
 """
@@ -83,7 +85,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="skewed",
                     choices=["skewed", "local", "tiny", "executor_heavy", "chromosome", "chromosome_rc",
-                             "skewed_matrix", "seeds"])
+                             "skewed_matrix", "chromosome_rounds", "seeds"])
+    ap.add_argument("--round-size", type=int, default=16384,
+                    help="chromosome_rounds: seeds per round of covered-seed suppression")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -269,10 +273,15 @@ def main():
     min_tb = w.get("min_tb")
     min_tb = -(1 << 62) if min_tb is None else min_tb
 
+    rounds = a.workload == "chromosome_rounds"
+
     def step():
         rc = bool(w.get("query_rc"))
         if local:
             return ctx.local(T, Q, S, w["scoring"], want_stats=True, query_rc=rc)
+        if rounds:
+            return ctx.extend_rounds(T, Q, S, w["scoring"], w["ydrop"], min_tb, a.round_size, want_stats=True,
+                                     query_rc=rc)
         return ctx.extend(T, Q, S, w["scoring"], w["ydrop"], min_tb, traceback=w.get("traceback", True),
                           want_stats=True, query_rc=rc)
 
@@ -289,6 +298,13 @@ def main():
         main_ms.append(st["ms_main"])
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    plain_ms = None
+    if rounds:
+        # the same seeds as one ordinary batch, for comparison (not timed above)
+        t1 = time.perf_counter()
+        ctx.extend(T, Q, S, w["scoring"], w["ydrop"], min_tb)
+        torch.cuda.synchronize()
+        plain_ms = (time.perf_counter() - t1) * 1e3
     copy_probe(a.copy_probe, dev)
     h = hits.cpu().numpy()
     cells = int(h[:, 8].sum())
@@ -315,6 +331,12 @@ def main():
         cfg["executor_batches"] = int(st["n_batches"])
         cfg["phase_ms"] = {k[3:]: round(float(st[k]), 1) for k in
                            ("ms_pack", "ms_inspect", "ms_bin", "ms_exec", "ms_gather")}
+    if rounds:
+        from smith_waterman_dp_amd import fz as _fz
+        cfg["round_size"] = a.round_size
+        cfg["rounds"] = -(-n // a.round_size)
+        cfg["covered_seeds"] = int(((h[:, 1] & _fz.FZ_HIT_COVERED) != 0).sum())
+        cfg["plain_batch_ms"] = round(plain_ms, 1)
     out = {"metric": METRIC if a.workload == "skewed" else "GCUPS on the %s batch, 1 MI355X" % a.workload,
            "value": round(gcups, 3), "unit": "GCUPS", "n_gpus": 1, "steps": steps, "warmup": a.warmup,
            "ms_per_step": round(ms_per_step, 3), "higher_is_better": True, "scaling": "weak",

@@ -161,7 +161,8 @@ enum {
     FZ_HIT_BELOW_MIN = 8,          /* score <= min_traceback_score: no CIGAR by request */
     FZ_HIT_EBAND = 16,             /* a side's band outgrew the widest kernel: result invalid */
     FZ_HIT_ESEED = 32,             /* seed outside its window or window outside the sequences */
-    FZ_HIT_ERANGE = 64             /* window too long for int32 scores with these parameters */
+    FZ_HIT_ERANGE = 64,            /* window too long for int32 scores with these parameters */
+    FZ_HIT_COVERED = 128           /* fz_extend_rounds: seed on an earlier round's alignment, not extended */
 };
 
 #define FZ_YDROP_INF 2147483647    /* ydrop >= this: no pruning */
@@ -217,6 +218,39 @@ int fz_extend_batch(fz_ctx *ctx,
                     int64_t min_traceback_score, uint32_t flags,
                     fz_hit *hits, const uint32_t **cigar, uint64_t *cigar_words,
                     fz_stats *stats, void *stream);
+
+/*
+ * Covered-seed suppression by rounds.  FastZ (SC'21) section 2.1 describes
+ * LASTZ ending a seed extension that reaches an alignment found earlier;
+ * section 3.4 explains why FastZ drops that rule (it orders the
+ * extensions).  This call applies it between rounds and keeps each round a
+ * data-parallel batch: seeds are taken in the given order in rounds of
+ * round_size; a seed of round r whose exact-match columns (t_pos + k,
+ * q_pos + k), k < seed_len, share a cell with an aligned (M) column of an
+ * alignment traced in an earlier round is not extended (its record is all
+ * zero but status = FZ_HIT_COVERED and bin = -1); every other seed of the
+ * round is extended exactly as fz_extend_batch extends it.  Seeds of one
+ * round never suppress each other, and alignments without a CIGAR (score
+ * not above min_traceback_score) suppress nothing.  A seed without columns,
+ * or with columns outside the sequences, is never covered.
+ *   arguments       as fz_extend_batch; flags must hold FZ_TRACEBACK and
+ *                   not FZ_LOCAL; sequences shorter than 2^31 bases
+ *   round_size      >= 1 seeds per round (>= n_seeds: one round, the same
+ *                   results as fz_extend_batch)
+ *   cigar, cigar_words   the words of all rounds, in seed order within a
+ *                   round and round after round; hits' cigar_off index them
+ *   stats           sums over the rounds
+ * The context keeps the aligned segments of the call (16 bytes per M run)
+ * until the next call.  Returns FZ_OK or a negative FZ_E* code.
+ */
+int fz_extend_rounds(fz_ctx *ctx,
+                     const uint8_t *target, uint64_t target_len,
+                     const uint8_t *query, uint64_t query_len,
+                     const fz_seed *seeds, uint64_t n_seeds,
+                     const fz_scoring *scoring, const fz_matrix *matrix, int32_t ydrop,
+                     int64_t min_traceback_score, uint32_t flags, uint64_t round_size,
+                     fz_hit *hits, const uint32_t **cigar, uint64_t *cigar_words,
+                     fz_stats *stats, void *stream);
 
 /*
  * Seed stage (FastZ, SC'21, section 2: whole-genome alignment first finds

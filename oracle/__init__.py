@@ -286,7 +286,8 @@ def extend_rounds(target, query, seeds, scoring, ydrop, min_tb, round_size, thre
     seeds are taken in the given order in rounds of `round_size`; a seed of
     round r whose exact-match columns (t_pos + k, q_pos + k), k < seed_len,
     share a cell with the aligned (M) columns of an alignment traced (given
-    a CIGAR) in rounds before r is not extended and gets status
+    a CIGAR) in rounds before r (a seed without columns, or with columns
+    outside the sequences, shares none) is not extended and gets status
     STATUS_COVERED with every other field zero; every other seed of round r
     is extended on its own, as run() extends it.  Seeds of one round never
     suppress each other.
@@ -296,6 +297,7 @@ def extend_rounds(target, query, seeds, scoring, ydrop, min_tb, round_size, thre
     """
     S = seeds_array(seeds)
     n = S.shape[0]
+    T_len, Q_len = _as_bytes(target).size, _as_bytes(query).size
     if round_size < 1:
         raise ValueError("round_size must be >= 1")
     hits = np.zeros(n, dtype=HIT_DTYPE)
@@ -306,7 +308,8 @@ def extend_rounds(target, query, seeds, scoring, ydrop, min_tb, round_size, thre
         keep = []
         for k in idx:
             t, q, L = int(S[k, 0]), int(S[k, 1]), int(S[k, 2])
-            covered = any(a < t + L and b > t for a, b in by_diag.get(t - q, ()))
+            inside = L >= 1 and t >= 0 and q >= 0 and t + L <= T_len and q + L <= Q_len
+            covered = inside and any(a < t + L and b > t for a, b in by_diag.get(t - q, ()))
             if covered:
                 hits["status"][k] = STATUS_COVERED
             else:

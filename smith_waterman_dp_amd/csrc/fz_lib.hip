@@ -32,6 +32,7 @@
 #include "fz_extend.hpp"
 #include "fz_local.hpp"
 #include "fz_seeds.hpp"
+#include "fz_rounds.hpp"
 
 using namespace fz;
 
@@ -86,6 +87,11 @@ struct fz_ctx {
     // ranks, library scratch, and the seeds of the last fz_find_seeds
     DevBuf sk_tk, sk_tk2, sk_tp, sk_tp2, sk_bend, sk_boff, sk_lo, sk_cnt, sk_off, sk_hit, sk_hit2, sk_flag, sk_rank, sk_tmp, sk_out;
     uint64_t last_seeds = 0;
+    // covered-seed rounds: round flags, scan, packed seeds and results, CIGAR
+    // words of all rounds, aligned segments (keys and ends, two of each for
+    // the sort), running maxima, library scratch
+    DevBuf rd_keep, rd_pos, rd_seeds, rd_hits, rd_cnt, rd_off, rd_cig, sg_key, sg_key2, sg_end, sg_end2, sg_v, sg_max,
+        rd_tmp;
     // the target index held in sk_tk2 / sk_tp2 / sk_boff (FZ_SEEDS_REUSE_INDEX)
     bool idx_valid = false;
     const uint8_t *idx_target = nullptr;
@@ -572,7 +578,9 @@ void fz_destroy(fz_ctx *ctx)
                       &ctx->counters, &ctx->ovl0, &ctx->ovl1, &ctx->bnd,
                       &ctx->sk_tk, &ctx->sk_tk2, &ctx->sk_tp, &ctx->sk_tp2, &ctx->sk_bend, &ctx->sk_boff, &ctx->sk_lo, &ctx->sk_cnt,
                       &ctx->sk_off, &ctx->sk_hit, &ctx->sk_hit2, &ctx->sk_flag, &ctx->sk_rank, &ctx->sk_tmp,
-                      &ctx->sk_out};
+                      &ctx->sk_out, &ctx->rd_keep, &ctx->rd_pos, &ctx->rd_seeds, &ctx->rd_hits, &ctx->rd_cnt,
+                      &ctx->rd_off, &ctx->rd_cig, &ctx->sg_key, &ctx->sg_key2, &ctx->sg_end, &ctx->sg_end2,
+                      &ctx->sg_v, &ctx->sg_max, &ctx->rd_tmp};
     for (auto &x : ctx->xs)
         if (x) (void)hipStreamSynchronize(x);
     for (DevBuf *b : bufs)
@@ -899,6 +907,198 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         *stats = S;
     }
     return FZ_OK;
+}
+
+// Grow b to at least `bytes`, keeping its first `keep` bytes.
+static int grow_keep(fz_ctx *ctx, DevBuf &b, size_t bytes, size_t keep, hipStream_t st)
+{
+    if (b.cap >= bytes) return FZ_OK;
+    DevBuf nb;
+    int rc = ensure(ctx, nb, bytes);
+    if (rc) return rc;
+    if (keep && b.p) {
+        HIP_OK(hipMemcpyAsync(nb.p, b.p, keep, hipMemcpyDeviceToDevice, st));
+        HIP_OK(hipStreamSynchronize(st));
+    }
+    if (b.p) (void)hipFree(b.p);
+    b = nb;
+    return FZ_OK;
+}
+
+static int rounds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const uint8_t *query, uint64_t qlen,
+                       const fz_seed *seeds, uint64_t n_seeds, const fz_scoring *scoring, const fz_matrix *matrix,
+                       int32_t ydrop, int64_t min_tb, uint32_t flags, uint64_t round_size, fz_hit *hits,
+                       const uint32_t **cigar, uint64_t *cigar_words, fz_stats *stats, hipStream_t st)
+{
+    if (cigar) *cigar = nullptr;
+    if (cigar_words) *cigar_words = 0;
+    int rc = check_args(ctx, target, tlen, query, qlen, seeds, n_seeds, scoring, matrix, ydrop, flags, hits);
+    if (rc != FZ_OK) return rc;
+    if (!(flags & FZ_TRACEBACK) || (flags & FZ_LOCAL))
+        return fail(ctx, FZ_EINVAL, "fz_extend_rounds needs FZ_TRACEBACK and no FZ_LOCAL");
+    if (round_size < 1) return fail(ctx, FZ_EINVAL, "round_size must be >= 1");
+    if (tlen >= (1ull << 31) || qlen >= (1ull << 31))
+        return fail(ctx, FZ_EINVAL, "sequences must be shorter than 2^31 bases for fz_extend_rounds");
+    fz_stats tot;
+    memset(&tot, 0, sizeof tot);
+    const int64_t n = (int64_t)n_seeds;
+    const int64_t B = (int64_t)std::min<uint64_t>(round_size, std::max<uint64_t>(n_seeds, 1));
+    if (n > 0) {
+        ENSURE(ctx->rd_keep, B * sizeof(uint32_t));
+        ENSURE(ctx->rd_pos, B * sizeof(uint32_t));
+        ENSURE(ctx->rd_seeds, B * sizeof(fz_seed));
+        ENSURE(ctx->rd_hits, B * sizeof(fz_hit));
+        ENSURE(ctx->rd_cnt, B * sizeof(uint64_t));
+        ENSURE(ctx->rd_off, B * sizeof(uint64_t));
+    }
+    int64_t acc_words = 0, nseg = 0;
+    for (int64_t r0 = 0; r0 < n; r0 += B) {
+        const int64_t nb = std::min<int64_t>(B, n - r0);
+        const fz_seed *rs = seeds + r0;
+        uint32_t *keep = as<uint32_t>(ctx->rd_keep), *pos = as<uint32_t>(ctx->rd_pos);
+        // which seeds of the round an earlier round covers
+        cover_kernel<<<blocks_for(nb, 256), 256, 0, st>>>(rs, nb, (int64_t)tlen, (int64_t)qlen,
+                                                          as<uint64_t>(ctx->sg_key), as<uint64_t>(ctx->sg_max),
+                                                          nseg, keep);
+        HIP_OK(hipGetLastError());
+        size_t tb = 0;
+        HIP_OK(hipcub::DeviceScan::ExclusiveSum(nullptr, tb, keep, pos, (int)nb, st));
+        ENSURE(ctx->rd_tmp, tb);
+        tb = ctx->rd_tmp.cap;
+        HIP_OK(hipcub::DeviceScan::ExclusiveSum(ctx->rd_tmp.p, tb, keep, pos, (int)nb, st));
+        uint32_t lastv[2] = {0, 0};
+        HIP_OK(hipMemcpyAsync(&lastv[0], pos + (nb - 1), sizeof(uint32_t), hipMemcpyDeviceToHost, st));
+        HIP_OK(hipMemcpyAsync(&lastv[1], keep + (nb - 1), sizeof(uint32_t), hipMemcpyDeviceToHost, st));
+        HIP_OK(hipStreamSynchronize(st));
+        const int64_t nkeep = (int64_t)lastv[0] + lastv[1];
+        compact_seeds_kernel<<<blocks_for(nb, 256), 256, 0, st>>>(rs, nb, keep, pos, as<fz_seed>(ctx->rd_seeds));
+        HIP_OK(hipGetLastError());
+        // the round: one ordinary batch
+        uint64_t words = 0;
+        if (nkeep > 0) {
+            fz_stats rsst;
+            rc = extend_impl(ctx, target, tlen, query, qlen, as<fz_seed>(ctx->rd_seeds), (uint64_t)nkeep, scoring,
+                             matrix, ydrop, min_tb, flags, as<fz_hit>(ctx->rd_hits), nullptr, &words,
+                             stats ? &rsst : nullptr, st);
+            if (rc) return rc;
+            if (stats) {
+                tot.cells += rsst.cells;
+                tot.executor_cells += rsst.executor_cells;
+                tot.pointer_bytes += rsst.pointer_bytes;
+                tot.n_sides += rsst.n_sides;
+                tot.n_eager += rsst.n_eager;
+                tot.n_executor += rsst.n_executor;
+                tot.n_overflow += rsst.n_overflow;
+                for (int b = 0; b < NBINS; ++b) tot.bin_hist[b] += rsst.bin_hist[b];
+                tot.n_batches += rsst.n_batches;
+                tot.ms_pack += rsst.ms_pack;
+                tot.ms_inspect += rsst.ms_inspect;
+                tot.ms_bin += rsst.ms_bin;
+                tot.ms_exec += rsst.ms_exec;
+                tot.ms_walk += rsst.ms_walk;
+                tot.ms_gather += rsst.ms_gather;
+                tot.ms_main += rsst.ms_main;
+            }
+            rc = grow_keep(ctx, ctx->rd_cig, (size_t)(acc_words + (int64_t)words + 1) * sizeof(uint32_t),
+                           (size_t)acc_words * sizeof(uint32_t), st);
+            if (rc) return rc;
+            if (words)
+                HIP_OK(hipMemcpyAsync(as<uint32_t>(ctx->rd_cig) + acc_words, ctx->cigar.p, words * sizeof(uint32_t),
+                                      hipMemcpyDeviceToDevice, st));
+        }
+        scatter_hits_kernel<<<blocks_for(nb, 256), 256, 0, st>>>(as<fz_hit>(ctx->rd_hits), nb, keep, pos, acc_words,
+                                                                 hits + r0);
+        HIP_OK(hipGetLastError());
+        acc_words += (int64_t)words;
+        if (nkeep == 0 || r0 + nb >= n) continue;     // nothing new, or no later round to cover
+        // this round's aligned segments, added to the sorted set
+        seg_count_kernel<<<blocks_for(nkeep, 256), 256, 0, st>>>(as<fz_hit>(ctx->rd_hits), nkeep,
+                                                                 as<uint32_t>(ctx->cigar), as<uint64_t>(ctx->rd_cnt));
+        HIP_OK(hipGetLastError());
+        tb = 0;
+        HIP_OK(hipcub::DeviceScan::ExclusiveSum(nullptr, tb, as<uint64_t>(ctx->rd_cnt), as<uint64_t>(ctx->rd_off),
+                                                (int)nkeep, st));
+        ENSURE(ctx->rd_tmp, tb);
+        tb = ctx->rd_tmp.cap;
+        HIP_OK(hipcub::DeviceScan::ExclusiveSum(ctx->rd_tmp.p, tb, as<uint64_t>(ctx->rd_cnt),
+                                                as<uint64_t>(ctx->rd_off), (int)nkeep, st));
+        uint64_t lastm[2] = {0, 0};
+        HIP_OK(hipMemcpyAsync(&lastm[0], as<uint64_t>(ctx->rd_off) + (nkeep - 1), sizeof(uint64_t),
+                              hipMemcpyDeviceToHost, st));
+        HIP_OK(hipMemcpyAsync(&lastm[1], as<uint64_t>(ctx->rd_cnt) + (nkeep - 1), sizeof(uint64_t),
+                              hipMemcpyDeviceToHost, st));
+        HIP_OK(hipStreamSynchronize(st));
+        const int64_t m = (int64_t)(lastm[0] + lastm[1]);
+        if (m == 0) continue;
+        if (nseg + m >= (1ll << 31)) return fail(ctx, FZ_ENOMEM, "more than 2^31 aligned segments");
+        const int64_t ns = nseg + m;
+        rc = grow_keep(ctx, ctx->sg_key, ns * sizeof(uint64_t), nseg * sizeof(uint64_t), st);
+        if (rc) return rc;
+        rc = grow_keep(ctx, ctx->sg_end, ns * sizeof(uint32_t), nseg * sizeof(uint32_t), st);
+        if (rc) return rc;
+        ENSURE(ctx->sg_key2, ns * sizeof(uint64_t));
+        ENSURE(ctx->sg_end2, ns * sizeof(uint32_t));
+        ENSURE(ctx->sg_v, ns * sizeof(uint64_t));
+        ENSURE(ctx->sg_max, ns * sizeof(uint64_t));
+        seg_emit_kernel<<<blocks_for(nkeep, 256), 256, 0, st>>>(as<fz_hit>(ctx->rd_hits), nkeep,
+                                                                as<uint32_t>(ctx->cigar), as<uint64_t>(ctx->rd_off),
+                                                                (int64_t)qlen, as<uint64_t>(ctx->sg_key) + nseg,
+                                                                as<uint32_t>(ctx->sg_end) + nseg);
+        HIP_OK(hipGetLastError());
+        size_t ts = 0, tm2 = 0;
+        HIP_OK(hipcub::DeviceRadixSort::SortPairs(nullptr, ts, as<uint64_t>(ctx->sg_key), as<uint64_t>(ctx->sg_key2),
+                                                  as<uint32_t>(ctx->sg_end), as<uint32_t>(ctx->sg_end2), (int)ns, 0, 64,
+                                                  st));
+        HIP_OK(hipcub::DeviceScan::InclusiveScan(nullptr, tm2, as<uint64_t>(ctx->sg_v), as<uint64_t>(ctx->sg_max),
+                                                 hipcub::Max(), (int)ns, st));
+        ENSURE(ctx->rd_tmp, std::max(ts, tm2));
+        ts = ctx->rd_tmp.cap;
+        HIP_OK(hipcub::DeviceRadixSort::SortPairs(ctx->rd_tmp.p, ts, as<uint64_t>(ctx->sg_key),
+                                                  as<uint64_t>(ctx->sg_key2), as<uint32_t>(ctx->sg_end),
+                                                  as<uint32_t>(ctx->sg_end2), (int)ns, 0, 64, st));
+        std::swap(ctx->sg_key, ctx->sg_key2);
+        std::swap(ctx->sg_end, ctx->sg_end2);
+        seg_diag_end_kernel<<<blocks_for(ns, 256), 256, 0, st>>>(as<uint64_t>(ctx->sg_key), as<uint32_t>(ctx->sg_end),
+                                                                 ns, as<uint64_t>(ctx->sg_v));
+        HIP_OK(hipGetLastError());
+        tm2 = ctx->rd_tmp.cap;
+        HIP_OK(hipcub::DeviceScan::InclusiveScan(ctx->rd_tmp.p, tm2, as<uint64_t>(ctx->sg_v),
+                                                 as<uint64_t>(ctx->sg_max), hipcub::Max(), (int)ns, st));
+        nseg = ns;
+    }
+    HIP_OK(hipStreamSynchronize(st));
+    // the words of every round become the context's CIGAR buffer
+    std::swap(ctx->cigar, ctx->rd_cig);
+    ctx->last_words = (uint64_t)acc_words;
+    if (cigar) *cigar = as<uint32_t>(ctx->cigar);
+    if (cigar_words) *cigar_words = (uint64_t)acc_words;
+    if (stats) *stats = tot;
+    return FZ_OK;
+}
+
+int fz_extend_rounds(fz_ctx *ctx, const uint8_t *target, uint64_t target_len, const uint8_t *query,
+                     uint64_t query_len, const fz_seed *seeds, uint64_t n_seeds, const fz_scoring *scoring,
+                     const fz_matrix *matrix, int32_t ydrop, int64_t min_traceback_score, uint32_t flags,
+                     uint64_t round_size, fz_hit *hits, const uint32_t **cigar, uint64_t *cigar_words,
+                     fz_stats *stats, void *stream)
+{
+    if (!ctx) return FZ_EINVAL;
+    ctx->err.clear();
+    ctx->last_words = 0;
+    int prev = 0;
+    if (hipGetDevice(&prev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ctx, FZ_EDEVICE, "hipGetDevice failed");
+    }
+    if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ctx, FZ_EDEVICE, "hipSetDevice(%d) failed", ctx->device);
+    }
+    const int rc = rounds_impl(ctx, target, target_len, query, query_len, seeds, n_seeds, scoring, matrix, ydrop,
+                               min_traceback_score, flags, round_size, hits, cigar, cigar_words, stats,
+                               (hipStream_t)stream);
+    if (prev != ctx->device) (void)hipSetDevice(prev);
+    return rc;
 }
 
 int fz_extend_batch(fz_ctx *ctx, const uint8_t *target, uint64_t target_len, const uint8_t *query, uint64_t query_len,

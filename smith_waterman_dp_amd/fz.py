@@ -15,6 +15,7 @@ FZ_TRACEBACK, FZ_LOCAL, FZ_STATS, FZ_QUERY_RC, FZ_SEEDS_ALL, FZ_SEEDS_REUSE_INDE
 FZ_OK, FZ_EINVAL, FZ_ENOMEM, FZ_EDEVICE, FZ_EBAND = 0, -1, -2, -3, -4
 FZ_HIT_TRACED, FZ_HIT_EAGER_LEFT, FZ_HIT_EAGER_RIGHT = 1, 2, 4
 FZ_HIT_BELOW_MIN, FZ_HIT_EBAND, FZ_HIT_ESEED, FZ_HIT_ERANGE = 8, 16, 32, 64
+FZ_HIT_COVERED = 128
 FZ_YDROP_INF = 2147483647
 
 HIT_FIELDS = ["score", "status", "t_begin", "t_end", "q_begin", "q_end", "cigar_off", "cigar_len",
@@ -23,7 +24,7 @@ SEED_FIELDS = ["t_pos", "q_pos", "seed_len", "t_lo", "t_hi", "q_lo", "q_hi"]
 
 # every symbol include/fz.h declares
 EXPORTS = ["fz_create", "fz_destroy", "fz_last_error", "fz_set_pointer_workspace", "fz_extend_batch",
-           "fz_find_seeds", "fz_copy_seeds", "fz_copy_cigar"]
+           "fz_extend_rounds", "fz_find_seeds", "fz_copy_seeds", "fz_copy_cigar"]
 
 
 class fz_scoring(ctypes.Structure):
@@ -103,6 +104,10 @@ def load_library(path=LIB_PATH):
                                     i32, i64,
                                     ctypes.c_uint32, P, ctypes.POINTER(P), ctypes.POINTER(u64),
                                     ctypes.POINTER(fz_stats), P]
+    lib.fz_extend_rounds.restype = ctypes.c_int
+    lib.fz_extend_rounds.argtypes = [P, P, u64, P, u64, P, u64, ctypes.POINTER(fz_scoring), ctypes.POINTER(fz_matrix),
+                                     i32, i64, ctypes.c_uint32, u64, P, ctypes.POINTER(P), ctypes.POINTER(u64),
+                                     ctypes.POINTER(fz_stats), P]
     lib.fz_copy_cigar.restype = ctypes.c_int
     lib.fz_copy_cigar.argtypes = [P, P, u64, P]
     lib.fz_find_seeds.restype = ctypes.c_int
@@ -149,7 +154,7 @@ def _stream_handle(stream):
 
 
 def fz_extend_batch(ctx, target, query, seeds, scoring, ydrop, min_traceback_score=-(1 << 62),
-                    flags=FZ_TRACEBACK, stream=None, want_stats=False):
+                    flags=FZ_TRACEBACK, stream=None, want_stats=False, round_size=None):
     """Run one batch.
 
     target, query: uint8 CUDA tensors of ASCII bases.  seeds: int64 CUDA
@@ -159,7 +164,9 @@ def fz_extend_batch(ctx, target, query, seeds, scoring, ydrop, min_traceback_sco
     also lets the sequences hold N.
     Returns (hits, cigar, stats): hits an int64 (n, 12) CUDA tensor in
     HIT_FIELDS order, cigar an int32 CUDA tensor of BAM-style words
-    (len << 4 | op), stats a dict or None.
+    (len << 4 | op), stats a dict or None.  With round_size, the call is
+    fz_extend_rounds (covered-seed suppression between rounds of that many
+    seeds; FZ_TRACEBACK required).
     """
     import torch
     lib = load_library()
@@ -179,12 +186,14 @@ def fz_extend_batch(ctx, target, query, seeds, scoring, ydrop, min_traceback_sco
     if want_stats:
         flags |= FZ_STATS
     strm = _stream_handle(stream)
-    rc = lib.fz_extend_batch(ctx, target.data_ptr(), target.numel(), query.data_ptr(), query.numel(),
-                             seeds.data_ptr(), n, ctypes.byref(sc), ctypes.byref(mx) if mx is not None else None,
-                             int(min(int(ydrop), FZ_YDROP_INF)),
-                             int(min_traceback_score), int(flags), hits.data_ptr() if n else None,
-                             ctypes.byref(cig_ptr), ctypes.byref(words),
-                             ctypes.byref(st), strm)
+    common = (ctx, target.data_ptr(), target.numel(), query.data_ptr(), query.numel(), seeds.data_ptr(), n,
+              ctypes.byref(sc), ctypes.byref(mx) if mx is not None else None, int(min(int(ydrop), FZ_YDROP_INF)),
+              int(min_traceback_score), int(flags))
+    tail = (hits.data_ptr() if n else None, ctypes.byref(cig_ptr), ctypes.byref(words), ctypes.byref(st), strm)
+    if round_size is None:
+        rc = lib.fz_extend_batch(*common, *tail)
+    else:
+        rc = lib.fz_extend_rounds(*common, int(round_size), *tail)
     _check(ctx, rc)
     cigar = torch.empty(max(words.value, 0), dtype=torch.int32, device=seeds.device)
     if words.value:
@@ -252,6 +261,15 @@ class Context:
         flags = (FZ_TRACEBACK if traceback else 0) | (FZ_QUERY_RC if query_rc else 0)
         return fz_extend_batch(self.h, target, query, seeds, scoring, ydrop, min_traceback_score, flags,
                                stream, want_stats)
+
+    def extend_rounds(self, target, query, seeds, scoring, ydrop, min_traceback_score, round_size, stream=None,
+                      want_stats=False, query_rc=False):
+        """Covered-seed suppression (fz_extend_rounds): rounds of round_size
+        seeds; a seed on an alignment traced in an earlier round is not
+        extended (status FZ_HIT_COVERED)."""
+        flags = FZ_TRACEBACK | (FZ_QUERY_RC if query_rc else 0)
+        return fz_extend_batch(self.h, target, query, seeds, scoring, ydrop, min_traceback_score, flags,
+                               stream, want_stats, round_size=round_size)
 
     def find_seeds(self, target, query, k=19, flank=32768, dedup=True, query_rc=False, stream=None,
                    want_stats=False, reuse_index=False):

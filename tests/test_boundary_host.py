@@ -42,6 +42,8 @@ def test_null_context_is_rejected():
     assert rc == fz.FZ_EINVAL
     assert lib.fz_set_pointer_workspace(None, 0) == fz.FZ_EINVAL
     assert lib.fz_copy_cigar(None, None, 0, None) == fz.FZ_EINVAL
+    assert lib.fz_extend_rounds(None, None, 0, None, 0, None, 0, ctypes.byref(sc), None, 9400, 0,
+                                fz.FZ_TRACEBACK, 16, None, None, None, None, None) == fz.FZ_EINVAL
     n = ctypes.c_uint64(7)
     assert lib.fz_find_seeds(None, None, 0, None, 0, 19, 0, 0, None, ctypes.byref(n), None, None, None) == fz.FZ_EINVAL
     assert lib.fz_copy_seeds(None, None, 0, None) == fz.FZ_EINVAL
