@@ -86,7 +86,7 @@ def parse():
     ap.add_argument("--workload", default="skewed",
                     choices=["skewed", "local", "tiny", "executor_heavy", "chromosome", "chromosome_rc",
                              "skewed_matrix", "chromosome_rounds", "seeds"])
-    ap.add_argument("--round-size", type=int, default=16384,
+    ap.add_argument("--round-size", type=int, default=4096,
                     help="chromosome_rounds: seeds per round of covered-seed suppression")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     ap.add_argument("--no-cpu", action="store_true")
