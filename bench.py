@@ -18,6 +18,9 @@ Workloads (seeded, synthetic; see smith_waterman_dp_amd/workloads.py):
                   fz_extend_rounds (covered-seed suppression, --round-size)
   seeds           the seed stage (fz_find_seeds) on the 20 Mbp chromosome pair,
                   both strands per step; reported in Mbp/s of target + query
+  pipeline        the whole chain on the 20 Mbp chromosome pair: per strand,
+                  the seed stage, then the seeds in a seeded random order
+                  through fz_extend_rounds; Mbp/s of target + query
 """
 import argparse
 import json
@@ -85,7 +88,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="skewed",
                     choices=["skewed", "local", "tiny", "executor_heavy", "chromosome", "chromosome_rc",
-                             "skewed_matrix", "chromosome_rounds", "seeds"])
+                             "skewed_matrix", "chromosome_rounds", "seeds", "pipeline"])
     ap.add_argument("--round-size", type=int, default=4096,
                     help="chromosome_rounds: seeds per round of covered-seed suppression")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
@@ -246,6 +249,103 @@ def bench_seeds(a):
     print(json.dumps(out), flush=True)
 
 
+def cpu_pipeline_baseline(w, target_seconds, round_size):
+    """The oracle's seed stage and rounds, as they stand, on growing prefixes
+    of the pair (both strands), until one run passes half the target time."""
+    import numpy as np
+
+    import oracle
+    threads = os.cpu_count() or 1
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    L = 1 << 12
+    full = min(w["target"].size, w["query"].size)
+    while True:
+        L = min(L, full)
+        T, Q = w["target"][:L], w["query"][:L]
+        t0 = time.time()
+        for rc in (False, True):
+            s, _ = oracle.find_seeds(T, Q, w["k"], w["flank"], query_rc=rc)
+            s = s[np.random.default_rng(7).permutation(len(s))]
+            oracle.extend_rounds(T, oracle.revcomp(Q) if rc else Q, s, w["scoring"], w["ydrop"], 3000, round_size,
+                                 threads=threads)
+        dt = time.time() - t0
+        if dt > target_seconds / 2 or L == full:
+            break
+        L *= 2
+    return {"value": round(2 * L / dt / 1e6, 4), "unit": "Mbp/s", "cores": threads, "kind": "oracle",
+            "sample": "first %d bases of target and query, both strands, %.1f s" % (L, dt)}
+
+
+def bench_pipeline(a):
+    import numpy as np
+    import torch
+
+    from smith_waterman_dp_amd import fz
+    from smith_waterman_dp_amd import workloads as W
+
+    steps = a.steps if a.steps is not None else 3
+    print("[bench] generating the 20 Mbp chromosome pair", file=sys.stderr, flush=True)
+    w = dict(W.chromosome_seed_stage(), scoring=dict(W.DEFAULT_SCORING), ydrop=W.DEFAULT_YDROP)
+    dev = torch.device("cuda:0")
+    T = torch.from_numpy(w["target"]).to(dev)
+    Q = torch.from_numpy(w["query"]).to(dev)
+    ctx = fz.Context(0)
+
+    def step():
+        out = []
+        for rc in (False, True):
+            seeds, _ = ctx.find_seeds(T, Q, w["k"], w["flank"], query_rc=rc, reuse_index=rc)
+            perm = torch.randperm(seeds.shape[0], generator=torch.Generator().manual_seed(7)).to(dev)
+            h, c, st = ctx.extend_rounds(T, Q, seeds[perm], w["scoring"], w["ydrop"], 3000, a.round_size,
+                                         want_stats=True, query_rc=rc)
+            out.append((seeds.shape[0], h, st))
+        return out
+
+    for k in range(a.warmup):
+        step()
+        print("[bench] warmup %d done" % k, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    res, main_ms = None, []
+    for k in range(steps):
+        res = step()
+        main_ms.append(sum(st["ms_main"] for _, _, st in res))
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_per_step = dt / steps * 1e3
+    cells = 0
+    per_strand = []
+    for n, h, st in res:
+        hh = h.cpu().numpy()
+        cells += int(hh[:, 8].sum())
+        per_strand.append({"seeds": int(n), "covered": int(((hh[:, 1] & fz.FZ_HIT_COVERED) != 0).sum()),
+                           "traced": int(((hh[:, 1] & fz.FZ_HIT_TRACED) != 0).sum())})
+    kern_s = float(np.mean(main_ms)) / 1e3
+    achieved = OPS_PER_CELL["extend"] * cells / kern_s / 1e12
+    peak = VALU_PEAK_OPS / 1e12
+    bases = int(w["target"].size + w["query"].size)
+    out = {"metric": "whole-pair alignment (seed stage + covered-seed rounds, both strands) on a 20 Mbp "
+                     "chromosome pair, 1 MI355X",
+           "value": round(bases / (ms_per_step / 1e3) / 1e6, 3), "unit": "Mbp/s", "n_gpus": 1, "steps": steps,
+           "warmup": a.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+           "config": {"workload": "chromosome_pipeline", "target_bp": int(w["target"].size),
+                      "query_bp": int(w["query"].size), "k": w["k"], "flank": w["flank"], "round_size": a.round_size,
+                      "min_traceback_score": 3000, "cells_per_step": cells, "strands": per_strand,
+                      "inspector_ms": round(kern_s * 1e3, 3)},
+           "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(peak, 3), "unit": "TOP/s",
+                        "frac": round(achieved / peak, 4), "traffic": None,
+                        "kernel": "extend_kernel (inspector, all rounds)", "ops_per_cell": OPS_PER_CELL["extend"]}}
+    if not a.no_cpu:
+        print("[bench] CPU oracle sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_pipeline_baseline(w, a.cpu_seconds, a.round_size)
+    ctx.close()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -254,6 +354,8 @@ def main():
         sys.exit(2)
     if a.workload == "seeds":
         return bench_seeds(a)
+    if a.workload == "pipeline":
+        return bench_pipeline(a)
     import numpy as np
     import torch
 

@@ -1,0 +1,54 @@
+"""The whole chain on the GPU -- seed stage, then covered-seed rounds -- on
+both strands of a chromosome pair, against the oracle's seed stage and
+rounds on the same inputs: every seed, every covered flag, every field and
+CIGAR of every extended seed."""
+import numpy as np
+import pytest
+
+import oracle
+from smith_waterman_dp_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+from smith_waterman_dp_amd import fz  # noqa: E402
+
+from test_gpu_parity import compare  # noqa: E402
+
+
+def log(msg):
+    print("[gpu] " + msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    torch.zeros(1, device="cuda:0").add_(1)
+    torch.cuda.synchronize()
+    c = fz.Context(0)
+    yield c
+    c.close()
+
+
+@pytest.mark.parametrize("rc", [False, True])
+def test_seed_stage_then_rounds(ctx, rc):
+    w = W.chromosome(length=250_000, inv_min=20_000, inv_max=60_000, seed=12)
+    T = torch.from_numpy(w["target"]).to("cuda:0")
+    Q = torch.from_numpy(w["query"]).to("cuda:0")
+    seeds, nh = ctx.find_seeds(T, Q, k=19, flank=32768, query_rc=rc)
+    qo = oracle.revcomp(w["query"]) if rc else w["query"]
+    ref_seeds, ref_nh = oracle.find_seeds(w["target"], w["query"], 19, 32768, query_rc=rc)
+    assert nh == ref_nh and np.array_equal(seeds.cpu().numpy(), ref_seeds)
+    # a seeded order, the same on both sides
+    perm = np.random.default_rng(5).permutation(len(ref_seeds))
+    S = ref_seeds[perm]
+    log("%s strand: %d seeds" % ("reverse" if rc else "forward", len(S)))
+    h, c, _ = ctx.extend_rounds(T, Q, seeds[torch.from_numpy(perm).to("cuda:0")], w["scoring"], w["ydrop"], 3000,
+                                128, query_rc=rc)
+    gh, gc = h.cpu().numpy(), c.cpu().numpy().view(np.uint32)
+    oh, ow, oo = oracle.extend_rounds(w["target"], qo, S, w["scoring"], w["ydrop"], 3000, 128)
+    gcov = (gh[:, 1] & fz.FZ_HIT_COVERED) != 0
+    assert np.array_equal(gcov, (oh["status"] & oracle.STATUS_COVERED) != 0)
+    idx = np.nonzero(~gcov)[0]
+    compare(gh, gc, oh[idx], ow, oo[idx], idx=idx, label="pipeline %s" % ("rc" if rc else "fwd"))
+    log("covered %d, extended %d" % (gcov.sum(), idx.size))
