@@ -116,7 +116,8 @@ for _k, _c in enumerate("ACGT"):
 
 def find_seeds(target, query, k=19, flank=32768, dedup=True, query_rc=False):
     """The seed stage: every (t, q) with target[t:t+k] == query[q:q+k] (with
-    query_rc, q indexes the query's reverse complement).
+    query_rc, q indexes the query's reverse complement), N (the unknown base,
+    either case) matching nothing, not even N.
 
     FastZ (SC'21), section 2: whole-genome alignment first finds short exact
     matches (19 bases) between the two sequences as seed sites and then
@@ -130,32 +131,40 @@ def find_seeds(target, query, k=19, flank=32768, dedup=True, query_rc=False):
     T = _as_bytes(target)
     Q = revcomp(query) if query_rc else _as_bytes(query)
     tc, qc = _CODE[T], _CODE[Q]
-    if (tc < 0).any() or (qc < 0).any():
-        raise ValueError("sequence holds a byte other than A, C, G, T")
+    tn, qn = (T | 0x20) == ord("n"), (Q | 0x20) == ord("n")
+    if ((tc < 0) & ~tn).any() or ((qc < 0) & ~qn).any():
+        raise ValueError("sequence holds a byte other than A, C, G, T, N")
     if not 1 <= k <= 32:
         raise ValueError("k must be 1..32")
     nt, nq = T.size - k + 1, Q.size - k + 1
     if nt <= 0 or nq <= 0:
         return np.zeros((0, 7), dtype=np.int64), 0
 
-    def kmers(c, n):
-        # the k codes from each start as a base-4 number, first base most significant
+    def kmers(c, isn, n):
+        # the k codes from each start as a base-4 number, first base most
+        # significant; and whether the k bases hold no N (N is no base: a
+        # k-mer with N matches nothing)
         v = np.zeros(n, dtype=np.uint64)
+        bad = np.zeros(n, dtype=bool)
         for i in range(k):
-            v = v * np.uint64(4) + c[i:i + n].astype(np.uint64)
-        return v
+            v = v * np.uint64(4) + np.maximum(c[i:i + n], 0).astype(np.uint64)
+            bad |= isn[i:i + n]
+        return v, ~bad
 
-    tk, qk = kmers(tc, nt), kmers(qc, nq)
+    tk, tv = kmers(tc, tn, nt)
+    qk, qv = kmers(qc, qn, nq)
+    tpos = np.nonzero(tv)[0]
+    tk = tk[tv]
     order = np.argsort(tk, kind="stable")
     st = tk[order]
     lo = np.searchsorted(st, qk, "left")
     hi = np.searchsorted(st, qk, "right")
-    cnt = hi - lo
+    cnt = np.where(qv, hi - lo, 0)
     n_hits = int(cnt.sum())
     q = np.repeat(np.arange(nq, dtype=np.int64), cnt)
     first = np.repeat(lo, cnt)
     nth = np.arange(n_hits, dtype=np.int64) - np.repeat(np.cumsum(cnt) - cnt, cnt)
-    t = order[first + nth].astype(np.int64)
+    t = tpos[order[first + nth]].astype(np.int64)
     diag = t - q
     o = np.lexsort((t, diag))
     t, q, diag = t[o], q[o], diag[o]

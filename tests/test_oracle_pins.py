@@ -438,7 +438,7 @@ def _seeds_by_enumeration(T, Q, k, flank, dedup):
     hits = []
     for t in range(len(T) - k + 1):
         for q in range(len(Q) - k + 1):
-            if T[t:t + k] == Q[q:q + k]:
+            if T[t:t + k] == Q[q:q + k] and "N" not in T[t:t + k]:
                 hits.append((t - q, t, q))
     hits.sort()
     out = []
@@ -451,17 +451,18 @@ def _seeds_by_enumeration(T, Q, k, flank, dedup):
     return out, len(hits)
 
 
-@pytest.mark.parametrize("seed,k", [(0, 3), (1, 5), (2, 8), (3, 4)])
-def test_find_seeds_enumeration(seed, k):
+@pytest.mark.parametrize("seed,k,alphabet", [(0, 3, "ACGT"), (1, 5, "ACGT"), (2, 8, "ACGT"), (3, 4, "ACGT"),
+                                             (4, 3, "ACGTN"), (5, 6, "AAACGTN")])
+def test_find_seeds_enumeration(seed, k, alphabet):
     """Random pairs with planted repeats and mutated copies, against the
-    enumeration of all start pairs."""
+    enumeration of all start pairs (N matches nothing)."""
     rng = random.Random(seed)
-    T = "".join(rng.choice("ACGT") for _ in range(150))
+    T = "".join(rng.choice(alphabet) for _ in range(150))
     rep = "".join(rng.choice("ACGT") for _ in range(12))
     T = T[:30] + rep + T[42:90] + rep + T[102:]
     Q = list(T[20:140])
     for _ in range(10):
-        Q[rng.randrange(len(Q))] = rng.choice("ACGT")
+        Q[rng.randrange(len(Q))] = rng.choice(alphabet)
     Q = "".join(Q) + rep.lower()
     for dedup in (False, True):
         got, n = oracle.find_seeds(T, Q, k=k, flank=7, dedup=dedup)
@@ -479,7 +480,10 @@ def test_find_seeds_reverse_strand_and_edges():
     assert na == nb and np.array_equal(a, b)
     assert oracle.find_seeds("ACG", "ACGT", k=4)[0].shape == (0, 7)        # target shorter than k
     with pytest.raises(ValueError):
-        oracle.find_seeds("ACGN", "ACGT", k=2)
+        oracle.find_seeds("ACGR", "ACGT", k=2)
+    # N matches nothing, not even N; k-mers around it still do
+    s, n = oracle.find_seeds("ACNNGT", "ACNNGT", k=2, flank=0)
+    assert n == 2 and s[:, :2].tolist() == [[0, 0], [4, 4]]
 
 
 # ---- 4x4 substitution matrix and N -------------------------------------
