@@ -12,7 +12,8 @@ namespace fz {
 // ASCII -> byte codes, forward and reversed, with PAD zero bytes on each
 // side.  role 0: codes 0..3 for A, C, G, T (N is an error); role 1 / 2: the
 // matrix mode's target / query codes (mx_target_code, the base itself),
-// with N (either case) accepted as MX_N.  revcomp: the reverse complement
+// with N (either case) accepted as MX_N; role 3: codes 0..3 with N as MX_N
+// (the seed stage).  revcomp: the reverse complement
 // is coded instead (complement = base ^ 3 with A=0, C=1, G=2, T=3; N stays
 // N).  Any other byte sets bit 0 of *err and is coded as A.
 __global__ void pack_kernel(const uint8_t *__restrict__ ascii, int64_t len, uint8_t *__restrict__ fwd,
@@ -31,7 +32,7 @@ __global__ void pack_kernel(const uint8_t *__restrict__ ascii, int64_t len, uint
                 code = 0;
             } else if (code != MX_N) {
                 if (revcomp) code ^= 3;
-                if (role == 1) code = mx_target_code(code);
+                if (role == 1) code = mx_target_code(code);     // roles 2, 3: the base itself
             }
         }
         fwd[x] = (uint8_t)code;

@@ -85,7 +85,7 @@ struct fz_ctx {
     // seed stage: target keys and positions (two of each for the sort), query
     // keys, join ranges and counts, hits (two for the sort), run flags and
     // ranks, library scratch, and the seeds of the last fz_find_seeds
-    DevBuf sk_tk, sk_tk2, sk_tp, sk_tp2, sk_bend, sk_boff, sk_lo, sk_cnt, sk_off, sk_hit, sk_hit2, sk_flag, sk_rank, sk_tmp, sk_out;
+    DevBuf sk_tk, sk_tk2, sk_tp, sk_tp2, sk_valid, sk_vpos, sk_bend, sk_boff, sk_lo, sk_cnt, sk_off, sk_hit, sk_hit2, sk_flag, sk_rank, sk_tmp, sk_out;
     uint64_t last_seeds = 0;
     // covered-seed rounds: round flags, scan, packed seeds and results, CIGAR
     // words of all rounds, aligned segments (keys and ends, two of each for
@@ -97,6 +97,7 @@ struct fz_ctx {
     const uint8_t *idx_target = nullptr;
     uint64_t idx_tlen = 0;
     uint32_t idx_k = 0;
+    int64_t idx_keys = 0;               // target k-mers without N in the index
     hipStream_t xs[EXEC_STREAMS - 1] = {};   // executor streams besides the caller's
     hipEvent_t fork_ev = nullptr, join_ev[EXEC_STREAMS - 1] = {};
     hipEvent_t ev[12] = {};
@@ -363,48 +364,78 @@ static int seeds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const u
     tm.mark();
     if (!reuse)
         pack_kernel<<<std::min<int64_t>(blocks_for(NT, 256), 8192), 256, 0, st>>>(
-            target, (int64_t)tlen, as<uint8_t>(ctx->Tf), as<uint8_t>(ctx->Tr), NT, &dc->err, 0, 0);
+            target, (int64_t)tlen, as<uint8_t>(ctx->Tf), as<uint8_t>(ctx->Tr), NT, &dc->err, 0, 3);
     pack_kernel<<<std::min<int64_t>(blocks_for(NQ, 256), 8192), 256, 0, st>>>(
         query, (int64_t)qlen, as<uint8_t>(ctx->Qf), as<uint8_t>(ctx->Qr), NQ, &dc->err, (flags & FZ_QUERY_RC) ? 1 : 0,
-        0);
+        3);
     HIP_OK(hipGetLastError());
     tm.mark();
 
-    // target keys, sorted with their positions, and a bucket table over the
-    // top bits of the key: about as many buckets as target keys (at most
-    // 2^30), all 2k bits when that is fewer
+    // target keys without N, sorted with their positions, and a bucket
+    // table over the top bits of the key: about as many buckets as keys (at
+    // most 2^30), all 2k bits when that is fewer
     const unsigned gb = 4 * (unsigned)ctx->n_cu * 4;
-    int nb_bits = 1;
-    while (nb_bits < 30 && (1ll << nb_bits) < nt) ++nb_bits;
-    nb_bits = std::min(nb_bits, (int)(2 * k));
-    const int shift = (int)(2 * k) - nb_bits;
-    const int64_t NB = 1ll << nb_bits;
+    int64_t ntv = reuse ? ctx->idx_keys : 0;
     size_t tmp_sort = 0, tmp_scan = 0, tmp_max = 0, tmp_sort2 = 0;
     HIP_OK(hipcub::DeviceScan::ExclusiveSum(nullptr, tmp_scan, as<uint64_t>(ctx->sk_cnt), as<uint64_t>(ctx->sk_off),
                                             (int)nq, st));
-    if (reuse) {
-        ENSURE(ctx->sk_tmp, tmp_scan);
-        tm.mark();
-        tm.mark();
-        tm.mark();
-    } else {
+    auto table_bits = [&](int64_t nkeys) {
+        int bits = 1;
+        while (bits < 30 && (1ll << bits) < nkeys) ++bits;
+        return std::min(bits, (int)(2 * k));
+    };
+    if (!reuse) {
         ENSURE(ctx->sk_tk, nt * sizeof(uint64_t));
         ENSURE(ctx->sk_tk2, nt * sizeof(uint64_t));
         ENSURE(ctx->sk_tp, nt * sizeof(uint32_t));
         ENSURE(ctx->sk_tp2, nt * sizeof(uint32_t));
+        ENSURE(ctx->sk_valid, nt * sizeof(uint32_t));
+        ENSURE(ctx->sk_vpos, nt * sizeof(uint32_t));
         kmer_keys_kernel<<<gb, 256, 0, st>>>(as<uint8_t>(ctx->Tf) + PAD, nt, (int)k, as<uint64_t>(ctx->sk_tk),
-                                             as<uint32_t>(ctx->sk_tp));
+                                             as<uint32_t>(ctx->sk_tp), as<uint32_t>(ctx->sk_valid));
         HIP_OK(hipGetLastError());
+        size_t tv = 0;
+        HIP_OK(hipcub::DeviceScan::ExclusiveSum(nullptr, tv, as<uint32_t>(ctx->sk_valid), as<uint32_t>(ctx->sk_vpos),
+                                                (int)nt, st));
+        ENSURE(ctx->sk_tmp, std::max(tv, tmp_scan));
+        tv = ctx->sk_tmp.cap;
+        HIP_OK(hipcub::DeviceScan::ExclusiveSum(ctx->sk_tmp.p, tv, as<uint32_t>(ctx->sk_valid),
+                                                as<uint32_t>(ctx->sk_vpos), (int)nt, st));
+        uint32_t lv[2] = {0, 0};
+        HIP_OK(hipMemcpyAsync(&lv[0], as<uint32_t>(ctx->sk_vpos) + (nt - 1), sizeof(uint32_t), hipMemcpyDeviceToHost,
+                              st));
+        HIP_OK(hipMemcpyAsync(&lv[1], as<uint32_t>(ctx->sk_valid) + (nt - 1), sizeof(uint32_t),
+                              hipMemcpyDeviceToHost, st));
+        HIP_OK(hipStreamSynchronize(st));
+        ntv = (int64_t)lv[0] + lv[1];
+        if (ntv < nt) {         // k-mers with N: keep the others, in order
+            compact_keys_kernel<<<gb, 256, 0, st>>>(as<uint64_t>(ctx->sk_tk), as<uint32_t>(ctx->sk_tp),
+                                                    as<uint32_t>(ctx->sk_valid), as<uint32_t>(ctx->sk_vpos), nt,
+                                                    as<uint64_t>(ctx->sk_tk2), as<uint32_t>(ctx->sk_tp2));
+            HIP_OK(hipGetLastError());
+            std::swap(ctx->sk_tk, ctx->sk_tk2);
+            std::swap(ctx->sk_tp, ctx->sk_tp2);
+        }
+    }
+    const int nb_bits = table_bits(ntv);
+    const int shift = (int)(2 * k) - nb_bits;
+    const int64_t NB = 1ll << nb_bits;
+    if (reuse || ntv == 0) {
+        ENSURE(ctx->sk_tmp, tmp_scan);
+        tm.mark();              // keys (done above unless reused), sort, table
+        tm.mark();
+        tm.mark();
+    } else {
         tm.mark();
         HIP_OK(hipcub::DeviceRadixSort::SortPairs(nullptr, tmp_sort, as<uint64_t>(ctx->sk_tk),
                                                   as<uint64_t>(ctx->sk_tk2), as<uint32_t>(ctx->sk_tp),
-                                                  as<uint32_t>(ctx->sk_tp2), (int)nt, 0, (int)(2 * k), st));
+                                                  as<uint32_t>(ctx->sk_tp2), (int)ntv, 0, (int)(2 * k), st));
         HIP_OK(hipcub::DeviceScan::InclusiveScan(nullptr, tmp_max, as<uint32_t>(ctx->sk_bend),
                                                  as<uint32_t>(ctx->sk_boff) + 1, hipcub::Max(), (int)NB, st));
         ENSURE(ctx->sk_tmp, std::max(std::max(tmp_sort, tmp_scan), tmp_max));
         HIP_OK(hipcub::DeviceRadixSort::SortPairs(ctx->sk_tmp.p, tmp_sort, as<uint64_t>(ctx->sk_tk),
                                                   as<uint64_t>(ctx->sk_tk2), as<uint32_t>(ctx->sk_tp),
-                                                  as<uint32_t>(ctx->sk_tp2), (int)nt, 0, (int)(2 * k), st));
+                                                  as<uint32_t>(ctx->sk_tp2), (int)ntv, 0, (int)(2 * k), st));
         tm.mark();
         ENSURE(ctx->sk_bend, NB * sizeof(uint32_t));
         ENSURE(ctx->sk_boff, (NB + 1) * sizeof(uint32_t));
@@ -412,7 +443,7 @@ static int seeds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const u
         if (rc) return rc;
         rc = zero(ctx, ctx->sk_boff.p, sizeof(uint32_t), st);
         if (rc) return rc;
-        bucket_end_kernel<<<gb, 256, 0, st>>>(as<uint64_t>(ctx->sk_tk2), nt, shift, as<uint32_t>(ctx->sk_bend));
+        bucket_end_kernel<<<gb, 256, 0, st>>>(as<uint64_t>(ctx->sk_tk2), ntv, shift, as<uint32_t>(ctx->sk_bend));
         HIP_OK(hipGetLastError());
         tmp_max = ctx->sk_tmp.cap;
         HIP_OK(hipcub::DeviceScan::InclusiveScan(ctx->sk_tmp.p, tmp_max, as<uint32_t>(ctx->sk_bend),
@@ -424,7 +455,7 @@ static int seeds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const u
     ENSURE(ctx->sk_lo, nq * sizeof(uint32_t));
     ENSURE(ctx->sk_cnt, nq * sizeof(uint64_t));
     ENSURE(ctx->sk_off, nq * sizeof(uint64_t));
-    join_count_kernel<<<gb, 256, 0, st>>>(as<uint64_t>(ctx->sk_tk2), as<uint32_t>(ctx->sk_boff), shift,
+    join_count_kernel<<<gb, 256, 0, st>>>(as<uint64_t>(ctx->sk_tk2), ntv, as<uint32_t>(ctx->sk_boff), shift,
                                           as<uint8_t>(ctx->Qf) + PAD, nq, (int)k, as<uint32_t>(ctx->sk_lo),
                                           as<uint64_t>(ctx->sk_cnt));
     HIP_OK(hipGetLastError());
@@ -439,12 +470,13 @@ static int seeds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const u
     Counters hc;
     HIP_OK(hipMemcpyAsync(&hc, dc, sizeof(Counters), hipMemcpyDeviceToHost, st));
     HIP_OK(hipStreamSynchronize(st));
-    if (hc.err & 1u) return fail(ctx, FZ_EINVAL, "sequence holds a byte other than A, C, G, T");
+    if (hc.err & 1u) return fail(ctx, FZ_EINVAL, "sequence holds a byte other than A, C, G, T, N");
     if (!reuse) {
         ctx->idx_valid = true;
         ctx->idx_target = target;
         ctx->idx_tlen = tlen;
         ctx->idx_k = k;
+        ctx->idx_keys = ntv;
     }
     const uint64_t H = last[0] + last[1];
     if (n_hits) *n_hits = H;
@@ -576,7 +608,8 @@ void fz_destroy(fz_ctx *ctx)
                       &ctx->eager, &ctx->side_trace, &ctx->run_cap, &ctx->run_off, &ctx->run_len, &ctx->runs,
                       &ctx->items, &ctx->batch_first, &ctx->scan_tmp, &ctx->cig, &ctx->cigar,
                       &ctx->counters, &ctx->ovl0, &ctx->ovl1, &ctx->bnd,
-                      &ctx->sk_tk, &ctx->sk_tk2, &ctx->sk_tp, &ctx->sk_tp2, &ctx->sk_bend, &ctx->sk_boff, &ctx->sk_lo, &ctx->sk_cnt,
+                      &ctx->sk_tk, &ctx->sk_tk2, &ctx->sk_tp, &ctx->sk_tp2, &ctx->sk_valid, &ctx->sk_vpos,
+                      &ctx->sk_bend, &ctx->sk_boff, &ctx->sk_lo, &ctx->sk_cnt,
                       &ctx->sk_off, &ctx->sk_hit, &ctx->sk_hit2, &ctx->sk_flag, &ctx->sk_rank, &ctx->sk_tmp,
                       &ctx->sk_out, &ctx->rd_keep, &ctx->rd_pos, &ctx->rd_seeds, &ctx->rd_hits, &ctx->rd_cnt,
                       &ctx->rd_off, &ctx->rd_cig, &ctx->sg_key, &ctx->sg_key2, &ctx->sg_end, &ctx->sg_end2,

@@ -7,7 +7,7 @@
 // first step plus the plainest filter, one seed per run of hits on one
 // diagonal:
 //   keys    the k codes at every target start position as one base-4
-//           number
+//           number; k-mers holding N (which matches nothing) are dropped
 //   sort    the target's (key, position) pairs by key (device radix sort)
 //   index   a direct-address table over the top bits of the key: for each
 //           bucket, where its keys start in the sorted array (about one key
@@ -30,16 +30,37 @@
 namespace fz {
 
 // key of every start position p < nkeys: codes[p .. p+k-1], first base most
-// significant (k <= 32, two bits per base)
+// significant (k <= 32, two bits per base); valid[p] = 0 when the k bases
+// hold an N (code MX_N), which matches nothing
 __global__ void kmer_keys_kernel(const uint8_t *__restrict__ codes, int64_t nkeys, int k, uint64_t *__restrict__ keys,
-                                 uint32_t *__restrict__ pos)
+                                 uint32_t *__restrict__ pos, uint32_t *__restrict__ valid)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < nkeys; p += stride) {
         uint64_t key = 0;
-        for (int i = 0; i < k; ++i) key = (key << 2) | (uint64_t)codes[p + i];
+        uint32_t any_n = 0;
+        for (int i = 0; i < k; ++i) {
+            const uint32_t c = codes[p + i];
+            any_n |= c;
+            key = (key << 2) | (uint64_t)(c & 3u);
+        }
         keys[p] = key;
-        if (pos) pos[p] = (uint32_t)p;
+        pos[p] = (uint32_t)p;
+        valid[p] = (any_n & MX_N) ? 0u : 1u;
+    }
+}
+
+// The valid (key, position) pairs, packed in order (vpos = exclusive scan
+// of valid).
+__global__ void compact_keys_kernel(const uint64_t *__restrict__ keys, const uint32_t *__restrict__ pos,
+                                    const uint32_t *__restrict__ valid, const uint32_t *__restrict__ vpos, int64_t n,
+                                    uint64_t *__restrict__ okeys, uint32_t *__restrict__ opos)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < n; p += stride) {
+        if (!valid[p]) continue;
+        okeys[vpos[p]] = keys[p];
+        opos[vpos[p]] = pos[p];
     }
 }
 
@@ -58,14 +79,24 @@ __global__ void bucket_end_kernel(const uint64_t *__restrict__ tkeys, int64_t nt
 
 // For every query position: its key (read from the codes), then where that
 // key's run starts in the sorted target keys, and how long it is.
-__global__ void join_count_kernel(const uint64_t *__restrict__ tkeys, const uint32_t *__restrict__ off, int shift,
-                                  const uint8_t *__restrict__ qcodes, int64_t nq, int k, uint32_t *__restrict__ lo_out,
-                                  uint64_t *__restrict__ cnt)
+__global__ void join_count_kernel(const uint64_t *__restrict__ tkeys, int64_t nt, const uint32_t *__restrict__ off,
+                                  int shift, const uint8_t *__restrict__ qcodes, int64_t nq, int k,
+                                  uint32_t *__restrict__ lo_out, uint64_t *__restrict__ cnt)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nq; q += stride) {
         uint64_t key = 0;
-        for (int i = 0; i < k; ++i) key = (key << 2) | (uint64_t)qcodes[q + i];
+        uint32_t any_n = 0;
+        for (int i = 0; i < k; ++i) {
+            const uint32_t c = qcodes[q + i];
+            any_n |= c;
+            key = (key << 2) | (uint64_t)(c & 3u);
+        }
+        if (nt == 0 || (any_n & MX_N)) {     // no target k-mers, or an N here: no hit
+            lo_out[q] = 0;
+            cnt[q] = 0;
+            continue;
+        }
         const uint64_t b = key >> shift;
         uint32_t a = off[b], e = off[b + 1];
         if (shift) {                        // the bucket holds other keys too

@@ -52,3 +52,27 @@ def test_seed_stage_then_rounds(ctx, rc):
     idx = np.nonzero(~gcov)[0]
     compare(gh, gc, oh[idx], ow, oo[idx], idx=idx, label="pipeline %s" % ("rc" if rc else "fwd"))
     log("covered %d, extended %d" % (gcov.sum(), idx.size))
+
+
+def test_chain_with_n_and_matrix(ctx):
+    """Sequences with runs of N scored with the 4x4 matrix: the seed stage
+    skips k-mers with N, the rounds extend through N with the N score."""
+    w = W.chromosome(length=150_000, inv_min=10_000, inv_max=30_000, seed=13)
+    rng = np.random.default_rng(14)
+    Tn = W.plant_n_runs(rng, w["target"], 15, 5, 400)
+    Qn = W.plant_n_runs(rng, w["query"], 15, 5, 400)
+    sc = W.matrix_scoring()
+    T = torch.from_numpy(Tn).to("cuda:0")
+    Q = torch.from_numpy(Qn).to("cuda:0")
+    seeds, nh = ctx.find_seeds(T, Q, k=19, flank=32768)
+    ref_seeds, ref_nh = oracle.find_seeds(Tn, Qn, 19, 32768)
+    assert nh == ref_nh and np.array_equal(seeds.cpu().numpy(), ref_seeds)
+    perm = np.random.default_rng(15).permutation(len(ref_seeds))
+    h, c, _ = ctx.extend_rounds(T, Q, seeds[torch.from_numpy(perm).to("cuda:0")], sc, w["ydrop"], 3000, 64)
+    gh, gc = h.cpu().numpy(), c.cpu().numpy().view(np.uint32)
+    oh, ow, oo = oracle.extend_rounds(Tn, Qn, ref_seeds[perm], sc, w["ydrop"], 3000, 64)
+    gcov = (gh[:, 1] & fz.FZ_HIT_COVERED) != 0
+    assert np.array_equal(gcov, (oh["status"] & oracle.STATUS_COVERED) != 0)
+    idx = np.nonzero(~gcov)[0]
+    compare(gh, gc, oh[idx], ow, oo[idx], idx=idx, label="chain with N and matrix")
+    log("%d seeds, covered %d" % (len(perm), gcov.sum()))

@@ -66,6 +66,26 @@ def repeat_pair(seed, n=4000):
     return T, Q
 
 
+@pytest.mark.parametrize("k", [3, 11, 19, 32])
+def test_seeds_with_n_runs(ctx, k):
+    """Runs of N (and single N) in both sequences: k-mers holding N are no
+    hits; both strands, with and without dedup, and reusing the index."""
+    T, Q = repeat_pair(100 + k)
+    rng = np.random.default_rng(k)
+    T = W.plant_n_runs(rng, np.frombuffer(T.encode(), dtype=np.uint8), 12, 1, 60)
+    Q = W.plant_n_runs(rng, np.frombuffer(Q.encode(), dtype=np.uint8), 12, 1, 60)
+    Q[::211] = ord("n")
+    for dedup in (True, False):
+        for rc in (False, True):
+            check(ctx, T, Q, k, 300, dedup, rc, "N runs k=%d" % k)
+    Td = dev(T)
+    ref = [ctx.find_seeds(Td, dev(Q), k=k, flank=300, query_rc=rc) for rc in (False, True)]
+    got = [ctx.find_seeds(Td, dev(Q), k=k, flank=300, query_rc=rc, reuse_index=(rc or i > 0))
+           for i, rc in enumerate((False, True))]
+    for (a, ha), (b, hb) in zip(ref, got):
+        assert ha == hb and torch.equal(a, b)
+
+
 @pytest.mark.parametrize("k", [3, 8, 19, 32])
 def test_seeds_repeat_pairs(ctx, k):
     T, Q = repeat_pair(k)
@@ -105,8 +125,12 @@ def test_seeds_edges_and_errors(ctx):
             ctx.find_seeds(dev(T), dev(Q), k=k)
         assert e.value.code == fz.FZ_EINVAL
     with pytest.raises(fz.FzError) as e:
-        ctx.find_seeds(dev("ACGTNACGT"), dev(Q), k=3)
+        ctx.find_seeds(dev("ACGTRACGT"), dev(Q), k=3)
     assert e.value.code == fz.FZ_EINVAL
+    # N matches nothing, not even N
+    check(ctx, "ACNNGT", "ACNNGT", 2, 0, True, False, "N")
+    s, h = ctx.find_seeds(dev("NNNN"), dev("NNNN"), k=2)           # every k-mer holds N
+    assert s.shape == (0, 7) and h == 0
     # the context stays usable after an error
     check(ctx, T, Q, 3, 2, True, True, "after errors")
 
@@ -148,7 +172,7 @@ def test_seeds_reuse_index(ctx):
     with pytest.raises(fz.FzError):
         ctx.find_seeds(Q, Q, k=11, flank=50, reuse_index=True)            # other target
     bad = T.clone()
-    bad[5] = ord("N")
+    bad[5] = ord("R")
     with pytest.raises(fz.FzError):
         ctx.find_seeds(bad, Q, k=11, flank=50)                            # failed build drops the index
     with pytest.raises(fz.FzError):
