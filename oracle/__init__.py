@@ -285,14 +285,28 @@ def aligned_segments(hits, words, offs):
     return segs
 
 
-def extend_rounds(target, query, seeds, scoring, ydrop, min_tb, round_size, threads=None):
+def round_bounds(n, round_size, doubling=False):
+    """[start, end) of each round: round_size seeds each, or, with doubling,
+    round_size for the first round and twice the previous size after it."""
+    out, r0, size = [], 0, int(round_size)
+    while r0 < n:
+        out.append((r0, min(r0 + size, n)))
+        r0 += size
+        if doubling:
+            size *= 2
+    return out
+
+
+def extend_rounds(target, query, seeds, scoring, ydrop, min_tb, round_size, threads=None, doubling=False):
     """Covered-seed suppression by rounds.
 
     FastZ (SC'21) section 2.1 describes LASTZ ending a seed extension that
     runs into an alignment it found before (joining the two would not pay),
     and section 3.4 why FastZ drops that rule: it depends on the order of
     the extensions.  Reading taken here, the data-parallel form of the rule:
-    seeds are taken in the given order in rounds of `round_size`; a seed of
+    seeds are taken in the given order in rounds of `round_size` (with
+    doubling, each round after the first twice the size of the one before;
+    see round_bounds); a seed of
     round r whose exact-match columns (t_pos + k, q_pos + k), k < seed_len,
     share a cell with the aligned (M) columns of an alignment traced (given
     a CIGAR) in rounds before r (a seed without columns, or with columns
@@ -312,8 +326,8 @@ def extend_rounds(target, query, seeds, scoring, ydrop, min_tb, round_size, thre
     hits = np.zeros(n, dtype=HIT_DTYPE)
     cig = [np.zeros(0, dtype=np.uint32) for _ in range(n)]
     by_diag = {}                       # diagonal -> list of (t_first, t_end) of earlier rounds
-    for r0 in range(0, n, round_size):
-        idx = np.arange(r0, min(r0 + round_size, n))
+    for r0, r1 in round_bounds(n, round_size, doubling):
+        idx = np.arange(r0, r1)
         keep = []
         for k in idx:
             t, q, L = int(S[k, 0]), int(S[k, 1]), int(S[k, 2])

@@ -621,21 +621,33 @@ def _cells_of(T, Q, hit, words):
     return cells
 
 
-@pytest.mark.parametrize("round_size", [3, 10, 40])
-def test_rounds_coverage_by_cells(round_size):
+def test_round_bounds():
+    assert oracle.round_bounds(10, 3) == [(0, 3), (3, 6), (6, 9), (9, 10)]
+    assert oracle.round_bounds(10, 1, doubling=True) == [(0, 1), (1, 3), (3, 7), (7, 10)]
+    assert oracle.round_bounds(0, 4) == []
+
+
+@pytest.mark.parametrize("round_size,doubling", [(3, False), (10, False), (40, False), (1, True), (4, True)])
+def test_rounds_coverage_by_cells(round_size, doubling):
     """Coverage recomputed from explicit cell sets: a seed is covered exactly
     when one of its columns is an aligned cell of an alignment traced in an
     earlier round; every extended seed has run()'s result."""
     w = W.homolog_rounds(length=16_000, seed=4)
     S = w["seeds"]
     h, words, offs = oracle.extend_rounds(w["target"], w["query"], S, w["scoring"], w["ydrop"], w["min_tb"],
-                                          round_size)
+                                          round_size, doubling=doubling)
     ref, rw, ro = oracle.run(w["target"], w["query"], S, w["scoring"], w["ydrop"], min_tb=w["min_tb"])
     earlier = set()
     n_cov = 0
-    for r0 in range(0, len(S), round_size):
+    bounds = []
+    r0, size = 0, round_size
+    while r0 < len(S):                      # the schedule, written out again
+        bounds.append((r0, min(r0 + size, len(S))))
+        r0 += size
+        size *= 2 if doubling else 1
+    for r0, r1 in bounds:
         this_round = set()
-        for k in range(r0, min(r0 + round_size, len(S))):
+        for k in range(r0, r1):
             t, q, L = (int(x) for x in S[k, :3])
             cov = any((t + i, q + i) in earlier for i in range(L))
             assert bool(h["status"][k] & oracle.STATUS_COVERED) == cov, k
