@@ -89,14 +89,19 @@ def parse():
     ap.add_argument("--workload", default="skewed",
                     choices=["skewed", "local", "tiny", "executor_heavy", "chromosome", "chromosome_rc",
                              "skewed_matrix", "chromosome_rounds", "seeds", "pipeline"])
-    ap.add_argument("--round-size", type=int, default=4096,
-                    help="chromosome_rounds: seeds per round of covered-seed suppression")
+    ap.add_argument("--round-size", type=int, default=2048,
+                    help="chromosome_rounds, pipeline: seeds per round of covered-seed suppression (with the "
+                         "doubling schedule, of the first round)")
+    ap.add_argument("--round-schedule", choices=["doubling", "fixed"], default="doubling",
+                    help="doubling: each round twice the size of the one before; fixed: all rounds alike")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after the timed steps, one plain device-to-device copy of this many MiB "
                          "(a known-size reference for HBM traffic counters)")
-    return ap.parse_args()
+    a = ap.parse_args()
+    a.round_doubling = a.round_schedule == "doubling"
+    return a
 
 
 def make_workload(name):
@@ -249,7 +254,7 @@ def bench_seeds(a):
     print(json.dumps(out), flush=True)
 
 
-def cpu_pipeline_baseline(w, target_seconds, round_size):
+def cpu_pipeline_baseline(w, target_seconds, round_size, doubling):
     """The oracle's seed stage and rounds, as they stand, on growing prefixes
     of the pair (both strands), until one run passes half the target time."""
     import numpy as np
@@ -270,7 +275,7 @@ def cpu_pipeline_baseline(w, target_seconds, round_size):
             s, _ = oracle.find_seeds(T, Q, w["k"], w["flank"], query_rc=rc)
             s = s[np.random.default_rng(7).permutation(len(s))]
             oracle.extend_rounds(T, oracle.revcomp(Q) if rc else Q, s, w["scoring"], w["ydrop"], 3000, round_size,
-                                 threads=threads)
+                                 threads=threads, doubling=doubling)
         dt = time.time() - t0
         if dt > target_seconds / 2 or L == full:
             break
@@ -300,7 +305,7 @@ def bench_pipeline(a):
             seeds, _ = ctx.find_seeds(T, Q, w["k"], w["flank"], query_rc=rc, reuse_index=rc)
             perm = torch.randperm(seeds.shape[0], generator=torch.Generator().manual_seed(7)).to(dev)
             h, c, st = ctx.extend_rounds(T, Q, seeds[perm], w["scoring"], w["ydrop"], 3000, a.round_size,
-                                         want_stats=True, query_rc=rc)
+                                         want_stats=True, query_rc=rc, doubling=a.round_doubling)
             out.append((seeds.shape[0], h, st))
         return out
 
@@ -334,6 +339,7 @@ def bench_pipeline(a):
            "vs_baseline": None, "dtype": "int32", "data": "synthetic",
            "config": {"workload": "chromosome_pipeline", "target_bp": int(w["target"].size),
                       "query_bp": int(w["query"].size), "k": w["k"], "flank": w["flank"], "round_size": a.round_size,
+                      "round_doubling": bool(a.round_doubling),
                       "min_traceback_score": 3000, "cells_per_step": cells, "strands": per_strand,
                       "inspector_ms": round(kern_s * 1e3, 3)},
            "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(peak, 3), "unit": "TOP/s",
@@ -341,7 +347,7 @@ def bench_pipeline(a):
                         "kernel": "extend_kernel (inspector, all rounds)", "ops_per_cell": OPS_PER_CELL["extend"]}}
     if not a.no_cpu:
         print("[bench] CPU oracle sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_pipeline_baseline(w, a.cpu_seconds, a.round_size)
+        out["cpu_baseline"] = cpu_pipeline_baseline(w, a.cpu_seconds, a.round_size, a.round_doubling)
     ctx.close()
     print(json.dumps(out), flush=True)
 
@@ -383,7 +389,7 @@ def main():
             return ctx.local(T, Q, S, w["scoring"], want_stats=True, query_rc=rc)
         if rounds:
             return ctx.extend_rounds(T, Q, S, w["scoring"], w["ydrop"], min_tb, a.round_size, want_stats=True,
-                                     query_rc=rc)
+                                     query_rc=rc, doubling=a.round_doubling)
         return ctx.extend(T, Q, S, w["scoring"], w["ydrop"], min_tb, traceback=w.get("traceback", True),
                           want_stats=True, query_rc=rc)
 
@@ -436,7 +442,12 @@ def main():
     if rounds:
         from smith_waterman_dp_amd import fz as _fz
         cfg["round_size"] = a.round_size
-        cfg["rounds"] = -(-n // a.round_size)
+        cfg["round_doubling"] = bool(a.round_doubling)
+        r0, size, nr = 0, a.round_size, 0
+        while r0 < n:
+            r0, nr = r0 + size, nr + 1
+            size *= 2 if a.round_doubling else 1
+        cfg["rounds"] = nr
         cfg["covered_seeds"] = int(((h[:, 1] & _fz.FZ_HIT_COVERED) != 0).sum())
         cfg["plain_batch_ms"] = round(plain_ms, 1)
     out = {"metric": METRIC if a.workload == "skewed" else "GCUPS on the %s batch, 1 MI355X" % a.workload,

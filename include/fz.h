@@ -134,7 +134,8 @@ enum {
     FZ_STATS = 1u << 2,            /* fill *stats (adds stream syncs for phase timings) */
     FZ_QUERY_RC = 1u << 3,         /* seeds lie on the query's reverse complement (see below) */
     FZ_SEEDS_ALL = 1u << 4,        /* fz_find_seeds: every shared k-mer, no diagonal dedup */
-    FZ_SEEDS_REUSE_INDEX = 1u << 5 /* fz_find_seeds: reuse the target index of an earlier call */
+    FZ_SEEDS_REUSE_INDEX = 1u << 5,/* fz_find_seeds: reuse the target index of an earlier call */
+    FZ_ROUNDS_DOUBLING = 1u << 6   /* fz_extend_rounds: each round twice the size of the one before */
 };
 
 /* FZ_QUERY_RC: the call aligns the target against the reverse complement
@@ -234,9 +235,13 @@ int fz_extend_batch(fz_ctx *ctx,
  * not above min_traceback_score) suppress nothing.  A seed without columns,
  * or with columns outside the sequences, is never covered.
  *   arguments       as fz_extend_batch; flags must hold FZ_TRACEBACK and
- *                   not FZ_LOCAL; sequences shorter than 2^31 bases
+ *                   not FZ_LOCAL, and may add FZ_ROUNDS_DOUBLING; sequences
+ *                   shorter than 2^31 bases
  *   round_size      >= 1 seeds per round (>= n_seeds: one round, the same
- *                   results as fz_extend_batch)
+ *                   results as fz_extend_batch); with FZ_ROUNDS_DOUBLING in
+ *                   flags, the size of the first round, each later round
+ *                   holding twice as many seeds as the one before (few
+ *                   early extensions cover most seeds, in few rounds)
  *   cigar, cigar_words   the words of all rounds, in seed order within a
  *                   round and round after round; hits' cigar_off index them
  *   stats           sums over the rounds

@@ -965,6 +965,8 @@ static int rounds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
 {
     if (cigar) *cigar = nullptr;
     if (cigar_words) *cigar_words = 0;
+    const bool doubling = (flags & FZ_ROUNDS_DOUBLING) != 0;
+    flags &= ~(uint32_t)FZ_ROUNDS_DOUBLING;
     int rc = check_args(ctx, target, tlen, query, qlen, seeds, n_seeds, scoring, matrix, ydrop, flags, hits);
     if (rc != FZ_OK) return rc;
     if (!(flags & FZ_TRACEBACK) || (flags & FZ_LOCAL))
@@ -975,18 +977,19 @@ static int rounds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     fz_stats tot;
     memset(&tot, 0, sizeof tot);
     const int64_t n = (int64_t)n_seeds;
-    const int64_t B = (int64_t)std::min<uint64_t>(round_size, std::max<uint64_t>(n_seeds, 1));
-    if (n > 0) {
-        ENSURE(ctx->rd_keep, B * sizeof(uint32_t));
-        ENSURE(ctx->rd_pos, B * sizeof(uint32_t));
-        ENSURE(ctx->rd_seeds, B * sizeof(fz_seed));
-        ENSURE(ctx->rd_hits, B * sizeof(fz_hit));
-        ENSURE(ctx->rd_cnt, B * sizeof(uint64_t));
-        ENSURE(ctx->rd_off, B * sizeof(uint64_t));
-    }
+    int64_t B = (int64_t)std::min<uint64_t>(round_size, std::max<uint64_t>(n_seeds, 1));
     int64_t acc_words = 0, nseg = 0;
-    for (int64_t r0 = 0; r0 < n; r0 += B) {
+    for (int64_t r0 = 0; r0 < n; r0 += B, B = doubling ? std::min<int64_t>(2 * B, n) : B) {
         const int64_t nb = std::min<int64_t>(B, n - r0);
+        // the per-round buffers may grow (doubling rounds): let the last
+        // round's kernels finish before any is reallocated
+        if (r0 > 0) HIP_OK(hipStreamSynchronize(st));
+        ENSURE(ctx->rd_keep, nb * sizeof(uint32_t));
+        ENSURE(ctx->rd_pos, nb * sizeof(uint32_t));
+        ENSURE(ctx->rd_seeds, nb * sizeof(fz_seed));
+        ENSURE(ctx->rd_hits, nb * sizeof(fz_hit));
+        ENSURE(ctx->rd_cnt, nb * sizeof(uint64_t));
+        ENSURE(ctx->rd_off, nb * sizeof(uint64_t));
         const fz_seed *rs = seeds + r0;
         uint32_t *keep = as<uint32_t>(ctx->rd_keep), *pos = as<uint32_t>(ctx->rd_pos);
         // which seeds of the round an earlier round covers

@@ -37,20 +37,20 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
 
 
-def run_rounds(ctx, w, round_size, seeds=None):
+def run_rounds(ctx, w, round_size, seeds=None, doubling=False):
     S = w["seeds"] if seeds is None else seeds
-    log("rounds: %d seeds, round size %d" % (len(S), round_size))
+    log("rounds: %d seeds, round size %d, doubling %d" % (len(S), round_size, doubling))
     h, c, st = ctx.extend_rounds(dev(w["target"]), dev(w["query"]), dev(S), w["scoring"], w["ydrop"], w["min_tb"],
-                                 round_size, want_stats=True, query_rc=bool(w.get("query_rc")))
+                                 round_size, want_stats=True, query_rc=bool(w.get("query_rc")), doubling=doubling)
     torch.cuda.synchronize()
     log("rounds done")
     return h.cpu().numpy(), c.cpu().numpy().view(np.uint32), st
 
 
-def check_against_oracle(ctx, w, round_size, label):
-    gh, gc, _ = run_rounds(ctx, w, round_size)
+def check_against_oracle(ctx, w, round_size, label, doubling=False):
+    gh, gc, _ = run_rounds(ctx, w, round_size, doubling=doubling)
     oh, ow, oo = oracle.extend_rounds(w["target"], oracle_query(w), w["seeds"], w["scoring"], w["ydrop"],
-                                      w["min_tb"], round_size)
+                                      w["min_tb"], round_size, doubling=doubling)
     gcov = (gh[:, 1] & fz.FZ_HIT_COVERED) != 0
     ocov = (oh["status"] & oracle.STATUS_COVERED) != 0
     assert np.array_equal(gcov, ocov), (label, np.nonzero(gcov != ocov)[0][:10])
@@ -68,6 +68,19 @@ def test_rounds_homolog_vs_oracle(ctx, round_size):
     w = W.homolog_rounds(length=16_000, seed=4)
     gh, gcov = check_against_oracle(ctx, w, round_size, "homolog rounds %d" % round_size)
     assert gcov.any() or round_size >= len(w["seeds"])
+
+
+@pytest.mark.parametrize("round_size", [1, 5])
+def test_rounds_doubling_vs_oracle(ctx, round_size):
+    w = W.homolog_rounds(length=16_000, seed=4)
+    gh, gcov = check_against_oracle(ctx, w, round_size, "homolog doubling %d" % round_size, doubling=True)
+    assert gcov.any()
+
+
+def test_rounds_doubling_chromosome_reduced(ctx):
+    w = W.chromosome_rounds(length=400_000, inv_min=5_000, inv_max=20_000, seed=3)
+    gh, gcov = check_against_oracle(ctx, w, 64, "chromosome doubling reduced", doubling=True)
+    log("covered %d of %d" % (gcov.sum(), len(gcov)))
 
 
 def test_rounds_one_round_is_the_batch(ctx):
@@ -131,24 +144,30 @@ def segments_of(gh, gc, rows):
     return t[m] - q[m], t[m], t[m] + n[m]
 
 
-@pytest.mark.skipif(os.environ.get("FZ_FULL_SIZE", "1") == "0", reason="full-size runs disabled")
-def test_rounds_chromosome_full_size(ctx):
-    """The 20 Mbp pair's 144,179 seeds in rounds of 16,384: the covered set
-    recomputed from the call's own alignments, round by round, and a sample
-    of extended seeds against the oracle's plain extension."""
+@pytest.fixture(scope="module")
+def chromosome_rounds_full():
     log("generating the chromosome pair")
-    w = W.chromosome_rounds()
+    return W.chromosome_rounds()
+
+
+@pytest.mark.skipif(os.environ.get("FZ_FULL_SIZE", "1") == "0", reason="full-size runs disabled")
+@pytest.mark.parametrize("B,doubling", [(16384, False), (256, True)])
+def test_rounds_chromosome_full_size(ctx, chromosome_rounds_full, B, doubling):
+    """The 20 Mbp pair's 144,179 seeds in rounds (fixed, or doubling from a
+    small first round): the covered set recomputed from the call's own
+    alignments, round by round, and a sample of extended seeds against the
+    oracle's plain extension."""
+    w = chromosome_rounds_full
     S = w["seeds"]
-    B = 16384
-    gh, gc, st = run_rounds(ctx, w, B)
+    gh, gc, st = run_rounds(ctx, w, B, doubling=doubling)
     gcov = (gh[:, 1] & fz.FZ_HIT_COVERED) != 0
     log("covered %d of %d, %d cells" % (gcov.sum(), len(S), st["cells"]))
     tlen, qlen = w["target"].size, w["query"].size
     D = np.zeros(0, dtype=np.int64)
     A = np.zeros(0, dtype=np.int64)
     Bn = np.zeros(0, dtype=np.int64)
-    for r0 in range(0, len(S), B):
-        rows = np.arange(r0, min(r0 + B, len(S)))
+    for r0, r1 in oracle.round_bounds(len(S), B, doubling):
+        rows = np.arange(r0, r1)
         order = np.argsort(D, kind="stable")
         Ds, As, Bs = D[order], A[order], Bn[order]
         for k in rows:
