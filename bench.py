@@ -61,7 +61,7 @@ TRAFFIC_WRITE_BYTES = 1.704e5 * 1024 / 1.0
 # The same for one join_count_kernel launch of the seed stage on the 20 Mbp
 # chromosome pair (mean of the forward and reverse-strand launches), valid
 # for the sources hashed from fz_seeds.hpp.
-SEED_TRAFFIC_SRC_HASH = "e1ff44293a6376ae"
+SEED_TRAFFIC_SRC_HASH = "1c0d0bf8ec6f018d"
 SEED_TRAFFIC_FETCH_BYTES = 1.910e6 * 1024 / 0.5
 SEED_TRAFFIC_WRITE_BYTES = 2.344e5 * 1024 / 1.0
 
