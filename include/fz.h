@@ -23,8 +23,16 @@
  *   smallest i.  Traceback prefers the diagonal move, then I, then D; inside
  *   a gap it prefers "opened here" over "extended".
  * A gap of g bases costs O + g*E.  sub() is `match` for equal bases,
- * `transition` for A<->G and C<->T, `transversion` otherwise.  The seed's own
- * columns are scored with sub() and added to the two sides' scores.
+ * `transition` for A<->G and C<->T, `transversion` otherwise, or, when an
+ * fz_matrix is passed, its entry for (target base, query base), with N
+ * against anything scoring its n_score.  The seed's own columns are scored
+ * with sub() and added to the two sides' scores.
+ *
+ * Around that path: FZ_QUERY_RC aligns against the query's reverse
+ * complement; fz_find_seeds is the seed stage that produces the seeds
+ * (section 2); fz_extend_rounds runs batches in rounds and skips seeds that
+ * lie on alignments of earlier rounds (LASTZ's rule of section 2.1, made
+ * data-parallel per round).
  *
  * Local mode (FZ_LOCAL): each record's windows are one pair; the whole
  * window is scored with S = max(0, H, I, D), no y-drop, and the result is
