@@ -76,17 +76,16 @@ typedef struct {
 /* ---------------------------------------------------------------- bases -- */
 
 /* 0..3 for A, C, G, T (either case); 4 for N (either case) when a matrix
- * is in use; -1 otherwise. */
+ * is in use; -1 otherwise.  (The table holds the code plus one; 0 = none.) */
+static const signed char CODE1[256] = {
+    ['A'] = 1, ['a'] = 1, ['C'] = 2, ['c'] = 2, ['G'] = 3, ['g'] = 3, ['T'] = 4, ['t'] = 4, ['N'] = 5, ['n'] = 5,
+};
+
 static int base_code(uint8_t c, const fzo_scoring *sc)
 {
-    switch (c) {
-    case 'A': case 'a': return 0;
-    case 'C': case 'c': return 1;
-    case 'G': case 'g': return 2;
-    case 'T': case 't': return 3;
-    case 'N': case 'n': return sc->use_matrix ? 4 : -1;
-    default: return -1;
-    }
+    int code = CODE1[c] - 1;
+    if (code == 4 && !sc->use_matrix) code = -1;
+    return code;
 }
 
 /* Substitution score.  With a matrix: its entry, or n_score for a pair with
@@ -99,6 +98,15 @@ static int64_t sub_score(int a, int b, const fzo_scoring *sc)
     int a_purine = (a == 0 || a == 2), b_purine = (b == 0 || b == 2);
     if (a_purine == b_purine) return sc->transition;
     return sc->transversion;
+}
+
+/* sub_score for every pair of codes 0..4, looked up in the per-cell loops
+ * (the same values, evaluated once per extension). */
+static void sub_table(const fzo_scoring *sc, int64_t tab[5][5])
+{
+    for (int a = 0; a < 5; a++)
+        for (int b = 0; b < 5; b++)
+            tab[a][b] = (a < 4 && b < 4) || sc->use_matrix ? sub_score(a, b, sc) : 0;
 }
 
 static int64_t add(int64_t x, int64_t y) { return (x == NEG) ? NEG : x + y; }
@@ -196,6 +204,8 @@ static void extend_side(const side_seq *s, const fzo_scoring *sc, int64_t ydrop,
                         band *b, side_result *r)
 {
     const int64_t OE = sc->gap_open + sc->gap_extend, E = sc->gap_extend;
+    int64_t tab[5][5];
+    sub_table(sc, tab);
     b->nd = 0; b->ncell = 0; b->err = 0;
     r->score = 0; r->ie = 0; r->je = 0; r->cells = 0; r->dend = 0;
 
@@ -244,7 +254,7 @@ static void extend_side(const side_seq *s, const fzo_scoring *sc, int64_t ydrop,
                     int e = 0;
                     int ca = side_base(s->t, s->tdir, i, sc, &e), cb = side_base(s->q, s->qdir, j, sc, &e);
                     b->err |= e;
-                    H = add(load(b, b->S, i - 1, j - 1), sub_score(ca, cb, sc));
+                    H = add(load(b, b->S, i - 1, j - 1), tab[ca][cb]);
                 }
                 S = max2(H, max2(I, D));
                 if (S == NEG || (thr != NEG && S < thr)) { S = NEG; I = NEG; D = NEG; }
@@ -399,6 +409,8 @@ static int64_t local_pair(const uint8_t *a, int64_t m, const uint8_t *bq, int64_
                           const fzo_scoring *sc, fzo_hit *h)
 {
     const int64_t OE = sc->gap_open + sc->gap_extend, E = sc->gap_extend;
+    int64_t tab[5][5];
+    sub_table(sc, tab);
     memset(h, 0, sizeof *h);
     int64_t *Sp = malloc((size_t)(n + 1) * sizeof(int64_t));   /* row i-1 */
     int64_t *Sc = malloc((size_t)(n + 1) * sizeof(int64_t));   /* row i */
@@ -424,7 +436,7 @@ static int64_t local_pair(const uint8_t *a, int64_t m, const uint8_t *bq, int64_
         for (int64_t j = 1; j <= n; j++) {
             I = max2(add(I, -E), Sc[j - 1] - OE);
             int64_t D = max2(add(Dp[j], -E), Sp[j] - OE);
-            int64_t H = Sp[j - 1] + sub_score(ca, cb[j], sc);
+            int64_t H = Sp[j - 1] + tab[ca][cb[j]];
             int64_t S = max2(0, max2(H, max2(I, D)));
             Sc[j] = S; Dc[j] = D;
             if (S > INT32_MAX) err |= FZO_ERANGE;
