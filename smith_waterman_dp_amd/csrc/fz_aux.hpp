@@ -129,17 +129,61 @@ struct CombineArgs {
     int64_t *cells_total;       // canonical cells over the batch
 };
 
+// Wave-wide sum and maximum (every lane of the wave takes part).
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v)
+{
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+    for (int off = 32; off > 0; off >>= 1) v = max(v, (uint64_t)__shfl_xor(v, off, 64));
+    return v;
+}
+
+// counts[key] += 1 for every active lane, with one atomic per distinct key
+// in the wave; returns the counter's old value plus this lane's rank among
+// the wave's lanes with the same key (every lane of the wave takes part).
+__device__ __forceinline__ uint32_t wave_grouped_inc(uint32_t *counts, int key, bool active)
+{
+    const int lane = lane_id();
+    uint32_t r = 0;
+    uint64_t todo = ballot(active);
+    while (todo) {
+        const int leader = ctz64(todo);
+        const int kk = __shfl(key, leader, 64);
+        const bool mine = active && key == kk;
+        const uint64_t grp = ballot(mine);
+        uint32_t old = 0;
+        if (lane == leader) old = atomicAdd(&counts[kk], (uint32_t)__popcll(grp));
+        old = (uint32_t)__shfl((int)old, leader, 64);
+        if (mine) r = old + (uint32_t)__popcll(grp & ((1ull << lane) - 1ull));
+        todo &= ~grp;
+    }
+    return r;
+}
+
 __global__ void combine_kernel(CombineArgs a)
 {
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= a.n) return;
-    const fz_seed s = a.seeds[k];
-    const SeedInfo in = a.info[k];
-    const SideOut L = a.out[2 * k], R = a.out[2 * k + 1];
+    const bool valid = k < a.n;
     fz_hit h = {};
     h.bin = -1;
     int tr[2] = {0, 0};
-    if (in.status) {
+    int bkey[2] = {0, 0};
+    uint64_t pmax = 0;
+    fz_seed s = {};
+    SeedInfo in = {0, 0};
+    SideOut L = {}, R = {};
+    if (valid) {
+        s = a.seeds[k];
+        in = a.info[k];
+        L = a.out[2 * k];
+        R = a.out[2 * k + 1];
+    }
+    if (!valid) {
+    } else if (in.status) {
         h.status = in.status;
     } else if ((L.flags | R.flags) & SO_OVERFLOW) {
         h.status = FZ_HIT_EBAND;
@@ -152,7 +196,6 @@ __global__ void combine_kernel(CombineArgs a)
         h.t_end = s.t_pos + s.seed_len + R.ie;
         h.q_end = s.q_pos + s.seed_len + R.je;
         h.cells = L.cells + R.cells;
-        atomicAdd((unsigned long long *)a.cells_total, (unsigned long long)h.cells);
         if (a.traceback) {
             if (h.score > a.min_tb) {
                 h.status |= FZ_HIT_TRACED;
@@ -166,8 +209,8 @@ __global__ void combine_kernel(CombineArgs a)
                         tr[q] = 2;
                         const int64_t len = max(sd[q]->ie, sd[q]->je);
                         const int cls = (sd[q]->flags & SO_WIDE_FLAG) ? 1 : 0;
-                        atomicAdd(&a.bin_count[cls * NBINS + bin_of(len)], 1u);
-                        atomicMax((unsigned long long *)a.max_ptr, (unsigned long long)sd[q]->ptr_bytes);
+                        bkey[q] = cls * NBINS + bin_of(len);
+                        pmax = max(pmax, (uint64_t)sd[q]->ptr_bytes);
                         longest = max(longest, len);
                     }
                 }
@@ -177,6 +220,15 @@ __global__ void combine_kernel(CombineArgs a)
             }
         }
     }
+    // totals with one atomic per wave (per bin: per distinct bin)
+    const uint64_t csum = wave_sum_u64((uint64_t)h.cells);
+    const uint64_t cmax = wave_max_u64(pmax);
+    if (lane_id() == 0) {
+        if (csum) atomicAdd((unsigned long long *)a.cells_total, (unsigned long long)csum);
+        if (cmax) atomicMax((unsigned long long *)a.max_ptr, (unsigned long long)cmax);
+    }
+    for (int q = 0; q < 2; ++q) (void)wave_grouped_inc(a.bin_count, bkey[q], tr[q] == 2);
+    if (!valid) return;
     for (int q = 0; q < 2; ++q) {
         const SideOut &o = q == 0 ? L : R;
         a.side_trace[2 * k + q] = tr[q];
@@ -190,11 +242,17 @@ __global__ void bin_scatter_kernel(int64_t nsides, const int32_t *side_trace, co
                                    const uint32_t *bin_base, uint32_t *bin_fill, ExecItem *items)
 {
     const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (s >= nsides || side_trace[s] != 2) return;
-    const SideOut o = out[s];
-    const int cls = (o.flags & SO_WIDE_FLAG) ? 1 : 0;
-    const int b = cls * NBINS + bin_of(max(o.ie, o.je));
-    const uint32_t slot = bin_base[b] + atomicAdd(&bin_fill[b], 1u);
+    const bool active = s < nsides && side_trace[s] == 2;
+    SideOut o = {};
+    int b = 0;
+    if (active) {
+        o = out[s];
+        const int cls = (o.flags & SO_WIDE_FLAG) ? 1 : 0;
+        b = cls * NBINS + bin_of(max(o.ie, o.je));
+    }
+    const uint32_t r = wave_grouped_inc(bin_fill, b, active);     // every lane of the wave
+    if (!active) return;
+    const uint32_t slot = bin_base[b] + r;
     ExecItem it;
     it.side = (int32_t)s;
     it.dstar = o.ie + o.je;
