@@ -100,6 +100,8 @@ struct fz_ctx {
     int64_t idx_keys = 0;               // target k-mers without N in the index
     hipStream_t xs[EXEC_STREAMS - 1] = {};   // executor streams besides the caller's
     hipEvent_t fork_ev = nullptr, join_ev[EXEC_STREAMS - 1] = {};
+    hipStream_t xw = nullptr;           // the wide-window executor and walker, beside the batches
+    hipEvent_t wide_ev = nullptr;
     hipEvent_t ev[12] = {};
     hipEvent_t kev[2] = {};             // brackets the dominant kernel
 };
@@ -586,8 +588,10 @@ int fz_create(fz_ctx **out, int device)
     }
     bool ok = hipEventCreateWithFlags(&ctx->fork_ev, hipEventDisableTiming) == hipSuccess;
     for (auto &e : ctx->join_ev) ok = ok && hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&ctx->wide_ev, hipEventDisableTiming) == hipSuccess;
     // default priority, no implicit ordering with the null stream
     for (auto &x : ctx->xs) ok = ok && hipStreamCreateWithFlags(&x, hipStreamNonBlocking) == hipSuccess;
+    ok = ok && hipStreamCreateWithFlags(&ctx->xw, hipStreamNonBlocking) == hipSuccess;
     if (!ok) {
         (void)hipSetDevice(prev);
         fz_destroy(ctx);
@@ -616,12 +620,15 @@ void fz_destroy(fz_ctx *ctx)
                       &ctx->sg_v, &ctx->sg_max, &ctx->rd_tmp};
     for (auto &x : ctx->xs)
         if (x) (void)hipStreamSynchronize(x);
+    if (ctx->xw) (void)hipStreamSynchronize(ctx->xw);
     for (DevBuf *b : bufs)
         if (b->p) (void)hipFree(b->p);
     for (auto &b : ctx->ptr_ws)
         if (b.p) (void)hipFree(b.p);
     for (auto &x : ctx->xs)
         if (x) (void)hipStreamDestroy(x);
+    if (ctx->xw) (void)hipStreamDestroy(ctx->xw);
+    if (ctx->wide_ev) (void)hipEventDestroy(ctx->wide_ev);
     if (ctx->fork_ev) (void)hipEventDestroy(ctx->fork_ev);
     for (auto &e : ctx->join_ev)
         if (e) (void)hipEventDestroy(e);
@@ -851,22 +858,28 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
             if (first[(size_t)b] > first[(size_t)b + 1]) first[(size_t)b] = first[(size_t)b + 1];
         S.n_batches = (uint64_t)nb;
         // batch b runs on stream b % nbuf with workspace b % nbuf; a
-        // workspace is reused only by later batches of its own stream
-        if (nbuf > 1) {
+        // workspace is reused only by later batches of its own stream.  When
+        // no workspace is reused (one batch per stream), the wide-window
+        // items (a few hundred long, low-occupancy waves) run on a stream of
+        // their own beside the batches, in their batch's workspace region
+        const bool wide_apart = nb <= nbuf && n_wide > 0;
+        if (nbuf > 1 || wide_apart) {
             HIP_OK(hipEventRecord(ctx->fork_ev, st));
             for (int k = 1; k < nbuf; ++k) HIP_OK(hipStreamWaitEvent(ctx->xs[k - 1], ctx->fork_ev, 0));
+            if (wide_apart) HIP_OK(hipStreamWaitEvent(ctx->xw, ctx->fork_ev, 0));
         }
         for (int64_t b = 0; b < nb; ++b) {
             const int64_t lo = first[(size_t)b], hi = first[(size_t)b + 1];
             if (hi <= lo) continue;
             const int kb = (int)(b % nbuf);
-            hipStream_t xst = kb == 0 ? st : ctx->xs[kb - 1];
+            const hipStream_t bst = kb == 0 ? st : ctx->xs[kb - 1];
             uint8_t *wsp = as<uint8_t>(ctx->ptr_ws[kb]);
             // class 1 (wide window) items come first in the list
             const int64_t segs[2][2] = {{std::max(lo, n_wide), hi}, {lo, std::min(hi, n_wide)}};
             for (int cls = 1; cls >= 0; --cls) {
                 const int64_t s0 = segs[cls][0], s1 = segs[cls][1];
                 if (s1 <= s0) continue;
+                const hipStream_t xst = (cls == 1 && wide_apart) ? ctx->xw : bst;
                 ExtendArgs xa = ea;
                 xa.exec = as<ExecItem>(ctx->items);
                 xa.exec_begin = s0;
@@ -895,6 +908,10 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         for (int k = 1; k < nbuf; ++k) {
             HIP_OK(hipEventRecord(ctx->join_ev[k - 1], ctx->xs[k - 1]));
             HIP_OK(hipStreamWaitEvent(st, ctx->join_ev[k - 1], 0));
+        }
+        if (wide_apart) {
+            HIP_OK(hipEventRecord(ctx->wide_ev, ctx->xw));
+            HIP_OK(hipStreamWaitEvent(st, ctx->wide_ev, 0));
         }
     }
     tm.mark();
