@@ -32,6 +32,8 @@ def test_struct_sizes_match_header():
     assert len(fz.SEED_FIELDS) == 7
     assert len(fz.HIT_FIELDS) == 12
     assert ctypes.sizeof(fz.fz_scoring) == 20
+    assert ctypes.sizeof(fz.fz_matrix) == 17 * 4           # sub[4][4] and n_score
+    assert ctypes.sizeof(fz.fz_seed_stats) == 11 * 4       # eleven float phase times
 
 
 def test_null_context_is_rejected():
