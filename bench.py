@@ -355,7 +355,7 @@ def bench_pipeline(a):
 def main():
     a = parse()
     if a.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d refused)" % a.gpus,
+        print("bench.py measures one GPU: the library has no multi-GPU path (--gpus %d refused)" % a.gpus,
               file=sys.stderr)
         sys.exit(2)
     if a.workload == "seeds":
