@@ -398,7 +398,8 @@ __device__ __forceinline__ void rle_push(uint32_t *runs, int64_t &n, uint32_t &c
 // anti-diagonals d - 127 .. d below the walk's current cell (i, j), lane l
 // loads rows d - 127 + l and d - 63 + l: header, and the pointer words the
 // walk can reach on the row (i never grows, and falls by at most one per
-// anti-diagonal), all loads in flight at once, into LDS.  The wave then
+// anti-diagonal: on row d - k, positions i - k .. i), all loads in flight at
+// once, into LDS.  The wave then
 // walks the chunk from LDS in uniform control flow; a run of diagonal moves
 // is taken in one round, lane l testing the l-th cell down the diagonal.
 constexpr int WALK_LANES = 64;
@@ -475,6 +476,11 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
                 const int plo = max(0, i - (d - dr)) - h[h2].ibase;
                 rw0[h2] = plo <= 0 ? 0 : (plo / C) * NW;
                 rnw[h2] = (dr <= d && rend[h2] > h[h2].off) ? (int)(rend[h2] - h[h2].off) : 0;
+                // words past the highest reachable position (i never grows)
+                // are never read: the row ends there for this chunk, and the
+                // clamped loads below repeat its last word (cache hits)
+                const int phi = i - h[h2].ibase;
+                rnw[h2] = min(rnw[h2], phi < 0 ? 0 : (phi / C) * NW + (phi % C) / 8 + 1);
                 rib[h2] = h[h2].ibase;
 #pragma unroll
                 for (int q = 0; q < WPR; ++q) {
