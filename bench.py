@@ -23,6 +23,8 @@ Workloads (seeded, synthetic; see smith_waterman_dp_amd/workloads.py):
                   through fz_extend_rounds; Mbp/s of target + query
 """
 import argparse
+import concurrent.futures as concurrent_futures
+import contextlib
 import json
 import os
 import sys
@@ -94,6 +96,9 @@ def parse():
                          "doubling schedule, of the first round)")
     ap.add_argument("--round-schedule", choices=["doubling", "fixed"], default="doubling",
                     help="doubling: each round twice the size of the one before; fixed: all rounds alike")
+    ap.add_argument("--strands", choices=["concurrent", "serial"], default="concurrent",
+                    help="pipeline: the two strands on two contexts and streams from two host threads, "
+                         "or one after the other on one context")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -297,17 +302,31 @@ def bench_pipeline(a):
     dev = torch.device("cuda:0")
     T = torch.from_numpy(w["target"]).to(dev)
     Q = torch.from_numpy(w["query"]).to(dev)
-    ctx = fz.Context(0)
+    concurrent = a.strands == "concurrent"
+    ctxs = [fz.Context(0), fz.Context(0)] if concurrent else [fz.Context(0)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()] if concurrent else [None]
+    torch.cuda.synchronize()
 
-    def step():
-        out = []
-        for rc in (False, True):
-            seeds, _ = ctx.find_seeds(T, Q, w["k"], w["flank"], query_rc=rc, reuse_index=rc)
+    def strand(rc):
+        # one strand: the seed stage, a seeded order, the rounds
+        k = 1 if (rc and concurrent) else 0
+        ctx, strm = ctxs[k], streams[k]
+        with torch.cuda.stream(strm) if strm is not None else contextlib.nullcontext():
+            seeds, _ = ctx.find_seeds(T, Q, w["k"], w["flank"], query_rc=rc, reuse_index=rc and not concurrent,
+                                      stream=strm)
             perm = torch.randperm(seeds.shape[0], generator=torch.Generator().manual_seed(7)).to(dev)
             h, c, st = ctx.extend_rounds(T, Q, seeds[perm], w["scoring"], w["ydrop"], 3000, a.round_size,
-                                         want_stats=True, query_rc=rc, doubling=a.round_doubling)
-            out.append((seeds.shape[0], h, st))
-        return out
+                                         want_stats=True, query_rc=rc, doubling=a.round_doubling, stream=strm)
+            if strm is not None:
+                strm.synchronize()
+        return seeds.shape[0], h, st
+
+    pool = concurrent_futures.ThreadPoolExecutor(2) if concurrent else None
+
+    def step():
+        if concurrent:
+            return list(pool.map(strand, (False, True)))
+        return [strand(False), strand(True)]
 
     for k in range(a.warmup):
         step()
@@ -339,7 +358,7 @@ def bench_pipeline(a):
            "vs_baseline": None, "dtype": "int32", "data": "synthetic",
            "config": {"workload": "chromosome_pipeline", "target_bp": int(w["target"].size),
                       "query_bp": int(w["query"].size), "k": w["k"], "flank": w["flank"], "round_size": a.round_size,
-                      "round_doubling": bool(a.round_doubling),
+                      "round_doubling": bool(a.round_doubling), "strands_run": a.strands,
                       "min_traceback_score": 3000, "cells_per_step": cells, "strands": per_strand,
                       "inspector_ms": round(kern_s * 1e3, 3)},
            "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(peak, 3), "unit": "TOP/s",
@@ -348,7 +367,10 @@ def bench_pipeline(a):
     if not a.no_cpu:
         print("[bench] CPU oracle sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_pipeline_baseline(w, a.cpu_seconds, a.round_size, a.round_doubling)
-    ctx.close()
+    if pool is not None:
+        pool.shutdown()
+    for c in ctxs:
+        c.close()
     print(json.dumps(out), flush=True)
 
 

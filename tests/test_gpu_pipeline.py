@@ -76,3 +76,36 @@ def test_chain_with_n_and_matrix(ctx):
     idx = np.nonzero(~gcov)[0]
     compare(gh, gc, oh[idx], ow, oo[idx], idx=idx, label="chain with N and matrix")
     log("%d seeds, covered %d" % (len(perm), gcov.sum()))
+
+
+def test_two_contexts_two_threads(ctx):
+    """Both strands at once, each on its own context and stream from its own
+    host thread, give exactly the results of running them one after the
+    other (the library keeps no state outside a context)."""
+    import concurrent.futures
+
+    w = W.chromosome(length=200_000, inv_min=20_000, inv_max=50_000, seed=16)
+    T = torch.from_numpy(w["target"]).to("cuda:0")
+    Q = torch.from_numpy(w["query"]).to("cuda:0")
+    torch.cuda.synchronize()
+
+    def chain(c, rc, strm):
+        with torch.cuda.stream(strm):
+            s, _ = c.find_seeds(T, Q, k=19, flank=32768, query_rc=rc, stream=strm)
+            h, cg, _ = c.extend_rounds(T, Q, s, w["scoring"], w["ydrop"], 3000, 64, query_rc=rc, doubling=True,
+                                       stream=strm)
+            strm.synchronize()
+        return s.cpu().numpy(), h.cpu().numpy(), cg.cpu().numpy()
+
+    serial = [chain(ctx, rc, torch.cuda.Stream()) for rc in (False, True)]
+    ctxs = [fz.Context(0), fz.Context(0)]
+    try:
+        with concurrent.futures.ThreadPoolExecutor(2) as pool:
+            par = list(pool.map(lambda a: chain(ctxs[a], bool(a), torch.cuda.Stream()), (0, 1)))
+    finally:
+        for c in ctxs:
+            c.close()
+    for x, y in zip(serial, par):
+        for u, v in zip(x, y):
+            assert np.array_equal(u, v)
+    log("strands: %d and %d seeds" % (len(serial[0][0]), len(serial[1][0])))
