@@ -192,7 +192,9 @@ const char *fz_last_error(const fz_ctx *ctx);
  * streams (three workspaces of a third each, each at least twice the
  * largest side's pointer rows); the executor works in batches that fit.
  * 0 restores the default: 70% of the device memory free at the call, at
- * most 200 GiB (allocated on first need and kept by the context). */
+ * most 200 GiB (allocated on first need and kept by the context).  Several
+ * contexts that work at once on one GPU should each be given a cap, since
+ * each default is taken from the memory free when that context asks. */
 int fz_set_pointer_workspace(fz_ctx *ctx, uint64_t bytes);
 
 /*
