@@ -639,3 +639,38 @@ def test_skewed_matrix_full_size_sampled(ctx):
     """The matrix benchmark batch (one million seeds, runs of N), sampled."""
     w = W.skewed_matrix()
     _full_size_sampled(ctx, w, 120, 4, "skewed matrix full")
+
+
+def test_matrix_wide_band(ctx):
+    """The 1024-position retry in matrix mode: no pruning on 700-base flanks
+    that hold N and an asymmetric matrix; every field against the oracle,
+    and the reverse strand of the same pair."""
+    rng = random.Random(18)
+    s = list("".join(rng.choice("ACGT") for _ in range(719)))
+    q = list(s)
+    for p in rng.sample(range(30, 719), 40):
+        q[p] = rng.choice("ACGTN")
+    s, q = "".join(s), "".join(q)
+    w = one_seed(s, q, 0, 0, 19)
+    w["scoring"] = W.matrix_scoring()
+    gh, gc, st = run_gpu(ctx, w, ydrop=fz.FZ_YDROP_INF)
+    oh, ow, oo = run_oracle(w, ydrop=oracle.YDROP_INF)
+    compare(gh, gc, oh, ow, oo, label="matrix wide")
+    assert st["n_overflow"] >= 1
+    wr = dict(w, query=np.frombuffer(oracle.revcomp(q).tobytes(), dtype=np.uint8).copy(), query_rc=True)
+    gh2, gc2, _ = run_gpu(ctx, wr, ydrop=fz.FZ_YDROP_INF)
+    oh2, ow2, oo2 = run_oracle(wr, ydrop=oracle.YDROP_INF)
+    compare(gh2, gc2, oh2, ow2, oo2, label="matrix wide rc")
+
+
+def test_matrix_local_strips(ctx):
+    """Local mode in matrix mode on windows taller than one strip (2,048
+    rows), so that the strip's last row is spilled and read back, with N."""
+    rng = random.Random(19)
+    w = W.local_pairs(n_pairs=6, length=2600, seed=20)
+    w["target"] = sprinkle_n(rng, w["target"], 0.01)
+    w["query"] = sprinkle_n(rng, w["query"], 0.01)
+    w["scoring"] = W.matrix_scoring()
+    gh, gc, _ = run_gpu(ctx, w, local=True)
+    oh, ow, oo = run_oracle(w, local=True)
+    compare(gh, gc, oh, ow, oo, local=True, label="matrix local strips")
