@@ -674,3 +674,27 @@ def test_matrix_local_strips(ctx):
     gh, gc, _ = run_gpu(ctx, w, local=True)
     oh, ow, oo = run_oracle(w, local=True)
     compare(gh, gc, oh, ow, oo, local=True, label="matrix local strips")
+
+
+WIDE_SC = dict(match=300, transition=-200, transversion=-400, gap_open=700, gap_extend=90)
+
+
+def test_wide_scores_wide_band_and_strips(ctx):
+    """Scores outside int8 (the general substitution path) in the
+    1024-position retry and in local mode across strips."""
+    rng = random.Random(21)
+    s = list("".join(rng.choice("ACGT") for _ in range(719)))
+    q = list(s)
+    for p in rng.sample(range(30, 719), 40):
+        q[p] = rng.choice("ACGT")
+    w = one_seed("".join(s), "".join(q), 0, 0, 19)
+    w["scoring"] = dict(WIDE_SC)
+    gh, gc, st = run_gpu(ctx, w, ydrop=fz.FZ_YDROP_INF)
+    oh, ow, oo = run_oracle(w, ydrop=oracle.YDROP_INF)
+    compare(gh, gc, oh, ow, oo, label="wide scores, wide band")
+    assert st["n_overflow"] >= 1
+    wl = W.local_pairs(n_pairs=4, length=2300, seed=22)
+    wl["scoring"] = dict(WIDE_SC)
+    gh, gc, _ = run_gpu(ctx, wl, local=True)
+    oh, ow, oo = run_oracle(wl, local=True)
+    compare(gh, gc, oh, ow, oo, local=True, label="wide scores, local strips")
