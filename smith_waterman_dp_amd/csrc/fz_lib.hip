@@ -838,7 +838,10 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         // the cap covers all workspaces; each holds at least two of the
         // largest sides
         uint64_t cap1 = std::max<uint64_t>(cap / EXEC_STREAMS, (uint64_t)2 * (uint64_t)max_item + 4096);
-        const int64_t ws = std::min<int64_t>((int64_t)cap1, total_ptr + 256);
+        // room for every side at once when the cap allows (one batch): a
+        // batch b holds the items whose offsets fall in [b*step, (b+1)*step),
+        // the last of which may reach max_item past the step
+        const int64_t ws = std::min<int64_t>((int64_t)cap1, total_ptr + max_item + 256);
         const int64_t step = std::max<int64_t>(1, ws - max_item);
         const int64_t nb = (total_ptr + step - 1) / step;
         const int nbuf = (int)std::min<int64_t>(nb, EXEC_STREAMS);
