@@ -243,7 +243,9 @@ int fz_extend_batch(fz_ctx *ctx,
  * round is extended exactly as fz_extend_batch extends it.  Seeds of one
  * round never suppress each other, and alignments without a CIGAR (score
  * not above min_traceback_score) suppress nothing.  A seed without columns,
- * or with columns outside the sequences, is never covered.
+ * or with columns outside the sequences, is never covered; coverage looks at
+ * the columns only, so a seed outside its window may still be covered
+ * (else it reports FZ_HIT_ESEED as in fz_extend_batch).
  *   arguments       as fz_extend_batch; flags must hold FZ_TRACEBACK and
  *                   not FZ_LOCAL, and may add FZ_ROUNDS_DOUBLING; sequences
  *                   shorter than 2^31 bases

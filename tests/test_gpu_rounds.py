@@ -185,3 +185,18 @@ def test_rounds_chromosome_full_size(ctx, chromosome_rounds_full, B, doubling):
     idx = np.sort(rng.choice(ext, min(40, ext.size), replace=False))
     oh, ow, oo = oracle.run(w["target"], w["query"], S[idx], w["scoring"], w["ydrop"], min_tb=w["min_tb"])
     compare(gh, gc, oh, ow, oo, idx=idx, label="chromosome rounds full")
+
+
+def test_rounds_with_invalid_and_empty_seeds(ctx):
+    """Seeds with no columns are never covered; seeds outside their windows
+    are covered like any other (coverage looks at the columns only) or, when
+    not, report FZ_HIT_ESEED as in a plain batch."""
+    w = W.homolog_rounds(length=12_000, seed=11)
+    S = w["seeds"].copy()
+    bad = S[:6].copy()
+    bad[:3, 3] = bad[:3, 0] + 1          # t_lo past the seed: invalid
+    bad[3:, 2] = 0                       # no columns
+    w = dict(w, seeds=np.concatenate([S[:4], bad, S[4:]]))
+    gh, gcov = check_against_oracle(ctx, w, 3, "rounds with invalid seeds", doubling=True)
+    assert not gcov[7:10].any()
+    assert (gh[4:7, 1] & (fz.FZ_HIT_ESEED | fz.FZ_HIT_COVERED)).all()
