@@ -157,7 +157,7 @@ enum {
 
 enum {
     FZ_OK = 0,
-    FZ_EINVAL = -1,                /* bad argument, or a byte other than ACGTacgt */
+    FZ_EINVAL = -1,                /* bad argument, or a byte the call does not accept */
     FZ_ENOMEM = -2,                /* device allocation failed */
     FZ_EDEVICE = -3,               /* HIP runtime error */
     FZ_EBAND = -4                  /* (reserved) */
