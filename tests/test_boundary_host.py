@@ -57,3 +57,11 @@ def test_create_bad_device_fails_cleanly():
     h = ctypes.c_void_p()
     assert lib.fz_create(ctypes.byref(h), 10_000) != fz.FZ_OK
     assert not h.value
+
+
+def test_build_lists_every_source():
+    from smith_waterman_dp_amd import build
+    csrc = os.path.join(ROOT, "smith_waterman_dp_amd", "csrc")
+    have = sorted(f for f in os.listdir(csrc) if f.endswith(".hpp"))
+    assert sorted(build.HEADERS) == have
+    assert sorted(build.SOURCES) == sorted(f for f in os.listdir(csrc) if f.endswith(".hip"))
