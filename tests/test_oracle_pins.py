@@ -567,6 +567,27 @@ def test_n_needs_a_matrix():
     assert r["status"] == 0 and r["score"] == 3 * SC["match"] - 7 and (r["ie"], r["je"]) == (4, 4)
 
 
+def test_matrix_orientation_closed_form():
+    """sub[a][b] scores target base a against query base b.  With an
+    asymmetric matrix the two orientations give different hand-derived
+    results; the transpose-symmetry pin alone would pass a consistently
+    transposed lookup."""
+    m = [[91, 50, -31, -123],
+         [-200, 91, -123, -31],
+         [-31, -123, 91, -123],
+         [-123, -31, -123, 91]]
+    sc = dict(matrix=m, n_score=-100, gap_open=400, gap_extend=30)
+    # target A against query C scores +50 per column: 4 * 50
+    r = oracle.side("AAAA", "CCCC", sc, oracle.YDROP_INF)
+    assert (r["score"], r["ie"], r["je"], r["ops"]) == (200, 4, 4, "MMMM")
+    # target C against query A scores -200, a gap 430: the empty extension wins
+    r = oracle.side("CCCC", "AAAA", sc, oracle.YDROP_INF)
+    assert (r["score"], r["ie"], r["je"], r["ops"]) == (0, 0, 0, "")
+    # one N in the target among matches: 3 * 91 + n_score
+    r = oracle.side("ANAA", "ACAA", sc, oracle.YDROP_INF)
+    assert (r["score"], r["ie"], r["je"]) == (3 * 91 - 100, 4, 4)
+
+
 # ---- covered-seed suppression by rounds --------------------------------
 
 def test_rounds_single_round_equals_run():
