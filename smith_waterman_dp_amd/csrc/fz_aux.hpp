@@ -497,6 +497,29 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
                     wl[h2 * WALK_LANES + lane][q] = rw0[h2] + q < rnw[h2] ? v[h2][q] : 0u;
         }
         __syncthreads();
+        // Length of a run of one kind of move from the current cell (i, j)
+        // on chunk row r: lane l tests cell (i - l di, j - l dj), on row
+        // r - l (di + dj), for the pointer bit; the run ends at the first
+        // cell without it, outside the chunk or the matrix, or (with
+        // stop_at_origin) at (0,0).  Row r' has its fields in lane r' % 64.
+        auto run_of = [&](int r, int di, int dj, uint32_t bit, bool stop_at_origin) -> int {
+            const int rl = r - (di + dj) * lane;
+            const int sl = rl < 0 ? 0 : rl;
+            const int src_lane = sl % WALK_LANES;
+            const int ib0 = __shfl(rib[0], src_lane), ib1 = __shfl(rib[1], src_lane);
+            const int w00 = __shfl(rw0[0], src_lane), w01 = __shfl(rw0[1], src_lane);
+            const int nw0 = __shfl(rnw[0], src_lane), nw1 = __shfl(rnw[1], src_lane);
+            const bool lo_half = sl < WALK_LANES;
+            const int lib = lo_half ? ib0 : ib1, lw0 = lo_half ? w00 : w01, lnw = lo_half ? nw0 : nw1;
+            const int il = i - di * lane, jl = j - dj * lane;
+            bool m = rl >= 0 && il >= 0 && jl >= 0 && !(stop_at_origin && il == 0 && jl == 0);
+            if (m) {
+                const uint32_t xl = nib_at(rl, il, lib, lw0, lnw);
+                m = xl <= 15u && (xl & bit);
+            }
+            const uint64_t stop = ~ballot(m);
+            return stop ? ctz64(stop) : WALK_LANES;
+        };
         while (!(st == 0 && i == 0 && j == 0)) {
             const int dd = i + j;
             if (dd < dlo) break;
@@ -510,42 +533,24 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
                 bad = true;
                 break;
             }
-            if (st == 1 && (x & PTR_EXT_I)) {
-                emit(1, 1);
-                --j;
-                ++moves;
-            } else if (st == 2 && (x & PTR_EXT_D)) {
-                emit(2, 1);
-                --i;
-                ++moves;
+            // in a gap, the run of cells whose pointer extends it (lane 0
+            // is this cell, so the run is empty exactly when the gap ends)
+            const int g = st == 0 ? 0 : run_of(r, st == 2 ? 1 : 0, st == 1 ? 1 : 0, st == 1 ? PTR_EXT_I : PTR_EXT_D,
+                                               false);
+            if (g > 0) {
+                emit((uint32_t)st, (uint32_t)g);
+                if (st == 1) j -= g;
+                else i -= g;
+                moves += g;
             } else {
                 // the gap (if any) ends here: this cell is taken in S
                 st = 0;
                 if (i == 0 && j == 0) break;
                 const uint32_t src = ptr_src(x);
                 if (src == 0) {
-                    // diagonal moves from here: lane l tests cell
-                    // (i - l, j - l) on row r - 2l; the run ends at the
-                    // first cell that is not a diagonal move, at the
-                    // origin, or at the chunk's end
-                    const int rl = r - 2 * lane;
-                    const int sl = rl < 0 ? 0 : rl;
-                    // row sl's fields: fetch both of lane sl % 64's rows,
-                    // pick here
-                    const int src_lane = sl % WALK_LANES;
-                    const int ib0 = __shfl(rib[0], src_lane), ib1 = __shfl(rib[1], src_lane);
-                    const int w00 = __shfl(rw0[0], src_lane), w01 = __shfl(rw0[1], src_lane);
-                    const int nw0 = __shfl(rnw[0], src_lane), nw1 = __shfl(rnw[1], src_lane);
-                    const bool lo_half = sl < WALK_LANES;
-                    const int lib = lo_half ? ib0 : ib1, lw0 = lo_half ? w00 : w01, lnw = lo_half ? nw0 : nw1;
-                    const int il = i - lane, jl = j - lane;
-                    bool m = rl >= 0 && il >= 0 && jl >= 0 && !(il == 0 && jl == 0);
-                    if (m) {
-                        const uint32_t xl = nib_at(rl, il, lib, lw0, lnw);
-                        m = xl <= 15u && (xl & PTR_DIAG);
-                    }
-                    const uint64_t stop = ~ballot(m);
-                    const int f = stop ? ctz64(stop) : WALK_LANES;   // >= 1: lane 0 is this cell
+                    // diagonal moves from here, up to the first cell that is
+                    // not a diagonal move, the origin, or the chunk's end
+                    const int f = run_of(r, 1, 1, PTR_DIAG, true);
                     if (f == 0) {
                         bad = true;     // cannot happen; never loop without progress
                         break;
