@@ -218,6 +218,104 @@ def test_band_bookkeeping_vs_full_matrix(case):
             assert r["S"][i, j] == S[i][j], (i, j)
 
 
+def canonical_cells_from_live(live, m, n):
+    """Sum of |R_d| rebuilt from a live set alone (FastZ section 2.1, Fig. 3a,
+    in the completed-scores form of section 3.4): R_0 = {(0,0)}; for d >= 1,
+    R_d is the hull of the cells of diagonal d, inside the matrix, that have
+    a live predecessor -- (i, j-1) or (i-1, j) on d-1, (i-1, j-1) on d-2;
+    the run ends at the first empty R_d.  No band bookkeeping: every cell of
+    every diagonal is tested against the live set."""
+    total = 1
+    for d in range(1, m + n + 2):
+        cand = [i for i in range(max(0, d - n), min(m, d) + 1)
+                if (i, d - i - 1) in live or (i - 1, d - i) in live or (i - 1, d - i - 1) in live]
+        if not cand:
+            break
+        total += max(cand) - min(cand) + 1
+    return total
+
+
+def _mutated(rng, a, edits):
+    b = list(a)
+    for _ in range(edits):
+        p = rng.randrange(len(b))
+        op = rng.random()
+        if op < 0.4:
+            b.insert(p, rng.choice("ACGT"))
+        elif op < 0.8 and len(b) > 1:
+            del b[p]
+        else:
+            b[p] = rng.choice("ACGT")
+    return "".join(b)
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_cell_count_vs_full_matrix_live_set(case):
+    """The oracle's canonical cell count (the GCUPS numerator) equals the
+    count rebuilt from the live set of the unbanded full-matrix y-drop DP."""
+    rng = random.Random(4200 + case)
+    m, n = rng.randint(1, 60), rng.randint(1, 60)
+    a = rand_seq(rng, m)
+    b = _mutated(rng, a, rng.randint(1, 8)) if case % 2 else rand_seq(rng, n)
+    ydrop = [0, 30, 120, 500, 900, 2000, 9400][case % 7]
+    sc = SC if case % 3 else rand_scoring(rng)
+    r = oracle.side(a, b, sc, ydrop)
+    S = full_matrix_ydrop(a, b, sc, ydrop)
+    live = {(i, j) for i in range(len(a) + 1) for j in range(len(b) + 1) if S[i][j] is not None}
+    assert r["cells"] == canonical_cells_from_live(live, len(a), len(b)), (a, b, sc, ydrop)
+
+
+@pytest.mark.parametrize("case", range(60))
+def test_cell_count_vs_enumeration(case):
+    """The same count from the live set of exhaustive path enumeration
+    (tiny pairs, several y-drops)."""
+    rng = random.Random(5100 + case)
+    alphabet = ["ACGT", "AC", "AG", "A"][case % 4]
+    a = rand_seq(rng, rng.randint(0, 5), alphabet)
+    b = rand_seq(rng, rng.randint(0, 5), alphabet)
+    sc = SC if case % 2 == 0 else rand_scoring(rng)
+    ydrop = [0, 100, 300, 600, 1500][case % 5]
+    r = oracle.side(a, b, sc, ydrop)
+    br = bf.extension_brute(a, b, sc, ydrop)
+    assert r["cells"] == canonical_cells_from_live(br["live"], len(a), len(b)), (a, b, sc, ydrop)
+
+
+def load_cell_counts():
+    rows = []
+    with open(os.path.join(HERE, "golden", "cell_counts.tsv")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            p = line.rstrip("\n").split("\t")
+            rows.append((p[0], p[1], p[2], int(p[3]), int(p[4]), int(p[5]), int(p[6]), int(p[7])))
+    return rows
+
+
+@pytest.mark.parametrize("row", load_cell_counts(), ids=lambda r: r[0])
+def test_cell_count_closed_forms(row):
+    """Hand-derived counts (tests/golden/cell_counts.tsv, derivations there)."""
+    name, a, b, ydrop, cells, score, ie, je = row
+    r = oracle.side(a, b, SC, ydrop)
+    assert (r["cells"], r["score"], r["ie"], r["je"]) == (cells, score, ie, je)
+    assert canonical_cells_from_live_of(a, b, ydrop) == cells
+
+
+def canonical_cells_from_live_of(a, b, ydrop):
+    S = full_matrix_ydrop(a, b, SC, ydrop)
+    live = {(i, j) for i in range(len(a) + 1) for j in range(len(b) + 1) if S[i][j] is not None}
+    return canonical_cells_from_live(live, len(a), len(b))
+
+
+@pytest.mark.parametrize("ell", [0, 1, 2, 17, 200])
+def test_cell_count_identical_ydrop0(ell):
+    """Identical flanks with ydrop 0: 1 + 3 * ell cells (derivation in
+    tests/golden/cell_counts.tsv)."""
+    rng = random.Random(ell)
+    a = rand_seq(rng, ell)
+    r = oracle.side(a, a, SC, 0)
+    assert (r["cells"], r["score"]) == (1 + 3 * ell, 91 * ell)
+
+
 # ------------------------------------------------------------- local mode --
 
 def textbook_sw_linear(a, b, sc):
@@ -622,6 +720,26 @@ def test_rounds_hand_example():
     assert not (h3["status"] & oracle.STATUS_COVERED).any()
 
 
+def test_rounds_seed_outside_sequences_never_covered():
+    """A seed whose columns run past an end of the sequences is not covered,
+    even where its columns inside overlap an earlier alignment: it is
+    extended as a plain batch extends it, which reports the seed invalid.
+    A seed inside the sequences on the same cells is covered."""
+    rng = random.Random(5)
+    T = rand_seq(rng, 400)
+    Q = T
+    seeds = np.array([[50, 50, 19, 0, 400, 0, 400],        # aligns 400M
+                      [390, 390, 19, 0, 400, 0, 400],      # columns 390..408: past both ends
+                      [-5, -5, 19, 0, 400, 0, 400],        # columns -5..13: before both starts
+                      [380, 380, 19, 0, 400, 0, 400]], dtype=np.int64)   # inside, on the 400M cells
+    h, w, o = oracle.extend_rounds(T, Q, seeds, SC, 9400, 0, 1)
+    assert oracle.cigar_string(w[o[0]:o[0] + h["n_runs"][0]]) == "400M"
+    for k in (1, 2):
+        assert not h["status"][k] & oracle.STATUS_COVERED, k
+        assert h["status"][k] & oracle.STATUS_ESEED, k
+    assert h["status"][3] == oracle.STATUS_COVERED
+
+
 def _cells_of(T, Q, hit, words):
     """Every aligned (t, q) cell of one alignment, read from its text CIGAR
     one column at a time."""
@@ -670,7 +788,10 @@ def test_rounds_coverage_by_cells(round_size, doubling):
         this_round = set()
         for k in range(r0, r1):
             t, q, L = (int(x) for x in S[k, :3])
-            cov = any((t + i, q + i) in earlier for i in range(L))
+            # a seed's columns are matrix cells only when they all lie inside
+            # the two sequences; a seed without such columns is never covered
+            inside = L >= 1 and t >= 0 and q >= 0 and t + L <= len(w["target"]) and q + L <= len(w["query"])
+            cov = inside and any((t + i, q + i) in earlier for i in range(L))
             assert bool(h["status"][k] & oracle.STATUS_COVERED) == cov, k
             if cov:
                 n_cov += 1
