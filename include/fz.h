@@ -231,6 +231,32 @@ int fz_extend_batch(fz_ctx *ctx,
                     fz_stats *stats, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * score-only form of fz_extend_batch (no FZ_TRACEBACK, no FZ_LOCAL) that
+ * allocates nothing.  Every buffer its kernels use beyond the caller's
+ * inputs and outputs lives in a static device array of
+ * FZ_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until
+ * the process ends; the call takes at most FZ_NOALLOC_MAX_SEEDS seeds and
+ * sequences of at most FZ_NOALLOC_MAX_BASES bases each, and rejects larger
+ * inputs with FZ_EINVAL.  Arguments, results (hits, and stats' cells,
+ * n_sides, n_overflow and ms_main) and errors are those of fz_extend_batch
+ * without traceback; flags may hold FZ_STATS and FZ_QUERY_RC.  All calls
+ * on one GPU share that GPU's array: calls that overlap in time on one GPU
+ * (other streams, other contexts, other threads) race and must not be
+ * made.  The call returns after its stream has run it.
+ */
+#define FZ_NOALLOC_MAX_SEEDS 65536
+#define FZ_NOALLOC_MAX_BASES 4194304
+#define FZ_NOALLOC_SCRATCH_BYTES 41943040
+int fz_extend_batch_noalloc(fz_ctx *ctx,
+                            const uint8_t *target, uint64_t target_len,
+                            const uint8_t *query, uint64_t query_len,
+                            const fz_seed *seeds, uint64_t n_seeds,
+                            const fz_scoring *scoring, const fz_matrix *matrix, int32_t ydrop,
+                            uint32_t flags, fz_hit *hits, fz_stats *stats, void *stream);
+
+/*
  * Covered-seed suppression by rounds.  FastZ (SC'21) section 2.1 describes
  * LASTZ ending a seed extension that reaches an alignment found earlier;
  * section 3.4 explains why FastZ drops that rule (it orders the

@@ -23,6 +23,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -71,6 +72,45 @@ constexpr int C_WIDE = 16;              // window 1024 positions
 constexpr int LOCAL_RL = 32;            // rows per lane in local mode
 
 }  // namespace
+
+// ---- static scratch of fz_extend_batch_noalloc --------------------------
+// For callers that cannot allocate device memory (code under graph capture,
+// tight serving loops): every buffer that call's kernels use beyond the
+// caller's inputs and outputs lives in one file-scope device array, sized
+// for at most FZ_NOALLOC_MAX_SEEDS seeds and sequences of at most
+// FZ_NOALLOC_MAX_BASES bases each.  Each GPU the library runs on holds its
+// own copy until the process ends.  In host code `scratch` only names the
+// symbol: its device address comes from hipGetSymbolAddress, taken once per
+// device (fz_create, with that device current) and kept in noalloc_base[].
+namespace {
+
+constexpr int64_t NA_SEQ = FZ_NOALLOC_MAX_BASES + 2 * PAD + 64;      // one packed copy
+constexpr int64_t NA_SIDES = 2 * (int64_t)FZ_NOALLOC_MAX_SEEDS;
+constexpr int64_t na_up(int64_t x) { return (x + 255) & ~(int64_t)255; }
+// byte offsets of the regions, each 256-aligned
+constexpr int64_t NA_TF = 0;
+constexpr int64_t NA_TR = NA_TF + na_up(NA_SEQ);
+constexpr int64_t NA_QF = NA_TR + na_up(NA_SEQ);
+constexpr int64_t NA_QR = NA_QF + na_up(NA_SEQ);
+constexpr int64_t NA_TASKS = NA_QR + na_up(NA_SEQ);
+constexpr int64_t NA_INFO = NA_TASKS + na_up(NA_SIDES * (int64_t)sizeof(SideTask));
+constexpr int64_t NA_OUT = NA_INFO + na_up(FZ_NOALLOC_MAX_SEEDS * (int64_t)sizeof(SeedInfo));
+constexpr int64_t NA_EAGER = NA_OUT + na_up(NA_SIDES * (int64_t)sizeof(SideOut));
+constexpr int64_t NA_OVL0 = NA_EAGER + na_up(NA_SIDES * EAGER_OPS);
+constexpr int64_t NA_OVL1 = NA_OVL0 + na_up(NA_SIDES * 4);
+constexpr int64_t NA_TRACE = NA_OVL1 + na_up(NA_SIDES * 4);
+constexpr int64_t NA_RUNCAP = NA_TRACE + na_up(NA_SIDES * 4);
+constexpr int64_t NA_COUNTERS = NA_RUNCAP + na_up(NA_SIDES * 8);
+constexpr int64_t NA_END = NA_COUNTERS + na_up((int64_t)sizeof(Counters));
+static_assert(NA_END <= FZ_NOALLOC_SCRATCH_BYTES, "noalloc scratch layout exceeds its array");
+
+constexpr int NA_MAX_DEVICES = 64;
+std::mutex noalloc_mu;
+uint8_t *noalloc_base[NA_MAX_DEVICES] = {};
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[FZ_NOALLOC_SCRATCH_BYTES];
 
 struct fz_ctx {
     int device = 0;
@@ -572,6 +612,21 @@ int fz_create(fz_ctx **out, int device)
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, device) == hipSuccess && prop.multiProcessorCount > 0)
         ctx->n_cu = prop.multiProcessorCount;
+    {
+        // this device's copy of the no-allocation scratch array, once per
+        // device, with the device current
+        std::lock_guard<std::mutex> lk(noalloc_mu);
+        if (device < NA_MAX_DEVICES && !noalloc_base[device]) {
+            void *p = nullptr;
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+                (void)hipGetLastError();
+                (void)hipSetDevice(prev);
+                fz_destroy(ctx);
+                return FZ_EDEVICE;
+            }
+            noalloc_base[device] = reinterpret_cast<uint8_t *>(p);
+        }
+    }
     for (auto &e : ctx->kev) {
         if (hipEventCreate(&e) != hipSuccess) {
             (void)hipSetDevice(prev);
@@ -962,6 +1017,111 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     return FZ_OK;
 }
 
+// fz_extend_batch_noalloc: the score-only extension path (pack, setup,
+// inspector, wide retry, combine) with every buffer carved from this
+// device's static scratch array.  No device allocation and no allocating
+// library call; the one read-back (the overflow count) goes to host stack
+// memory.
+static int noalloc_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const uint8_t *query, uint64_t qlen,
+                        const fz_seed *seeds, uint64_t n_seeds, const fz_scoring *scoring, const fz_matrix *matrix,
+                        int32_t ydrop, uint32_t flags, fz_hit *hits, fz_stats *stats, hipStream_t st)
+{
+    int rc = check_args(ctx, target, tlen, query, qlen, seeds, n_seeds, scoring, matrix, ydrop, flags, hits);
+    if (rc != FZ_OK) return rc;
+    if (flags & (FZ_TRACEBACK | FZ_LOCAL))
+        return fail(ctx, FZ_EINVAL, "fz_extend_batch_noalloc is score-only: FZ_TRACEBACK and FZ_LOCAL are not accepted");
+    if (n_seeds > (uint64_t)FZ_NOALLOC_MAX_SEEDS)
+        return fail(ctx, FZ_EINVAL, "fz_extend_batch_noalloc takes at most %d seeds (got %llu)", FZ_NOALLOC_MAX_SEEDS,
+                    (unsigned long long)n_seeds);
+    if (tlen > (uint64_t)FZ_NOALLOC_MAX_BASES || qlen > (uint64_t)FZ_NOALLOC_MAX_BASES)
+        return fail(ctx, FZ_EINVAL, "fz_extend_batch_noalloc takes sequences of at most %d bases (got %llu and %llu)",
+                    FZ_NOALLOC_MAX_BASES, (unsigned long long)tlen, (unsigned long long)qlen);
+    uint8_t *base = ctx->device < NA_MAX_DEVICES ? noalloc_base[ctx->device] : nullptr;
+    if (!base) return fail(ctx, FZ_EDEVICE, "no scratch address for device %d", ctx->device);
+    fz_stats S;
+    memset(&S, 0, sizeof S);
+    const int64_t n = (int64_t)n_seeds;
+    if (n == 0) {
+        if (stats) *stats = S;
+        return FZ_OK;
+    }
+    const Scoring sc = make_scoring(scoring, matrix, ydrop);
+    const int64_t NT = (int64_t)tlen + 2 * PAD, NQ = (int64_t)qlen + 2 * PAD;
+    uint8_t *Tf = base + NA_TF, *Tr = base + NA_TR, *Qf = base + NA_QF, *Qr = base + NA_QR;
+    SideTask *tasks = reinterpret_cast<SideTask *>(base + NA_TASKS);
+    SeedInfo *info = reinterpret_cast<SeedInfo *>(base + NA_INFO);
+    SideOut *out = reinterpret_cast<SideOut *>(base + NA_OUT);
+    Counters *dc = reinterpret_cast<Counters *>(base + NA_COUNTERS);
+    // the counters keep the last call's values: clear them (a kernel, not a memset)
+    rc = zero(ctx, dc, sizeof(Counters), st);
+    if (rc) return rc;
+    const int mxr = sc.mode == SUB_MATRIX ? 1 : 0;
+    pack_kernel<<<std::min<int64_t>(blocks_for(NT, 256), 8192), 256, 0, st>>>(target, (int64_t)tlen, Tf, Tr, NT,
+                                                                                &dc->err, 0, mxr);
+    HIP_OK(hipGetLastError());
+    pack_kernel<<<std::min<int64_t>(blocks_for(NQ, 256), 8192), 256, 0, st>>>(
+        query, (int64_t)qlen, Qf, Qr, NQ, &dc->err, (flags & FZ_QUERY_RC) ? 1 : 0, 2 * mxr);
+    HIP_OK(hipGetLastError());
+    setup_kernel<<<blocks_for(n, 256), 256, 0, st>>>(seeds, n, (int64_t)tlen, (int64_t)qlen, Tf, Tr, Qf, Qr, NT, NQ,
+                                                      sc, tasks, info);
+    HIP_OK(hipGetLastError());
+    const int64_t nsides = 2 * n;
+    ExtendArgs ea = {};
+    ea.tasks = tasks;
+    ea.list = nullptr;
+    ea.nlist = (int32_t)nsides;
+    ea.out = out;
+    ea.eager_ops = base + NA_EAGER;
+    ea.overflow_list = reinterpret_cast<int32_t *>(base + NA_OVL0);
+    ea.overflow_count = &dc->overflow_count[0];
+    ea.exec_cells = &dc->exec_cells;
+    ea.result_flags = 0;
+    ea.sc = sc;
+    HIP_OK(hipEventRecord(ctx->kev[0], st));
+    rc = launch_extend<C_STD, false>(ctx, ea, nsides, st);
+    if (rc) return rc;
+    HIP_OK(hipEventRecord(ctx->kev[1], st));
+    Counters hc;
+    HIP_OK(hipMemcpyAsync(&hc, dc, sizeof(Counters), hipMemcpyDeviceToHost, st));
+    HIP_OK(hipStreamSynchronize(st));
+    if (hc.err & 1u) return fail(ctx, FZ_EINVAL, "%s", bad_byte_msg(sc));
+    if (hc.overflow_count[0] > 0) {
+        ExtendArgs wa = ea;
+        wa.list = reinterpret_cast<int32_t *>(base + NA_OVL0);
+        wa.nlist = (int32_t)hc.overflow_count[0];
+        wa.overflow_list = reinterpret_cast<int32_t *>(base + NA_OVL1);
+        wa.overflow_count = &dc->overflow_count[1];
+        wa.result_flags = SO_WIDE_FLAG;
+        rc = launch_extend<C_WIDE, false>(ctx, wa, wa.nlist, st);
+        if (rc) return rc;
+    }
+    CombineArgs ca;
+    ca.seeds = seeds;
+    ca.n = n;
+    ca.out = out;
+    ca.info = info;
+    ca.min_tb = 0;
+    ca.traceback = 0;
+    ca.hits = hits;
+    ca.side_trace = reinterpret_cast<int32_t *>(base + NA_TRACE);
+    ca.run_cap = reinterpret_cast<int64_t *>(base + NA_RUNCAP);
+    ca.bin_count = dc->bin_count;
+    ca.max_ptr = &dc->max_ptr;
+    ca.cells_total = &dc->totals[3];
+    combine_kernel<<<blocks_for(n, 256), 256, 0, st>>>(ca);
+    HIP_OK(hipGetLastError());
+    if (stats) {
+        HIP_OK(hipMemcpyAsync(&hc, dc, sizeof(Counters), hipMemcpyDeviceToHost, st));
+        HIP_OK(hipStreamSynchronize(st));
+        S.n_sides = (uint64_t)nsides;
+        S.cells = (uint64_t)hc.totals[3];
+        S.n_overflow = hc.overflow_count[0];
+        (void)hipEventElapsedTime(&S.ms_main, ctx->kev[0], ctx->kev[1]);
+        *stats = S;
+    }
+    return FZ_OK;
+}
+
 // Grow b to at least `bytes`, keeping its first `keep` bytes.
 static int grow_keep(fz_ctx *ctx, DevBuf &b, size_t bytes, size_t keep, hipStream_t st)
 {
@@ -1177,6 +1337,28 @@ int fz_extend_batch(fz_ctx *ctx, const uint8_t *target, uint64_t target_len, con
     }
     const int rc = extend_impl(ctx, target, target_len, query, query_len, seeds, n_seeds, scoring, matrix, ydrop,
                                min_traceback_score, flags, hits, cigar, cigar_words, stats, (hipStream_t)stream);
+    if (prev != ctx->device) (void)hipSetDevice(prev);
+    return rc;
+}
+
+int fz_extend_batch_noalloc(fz_ctx *ctx, const uint8_t *target, uint64_t target_len, const uint8_t *query,
+                            uint64_t query_len, const fz_seed *seeds, uint64_t n_seeds, const fz_scoring *scoring,
+                            const fz_matrix *matrix, int32_t ydrop, uint32_t flags, fz_hit *hits, fz_stats *stats,
+                            void *stream)
+{
+    if (!ctx) return FZ_EINVAL;
+    ctx->err.clear();
+    int prev = 0;
+    if (hipGetDevice(&prev) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ctx, FZ_EDEVICE, "hipGetDevice failed");
+    }
+    if (prev != ctx->device && hipSetDevice(ctx->device) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ctx, FZ_EDEVICE, "hipSetDevice(%d) failed", ctx->device);
+    }
+    const int rc = noalloc_impl(ctx, target, target_len, query, query_len, seeds, n_seeds, scoring, matrix, ydrop,
+                                flags, hits, stats, (hipStream_t)stream);
     if (prev != ctx->device) (void)hipSetDevice(prev);
     return rc;
 }

@@ -18,6 +18,7 @@ FZ_HIT_TRACED, FZ_HIT_EAGER_LEFT, FZ_HIT_EAGER_RIGHT = 1, 2, 4
 FZ_HIT_BELOW_MIN, FZ_HIT_EBAND, FZ_HIT_ESEED, FZ_HIT_ERANGE = 8, 16, 32, 64
 FZ_HIT_COVERED = 128
 FZ_YDROP_INF = 2147483647
+FZ_NOALLOC_MAX_SEEDS, FZ_NOALLOC_MAX_BASES = 65536, 4194304
 
 HIT_FIELDS = ["score", "status", "t_begin", "t_end", "q_begin", "q_end", "cigar_off", "cigar_len",
               "cells", "score_left", "score_right", "bin"]
@@ -25,7 +26,7 @@ SEED_FIELDS = ["t_pos", "q_pos", "seed_len", "t_lo", "t_hi", "q_lo", "q_hi"]
 
 # every symbol include/fz.h declares
 EXPORTS = ["fz_create", "fz_destroy", "fz_last_error", "fz_set_pointer_workspace", "fz_extend_batch",
-           "fz_extend_rounds", "fz_find_seeds", "fz_copy_seeds", "fz_copy_cigar"]
+           "fz_extend_rounds", "fz_find_seeds", "fz_copy_seeds", "fz_copy_cigar", "fz_extend_batch_noalloc"]
 
 
 class fz_scoring(ctypes.Structure):
@@ -111,6 +112,10 @@ def load_library(path=LIB_PATH):
                                      ctypes.POINTER(fz_stats), P]
     lib.fz_copy_cigar.restype = ctypes.c_int
     lib.fz_copy_cigar.argtypes = [P, P, u64, P]
+    lib.fz_extend_batch_noalloc.restype = ctypes.c_int
+    lib.fz_extend_batch_noalloc.argtypes = [P, P, u64, P, u64, P, u64, ctypes.POINTER(fz_scoring),
+                                            ctypes.POINTER(fz_matrix), i32, ctypes.c_uint32, P,
+                                            ctypes.POINTER(fz_stats), P]
     lib.fz_find_seeds.restype = ctypes.c_int
     lib.fz_find_seeds.argtypes = [P, P, u64, P, u64, ctypes.c_uint32, i64, ctypes.c_uint32, ctypes.POINTER(P),
                                   ctypes.POINTER(u64), ctypes.POINTER(u64), ctypes.POINTER(fz_seed_stats), P]
@@ -202,6 +207,35 @@ def fz_extend_batch(ctx, target, query, seeds, scoring, ydrop, min_traceback_sco
     return hits, cigar, (st.as_dict() if want_stats else None)
 
 
+def fz_extend_batch_noalloc(ctx, target, query, seeds, scoring, ydrop, flags=0, stream=None, want_stats=False):
+    """The score-only extension without device allocation
+    (fz_extend_batch_noalloc): arguments as fz_extend_batch; the library
+    allocates nothing, the caller's hits tensor is allocated here by torch.
+    Returns (hits, stats)."""
+    import torch
+    lib = load_library()
+    for name, t, dt in (("target", target, torch.uint8), ("query", query, torch.uint8), ("seeds", seeds, torch.int64)):
+        if not t.is_cuda or t.dtype != dt or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous %s CUDA tensor" % (name, dt))
+    if seeds.dim() != 2 or seeds.shape[1] != 7:
+        raise ValueError("seeds must have shape (n, 7)")
+    n = seeds.shape[0]
+    hits = torch.empty((n, len(HIT_FIELDS)), dtype=torch.int64, device=seeds.device)
+    sc = fz_scoring(int(scoring.get("match", 0)), int(scoring.get("transition", 0)),
+                    int(scoring.get("transversion", 0)), int(scoring["gap_open"]), int(scoring["gap_extend"]))
+    mx = _matrix_of(scoring)
+    st = fz_stats()
+    if want_stats:
+        flags |= FZ_STATS
+    rc = lib.fz_extend_batch_noalloc(ctx, target.data_ptr(), target.numel(), query.data_ptr(), query.numel(),
+                                     seeds.data_ptr(), n, ctypes.byref(sc),
+                                     ctypes.byref(mx) if mx is not None else None,
+                                     int(min(int(ydrop), FZ_YDROP_INF)), int(flags),
+                                     hits.data_ptr() if n else None, ctypes.byref(st), _stream_handle(stream))
+    _check(ctx, rc)
+    return hits, (st.as_dict() if want_stats else None)
+
+
 def fz_find_seeds(ctx, target, query, k=19, flank=32768, flags=0, stream=None, want_stats=False):
     """The seed stage: shared k-mers of target and query (of the query's
     reverse complement with FZ_QUERY_RC), one per diagonal run unless
@@ -283,6 +317,11 @@ class Context:
         flags = ((0 if dedup else FZ_SEEDS_ALL) | (FZ_QUERY_RC if query_rc else 0)
                  | (FZ_SEEDS_REUSE_INDEX if reuse_index else 0))
         return fz_find_seeds(self.h, target, query, k, flank, flags, stream, want_stats)
+
+    def extend_noalloc(self, target, query, seeds, scoring, ydrop, stream=None, want_stats=False, query_rc=False):
+        """Score-only extension through fz_extend_batch_noalloc."""
+        return fz_extend_batch_noalloc(self.h, target, query, seeds, scoring, ydrop,
+                                       FZ_QUERY_RC if query_rc else 0, stream, want_stats)
 
     def local(self, target, query, seeds, scoring, stream=None, want_stats=False, query_rc=False):
         flags = FZ_LOCAL | (FZ_QUERY_RC if query_rc else 0)
