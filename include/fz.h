@@ -113,10 +113,12 @@ typedef struct {
     uint64_t n_sides, n_eager, n_executor, n_overflow;
     uint64_t bin_hist[8];
     uint64_t n_batches;
+    uint64_t max_band;             /* widest range R_d (cells of one anti-diagonal) of any side */
     float ms_pack, ms_inspect, ms_bin, ms_exec, ms_walk, ms_gather;
-                                   /* phase spans; the walks run interleaved with the
-                                    * executor batches and are part of ms_exec (ms_walk
-                                    * stays 0) */
+                                   /* phase spans between HIP events on the call's stream;
+                                    * ms_walk is the summed duration of the traceback walker
+                                    * launches, which run inside the executor phase (ms_exec)
+                                    * on its streams, beside other batches */
     float ms_main;                 /* the dominant kernel alone (inspector, or the local kernel) */
 } fz_stats;
 
@@ -159,9 +161,10 @@ enum {
     FZ_OK = 0,
     FZ_EINVAL = -1,                /* bad argument, or a byte the call does not accept */
     FZ_ENOMEM = -2,                /* device allocation failed */
-    FZ_EDEVICE = -3,               /* HIP runtime error */
-    FZ_EBAND = -4                  /* (reserved) */
+    FZ_EDEVICE = -3                /* HIP runtime error, or an internal check that failed */
 };
+/* A band too wide for the widest window is a per-seed condition
+ * (FZ_HIT_EBAND below), never a call-level error. */
 
 enum {
     FZ_HIT_TRACED = 1,             /* CIGAR present */
@@ -171,15 +174,20 @@ enum {
     FZ_HIT_EBAND = 16,             /* a side's band outgrew the widest kernel: result invalid */
     FZ_HIT_ESEED = 32,             /* seed outside its window or window outside the sequences */
     FZ_HIT_ERANGE = 64,            /* window too long for int32 scores with these parameters */
-    FZ_HIT_COVERED = 128           /* fz_extend_rounds: seed on an earlier round's alignment, not extended */
+    FZ_HIT_COVERED = 128,          /* fz_extend_rounds: seed on an earlier round's alignment, not extended */
+    FZ_HIT_EEXEC = 256             /* the executor's recompute of a side disagreed with the inspector
+                                    * (best score, best cell or pointer-row size): score and
+                                    * coordinates stand, no CIGAR is given (FZ_HIT_TRACED is clear) */
 };
 
 #define FZ_YDROP_INF 2147483647    /* ydrop >= this: no pruning */
 
 /* Create a context on HIP device `device`.  The context owns its device
  * workspace (grown on demand, reused across calls) and the CIGAR buffer.
- * Returns FZ_OK or a negative code; *out is NULL on failure. */
-int fz_create(fz_ctx **out, int device);
+ * workspace_bytes caps the traceback-pointer workspace, the one large
+ * buffer (as fz_set_pointer_workspace; 0 = the default there).  Returns
+ * FZ_OK or a negative code; *out is NULL on failure. */
+int fz_create(fz_ctx **out, int device, uint64_t workspace_bytes);
 
 /* Free the context and every device buffer it owns.  NULL is ignored. */
 void fz_destroy(fz_ctx *ctx);
@@ -339,6 +347,15 @@ int fz_find_seeds(fz_ctx *ctx,
  * guarantees the target bytes have not changed since.  Searching both
  * strands of one query, or many queries against one target, builds the
  * index once.  fz_extend_batch does not touch the index. */
+
+/* Failure injection for tests of the library's own checks.
+ * FZ_DEBUG_SHRINK_ROWS: every executor side is given `value` fewer
+ * pointer-row words than the inspector sized for it, so that the executor's
+ * row-capacity check trips on each side that needs rows (its results then
+ * carry FZ_HIT_EEXEC); 0 restores normal sizing.  Returns FZ_OK, or
+ * FZ_EINVAL for an unknown `what` or a negative value. */
+enum { FZ_DEBUG_SHRINK_ROWS = 1 };
+int fz_debug_set(fz_ctx *ctx, int what, int64_t value);
 
 /* Copy the first n seeds of the last successful fz_find_seeds to dst
  * (device, n records). */

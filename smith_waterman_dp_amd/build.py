@@ -13,7 +13,8 @@ LIB = os.path.join(HERE, "libfz.so")
 ARCH = os.environ.get("FZ_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["fz_lib.hip"]
-HEADERS = ["fz_device.hpp", "fz_extend.hpp", "fz_aux.hpp", "fz_local.hpp", "fz_seeds.hpp", "fz_rounds.hpp"]
+HEADERS = ["fz_device.hpp", "fz_extend.hpp", "fz_aux.hpp", "fz_local.hpp", "fz_seeds.hpp", "fz_rounds.hpp",
+           "fz_sort.hpp"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -127,6 +127,7 @@ struct CombineArgs {
     uint32_t *bin_count;        // [2][NBINS]
     int64_t *max_ptr;           // max executor pointer bytes of one side
     int64_t *cells_total;       // canonical cells over the batch
+    int64_t *max_band;          // widest range R_d over the batch
 };
 
 // Wave-wide sum and maximum (every lane of the wave takes part).
@@ -172,7 +173,7 @@ __global__ void combine_kernel(CombineArgs a)
     h.bin = -1;
     int tr[2] = {0, 0};
     int bkey[2] = {0, 0};
-    uint64_t pmax = 0;
+    uint64_t pmax = 0, bmax = 0;
     fz_seed s = {};
     SeedInfo in = {0, 0};
     SideOut L = {}, R = {};
@@ -196,6 +197,7 @@ __global__ void combine_kernel(CombineArgs a)
         h.t_end = s.t_pos + s.seed_len + R.ie;
         h.q_end = s.q_pos + s.seed_len + R.je;
         h.cells = L.cells + R.cells;
+        bmax = (uint64_t)max(L.max_band, R.max_band);
         if (a.traceback) {
             if (h.score > a.min_tb) {
                 h.status |= FZ_HIT_TRACED;
@@ -223,9 +225,11 @@ __global__ void combine_kernel(CombineArgs a)
     // totals with one atomic per wave (per bin: per distinct bin)
     const uint64_t csum = wave_sum_u64((uint64_t)h.cells);
     const uint64_t cmax = wave_max_u64(pmax);
+    const uint64_t wmax = wave_max_u64(bmax);
     if (lane_id() == 0) {
         if (csum) atomicAdd((unsigned long long *)a.cells_total, (unsigned long long)csum);
         if (cmax) atomicMax((unsigned long long *)a.max_ptr, (unsigned long long)cmax);
+        if (wmax) atomicMax((unsigned long long *)a.max_band, (unsigned long long)wmax);
     }
     for (int q = 0; q < 2; ++q) (void)wave_grouped_inc(a.bin_count, bkey[q], tr[q] == 2);
     if (!valid) return;
@@ -238,8 +242,11 @@ __global__ void combine_kernel(CombineArgs a)
 }
 
 // Scatter executor sides by (class, bin): class 0 first, larger bins first.
+// shrink_words > 0 (failure injection only) gives every side that many
+// fewer pointer-row words than the inspector sized, at least one.
 __global__ void bin_scatter_kernel(int64_t nsides, const int32_t *side_trace, const SideOut *out,
-                                   const uint32_t *bin_base, uint32_t *bin_fill, ExecItem *items)
+                                   const uint32_t *bin_base, uint32_t *bin_fill, ExecItem *items,
+                                   int64_t shrink_words)
 {
     const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const bool active = s < nsides && side_trace[s] == 2;
@@ -258,6 +265,10 @@ __global__ void bin_scatter_kernel(int64_t nsides, const int32_t *side_trace, co
     it.dstar = o.ie + o.je;
     it.ptr_off = 0;
     it.ptr_bytes = o.ptr_bytes;
+    if (shrink_words > 0) {
+        const int64_t hdr_bytes = 8 * ((int64_t)it.dstar + 1);
+        it.ptr_bytes = max(hdr_bytes + 4, it.ptr_bytes - 4 * shrink_words);
+    }
     it.batch = 0;
     items[slot] = it;
 }
@@ -424,6 +435,12 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
 
     // states: 0 = S; 1 = arrived in I (continue if the cell's PTR_EXT_I
     // says the gap extends); 2 = arrived in D (PTR_EXT_D)
+    if (o.flags & SO_EXEC_MISMATCH) {
+        // the recompute disagreed with the inspector: its rows are not
+        // trusted; the seed is reported without a CIGAR (FZ_HIT_EEXEC)
+        if (lane == 0) a.run_len[it.side] = 0;
+        return;
+    }
     int i = o.ie, j = o.je, st = 0;
     bool bad = i < 0 || j < 0 || i + j > it.dstar || total_rows == 0;
     int64_t n = 0, moves = 0;
@@ -640,6 +657,7 @@ __device__ __forceinline__ int64_t assemble_one(const uint32_t *lr, int64_t nl, 
 
 struct AssembleArgs {
     const fz_seed *seeds;
+    const SideOut *out;
     int64_t n;
     const int64_t *run_off;
     const int64_t *run_len;
@@ -656,6 +674,11 @@ __global__ void assemble_kernel(AssembleArgs a)
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= a.n) return;
     fz_hit *h = &a.hits[k];
+    if (!WRITE && (h->status & FZ_HIT_TRACED) &&
+        ((a.out[2 * k].flags | a.out[2 * k + 1].flags) & SO_EXEC_MISMATCH)) {
+        // the executor disagreed with the inspector on a side: no CIGAR
+        h->status = (h->status & ~(int64_t)FZ_HIT_TRACED) | FZ_HIT_EEXEC;
+    }
     if (!(h->status & FZ_HIT_TRACED)) {
         if (!WRITE) a.cig_len[k] = 0;
         else {

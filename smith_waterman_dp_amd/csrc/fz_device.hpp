@@ -105,6 +105,7 @@ struct SideOut {
     int64_t cells;
     int64_t ptr_bytes;          // executor pointer bytes through the best anti-diagonal
     int32_t flags, eager_len;
+    int32_t max_band, pad_;     // widest range R_d of the side
 };
 
 // One side queued for the executor / walker.

@@ -80,6 +80,7 @@ struct SideDP {
     int64_t cells, cum_bytes, ptr_at_best;  // totals up to diagonal dflush
     int dflush;
     int32_t acc_cells, acc_words;   // since dflush: sum of (|R_d| - 1), of (row words - NWORD)
+    int32_t bmax;               // widest range so far, minus one
     bool overflow;
     // executor
     uint32_t rowoff, rowcap;    // rows written / rows the inspector sized
@@ -303,6 +304,7 @@ struct SideDP {
         // Σ|R_d| and the pointer-row sizes, as 32-bit sums that flush()
         // folds into the totals (the per-diagonal constants are added there)
         acc_cells += rhi - rlo;
+        bmax = max(bmax, rhi - rlo);
         // pointer row: the lanes of the live hull; with C = 3, lane pairs
         // share a dword so that rows keep the six-cells-per-dword format
         const int rlane0 = PAIRED ? (llo & ~1) : llo;
@@ -416,6 +418,7 @@ struct SideDP {
         cum_bytes = 8 + 4 * NWORD;
         ptr_at_best = cum_bytes;
         dflush = 0; acc_cells = 0; acc_words = 0;
+        bmax = 0;
         overflow = false;
         rowoff = 0;
         {
@@ -554,6 +557,7 @@ struct SideDP {
         best = o.best; bi = o.bi; bj = o.bj; dend = o.dend; T = o.T;
         cells = o.cells; cum_bytes = o.cum_bytes; ptr_at_best = o.ptr_at_best;
         dflush = o.dflush; acc_cells = 0; acc_words = 0;        // (the other side flushed)
+        bmax = o.bmax;
         overflow = o.overflow;
         rowoff = o.rowoff; rowcap = o.rowcap; hdr = o.hdr; rows = o.rows;
         lane = fresh_lane_id();
@@ -606,14 +610,14 @@ struct SideDP {
 
 // What a side's extension reports, from whichever layout finished it.
 struct SideResult {
-    int best, bi, bj, dend;
+    int best, bi, bj, dend, band;
     int64_t cells, ptr_at_best;
     bool overflow;
     template <class DP>
     __device__ __forceinline__ void take(DP &dp)
     {
         dp.flush();
-        best = dp.best; bi = dp.bi; bj = dp.bj; dend = dp.dend;
+        best = dp.best; bi = dp.bi; bj = dp.bj; dend = dp.dend; band = dp.bmax + 1;
         cells = dp.cells; ptr_at_best = dp.ptr_at_best;
         overflow = dp.overflow;
     }
@@ -737,6 +741,8 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <=
     r.ptr_bytes = x.ptr_at_best;
     r.flags = (x.overflow ? SO_OVERFLOW : 0) | a.result_flags;
     r.eager_len = 0;
+    r.max_band = x.band;
+    r.pad_ = 0;
     if (!x.overflow && x.bi <= EAGER_EDGE && x.bj <= EAGER_EDGE) {
         // the best cell lies in the eager block, which the start layout
         // kept (no layout change happens before diagonal 34)

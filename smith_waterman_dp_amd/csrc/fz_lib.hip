@@ -17,7 +17,6 @@
 // Local mode runs pack and one full-window kernel.  fz_find_seeds is the seed
 // stage before all this (fz_seeds.hpp).
 #include <hip/hip_runtime.h>
-#include <hipcub/hipcub.hpp>
 
 #include <algorithm>
 #include <cstdarg>
@@ -34,6 +33,7 @@
 #include "fz_local.hpp"
 #include "fz_seeds.hpp"
 #include "fz_rounds.hpp"
+#include "fz_sort.hpp"
 
 using namespace fz;
 
@@ -54,6 +54,7 @@ struct Counters {
     int64_t max_ptr;
     int64_t exec_cells;
     int64_t totals[4];
+    int64_t max_band;
 };
 
 // One wave per workgroup for the wave-per-side kernels: sides differ in
@@ -117,21 +118,23 @@ struct fz_ctx {
     int n_cu = 256;
     std::string err;
     uint64_t ptr_cap = 0;               // 0 = default
+    int64_t dbg_shrink_rows = 0;        // fz_debug_set(FZ_DEBUG_SHRINK_ROWS)
+    std::vector<hipEvent_t> walk_ev;    // brackets of the walker launches (FZ_STATS)
     uint64_t last_words = 0;            // CIGAR words of the last successful call
     DevBuf Tf, Tr, Qf, Qr;
     DevBuf tasks, info, out, eager, side_trace, run_cap, run_off, run_len, runs;
     DevBuf items, batch_first, scan_tmp, cig, cigar, counters, ovl0, ovl1, bnd;
+    DevBuf rs_cnt, ps_tmp;              // radix-sort digit counts, tile totals of the generic scans
     DevBuf ptr_ws[EXEC_STREAMS];        // one pointer workspace per executor stream
     // seed stage: target keys and positions (two of each for the sort), query
     // keys, join ranges and counts, hits (two for the sort), run flags and
-    // ranks, library scratch, and the seeds of the last fz_find_seeds
-    DevBuf sk_tk, sk_tk2, sk_tp, sk_tp2, sk_valid, sk_vpos, sk_bend, sk_boff, sk_lo, sk_cnt, sk_off, sk_hit, sk_hit2, sk_flag, sk_rank, sk_tmp, sk_out;
+    // ranks, and the seeds of the last fz_find_seeds
+    DevBuf sk_tk, sk_tk2, sk_tp, sk_tp2, sk_valid, sk_vpos, sk_bend, sk_boff, sk_lo, sk_cnt, sk_off, sk_hit, sk_hit2, sk_flag, sk_rank, sk_out;
     uint64_t last_seeds = 0;
     // covered-seed rounds: round flags, scan, packed seeds and results, CIGAR
     // words of all rounds, aligned segments (keys and ends, two of each for
-    // the sort), running maxima, library scratch
-    DevBuf rd_keep, rd_pos, rd_seeds, rd_hits, rd_cnt, rd_off, rd_cig, sg_key, sg_key2, sg_end, sg_end2, sg_v, sg_max,
-        rd_tmp;
+    // the sort), running maxima
+    DevBuf rd_keep, rd_pos, rd_seeds, rd_hits, rd_cnt, rd_off, rd_cig, sg_key, sg_key2, sg_end, sg_end2, sg_v, sg_max;
     // the target index held in sk_tk2 / sk_tp2 / sk_boff (FZ_SEEDS_REUSE_INDEX)
     bool idx_valid = false;
     const uint8_t *idx_target = nullptr;
@@ -230,6 +233,52 @@ int scan(fz_ctx *ctx, const int64_t *vals, int64_t stride, int64_t n, int64_t *o
     if (n > 0) {
         scan_apply_kernel<<<(unsigned)nb, SCAN_BLOCK, 0, st>>>(vals, stride, n, bs, outv, ostride);
         HIP_OK(hipGetLastError());
+    }
+    return FZ_OK;
+}
+
+// Scan of n values with OP (fz_sort.hpp), exclusive or inclusive; out may
+// be in.  Uses ctx->ps_tmp for the tile totals.
+template <class T, class OP, bool INCL>
+int device_scan(fz_ctx *ctx, const T *in, T *out, int64_t n, hipStream_t st)
+{
+    if (n <= 0) return FZ_OK;
+    const int64_t nt = (n + PS_TILE - 1) / PS_TILE;
+    ENSURE(ctx->ps_tmp, (size_t)nt * sizeof(T));
+    T *tt = as<T>(ctx->ps_tmp);
+    pscan_reduce_kernel<T, OP><<<(unsigned)nt, PS_BLOCK, 0, st>>>(in, n, tt);
+    HIP_OK(hipGetLastError());
+    pscan_top_kernel<T, OP><<<1, PS_BLOCK, 0, st>>>(tt, nt);
+    HIP_OK(hipGetLastError());
+    pscan_apply_kernel<T, OP, INCL><<<(unsigned)nt, PS_BLOCK, 0, st>>>(in, n, tt, out);
+    HIP_OK(hipGetLastError());
+    return FZ_OK;
+}
+
+// Stable sort of n 64-bit keys (and their 32-bit values when va is given)
+// by bits [0, bits), eight per pass, ping-ponging between the a and b
+// buffers (both hold n entries).  *in_b tells where the result ends up.
+int radix_sort(fz_ctx *ctx, uint64_t *ka, uint64_t *kb, uint32_t *va, uint32_t *vb, int64_t n, int bits,
+               hipStream_t st, bool *in_b)
+{
+    *in_b = false;
+    if (n <= 1 || bits <= 0) return FZ_OK;
+    if (n >= ((int64_t)1 << 32)) return fail(ctx, FZ_EINVAL, "radix sort of %lld keys: at most 2^32 - 1", (long long)n);
+    const int64_t ntiles = (n + RS_TILE - 1) / RS_TILE;
+    ENSURE(ctx->rs_cnt, (size_t)RS_BINS * ntiles * sizeof(uint32_t));
+    uint32_t *cnt = as<uint32_t>(ctx->rs_cnt);
+    for (int shift = 0; shift < bits; shift += 8) {
+        rs_hist_kernel<<<(unsigned)ntiles, RS_BLOCK, 0, st>>>(ka, n, shift, cnt, ntiles);
+        HIP_OK(hipGetLastError());
+        int rc = device_scan<uint32_t, ScanSum, false>(ctx, cnt, cnt, (int64_t)RS_BINS * ntiles, st);
+        if (rc) return rc;
+        if (va) rs_scatter_kernel<true><<<(unsigned)ntiles, RS_BLOCK, 0, st>>>(ka, kb, va, vb, n, shift, cnt, ntiles);
+        else rs_scatter_kernel<false><<<(unsigned)ntiles, RS_BLOCK, 0, st>>>(ka, kb, nullptr, nullptr, n, shift, cnt,
+                                                                              ntiles);
+        HIP_OK(hipGetLastError());
+        std::swap(ka, kb);
+        std::swap(va, vb);
+        *in_b = !*in_b;
     }
     return FZ_OK;
 }
@@ -418,9 +467,6 @@ static int seeds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const u
     // most 2^30), all 2k bits when that is fewer
     const unsigned gb = 4 * (unsigned)ctx->n_cu * 4;
     int64_t ntv = reuse ? ctx->idx_keys : 0;
-    size_t tmp_sort = 0, tmp_scan = 0, tmp_max = 0, tmp_sort2 = 0;
-    HIP_OK(hipcub::DeviceScan::ExclusiveSum(nullptr, tmp_scan, as<uint64_t>(ctx->sk_cnt), as<uint64_t>(ctx->sk_off),
-                                            (int)nq, st));
     auto table_bits = [&](int64_t nkeys) {
         int bits = 1;
         while (bits < 30 && (1ll << bits) < nkeys) ++bits;
@@ -436,13 +482,9 @@ static int seeds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const u
         kmer_keys_kernel<<<gb, 256, 0, st>>>(as<uint8_t>(ctx->Tf) + PAD, nt, (int)k, as<uint64_t>(ctx->sk_tk),
                                              as<uint32_t>(ctx->sk_tp), as<uint32_t>(ctx->sk_valid));
         HIP_OK(hipGetLastError());
-        size_t tv = 0;
-        HIP_OK(hipcub::DeviceScan::ExclusiveSum(nullptr, tv, as<uint32_t>(ctx->sk_valid), as<uint32_t>(ctx->sk_vpos),
-                                                (int)nt, st));
-        ENSURE(ctx->sk_tmp, std::max(tv, tmp_scan));
-        tv = ctx->sk_tmp.cap;
-        HIP_OK(hipcub::DeviceScan::ExclusiveSum(ctx->sk_tmp.p, tv, as<uint32_t>(ctx->sk_valid),
-                                                as<uint32_t>(ctx->sk_vpos), (int)nt, st));
+        rc = device_scan<uint32_t, ScanSum, false>(ctx, as<uint32_t>(ctx->sk_valid), as<uint32_t>(ctx->sk_vpos),
+                                                   nt, st);
+        if (rc) return rc;
         uint32_t lv[2] = {0, 0};
         HIP_OK(hipMemcpyAsync(&lv[0], as<uint32_t>(ctx->sk_vpos) + (nt - 1), sizeof(uint32_t), hipMemcpyDeviceToHost,
                               st));
@@ -463,21 +505,20 @@ static int seeds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const u
     const int shift = (int)(2 * k) - nb_bits;
     const int64_t NB = 1ll << nb_bits;
     if (reuse || ntv == 0) {
-        ENSURE(ctx->sk_tmp, tmp_scan);
         tm.mark();              // keys (done above unless reused), sort, table
         tm.mark();
         tm.mark();
     } else {
         tm.mark();
-        HIP_OK(hipcub::DeviceRadixSort::SortPairs(nullptr, tmp_sort, as<uint64_t>(ctx->sk_tk),
-                                                  as<uint64_t>(ctx->sk_tk2), as<uint32_t>(ctx->sk_tp),
-                                                  as<uint32_t>(ctx->sk_tp2), (int)ntv, 0, (int)(2 * k), st));
-        HIP_OK(hipcub::DeviceScan::InclusiveScan(nullptr, tmp_max, as<uint32_t>(ctx->sk_bend),
-                                                 as<uint32_t>(ctx->sk_boff) + 1, hipcub::Max(), (int)NB, st));
-        ENSURE(ctx->sk_tmp, std::max(std::max(tmp_sort, tmp_scan), tmp_max));
-        HIP_OK(hipcub::DeviceRadixSort::SortPairs(ctx->sk_tmp.p, tmp_sort, as<uint64_t>(ctx->sk_tk),
-                                                  as<uint64_t>(ctx->sk_tk2), as<uint32_t>(ctx->sk_tp),
-                                                  as<uint32_t>(ctx->sk_tp2), (int)ntv, 0, (int)(2 * k), st));
+        // the sorted index ends in sk_tk2 / sk_tp2
+        bool in_b = false;
+        rc = radix_sort(ctx, as<uint64_t>(ctx->sk_tk), as<uint64_t>(ctx->sk_tk2), as<uint32_t>(ctx->sk_tp),
+                        as<uint32_t>(ctx->sk_tp2), ntv, (int)(2 * k), st, &in_b);
+        if (rc) return rc;
+        if (!in_b) {
+            std::swap(ctx->sk_tk, ctx->sk_tk2);
+            std::swap(ctx->sk_tp, ctx->sk_tp2);
+        }
         tm.mark();
         ENSURE(ctx->sk_bend, NB * sizeof(uint32_t));
         ENSURE(ctx->sk_boff, (NB + 1) * sizeof(uint32_t));
@@ -487,9 +528,9 @@ static int seeds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const u
         if (rc) return rc;
         bucket_end_kernel<<<gb, 256, 0, st>>>(as<uint64_t>(ctx->sk_tk2), ntv, shift, as<uint32_t>(ctx->sk_bend));
         HIP_OK(hipGetLastError());
-        tmp_max = ctx->sk_tmp.cap;
-        HIP_OK(hipcub::DeviceScan::InclusiveScan(ctx->sk_tmp.p, tmp_max, as<uint32_t>(ctx->sk_bend),
-                                                 as<uint32_t>(ctx->sk_boff) + 1, hipcub::Max(), (int)NB, st));
+        rc = device_scan<uint32_t, ScanMax, true>(ctx, as<uint32_t>(ctx->sk_bend), as<uint32_t>(ctx->sk_boff) + 1, NB,
+                                                  st);
+        if (rc) return rc;
         tm.mark();
     }
 
@@ -502,9 +543,8 @@ static int seeds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const u
                                           as<uint64_t>(ctx->sk_cnt));
     HIP_OK(hipGetLastError());
     tm.mark();
-    tmp_scan = ctx->sk_tmp.cap;
-    HIP_OK(hipcub::DeviceScan::ExclusiveSum(ctx->sk_tmp.p, tmp_scan, as<uint64_t>(ctx->sk_cnt),
-                                            as<uint64_t>(ctx->sk_off), (int)nq, st));
+    rc = device_scan<uint64_t, ScanSum, false>(ctx, as<uint64_t>(ctx->sk_cnt), as<uint64_t>(ctx->sk_off), nq, st);
+    if (rc) return rc;
     tm.mark();
     uint64_t last[2] = {0, 0};
     HIP_OK(hipMemcpyAsync(&last[0], as<uint64_t>(ctx->sk_off) + (nq - 1), sizeof(uint64_t), hipMemcpyDeviceToHost, st));
@@ -552,22 +592,24 @@ static int seeds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const u
                                          as<uint64_t>(ctx->sk_hit));
     HIP_OK(hipGetLastError());
     tm.mark();
-    HIP_OK(hipcub::DeviceRadixSort::SortKeys(nullptr, tmp_sort2, as<uint64_t>(ctx->sk_hit),
-                                             as<uint64_t>(ctx->sk_hit2), (int)H, 0, 64, st));
-    size_t tmp_scan2 = 0;
-    HIP_OK(hipcub::DeviceScan::ExclusiveSum(nullptr, tmp_scan2, as<uint64_t>(ctx->sk_flag),
-                                            as<uint64_t>(ctx->sk_rank), (int)H, st));
-    ENSURE(ctx->sk_tmp, std::max(tmp_sort2, tmp_scan2));
-    size_t t2 = ctx->sk_tmp.cap;
-    HIP_OK(hipcub::DeviceRadixSort::SortKeys(ctx->sk_tmp.p, t2, as<uint64_t>(ctx->sk_hit), as<uint64_t>(ctx->sk_hit2),
-                                             (int)H, 0, 64, st));
+    {
+        // the word's diagonal field holds t - q + query_len < target_len + query_len;
+        // the sorted words end in sk_hit2
+        int bits = 32;
+        while (bits < 64 && (tlen + qlen) >> (bits - 32)) ++bits;
+        bool in_b = false;
+        rc = radix_sort(ctx, as<uint64_t>(ctx->sk_hit), as<uint64_t>(ctx->sk_hit2), nullptr, nullptr, (int64_t)H, bits,
+                        st, &in_b);
+        if (rc) return rc;
+        if (!in_b) std::swap(ctx->sk_hit, ctx->sk_hit2);
+    }
     tm.mark();
     run_start_kernel<<<gb, 256, 0, st>>>(as<uint64_t>(ctx->sk_hit2), (int64_t)H, (flags & FZ_SEEDS_ALL) ? 0 : 1,
                                          as<uint64_t>(ctx->sk_flag));
     HIP_OK(hipGetLastError());
-    t2 = ctx->sk_tmp.cap;
-    HIP_OK(hipcub::DeviceScan::ExclusiveSum(ctx->sk_tmp.p, t2, as<uint64_t>(ctx->sk_flag), as<uint64_t>(ctx->sk_rank),
-                                            (int)H, st));
+    rc = device_scan<uint64_t, ScanSum, false>(ctx, as<uint64_t>(ctx->sk_flag), as<uint64_t>(ctx->sk_rank), (int64_t)H,
+                                               st);
+    if (rc) return rc;
     tm.mark();
     HIP_OK(hipMemcpyAsync(&last[0], as<uint64_t>(ctx->sk_rank) + (H - 1), sizeof(uint64_t), hipMemcpyDeviceToHost, st));
     HIP_OK(hipMemcpyAsync(&last[1], as<uint64_t>(ctx->sk_flag) + (H - 1), sizeof(uint64_t), hipMemcpyDeviceToHost, st));
@@ -592,7 +634,7 @@ static int seeds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const u
 
 extern "C" {
 
-int fz_create(fz_ctx **out, int device)
+int fz_create(fz_ctx **out, int device, uint64_t workspace_bytes)
 {
     if (!out) return FZ_EINVAL;
     *out = nullptr;
@@ -603,6 +645,7 @@ int fz_create(fz_ctx **out, int device)
     }
     fz_ctx *ctx = new fz_ctx;
     ctx->device = device;
+    ctx->ptr_cap = workspace_bytes;
     int prev = 0;
     (void)hipGetDevice(&prev);
     if (hipSetDevice(device) != hipSuccess) {
@@ -669,10 +712,10 @@ void fz_destroy(fz_ctx *ctx)
                       &ctx->counters, &ctx->ovl0, &ctx->ovl1, &ctx->bnd,
                       &ctx->sk_tk, &ctx->sk_tk2, &ctx->sk_tp, &ctx->sk_tp2, &ctx->sk_valid, &ctx->sk_vpos,
                       &ctx->sk_bend, &ctx->sk_boff, &ctx->sk_lo, &ctx->sk_cnt,
-                      &ctx->sk_off, &ctx->sk_hit, &ctx->sk_hit2, &ctx->sk_flag, &ctx->sk_rank, &ctx->sk_tmp,
+                      &ctx->sk_off, &ctx->sk_hit, &ctx->sk_hit2, &ctx->sk_flag, &ctx->sk_rank,
                       &ctx->sk_out, &ctx->rd_keep, &ctx->rd_pos, &ctx->rd_seeds, &ctx->rd_hits, &ctx->rd_cnt,
                       &ctx->rd_off, &ctx->rd_cig, &ctx->sg_key, &ctx->sg_key2, &ctx->sg_end, &ctx->sg_end2,
-                      &ctx->sg_v, &ctx->sg_max, &ctx->rd_tmp};
+                      &ctx->sg_v, &ctx->sg_max, &ctx->rs_cnt, &ctx->ps_tmp};
     for (auto &x : ctx->xs)
         if (x) (void)hipStreamSynchronize(x);
     if (ctx->xw) (void)hipStreamSynchronize(ctx->xw);
@@ -691,6 +734,8 @@ void fz_destroy(fz_ctx *ctx)
         if (e) (void)hipEventDestroy(e);
     for (auto &e : ctx->kev)
         if (e) (void)hipEventDestroy(e);
+    for (auto &e : ctx->walk_ev)
+        if (e) (void)hipEventDestroy(e);
     (void)hipSetDevice(prev);
     delete ctx;
 }
@@ -701,6 +746,14 @@ int fz_set_pointer_workspace(fz_ctx *ctx, uint64_t bytes)
 {
     if (!ctx) return FZ_EINVAL;
     ctx->ptr_cap = bytes;
+    return FZ_OK;
+}
+
+int fz_debug_set(fz_ctx *ctx, int what, int64_t value)
+{
+    if (!ctx) return FZ_EINVAL;
+    if (what != FZ_DEBUG_SHRINK_ROWS || value < 0) return fail(ctx, FZ_EINVAL, "unknown debug setting or negative value");
+    ctx->dbg_shrink_rows = value;
     return FZ_OK;
 }
 
@@ -833,6 +886,7 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     ca.bin_count = dc->bin_count;
     ca.max_ptr = &dc->max_ptr;
     ca.cells_total = &dc->totals[3];
+    ca.max_band = &dc->max_band;
     combine_kernel<<<blocks_for(n, 256), 256, 0, st>>>(ca);
     HIP_OK(hipGetLastError());
     // run slots of traced sides
@@ -859,7 +913,8 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         ENSURE(ctx->items, n_exec * sizeof(ExecItem));
         bin_scatter_kernel<<<blocks_for(nsides, 256), 256, 0, st>>>(nsides, as<int32_t>(ctx->side_trace),
                                                                     as<SideOut>(ctx->out), dc->bin_base,
-                                                                    dc->bin_fill, as<ExecItem>(ctx->items));
+                                                                    dc->bin_fill, as<ExecItem>(ctx->items),
+                                                                    ctx->dbg_shrink_rows);
         HIP_OK(hipGetLastError());
         const int64_t stride = sizeof(ExecItem) / sizeof(int64_t);
         ExecItem *it = as<ExecItem>(ctx->items);
@@ -875,6 +930,7 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     tm.mark();
 
     // ---- execute + walk, in batches
+    size_t n_walks = 0;
     if (n_exec > 0) {
         if ((rc = read_counters())) return rc;
         const int64_t total_ptr = hc.totals[1], max_item = hc.max_ptr;
@@ -958,9 +1014,19 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
                 wk.run_off = as<int64_t>(ctx->run_off);
                 wk.runs = as<uint32_t>(ctx->runs);
                 wk.run_len = as<int64_t>(ctx->run_len);
+                if (tm.on) {
+                    // a pair of events around each walker launch (ms_walk)
+                    while (ctx->walk_ev.size() < 2 * (n_walks + 1)) {
+                        hipEvent_t e = nullptr;
+                        HIP_OK(hipEventCreate(&e));
+                        ctx->walk_ev.push_back(e);
+                    }
+                    HIP_OK(hipEventRecord(ctx->walk_ev[2 * n_walks], xst));
+                }
                 if (cls == 0) walk_wave_kernel<C_STD><<<(unsigned)(s1 - s0), 64, 0, xst>>>(wk);
                 else walk_wave_kernel<C_WIDE><<<(unsigned)(s1 - s0), 64, 0, xst>>>(wk);
                 HIP_OK(hipGetLastError());
+                if (tm.on) HIP_OK(hipEventRecord(ctx->walk_ev[2 * n_walks++ + 1], xst));
             }
         }
         for (int k = 1; k < nbuf; ++k) {
@@ -978,6 +1044,7 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     ENSURE(ctx->cig, n * sizeof(int64_t));
     AssembleArgs aa;
     aa.seeds = seeds;
+    aa.out = as<SideOut>(ctx->out);
     aa.n = n;
     aa.run_off = as<int64_t>(ctx->run_off);
     aa.run_len = as<int64_t>(ctx->run_len);
@@ -1006,6 +1073,12 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         S.n_sides = (uint64_t)nsides;
         S.cells = (uint64_t)hc.totals[3];
         S.executor_cells = (uint64_t)hc.exec_cells;
+        S.max_band = (uint64_t)hc.max_band;
+        for (size_t w = 0; w < n_walks; ++w) {
+            float v = 0.f;
+            (void)hipEventElapsedTime(&v, ctx->walk_ev[2 * w], ctx->walk_ev[2 * w + 1]);
+            S.ms_walk += v;
+        }
         S.ms_pack = tm.ms(0, 1);
         S.ms_inspect = tm.ms(1, 2);
         S.ms_bin = tm.ms(2, 3);
@@ -1108,6 +1181,7 @@ static int noalloc_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const
     ca.bin_count = dc->bin_count;
     ca.max_ptr = &dc->max_ptr;
     ca.cells_total = &dc->totals[3];
+    ca.max_band = &dc->max_band;
     combine_kernel<<<blocks_for(n, 256), 256, 0, st>>>(ca);
     HIP_OK(hipGetLastError());
     if (stats) {
@@ -1115,6 +1189,7 @@ static int noalloc_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const
         HIP_OK(hipStreamSynchronize(st));
         S.n_sides = (uint64_t)nsides;
         S.cells = (uint64_t)hc.totals[3];
+        S.max_band = (uint64_t)hc.max_band;
         S.n_overflow = hc.overflow_count[0];
         (void)hipEventElapsedTime(&S.ms_main, ctx->kev[0], ctx->kev[1]);
         *stats = S;
@@ -1177,11 +1252,8 @@ static int rounds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
                                                           as<uint64_t>(ctx->sg_key), as<uint64_t>(ctx->sg_max),
                                                           nseg, keep);
         HIP_OK(hipGetLastError());
-        size_t tb = 0;
-        HIP_OK(hipcub::DeviceScan::ExclusiveSum(nullptr, tb, keep, pos, (int)nb, st));
-        ENSURE(ctx->rd_tmp, tb);
-        tb = ctx->rd_tmp.cap;
-        HIP_OK(hipcub::DeviceScan::ExclusiveSum(ctx->rd_tmp.p, tb, keep, pos, (int)nb, st));
+        rc = device_scan<uint32_t, ScanSum, false>(ctx, keep, pos, nb, st);
+        if (rc) return rc;
         uint32_t lastv[2] = {0, 0};
         HIP_OK(hipMemcpyAsync(&lastv[0], pos + (nb - 1), sizeof(uint32_t), hipMemcpyDeviceToHost, st));
         HIP_OK(hipMemcpyAsync(&lastv[1], keep + (nb - 1), sizeof(uint32_t), hipMemcpyDeviceToHost, st));
@@ -1214,6 +1286,7 @@ static int rounds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
                 tot.ms_walk += rsst.ms_walk;
                 tot.ms_gather += rsst.ms_gather;
                 tot.ms_main += rsst.ms_main;
+                tot.max_band = std::max(tot.max_band, rsst.max_band);
             }
             rc = grow_keep(ctx, ctx->rd_cig, (size_t)(acc_words + (int64_t)words + 1) * sizeof(uint32_t),
                            (size_t)acc_words * sizeof(uint32_t), st);
@@ -1231,13 +1304,9 @@ static int rounds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         seg_count_kernel<<<blocks_for(nkeep, 256), 256, 0, st>>>(as<fz_hit>(ctx->rd_hits), nkeep,
                                                                  as<uint32_t>(ctx->cigar), as<uint64_t>(ctx->rd_cnt));
         HIP_OK(hipGetLastError());
-        tb = 0;
-        HIP_OK(hipcub::DeviceScan::ExclusiveSum(nullptr, tb, as<uint64_t>(ctx->rd_cnt), as<uint64_t>(ctx->rd_off),
-                                                (int)nkeep, st));
-        ENSURE(ctx->rd_tmp, tb);
-        tb = ctx->rd_tmp.cap;
-        HIP_OK(hipcub::DeviceScan::ExclusiveSum(ctx->rd_tmp.p, tb, as<uint64_t>(ctx->rd_cnt),
-                                                as<uint64_t>(ctx->rd_off), (int)nkeep, st));
+        rc = device_scan<uint64_t, ScanSum, false>(ctx, as<uint64_t>(ctx->rd_cnt), as<uint64_t>(ctx->rd_off), nkeep,
+                                                   st);
+        if (rc) return rc;
         uint64_t lastm[2] = {0, 0};
         HIP_OK(hipMemcpyAsync(&lastm[0], as<uint64_t>(ctx->rd_off) + (nkeep - 1), sizeof(uint64_t),
                               hipMemcpyDeviceToHost, st));
@@ -1261,25 +1330,24 @@ static int rounds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
                                                                 (int64_t)qlen, as<uint64_t>(ctx->sg_key) + nseg,
                                                                 as<uint32_t>(ctx->sg_end) + nseg);
         HIP_OK(hipGetLastError());
-        size_t ts = 0, tm2 = 0;
-        HIP_OK(hipcub::DeviceRadixSort::SortPairs(nullptr, ts, as<uint64_t>(ctx->sg_key), as<uint64_t>(ctx->sg_key2),
-                                                  as<uint32_t>(ctx->sg_end), as<uint32_t>(ctx->sg_end2), (int)ns, 0, 64,
-                                                  st));
-        HIP_OK(hipcub::DeviceScan::InclusiveScan(nullptr, tm2, as<uint64_t>(ctx->sg_v), as<uint64_t>(ctx->sg_max),
-                                                 hipcub::Max(), (int)ns, st));
-        ENSURE(ctx->rd_tmp, std::max(ts, tm2));
-        ts = ctx->rd_tmp.cap;
-        HIP_OK(hipcub::DeviceRadixSort::SortPairs(ctx->rd_tmp.p, ts, as<uint64_t>(ctx->sg_key),
-                                                  as<uint64_t>(ctx->sg_key2), as<uint32_t>(ctx->sg_end),
-                                                  as<uint32_t>(ctx->sg_end2), (int)ns, 0, 64, st));
-        std::swap(ctx->sg_key, ctx->sg_key2);
-        std::swap(ctx->sg_end, ctx->sg_end2);
+        {
+            // keys are (t - q + query_len) << 32 | t; the sorted set ends in sg_key / sg_end
+            int bits = 32;
+            while (bits < 64 && (tlen + qlen) >> (bits - 32)) ++bits;
+            bool in_b = false;
+            rc = radix_sort(ctx, as<uint64_t>(ctx->sg_key), as<uint64_t>(ctx->sg_key2), as<uint32_t>(ctx->sg_end),
+                            as<uint32_t>(ctx->sg_end2), ns, bits, st, &in_b);
+            if (rc) return rc;
+            if (in_b) {
+                std::swap(ctx->sg_key, ctx->sg_key2);
+                std::swap(ctx->sg_end, ctx->sg_end2);
+            }
+        }
         seg_diag_end_kernel<<<blocks_for(ns, 256), 256, 0, st>>>(as<uint64_t>(ctx->sg_key), as<uint32_t>(ctx->sg_end),
                                                                  ns, as<uint64_t>(ctx->sg_v));
         HIP_OK(hipGetLastError());
-        tm2 = ctx->rd_tmp.cap;
-        HIP_OK(hipcub::DeviceScan::InclusiveScan(ctx->rd_tmp.p, tm2, as<uint64_t>(ctx->sg_v),
-                                                 as<uint64_t>(ctx->sg_max), hipcub::Max(), (int)ns, st));
+        rc = device_scan<uint64_t, ScanMax, true>(ctx, as<uint64_t>(ctx->sg_v), as<uint64_t>(ctx->sg_max), ns, st);
+        if (rc) return rc;
         nseg = ns;
     }
     HIP_OK(hipStreamSynchronize(st));

@@ -13,10 +13,11 @@ LIB_PATH = os.path.join(HERE, "libfz.so")
 
 FZ_TRACEBACK, FZ_LOCAL, FZ_STATS, FZ_QUERY_RC, FZ_SEEDS_ALL, FZ_SEEDS_REUSE_INDEX = 1, 2, 4, 8, 16, 32
 FZ_ROUNDS_DOUBLING = 64
-FZ_OK, FZ_EINVAL, FZ_ENOMEM, FZ_EDEVICE, FZ_EBAND = 0, -1, -2, -3, -4
+FZ_OK, FZ_EINVAL, FZ_ENOMEM, FZ_EDEVICE = 0, -1, -2, -3
 FZ_HIT_TRACED, FZ_HIT_EAGER_LEFT, FZ_HIT_EAGER_RIGHT = 1, 2, 4
 FZ_HIT_BELOW_MIN, FZ_HIT_EBAND, FZ_HIT_ESEED, FZ_HIT_ERANGE = 8, 16, 32, 64
-FZ_HIT_COVERED = 128
+FZ_HIT_COVERED, FZ_HIT_EEXEC = 128, 256
+FZ_DEBUG_SHRINK_ROWS = 1
 FZ_YDROP_INF = 2147483647
 FZ_NOALLOC_MAX_SEEDS, FZ_NOALLOC_MAX_BASES = 65536, 4194304
 
@@ -26,7 +27,8 @@ SEED_FIELDS = ["t_pos", "q_pos", "seed_len", "t_lo", "t_hi", "q_lo", "q_hi"]
 
 # every symbol include/fz.h declares
 EXPORTS = ["fz_create", "fz_destroy", "fz_last_error", "fz_set_pointer_workspace", "fz_extend_batch",
-           "fz_extend_rounds", "fz_find_seeds", "fz_copy_seeds", "fz_copy_cigar", "fz_extend_batch_noalloc"]
+           "fz_extend_rounds", "fz_find_seeds", "fz_copy_seeds", "fz_copy_cigar", "fz_extend_batch_noalloc",
+           "fz_debug_set"]
 
 
 class fz_scoring(ctypes.Structure):
@@ -56,7 +58,7 @@ class fz_stats(ctypes.Structure):
     _fields_ = [("cells", ctypes.c_uint64), ("executor_cells", ctypes.c_uint64),
                 ("pointer_bytes", ctypes.c_uint64), ("n_sides", ctypes.c_uint64), ("n_eager", ctypes.c_uint64),
                 ("n_executor", ctypes.c_uint64), ("n_overflow", ctypes.c_uint64),
-                ("bin_hist", ctypes.c_uint64 * 8), ("n_batches", ctypes.c_uint64),
+                ("bin_hist", ctypes.c_uint64 * 8), ("n_batches", ctypes.c_uint64), ("max_band", ctypes.c_uint64),
                 ("ms_pack", ctypes.c_float), ("ms_inspect", ctypes.c_float), ("ms_bin", ctypes.c_float),
                 ("ms_exec", ctypes.c_float), ("ms_walk", ctypes.c_float), ("ms_gather", ctypes.c_float),
                 ("ms_main", ctypes.c_float)]
@@ -94,7 +96,9 @@ def load_library(path=LIB_PATH):
     lib = ctypes.CDLL(path)
     P, u64, i32, i64 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int64
     lib.fz_create.restype = ctypes.c_int
-    lib.fz_create.argtypes = [ctypes.POINTER(P), ctypes.c_int]
+    lib.fz_create.argtypes = [ctypes.POINTER(P), ctypes.c_int, u64]
+    lib.fz_debug_set.restype = ctypes.c_int
+    lib.fz_debug_set.argtypes = [P, ctypes.c_int, i64]
     lib.fz_destroy.restype = None
     lib.fz_destroy.argtypes = [P]
     lib.fz_last_error.restype = ctypes.c_char_p
@@ -131,10 +135,10 @@ def _check(ctx, rc):
         raise FzError(rc, msg)
 
 
-def fz_create(device=0):
+def fz_create(device=0, workspace_bytes=0):
     lib = load_library()
     h = ctypes.c_void_p()
-    rc = lib.fz_create(ctypes.byref(h), int(device))
+    rc = lib.fz_create(ctypes.byref(h), int(device), int(workspace_bytes))
     if rc != FZ_OK:
         raise FzError(rc, "fz_create(%d) failed" % device)
     return h
@@ -150,6 +154,10 @@ def fz_last_error(ctx):
 
 def fz_set_pointer_workspace(ctx, nbytes):
     _check(ctx, load_library().fz_set_pointer_workspace(ctx, int(nbytes)))
+
+
+def fz_debug_set(ctx, what, value):
+    _check(ctx, load_library().fz_debug_set(ctx, int(what), int(value)))
 
 
 def _stream_handle(stream):
@@ -275,9 +283,9 @@ def fz_copy_cigar(ctx, dst, words, stream=None):
 class Context:
     """Owns one fz_ctx; `extend` and `local` wrap fz_extend_batch."""
 
-    def __init__(self, device=0):
+    def __init__(self, device=0, workspace_bytes=0):
         self.device = device
-        self.h = fz_create(device)
+        self.h = fz_create(device, workspace_bytes)
 
     def close(self):
         if self.h:

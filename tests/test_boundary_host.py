@@ -34,6 +34,8 @@ def test_struct_sizes_match_header():
     assert ctypes.sizeof(fz.fz_scoring) == 20
     assert ctypes.sizeof(fz.fz_matrix) == 17 * 4           # sub[4][4] and n_score
     assert ctypes.sizeof(fz.fz_seed_stats) == 11 * 4       # eleven float phase times
+    # fz_stats: 17 uint64 counters (bin_hist holds 8), seven float times, padding to 8 bytes
+    assert ctypes.sizeof(fz.fz_stats) == 17 * 8 + 7 * 4 + 4
 
 
 def test_null_context_is_rejected():
@@ -49,13 +51,16 @@ def test_null_context_is_rejected():
     n = ctypes.c_uint64(7)
     assert lib.fz_find_seeds(None, None, 0, None, 0, 19, 0, 0, None, ctypes.byref(n), None, None, None) == fz.FZ_EINVAL
     assert lib.fz_copy_seeds(None, None, 0, None) == fz.FZ_EINVAL
+    assert lib.fz_debug_set(None, fz.FZ_DEBUG_SHRINK_ROWS, 1) == fz.FZ_EINVAL
+    assert lib.fz_extend_batch_noalloc(None, None, 0, None, 0, None, 0, ctypes.byref(sc), None, 9400, 0, None,
+                                       None, None) == fz.FZ_EINVAL
     lib.fz_destroy(None)
 
 
 def test_create_bad_device_fails_cleanly():
     lib = fz.load_library()
     h = ctypes.c_void_p()
-    assert lib.fz_create(ctypes.byref(h), 10_000) != fz.FZ_OK
+    assert lib.fz_create(ctypes.byref(h), 10_000, 0) != fz.FZ_OK
     assert not h.value
 
 

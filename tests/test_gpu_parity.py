@@ -303,6 +303,58 @@ def test_pointer_workspace_batches(ctx):
     compare(gh, gc, oh, ow, oo, label="executor batches")
 
 
+def test_workspace_cap_at_create():
+    """fz_create's workspace_bytes caps the pointer workspace as
+    fz_set_pointer_workspace does: many batches, the same results."""
+    w = W.executor_heavy(n_pairs=40, len_min=300, len_max=3000, seed=6)
+    c0 = fz.Context(0)
+    c1 = fz.Context(0, workspace_bytes=4 << 20)
+    try:
+        ref = run_gpu(c0, w)
+        gh, gc, st = run_gpu(c1, w)
+    finally:
+        c0.close()
+        c1.close()
+    assert st["n_batches"] > 1
+    assert np.array_equal(gh, ref[0]) and np.array_equal(gc, ref[1])
+
+
+def test_executor_mismatch_is_reported(ctx):
+    """A forced disagreement between executor and inspector (every executor
+    side gets one pointer-row word fewer than the inspector sized, so the
+    executor's row-capacity check trips) comes back as FZ_HIT_EEXEC on the
+    affected seeds, without a CIGAR, while scores and coordinates stay the
+    oracle's; seeds traced wholly in the inspector are untouched."""
+    w = W.tiny(n_seeds=150, seed=12)
+    oh, ow, oo = run_oracle(w)
+    fz.fz_debug_set(ctx.h, fz.FZ_DEBUG_SHRINK_ROWS, 1)
+    try:
+        gh, gc, st = run_gpu(ctx, w)
+    finally:
+        fz.fz_debug_set(ctx.h, fz.FZ_DEBUG_SHRINK_ROWS, 0)
+    assert st["n_executor"] > 0
+    eager_both = fz.FZ_HIT_EAGER_LEFT | fz.FZ_HIT_EAGER_RIGHT
+    n_flagged = 0
+    for k in range(len(oh)):
+        g = dict(zip(fz.HIT_FIELDS, gh[k].tolist()))
+        for gf, of in (("score", "score"), ("t_begin", "t_begin"), ("t_end", "t_end"), ("q_begin", "q_begin"),
+                       ("q_end", "q_end")):
+            assert g[gf] == int(oh[of][k]), (k, gf)
+        if (g["status"] & eager_both) == eager_both:
+            assert g["status"] & fz.FZ_HIT_TRACED and not g["status"] & fz.FZ_HIT_EEXEC, k
+        else:
+            assert g["status"] & fz.FZ_HIT_EEXEC and not g["status"] & fz.FZ_HIT_TRACED, k
+            assert g["cigar_len"] == 0
+            n_flagged += 1
+    assert n_flagged > 0
+    # normal sizing again: every field matches
+    gh, gc, st = run_gpu(ctx, w)
+    compare(gh, gc, oh, ow, oo, label="after shrink")
+    assert st["max_band"] > 0 and st["ms_walk"] > 0
+    with pytest.raises(fz.FzError):
+        fz.fz_debug_set(ctx.h, 99, 1)
+
+
 # --------------------------------------------------------------- local --
 
 def test_local_small_full(ctx):
