@@ -3,10 +3,13 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one whole fz_extend_batch call (every phase of the path) over the
-workload's batch, inputs already resident in device memory.  Prints one JSON
-line: GCUPS (canonical cells / step time), seed extensions per second, the
-roofline of the dominant kernel (integer VALU bound), and the CPU oracle
-timed on a bounded sample of the same batch on this host's cores.
+workload's batch, inputs already resident in device memory; the reported
+step time is the median over the timed steps.  Prints one JSON line: GCUPS
+(canonical cells / step time), seed extensions per second, the roofline of
+the dominant kernel (integer VALU bound) and of the whole call against the
+same peak (roofline.end_to_end), the int32 VALU rate measured by a probe
+kernel beside the peak from unit counts, and the CPU oracle timed on a
+bounded sample of the same batch on this host's cores.
 
 Workloads (seeded, synthetic; see smith_waterman_dp_amd/workloads.py):
   skewed          one million 19-mer seeds on a 10 Mbp pair (default)
@@ -374,6 +377,39 @@ def bench_pipeline(a):
     print(json.dumps(out), flush=True)
 
 
+def call_overhead_ms(ctx, T, Q, S, w, min_tb, calls=20):
+    """Median wall time of a one-seed call: the fixed cost of the call's
+    launches and its host read-backs of sizes."""
+    import numpy as np
+    import torch
+    one = S[:1].contiguous()
+    times = []
+    for _ in range(calls):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        ctx.extend(T, Q, one, w["scoring"], w["ydrop"], min_tb, traceback=w.get("traceback", True))
+        torch.cuda.synchronize()
+        times.append((time.perf_counter() - t) * 1e3)
+    return float(np.median(times))
+
+
+def measured_valu_peak():
+    """int32 add/max issue rate measured by libfz_probe.so (TOP/s of lane
+    operations), or None when the probe is not built."""
+    import ctypes
+    path = os.path.join(ROOT, "smith_waterman_dp_amd", "libfz_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.fz_probe_valu.restype = ctypes.c_int
+    lib.fz_probe_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float),
+                                  ctypes.POINTER(ctypes.c_double)]
+    ms, ops = ctypes.c_float(0), ctypes.c_double(0)
+    if lib.fz_probe_valu(0, 8, 1 << 14, ctypes.byref(ms), ctypes.byref(ops)) != 0 or ms.value <= 0:
+        return None
+    return round(ops.value / (ms.value / 1e3) / 1e12, 3)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -419,15 +455,19 @@ def main():
         step()
         print("[bench] warmup %d done" % k, file=sys.stderr, flush=True)
     torch.cuda.synchronize()
-    main_ms = []
+    main_ms, step_ms = [], []
     t0 = time.perf_counter()
     hits = None
     st = None
     for k in range(steps):
+        ts = time.perf_counter()
         hits, cig, st = step()
+        torch.cuda.synchronize()
+        step_ms.append((time.perf_counter() - ts) * 1e3)
         main_ms.append(st["ms_main"])
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    call_ms = None if local or rounds else call_overhead_ms(ctx, T, Q, S, w, min_tb)
     plain_ms = None
     if rounds:
         # the same seeds as one ordinary batch, for comparison (not timed above)
@@ -439,10 +479,11 @@ def main():
     h = hits.cpu().numpy()
     cells = int(h[:, 8].sum())
     n = len(w["seeds"])
-    ms_per_step = dt / steps * 1e3
+    # the median step (every step is one call, synchronised at its end)
+    ms_per_step = float(np.median(step_ms))
     gcups = cells / (ms_per_step / 1e3) / 1e9
     ops = OPS_PER_CELL["local" if local else "extend"]
-    kern_s = float(np.mean(main_ms)) / 1e3
+    kern_s = float(np.median(main_ms)) / 1e3
     achieved = ops * cells / kern_s / 1e12
     peak = VALU_PEAK_OPS / 1e12
     traffic = None
@@ -450,7 +491,10 @@ def main():
         traffic = measured_traffic(TRAFFIC_FETCH_BYTES, TRAFFIC_WRITE_BYTES, kern_s)
     cfg = {"workload": a.workload, "records": n, "target_bp": int(w["target"].size), "query_bp": int(w["query"].size),
            "cells_per_step": cells, "scoring": w["scoring"], "ydrop": None if local else w["ydrop"],
-           "min_traceback_score": w.get("min_tb"), "main_kernel_ms": round(kern_s * 1e3, 3)}
+           "min_traceback_score": w.get("min_tb"), "main_kernel_ms": round(kern_s * 1e3, 3),
+           "timing": "median of %d steps after %d warm-up; mean %.3f ms" % (steps, a.warmup, dt / steps * 1e3)}
+    if call_ms is not None:
+        cfg["call_ms"] = round(call_ms, 3)
     if not local:
         cfg["extensions_per_sec"] = round(n / (ms_per_step / 1e3), 1)
         # last step's statistics (phase times are stream-event spans; "exec"
@@ -460,7 +504,8 @@ def main():
         cfg["executor_sides"] = int(st["n_executor"])
         cfg["executor_batches"] = int(st["n_batches"])
         cfg["phase_ms"] = {k[3:]: round(float(st[k]), 1) for k in
-                           ("ms_pack", "ms_inspect", "ms_bin", "ms_exec", "ms_gather")}
+                           ("ms_pack", "ms_inspect", "ms_bin", "ms_exec", "ms_walk", "ms_gather")}
+        cfg["max_band"] = int(st["max_band"])
     if rounds:
         from smith_waterman_dp_amd import fz as _fz
         cfg["round_size"] = a.round_size
@@ -479,7 +524,13 @@ def main():
            "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(peak, 3), "unit": "TOP/s",
                         "frac": round(achieved / peak, 4), "traffic": traffic,
                         "kernel": "local_kernel" if local else "extend_kernel (inspector)",
-                        "ops_per_cell": ops}}
+                        "ops_per_cell": ops,
+                        # the whole call against the same peak: ops_per_cell x GCUPS
+                        "end_to_end": {"achieved": round(ops * gcups / 1e3, 3),
+                                       "frac": round(ops * gcups / 1e3 / peak, 4)}}}
+    probe = measured_valu_peak()
+    if probe is not None:
+        out["roofline"]["peak_measured"] = probe
     if not a.no_cpu:
         print("[bench] CPU oracle sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds, local)

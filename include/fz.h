@@ -145,8 +145,16 @@ enum {
     FZ_QUERY_RC = 1u << 3,         /* seeds lie on the query's reverse complement (see below) */
     FZ_SEEDS_ALL = 1u << 4,        /* fz_find_seeds: every shared k-mer, no diagonal dedup */
     FZ_SEEDS_REUSE_INDEX = 1u << 5,/* fz_find_seeds: reuse the target index of an earlier call */
-    FZ_ROUNDS_DOUBLING = 1u << 6   /* fz_extend_rounds: each round twice the size of the one before */
+    FZ_ROUNDS_DOUBLING = 1u << 6,  /* fz_extend_rounds: each round twice the size of the one before */
+    FZ_EXACT32 = 1u << 7           /* fz_extend_batch: keep every cell in a 32-bit lane (see below) */
 };
+
+/* FZ_EXACT32: by default, scorings with int8 match / transition /
+ * transversion, ydrop <= 16000 and gap_open + 2 * gap_extend <= 4000 are
+ * computed with two cells per 32-bit lane register (16-bit values relative
+ * to the y-drop threshold, which hold every value that can decide a result
+ * exactly); the results are identical either way.  This flag keeps the
+ * 32-bit layouts, e.g. to check that. */
 
 /* FZ_QUERY_RC: the call aligns the target against the reverse complement
  * of `query` (base j of it is the complement of query[query_len - 1 - j];
@@ -256,7 +264,7 @@ int fz_extend_batch(fz_ctx *ctx,
  */
 #define FZ_NOALLOC_MAX_SEEDS 65536
 #define FZ_NOALLOC_MAX_BASES 4194304
-#define FZ_NOALLOC_SCRATCH_BYTES 41943040
+#define FZ_NOALLOC_SCRATCH_BYTES 83886080
 int fz_extend_batch_noalloc(fz_ctx *ctx,
                             const uint8_t *target, uint64_t target_len,
                             const uint8_t *query, uint64_t query_len,

@@ -10,11 +10,13 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfz.so")
+PROBE_LIB = os.path.join(HERE, "libfz_probe.so")
 ARCH = os.environ.get("FZ_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["fz_lib.hip"]
+PROBE_SOURCES = ["fz_probe.hip"]
 HEADERS = ["fz_device.hpp", "fz_extend.hpp", "fz_aux.hpp", "fz_local.hpp", "fz_seeds.hpp", "fz_rounds.hpp",
-           "fz_sort.hpp"]
+           "fz_sort.hpp", "fz_packed.hpp"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -32,14 +34,20 @@ def hipcc():
     return "hipcc"
 
 
-def build(verbose=False, extra=()):
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+def _compile(srcs, lib, verbose, extra):
+    tmp = lib + ".tmp"
     cmd = [hipcc()] + FLAGS + list(extra) + ["-I", os.path.join(HERE, "..", "include")] + srcs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False, extra=()):
+    """libfz.so (the library) and libfz_probe.so (the VALU-rate probe the
+    benchmark reports beside the peak from unit counts)."""
+    _compile([os.path.join(CSRC, s) for s in SOURCES], LIB, verbose, extra)
+    _compile([os.path.join(CSRC, s) for s in PROBE_SOURCES], PROBE_LIB, verbose, extra)
     return LIB
 
 

@@ -16,8 +16,13 @@ namespace fz {
 // (the seed stage).  revcomp: the reverse complement
 // is coded instead (complement = base ^ 3 with A=0, C=1, G=2, T=3; N stays
 // N).  Any other byte sets bit 0 of *err and is coded as A.
+// With fwd16 (role 0 only), the same codes are also written as the 16-bit
+// pairs of the packed layouts: target (2c, 2c + 1) when pk_query is 0,
+// query (2c, 2c) when it is 1 (see pk_target_code, pk_query_code).
 __global__ void pack_kernel(const uint8_t *__restrict__ ascii, int64_t len, uint8_t *__restrict__ fwd,
-                            uint8_t *__restrict__ rev, int64_t padded, uint32_t *err, int revcomp, int role)
+                            uint8_t *__restrict__ rev, int64_t padded, uint32_t *err, int revcomp, int role,
+                            uint16_t *__restrict__ fwd16 = nullptr, uint16_t *__restrict__ rev16 = nullptr,
+                            int pk_query = 0)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     bool bad = false;
@@ -37,6 +42,11 @@ __global__ void pack_kernel(const uint8_t *__restrict__ ascii, int64_t len, uint
         }
         fwd[x] = (uint8_t)code;
         rev[padded - 1 - x] = (uint8_t)code;
+        if (fwd16) {
+            const uint16_t c2 = (uint16_t)((2u * code) | ((2u * code + (pk_query ? 0u : 1u)) << 8));
+            fwd16[x] = c2;
+            rev16[padded - 1 - x] = c2;
+        }
     }
     if (__ballot(bad) && lane_id() == 0) atomicOr(err, 1u);
 }
@@ -48,10 +58,14 @@ struct SeedInfo {
     int64_t status;
 };
 
+// T16f .. Q16r: the 16-bit copies of the packed layouts (may be null when
+// they are not used).
 __global__ void setup_kernel(const fz_seed *__restrict__ seeds, int64_t n, int64_t tlen, int64_t qlen,
                              const uint8_t *Tf, const uint8_t *Tr, const uint8_t *Qf, const uint8_t *Qr,
                              int64_t NT, int64_t NQ, Scoring sc, SideTask *__restrict__ tasks,
-                             SeedInfo *__restrict__ info)
+                             SeedInfo *__restrict__ info, const uint8_t *T16f = nullptr,
+                             const uint8_t *T16r = nullptr, const uint8_t *Q16f = nullptr,
+                             const uint8_t *Q16r = nullptr)
 {
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= n) return;
@@ -81,12 +95,16 @@ __global__ void setup_kernel(const fz_seed *__restrict__ seeds, int64_t n, int64
             for (int64_t c = 0; c < Ls; ++c) ss += sub_pair(Tf[PAD + s.t_pos + c], Qf[PAD + s.q_pos + c], sc);
             in.seed_score = ss;
             L.A = Tr;
+            L.A16 = T16r;
+            L.B16 = Q16f;
             L.abase = NT - 1 - PAD - s.t_pos;
             L.B = Qf;
             L.bbase = PAD + s.q_pos;
             L.m = (int32_t)ml;
             L.n = (int32_t)nl;
             R.A = Tf;
+            R.A16 = T16f;
+            R.B16 = Q16r;
             R.abase = PAD + s.t_pos + Ls - 1;
             R.B = Qr;
             R.bbase = NQ - PAD - s.q_pos - Ls;
@@ -383,7 +401,6 @@ struct WalkArgs {
     int64_t begin, end;
     const uint8_t *ptr_ws;
     int64_t ptr_base_off;
-    int32_t C;
     const SideOut *out;
     const int64_t *run_off;
     uint32_t *runs;
@@ -416,11 +433,14 @@ __device__ __forceinline__ void rle_push(uint32_t *runs, int64_t &n, uint32_t &c
 constexpr int WALK_LANES = 64;
 constexpr int WALK_CHUNK = 2 * WALK_LANES;
 
-template <int C>
+// Rows hold 6 or 8 positions per word (RowHdr); position p of a row is in
+// word p / cpw at nibble shift 4 * (cpw - 1 - p % cpw).
+__device__ __forceinline__ int row_word(int p, bool cpw8) { return cpw8 ? (p >> 3) : p / 6; }
+__device__ __forceinline__ int row_shift(int p, bool cpw8) { return cpw8 ? 4 * (7 - (p & 7)) : 4 * (5 - p % 6); }
+
 __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
 {
-    constexpr int NW = (C + 7) / 8;                      // pointer words per lane per row
-    constexpr int WPR = (WALK_CHUNK / C + 2) * NW;       // words staged per row
+    constexpr int WPR = WALK_CHUNK / 6 + 2;              // words staged per row (at most)
     __shared__ uint32_t wl[WALK_CHUNK][WPR];
     const int lane = lane_id();
     const int64_t k = a.begin + (int64_t)blockIdx.x;
@@ -457,14 +477,17 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
         clen = cnt;
     };
     // the staged pointer nibble of cell (ii, dd - ii) on chunk row r, or 16
-    // when the row does not hold it (fields of row r live in lane r % 64)
-    auto nib_at = [&](int r, int ii, int ib, int w0, int nw) -> uint32_t {
-        const int p = ii - ib;
+    // when the row does not hold it (fields of row r live in lane r % 64;
+    // the row's cell format is the sign bit of ib8, ib8 & 0x7fffffff its ibase
+    // biased by 2^30)
+    auto nib_at = [&](int r, int ii, int ib8, int w0, int nw) -> uint32_t {
+        const bool cpw8 = ib8 < 0;
+        const int p = ii - ((ib8 & 0x7fffffff) - (1 << 30));
         if (p < 0) return 16u;
-        const int w = (p / C) * NW + (p % C) / 8;
+        const int w = row_word(p, cpw8);
         const int q = w - w0;
         if (w >= nw || q < 0 || q >= WPR) return 16u;
-        return (wl[r][q] >> ptr_shift<C>(p % C)) & 0xFu;
+        return (wl[r][q] >> row_shift(p, cpw8)) & 0xFu;
     };
     while (!bad && !(st == 0 && i == 0 && j == 0)) {
         const int d = i + j;
@@ -483,28 +506,32 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
                 h[h2] = hdr[dr];
                 // (clamped to the side's rows, so that no header value can
                 // send a read outside them)
-                const uint32_t next_off = hdr[min(dr + 1, it.dstar)].off;
+                const uint32_t next_off = hdr[min(dr + 1, it.dstar)].off & ~ROW_CPW8;
                 rend[h2] = min(dr < it.dstar ? next_off : total_rows, total_rows);
             }
             uint32_t v[2][WPR];
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 const int dr = dlo + h2 * WALK_LANES + lane;
+                const bool cpw8 = (h[h2].off & ROW_CPW8) != 0;
+                const uint32_t off = h[h2].off & ~ROW_CPW8;
                 const int plo = max(0, i - (d - dr)) - h[h2].ibase;
-                rw0[h2] = plo <= 0 ? 0 : (plo / C) * NW;
-                rnw[h2] = (dr <= d && rend[h2] > h[h2].off) ? (int)(rend[h2] - h[h2].off) : 0;
+                rw0[h2] = plo <= 0 ? 0 : row_word(plo, cpw8);
+                rnw[h2] = (dr <= d && rend[h2] > off) ? (int)(rend[h2] - off) : 0;
                 // words past the highest reachable position (i never grows)
                 // are never read: the row ends there for this chunk, and the
                 // clamped loads below repeat its last word (cache hits)
                 const int phi = i - h[h2].ibase;
-                rnw[h2] = min(rnw[h2], phi < 0 ? 0 : (phi / C) * NW + (phi % C) / 8 + 1);
-                rib[h2] = h[h2].ibase;
+                rnw[h2] = min(rnw[h2], phi < 0 ? 0 : row_word(phi, cpw8) + 1);
+                // ibase biased by 2^30 (rows' ibase lies within +-2^30), the
+                // format in the sign bit
+                rib[h2] = (int)((uint32_t)(h[h2].ibase + (1 << 30)) | (cpw8 ? 0x80000000u : 0u));
 #pragma unroll
                 for (int q = 0; q < WPR; ++q) {
                     // every load in bounds (the side's first word when the
                     // row is empty), all issued before any is used
                     const int w = min(rw0[h2] + q, rnw[h2] - 1);
-                    v[h2][q] = rows[rnw[h2] > 0 ? h[h2].off + (uint32_t)w : 0u];
+                    v[h2][q] = rows[rnw[h2] > 0 ? off + (uint32_t)w : 0u];
                 }
             }
 #pragma unroll

@@ -93,6 +93,8 @@ __host__ __device__ inline int sub_pair(uint32_t ta, uint32_t qb, const Scoring 
 struct SideTask {
     const uint8_t *A;
     const uint8_t *B;
+    const uint8_t *A16;         // the same sequences as 16-bit codes (packed layouts), same element index
+    const uint8_t *B16;
     int64_t abase, bbase;
     int32_t m, n;               // m < 0: skip (invalid seed)
     int32_t seed, side;         // side 0 = left, 1 = right
@@ -117,11 +119,21 @@ struct ExecItem {
     int64_t batch;
 };
 
-// Row header of the executor's pointer store, one per anti-diagonal.
+// Row header of the executor's pointer store, one per anti-diagonal.  A
+// row word holds 6 or 8 consecutive positions' nibbles, the first position
+// in the highest nibble: 8 when off carries ROW_CPW8 (the 1024-position and
+// the packed 256-position layouts), 6 otherwise (the 192- and 384-position
+// layouts, which keep the six-cells-per-word format).
+constexpr uint32_t ROW_CPW8 = 0x80000000u;
 struct RowHdr {
-    uint32_t off;               // dword offset of the row inside the side's row area
+    uint32_t off;               // dword offset of the row inside the side's row area (| ROW_CPW8)
     int32_t ibase;              // i of slot 0 of the row's first lane
 };
+
+// Entries per array of the LDS hand-over between layouts (S of two
+// diagonals and the two gap states of the union of the last two hulls,
+// which is at most 256 positions wide when a side changes layout).
+constexpr int XFER_STRIDE = 256;
 
 // ----------------------------------------------------------- wave helpers --
 

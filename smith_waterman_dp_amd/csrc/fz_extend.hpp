@@ -341,7 +341,7 @@ struct SideDP {
             }
             if (lane == 0) {
                 RowHdr h;
-                h.off = rowoff;
+                h.off = rowoff | (NWORD == 2 ? ROW_CPW8 : 0u);
                 h.ibase = rlane0 * C + od;
                 hdr[d] = h;
             }
@@ -515,7 +515,7 @@ struct SideDP {
     // -inf, and the handed-on gap values come from dead cells, which lie
     // below the threshold and act as -inf (see the top of this file).  x
     // holds four arrays of XFER_W entries, indexed by position - ul.
-    static constexpr int XFER_W = 192;
+    static constexpr int XFER_W = XFER_STRIDE;
     __device__ __forceinline__ void export_regs(uint32_t *x, int ul, int uh) const
     {
         // (an opaque base keeps per-slot position constants from being
@@ -686,77 +686,6 @@ __device__ __forceinline__ SideResult run_side(const SideTask &task, const Scori
                 return r;
             }
             switch_layout(dn, dw, xfer, d);
-        }
-    }
-}
-
-// One wave per side; the grid covers the work list (the hardware dispatcher
-// hands waves to CUs as others retire, which balances sides of very
-// different lengths).  Register budgets of the standard kernels: the
-// inspector fits 64 VGPRs (8 waves per SIMD), the executor 72 (7 waves)
-// with byte substitution scores and 80 (6) without; more waves let a SIMD
-// pair one wave's VALU instruction with another's SALU instruction.
-template <int C, bool EXEC, int SUB, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <= 8 ? (EXEC ? (SUB != SUB_WIDE ? 7 : 6) : 8) : 1))) void extend_kernel(ExtendArgs a)
-{
-    using DP = SideDP<C, EXEC, SUB>;
-    using EDP = SideDP<StartLayout<C>::value, EXEC, SUB>;     // holds the eager block
-    __shared__ uint32_t eager_lds_all[WAVES][EAGER_ROWS * EDP::NEL * EDP::NWORD];
-    __shared__ uint32_t xfer_all[WAVES][C == 6 ? 4 * DP::XFER_W : 1];
-    const int wv = uniform((int)(threadIdx.x / 64));
-    uint32_t *eager_lds = eager_lds_all[wv];
-    uint32_t *xfer = xfer_all[wv];
-    const int idx = (int)blockIdx.x * WAVES + wv;
-    if (idx >= a.nlist) return;
-    const int64_t item = EXEC ? a.exec_begin + idx : (int64_t)idx;
-    const int sid = EXEC ? a.exec[item].side : (a.list ? a.list[item] : (int)item);
-    const SideTask task = a.tasks[sid];
-    SideOut *o = &a.out[sid];
-    if (task.m < 0) {
-        if (!EXEC && fresh_lane_id() == 0) {
-            SideOut r = {};
-            r.flags = SO_SKIPPED;
-            *o = r;
-        }
-        return;
-    }
-    if (EXEC) {
-        const ExecItem it = a.exec[item];
-        const SideResult x = run_side<C, EXEC, SUB>(task, a.sc, it.dstar, nullptr, xfer,
-                                                      a.ptr_ws + (it.ptr_off - a.ptr_base_off), it.ptr_bytes);
-        if (fresh_lane_id() == 0) {
-            atomicAdd((unsigned long long *)a.exec_cells, (unsigned long long)x.cells);
-            if (x.overflow || x.best != o->score || x.bi != o->ie) atomicOr(&o->flags, SO_EXEC_MISMATCH);
-        }
-        return;
-    }
-    const SideResult x = run_side<C, EXEC, SUB>(task, a.sc, 0x7fffffff, eager_lds, xfer, nullptr, 0);
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    SideOut r;
-    r.score = x.best;
-    r.ie = x.bi;
-    r.je = x.bj;
-    r.dend = x.dend;
-    r.cells = x.cells;
-    r.ptr_bytes = x.ptr_at_best;
-    r.flags = (x.overflow ? SO_OVERFLOW : 0) | a.result_flags;
-    r.eager_len = 0;
-    r.max_band = x.band;
-    r.pad_ = 0;
-    if (!x.overflow && x.bi <= EAGER_EDGE && x.bj <= EAGER_EDGE) {
-        // the best cell lies in the eager block, which the start layout
-        // kept (no layout change happens before diagonal 34)
-        EDP e(task, a.sc);
-        e.bi = x.bi;
-        e.bj = x.bj;
-        r.flags |= SO_EAGER;
-        r.eager_len = e.eager_walk(eager_lds, a.eager_ops + (int64_t)sid * EAGER_OPS);
-    }
-    if (fresh_lane_id() == 0) {
-        *o = r;
-        if (x.overflow) {
-            const uint32_t k = atomicAdd(a.overflow_count, 1u);
-            a.overflow_list[k] = sid;
         }
     }
 }

@@ -30,6 +30,7 @@
 #include "fz_aux.hpp"
 #include "fz_device.hpp"
 #include "fz_extend.hpp"
+#include "fz_packed.hpp"
 #include "fz_local.hpp"
 #include "fz_seeds.hpp"
 #include "fz_rounds.hpp"
@@ -93,7 +94,11 @@ constexpr int64_t NA_TF = 0;
 constexpr int64_t NA_TR = NA_TF + na_up(NA_SEQ);
 constexpr int64_t NA_QF = NA_TR + na_up(NA_SEQ);
 constexpr int64_t NA_QR = NA_QF + na_up(NA_SEQ);
-constexpr int64_t NA_TASKS = NA_QR + na_up(NA_SEQ);
+constexpr int64_t NA_TF16 = NA_QR + na_up(NA_SEQ);
+constexpr int64_t NA_TR16 = NA_TF16 + na_up(2 * NA_SEQ);
+constexpr int64_t NA_QF16 = NA_TR16 + na_up(2 * NA_SEQ);
+constexpr int64_t NA_QR16 = NA_QF16 + na_up(2 * NA_SEQ);
+constexpr int64_t NA_TASKS = NA_QR16 + na_up(2 * NA_SEQ);
 constexpr int64_t NA_INFO = NA_TASKS + na_up(NA_SIDES * (int64_t)sizeof(SideTask));
 constexpr int64_t NA_OUT = NA_INFO + na_up(FZ_NOALLOC_MAX_SEEDS * (int64_t)sizeof(SeedInfo));
 constexpr int64_t NA_EAGER = NA_OUT + na_up(NA_SIDES * (int64_t)sizeof(SideOut));
@@ -122,6 +127,7 @@ struct fz_ctx {
     std::vector<hipEvent_t> walk_ev;    // brackets of the walker launches (FZ_STATS)
     uint64_t last_words = 0;            // CIGAR words of the last successful call
     DevBuf Tf, Tr, Qf, Qr;
+    DevBuf Tf16, Tr16, Qf16, Qr16;      // 16-bit code copies of the packed layouts
     DevBuf tasks, info, out, eager, side_trace, run_cap, run_off, run_len, runs;
     DevBuf items, batch_first, scan_tmp, cig, cigar, counters, ovl0, ovl1, bnd;
     DevBuf rs_cnt, ps_tmp;              // radix-sort digit counts, tile totals of the generic scans
@@ -324,11 +330,25 @@ Scoring make_scoring(const fz_scoring *s, const fz_matrix *mx, int32_t ydrop)
     return sc;
 }
 
+// The packed 16-bit layouts give the same results as the 32-bit ones for
+// scorings within their exact range (fz_packed.hpp).
+bool packed_ok(const Scoring &sc, uint32_t flags)
+{
+    return !(flags & FZ_EXACT32) && sc.mode == SUB_LUT && sc.ydrop <= PK_MAX_YDROP && sc.oe + sc.e <= PK_MAX_OE;
+}
+
 template <int C, bool EXEC>
-int launch_extend(fz_ctx *ctx, const ExtendArgs &a, int64_t nwork, hipStream_t st)
+int launch_extend(fz_ctx *ctx, const ExtendArgs &a, int64_t nwork, hipStream_t st, bool pk = false)
 {
     if (nwork <= 0) return FZ_OK;
     const unsigned blocks = (unsigned)((nwork + EXT_WAVES - 1) / EXT_WAVES);
+    if constexpr (C == C_STD) {
+        if (pk) {
+            extend_kernel<C, EXEC, SUB_LUT, EXT_WAVES, true><<<blocks, 64 * EXT_WAVES, 0, st>>>(a);
+            HIP_OK(hipGetLastError());
+            return FZ_OK;
+        }
+    }
     if (a.sc.mode == SUB_MATRIX) extend_kernel<C, EXEC, SUB_MATRIX, EXT_WAVES><<<blocks, 64 * EXT_WAVES, 0, st>>>(a);
     else if (a.sc.mode == SUB_LUT) extend_kernel<C, EXEC, SUB_LUT, EXT_WAVES><<<blocks, 64 * EXT_WAVES, 0, st>>>(a);
     else extend_kernel<C, EXEC, SUB_WIDE, EXT_WAVES><<<blocks, 64 * EXT_WAVES, 0, st>>>(a);
@@ -357,7 +377,7 @@ int check_args(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const uint8_t 
         sc->transition < -lim || sc->transversion > lim || sc->transversion < -lim)
         return fail(ctx, FZ_EINVAL, "scoring values must lie in [-2^24, 2^24]");
     if (!(flags & FZ_LOCAL) && ydrop < 0) return fail(ctx, FZ_EINVAL, "ydrop must be >= 0");
-    if (flags & ~(uint32_t)(FZ_TRACEBACK | FZ_LOCAL | FZ_STATS | FZ_QUERY_RC))
+    if (flags & ~(uint32_t)(FZ_TRACEBACK | FZ_LOCAL | FZ_STATS | FZ_QUERY_RC | FZ_EXACT32))
         return fail(ctx, FZ_EINVAL, "unknown flag bits");
     if ((flags & FZ_LOCAL) && (flags & FZ_TRACEBACK)) return fail(ctx, FZ_EINVAL, "local mode has no traceback");
     return FZ_OK;
@@ -706,7 +726,8 @@ void fz_destroy(fz_ctx *ctx)
     int prev = 0;
     (void)hipGetDevice(&prev);
     (void)hipSetDevice(ctx->device);
-    DevBuf *bufs[] = {&ctx->Tf, &ctx->Tr, &ctx->Qf, &ctx->Qr, &ctx->tasks, &ctx->info, &ctx->out,
+    DevBuf *bufs[] = {&ctx->Tf, &ctx->Tr, &ctx->Qf, &ctx->Qr, &ctx->Tf16, &ctx->Tr16, &ctx->Qf16, &ctx->Qr16,
+                      &ctx->tasks, &ctx->info, &ctx->out,
                       &ctx->eager, &ctx->side_trace, &ctx->run_cap, &ctx->run_off, &ctx->run_len, &ctx->runs,
                       &ctx->items, &ctx->batch_first, &ctx->scan_tmp, &ctx->cig, &ctx->cigar,
                       &ctx->counters, &ctx->ovl0, &ctx->ovl1, &ctx->bnd,
@@ -788,17 +809,27 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     ENSURE(ctx->Tr, NT + 64);
     ENSURE(ctx->Qf, NQ + 64);
     ENSURE(ctx->Qr, NQ + 64);
+    const bool pk = !(flags & FZ_LOCAL) && packed_ok(sc, flags);
+    if (pk) {
+        ENSURE(ctx->Tf16, 2 * (NT + 64));
+        ENSURE(ctx->Tr16, 2 * (NT + 64));
+        ENSURE(ctx->Qf16, 2 * (NQ + 64));
+        ENSURE(ctx->Qr16, 2 * (NQ + 64));
+    }
     {
         const unsigned bt = std::min<int64_t>(blocks_for(NT, 256), 8192);
         const int mxr = sc.mode == SUB_MATRIX ? 1 : 0;     // matrix mode: role codes, N accepted
         pack_kernel<<<bt, 256, 0, st>>>(target, (int64_t)tlen, as<uint8_t>(ctx->Tf), as<uint8_t>(ctx->Tr), NT,
-                                        &dc->err, 0, mxr);
+                                        &dc->err, 0, mxr, pk ? as<uint16_t>(ctx->Tf16) : nullptr,
+                                        pk ? as<uint16_t>(ctx->Tr16) : nullptr, 0);
         HIP_OK(hipGetLastError());
         const unsigned bq = std::min<int64_t>(blocks_for(NQ, 256), 8192);
         // with FZ_QUERY_RC every later step sees the query's reverse
         // complement: seeds, windows and results are in its coordinates
         pack_kernel<<<bq, 256, 0, st>>>(query, (int64_t)qlen, as<uint8_t>(ctx->Qf), as<uint8_t>(ctx->Qr), NQ,
-                                        &dc->err, (flags & FZ_QUERY_RC) ? 1 : 0, 2 * mxr);
+                                        &dc->err, (flags & FZ_QUERY_RC) ? 1 : 0, 2 * mxr,
+                                        pk ? as<uint16_t>(ctx->Qf16) : nullptr, pk ? as<uint16_t>(ctx->Qr16) : nullptr,
+                                        1);
         HIP_OK(hipGetLastError());
     }
     Counters hc;
@@ -831,7 +862,10 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     setup_kernel<<<blocks_for(n, 256), 256, 0, st>>>(seeds, n, (int64_t)tlen, (int64_t)qlen, as<uint8_t>(ctx->Tf),
                                                       as<uint8_t>(ctx->Tr), as<uint8_t>(ctx->Qf),
                                                       as<uint8_t>(ctx->Qr), NT, NQ, sc, as<SideTask>(ctx->tasks),
-                                                      as<SeedInfo>(ctx->info));
+                                                      as<SeedInfo>(ctx->info), pk ? as<uint8_t>(ctx->Tf16) : nullptr,
+                                                      pk ? as<uint8_t>(ctx->Tr16) : nullptr,
+                                                      pk ? as<uint8_t>(ctx->Qf16) : nullptr,
+                                                      pk ? as<uint8_t>(ctx->Qr16) : nullptr);
     HIP_OK(hipGetLastError());
     tm.mark();
 
@@ -850,7 +884,7 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     ea.result_flags = 0;
     ea.sc = sc;
     HIP_OK(hipEventRecord(ctx->kev[0], st));
-    rc = launch_extend<C_STD, false>(ctx, ea, nsides, st);
+    rc = launch_extend<C_STD, false>(ctx, ea, nsides, st, pk);
     if (rc) return rc;
     HIP_OK(hipEventRecord(ctx->kev[1], st));
     if ((rc = read_counters())) return rc;
@@ -1000,7 +1034,7 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
                 xa.nlist = (int32_t)(s1 - s0);
                 xa.ptr_ws = wsp;
                 xa.ptr_base_off = b * step;
-                rc = cls == 0 ? launch_extend<C_STD, true>(ctx, xa, s1 - s0, xst)
+                rc = cls == 0 ? launch_extend<C_STD, true>(ctx, xa, s1 - s0, xst, pk)
                               : launch_extend<C_WIDE, true>(ctx, xa, s1 - s0, xst);
                 if (rc) return rc;
                 WalkArgs wk;
@@ -1009,7 +1043,6 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
                 wk.end = s1;
                 wk.ptr_ws = wsp;
                 wk.ptr_base_off = b * step;
-                wk.C = cls == 0 ? C_STD : C_WIDE;
                 wk.out = as<SideOut>(ctx->out);
                 wk.run_off = as<int64_t>(ctx->run_off);
                 wk.runs = as<uint32_t>(ctx->runs);
@@ -1023,8 +1056,7 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
                     }
                     HIP_OK(hipEventRecord(ctx->walk_ev[2 * n_walks], xst));
                 }
-                if (cls == 0) walk_wave_kernel<C_STD><<<(unsigned)(s1 - s0), 64, 0, xst>>>(wk);
-                else walk_wave_kernel<C_WIDE><<<(unsigned)(s1 - s0), 64, 0, xst>>>(wk);
+                walk_wave_kernel<<<(unsigned)(s1 - s0), 64, 0, xst>>>(wk);
                 HIP_OK(hipGetLastError());
                 if (tm.on) HIP_OK(hipEventRecord(ctx->walk_ev[2 * n_walks++ + 1], xst));
             }
@@ -1121,6 +1153,11 @@ static int noalloc_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const
     const Scoring sc = make_scoring(scoring, matrix, ydrop);
     const int64_t NT = (int64_t)tlen + 2 * PAD, NQ = (int64_t)qlen + 2 * PAD;
     uint8_t *Tf = base + NA_TF, *Tr = base + NA_TR, *Qf = base + NA_QF, *Qr = base + NA_QR;
+    const bool pk = packed_ok(sc, flags);
+    uint16_t *Tf16 = pk ? reinterpret_cast<uint16_t *>(base + NA_TF16) : nullptr;
+    uint16_t *Tr16 = pk ? reinterpret_cast<uint16_t *>(base + NA_TR16) : nullptr;
+    uint16_t *Qf16 = pk ? reinterpret_cast<uint16_t *>(base + NA_QF16) : nullptr;
+    uint16_t *Qr16 = pk ? reinterpret_cast<uint16_t *>(base + NA_QR16) : nullptr;
     SideTask *tasks = reinterpret_cast<SideTask *>(base + NA_TASKS);
     SeedInfo *info = reinterpret_cast<SeedInfo *>(base + NA_INFO);
     SideOut *out = reinterpret_cast<SideOut *>(base + NA_OUT);
@@ -1130,13 +1167,16 @@ static int noalloc_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const
     if (rc) return rc;
     const int mxr = sc.mode == SUB_MATRIX ? 1 : 0;
     pack_kernel<<<std::min<int64_t>(blocks_for(NT, 256), 8192), 256, 0, st>>>(target, (int64_t)tlen, Tf, Tr, NT,
-                                                                                &dc->err, 0, mxr);
+                                                                                &dc->err, 0, mxr, Tf16, Tr16, 0);
     HIP_OK(hipGetLastError());
     pack_kernel<<<std::min<int64_t>(blocks_for(NQ, 256), 8192), 256, 0, st>>>(
-        query, (int64_t)qlen, Qf, Qr, NQ, &dc->err, (flags & FZ_QUERY_RC) ? 1 : 0, 2 * mxr);
+        query, (int64_t)qlen, Qf, Qr, NQ, &dc->err, (flags & FZ_QUERY_RC) ? 1 : 0, 2 * mxr, Qf16, Qr16, 1);
     HIP_OK(hipGetLastError());
     setup_kernel<<<blocks_for(n, 256), 256, 0, st>>>(seeds, n, (int64_t)tlen, (int64_t)qlen, Tf, Tr, Qf, Qr, NT, NQ,
-                                                      sc, tasks, info);
+                                                      sc, tasks, info, reinterpret_cast<uint8_t *>(Tf16),
+                                                      reinterpret_cast<uint8_t *>(Tr16),
+                                                      reinterpret_cast<uint8_t *>(Qf16),
+                                                      reinterpret_cast<uint8_t *>(Qr16));
     HIP_OK(hipGetLastError());
     const int64_t nsides = 2 * n;
     ExtendArgs ea = {};
@@ -1151,7 +1191,7 @@ static int noalloc_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const
     ea.result_flags = 0;
     ea.sc = sc;
     HIP_OK(hipEventRecord(ctx->kev[0], st));
-    rc = launch_extend<C_STD, false>(ctx, ea, nsides, st);
+    rc = launch_extend<C_STD, false>(ctx, ea, nsides, st, pk);
     if (rc) return rc;
     HIP_OK(hipEventRecord(ctx->kev[1], st));
     Counters hc;

@@ -1,0 +1,673 @@
+// fz_packed.hpp -- the extension's cell sweep with two cells per 32-bit lane
+// register (gfx950 packed 16-bit integer VALU).
+//
+// The layouts here hold C = 2 * C2 positions per lane (C2 registers per
+// state, two positions per register: the even one in the low half, the odd
+// one in the high half), so one v_pk_* instruction updates two cells.  They
+// take over from the 32-bit layout of fz_extend.hpp once the eager block is
+// done (diagonal 34) and run the rest of the side, for the inspector and the
+// executor alike, with the same window geometry, ranges, slides, kills and
+// pointer rows as the 32-bit layouts (FastZ section 2.2 and section 3.2: one
+// wave per extension, three rolling anti-diagonals in registers).
+//
+// Scores relative to the threshold.  Each stored value is V = S - T, where
+// T is the y-drop threshold of the next diagonal to evaluate.  A cell is live
+// exactly when V >= 0, so the kill is one arithmetic shift (the sign of
+// each half) and one bit select that puts DEAD (-16384) in the dead halves.
+// When the best score grows, T grows by the same amount and every stored
+// value is moved down by it (one packed subtraction per register).  The
+// values that decide anything lie within a few thousand of T: live scores
+// are at most ydrop + (largest substitution score) above it, and the gap
+// states that can still feed a live cell are at most gap_open + gap_extend
+// below it; dead cells and everything built from them stay below -15000.
+// So for ydrop <= PK_MAX_YDROP, |substitution| <= 127 and gap_open +
+// gap_extend <= PK_MAX_OE no value wraps or saturates, and every live value,
+// kill and traceback choice equals the 32-bit computation's.  The host runs
+// other scorings on the 32-bit layouts.
+#pragma once
+
+#include "fz_extend.hpp"
+
+namespace fz {
+
+constexpr int PK_MAX_YDROP = 16000;
+constexpr int PK_MAX_OE = 4000;
+constexpr int32_t PK_DEAD = -16384;
+constexpr uint32_t PK_DEAD2 = 0xC000C000u;          // PK_DEAD in both halves
+constexpr int32_t PK_DEAD_LIMIT = -8192;            // below this a value counts as dead (-inf)
+
+// packed 16-bit helpers; the ones the compiler would scalarize are written
+// as single instructions
+typedef short pk_s16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ pk_s16x2 pk_v(uint32_t x) { return __builtin_bit_cast(pk_s16x2, x); }
+__device__ __forceinline__ uint32_t pk_u(pk_s16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ uint32_t pk_add(uint32_t a, uint32_t b) { return pk_u(pk_v(a) + pk_v(b)); }
+__device__ __forceinline__ uint32_t pk_sub(uint32_t a, uint32_t b) { return pk_u(pk_v(a) - pk_v(b)); }
+__device__ __forceinline__ uint32_t pk_max(uint32_t a, uint32_t b)
+{
+    return pk_u(__builtin_elementwise_max(pk_v(a), pk_v(b)));
+}
+// 0xFFFF in each half whose value is negative, 0 elsewhere.  (An inline
+// constant of a packed instruction is a 32-bit value: op_sel_hi 0 makes
+// the high half read its low 16 bits too.)
+__device__ __forceinline__ uint32_t pk_neg_mask(uint32_t x)
+{
+    uint32_t r;
+    asm("v_pk_ashrrev_i16 %0, 15, %1 op_sel_hi:[0,1]" : "=v"(r) : "v"(x));
+    return r;
+}
+// (m & a) | (~m & b)
+__device__ __forceinline__ uint32_t bit_select(uint32_t m, uint32_t a, uint32_t b)
+{
+    uint32_t r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "s"(a), "v"(b));
+    return r;
+}
+// per half: 1 if the (unsigned) value is 0, else 0
+__device__ __forceinline__ uint32_t pk_is_zero(uint32_t x)
+{
+    uint32_t r;
+    asm("v_pk_sub_u16 %0, 1, %1 op_sel_hi:[0,1] clamp" : "=v"(r) : "v"(x));
+    return r;
+}
+// per half: 1 if the (unsigned) value is not 0, else 0
+__device__ __forceinline__ uint32_t pk_nonzero(uint32_t x)
+{
+    uint32_t r;
+    asm("v_pk_min_u16 %0, %1, 1 op_sel_hi:[1,0]" : "=v"(r) : "v"(x));
+    return r;
+}
+// per half: a * 2 + b (a, b small unsigned)
+__device__ __forceinline__ uint32_t pk_shl1_add(uint32_t a, uint32_t b)
+{
+    uint32_t r;
+    asm("v_pk_mad_u16 %0, %1, 2, %2 op_sel_hi:[1,0,1]" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+// sign-extended low / high half
+__device__ __forceinline__ int pk_lo(uint32_t x) { return (int)(int16_t)(x & 0xFFFFu); }
+__device__ __forceinline__ int pk_hi(uint32_t x) { return (int)(int16_t)(x >> 16); }
+
+// Packed 16-bit codes of the two sequences: a target base a is stored as
+// the byte pair (2a, 2a + 1) and a query base b as (2b, 2b), so that the
+// xor of a target pair and a query pair is the byte pair (2x, 2x + 1) with
+// x = a ^ b: a byte-permute selector for entry x of a table of four int16
+// scores (match, transversion, transition, transversion).
+__host__ __device__ constexpr uint32_t pk_target_code(uint32_t base) { return (2u * base) | ((2u * base + 1u) << 8); }
+__host__ __device__ constexpr uint32_t pk_query_code(uint32_t base) { return (2u * base) | ((2u * base) << 8); }
+
+template <int N> struct Unaligned3;
+template <> struct Unaligned3<3> { typedef uint32_t T __attribute__((ext_vector_type(3), aligned(1))); };
+
+template <int N>
+__device__ __forceinline__ void load_unaligned_pk(const GlobalU8 *p, uint32_t (&out)[N])
+{
+    if constexpr (N == 3) {
+        typedef typename Unaligned3<3>::T V;
+        const V v = *reinterpret_cast<const __attribute__((address_space(1))) V *>(p);
+        out[0] = v[0];
+        out[1] = v[1];
+        out[2] = v[2];
+    } else {
+        load_unaligned<N>(p, out);
+    }
+}
+
+template <int C2, bool EXEC>
+struct SidePk {
+    static constexpr int C = 2 * C2;                 // positions per lane
+    static constexpr int W = 64 * C;
+    static constexpr bool PAIRED = C2 == 2;          // pointer rows: two lanes (16 bits each) per dword
+    static constexpr int CPW = PAIRED ? 8 : C;       // cells per pointer word
+    static constexpr int NWORD = 1;
+    static constexpr int NONE_LO = 1 << 29, NONE_HI = -(1 << 29);
+
+    // registers (packed pairs)
+    uint32_t SA[C2], SB[C2], R[C2], Dn[C2];
+    uint32_t TA[C2], QB[C2], TAn[C2], QBn[C2];
+    uint32_t crossL, crossR;    // DPP targets whose edge lane keeps PK_DEAD2
+    const GlobalU8 *ba, *bb;    // 16-bit code arrays, uniform bases (bytes)
+    uint32_t ua, ub;            // element offsets of slot 0 of lane 0 (as in SideDP)
+    // wave-uniform state
+    int K, dmask;
+    int lo1, hi1, lo2, hi2;
+    int best, bi, bj, dend;     // best: absolute score
+    int T;                      // absolute threshold of the next diagonal; values are stored as S - T
+    int64_t cells, cum_bytes, ptr_at_best;
+    int dflush;
+    int32_t acc_cells, acc_words, bmax;
+    bool overflow;
+    uint32_t rowoff, rowcap;
+    RowHdr *hdr;
+    uint32_t *rows;
+
+    const SideTask &t;
+    const Scoring &sc;
+    int lane;
+    uint32_t oe2, e2, lut_lo, lut_hi;   // packed constants
+
+    __device__ SidePk(const SideTask &task, const Scoring &s) : t(task), sc(s), lane(fresh_lane_id())
+    {
+        oe2 = ((uint32_t)sc.oe & 0xFFFFu) * 0x10001u;
+        e2 = ((uint32_t)sc.e & 0xFFFFu) * 0x10001u;
+        lut_lo = ((uint32_t)sc.match & 0xFFFFu) | ((uint32_t)sc.tv << 16);
+        lut_hi = ((uint32_t)sc.ts & 0xFFFFu) | ((uint32_t)sc.tv << 16);
+    }
+
+    __device__ __forceinline__ void fetch(const GlobalU8 *base, uint32_t off, uint32_t (&out)[C2]) const
+    {
+        load_unaligned_pk<C2>(base + 2u * (off + (uint32_t)(lane * C)), out);
+    }
+
+    __device__ __forceinline__ void reload(int d, int od)
+    {
+        fetch(ba, ua + od, TA);
+        fetch(bb, ub + (od - d), QB);
+        fetch(ba, ua + (od + 1), TAn);
+        fetch(bb, ub + (od - d - 1), QBn);
+    }
+
+    __device__ __forceinline__ void set_dmask() { dmask = min(2 * (t.m - W + 2) - K, 2 * t.n + 1 + K); }
+
+    __device__ __forceinline__ void init_bases()
+    {
+        const int64_t aoff = (t.abase - W - 8) & ~(int64_t)3;
+        const int64_t boff = (t.bbase - (int64_t)t.n - W - 8) & ~(int64_t)3;
+        ba = reinterpret_cast<const GlobalU8 *>(reinterpret_cast<uintptr_t>(t.A16 + 2 * aoff));
+        bb = reinterpret_cast<const GlobalU8 *>(reinterpret_cast<uintptr_t>(t.B16 + 2 * boff));
+        ua = (uint32_t)(t.abase - aoff);
+        ub = (uint32_t)(t.bbase - boff);
+    }
+
+    // Evaluate one diagonal (DELTA = o_d - o_(d-1)); SN holds S of d-2 and
+    // receives S of d.  Returns the lane's live mask (one byte per position,
+    // 0xFF dead, 0x00 live; positions 0-3 in m0, 4-5 in m1) and the lane's
+    // best value; with PTR, word receives the lane's pointer nibbles in the
+    // row format (PAIRED: 16 bits, first position highest; else C nibbles).
+    template <int DELTA, bool PTR, bool MASKED>
+    __device__ __forceinline__ void cells_of(uint32_t (&SN)[C2], int rlo, int rhi, uint32_t &m0, uint32_t &m1,
+                                             uint32_t &dmax, uint32_t &word)
+    {
+        uint32_t X[C2];
+#pragma unroll
+        for (int r = 0; r < C2; ++r) X[r] = __builtin_amdgcn_perm(lut_hi, lut_lo, TA[r] ^ QB[r]);
+        uint32_t Iv[C2], Dv[C2];
+        if (DELTA == 1) {
+            crossL = (uint32_t)__builtin_amdgcn_update_dpp((int)crossL, (int)R[0], 0x130 /* wave_shl:1 */, 0xF, 0xF,
+                                                           false);
+#pragma unroll
+            for (int r = 0; r < C2; ++r) {
+                Iv[r] = __builtin_amdgcn_alignbyte(r + 1 < C2 ? R[r + 1 < C2 ? r + 1 : 0] : crossL, R[r], 2);
+                Dv[r] = Dn[r];
+            }
+        } else {
+            crossR = (uint32_t)__builtin_amdgcn_update_dpp((int)crossR, (int)Dn[C2 - 1], 0x138 /* wave_shr:1 */, 0xF,
+                                                           0xF, false);
+#pragma unroll
+            for (int r = 0; r < C2; ++r) {
+                Iv[r] = R[r];
+                Dv[r] = __builtin_amdgcn_alignbyte(Dn[r], r > 0 ? Dn[r > 0 ? r - 1 : 0] : crossR, 2);
+            }
+        }
+        dmax = PK_DEAD2;
+        uint32_t Kd[C2];
+        const int mbase = MASKED ? lane * C - rlo : 0;
+        const uint32_t span = (uint32_t)(rhi - rlo);
+        uint32_t nib[C2];
+#pragma unroll
+        for (int r = 0; r < C2; ++r) {
+            const uint32_t H = pk_add(SN[r], X[r]);
+            const uint32_t S = pk_max(pk_max(H, Iv[r]), Dv[r]);
+            uint32_t Kr = pk_neg_mask(S);
+            if (MASKED) {
+                // positions outside [rlo, rhi] are dead
+                const uint32_t out_lo = (uint32_t)(mbase + 2 * r) > span ? 0x0000FFFFu : 0u;
+                const uint32_t out_hi = (uint32_t)(mbase + 2 * r + 1) > span ? 0xFFFF0000u : 0u;
+                Kr |= out_lo | out_hi;
+            }
+            Kd[r] = Kr;
+            const uint32_t Sk = bit_select(Kr, PK_DEAD2, S);
+            const uint32_t U = pk_sub(Sk, oe2);
+            const uint32_t Rn = pk_max(pk_sub(Iv[r], e2), U);
+            const uint32_t Dnn = pk_max(pk_sub(Dv[r], e2), U);
+            if (PTR) {
+                // bits per cell: diagonal (S == H), from I (S == I), I
+                // extends (Rn != U), D extends (Dnn != U)
+                const uint32_t b3 = pk_is_zero(pk_sub(S, H));
+                const uint32_t b2 = pk_is_zero(pk_sub(S, Iv[r]));
+                const uint32_t b1 = pk_nonzero(pk_sub(Rn, U));
+                const uint32_t b0 = pk_nonzero(pk_sub(Dnn, U));
+                nib[r] = pk_shl1_add(pk_shl1_add(pk_shl1_add(b3, b2), b1), b0);
+            }
+            R[r] = Rn;
+            Dn[r] = Dnn;
+            SN[r] = Sk;
+            dmax = pk_max(dmax, Sk);
+        }
+        if (PTR) {
+            // the row format: position 0 in the highest nibble
+            if constexpr (C2 == 2) {
+                // lo halves: positions 0, 2; hi halves: 1, 3
+                const uint32_t a = nib[0] << 4;               // lo: p0 << 4, hi: p1 << 4 (bits 20-23)
+                const uint32_t b = a | (nib[1] & 0x000F000Fu);  // lo: p0 << 4 | p2, hi: p1 << 4 | p3
+                // 16 bits: p0 p1 p2 p3 (highest first)
+                word = ((b & 0xF0u) << 8) | ((b >> 12) & 0xF00u) | ((b & 0xFu) << 4) | ((b >> 16) & 0xFu);
+            } else {
+                uint32_t w = 0;
+#pragma unroll
+                for (int r = 0; r < C2; ++r) w = (w << 8) | ((nib[r] & 0xFu) << 4) | ((nib[r] >> 16) & 0xFu);
+                word = w;
+            }
+        }
+        // dead-byte masks: the sign byte of each half
+        if constexpr (C2 == 2) {
+            m0 = __builtin_amdgcn_perm(Kd[1], Kd[0], 0x07050301u);
+            m1 = 0xFFFFFFFFu;
+        } else {
+            m0 = __builtin_amdgcn_perm(Kd[1], Kd[0], 0x07050301u);
+            m1 = __builtin_amdgcn_perm(Kd[2], Kd[2], 0x0D0D0301u);
+        }
+    }
+
+    __device__ __forceinline__ void slide(int s)
+    {
+        while (s > 0) {
+#pragma unroll
+            for (int r = 0; r < C2; ++r) {
+                SA[r] = (uint32_t)from_next_lane((int)SA[r], (int)PK_DEAD2);
+                SB[r] = (uint32_t)from_next_lane((int)SB[r], (int)PK_DEAD2);
+                R[r] = (uint32_t)from_next_lane((int)R[r], (int)PK_DEAD2);
+                Dn[r] = (uint32_t)from_next_lane((int)Dn[r], (int)PK_DEAD2);
+            }
+            --s;
+        }
+        while (s < 0) {
+#pragma unroll
+            for (int r = 0; r < C2; ++r) {
+                SA[r] = (uint32_t)from_prev_lane((int)SA[r], (int)PK_DEAD2);
+                SB[r] = (uint32_t)from_prev_lane((int)SB[r], (int)PK_DEAD2);
+                R[r] = (uint32_t)from_prev_lane((int)R[r], (int)PK_DEAD2);
+                Dn[r] = (uint32_t)from_prev_lane((int)Dn[r], (int)PK_DEAD2);
+            }
+            ++s;
+        }
+    }
+
+    // Move every stored value down by delta (the threshold grew by delta).
+    __device__ __forceinline__ void rebase(int delta)
+    {
+        const uint32_t d2 = ((uint32_t)delta & 0xFFFFu) * 0x10001u;
+#pragma unroll
+        for (int r = 0; r < C2; ++r) {
+            SA[r] = pk_sub(SA[r], d2);
+            SB[r] = pk_sub(SB[r], d2);
+            R[r] = pk_sub(R[r], d2);
+            Dn[r] = pk_sub(Dn[r], d2);
+        }
+    }
+
+    template <int DELTA, bool PTR>
+    __device__ __forceinline__ bool step(int d, int dstop)
+    {
+        if (EXEC && d > dstop) return false;
+        int od = (d + K) >> 1;
+        if (DELTA == 1) {
+#pragma unroll
+            for (int k = 0; k < C2; ++k) TA[k] = TAn[k];
+            fetch(ba, ua + (od + 1), TAn);
+        } else {
+#pragma unroll
+            for (int k = 0; k < C2; ++k) QB[k] = QBn[k];
+            fetch(bb, ub + (od - d - 1), QBn);
+        }
+        int rlo = min(lo1 - DELTA, lo2);
+        int rhi = max(hi1 - DELTA + 1, hi2);
+        bool masked = false;
+        if (((dmask - 1 - d) | rlo | (W - 1 - rhi) | (rhi - rlo)) < 0) {
+            const int vlo = max(0, d - t.n) - od, vhi = min(t.m, d) - od;
+            rlo = max(rlo, vlo);
+            rhi = min(rhi, vhi);
+            if (rlo > rhi) return false;
+            if (rlo < 0 || rhi > W - 1) {
+                const int smin = floordiv(rhi - (W - 1) + C - 1, C), smax = floordiv(rlo, C);
+                if (smin > smax) {
+                    overflow = true;
+                    return false;
+                }
+                int s = floordiv((rlo + rhi + 1) / 2 - W / 2, C);
+                s = s < smin ? smin : (s > smax ? smax : s);
+                slide(s);
+                const int sh = s * C;
+                K += 2 * sh;
+                od += sh;
+                lo1 -= sh; hi1 -= sh; lo2 -= sh; hi2 -= sh;
+                rlo -= sh; rhi -= sh;
+                set_dmask();
+                reload(d, od);
+            }
+            masked = (W - 1 + od > t.m) || (d - od > t.n);
+        }
+        uint32_t m0, m1, dmax, word = 0;
+        if (masked) {
+            if (DELTA == 1) cells_of<DELTA, PTR, true>(SA, rlo, rhi, m0, m1, dmax, word);
+            else cells_of<DELTA, PTR, true>(SB, rlo, rhi, m0, m1, dmax, word);
+        } else {
+            if (DELTA == 1) cells_of<DELTA, PTR, false>(SA, rlo, rhi, m0, m1, dmax, word);
+            else cells_of<DELTA, PTR, false>(SB, rlo, rhi, m0, m1, dmax, word);
+        }
+
+        // live hull of d: lanes from the ballot, positions from the edge
+        // lanes' dead-byte masks
+        const uint64_t anyl = ballot((m0 & m1) != 0xFFFFFFFFu);
+        int lo = NONE_LO, hi = NONE_HI, llo = 0, lhi = -1;
+        if (anyl) {
+            llo = ctz64(anyl);
+            lhi = hibit64(anyl);
+            const uint32_t a0 = ~(uint32_t)__builtin_amdgcn_readlane((int)m0, llo);
+            const uint32_t b0 = ~(uint32_t)__builtin_amdgcn_readlane((int)m1, llo);
+            const uint32_t a1 = ~(uint32_t)__builtin_amdgcn_readlane((int)m0, lhi);
+            const uint32_t b1 = ~(uint32_t)__builtin_amdgcn_readlane((int)m1, lhi);
+            const int flo = a0 ? (__builtin_ctz(a0) >> 3) : 4 + (__builtin_ctz(b0) >> 3);
+            const int fhi = b1 ? 4 + ((31 - __builtin_clz(b1)) >> 3) : ((31 - __builtin_clz(a1)) >> 3);
+            lo = llo * C + flo;
+            hi = lhi * C + fhi;
+        }
+        acc_cells += rhi - rlo;
+        bmax = max(bmax, rhi - rlo);
+        const int rlane0 = PAIRED ? (llo & ~1) : llo;
+        const int nl1 = PAIRED ? (lhi >> 1) - (llo >> 1) : lhi - llo;
+        const int nl = nl1 + 1;
+        if (!EXEC) acc_words += nl1;
+
+        const int lmax = max(pk_lo(dmax), pk_hi(dmax));
+        const int vbest = best - T;          // the best score in this diagonal's terms (= ydrop)
+        if (ballot(lmax > vbest)) {
+            int nb = wave_max(lmax);
+            // first position holding it
+            int slot = C;
+#pragma unroll
+            for (int r = C2 - 1; r >= 0; --r) {
+                const uint32_t Sv = DELTA == 1 ? SA[r] : SB[r];
+                slot = pk_hi(Sv) == nb ? 2 * r + 1 : slot;
+                slot = pk_lo(Sv) == nb ? 2 * r : slot;
+            }
+            const int fl = ctz64(ballot(slot < C));
+            const int pbest = fl * C + __builtin_amdgcn_readlane(slot, fl);
+            const int delta = nb - vbest;     // the best grows by delta, and so does the threshold
+            best += delta;
+            T += delta;
+            rebase(delta);
+            bi = pbest + od;
+            bj = d - bi;
+            const int n = d - dflush;
+            ptr_at_best = cum_bytes + 8 * (int64_t)n + 4 * NWORD * ((int64_t)acc_words + n);
+        }
+
+        if (EXEC) {
+            if (rowoff + (uint32_t)nl > rowcap) {
+                overflow = true;
+                return false;
+            }
+            if (lane == 0) {
+                RowHdr h;
+                h.off = rowoff | (CPW == 8 ? ROW_CPW8 : 0u);
+                h.ibase = rlane0 * C + od;
+                hdr[d] = h;
+            }
+            if (PAIRED) {
+                // the odd lane's 16 bits under the even lane's
+                const uint32_t odd = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0xB1, 0xF, 0xF, false);
+                if (!(lane & 1) && lane >= rlane0 && lane <= lhi)
+                    rows[rowoff + ((lane - rlane0) >> 1)] = (word << 16) | odd;
+            } else if (lane >= llo && lane <= lhi) {
+                rows[rowoff + (lane - llo)] = word;
+            }
+            rowoff += (uint32_t)nl;
+        }
+
+        lo2 = lo1; hi2 = hi1;
+        lo1 = lo; hi1 = hi;
+        dend = d;
+        return true;
+    }
+
+    __device__ __forceinline__ void flush()
+    {
+        const int n = dend - dflush;
+        cells += (int64_t)acc_cells + n;
+        cum_bytes += 8 * (int64_t)n + 4 * NWORD * ((int64_t)acc_words + n);
+        acc_cells = 0;
+        acc_words = 0;
+        dflush = dend;
+    }
+
+    __device__ __forceinline__ int hull_width() const
+    {
+        const int ul = min(lo1, lo2), uh = max(hi1, hi2);
+        return ul <= uh ? uh - ul : -1;
+    }
+
+    // The packed layouts switch between 256 and 384 positions; the test runs
+    // every 8 diagonals, during which a union can widen by at most 16.
+    static constexpr int SWITCH_EVERY = 8;
+    static constexpr int NARROW_ENTER = 216;     // union hull width to enter the 256-position layout
+    static constexpr int NARROW_LEAVE = 232;     // ... and to leave it (232 + 16 + 3 <= 256 - 4)
+
+    __device__ __forceinline__ bool want_switch() const
+    {
+        const int w = hull_width();
+        if (C2 == 3) return w >= 0 && w <= NARROW_ENTER;
+        return w > NARROW_LEAVE;
+    }
+
+    // Diagonals from d (even) on until the end (-1) or a layout change
+    // (returns the next d, even).
+    __device__ int advance(int d, int dstop)
+    {
+        lane = fresh_lane_id();
+        for (;; d += 2) {
+            if (!step<1, EXEC>(d, dstop)) return -1;
+            if (!step<0, EXEC>(d + 1, dstop)) return -1;
+            if (((d + 1) & (SWITCH_EVERY - 1)) == SWITCH_EVERY - 1) {
+                flush();
+                if (want_switch()) return d + 2;
+            }
+        }
+    }
+
+    // Hand-over through LDS, as SideDP::export_regs / adopt: absolute int32
+    // scores by position (NEG for dead ones) of the union [ul, uh].
+    static constexpr int XFER_W = XFER_STRIDE;
+    __device__ __forceinline__ void export_regs(uint32_t *x, int ul, int uh) const
+    {
+        const int q0 = fresh_lane_id() * C - ul;
+        auto absval = [&](int v) -> uint32_t { return (uint32_t)(v < PK_DEAD_LIMIT ? NEG : v + T); };
+#pragma unroll
+        for (int r = 0; r < C2; ++r) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int q = q0 + 2 * r + h;
+                if ((uint32_t)q <= (uint32_t)(uh - ul)) {
+                    x[q] = absval(h ? pk_hi(SA[r]) : pk_lo(SA[r]));
+                    x[XFER_W + q] = absval(h ? pk_hi(SB[r]) : pk_lo(SB[r]));
+                    x[2 * XFER_W + q] = absval(h ? pk_hi(R[r]) : pk_lo(R[r]));
+                    x[3 * XFER_W + q] = absval(h ? pk_hi(Dn[r]) : pk_lo(Dn[r]));
+                }
+            }
+        }
+    }
+
+    template <class O>
+    __device__ __forceinline__ void adopt(const O &o, int s, const uint32_t *x, int ul, int uh, int dlast)
+    {
+        K = o.K + 2 * s;
+        T = o.T;
+        const int q0 = fresh_lane_id() * C + s - ul;
+        auto rel = [&](uint32_t v) -> uint32_t {
+            const int a = (int)v;
+            const int r = (a <= NEG / 2) ? PK_DEAD : max(a - T, PK_DEAD);
+            return (uint32_t)r & 0xFFFFu;
+        };
+#pragma unroll
+        for (int r = 0; r < C2; ++r) {
+            uint32_t va[2], vb[2], vr[2], vd[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int q = q0 + 2 * r + h;
+                const bool in = (uint32_t)q <= (uint32_t)(uh - ul);
+                const int qq = in ? q : 0;
+                va[h] = in ? rel(x[qq]) : (uint32_t)PK_DEAD & 0xFFFFu;
+                vb[h] = in ? rel(x[XFER_W + qq]) : (uint32_t)PK_DEAD & 0xFFFFu;
+                vr[h] = in ? rel(x[2 * XFER_W + qq]) : (uint32_t)PK_DEAD & 0xFFFFu;
+                vd[h] = in ? rel(x[3 * XFER_W + qq]) : (uint32_t)PK_DEAD & 0xFFFFu;
+            }
+            SA[r] = va[0] | (va[1] << 16);
+            SB[r] = vb[0] | (vb[1] << 16);
+            R[r] = vr[0] | (vr[1] << 16);
+            Dn[r] = vd[0] | (vd[1] << 16);
+        }
+        crossL = PK_DEAD2;
+        crossR = PK_DEAD2;
+        auto mlo = [&](int v) { return v == NONE_LO ? v : v - s; };
+        auto mhi = [&](int v) { return v == NONE_HI ? v : v - s; };
+        lo1 = mlo(o.lo1); hi1 = mhi(o.hi1);
+        lo2 = mlo(o.lo2); hi2 = mhi(o.hi2);
+        best = o.best; bi = o.bi; bj = o.bj; dend = o.dend;
+        cells = o.cells; cum_bytes = o.cum_bytes; ptr_at_best = o.ptr_at_best;
+        dflush = o.dflush; acc_cells = 0; acc_words = 0;
+        bmax = o.bmax;
+        overflow = o.overflow;
+        rowoff = o.rowoff; rowcap = o.rowcap; hdr = o.hdr; rows = o.rows;
+        lane = fresh_lane_id();
+        set_dmask();
+        init_bases();
+        reload(dlast, (dlast + K) >> 1);
+    }
+};
+
+// One side with the packed layouts: the 192-position 32-bit layout for
+// diagonals 0..33 (the eager block and its pointers), then the packed
+// 256-position layout, moving to the 384-position one while the band is
+// wider than 232 positions and back when it narrows to 216.  The executor
+// makes the same moves at the same diagonals, so its pointer rows match the
+// inspector's sizing.
+template <bool EXEC>
+__device__ __forceinline__ SideResult run_side_pk(const SideTask &task, const Scoring &sc, int dstop,
+                                                  uint32_t *eager_lds, uint32_t *xfer, uint8_t *ptr_base,
+                                                  int64_t ptr_bytes)
+{
+    SideResult r;
+    SideDP<3, EXEC, SUB_LUT> dn(task, sc);
+    int d = dn.start(dstop, eager_lds, ptr_base, ptr_bytes);
+    // (the inspector's start runs to diagonal 33, the executor's to 1)
+    while (d >= 0 && d < EAGER_ROWS + 1) {
+        if (!dn.template step<1, EXEC>(d, dstop, eager_lds) || !dn.template step<0, EXEC>(d + 1, dstop, eager_lds)) {
+            d = -1;
+            break;
+        }
+        d += 2;
+    }
+    if (d < 0) {
+        r.take(dn);
+        return r;
+    }
+    SidePk<2, EXEC> p4(task, sc);
+    SidePk<3, EXEC> p6(task, sc);
+    switch_layout(p4, dn, xfer, d);
+    for (;;) {
+        d = p4.advance(d, dstop);
+        if (d < 0) {
+            r.take(p4);
+            return r;
+        }
+        switch_layout(p6, p4, xfer, d);
+        d = p6.advance(d, dstop);
+        if (d < 0) {
+            r.take(p6);
+            return r;
+        }
+        switch_layout(p4, p6, xfer, d);
+    }
+}
+
+// One wave per side; the grid covers the work list (the hardware dispatcher
+// hands waves to CUs as others retire, which balances sides of very
+// different lengths).  Register budgets of the standard kernels: the
+// inspector fits 64 VGPRs (8 waves per SIMD), the executor 72 (7 waves)
+// with byte substitution scores and 80 (6) without; more waves let a SIMD
+// pair one wave's VALU instruction with another's SALU instruction.
+//
+// PK: the packed layouts (fz_packed.hpp) after the eager block; the host
+// launches it for scorings within their exact range (C = 6, SUB_LUT).
+template <int C, bool EXEC, int SUB, int WAVES, bool PK = false>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <= 8 ? (EXEC ? (SUB != SUB_WIDE ? 7 : 6) : 8) : 1))) void extend_kernel(ExtendArgs a)
+{
+    using DP = SideDP<C, EXEC, SUB>;
+    using EDP = SideDP<StartLayout<C>::value, EXEC, SUB>;     // holds the eager block
+    __shared__ uint32_t eager_lds_all[WAVES][EAGER_ROWS * EDP::NEL * EDP::NWORD];
+    __shared__ uint32_t xfer_all[WAVES][C == 6 ? 4 * DP::XFER_W : 1];
+    const int wv = uniform((int)(threadIdx.x / 64));
+    uint32_t *eager_lds = eager_lds_all[wv];
+    uint32_t *xfer = xfer_all[wv];
+    const int idx = (int)blockIdx.x * WAVES + wv;
+    if (idx >= a.nlist) return;
+    const int64_t item = EXEC ? a.exec_begin + idx : (int64_t)idx;
+    const int sid = EXEC ? a.exec[item].side : (a.list ? a.list[item] : (int)item);
+    const SideTask task = a.tasks[sid];
+    SideOut *o = &a.out[sid];
+    if (task.m < 0) {
+        if (!EXEC && fresh_lane_id() == 0) {
+            SideOut r = {};
+            r.flags = SO_SKIPPED;
+            *o = r;
+        }
+        return;
+    }
+    if (EXEC) {
+        const ExecItem it = a.exec[item];
+        SideResult x;
+        if constexpr (PK) x = run_side_pk<EXEC>(task, a.sc, it.dstar, nullptr, xfer,
+                                                a.ptr_ws + (it.ptr_off - a.ptr_base_off), it.ptr_bytes);
+        else x = run_side<C, EXEC, SUB>(task, a.sc, it.dstar, nullptr, xfer,
+                                        a.ptr_ws + (it.ptr_off - a.ptr_base_off), it.ptr_bytes);
+        if (fresh_lane_id() == 0) {
+            atomicAdd((unsigned long long *)a.exec_cells, (unsigned long long)x.cells);
+            if (x.overflow || x.best != o->score || x.bi != o->ie) atomicOr(&o->flags, SO_EXEC_MISMATCH);
+        }
+        return;
+    }
+    SideResult x;
+    if constexpr (PK) x = run_side_pk<EXEC>(task, a.sc, 0x7fffffff, eager_lds, xfer, nullptr, 0);
+    else x = run_side<C, EXEC, SUB>(task, a.sc, 0x7fffffff, eager_lds, xfer, nullptr, 0);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    SideOut r;
+    r.score = x.best;
+    r.ie = x.bi;
+    r.je = x.bj;
+    r.dend = x.dend;
+    r.cells = x.cells;
+    r.ptr_bytes = x.ptr_at_best;
+    r.flags = (x.overflow ? SO_OVERFLOW : 0) | a.result_flags;
+    r.eager_len = 0;
+    r.max_band = x.band;
+    r.pad_ = 0;
+    if (!x.overflow && x.bi <= EAGER_EDGE && x.bj <= EAGER_EDGE) {
+        // the best cell lies in the eager block, which the start layout
+        // kept (no layout change happens before diagonal 34)
+        EDP e(task, a.sc);
+        e.bi = x.bi;
+        e.bj = x.bj;
+        r.flags |= SO_EAGER;
+        r.eager_len = e.eager_walk(eager_lds, a.eager_ops + (int64_t)sid * EAGER_OPS);
+    }
+    if (fresh_lane_id() == 0) {
+        *o = r;
+        if (x.overflow) {
+            const uint32_t k = atomicAdd(a.overflow_count, 1u);
+            a.overflow_list[k] = sid;
+        }
+    }
+}
+
+}  // namespace fz

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfz.so")
 
 FZ_TRACEBACK, FZ_LOCAL, FZ_STATS, FZ_QUERY_RC, FZ_SEEDS_ALL, FZ_SEEDS_REUSE_INDEX = 1, 2, 4, 8, 16, 32
-FZ_ROUNDS_DOUBLING = 64
+FZ_ROUNDS_DOUBLING, FZ_EXACT32 = 64, 128
 FZ_OK, FZ_EINVAL, FZ_ENOMEM, FZ_EDEVICE = 0, -1, -2, -3
 FZ_HIT_TRACED, FZ_HIT_EAGER_LEFT, FZ_HIT_EAGER_RIGHT = 1, 2, 4
 FZ_HIT_BELOW_MIN, FZ_HIT_EBAND, FZ_HIT_ESEED, FZ_HIT_ERANGE = 8, 16, 32, 64
@@ -299,19 +299,23 @@ class Context:
             pass
 
     def extend(self, target, query, seeds, scoring, ydrop, min_traceback_score=-(1 << 62), traceback=True,
-               stream=None, want_stats=False, query_rc=False):
-        """query_rc: seeds lie on the query's reverse complement (FZ_QUERY_RC)."""
-        flags = (FZ_TRACEBACK if traceback else 0) | (FZ_QUERY_RC if query_rc else 0)
+               stream=None, want_stats=False, query_rc=False, exact32=False):
+        """query_rc: seeds lie on the query's reverse complement (FZ_QUERY_RC).
+        exact32: keep every cell in a 32-bit lane (FZ_EXACT32); the results
+        are the same as with the packed 16-bit layouts."""
+        flags = ((FZ_TRACEBACK if traceback else 0) | (FZ_QUERY_RC if query_rc else 0)
+                 | (FZ_EXACT32 if exact32 else 0))
         return fz_extend_batch(self.h, target, query, seeds, scoring, ydrop, min_traceback_score, flags,
                                stream, want_stats)
 
     def extend_rounds(self, target, query, seeds, scoring, ydrop, min_traceback_score, round_size, stream=None,
-                      want_stats=False, query_rc=False, doubling=False):
+                      want_stats=False, query_rc=False, doubling=False, exact32=False):
         """Covered-seed suppression (fz_extend_rounds): rounds of round_size
         seeds (doubling: the first round's size, each later round twice the
         one before); a seed on an alignment traced in an earlier round is not
         extended (status FZ_HIT_COVERED)."""
-        flags = FZ_TRACEBACK | (FZ_QUERY_RC if query_rc else 0) | (FZ_ROUNDS_DOUBLING if doubling else 0)
+        flags = (FZ_TRACEBACK | (FZ_QUERY_RC if query_rc else 0) | (FZ_ROUNDS_DOUBLING if doubling else 0)
+                 | (FZ_EXACT32 if exact32 else 0))
         return fz_extend_batch(self.h, target, query, seeds, scoring, ydrop, min_traceback_score, flags,
                                stream, want_stats, round_size=round_size)
 

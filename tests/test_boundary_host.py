@@ -69,4 +69,4 @@ def test_build_lists_every_source():
     csrc = os.path.join(ROOT, "smith_waterman_dp_amd", "csrc")
     have = sorted(f for f in os.listdir(csrc) if f.endswith(".hpp"))
     assert sorted(build.HEADERS) == have
-    assert sorted(build.SOURCES) == sorted(f for f in os.listdir(csrc) if f.endswith(".hip"))
+    assert sorted(build.SOURCES + build.PROBE_SOURCES) == sorted(f for f in os.listdir(csrc) if f.endswith(".hip"))
