@@ -61,7 +61,7 @@ __device__ __forceinline__ uint32_t pk_neg_mask(uint32_t x)
 __device__ __forceinline__ uint32_t bit_select(uint32_t m, uint32_t a, uint32_t b)
 {
     uint32_t r;
-    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "s"(a), "v"(b));
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(a), "v"(b));
     return r;
 }
 // per half: 1 if the (unsigned) value is 0, else 0
@@ -83,6 +83,15 @@ __device__ __forceinline__ uint32_t pk_shl1_add(uint32_t a, uint32_t b)
 {
     uint32_t r;
     asm("v_pk_mad_u16 %0, %1, 2, %2 op_sel_hi:[1,0,1]" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+// A VGPR copy of a wave-uniform value: the packed constants of the cell
+// updates live in vector registers, which this kernel has to spare, and not
+// in the scalar file, which its wave-uniform state fills.
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t x)
+{
+    uint32_t r;
+    asm("v_mov_b32 %0, %1" : "=v"(r) : "s"(x));
     return r;
 }
 // sign-extended low / high half
@@ -145,14 +154,20 @@ struct SidePk {
     const SideTask &t;
     const Scoring &sc;
     int lane;
-    uint32_t oe2, e2, lut_lo, lut_hi;   // packed constants
+    uint32_t oe2, e2, lut_lo, lut_hi, dead2;    // packed constants (VGPR copies)
 
-    __device__ SidePk(const SideTask &task, const Scoring &s) : t(task), sc(s), lane(fresh_lane_id())
+    __device__ SidePk(const SideTask &task, const Scoring &s) : t(task), sc(s), lane(fresh_lane_id()) {}
+
+    // lane-held values of this layout's run, formed when the run starts (not
+    // once per side, where both layouts' sets would hold registers)
+    __device__ __forceinline__ void enter()
     {
-        oe2 = ((uint32_t)sc.oe & 0xFFFFu) * 0x10001u;
-        e2 = ((uint32_t)sc.e & 0xFFFFu) * 0x10001u;
-        lut_lo = ((uint32_t)sc.match & 0xFFFFu) | ((uint32_t)sc.tv << 16);
-        lut_hi = ((uint32_t)sc.ts & 0xFFFFu) | ((uint32_t)sc.tv << 16);
+        lane = fresh_lane_id();
+        oe2 = in_vgpr(((uint32_t)sc.oe & 0xFFFFu) * 0x10001u);
+        e2 = in_vgpr(((uint32_t)sc.e & 0xFFFFu) * 0x10001u);
+        lut_lo = in_vgpr(((uint32_t)sc.match & 0xFFFFu) | ((uint32_t)sc.tv << 16));
+        lut_hi = in_vgpr(((uint32_t)sc.ts & 0xFFFFu) | ((uint32_t)sc.tv << 16));
+        dead2 = in_vgpr(PK_DEAD2);
     }
 
     __device__ __forceinline__ void fetch(const GlobalU8 *base, uint32_t off, uint32_t (&out)[C2]) const
@@ -227,7 +242,7 @@ struct SidePk {
                 Kr |= out_lo | out_hi;
             }
             Kd[r] = Kr;
-            const uint32_t Sk = bit_select(Kr, PK_DEAD2, S);
+            const uint32_t Sk = bit_select(Kr, dead2, S);
             const uint32_t U = pk_sub(Sk, oe2);
             const uint32_t Rn = pk_max(pk_sub(Iv[r], e2), U);
             const uint32_t Dnn = pk_max(pk_sub(Dv[r], e2), U);
@@ -307,10 +322,16 @@ struct SidePk {
         }
     }
 
+    // Evaluate diagonal d; false when the side has ended before it (an
+    // empty range, a band wider than the window (overflow), or, in the
+    // executor, d past the best cell's diagonal).  There is no early exit:
+    // an ended side runs the masked sweep over an empty range (every cell
+    // dead, nothing counted) and keeps empty hulls, so that later diagonals
+    // end too, and the caller leaves its loop in one place with every value
+    // of the side's state defined.
     template <int DELTA, bool PTR>
     __device__ __forceinline__ bool step(int d, int dstop)
     {
-        if (EXEC && d > dstop) return false;
         int od = (d + K) >> 1;
         if (DELTA == 1) {
 #pragma unroll
@@ -323,30 +344,36 @@ struct SidePk {
         }
         int rlo = min(lo1 - DELTA, lo2);
         int rhi = max(hi1 - DELTA + 1, hi2);
-        bool masked = false;
-        if (((dmask - 1 - d) | rlo | (W - 1 - rhi) | (rhi - rlo)) < 0) {
+        bool masked = false, live = true;
+        if (((dmask - 1 - d) | rlo | (W - 1 - rhi) | (rhi - rlo) | (EXEC ? dstop - d : 0)) < 0) {
             const int vlo = max(0, d - t.n) - od, vhi = min(t.m, d) - od;
             rlo = max(rlo, vlo);
-            rhi = min(rhi, vhi);
-            if (rlo > rhi) return false;
-            if (rlo < 0 || rhi > W - 1) {
+            rhi = min(rhi, EXEC && d > dstop ? rlo - 1 : vhi);
+            if (rlo <= rhi && (rlo < 0 || rhi > W - 1)) {
                 const int smin = floordiv(rhi - (W - 1) + C - 1, C), smax = floordiv(rlo, C);
                 if (smin > smax) {
                     overflow = true;
-                    return false;
+                    rhi = rlo - 1;
+                } else {
+                    int s = floordiv((rlo + rhi + 1) / 2 - W / 2, C);
+                    s = s < smin ? smin : (s > smax ? smax : s);
+                    slide(s);
+                    const int sh = s * C;
+                    K += 2 * sh;
+                    od += sh;
+                    lo1 -= sh; hi1 -= sh; lo2 -= sh; hi2 -= sh;
+                    rlo -= sh; rhi -= sh;
+                    set_dmask();
+                    reload(d, od);
                 }
-                int s = floordiv((rlo + rhi + 1) / 2 - W / 2, C);
-                s = s < smin ? smin : (s > smax ? smax : s);
-                slide(s);
-                const int sh = s * C;
-                K += 2 * sh;
-                od += sh;
-                lo1 -= sh; hi1 -= sh; lo2 -= sh; hi2 -= sh;
-                rlo -= sh; rhi -= sh;
-                set_dmask();
-                reload(d, od);
             }
             masked = (W - 1 + od > t.m) || (d - od > t.n);
+            if (rlo > rhi) {
+                live = false;
+                masked = true;
+                rlo = NONE_LO;      // no position of the window lies in [rlo, rhi]
+                rhi = NONE_LO;
+            }
         }
         uint32_t m0, m1, dmax, word = 0;
         if (masked) {
@@ -373,13 +400,14 @@ struct SidePk {
             lo = llo * C + flo;
             hi = lhi * C + fhi;
         }
-        acc_cells += rhi - rlo;
+        acc_cells += rhi - rlo;                 // 0 for an ended side
         bmax = max(bmax, rhi - rlo);
         const int rlane0 = PAIRED ? (llo & ~1) : llo;
         const int nl1 = PAIRED ? (lhi >> 1) - (llo >> 1) : lhi - llo;
         const int nl = nl1 + 1;
-        if (!EXEC) acc_words += nl1;
+        if (!EXEC) acc_words += live ? nl1 : 0;
 
+        // (no cell of an ended side is live, so its best cannot move)
         const int lmax = max(pk_lo(dmax), pk_hi(dmax));
         const int vbest = best - T;          // the best score in this diagonal's terms (= ydrop)
         if (ballot(lmax > vbest)) {
@@ -404,32 +432,35 @@ struct SidePk {
             ptr_at_best = cum_bytes + 8 * (int64_t)n + 4 * NWORD * ((int64_t)acc_words + n);
         }
 
-        if (EXEC) {
+        if (EXEC && live) {
             if (rowoff + (uint32_t)nl > rowcap) {
+                // the recompute disagrees with the inspector's sizing
                 overflow = true;
-                return false;
+                live = false;
+            } else {
+                if (lane == 0) {
+                    RowHdr h;
+                    h.off = rowoff | (CPW == 8 ? ROW_CPW8 : 0u);
+                    h.ibase = rlane0 * C + od;
+                    hdr[d] = h;
+                }
+                if (PAIRED) {
+                    // the odd lane's 16 bits under the even lane's
+                    const uint32_t odd = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0xB1, 0xF, 0xF, false);
+                    if (!(lane & 1) && lane >= rlane0 && lane <= lhi)
+                        rows[rowoff + ((lane - rlane0) >> 1)] = (word << 16) | odd;
+                } else if (lane >= llo && lane <= lhi) {
+                    rows[rowoff + (lane - llo)] = word;
+                }
+                rowoff += (uint32_t)nl;
             }
-            if (lane == 0) {
-                RowHdr h;
-                h.off = rowoff | (CPW == 8 ? ROW_CPW8 : 0u);
-                h.ibase = rlane0 * C + od;
-                hdr[d] = h;
-            }
-            if (PAIRED) {
-                // the odd lane's 16 bits under the even lane's
-                const uint32_t odd = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0xB1, 0xF, 0xF, false);
-                if (!(lane & 1) && lane >= rlane0 && lane <= lhi)
-                    rows[rowoff + ((lane - rlane0) >> 1)] = (word << 16) | odd;
-            } else if (lane >= llo && lane <= lhi) {
-                rows[rowoff + (lane - llo)] = word;
-            }
-            rowoff += (uint32_t)nl;
         }
 
-        lo2 = lo1; hi2 = hi1;
+        lo2 = live ? lo1 : NONE_LO;
+        hi2 = live ? hi1 : NONE_HI;
         lo1 = lo; hi1 = hi;
-        dend = d;
-        return true;
+        dend = live ? d : dend;
+        return live;
     }
 
     __device__ __forceinline__ void flush()
@@ -465,10 +496,11 @@ struct SidePk {
     // (returns the next d, even).
     __device__ int advance(int d, int dstop)
     {
-        lane = fresh_lane_id();
+        enter();
         for (;; d += 2) {
-            if (!step<1, EXEC>(d, dstop)) return -1;
-            if (!step<0, EXEC>(d + 1, dstop)) return -1;
+            const bool a = step<1, EXEC>(d, dstop);
+            const bool b = step<0, EXEC>(d + 1, dstop);
+            if (!(a && b)) return -1;
             if (((d + 1) & (SWITCH_EVERY - 1)) == SWITCH_EVERY - 1) {
                 flush();
                 if (want_switch()) return d + 2;
