@@ -142,7 +142,7 @@ struct SidePk {
     int K, dmask;
     int lo1, hi1, lo2, hi2;
     int best, bi, bj, dend;     // best: absolute score
-    int T;                      // absolute threshold of the next diagonal; values are stored as S - T
+    int ydrop;                  // values are stored as S - T with T = best - ydrop, the next diagonal's threshold
     int64_t cells, cum_bytes, ptr_at_best;
     int dflush;
     int32_t acc_cells, acc_words, bmax;
@@ -156,7 +156,9 @@ struct SidePk {
     int lane;
     uint32_t oe2, e2, lut_lo, lut_hi, dead2;    // packed constants (VGPR copies)
 
-    __device__ SidePk(const SideTask &task, const Scoring &s) : t(task), sc(s), lane(fresh_lane_id()) {}
+    __device__ SidePk(const SideTask &task, const Scoring &s) : ydrop(s.ydrop), t(task), sc(s), lane(fresh_lane_id())
+    {
+    }
 
     // lane-held values of this layout's run, formed when the run starts (not
     // once per side, where both layouts' sets would hold registers)
@@ -225,7 +227,6 @@ struct SidePk {
                 Dv[r] = __builtin_amdgcn_alignbyte(Dn[r], r > 0 ? Dn[r > 0 ? r - 1 : 0] : crossR, 2);
             }
         }
-        dmax = PK_DEAD2;
         uint32_t Kd[C2];
         const int mbase = MASKED ? lane * C - rlo : 0;
         const uint32_t span = (uint32_t)(rhi - rlo);
@@ -258,7 +259,7 @@ struct SidePk {
             R[r] = Rn;
             Dn[r] = Dnn;
             SN[r] = Sk;
-            dmax = pk_max(dmax, Sk);
+            dmax = r == 0 ? Sk : pk_max(dmax, Sk);     // (killed halves hold DEAD)
         }
         if (PTR) {
             // the row format: position 0 in the highest nibble
@@ -373,6 +374,9 @@ struct SidePk {
                 masked = true;
                 rlo = NONE_LO;      // no position of the window lies in [rlo, rhi]
                 rhi = NONE_LO;
+                lo1 = NONE_LO;      // (read above): the next diagonal's range is empty too
+                hi1 = NONE_HI;
+                if (!EXEC) acc_words += 1;      // the empty hull's row count below is -1
             }
         }
         uint32_t m0, m1, dmax, word = 0;
@@ -405,12 +409,11 @@ struct SidePk {
         const int rlane0 = PAIRED ? (llo & ~1) : llo;
         const int nl1 = PAIRED ? (lhi >> 1) - (llo >> 1) : lhi - llo;
         const int nl = nl1 + 1;
-        if (!EXEC) acc_words += live ? nl1 : 0;
+        if (!EXEC) acc_words += nl1;
 
         // (no cell of an ended side is live, so its best cannot move)
         const int lmax = max(pk_lo(dmax), pk_hi(dmax));
-        const int vbest = best - T;          // the best score in this diagonal's terms (= ydrop)
-        if (ballot(lmax > vbest)) {
+        if (ballot(lmax > ydrop)) {          // (the best score is ydrop in these terms)
             int nb = wave_max(lmax);
             // first position holding it
             int slot = C;
@@ -422,9 +425,8 @@ struct SidePk {
             }
             const int fl = ctz64(ballot(slot < C));
             const int pbest = fl * C + __builtin_amdgcn_readlane(slot, fl);
-            const int delta = nb - vbest;     // the best grows by delta, and so does the threshold
+            const int delta = nb - ydrop;     // the best grows by delta, and so does the threshold
             best += delta;
-            T += delta;
             rebase(delta);
             bi = pbest + od;
             bj = d - bi;
@@ -456,10 +458,8 @@ struct SidePk {
             }
         }
 
-        lo2 = live ? lo1 : NONE_LO;
-        hi2 = live ? hi1 : NONE_HI;
+        lo2 = lo1; hi2 = hi1;
         lo1 = lo; hi1 = hi;
-        dend = live ? d : dend;
         return live;
     }
 
@@ -500,8 +500,12 @@ struct SidePk {
         for (;; d += 2) {
             const bool a = step<1, EXEC>(d, dstop);
             const bool b = step<0, EXEC>(d + 1, dstop);
-            if (!(a && b)) return -1;
+            if (!(a && b)) {
+                dend = a ? d : d - 1;       // the last live diagonal
+                return -1;
+            }
             if (((d + 1) & (SWITCH_EVERY - 1)) == SWITCH_EVERY - 1) {
+                dend = d + 1;
                 flush();
                 if (want_switch()) return d + 2;
             }
@@ -514,6 +518,7 @@ struct SidePk {
     __device__ __forceinline__ void export_regs(uint32_t *x, int ul, int uh) const
     {
         const int q0 = fresh_lane_id() * C - ul;
+        const int T = best - ydrop;
         auto absval = [&](int v) -> uint32_t { return (uint32_t)(v < PK_DEAD_LIMIT ? NEG : v + T); };
 #pragma unroll
         for (int r = 0; r < C2; ++r) {
@@ -534,7 +539,7 @@ struct SidePk {
     __device__ __forceinline__ void adopt(const O &o, int s, const uint32_t *x, int ul, int uh, int dlast)
     {
         K = o.K + 2 * s;
-        T = o.T;
+        const int T = o.best - ydrop;       // the 32-bit layouts' threshold too (ydrop is small here)
         const int q0 = fresh_lane_id() * C + s - ul;
         auto rel = [&](uint32_t v) -> uint32_t {
             const int a = (int)v;
