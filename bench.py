@@ -39,9 +39,11 @@ sys.path.insert(0, ROOT)
 METRIC = "GCUPS and seed extensions/sec on 1M-seed skewed batch, 1 MI355X"
 
 # Integer VALU peak of MI355X: 256 CUs x 4 SIMD x 16 lanes (64 lane-ops per
-# clock per CU) x 2.4 GHz peak engine clock.
+# clock per CU) x 2.4 GHz peak engine clock; packed 16-bit instructions do
+# two operations per lane, so the extension's packed layouts have twice that.
 N_CU, LANE_OPS_PER_CLK_PER_CU, CLOCK_HZ = 256, 64, 2.4e9
 VALU_PEAK_OPS = N_CU * LANE_OPS_PER_CLK_PER_CU * CLOCK_HZ
+VALU_PEAK_OPS_PK16 = 2 * VALU_PEAK_OPS
 
 # Algorithmic integer operations per cell (fixed, independent of the code):
 #   extension: 5 adds + 4 compares of the three-state cell (FastZ section 2.2,
@@ -352,13 +354,14 @@ def bench_pipeline(a):
                            "traced": int(((hh[:, 1] & fz.FZ_HIT_TRACED) != 0).sum())})
     kern_s = float(np.mean(main_ms)) / 1e3
     achieved = OPS_PER_CELL["extend"] * cells / kern_s / 1e12
-    peak = VALU_PEAK_OPS / 1e12
+    packed = all(int(st["n_packed"]) > 0 for _, _, st in res)
+    peak = (VALU_PEAK_OPS_PK16 if packed else VALU_PEAK_OPS) / 1e12
     bases = int(w["target"].size + w["query"].size)
     out = {"metric": "whole-pair alignment (seed stage + covered-seed rounds, both strands) on a 20 Mbp "
                      "chromosome pair, 1 MI355X",
            "value": round(bases / (ms_per_step / 1e3) / 1e6, 3), "unit": "Mbp/s", "n_gpus": 1, "steps": steps,
            "warmup": a.warmup, "ms_per_step": round(ms_per_step, 3), "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+           "vs_baseline": None, "dtype": "int16x2" if packed else "int32", "data": "synthetic",
            "config": {"workload": "chromosome_pipeline", "target_bp": int(w["target"].size),
                       "query_bp": int(w["query"].size), "k": w["k"], "flank": w["flank"], "round_size": a.round_size,
                       "round_doubling": bool(a.round_doubling), "strands_run": a.strands,
@@ -393,19 +396,21 @@ def call_overhead_ms(ctx, T, Q, S, w, min_tb, calls=20):
     return float(np.median(times))
 
 
-def measured_valu_peak():
+def measured_valu_peak(packed=False):
     """int32 add/max issue rate measured by libfz_probe.so (TOP/s of lane
+    operations; packed: v_pk_add_u16 / v_pk_max_i16, TOP/s of 16-bit
     operations), or None when the probe is not built."""
     import ctypes
     path = os.path.join(ROOT, "smith_waterman_dp_amd", "libfz_probe.so")
     if not os.path.exists(path):
         return None
     lib = ctypes.CDLL(path)
-    lib.fz_probe_valu.restype = ctypes.c_int
-    lib.fz_probe_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float),
-                                  ctypes.POINTER(ctypes.c_double)]
+    fn = lib.fz_probe_valu_pk16 if packed else lib.fz_probe_valu
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float),
+                   ctypes.POINTER(ctypes.c_double)]
     ms, ops = ctypes.c_float(0), ctypes.c_double(0)
-    if lib.fz_probe_valu(0, 8, 1 << 14, ctypes.byref(ms), ctypes.byref(ops)) != 0 or ms.value <= 0:
+    if fn(0, 8, 1 << 14, ctypes.byref(ms), ctypes.byref(ops)) != 0 or ms.value <= 0:
         return None
     return round(ops.value / (ms.value / 1e3) / 1e12, 3)
 
@@ -485,7 +490,11 @@ def main():
     ops = OPS_PER_CELL["local" if local else "extend"]
     kern_s = float(np.median(main_ms)) / 1e3
     achieved = ops * cells / kern_s / 1e12
-    peak = VALU_PEAK_OPS / 1e12
+    # the extension's cells run in packed 16-bit layouts when the scoring
+    # allows it (every side after its first 34 anti-diagonals): their peak
+    # is the packed rate
+    packed = (not local) and int(st["n_packed"]) > 0
+    peak = (VALU_PEAK_OPS_PK16 if packed else VALU_PEAK_OPS) / 1e12
     traffic = None
     if a.workload == "skewed" and kernel_src_hash() == TRAFFIC_SRC_HASH:
         traffic = measured_traffic(TRAFFIC_FETCH_BYTES, TRAFFIC_WRITE_BYTES, kern_s)
@@ -520,7 +529,7 @@ def main():
     out = {"metric": METRIC if a.workload == "skewed" else "GCUPS on the %s batch, 1 MI355X" % a.workload,
            "value": round(gcups, 3), "unit": "GCUPS", "n_gpus": 1, "steps": steps, "warmup": a.warmup,
            "ms_per_step": round(ms_per_step, 3), "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "int32", "data": "synthetic", "config": cfg,
+           "vs_baseline": None, "dtype": "int16x2" if packed else "int32", "data": "synthetic", "config": cfg,
            "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(peak, 3), "unit": "TOP/s",
                         "frac": round(achieved / peak, 4), "traffic": traffic,
                         "kernel": "local_kernel" if local else "extend_kernel (inspector)",
@@ -528,7 +537,12 @@ def main():
                         # the whole call against the same peak: ops_per_cell x GCUPS
                         "end_to_end": {"achieved": round(ops * gcups / 1e3, 3),
                                        "frac": round(ops * gcups / 1e3 / peak, 4)}}}
-    probe = measured_valu_peak()
+    if packed:
+        # for comparison with 32-bit builds: the same figure against the
+        # int32 lane rate
+        out["roofline"]["frac_of_int32_peak"] = round(achieved / (VALU_PEAK_OPS / 1e12), 4)
+        out["roofline"]["arith"] = "packed int16 pairs after anti-diagonal 33, int32 before"
+    probe = measured_valu_peak(packed)
     if probe is not None:
         out["roofline"]["peak_measured"] = probe
     if not a.no_cpu:

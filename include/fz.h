@@ -114,6 +114,9 @@ typedef struct {
     uint64_t bin_hist[8];
     uint64_t n_batches;
     uint64_t max_band;             /* widest range R_d (cells of one anti-diagonal) of any side */
+    uint64_t n_packed;             /* sides swept in the packed 16-bit layouts after their first 34
+                                    * anti-diagonals (0 with FZ_EXACT32, FZ_LOCAL, or a scoring
+                                    * outside the packed range) */
     float ms_pack, ms_inspect, ms_bin, ms_exec, ms_walk, ms_gather;
                                    /* phase spans between HIP events on the call's stream;
                                     * ms_walk is the summed duration of the traceback walker

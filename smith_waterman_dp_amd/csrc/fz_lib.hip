@@ -1106,6 +1106,7 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         S.cells = (uint64_t)hc.totals[3];
         S.executor_cells = (uint64_t)hc.exec_cells;
         S.max_band = (uint64_t)hc.max_band;
+        S.n_packed = pk ? (uint64_t)nsides : 0;
         for (size_t w = 0; w < n_walks; ++w) {
             float v = 0.f;
             (void)hipEventElapsedTime(&v, ctx->walk_ev[2 * w], ctx->walk_ev[2 * w + 1]);
@@ -1230,6 +1231,7 @@ static int noalloc_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const
         S.n_sides = (uint64_t)nsides;
         S.cells = (uint64_t)hc.totals[3];
         S.max_band = (uint64_t)hc.max_band;
+        S.n_packed = pk ? (uint64_t)nsides : 0;
         S.n_overflow = hc.overflow_count[0];
         (void)hipEventElapsedTime(&S.ms_main, ctx->kev[0], ctx->kev[1]);
         *stats = S;
@@ -1327,6 +1329,7 @@ static int rounds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
                 tot.ms_gather += rsst.ms_gather;
                 tot.ms_main += rsst.ms_main;
                 tot.max_band = std::max(tot.max_band, rsst.max_band);
+                tot.n_packed += rsst.n_packed;
             }
             rc = grow_keep(ctx, ctx->rd_cig, (size_t)(acc_words + (int64_t)words + 1) * sizeof(uint32_t),
                            (size_t)acc_words * sizeof(uint32_t), st);

@@ -11,18 +11,26 @@
 // wave per extension, three rolling anti-diagonals in registers).
 //
 // Scores relative to the threshold.  Each stored value is V = S - T, where
-// T is the y-drop threshold of the next diagonal to evaluate.  A cell is live
-// exactly when V >= 0, so the kill is one arithmetic shift (the sign of
-// each half) and one bit select that puts DEAD (-16384) in the dead halves.
-// When the best score grows, T grows by the same amount and every stored
-// value is moved down by it (one packed subtraction per register).  The
-// values that decide anything lie within a few thousand of T: live scores
-// are at most ydrop + (largest substitution score) above it, and the gap
-// states that can still feed a live cell are at most gap_open + gap_extend
-// below it; dead cells and everything built from them stay below -15000.
-// So for ydrop <= PK_MAX_YDROP, |substitution| <= 127 and gap_open +
-// gap_extend <= PK_MAX_OE no value wraps or saturates, and every live value,
-// kill and traceback choice equals the 32-bit computation's.  The host runs
+// T = best - ydrop is the y-drop threshold of the next diagonal to evaluate.
+// A cell is live exactly when V >= 0, so the kill is one arithmetic shift
+// (the sign of each half) and one bit select that puts DEAD (-16384) in the
+// dead halves.  When the best score grows by delta, T grows by the same
+// amount and every stored value is moved down by it (one packed subtraction
+// per register); delta is at most the largest substitution score, since a
+// cell's score exceeds its predecessors' best by no more than that.
+//
+// Range.  Live values: 0 <= V <= ydrop + 127.  Below: a dead cell holds
+// DEAD; a gap value is at least DEAD - (gap_open + gap_extend) when formed
+// (it is a maximum with the value opened from this cell) and at most
+// gap_extend + 127 lower when next used; a diagonal term is at least
+// DEAD - 2 * 127 - 128.  With ydrop <=
+// PK_MAX_YDROP, substitution scores in [-128, 127] and gap_open +
+// 2 * gap_extend <= PK_MAX_OE every value stays in [-20,800, 16,300]: no
+// sum or difference wraps, and the differences the pointer bits test for
+// zero are below 2^16 in magnitude.  Values below 0 never become live again
+// (they only decrease), so a dead-derived value and the 32-bit layouts'
+// -inf make the same decisions, and every live value, kill, best-cell
+// choice and traceback bit equals the 32-bit computation's.  The host runs
 // other scorings on the 32-bit layouts.
 #pragma once
 

@@ -59,6 +59,7 @@ class fz_stats(ctypes.Structure):
                 ("pointer_bytes", ctypes.c_uint64), ("n_sides", ctypes.c_uint64), ("n_eager", ctypes.c_uint64),
                 ("n_executor", ctypes.c_uint64), ("n_overflow", ctypes.c_uint64),
                 ("bin_hist", ctypes.c_uint64 * 8), ("n_batches", ctypes.c_uint64), ("max_band", ctypes.c_uint64),
+                ("n_packed", ctypes.c_uint64),
                 ("ms_pack", ctypes.c_float), ("ms_inspect", ctypes.c_float), ("ms_bin", ctypes.c_float),
                 ("ms_exec", ctypes.c_float), ("ms_walk", ctypes.c_float), ("ms_gather", ctypes.c_float),
                 ("ms_main", ctypes.c_float)]

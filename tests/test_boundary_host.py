@@ -35,7 +35,7 @@ def test_struct_sizes_match_header():
     assert ctypes.sizeof(fz.fz_matrix) == 17 * 4           # sub[4][4] and n_score
     assert ctypes.sizeof(fz.fz_seed_stats) == 11 * 4       # eleven float phase times
     # fz_stats: 17 uint64 counters (bin_hist holds 8), seven float times, padding to 8 bytes
-    assert ctypes.sizeof(fz.fz_stats) == 17 * 8 + 7 * 4 + 4
+    assert ctypes.sizeof(fz.fz_stats) == 18 * 8 + 7 * 4 + 4
 
 
 def test_null_context_is_rejected():

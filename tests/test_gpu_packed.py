@@ -106,6 +106,7 @@ def test_packed_tiny_equals_exact32(ctx):
     same(a, b, "tiny")
     assert a[2]["n_executor"] > 0
     assert a[2]["pointer_bytes"] < b[2]["pointer_bytes"]
+    assert a[2]["n_packed"] == 2 * len(w["seeds"]) and b[2]["n_packed"] == 0
 
 
 # cheap gaps widen the band: a cell k diagonals off the main one on
@@ -138,26 +139,29 @@ def test_packed_identical_flanks(ctx, length):
                 assert a[2]["n_overflow"] >= 1, label
 
 
+# (scoring, ydrop, packed)
 LIMIT_SCORINGS = [
     # the packed range's edges
-    (dict(match=127, transition=-128, transversion=-128, gap_open=3940, gap_extend=30), 16000),
-    (dict(match=127, transition=-1, transversion=-2, gap_open=0, gap_extend=1), 16000),
-    (dict(match=1, transition=-1, transversion=-1, gap_open=0, gap_extend=1), 0),
-    (dict(match=1, transition=-1, transversion=-1, gap_open=0, gap_extend=1), 1),
-    (dict(match=91, transition=-31, transversion=-123, gap_open=2000, gap_extend=1000), 16000),
+    (dict(match=127, transition=-128, transversion=-128, gap_open=3940, gap_extend=30), 16000, True),
+    (dict(match=127, transition=-1, transversion=-2, gap_open=0, gap_extend=1), 16000, True),
+    (dict(match=1, transition=-1, transversion=-1, gap_open=0, gap_extend=1), 0, True),
+    (dict(match=1, transition=-1, transversion=-1, gap_open=0, gap_extend=1), 1, True),
+    (dict(match=91, transition=-31, transversion=-123, gap_open=2000, gap_extend=1000), 16000, True),
     # just outside it: the 32-bit layouts
-    (dict(match=91, transition=-31, transversion=-123, gap_open=400, gap_extend=30), 16001),
-    (dict(match=91, transition=-31, transversion=-123, gap_open=3942, gap_extend=30), 9400),
+    (dict(match=91, transition=-31, transversion=-123, gap_open=400, gap_extend=30), 16001, False),
+    (dict(match=91, transition=-31, transversion=-123, gap_open=3942, gap_extend=30), 9400, False),
+    (dict(match=128, transition=-31, transversion=-123, gap_open=400, gap_extend=30), 9400, False),
 ]
 
 
 @pytest.mark.parametrize("case", range(len(LIMIT_SCORINGS)))
 def test_packed_limit_scorings(ctx, case):
-    sc, ydrop = LIMIT_SCORINGS[case]
+    sc, ydrop, packed = LIMIT_SCORINGS[case]
     w = W.tiny(n_seeds=300, flank=400, seed=20 + case)
     a = run(ctx, w, False, ydrop=ydrop, scoring=sc)
     b = run(ctx, w, True, ydrop=ydrop, scoring=sc)
     same(a, b, "limit scoring %d" % case)
+    assert (a[2]["n_packed"] > 0) == packed and b[2]["n_packed"] == 0
     against_oracle(w, a, ydrop=ydrop, scoring=sc, label="limit scoring %d" % case)
 
 
