@@ -120,15 +120,12 @@ def make_workload(name):
 
 
 def cpu_baseline(w, target_seconds, local):
-    """The oracle, as it stands, on a seeded sample of the batch, all host cores."""
+    """The oracle, as it stands, on a seeded sample of the batch, on the host
+    cores this process may use (at most 16)."""
     import numpy as np
 
     import oracle
-    threads = os.cpu_count() or 1
-    try:
-        threads = len(os.sched_getaffinity(0))
-    except (AttributeError, OSError):
-        pass
+    threads = oracle.default_threads()
     rng = np.random.default_rng(123)
     seeds = w["seeds"]
     query = oracle.revcomp(w["query"]) if w.get("query_rc") else w["query"]
@@ -270,11 +267,7 @@ def cpu_pipeline_baseline(w, target_seconds, round_size, doubling):
     import numpy as np
 
     import oracle
-    threads = os.cpu_count() or 1
-    try:
-        threads = len(os.sched_getaffinity(0))
-    except (AttributeError, OSError):
-        pass
+    threads = oracle.default_threads()
     L = 1 << 12
     full = min(w["target"].size, w["query"].size)
     while True:

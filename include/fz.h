@@ -186,9 +186,11 @@ enum {
     FZ_HIT_ESEED = 32,             /* seed outside its window or window outside the sequences */
     FZ_HIT_ERANGE = 64,            /* window too long for int32 scores with these parameters */
     FZ_HIT_COVERED = 128,          /* fz_extend_rounds: seed on an earlier round's alignment, not extended */
-    FZ_HIT_EEXEC = 256             /* the executor's recompute of a side disagreed with the inspector
+    FZ_HIT_EEXEC = 256,            /* the executor's recompute of a side disagreed with the inspector
                                     * (best score, best cell or pointer-row size): score and
                                     * coordinates stand, no CIGAR is given (FZ_HIT_TRACED is clear) */
+    FZ_HIT_WIDE = 512              /* information only: a side's band passed 384 positions and the
+                                    * side was redone in the 1024-position window */
 };
 
 #define FZ_YDROP_INF 2147483647    /* ydrop >= this: no pruning */

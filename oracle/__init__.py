@@ -62,6 +62,8 @@ def _load():
         lib.fzo_free.argtypes = [P]
         lib.fzo_side_matrix.restype = i64
         lib.fzo_side_matrix.argtypes = [P, i64, P, i64, P, i64, P, P, P, P, P, P]
+        lib.fzo_rescore.restype = i64
+        lib.fzo_rescore.argtypes = [P, i64, P, i64, P, P, P, P, P, P, i64, P]
         _lib = lib
     return _lib
 
@@ -189,6 +191,16 @@ def seeds_array(seeds):
     return a.reshape(-1, 7)
 
 
+def default_threads():
+    """Worker threads of a batch run: the CPUs this process may use, at most
+    16 (a GPU host's share per GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
 def run(target, query, seeds, scoring, ydrop, min_tb=None, traceback=True, local=False,
         threads=None):
     """Run the oracle on a batch.
@@ -206,7 +218,7 @@ def run(target, query, seeds, scoring, ydrop, min_tb=None, traceback=True, local
     sc = _scoring_arr(scoring)
     hits = np.zeros(n, dtype=HIT_DTYPE)
     if threads is None:
-        threads = os.cpu_count() or 1
+        threads = default_threads()
     if min_tb is None:
         min_tb = -(1 << 62)
     h = lib.fzo_run(T.ctypes.data, T.size, Q.ctypes.data, Q.size, S.ctypes.data, n, sc.ctypes.data,
@@ -356,3 +368,28 @@ def extend_rounds(target, query, seeds, scoring, ydrop, min_tb, round_size, thre
 def cigar_string(words):
     """BAM-style run words -> text CIGAR."""
     return "".join("%d%s" % (w >> 4, "MID"[w & 15]) for w in np.asarray(words, dtype=np.uint32).tolist())
+
+
+def rescore(target, query, t_begin, q_begin, cigar_off, cigar_len, words, scoring):
+    """Score CIGARs laid on the sequences (a check of alignments at any batch
+    size): row k's runs words[cigar_off[k] : cigar_off[k] + cigar_len[k]]
+    from (t_begin[k], q_begin[k]), M columns by their substitution scores,
+    each gap run of length g at -(gap_open + g * gap_extend).  Returns
+    (score, t_end, q_end, n_bad) with int64 arrays; rows that leave the
+    sequences or hold an unknown code or base count in n_bad and read 0."""
+    lib = _load()
+    T = _as_bytes(target)
+    Q = _as_bytes(query)
+    sc = _scoring_arr(scoring)
+    tb = np.ascontiguousarray(t_begin, dtype=np.int64)
+    qb = np.ascontiguousarray(q_begin, dtype=np.int64)
+    off = np.ascontiguousarray(cigar_off, dtype=np.int64)
+    ln = np.ascontiguousarray(cigar_len, dtype=np.int64)
+    W = np.ascontiguousarray(words, dtype=np.uint32)
+    if W.size == 0:
+        W = np.zeros(1, dtype=np.uint32)
+    n = tb.size
+    out = np.zeros((max(n, 1), 3), dtype=np.int64)
+    bad = lib.fzo_rescore(T.ctypes.data, T.size, Q.ctypes.data, Q.size, sc.ctypes.data, tb.ctypes.data,
+                          qb.ctypes.data, off.ctypes.data, ln.ctypes.data, W.ctypes.data, n, out.ctypes.data)
+    return out[:n, 0].copy(), out[:n, 1].copy(), out[:n, 2].copy(), int(bad)

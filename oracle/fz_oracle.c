@@ -582,3 +582,57 @@ int64_t fzo_side_matrix(const uint8_t *a, int64_t m, const uint8_t *bq, int64_t 
     band_free(&b);
     return err;
 }
+
+/* ------------------------------------------------------ CIGAR rescoring -- */
+
+/* The score of an alignment given as a CIGAR, for checks at any batch size.
+ * Row k lays words[off[k] .. off[k] + len[k]) (BAM-style runs, len << 4 |
+ * code, code 0 = M: target and query advance; 1 = I: query only; 2 = D:
+ * target only) on the sequences from (t_begin[k], q_begin[k]): the sum of
+ * the substitution scores of its M columns (the seed's own included) minus
+ * gap_open + g * gap_extend for every gap run of length g.  out[3k] gets the
+ * score, out[3k + 1] and out[3k + 2] the end coordinates (one past the last
+ * column).  Returns the number of rows that leave the sequences, hold an
+ * unknown code or an invalid base (their out entries are left at 0). */
+int64_t fzo_rescore(const uint8_t *T, int64_t tlen, const uint8_t *Q, int64_t qlen, const fzo_scoring *sc,
+                    const int64_t *t_begin, const int64_t *q_begin, const int64_t *off, const int64_t *len,
+                    const uint32_t *words, int64_t n, int64_t *out)
+{
+    int64_t tab[5][5];
+    sub_table(sc, tab);
+    int64_t bad = 0;
+    for (int64_t k = 0; k < n; k++) {
+        int64_t t = t_begin[k], q = q_begin[k], score = 0;
+        int ok = t >= 0 && q >= 0;
+        for (int64_t r = 0; ok && r < len[k]; r++) {
+            const uint32_t w = words[off[k] + r];
+            const int64_t g = (int64_t)(w >> 4);
+            const uint32_t code = w & 15u;
+            if (code == 0) {
+                if (t + g > tlen || q + g > qlen) { ok = 0; break; }
+                for (int64_t c = 0; c < g; c++) {
+                    const int a = base_code(T[t + c], sc), b = base_code(Q[q + c], sc);
+                    if (a < 0 || b < 0) { ok = 0; break; }
+                    score += tab[a][b];
+                }
+                t += g;
+                q += g;
+            } else if (code == 1 || code == 2) {
+                score -= sc->gap_open + g * sc->gap_extend;
+                if (code == 1) q += g; else t += g;
+                if (t > tlen || q > qlen) ok = 0;
+            } else {
+                ok = 0;
+            }
+        }
+        if (ok) {
+            out[3 * k] = score;
+            out[3 * k + 1] = t;
+            out[3 * k + 2] = q;
+        } else {
+            out[3 * k] = out[3 * k + 1] = out[3 * k + 2] = 0;
+            bad++;
+        }
+    }
+    return bad;
+}

@@ -216,6 +216,7 @@ __global__ void combine_kernel(CombineArgs a)
         h.q_end = s.q_pos + s.seed_len + R.je;
         h.cells = L.cells + R.cells;
         bmax = (uint64_t)max(L.max_band, R.max_band);
+        if ((L.flags | R.flags) & SO_WIDE_FLAG) h.status |= FZ_HIT_WIDE;
         if (a.traceback) {
             if (h.score > a.min_tb) {
                 h.status |= FZ_HIT_TRACED;

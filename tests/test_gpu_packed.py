@@ -57,8 +57,15 @@ def run(ctx, w, exact32, ydrop=None, scoring=None, traceback=True):
 
 
 def same(a, b, label):
+    """Equal results.  Which sides go to the 1024-position retry (the
+    FZ_HIT_WIDE bit) may differ: the packed and 32-bit 384-position windows
+    slide on different lane grids, so a band of about 384 positions fits one
+    and not the other; the retry's results are the same."""
     ha, ca, sa = a
     hb, cb, sb = b
+    ha, hb = ha.copy(), hb.copy()
+    ha[:, 1] &= ~fz.FZ_HIT_WIDE
+    hb[:, 1] &= ~fz.FZ_HIT_WIDE
     diff = np.nonzero((ha[:, COLS] != hb[:, COLS]).any(axis=1))[0]
     assert diff.size == 0, "%s: %d seeds differ, first %d: %s vs %s" % (
         label, diff.size, diff[0], ha[diff[0]].tolist(), hb[diff[0]].tolist())

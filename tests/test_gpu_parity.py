@@ -31,7 +31,8 @@ SC = dict(W.DEFAULT_SCORING)
 # hung after its first side; the batch itself was not special.  The current
 # kernels take their side from blockIdx and have no per-lane loop exit
 # (tests/test_kernel_isa.py checks the compiled code for it).
-OK_BITS = fz.FZ_HIT_TRACED | fz.FZ_HIT_EAGER_LEFT | fz.FZ_HIT_EAGER_RIGHT | fz.FZ_HIT_BELOW_MIN
+OK_BITS = (fz.FZ_HIT_TRACED | fz.FZ_HIT_EAGER_LEFT | fz.FZ_HIT_EAGER_RIGHT | fz.FZ_HIT_BELOW_MIN
+           | fz.FZ_HIT_WIDE)
 
 
 def log(msg):
@@ -282,7 +283,7 @@ def test_wide_band_and_overflow(ctx):
     gh, gc, st = run_gpu(ctx, w, ydrop=fz.FZ_YDROP_INF)
     oh, ow, oo = run_oracle(w, ydrop=oracle.YDROP_INF)
     compare(gh, gc, oh, ow, oo, label="wide")
-    assert st["n_overflow"] >= 1
+    assert st["n_overflow"] >= 1 and gh[0, 1] & fz.FZ_HIT_WIDE
     w2 = one_seed(s, s, 0, 0, 19)
     gh2, _, _ = run_gpu(ctx, w2, ydrop=fz.FZ_YDROP_INF)
     assert gh2[0, 1] & fz.FZ_HIT_EBAND
@@ -397,62 +398,33 @@ def test_local_identical_closed_form(ctx):
     assert (gh[0, 0], gh[0, 3], gh[0, 5]) == (91 * 2048, 2048, 2048)
 
 
-def test_local_full_size_sampled(ctx):
-    """The 4,096 x 2048^2 batch in the benchmark's launch configuration;
-    a seeded sample of pairs against the oracle."""
+def test_local_full_size_all(ctx):
+    """The 4,096 x 2048^2 batch in the benchmark's launch configuration:
+    every pair against the oracle."""
     w = W.local_pairs()
     gh, _, _ = run_gpu(ctx, w, local=True)
-    rng = np.random.default_rng(0)
-    idx = np.sort(rng.choice(len(w["seeds"]), 24, replace=False))
-    oh, ow, oo = run_oracle(w, seeds=w["seeds"][idx], local=True, traceback=False)
-    compare(gh, None, oh, ow, oo, idx=idx, local=True, label="local full")
+    log("local full: oracle on all %d pairs" % len(w["seeds"]))
+    oh, ow, oo = run_oracle(w, local=True, traceback=False)
+    compare(gh, None, oh, ow, oo, local=True, label="local full")
     assert (gh[:, 0] >= 0).all()
 
 
 # ------------------------------------------------------- larger batches --
 
-def check_invariants(w, gh, gc, label, limit=1500):
-    """Rescore CIGARs from the sequences and check spans (any size); at most
-    `limit` traced seeds, chosen by a seeded draw."""
-    T, Q = w["target"], oracle_query(w)
-    code = np.full(256, -1, dtype=np.int64)
-    for k, c in enumerate(b"ACGTN"):
-        code[c] = k
-        code[c + 32] = k
-    sc = w["scoring"]
-    # score of (target code, query code), N = 4
-    table = np.zeros((5, 5), dtype=np.int64)
-    if "matrix" in sc:
-        table[:4, :4] = np.asarray(sc["matrix"], dtype=np.int64)
-        table[4, :] = table[:, 4] = sc["n_score"]
-    else:
-        cls = [sc["match"], sc["transversion"], sc["transition"], sc["transversion"]]
-        for x in range(4):
-            for y in range(4):
-                table[x, y] = cls[x ^ y]
+def check_invariants(w, gh, gc, label):
+    """Every traced seed's CIGAR, laid on the sequences from its begin
+    coordinates, rescores to its score and ends at its end coordinates
+    (oracle.rescore, any batch size).  Returns the number checked."""
     traced = np.nonzero(gh[:, 1] & fz.FZ_HIT_TRACED)[0]
-    if traced.size > limit:
-        traced = np.sort(np.random.default_rng(1).choice(traced, limit, replace=False))
-    for k in traced:
-        g = dict(zip(fz.HIT_FIELDS, gh[k].tolist()))
-        words = gc[g["cigar_off"]:g["cigar_off"] + g["cigar_len"]]
-        t, q, total = g["t_begin"], g["q_begin"], 0
-        for wd in words.tolist():
-            n, op = wd >> 4, wd & 15
-            if op == 0:
-                a = code[T[t:t + n]]
-                b = code[Q[q:q + n]]
-                total += int(table[a, b].sum())
-                t += n
-                q += n
-            else:
-                total -= sc["gap_open"] + n * sc["gap_extend"]
-                if op == 1:
-                    q += n
-                else:
-                    t += n
-        assert (t, q) == (g["t_end"], g["q_end"]), (label, k)
-        assert total == g["score"], (label, k)
+    if traced.size == 0:
+        return 0
+    s, te, qe, bad = oracle.rescore(w["target"], oracle_query(w), gh[traced, 2], gh[traced, 4], gh[traced, 6],
+                                    gh[traced, 7], gc, w["scoring"])
+    assert bad == 0, (label, bad)
+    wrong = np.nonzero((s != gh[traced, 0]) | (te != gh[traced, 3]) | (qe != gh[traced, 5]))[0]
+    assert wrong.size == 0, (label, "seed", int(traced[wrong[0]]), int(s[wrong[0]]), gh[traced[wrong[0]]].tolist())
+    log("%s: %d traced alignments rescored" % (label, traced.size))
+    return traced.size
 
 
 def sample_compare(ctx, w, n_sample, label, seed=0, extra_idx=None):
@@ -484,57 +456,83 @@ def test_executor_heavy_reduced(ctx):
 def test_chromosome_reduced(ctx):
     w = W.chromosome(length=600_000, inv_min=5_000, inv_max=20_000, seed=3)
     gh, gc, st = sample_compare(ctx, w, 40, "chromosome reduced")
-    check_invariants(w, gh, gc, "chromosome reduced", limit=200)
+    check_invariants(w, gh, gc, "chromosome reduced")
+
+
+def stratified(gh, rng, n_uniform, per_bin, n_wide, n_eager, n_below, n_longest):
+    """Seed indices for a full-size comparison: a uniform draw, then up to
+    per_bin seeds of every executor length bin, the sides redone in the wide
+    window, seeds traced wholly (or half) in the inspector, seeds below the
+    traceback threshold, and the longest alignments."""
+    n = len(gh)
+    parts = [rng.choice(n, min(n_uniform, n), replace=False)]
+
+    def some(mask, k):
+        cand = np.nonzero(mask)[0]
+        return rng.choice(cand, min(k, cand.size), replace=False) if cand.size else cand
+
+    st = gh[:, 1]
+    for b in range(8):
+        parts.append(some(gh[:, 11] == b, per_bin))
+    parts.append(some((st & fz.FZ_HIT_WIDE) != 0, n_wide))
+    both = fz.FZ_HIT_EAGER_LEFT | fz.FZ_HIT_EAGER_RIGHT
+    parts.append(some((st & both) == both, n_eager))
+    parts.append(some(((st & both) != 0) & ((st & both) != both), n_eager))
+    parts.append(some((st & fz.FZ_HIT_BELOW_MIN) != 0, n_below))
+    span = gh[:, 3] - gh[:, 2]
+    parts.append(np.argsort(span)[-n_longest:])
+    return np.unique(np.concatenate(parts))
 
 
 @pytest.mark.skipif(os.environ.get("FZ_FULL_SIZE", "1") == "0", reason="full-size runs disabled")
-def test_skewed_full_size_sampled(ctx):
-    """The one-million-seed skewed batch as the benchmark runs it; a seeded
-    sample (plus the longest alignments) against the oracle."""
+def test_skewed_full_size_stratified(ctx):
+    """The one-million-seed skewed batch as the benchmark runs it: over
+    10,000 seeds against the oracle field by field (a uniform draw plus
+    every stratum: each executor length bin, wide-window retries, eager
+    sides, untraced seeds, the longest alignments), and every traced
+    alignment rescored."""
     w = W.skewed()
     gh, gc, st = run_gpu(ctx, w, min_tb=w["min_tb"])
-    rng = np.random.default_rng(0)
-    n = len(w["seeds"])
-    idx = rng.choice(n, 160, replace=False)
-    span = gh[:, 3] - gh[:, 2]
-    idx = np.unique(np.concatenate([idx, np.argsort(span)[-6:]]))
+    idx = stratified(gh, np.random.default_rng(0), 7200, 400, 600, 600, 400, 40)
+    log("skewed full: oracle on %d seeds (%.3g cells)" % (len(idx), float(gh[idx, 8].sum())))
+    assert len(idx) >= 10000
     oh, ow, oo = run_oracle(w, seeds=w["seeds"][idx], min_tb=w["min_tb"])
     compare(gh, gc, oh, ow, oo, idx=idx, label="skewed full")
-    assert not (gh[:, 1] & (fz.FZ_HIT_EBAND | fz.FZ_HIT_ERANGE | fz.FZ_HIT_ESEED)).any()
-    check_invariants(w, gh, gc, "skewed full")
+    assert not (gh[:, 1] & (fz.FZ_HIT_EBAND | fz.FZ_HIT_ERANGE | fz.FZ_HIT_ESEED | fz.FZ_HIT_EEXEC)).any()
+    assert check_invariants(w, gh, gc, "skewed full") == int(((gh[:, 1] & fz.FZ_HIT_TRACED) != 0).sum())
 
 
-def _full_size_sampled(ctx, w, n_sample, n_longest, label):
+def _full_size_sampled(ctx, w, n_uniform, per_bin, n_longest, label):
     log("%s: %d records, target %d bp" % (label, len(w["seeds"]), w["target"].size))
     gh, gc, st = run_gpu(ctx, w, min_tb=w.get("min_tb"))
     log("%s: %d executor sides, %d batches, %.3g pointer bytes" % (label, st["n_executor"], st["n_batches"],
                                                                    st["pointer_bytes"]))
-    rng = np.random.default_rng(0)
-    n = len(w["seeds"])
-    idx = rng.choice(n, min(n_sample, n), replace=False)
-    span = gh[:, 3] - gh[:, 2]
-    idx = np.unique(np.concatenate([idx, np.argsort(span)[-n_longest:]]))
+    idx = stratified(gh, np.random.default_rng(0), n_uniform, per_bin, per_bin, per_bin, per_bin, n_longest)
     oh, ow, oo = run_oracle(w, seeds=w["seeds"][idx], min_tb=w.get("min_tb"))
     log("%s: oracle done on %d records" % (label, len(idx)))
     compare(gh, gc, oh, ow, oo, idx=idx, label=label)
-    assert not (gh[:, 1] & (fz.FZ_HIT_EBAND | fz.FZ_HIT_ERANGE | fz.FZ_HIT_ESEED)).any(), label
-    check_invariants(w, gh, gc, label)
+    assert not (gh[:, 1] & (fz.FZ_HIT_EBAND | fz.FZ_HIT_ERANGE | fz.FZ_HIT_ESEED | fz.FZ_HIT_EEXEC)).any(), label
+    assert check_invariants(w, gh, gc, label) == int(((gh[:, 1] & fz.FZ_HIT_TRACED) != 0).sum())
+    return idx
 
 
 @pytest.mark.skipif(os.environ.get("FZ_FULL_SIZE", "1") == "0", reason="full-size runs disabled")
 def test_executor_heavy_full_size_sampled(ctx):
-    """100,000 pairs of 1-20 kb homology, every seed traced: a seeded sample
-    and the longest alignments against the oracle, invariants on the rest."""
+    """100,000 pairs of 1-20 kb homology, every seed traced: 1,500 seeds by
+    a seeded draw, up to 100 per executor length bin and the 20 longest
+    alignments against the oracle; every traced alignment rescored."""
     log("generating the executor-heavy batch")
-    _full_size_sampled(ctx, W.executor_heavy(), 40, 4, "executor heavy full")
+    _full_size_sampled(ctx, W.executor_heavy(), 1500, 100, 20, "executor heavy full")
 
 
 @pytest.mark.skipif(os.environ.get("FZ_FULL_SIZE", "1") == "0", reason="full-size runs disabled")
 def test_chromosome_full_size_sampled(ctx):
     """Two 20 Mbp chromosomes, all forward shared 19-mers after diagonal
-    dedup: a seeded sample and the longest alignments against the oracle."""
+    dedup: 600 seeds by a seeded draw, up to 40 per stratum and the 10
+    longest alignments against the oracle; every traced alignment
+    rescored."""
     log("generating the chromosome pair")
-    _full_size_sampled(ctx, W.chromosome(), 24, 4, "chromosome full")
+    _full_size_sampled(ctx, W.chromosome(), 600, 40, 10, "chromosome full")
 
 
 # ------------------------------------------------------ reverse strand --
@@ -574,16 +572,17 @@ def test_chromosome_rc_reduced(ctx):
     """Reverse-strand seeds of a 600 kb chromosome pair (the inversions)."""
     w = W.chromosome_rc(length=600_000, inv_min=5_000, inv_max=20_000, seed=3)
     gh, gc, st = sample_compare(ctx, w, 40, "chromosome rc reduced")
-    check_invariants(w, gh, gc, "chromosome rc reduced", limit=200)
+    check_invariants(w, gh, gc, "chromosome rc reduced")
 
 
 @pytest.mark.skipif(os.environ.get("FZ_FULL_SIZE", "1") == "0", reason="full-size runs disabled")
 def test_chromosome_rc_full_size_sampled(ctx):
     """The 20 Mbp chromosome pair searched on the reverse strand (seeds in
-    the five inversions and chance hits): a seeded sample and the longest
-    alignments against the oracle, invariants on the rest."""
+    the five inversions and chance hits): 400 seeds by a seeded draw, up to
+    30 per stratum and the 6 longest alignments against the oracle; every
+    traced alignment rescored."""
     log("generating the chromosome pair, reverse-strand seeds")
-    _full_size_sampled(ctx, W.chromosome_rc(), 24, 4, "chromosome rc full")
+    _full_size_sampled(ctx, W.chromosome_rc(), 400, 30, 6, "chromosome rc full")
 
 
 # ------------------------------------------------ 4x4 matrix and N ---
@@ -646,7 +645,7 @@ def test_matrix_reverse_strand(ctx):
     w = W.with_matrix_and_n(W.chromosome_rc(length=300_000, inv_min=5_000, inv_max=20_000, seed=6), 30, 5, 200,
                             seed=7)
     gh, gc, st = sample_compare(ctx, w, 60, "matrix chromosome rc reduced")
-    check_invariants(w, gh, gc, "matrix chromosome rc reduced", limit=200)
+    check_invariants(w, gh, gc, "matrix chromosome rc reduced")
 
 
 def test_matrix_local(ctx):
@@ -687,9 +686,11 @@ def test_matrix_errors(ctx):
 
 @pytest.mark.skipif(os.environ.get("FZ_FULL_SIZE", "1") == "0", reason="full-size runs disabled")
 def test_skewed_matrix_full_size_sampled(ctx):
-    """The matrix benchmark batch (one million seeds, runs of N), sampled."""
+    """The matrix benchmark batch (one million seeds, runs of N): 1,500
+    seeds by a seeded draw, up to 150 per stratum and the 20 longest
+    alignments against the oracle; every traced alignment rescored."""
     w = W.skewed_matrix()
-    _full_size_sampled(ctx, w, 120, 4, "skewed matrix full")
+    _full_size_sampled(ctx, w, 1500, 150, 20, "skewed matrix full")
 
 
 def test_matrix_wide_band(ctx):

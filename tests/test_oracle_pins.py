@@ -804,3 +804,46 @@ def test_rounds_coverage_by_cells(round_size, doubling):
                 this_round |= _cells_of(w["target"], w["query"], h[k], got)
         earlier |= this_round
     assert 0 < n_cov < len(S)
+
+
+# ------------------------------------------------------ CIGAR rescoring --
+
+def test_rescore_hand_examples():
+    """oracle.rescore (the full-size invariant check) against scores written
+    out by hand: M columns by match / transition / transversion, a gap run
+    of g at -(open + g * extend), I on the query only, D on the target only."""
+    m, ts, tv, go, ge = SC["match"], SC["transition"], SC["transversion"], SC["gap_open"], SC["gap_extend"]
+    T = b"ACGTACGTAC"
+    Q = b"ACGAACGTTTAC"
+    # 8M: A-A C-C G-G T-A (transversion) A-A C-C G-G T-T
+    W8 = np.array([8 << 4], dtype=np.uint32)
+    # 3M 2I 5M from (0, 0): ACG/ACG, insert "AA" in the query, then CGTAC/CGTTT
+    WI = np.array([3 << 4, (2 << 4) | 1, 5 << 4], dtype=np.uint32)
+    # 2M 1D 2M from (0, 0): AC/AC, skip target G, TA/GA (transversion T-G, then A-A)
+    WD = np.array([2 << 4, (1 << 4) | 2, 2 << 4], dtype=np.uint32)
+    words = np.concatenate([W8, WI, WD])
+    s, te, qe, bad = oracle.rescore(T, Q, [0, 0, 0], [0, 0, 0], [0, 1, 4], [1, 3, 3], words, SC)
+    assert bad == 0
+    assert s[0] == 7 * m + tv and (te[0], qe[0]) == (8, 8)
+    assert (te[1], qe[1]) == (8, 10)
+    # WI's 5M aligns T[3:8] = "TACGT" with Q[5:10] = "CGTTT": T-C ts, A-G ts, C-T ts, G-T tv, T-T m
+    assert s[1] == 3 * m - (go + 2 * ge) + (ts + ts + ts + tv + m)
+    assert s[2] == 2 * m - (go + ge) + (tv + m) and (te[2], qe[2]) == (5, 4)
+
+
+def test_rescore_flags_bad_rows():
+    T, Q = b"ACGT", b"ACGT"
+    words = np.array([5 << 4, 2 << 4, (1 << 4) | 7], dtype=np.uint32)
+    s, te, qe, bad = oracle.rescore(T, Q, [0, 3, 0], [0, 0, 0], [0, 1, 2], [1, 1, 1], words, SC)
+    assert bad == 3 and (s == 0).all()
+
+
+def test_rescore_matches_oracle_alignments(tiny_small):
+    """Every alignment the oracle traces rescores to its own score and end."""
+    w = tiny_small
+    oh, ow, oo = oracle.run(w["target"], w["query"], w["seeds"], w["scoring"], w["ydrop"])
+    ok = (oh["status"] == 0) & (oh["n_runs"] > 0)
+    s, te, qe, bad = oracle.rescore(w["target"], w["query"], oh["t_begin"][ok], oh["q_begin"][ok], oo[ok],
+                                    oh["n_runs"][ok], ow, w["scoring"])
+    assert bad == 0 and ok.sum() > 50
+    assert (s == oh["score"][ok]).all() and (te == oh["t_end"][ok]).all() and (qe == oh["q_end"][ok]).all()
