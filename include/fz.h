@@ -184,7 +184,8 @@ enum {
     FZ_HIT_BELOW_MIN = 8,          /* score <= min_traceback_score: no CIGAR by request */
     FZ_HIT_EBAND = 16,             /* a side's band outgrew the widest kernel: result invalid */
     FZ_HIT_ESEED = 32,             /* seed outside its window or window outside the sequences */
-    FZ_HIT_ERANGE = 64,            /* window too long for int32 scores with these parameters */
+    FZ_HIT_ERANGE = 64,            /* window too long for int32 scores with these parameters, or a
+                                    * side window longer than 2^28 bases */
     FZ_HIT_COVERED = 128,          /* fz_extend_rounds: seed on an earlier round's alignment, not extended */
     FZ_HIT_EEXEC = 256,            /* the executor's recompute of a side disagreed with the inspector
                                     * (best score, best cell or pointer-row size): score and

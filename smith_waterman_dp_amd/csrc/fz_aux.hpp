@@ -88,7 +88,8 @@ __global__ void setup_kernel(const fz_seed *__restrict__ seeds, int64_t n, int64
         // far from the int32 sentinels
         const int64_t msub = sc.msub;
         const int64_t span = (s.t_hi - s.t_lo) + (s.q_hi - s.q_lo) + 2;
-        if ((msub + sc.e) * span + sc.oe >= SCORE_LIMIT / 2) {
+        if ((msub + sc.e) * span + sc.oe >= SCORE_LIMIT / 2 || s.t_hi - s.t_lo > MAX_SIDE_LEN ||
+            s.q_hi - s.q_lo > MAX_SIDE_LEN) {
             in.status = FZ_HIT_ERANGE;
         } else {
             int64_t ss = 0;
@@ -437,7 +438,13 @@ constexpr int WALK_CHUNK = 2 * WALK_LANES;
 // Rows hold 6 or 8 positions per word (RowHdr); position p of a row is in
 // word p / cpw at nibble shift 4 * (cpw - 1 - p % cpw).
 __device__ __forceinline__ int row_word(int p, bool cpw8) { return cpw8 ? (p >> 3) : p / 6; }
-__device__ __forceinline__ int row_shift(int p, bool cpw8) { return cpw8 ? 4 * (7 - (p & 7)) : 4 * (5 - p % 6); }
+// bit offset of cell p's nibble in its word (formats at RowHdr)
+__device__ __forceinline__ int row_shift(int p, bool cpw8, bool pk)
+{
+    if (!pk) return cpw8 ? 4 * (7 - (p & 7)) : 4 * (5 - p % 6);
+    const int k = cpw8 ? (p & 7) : p % 6;
+    return 8 * (k >> 2) * (cpw8 ? 1 : 0) + 4 * ((cpw8 ? k & 3 : k) >> 1) + 16 * (k & 1);
+}
 
 __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
 {
@@ -479,16 +486,16 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
     };
     // the staged pointer nibble of cell (ii, dd - ii) on chunk row r, or 16
     // when the row does not hold it (fields of row r live in lane r % 64;
-    // the row's cell format is the sign bit of ib8, ib8 & 0x7fffffff its ibase
-    // biased by 2^30)
+    // the row's format flags are the top two bits of ib8 (ROW_CPW8, ROW_PK),
+    // ib8 & ROW_OFF_MASK its ibase biased by 2^29)
     auto nib_at = [&](int r, int ii, int ib8, int w0, int nw) -> uint32_t {
-        const bool cpw8 = ib8 < 0;
-        const int p = ii - ((ib8 & 0x7fffffff) - (1 << 30));
+        const bool cpw8 = ((uint32_t)ib8 & ROW_CPW8) != 0, pk = ((uint32_t)ib8 & ROW_PK) != 0;
+        const int p = ii - ((int)((uint32_t)ib8 & ROW_OFF_MASK) - (1 << 29));
         if (p < 0) return 16u;
         const int w = row_word(p, cpw8);
         const int q = w - w0;
         if (w >= nw || q < 0 || q >= WPR) return 16u;
-        return (wl[r][q] >> row_shift(p, cpw8)) & 0xFu;
+        return (wl[r][q] >> row_shift(p, cpw8, pk)) & 0xFu;
     };
     while (!bad && !(st == 0 && i == 0 && j == 0)) {
         const int d = i + j;
@@ -507,7 +514,7 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
                 h[h2] = hdr[dr];
                 // (clamped to the side's rows, so that no header value can
                 // send a read outside them)
-                const uint32_t next_off = hdr[min(dr + 1, it.dstar)].off & ~ROW_CPW8;
+                const uint32_t next_off = hdr[min(dr + 1, it.dstar)].off & ROW_OFF_MASK;
                 rend[h2] = min(dr < it.dstar ? next_off : total_rows, total_rows);
             }
             uint32_t v[2][WPR];
@@ -515,7 +522,7 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
             for (int h2 = 0; h2 < 2; ++h2) {
                 const int dr = dlo + h2 * WALK_LANES + lane;
                 const bool cpw8 = (h[h2].off & ROW_CPW8) != 0;
-                const uint32_t off = h[h2].off & ~ROW_CPW8;
+                const uint32_t off = h[h2].off & ROW_OFF_MASK;
                 const int plo = max(0, i - (d - dr)) - h[h2].ibase;
                 rw0[h2] = plo <= 0 ? 0 : row_word(plo, cpw8);
                 rnw[h2] = (dr <= d && rend[h2] > off) ? (int)(rend[h2] - off) : 0;
@@ -524,9 +531,9 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
                 // clamped loads below repeat its last word (cache hits)
                 const int phi = i - h[h2].ibase;
                 rnw[h2] = min(rnw[h2], phi < 0 ? 0 : row_word(phi, cpw8) + 1);
-                // ibase biased by 2^30 (rows' ibase lies within +-2^30), the
-                // format in the sign bit
-                rib[h2] = (int)((uint32_t)(h[h2].ibase + (1 << 30)) | (cpw8 ? 0x80000000u : 0u));
+                // ibase biased by 2^29 (rows' ibase lies within +-2^29: sides
+                // are at most MAX_SIDE_LEN long), the format flags above it
+                rib[h2] = (int)((uint32_t)(h[h2].ibase + (1 << 29)) | (h[h2].off & (ROW_CPW8 | ROW_PK)));
 #pragma unroll
                 for (int q = 0; q < WPR; ++q) {
                     // every load in bounds (the side's first word when the

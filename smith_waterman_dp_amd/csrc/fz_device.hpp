@@ -120,15 +120,24 @@ struct ExecItem {
 };
 
 // Row header of the executor's pointer store, one per anti-diagonal.  A
-// row word holds 6 or 8 consecutive positions' nibbles, the first position
-// in the highest nibble: 8 when off carries ROW_CPW8 (the 1024-position and
-// the packed 256-position layouts), 6 otherwise (the 192- and 384-position
-// layouts, which keep the six-cells-per-word format).
+// row word holds 6 or 8 consecutive positions' nibbles: 8 when off carries
+// ROW_CPW8 (the 1024-position and the packed 256-position layouts), 6
+// otherwise.  The 32-bit layouts put the first position in the highest
+// nibble.  The packed layouts (ROW_PK) put position k of a lane (two per
+// register) at bit 4 * (k >> 1) + 16 * (k & 1), and in the 256-position
+// layout the odd lane of a pair 8 bits above the even one: bit
+// 8 * (p >> 2) + 4 * ((p >> 1) & 1) + 16 * (p & 1) for cell p of the word.
 constexpr uint32_t ROW_CPW8 = 0x80000000u;
+constexpr uint32_t ROW_PK = 0x40000000u;
+constexpr uint32_t ROW_OFF_MASK = 0x3FFFFFFFu;
 struct RowHdr {
-    uint32_t off;               // dword offset of the row inside the side's row area (| ROW_CPW8)
+    uint32_t off;               // dword offset of the row inside the side's row area (| format flags)
     int32_t ibase;              // i of slot 0 of the row's first lane
 };
+
+// Longest side window: keeps every position, and the walker's packed
+// (position, row format) words, far inside 32 bits.
+constexpr int64_t MAX_SIDE_LEN = (int64_t)1 << 28;
 
 // Entries per array of the LDS hand-over between layouts (S of two
 // diagonals and the two gap states of the union of the last two hulls,

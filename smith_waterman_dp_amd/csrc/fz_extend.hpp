@@ -443,7 +443,9 @@ struct SideDP {
                 for (int k = 0; k < NWORD; ++k) rows[k] = 0u;   // (0,0): no gap extends through it
             }
             rowoff = NWORD;
-            rowcap = (uint32_t)((ptr_bytes - 8 * ((int64_t)dstop + 1)) / 4);
+            // (row offsets share their word with the format flags: a side
+            // with more rows than they can address ends in a mismatch)
+            rowcap = (uint32_t)min<int64_t>((ptr_bytes - 8 * ((int64_t)dstop + 1)) / 4, (int64_t)ROW_OFF_MASK);
             return step<0, EXEC>(1, dstop, eager_lds) ? 2 : -1;
         }
         if (lane >= EL0 && lane <= EL1) {

@@ -270,19 +270,12 @@ struct SidePk {
             dmax = r == 0 ? Sk : pk_max(dmax, Sk);     // (killed halves hold DEAD)
         }
         if (PTR) {
-            // the row format: position 0 in the highest nibble
-            if constexpr (C2 == 2) {
-                // lo halves: positions 0, 2; hi halves: 1, 3
-                const uint32_t a = nib[0] << 4;               // lo: p0 << 4, hi: p1 << 4 (bits 20-23)
-                const uint32_t b = a | (nib[1] & 0x000F000Fu);  // lo: p0 << 4 | p2, hi: p1 << 4 | p3
-                // 16 bits: p0 p1 p2 p3 (highest first)
-                word = ((b & 0xF0u) << 8) | ((b >> 12) & 0xF00u) | ((b & 0xFu) << 4) | ((b >> 16) & 0xFu);
-            } else {
-                uint32_t w = 0;
+            // the packed row order (RowHdr): register r's two nibbles at bits
+            // 4r and 4r + 16, one shift-or per register
+            uint32_t w = nib[0];
 #pragma unroll
-                for (int r = 0; r < C2; ++r) w = (w << 8) | ((nib[r] & 0xFu) << 4) | ((nib[r] >> 16) & 0xFu);
-                word = w;
-            }
+            for (int r = 1; r < C2; ++r) w |= nib[r] << (4 * r);
+            word = w;
         }
         // dead-byte masks: the sign byte of each half
         if constexpr (C2 == 2) {
@@ -450,15 +443,15 @@ struct SidePk {
             } else {
                 if (lane == 0) {
                     RowHdr h;
-                    h.off = rowoff | (CPW == 8 ? ROW_CPW8 : 0u);
+                    h.off = rowoff | (CPW == 8 ? ROW_CPW8 : 0u) | ROW_PK;
                     h.ibase = rlane0 * C + od;
                     hdr[d] = h;
                 }
                 if (PAIRED) {
-                    // the odd lane's 16 bits under the even lane's
+                    // the odd lane's nibbles 8 bits above the even lane's
                     const uint32_t odd = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0xB1, 0xF, 0xF, false);
                     if (!(lane & 1) && lane >= rlane0 && lane <= lhi)
-                        rows[rowoff + ((lane - rlane0) >> 1)] = (word << 16) | odd;
+                        rows[rowoff + ((lane - rlane0) >> 1)] = word | (odd << 8);
                 } else if (lane >= llo && lane <= lhi) {
                     rows[rowoff + (lane - llo)] = word;
                 }
