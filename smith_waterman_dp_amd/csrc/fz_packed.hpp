@@ -142,7 +142,9 @@ struct SidePk {
 
     // registers (packed pairs)
     uint32_t SA[C2], SB[C2], R[C2], Dn[C2];
-    uint32_t TA[C2], QB[C2], TAn[C2], QBn[C2];
+    // sequence codes in two buffers per sequence, used in turn (see step):
+    // no register copies when a diagonal's prefetch becomes current
+    uint32_t Ta[2][C2], Qb[2][C2];
     uint32_t crossL, crossR;    // DPP targets whose edge lane keeps PK_DEAD2
     const GlobalU8 *ba, *bb;    // 16-bit code arrays, uniform bases (bytes)
     uint32_t ua, ub;            // element offsets of slot 0 of lane 0 (as in SideDP)
@@ -185,12 +187,38 @@ struct SidePk {
         load_unaligned_pk<C2>(base + 2u * (off + (uint32_t)(lane * C)), out);
     }
 
+    // After a slide inside step<DELTA, P>(d): this diagonal's codes and the
+    // prefetches, in the buffers that step uses.
+    template <int DELTA, int P>
     __device__ __forceinline__ void reload(int d, int od)
     {
-        fetch(ba, ua + od, TA);
-        fetch(bb, ub + (od - d), QB);
-        fetch(ba, ua + (od + 1), TAn);
-        fetch(bb, ub + (od - d - 1), QBn);
+        fetch(ba, ua + od, Ta[P]);
+        fetch(bb, ub + (od - d), Qb[DELTA == 1 ? P ^ 1 : P]);
+        fetch(ba, ua + (od + 1), Ta[P ^ 1]);
+        fetch(bb, ub + (od - d - 1), Qb[DELTA == 1 ? P : P ^ 1]);
+    }
+
+    // The state step<1, 0>(d + 1) starts from, after diagonal d (odd):
+    // Ta[0] holds the target codes of d + 1, Qb[1] the query codes of d + 1
+    // (the same as d's), Qb[0] those of d + 2.
+    __device__ __forceinline__ void reload_entry(int d, int od)
+    {
+        fetch(ba, ua + (od + 1), Ta[0]);
+        fetch(bb, ub + (od - d), Qb[1]);
+        fetch(bb, ub + (od - d - 1), Qb[0]);
+    }
+
+    // Swap the buffers' roles (a single pair before the four-diagonal loop).
+    __device__ __forceinline__ void swap_buffers()
+    {
+#pragma unroll
+        for (int k = 0; k < C2; ++k) {
+            const uint32_t a = Ta[0][k], b = Qb[0][k];
+            Ta[0][k] = Ta[1][k];
+            Qb[0][k] = Qb[1][k];
+            Ta[1][k] = a;
+            Qb[1][k] = b;
+        }
     }
 
     __device__ __forceinline__ void set_dmask() { dmask = min(2 * (t.m - W + 2) - K, 2 * t.n + 1 + K); }
@@ -211,8 +239,9 @@ struct SidePk {
     // best value; with PTR, word receives the lane's pointer nibbles in the
     // row format (PAIRED: 16 bits, first position highest; else C nibbles).
     template <int DELTA, bool PTR, bool MASKED>
-    __device__ __forceinline__ void cells_of(uint32_t (&SN)[C2], int rlo, int rhi, uint32_t &m0, uint32_t &m1,
-                                             uint32_t &dmax, uint32_t &word)
+    __device__ __forceinline__ void cells_of(uint32_t (&SN)[C2], const uint32_t (&TA)[C2], const uint32_t (&QB)[C2],
+                                             int rlo, int rhi, uint32_t &m0, uint32_t &m1, uint32_t &dmax,
+                                             uint32_t &word)
     {
         uint32_t X[C2];
 #pragma unroll
@@ -331,19 +360,19 @@ struct SidePk {
     // dead, nothing counted) and keeps empty hulls, so that later diagonals
     // end too, and the caller leaves its loop in one place with every value
     // of the side's state defined.
-    template <int DELTA, bool PTR>
+    //
+    // Buffers (P = 0, 1 in turn over the diagonal pairs): step<1, P> reads
+    // the target codes in Ta[P] and the query codes in Qb[P ^ 1] and
+    // prefetches the target codes of d + 2 into Ta[P ^ 1]; step<0, P> reads
+    // Ta[P] and Qb[P] and prefetches the query codes of d + 2 into
+    // Qb[P ^ 1].  After the four steps of P = 0, 1 every buffer is back in
+    // its role.
+    template <int DELTA, bool PTR, int P>
     __device__ __forceinline__ bool step(int d, int dstop)
     {
         int od = (d + K) >> 1;
-        if (DELTA == 1) {
-#pragma unroll
-            for (int k = 0; k < C2; ++k) TA[k] = TAn[k];
-            fetch(ba, ua + (od + 1), TAn);
-        } else {
-#pragma unroll
-            for (int k = 0; k < C2; ++k) QB[k] = QBn[k];
-            fetch(bb, ub + (od - d - 1), QBn);
-        }
+        if (DELTA == 1) fetch(ba, ua + (od + 1), Ta[P ^ 1]);
+        else fetch(bb, ub + (od - d - 1), Qb[P ^ 1]);
         int rlo = min(lo1 - DELTA, lo2);
         int rhi = max(hi1 - DELTA + 1, hi2);
         bool masked = false, live = true;
@@ -366,7 +395,7 @@ struct SidePk {
                     lo1 -= sh; hi1 -= sh; lo2 -= sh; hi2 -= sh;
                     rlo -= sh; rhi -= sh;
                     set_dmask();
-                    reload(d, od);
+                    reload<DELTA, P>(d, od);
                 }
             }
             masked = (W - 1 + od > t.m) || (d - od > t.n);
@@ -381,12 +410,14 @@ struct SidePk {
             }
         }
         uint32_t m0, m1, dmax, word = 0;
+        const uint32_t(&TAc)[C2] = Ta[P];
+        const uint32_t(&QBc)[C2] = Qb[DELTA == 1 ? P ^ 1 : P];
         if (masked) {
-            if (DELTA == 1) cells_of<DELTA, PTR, true>(SA, rlo, rhi, m0, m1, dmax, word);
-            else cells_of<DELTA, PTR, true>(SB, rlo, rhi, m0, m1, dmax, word);
+            if (DELTA == 1) cells_of<DELTA, PTR, true>(SA, TAc, QBc, rlo, rhi, m0, m1, dmax, word);
+            else cells_of<DELTA, PTR, true>(SB, TAc, QBc, rlo, rhi, m0, m1, dmax, word);
         } else {
-            if (DELTA == 1) cells_of<DELTA, PTR, false>(SA, rlo, rhi, m0, m1, dmax, word);
-            else cells_of<DELTA, PTR, false>(SB, rlo, rhi, m0, m1, dmax, word);
+            if (DELTA == 1) cells_of<DELTA, PTR, false>(SA, TAc, QBc, rlo, rhi, m0, m1, dmax, word);
+            else cells_of<DELTA, PTR, false>(SB, TAc, QBc, rlo, rhi, m0, m1, dmax, word);
         }
 
         // live hull of d: lanes from the ballot, positions from the edge
@@ -495,20 +526,43 @@ struct SidePk {
 
     // Diagonals from d (even) on until the end (-1) or a layout change
     // (returns the next d, even).
+    //
+    // Four diagonals per trip (the two buffer parities); a side entering at
+    // d = 2 (mod 4) first takes one pair.  An ended side stays ended (its
+    // hulls stay empty), so the number of live results of a trip gives the
+    // last live diagonal.
     __device__ int advance(int d, int dstop)
     {
         enter();
-        for (;; d += 2) {
-            const bool a = step<1, EXEC>(d, dstop);
-            const bool b = step<0, EXEC>(d + 1, dstop);
+        if (d & 2) {
+            const bool a = step<1, EXEC, 0>(d, dstop);
+            const bool b = step<0, EXEC, 0>(d + 1, dstop);
             if (!(a && b)) {
                 dend = a ? d : d - 1;       // the last live diagonal
                 return -1;
             }
-            if (((d + 1) & (SWITCH_EVERY - 1)) == SWITCH_EVERY - 1) {
-                dend = d + 1;
+            d += 2;
+            swap_buffers();
+        }
+        for (;;) {
+            // (scheduling barriers: each step's loads stay in its step, so
+            // the unrolled steps do not hold each other's registers)
+            const bool a = step<1, EXEC, 0>(d, dstop);
+            __builtin_amdgcn_sched_barrier(0);
+            const bool b = step<0, EXEC, 0>(d + 1, dstop);
+            __builtin_amdgcn_sched_barrier(0);
+            const bool c = step<1, EXEC, 1>(d + 2, dstop);
+            __builtin_amdgcn_sched_barrier(0);
+            const bool e = step<0, EXEC, 1>(d + 3, dstop);
+            if (!(a && b && c && e)) {
+                dend = d - 1 + (int)a + (int)b + (int)c + (int)e;
+                return -1;
+            }
+            d += 4;
+            if ((d & (SWITCH_EVERY - 1)) == 0) {
+                dend = d - 1;
                 flush();
-                if (want_switch()) return d + 2;
+                if (want_switch()) return d;
             }
         }
     }
@@ -580,7 +634,7 @@ struct SidePk {
         lane = fresh_lane_id();
         set_dmask();
         init_bases();
-        reload(dlast, (dlast + K) >> 1);
+        reload_entry(dlast, (dlast + K) >> 1);
     }
 };
 
