@@ -56,14 +56,12 @@ __device__ __forceinline__ uint32_t pk_max(uint32_t a, uint32_t b)
 {
     return pk_u(__builtin_elementwise_max(pk_v(a), pk_v(b)));
 }
-// 0xFFFF in each half whose value is negative, 0 elsewhere.  (An inline
-// constant of a packed instruction is a 32-bit value: op_sel_hi 0 makes
-// the high half read its low 16 bits too.)
+// 0xFFFF in each half whose value is negative, 0 elsewhere (one
+// v_pk_ashrrev_i16; the compiler keeps it as a shift since only the
+// inline-assembly bit select below reads it)
 __device__ __forceinline__ uint32_t pk_neg_mask(uint32_t x)
 {
-    uint32_t r;
-    asm("v_pk_ashrrev_i16 %0, 15, %1 op_sel_hi:[0,1]" : "=v"(r) : "v"(x));
-    return r;
+    return pk_u(pk_v(x) >> (pk_s16x2){15, 15});
 }
 // (m & a) | (~m & b)
 __device__ __forceinline__ uint32_t bit_select(uint32_t m, uint32_t a, uint32_t b)
