@@ -70,12 +70,13 @@ __device__ __forceinline__ uint32_t bit_select(uint32_t m, uint32_t a, uint32_t 
     asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(a), "v"(b));
     return r;
 }
-// per half: 1 if the (unsigned) value is 0, else 0
+typedef unsigned short pk_u16x2 __attribute__((ext_vector_type(2)));
+// per half: 1 if the (unsigned) value is 0, else 0 (saturating 1 - x: one
+// v_pk_sub_u16 with clamp)
 __device__ __forceinline__ uint32_t pk_is_zero(uint32_t x)
 {
-    uint32_t r;
-    asm("v_pk_sub_u16 %0, 1, %1 op_sel_hi:[0,1] clamp" : "=v"(r) : "v"(x));
-    return r;
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_sub_sat((pk_u16x2){1, 1},
+                                                                      __builtin_bit_cast(pk_u16x2, x)));
 }
 // per half: 1 if the (unsigned) value is not 0, else 0
 __device__ __forceinline__ uint32_t pk_nonzero(uint32_t x)
