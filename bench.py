@@ -58,11 +58,11 @@ OPS_PER_CELL = {"extend": 13, "local": 12}
 # rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) scaled by what the same
 # counters read for a plain 1 GiB device copy in the same run (FETCH_SIZE
 # reads 0.5 GiB for it, WRITE_SIZE 1.0 GiB).  Valid only for the kernel
-# sources it was taken on (hash of fz_extend.hpp + fz_device.hpp); reported
-# as null otherwise.
-TRAFFIC_SRC_HASH = "c5d4c1d4c1b1f087"
-TRAFFIC_FETCH_BYTES = 2.120e6 * 1024 / 0.5
-TRAFFIC_WRITE_BYTES = 1.704e5 * 1024 / 1.0
+# sources it was taken on (hash of fz_extend.hpp, fz_device.hpp and
+# fz_packed.hpp); reported as null otherwise.
+TRAFFIC_SRC_HASH = "6a2de3bcf1998d63"
+TRAFFIC_FETCH_BYTES = 5.449e6 * 1024 / 0.5
+TRAFFIC_WRITE_BYTES = 3.436e6 * 1024 / 1.0
 
 
 # The same for one join_count_kernel launch of the seed stage on the 20 Mbp
@@ -73,7 +73,7 @@ SEED_TRAFFIC_FETCH_BYTES = 1.910e6 * 1024 / 0.5
 SEED_TRAFFIC_WRITE_BYTES = 2.344e5 * 1024 / 1.0
 
 
-def kernel_src_hash(files=("fz_extend.hpp", "fz_device.hpp")):
+def kernel_src_hash(files=("fz_extend.hpp", "fz_device.hpp", "fz_packed.hpp")):
     """sha256 over the files' sha256 hex digests, first 16 hex digits."""
     import hashlib
     d = os.path.join(ROOT, "smith_waterman_dp_amd", "csrc")
