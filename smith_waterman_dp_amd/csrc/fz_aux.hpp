@@ -443,7 +443,7 @@ __device__ __forceinline__ int row_shift(int p, bool cpw8, bool pk)
 {
     if (!pk) return cpw8 ? 4 * (7 - (p & 7)) : 4 * (5 - p % 6);
     const int k = cpw8 ? (p & 7) : p % 6;
-    return 8 * (k >> 2) * (cpw8 ? 1 : 0) + 4 * ((cpw8 ? k & 3 : k) >> 1) + 16 * (k & 1);
+    return 16 * (k >> 2) + 8 * (k & 1) + 4 * ((k >> 1) & 1);
 }
 
 __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
@@ -495,7 +495,8 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
         const int w = row_word(p, cpw8);
         const int q = w - w0;
         if (w >= nw || q < 0 || q >= WPR) return 16u;
-        return (wl[r][q] >> row_shift(p, cpw8, pk)) & 0xFu;
+        // (packed rows hold PTR_DIAG and PTR_FROM_I inverted)
+        return ((wl[r][q] >> row_shift(p, cpw8, pk)) & 0xFu) ^ (pk ? (PTR_DIAG | PTR_FROM_I) : 0u);
     };
     while (!bad && !(st == 0 && i == 0 && j == 0)) {
         const int d = i + j;

@@ -123,10 +123,10 @@ struct ExecItem {
 // row word holds 6 or 8 consecutive positions' nibbles: 8 when off carries
 // ROW_CPW8 (the 1024-position and the packed 256-position layouts), 6
 // otherwise.  The 32-bit layouts put the first position in the highest
-// nibble.  The packed layouts (ROW_PK) put position k of a lane (two per
-// register) at bit 4 * (k >> 1) + 16 * (k & 1), and in the 256-position
-// layout the odd lane of a pair 8 bits above the even one: bit
-// 8 * (p >> 2) + 4 * ((p >> 1) & 1) + 16 * (p & 1) for cell p of the word.
+// nibble.  The packed layouts (ROW_PK) put cell k of a word (k = p % 6, or
+// p % 8 with ROW_CPW8, where the odd lane of a pair fills the upper half)
+// at bit 16 * (k >> 2) + 8 * (k & 1) + 4 * ((k >> 1) & 1), and store the
+// PTR_DIAG and PTR_FROM_I bits inverted.
 constexpr uint32_t ROW_CPW8 = 0x80000000u;
 constexpr uint32_t ROW_PK = 0x40000000u;
 constexpr uint32_t ROW_OFF_MASK = 0x3FFFFFFFu;

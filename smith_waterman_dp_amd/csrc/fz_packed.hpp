@@ -85,6 +85,11 @@ __device__ __forceinline__ uint32_t pk_nonzero(uint32_t x)
     asm("v_pk_min_u16 %0, %1, 1 op_sel_hi:[1,0]" : "=v"(r) : "v"(x));
     return r;
 }
+// per half: a - b saturated to the int16 range (keeps the sign right)
+__device__ __forceinline__ uint32_t pk_sub_sat(uint32_t a, uint32_t b)
+{
+    return pk_u(__builtin_elementwise_sub_sat(pk_v(a), pk_v(b)));
+}
 // per half: a * 2 + b (a, b small unsigned)
 __device__ __forceinline__ uint32_t pk_shl1_add(uint32_t a, uint32_t b)
 {
@@ -266,7 +271,7 @@ struct SidePk {
         uint32_t Kd[C2];
         const int mbase = MASKED ? lane * C - rlo : 0;
         const uint32_t span = (uint32_t)(rhi - rlo);
-        uint32_t nib[C2];
+        uint32_t bits[C2];
 #pragma unroll
         for (int r = 0; r < C2; ++r) {
             const uint32_t H = pk_add(SN[r], X[r]);
@@ -284,13 +289,20 @@ struct SidePk {
             const uint32_t Rn = pk_max(pk_sub(Iv[r], e2), U);
             const uint32_t Dnn = pk_max(pk_sub(Dv[r], e2), U);
             if (PTR) {
-                // bits per cell: diagonal (S == H), from I (S == I), I
-                // extends (Rn != U), D extends (Dnn != U)
-                const uint32_t b3 = pk_is_zero(pk_sub(S, H));
-                const uint32_t b2 = pk_is_zero(pk_sub(S, Iv[r]));
-                const uint32_t b1 = pk_nonzero(pk_sub(Rn, U));
-                const uint32_t b0 = pk_nonzero(pk_sub(Dnn, U));
-                nib[r] = pk_shl1_add(pk_shl1_add(pk_shl1_add(b3, b2), b1), b0);
+                // the four pointer bits of the register's two cells as
+                // sign bits (saturating differences): H - S < 0 when S did
+                // not come by the diagonal, I - S < 0 when not from I,
+                // U - (I - E) < 0 when I extends, U - (D - E) < 0 when D
+                // extends.  Two permutes gather the signs as 0x00 / 0xFF
+                // bytes (selectors 8..11 replicate the sign bits of the
+                // halves), masks place them: bytes 0, 1 hold the gap bits
+                // (bits 1, 0) of the low and high cell, bytes 2, 3 the
+                // "not diagonal", "not from I" bits (bits 3, 2).
+                const uint32_t x3 = pk_sub_sat(H, S), x2 = pk_sub_sat(Iv[r], S);
+                const uint32_t x1 = pk_sub_sat(U, pk_sub(Iv[r], e2)), x0 = pk_sub_sat(U, pk_sub(Dv[r], e2));
+                const uint32_t p31 = __builtin_amdgcn_perm(x3, x1, 0x0B0A0908u);
+                const uint32_t p20 = __builtin_amdgcn_perm(x2, x0, 0x0B0A0908u);
+                bits[r] = (p31 & 0x08080202u) | (p20 & 0x04040101u);
             }
             R[r] = Rn;
             Dn[r] = Dnn;
@@ -298,12 +310,17 @@ struct SidePk {
             dmax = r == 0 ? Sk : pk_max(dmax, Sk);     // (killed halves hold DEAD)
         }
         if (PTR) {
-            // the packed row order (RowHdr): register r's two nibbles at bits
-            // 4r and 4r + 16, one shift-or per register
-            uint32_t w = nib[0];
-#pragma unroll
-            for (int r = 1; r < C2; ++r) w |= nib[r] << (4 * r);
-            word = w;
+            // the packed row order (RowHdr): cell k of the lane at bit
+            // 16 * (k >> 2) + 8 * (k & 1) + 4 * ((k >> 1) & 1); the two bit
+            // bytes of each cell are ORed into its nibble
+            const uint32_t t = bits[0] | (bits[1] << 4);
+            const uint32_t f = t | (t >> 16);               // bytes 0, 1: cells 0 | 2, 1 | 3
+            if constexpr (C2 == 2) {
+                word = f & 0xFFFFu;
+            } else {
+                const uint32_t g = bits[2] | (bits[2] >> 16);    // bytes 0, 1: cells 4, 5
+                word = __builtin_amdgcn_perm(g, f, 0x05040100u);
+            }
         }
         // dead-byte masks: the sign byte of each half
         if constexpr (C2 == 2) {
@@ -478,10 +495,10 @@ struct SidePk {
                     hdr[d] = h;
                 }
                 if (PAIRED) {
-                    // the odd lane's nibbles 8 bits above the even lane's
+                    // the odd lane's 16 bits above the even lane's
                     const uint32_t odd = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0xB1, 0xF, 0xF, false);
                     if (!(lane & 1) && lane >= rlane0 && lane <= lhi)
-                        rows[rowoff + ((lane - rlane0) >> 1)] = word | (odd << 8);
+                        rows[rowoff + ((lane - rlane0) >> 1)] = word | (odd << 16);
                 } else if (lane >= llo && lane <= lhi) {
                     rows[rowoff + (lane - llo)] = word;
                 }
