@@ -709,7 +709,7 @@ __device__ __forceinline__ SideResult run_side_pk(const SideTask &task, const Sc
 // PK: the packed layouts (fz_packed.hpp) after the eager block; the host
 // launches it for scorings within their exact range (C = 6, SUB_LUT).
 template <int C, bool EXEC, int SUB, int WAVES, bool PK = false>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <= 8 ? (EXEC ? (SUB != SUB_WIDE ? 7 : 6) : 8) : 1))) void extend_kernel(ExtendArgs a)
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <= 8 ? (EXEC ? (PK ? 8 : SUB != SUB_WIDE ? 7 : 6) : 8) : 1))) void extend_kernel(ExtendArgs a)
 {
     using DP = SideDP<C, EXEC, SUB>;
     using EDP = SideDP<StartLayout<C>::value, EXEC, SUB>;     // holds the eager block
