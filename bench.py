@@ -106,6 +106,8 @@ def parse():
                          "or one after the other on one context")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--two-pass", action="store_true",
+                    help="every side through the inspector and the two-pass executor (FZ_TWO_PASS)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after the timed steps, one plain device-to-device copy of this many MiB "
                          "(a known-size reference for HBM traffic counters)")
@@ -445,9 +447,9 @@ def main():
             return ctx.local(T, Q, S, w["scoring"], want_stats=True, query_rc=rc)
         if rounds:
             return ctx.extend_rounds(T, Q, S, w["scoring"], w["ydrop"], min_tb, a.round_size, want_stats=True,
-                                     query_rc=rc, doubling=a.round_doubling)
+                                     query_rc=rc, doubling=a.round_doubling, two_pass=a.two_pass)
         return ctx.extend(T, Q, S, w["scoring"], w["ydrop"], min_tb, traceback=w.get("traceback", True),
-                          want_stats=True, query_rc=rc)
+                          want_stats=True, query_rc=rc, two_pass=a.two_pass)
 
     for k in range(a.warmup):
         step()
@@ -505,8 +507,11 @@ def main():
         cfg["pointer_bytes"] = int(st["pointer_bytes"])
         cfg["executor_sides"] = int(st["n_executor"])
         cfg["executor_batches"] = int(st["n_batches"])
+        cfg["onepass_sides"] = int(st["n_onepass"])
+        cfg["onepass_cells"] = int(st["onepass_cells"])
+        cfg["onepass_pool_bytes"] = int(st["onepass_bytes"])
         cfg["phase_ms"] = {k[3:]: round(float(st[k]), 1) for k in
-                           ("ms_pack", "ms_inspect", "ms_bin", "ms_exec", "ms_walk", "ms_gather")}
+                           ("ms_pack", "ms_inspect", "ms_onepass", "ms_bin", "ms_exec", "ms_walk", "ms_gather")}
         cfg["max_band"] = int(st["max_band"])
     if rounds:
         from smith_waterman_dp_amd import fz as _fz

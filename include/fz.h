@@ -117,12 +117,19 @@ typedef struct {
     uint64_t n_packed;             /* sides swept in the packed 16-bit layouts after their first 34
                                     * anti-diagonals (0 with FZ_EXACT32, FZ_LOCAL, or a scoring
                                     * outside the packed range) */
+    uint64_t n_onepass;            /* sides the one-pass executor extended and traced (see
+                                    * FZ_TWO_PASS); executor_cells and pointer_bytes do not
+                                    * count them */
+    uint64_t onepass_cells;        /* their canonical cells (all of them, best to band's end too) */
+    uint64_t onepass_bytes;        /* pool bytes their row blocks, block tables and arenas took */
     float ms_pack, ms_inspect, ms_bin, ms_exec, ms_walk, ms_gather;
                                    /* phase spans between HIP events on the call's stream;
-                                    * ms_walk is the summed duration of the traceback walker
-                                    * launches, which run inside the executor phase (ms_exec)
-                                    * on its streams, beside other batches */
+                                    * ms_inspect includes the one-pass executor; ms_walk is the
+                                    * summed duration of the traceback walker launches, which run
+                                    * inside the executor phase (ms_exec) on its streams, beside
+                                    * other batches */
     float ms_main;                 /* the dominant kernel alone (inspector, or the local kernel) */
+    float ms_onepass;              /* the one-pass executor launch (0 when none ran) */
 } fz_stats;
 
 /* Phase times of one fz_find_seeds call, milliseconds between HIP events on
@@ -149,7 +156,8 @@ enum {
     FZ_SEEDS_ALL = 1u << 4,        /* fz_find_seeds: every shared k-mer, no diagonal dedup */
     FZ_SEEDS_REUSE_INDEX = 1u << 5,/* fz_find_seeds: reuse the target index of an earlier call */
     FZ_ROUNDS_DOUBLING = 1u << 6,  /* fz_extend_rounds: each round twice the size of the one before */
-    FZ_EXACT32 = 1u << 7           /* fz_extend_batch: keep every cell in a 32-bit lane (see below) */
+    FZ_EXACT32 = 1u << 7,          /* fz_extend_batch: keep every cell in a 32-bit lane (see below) */
+    FZ_TWO_PASS = 1u << 8          /* fz_extend_batch / _rounds: no one-pass executor (see below) */
 };
 
 /* FZ_EXACT32: by default, scorings with int8 match / transition /
@@ -158,6 +166,19 @@ enum {
  * to the y-drop threshold, which hold every value that can decide a result
  * exactly); the results are identical either way.  This flag keeps the
  * 32-bit layouts, e.g. to check that. */
+
+/* FZ_TWO_PASS: by default (packed layouts, with FZ_TRACEBACK), a side whose
+ * best score at anti-diagonal 256 already makes its seed traced, whatever
+ * the other side scores (best >= min_traceback_score - seed score + 1), and
+ * whose best was found within the last 64 anti-diagonals, leaves the
+ * inspector there: a one-pass executor extends it again from the start to
+ * its end, finding its best cell and writing its pointer rows in the same
+ * pass, so that the inspector does not sweep it to its end before the
+ * executor sweeps it again to its best cell.  Its rows go to blocks of 64
+ * anti-diagonals carved from a device pool that the context keeps; sides
+ * that do not fit go back to the inspector and the two-pass executor.
+ * The results are identical either way; this flag keeps every side in the
+ * inspector / executor scheme of FastZ section 3. */
 
 /* FZ_QUERY_RC: the call aligns the target against the reverse complement
  * of `query` (base j of it is the complement of query[query_len - 1 - j];
@@ -213,10 +234,15 @@ const char *fz_last_error(const fz_ctx *ctx);
 /* Cap (bytes) of the traceback-pointer workspace, shared by the executor's
  * streams (three workspaces of a third each, each at least twice the
  * largest side's pointer rows); the executor works in batches that fit.
+ * The one-pass executor's pool (FZ_TWO_PASS) is held to the same cap
+ * (sides it cannot hold go to the two-pass executor).
  * 0 restores the default: 70% of the device memory free at the call, at
- * most 200 GiB (allocated on first need and kept by the context).  Several
- * contexts that work at once on one GPU should each be given a cap, since
- * each default is taken from the memory free when that context asks. */
+ * most 200 GiB (allocated on first need and kept by the context); the
+ * pool's default is sized from the deferred sides' windows, at most 70% of
+ * the free memory and 60% of the device, and the executor's workspaces are
+ * released when the pool must grow.  Several contexts that work at once on
+ * one GPU should each be given a cap, since each default is taken from the
+ * memory free when that context asks. */
 int fz_set_pointer_workspace(fz_ctx *ctx, uint64_t bytes);
 
 /*
@@ -366,9 +392,13 @@ int fz_find_seeds(fz_ctx *ctx,
  * FZ_DEBUG_SHRINK_ROWS: every executor side is given `value` fewer
  * pointer-row words than the inspector sized for it, so that the executor's
  * row-capacity check trips on each side that needs rows (its results then
- * carry FZ_HIT_EEXEC); 0 restores normal sizing.  Returns FZ_OK, or
- * FZ_EINVAL for an unknown `what` or a negative value. */
-enum { FZ_DEBUG_SHRINK_ROWS = 1 };
+ * carry FZ_HIT_EEXEC); 0 restores normal sizing (while it is set, no side
+ * goes to the one-pass executor).
+ * FZ_DEBUG_ONEPASS_POOL: the one-pass executor's pool is `value` bytes, so
+ * that sides run out of it and go back to the inspector; 0 turns the
+ * one-pass executor off, -1 restores the library's sizing.  Returns FZ_OK,
+ * or FZ_EINVAL for an unknown `what` or a value out of range. */
+enum { FZ_DEBUG_SHRINK_ROWS = 1, FZ_DEBUG_ONEPASS_POOL = 2 };
 int fz_debug_set(fz_ctx *ctx, int what, int64_t value);
 
 /* Copy the first n seeds of the last successful fz_find_seeds to dst

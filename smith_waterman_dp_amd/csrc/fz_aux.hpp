@@ -65,7 +65,7 @@ __global__ void setup_kernel(const fz_seed *__restrict__ seeds, int64_t n, int64
                              int64_t NT, int64_t NQ, Scoring sc, SideTask *__restrict__ tasks,
                              SeedInfo *__restrict__ info, const uint8_t *T16f = nullptr,
                              const uint8_t *T16r = nullptr, const uint8_t *Q16f = nullptr,
-                             const uint8_t *Q16r = nullptr)
+                             const uint8_t *Q16r = nullptr, bool defer_on = false, int64_t min_tb = 0)
 {
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= n) return;
@@ -75,6 +75,7 @@ __global__ void setup_kernel(const fz_seed *__restrict__ seeds, int64_t n, int64
     L.side = 0;
     R.side = 1;
     L.m = L.n = R.m = R.n = -1;
+    L.defer_need = R.defer_need = INT32_MAX;
     SeedInfo in = {0, 0};
     const int64_t Ls = s.seed_len;
     const bool ok = Ls >= 0 && s.t_lo >= 0 && s.q_lo >= 0 && s.t_hi <= tlen && s.q_hi <= qlen &&
@@ -111,11 +112,26 @@ __global__ void setup_kernel(const fz_seed *__restrict__ seeds, int64_t n, int64
             R.bbase = NQ - PAD - s.q_pos - Ls;
             R.m = (int32_t)mr;
             R.n = (int32_t)nr;
+            if (defer_on) {
+                // a seed is traced when left + seed + right > min_tb, and
+                // neither side scores below 0
+                const int64_t need = min_tb - ss + 1;
+                L.defer_need = R.defer_need = (int32_t)max<int64_t>(min<int64_t>(need, SCORE_LIMIT), -SCORE_LIMIT);
+            }
         }
     }
     tasks[2 * k] = L;
     tasks[2 * k + 1] = R;
     info[k] = in;
+}
+
+// Classes of traced sides past the eager block, in the order of the
+// executor's item list: one-pass sides (walked only), wide-window sides,
+// standard ones.
+enum : int { EXEC_CLASS_STD = 0, EXEC_CLASS_WIDE = 1, EXEC_CLASS_ONEPASS = 2, EXEC_CLASSES = 3 };
+__device__ __forceinline__ int exec_class(int32_t flags)
+{
+    return (flags & SO_ONEPASS) ? EXEC_CLASS_ONEPASS : (flags & SO_WIDE_FLAG) ? EXEC_CLASS_WIDE : EXEC_CLASS_STD;
 }
 
 __device__ __forceinline__ int bin_of(int64_t len)
@@ -143,7 +159,7 @@ struct CombineArgs {
     fz_hit *hits;
     int32_t *side_trace;        // per side: 0 none, 1 eager, 2 executor
     int64_t *run_cap;           // per side: run-word capacity (0 when not traced)
-    uint32_t *bin_count;        // [2][NBINS]
+    uint32_t *bin_count;        // [EXEC_CLASSES][NBINS]
     int64_t *max_ptr;           // max executor pointer bytes of one side
     int64_t *cells_total;       // canonical cells over the batch
     int64_t *max_band;          // widest range R_d over the batch
@@ -230,9 +246,10 @@ __global__ void combine_kernel(CombineArgs a)
                     } else {
                         tr[q] = 2;
                         const int64_t len = max(sd[q]->ie, sd[q]->je);
-                        const int cls = (sd[q]->flags & SO_WIDE_FLAG) ? 1 : 0;
+                        const int cls = exec_class(sd[q]->flags);
                         bkey[q] = cls * NBINS + bin_of(len);
-                        pmax = max(pmax, (uint64_t)sd[q]->ptr_bytes);
+                        // (one-pass sides have their rows already)
+                        if (cls != EXEC_CLASS_ONEPASS) pmax = max(pmax, (uint64_t)sd[q]->ptr_bytes);
                         longest = max(longest, len);
                     }
                 }
@@ -274,8 +291,7 @@ __global__ void bin_scatter_kernel(int64_t nsides, const int32_t *side_trace, co
     int b = 0;
     if (active) {
         o = out[s];
-        const int cls = (o.flags & SO_WIDE_FLAG) ? 1 : 0;
-        b = cls * NBINS + bin_of(max(o.ie, o.je));
+        b = exec_class(o.flags) * NBINS + bin_of(max(o.ie, o.je));
     }
     const uint32_t r = wave_grouped_inc(bin_fill, b, active);     // every lane of the wave
     if (!active) return;
@@ -284,8 +300,8 @@ __global__ void bin_scatter_kernel(int64_t nsides, const int32_t *side_trace, co
     it.side = (int32_t)s;
     it.dstar = o.ie + o.je;
     it.ptr_off = 0;
-    it.ptr_bytes = o.ptr_bytes;
-    if (shrink_words > 0) {
+    it.ptr_bytes = (o.flags & SO_ONEPASS) ? 0 : o.ptr_bytes;    // (one-pass rows are in the pool)
+    if (shrink_words > 0 && !(o.flags & SO_ONEPASS)) {
         const int64_t hdr_bytes = 8 * ((int64_t)it.dstar + 1);
         it.ptr_bytes = max(hdr_bytes + 4, it.ptr_bytes - 4 * shrink_words);
     }
@@ -379,6 +395,14 @@ __global__ void batch_assign_kernel(ExecItem *items, int64_t n, int64_t step, in
     for (int64_t q = bp + 1; q <= b; ++q) batch_first[q] = k;
 }
 
+// Sides the one-pass executor gave back (pool exhausted): the inspector
+// takes them again and keeps them.
+__global__ void undefer_kernel(const int32_t *list, int64_t n, SideTask *tasks)
+{
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k < n) tasks[list[k]].defer_need = INT32_MAX;
+}
+
 __global__ void fill_i64_kernel(int64_t *p, int64_t n, int64_t v)
 {
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -403,6 +427,7 @@ struct WalkArgs {
     int64_t begin, end;
     const uint8_t *ptr_ws;
     int64_t ptr_base_off;
+    const uint64_t *op_btab;    // one-pass sides (OP): each side's block table
     const SideOut *out;
     const int64_t *run_off;
     uint32_t *runs;
@@ -446,6 +471,9 @@ __device__ __forceinline__ int row_shift(int p, bool cpw8, bool pk)
     return 16 * (k >> 2) + 8 * (k & 1) + 4 * ((k >> 1) & 1);
 }
 
+// OP: the side's rows are the one-pass executor's blocks (fz_device.hpp,
+// OP_BLOCK), found through its block table; else one executor area.
+template <bool OP>
 __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
 {
     constexpr int WPR = WALK_CHUNK / 6 + 2;              // words staged per row (at most)
@@ -455,11 +483,12 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
     if (k >= a.end) return;
     const ExecItem it = a.items[k];
     const SideOut o = a.out[it.side];
-    const uint8_t *base = a.ptr_ws + (it.ptr_off - a.ptr_base_off);
+    const uint8_t *base = OP ? nullptr : a.ptr_ws + (it.ptr_off - a.ptr_base_off);
     const RowHdr *hdr = reinterpret_cast<const RowHdr *>(base);
-    const uint32_t *rows = reinterpret_cast<const uint32_t *>(base + 8 * ((int64_t)it.dstar + 1));
+    const uint32_t *rows = OP ? nullptr : reinterpret_cast<const uint32_t *>(base + 8 * ((int64_t)it.dstar + 1));
+    const uint64_t *btab = OP ? reinterpret_cast<const uint64_t *>(a.op_btab[it.side]) : nullptr;
     uint32_t *runs = a.runs + a.run_off[it.side];
-    const uint32_t total_rows = (uint32_t)((it.ptr_bytes - 8 * ((int64_t)it.dstar + 1)) / 4);
+    const uint32_t total_rows = OP ? OP_BLOCK_WORDS : (uint32_t)((it.ptr_bytes - 8 * ((int64_t)it.dstar + 1)) / 4);
 
     // states: 0 = S; 1 = arrived in I (continue if the cell's PTR_EXT_I
     // says the gap extends); 2 = arrived in D (PTR_EXT_D)
@@ -470,7 +499,7 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
         return;
     }
     int i = o.ie, j = o.je, st = 0;
-    bool bad = i < 0 || j < 0 || i + j > it.dstar || total_rows == 0;
+    bool bad = i < 0 || j < 0 || i + j > it.dstar || total_rows == 0 || (OP && !btab);
     int64_t n = 0, moves = 0;
     uint32_t cop = 0, clen = 0;
     const int64_t limit = (int64_t)o.ie + o.je;
@@ -504,19 +533,33 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
         int rib[2] = {0, 0}, rw0[2] = {0, 0}, rnw[2] = {0, 0};
         {
             // both rows' headers, then every word load of both rows, then
-            // the LDS stores: two memory round trips per chunk
+            // the LDS stores: two memory round trips per chunk (three with
+            // one-pass blocks: block address, headers, words)
             RowHdr h[2];
             uint32_t rend[2];
+            const uint32_t *rb[2] = {rows, rows};
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 // rows past d are not needed: they read row d's header,
                 // unconditionally (no divergent branch between the loads)
                 const int dr = min(dlo + h2 * WALK_LANES + lane, d);
-                h[h2] = hdr[dr];
-                // (clamped to the side's rows, so that no header value can
-                // send a read outside them)
-                const uint32_t next_off = hdr[min(dr + 1, it.dstar)].off & ROW_OFF_MASK;
-                rend[h2] = min(dr < it.dstar ? next_off : total_rows, total_rows);
+                if constexpr (OP) {
+                    // the block's headers hold one more slot, the block's
+                    // word count, so the next header is the row's end also
+                    // for the block's last row (and the side's)
+                    const uint8_t *blk = reinterpret_cast<const uint8_t *>(btab[dr / OP_BLOCK]);
+                    const RowHdr *bh = reinterpret_cast<const RowHdr *>(blk);
+                    const int q = dr & (OP_BLOCK - 1);
+                    h[h2] = bh[q];
+                    rend[h2] = min(bh[q + 1].off & ROW_OFF_MASK, total_rows);
+                    rb[h2] = reinterpret_cast<const uint32_t *>(blk + 8 * OP_HDRS);
+                } else {
+                    h[h2] = hdr[dr];
+                    // (clamped to the side's rows, so that no header value
+                    // can send a read outside them)
+                    const uint32_t next_off = hdr[min(dr + 1, it.dstar)].off & ROW_OFF_MASK;
+                    rend[h2] = min(dr < it.dstar ? next_off : total_rows, total_rows);
+                }
             }
             uint32_t v[2][WPR];
 #pragma unroll
@@ -540,7 +583,7 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
                     // every load in bounds (the side's first word when the
                     // row is empty), all issued before any is used
                     const int w = min(rw0[h2] + q, rnw[h2] - 1);
-                    v[h2][q] = rows[rnw[h2] > 0 ? off + (uint32_t)w : 0u];
+                    v[h2][q] = rb[h2][rnw[h2] > 0 ? off + (uint32_t)w : 0u];
                 }
             }
 #pragma unroll

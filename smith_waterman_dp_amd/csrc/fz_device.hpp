@@ -98,9 +98,20 @@ struct SideTask {
     int64_t abase, bbase;
     int32_t m, n;               // m < 0: skip (invalid seed)
     int32_t seed, side;         // side 0 = left, 1 = right
+    // The inspector hands the side to the one-pass executor when, at
+    // anti-diagonal ONEPASS_AT, its best score is at least this (its seed is
+    // then traced whatever the other side scores) and still growing;
+    // INT32_MAX: never.
+    int32_t defer_need, pad_;
 };
 
-enum : int32_t { SO_OVERFLOW = 1, SO_EAGER = 2, SO_SKIPPED = 4, SO_EXEC_MISMATCH = 8, SO_WIDE_FLAG = 16 };
+// SO_DEFERRED: the inspector stopped the side at ONEPASS_AT for the one-pass
+// executor (a transient state); SO_ONEPASS: the one-pass executor extended
+// it and wrote its complete pointer rows (walked from its block table).
+enum : int32_t {
+    SO_OVERFLOW = 1, SO_EAGER = 2, SO_SKIPPED = 4, SO_EXEC_MISMATCH = 8, SO_WIDE_FLAG = 16,
+    SO_DEFERRED = 32, SO_ONEPASS = 64
+};
 
 struct SideOut {
     int32_t score, ie, je, dend;
@@ -139,6 +150,24 @@ struct RowHdr {
 // (position, row format) words, far inside 32 bits.
 constexpr int64_t MAX_SIDE_LEN = (int64_t)1 << 28;
 
+// One-pass executor (sides whose seed is certain to be traced once they pass
+// ONEPASS_AT with a growing best): one extension that writes its pointer
+// rows as it goes, without a known end.  Its rows go to blocks of OP_BLOCK
+// anti-diagonals, each laid out like an executor area: OP_BLOCK + 1 row
+// headers (the last one holds only the block's word count, so that every
+// row's end is the next header's offset), then the rows, at most
+// OP_ROW_WORDS words each, offsets relative to the block's first row word.
+// A side's block table (one 64-bit address per block) and its blocks are
+// carved out of per-wave arenas of OP_ARENA bytes taken from one pool.
+constexpr int ONEPASS_AT = 256;             // a multiple of 8 (a flush point of the packed layouts)
+constexpr int ONEPASS_RECENT = 64;          // best found at most this many anti-diagonals before
+constexpr int OP_BLOCK = 64;                // anti-diagonals per block (a power of two, a multiple of 8)
+constexpr int OP_HDRS = OP_BLOCK + 1;
+constexpr int OP_ROW_WORDS = 64;            // widest row of the eager and packed layouts
+constexpr int64_t OP_BLOCK_BYTES = ((8 * OP_HDRS + 4 * OP_BLOCK * OP_ROW_WORDS) + 15) & ~(int64_t)15;
+constexpr int64_t OP_ARENA = (int64_t)256 << 10;
+constexpr uint32_t OP_BLOCK_WORDS = OP_BLOCK * OP_ROW_WORDS;
+
 // Entries per array of the LDS hand-over between layouts (S of two
 // diagonals and the two gap states of the union of the last two hulls,
 // which is at most 256 positions wide when a side changes layout).
@@ -150,6 +179,21 @@ constexpr int XFER_STRIDE = 256;
 // global_load instructions, which return in order.
 typedef __attribute__((address_space(1))) const uint32_t GlobalU32;
 typedef __attribute__((address_space(1))) const uint8_t GlobalU8;
+
+// Stores of pointer rows and their headers, which always lie in device
+// memory: global (not flat) stores whatever the pointer's provenance.
+__device__ __forceinline__ void gstore(uint32_t *p, uint32_t v)
+{
+    *(__attribute__((address_space(1))) uint32_t *)p = v;
+}
+__device__ __forceinline__ void gstore64(uint64_t *p, uint64_t v)
+{
+    *(__attribute__((address_space(1))) uint64_t *)p = v;
+}
+__device__ __forceinline__ void store_hdr(RowHdr *p, uint32_t off, int32_t ibase)
+{
+    gstore64(reinterpret_cast<uint64_t *>(p), (uint64_t)off | ((uint64_t)(uint32_t)ibase << 32));
+}
 
 // N dwords at any byte address in device memory, as one global load
 // (gfx9 and later serve unaligned global loads; the compiler emits a single

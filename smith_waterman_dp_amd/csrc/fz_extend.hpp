@@ -48,6 +48,19 @@ struct ExtendArgs {
     uint32_t *overflow_count;
     int64_t *exec_cells;        // executor: cells recomputed (stats)
     int32_t result_flags;       // OR'ed into every inspector result (SO_WIDE_FLAG for the wide pass)
+    // inspector: sides stopped for the one-pass executor (SO_DEFERRED)
+    int32_t *defer_list;
+    uint32_t *defer_count;
+    unsigned long long *defer_diags;    // sum of their m + n + 1 (one-pass pool sizing)
+    // one-pass executor: the pool its arenas come from, each side's block
+    // table address (by side), and the sides it could not finish for lack of
+    // pool (they go back to the inspector)
+    uint8_t *op_pool;
+    uint64_t op_pool_bytes;
+    unsigned long long *op_pool_used;
+    uint64_t *op_btab;
+    int32_t *op_fail_list;
+    uint32_t *op_fail_count;
     Scoring sc;
 };
 
@@ -343,16 +356,16 @@ struct SideDP {
                 RowHdr h;
                 h.off = rowoff | (NWORD == 2 ? ROW_CPW8 : 0u);
                 h.ibase = rlane0 * C + od;
-                hdr[d] = h;
+                store_hdr(hdr + d, h.off, h.ibase);
             }
             if (PAIRED) {
                 // the odd lane's three nibbles go under the even lane's
                 const uint32_t odd = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word[0], 0xB1, 0xF, 0xF, false);
                 if (!(lane & 1) && lane >= rlane0 && lane <= lhi)
-                    rows[rowoff + ((lane - rlane0) >> 1)] = (word[0] << 12) | odd;
+                    gstore(rows + rowoff + ((lane - rlane0) >> 1), (word[0] << 12) | odd);
             } else if (lane >= llo && lane <= lhi) {
 #pragma unroll
-                for (int k = 0; k < NWORD; ++k) rows[rowoff + (lane - llo) * NWORD + k] = word[k];
+                for (int k = 0; k < NWORD; ++k) gstore(rows + rowoff + (lane - llo) * NWORD + k, word[k]);
             }
             rowoff += (uint32_t)nl;
         } else if (PTR) {
@@ -397,9 +410,11 @@ struct SideDP {
 
     // d = 0 and diagonal 1 (the executor), or diagonals 0..33 with the eager
     // pointers of 1..32 (the inspector).  Returns the next diagonal, which is
-    // even, or -1 when the extension is over.
-    __device__ int start(int dstop, uint32_t *eager_lds, uint8_t *ptr_base, int64_t ptr_bytes)
+    // even, or -1 when the extension is over.  The executor's area holds
+    // nhdr row headers (dstop + 1 when nhdr < 0), then the rows.
+    __device__ int start(int dstop, uint32_t *eager_lds, uint8_t *ptr_base, int64_t ptr_bytes, int64_t nhdr = -1)
     {
+        if (nhdr < 0) nhdr = (int64_t)dstop + 1;
 #pragma unroll
         for (int c = 0; c < C; ++c) { SA[c] = NEG; SB[c] = NEG; R[c] = NEG; Dn[c] = NEG; }
         K = -W;
@@ -431,21 +446,21 @@ struct SideDP {
         }
         if (EXEC) {
             hdr = reinterpret_cast<RowHdr *>(ptr_base);
-            rows = reinterpret_cast<uint32_t *>(ptr_base + 8 * ((int64_t)dstop + 1));
+            rows = reinterpret_cast<uint32_t *>(ptr_base + 8 * nhdr);
             if (lane == 0) {
                 RowHdr h;
                 h.off = 0;
                 h.ibase = 0;         // lane 32 slot 0 is i = 0
-                hdr[0] = h;
+                store_hdr(hdr, h.off, h.ibase);
             }
             if (lane == P0 / C) {
 #pragma unroll
-                for (int k = 0; k < NWORD; ++k) rows[k] = 0u;   // (0,0): no gap extends through it
+                for (int k = 0; k < NWORD; ++k) gstore(rows + k, 0u);   // (0,0): no gap extends through it
             }
             rowoff = NWORD;
             // (row offsets share their word with the format flags: a side
             // with more rows than they can address ends in a mismatch)
-            rowcap = (uint32_t)min<int64_t>((ptr_bytes - 8 * ((int64_t)dstop + 1)) / 4, (int64_t)ROW_OFF_MASK);
+            rowcap = (uint32_t)min<int64_t>((ptr_bytes - 8 * nhdr) / 4, (int64_t)ROW_OFF_MASK);
             return step<0, EXEC>(1, dstop, eager_lds) ? 2 : -1;
         }
         if (lane >= EL0 && lane <= EL1) {
@@ -615,6 +630,7 @@ struct SideResult {
     int best, bi, bj, dend, band;
     int64_t cells, ptr_at_best;
     bool overflow;
+    int state = 0;              // packed layouts: SidePk's END_* reason (deferred, pool exhausted)
     template <class DP>
     __device__ __forceinline__ void take(DP &dp)
     {

@@ -49,13 +49,17 @@ struct DevBuf {
 struct Counters {
     uint32_t err;               // bit 0: non-ACGT byte; bit 1: broken traceback
     uint32_t overflow_count[2];
-    uint32_t bin_count[2 * NBINS];
-    uint32_t bin_base[2 * NBINS];
-    uint32_t bin_fill[2 * NBINS];
+    uint32_t bin_count[EXEC_CLASSES * NBINS];
+    uint32_t bin_base[EXEC_CLASSES * NBINS];
+    uint32_t bin_fill[EXEC_CLASSES * NBINS];
     int64_t max_ptr;
     int64_t exec_cells;
     int64_t totals[4];
     int64_t max_band;
+    uint32_t defer_count, op_fail_count;    // one-pass executor: sides handed over, given back
+    uint64_t defer_diags;                   // the deferred sides' anti-diagonals (m + n + 1 each)
+    uint64_t op_pool_used;
+    int64_t op_cells;
 };
 
 // One wave per workgroup for the wave-per-side kernels: sides differ in
@@ -124,6 +128,7 @@ struct fz_ctx {
     std::string err;
     uint64_t ptr_cap = 0;               // 0 = default
     int64_t dbg_shrink_rows = 0;        // fz_debug_set(FZ_DEBUG_SHRINK_ROWS)
+    int64_t dbg_op_pool = -1;           // fz_debug_set(FZ_DEBUG_ONEPASS_POOL): pool bytes (-1: sized by the library)
     std::vector<hipEvent_t> walk_ev;    // brackets of the walker launches (FZ_STATS)
     uint64_t last_words = 0;            // CIGAR words of the last successful call
     DevBuf Tf, Tr, Qf, Qr;
@@ -132,6 +137,9 @@ struct fz_ctx {
     DevBuf items, batch_first, scan_tmp, cig, cigar, counters, ovl0, ovl1, bnd;
     DevBuf rs_cnt, ps_tmp;              // radix-sort digit counts, tile totals of the generic scans
     DevBuf ptr_ws[EXEC_STREAMS];        // one pointer workspace per executor stream
+    // one-pass executor: deferred sides, sides given back, block tables (by
+    // side), the pool of row blocks
+    DevBuf defer_list, op_fail, op_btab, op_pool;
     // seed stage: target keys and positions (two of each for the sort), query
     // keys, join ranges and counts, hits (two for the sort), run flags and
     // ranks, and the seeds of the last fz_find_seeds
@@ -152,7 +160,7 @@ struct fz_ctx {
     hipStream_t xw = nullptr;           // the wide-window executor and walker, beside the batches
     hipEvent_t wide_ev = nullptr;
     hipEvent_t ev[12] = {};
-    hipEvent_t kev[2] = {};             // brackets the dominant kernel
+    hipEvent_t kev[4] = {};             // brackets the dominant kernel, then the one-pass executor
 };
 
 namespace {
@@ -356,6 +364,15 @@ int launch_extend(fz_ctx *ctx, const ExtendArgs &a, int64_t nwork, hipStream_t s
     return FZ_OK;
 }
 
+// The one-pass executor over a.list (one wave per side, like the others).
+int launch_onepass(fz_ctx *ctx, const ExtendArgs &a, int64_t nwork, hipStream_t st)
+{
+    if (nwork <= 0) return FZ_OK;
+    extend_kernel<C_STD, true, SUB_LUT, 1, true, true><<<(unsigned)nwork, 64, 0, st>>>(a);
+    HIP_OK(hipGetLastError());
+    return FZ_OK;
+}
+
 int check_args(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const uint8_t *query, uint64_t qlen,
                const fz_seed *seeds, uint64_t n, const fz_scoring *sc, const fz_matrix *mx, int32_t ydrop,
                uint32_t flags, fz_hit *hits)
@@ -377,7 +394,7 @@ int check_args(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const uint8_t 
         sc->transition < -lim || sc->transversion > lim || sc->transversion < -lim)
         return fail(ctx, FZ_EINVAL, "scoring values must lie in [-2^24, 2^24]");
     if (!(flags & FZ_LOCAL) && ydrop < 0) return fail(ctx, FZ_EINVAL, "ydrop must be >= 0");
-    if (flags & ~(uint32_t)(FZ_TRACEBACK | FZ_LOCAL | FZ_STATS | FZ_QUERY_RC | FZ_EXACT32))
+    if (flags & ~(uint32_t)(FZ_TRACEBACK | FZ_LOCAL | FZ_STATS | FZ_QUERY_RC | FZ_EXACT32 | FZ_TWO_PASS))
         return fail(ctx, FZ_EINVAL, "unknown flag bits");
     if ((flags & FZ_LOCAL) && (flags & FZ_TRACEBACK)) return fail(ctx, FZ_EINVAL, "local mode has no traceback");
     return FZ_OK;
@@ -736,7 +753,8 @@ void fz_destroy(fz_ctx *ctx)
                       &ctx->sk_off, &ctx->sk_hit, &ctx->sk_hit2, &ctx->sk_flag, &ctx->sk_rank,
                       &ctx->sk_out, &ctx->rd_keep, &ctx->rd_pos, &ctx->rd_seeds, &ctx->rd_hits, &ctx->rd_cnt,
                       &ctx->rd_off, &ctx->rd_cig, &ctx->sg_key, &ctx->sg_key2, &ctx->sg_end, &ctx->sg_end2,
-                      &ctx->sg_v, &ctx->sg_max, &ctx->rs_cnt, &ctx->ps_tmp};
+                      &ctx->sg_v, &ctx->sg_max, &ctx->rs_cnt, &ctx->ps_tmp, &ctx->defer_list, &ctx->op_fail,
+                      &ctx->op_btab, &ctx->op_pool};
     for (auto &x : ctx->xs)
         if (x) (void)hipStreamSynchronize(x);
     if (ctx->xw) (void)hipStreamSynchronize(ctx->xw);
@@ -773,8 +791,96 @@ int fz_set_pointer_workspace(fz_ctx *ctx, uint64_t bytes)
 int fz_debug_set(fz_ctx *ctx, int what, int64_t value)
 {
     if (!ctx) return FZ_EINVAL;
-    if (what != FZ_DEBUG_SHRINK_ROWS || value < 0) return fail(ctx, FZ_EINVAL, "unknown debug setting or negative value");
-    ctx->dbg_shrink_rows = value;
+    if (what == FZ_DEBUG_SHRINK_ROWS && value >= 0) {
+        ctx->dbg_shrink_rows = value;
+        return FZ_OK;
+    }
+    if (what == FZ_DEBUG_ONEPASS_POOL && value >= -1) {
+        ctx->dbg_op_pool = value;
+        return FZ_OK;
+    }
+    return fail(ctx, FZ_EINVAL, "unknown debug setting or value out of range");
+}
+
+// The one-pass executor over the inspector's deferred sides (n of them in
+// ctx->defer_list); *given_back when it could not run at all (no pool).
+// Its pool is sized from the deferred sides' windows
+// (anti-diagonals times a 256-position row with its header, plus an arena
+// and a block table each), at most 7/10 of the free device memory (this
+// context's pointer workspaces counted as free, and released when the pool
+// must grow) and 3/5 of the device.  Sides that outgrow it are given back
+// (the caller re-runs them in the inspector); with no pool at all every
+// side is given back.
+static int run_onepass(fz_ctx *ctx, const ExtendArgs &ea, int64_t n, uint64_t diags, int64_t nsides,
+                       void *counters, hipStream_t st, bool *given_back)
+{
+    *given_back = false;
+    Counters *dc = static_cast<Counters *>(counters);
+    ENSURE(ctx->op_btab, nsides * sizeof(uint64_t));
+    ENSURE(ctx->op_fail, n * sizeof(int32_t));
+    uint64_t want = 0;
+    if (ctx->dbg_op_pool > 0) {
+        want = (uint64_t)ctx->dbg_op_pool;
+    } else {
+        size_t fr = 0, tot = 0;
+        HIP_OK(hipMemGetInfo(&fr, &tot));
+        uint64_t avail = (uint64_t)fr + ctx->op_pool.cap;
+        for (const auto &b : ctx->ptr_ws) avail += b.cap;
+        const uint64_t cap = std::min<uint64_t>(avail / 10 * 7, (uint64_t)tot / 5 * 3);
+        const uint64_t need = diags * (8 + 4 * 32) + (uint64_t)n * (uint64_t)(OP_ARENA + 8192) + ((uint64_t)64 << 20);
+        want = std::min(need, cap);
+        // a pointer-memory cap set on the context bounds the pool too
+        if (ctx->ptr_cap) want = std::min<uint64_t>(want, ctx->ptr_cap);
+    }
+    if (ctx->op_pool.cap < want) {
+        size_t fr = 0, tot = 0;
+        HIP_OK(hipMemGetInfo(&fr, &tot));
+        if ((uint64_t)fr < want - ctx->op_pool.cap + ((uint64_t)1 << 30)) {
+            // the executor's workspaces come back later at their own size
+            HIP_OK(hipStreamSynchronize(st));
+            for (auto &b : ctx->ptr_ws)
+                if (b.p) {
+                    (void)hipFree(b.p);
+                    b.p = nullptr;
+                    b.cap = 0;
+                }
+        }
+        if (ctx->op_pool.p) {
+            HIP_OK(hipStreamSynchronize(st));
+            (void)hipFree(ctx->op_pool.p);
+            ctx->op_pool.p = nullptr;
+            ctx->op_pool.cap = 0;
+        }
+        // what the device gives, down to a quarter of the request
+        for (uint64_t b = want; b >= want / 4 && b >= (uint64_t)OP_ARENA; b /= 2) {
+            if (hipMalloc(&ctx->op_pool.p, b) == hipSuccess) {
+                ctx->op_pool.cap = b;
+                break;
+            }
+            (void)hipGetLastError();
+            ctx->op_pool.p = nullptr;
+        }
+    }
+    const uint64_t pool_bytes = ctx->op_pool.p ? std::min<uint64_t>(want, ctx->op_pool.cap) : 0;
+    if (pool_bytes < (uint64_t)(OP_BLOCK_BYTES + OP_ARENA)) {
+        // (the pool's sink and one arena at least)
+        *given_back = true;
+        return FZ_OK;
+    }
+    ExtendArgs oa = ea;
+    oa.list = as<int32_t>(ctx->defer_list);
+    oa.nlist = (int32_t)n;
+    oa.exec_cells = &dc->op_cells;
+    oa.op_pool = as<uint8_t>(ctx->op_pool);
+    oa.op_pool_bytes = pool_bytes;
+    oa.op_pool_used = reinterpret_cast<unsigned long long *>(&dc->op_pool_used);
+    oa.op_btab = as<uint64_t>(ctx->op_btab);
+    oa.op_fail_list = as<int32_t>(ctx->op_fail);
+    oa.op_fail_count = &dc->op_fail_count;
+    HIP_OK(hipEventRecord(ctx->kev[2], st));
+    int rc = launch_onepass(ctx, oa, n, st);
+    if (rc) return rc;
+    HIP_OK(hipEventRecord(ctx->kev[3], st));
     return FZ_OK;
 }
 
@@ -859,13 +965,18 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     ENSURE(ctx->info, n * sizeof(SeedInfo));
     ENSURE(ctx->out, nsides * sizeof(SideOut));
     ENSURE(ctx->eager, nsides * EAGER_OPS);
+    // sides certain to be traced go to the one-pass executor (packed
+    // layouts, with traceback; not under the test-only row shrink, which
+    // exercises the two-pass executor's disagreement check)
+    const bool defer_on = pk && (flags & FZ_TRACEBACK) && !(flags & FZ_TWO_PASS) && ctx->dbg_shrink_rows == 0 &&
+                          ctx->dbg_op_pool != 0;
     setup_kernel<<<blocks_for(n, 256), 256, 0, st>>>(seeds, n, (int64_t)tlen, (int64_t)qlen, as<uint8_t>(ctx->Tf),
                                                       as<uint8_t>(ctx->Tr), as<uint8_t>(ctx->Qf),
                                                       as<uint8_t>(ctx->Qr), NT, NQ, sc, as<SideTask>(ctx->tasks),
                                                       as<SeedInfo>(ctx->info), pk ? as<uint8_t>(ctx->Tf16) : nullptr,
                                                       pk ? as<uint8_t>(ctx->Tr16) : nullptr,
                                                       pk ? as<uint8_t>(ctx->Qf16) : nullptr,
-                                                      pk ? as<uint8_t>(ctx->Qr16) : nullptr);
+                                                      pk ? as<uint8_t>(ctx->Qr16) : nullptr, defer_on, min_tb);
     HIP_OK(hipGetLastError());
     tm.mark();
 
@@ -883,12 +994,44 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     ea.exec_cells = &dc->exec_cells;
     ea.result_flags = 0;
     ea.sc = sc;
+    if (defer_on) {
+        ENSURE(ctx->defer_list, nsides * sizeof(int32_t));
+        ea.defer_list = as<int32_t>(ctx->defer_list);
+        ea.defer_count = &dc->defer_count;
+        ea.defer_diags = reinterpret_cast<unsigned long long *>(&dc->defer_diags);
+    }
     HIP_OK(hipEventRecord(ctx->kev[0], st));
     rc = launch_extend<C_STD, false>(ctx, ea, nsides, st, pk);
     if (rc) return rc;
     HIP_OK(hipEventRecord(ctx->kev[1], st));
     if ((rc = read_counters())) return rc;
     if (hc.err & 1u) return fail(ctx, FZ_EINVAL, "%s", bad_byte_msg(sc));
+    bool onepass_ran = false;
+    if (hc.defer_count > 0) {
+        // ---- one-pass executor over the deferred sides
+        bool all_back = false;
+        rc = run_onepass(ctx, ea, (int64_t)hc.defer_count, hc.defer_diags, nsides, dc, st, &all_back);
+        if (rc) return rc;
+        onepass_ran = !all_back;
+        if ((rc = read_counters())) return rc;
+        const uint32_t n_back = all_back ? hc.defer_count : hc.op_fail_count;
+        S.n_onepass = (uint64_t)(hc.defer_count - n_back);
+        S.onepass_cells = (uint64_t)hc.op_cells;
+        S.onepass_bytes = hc.op_pool_used;
+        if (n_back > 0) {
+            // the pool ran out: the inspector takes those sides back and
+            // keeps them (the two-pass executor traces them)
+            int32_t *back = all_back ? as<int32_t>(ctx->defer_list) : as<int32_t>(ctx->op_fail);
+            undefer_kernel<<<blocks_for(n_back, 256), 256, 0, st>>>(back, (int64_t)n_back, as<SideTask>(ctx->tasks));
+            HIP_OK(hipGetLastError());
+            ExtendArgs ra = ea;
+            ra.list = back;
+            ra.nlist = (int32_t)n_back;
+            rc = launch_extend<C_STD, false>(ctx, ra, ra.nlist, st, pk);
+            if (rc) return rc;
+            if ((rc = read_counters())) return rc;
+        }
+    }
     S.n_overflow = hc.overflow_count[0];
     if (hc.overflow_count[0] > 0) {
         ExtendArgs wa = ea;
@@ -928,19 +1071,21 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     if (rc) return rc;
     if ((rc = read_counters())) return rc;
     const int64_t total_runs = hc.totals[0];
-    uint32_t base[2 * NBINS];
-    // executor order: wide-window sides first (they are few and slow, so
-    // they overlap everything after them), then the standard ones, each
-    // class longest bins first
-    int64_t n_exec = 0, n_wide = 0;
-    for (int cls = 1; cls >= 0; --cls)
+    uint32_t base[EXEC_CLASSES * NBINS];
+    // item order: one-pass sides (walked only), then wide-window sides (few
+    // and slow, so they overlap everything after them), then the standard
+    // ones, each class longest bins first; items [0, n_op) are one-pass,
+    // [n_op, n_wide) wide
+    int64_t n_exec = 0, n_op = 0, n_wide = 0;
+    for (int cls = EXEC_CLASSES - 1; cls >= 0; --cls)
         for (int b = NBINS - 1; b >= 0; --b) {
             base[cls * NBINS + b] = (uint32_t)n_exec;
             n_exec += hc.bin_count[cls * NBINS + b];
-            if (cls == 1) n_wide = n_exec;
+            if (cls == EXEC_CLASS_ONEPASS) n_op = n_exec;
+            if (cls == EXEC_CLASS_WIDE) n_wide = n_exec;
             S.bin_hist[b] += hc.bin_count[cls * NBINS + b];
         }
-    S.n_executor = (uint64_t)n_exec;
+    S.n_executor = (uint64_t)(n_exec - n_op);
     ENSURE(ctx->runs, std::max<int64_t>(total_runs, 1) * sizeof(uint32_t));
     if (n_exec > 0) {
         HIP_OK(hipMemcpyAsync(dc->bin_base, base, sizeof base, hipMemcpyHostToDevice, st));
@@ -1009,21 +1154,52 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         // workspace is reused only by later batches of its own stream.  When
         // no workspace is reused (one batch per stream), the wide-window
         // items (a few hundred long, low-occupancy waves) run on a stream of
-        // their own beside the batches, in their batch's workspace region
-        const bool wide_apart = nb <= nbuf && n_wide > 0;
-        if (nbuf > 1 || wide_apart) {
+        // their own beside the batches, in their batch's workspace region.
+        // The one-pass sides' walks go first on that stream.
+        const bool wide_apart = nb <= nbuf && n_wide > n_op;
+        const bool side_stream = wide_apart || n_op > 0;
+        if (nbuf > 1 || side_stream) {
             HIP_OK(hipEventRecord(ctx->fork_ev, st));
             for (int k = 1; k < nbuf; ++k) HIP_OK(hipStreamWaitEvent(ctx->xs[k - 1], ctx->fork_ev, 0));
-            if (wide_apart) HIP_OK(hipStreamWaitEvent(ctx->xw, ctx->fork_ev, 0));
+            if (side_stream) HIP_OK(hipStreamWaitEvent(ctx->xw, ctx->fork_ev, 0));
         }
+        auto walk = [&](int64_t s0, int64_t s1, hipStream_t xst, uint8_t *wsp, int64_t base_off, bool op) -> int {
+            WalkArgs wk;
+            wk.items = as<ExecItem>(ctx->items);
+            wk.begin = s0;
+            wk.end = s1;
+            wk.ptr_ws = wsp;
+            wk.ptr_base_off = base_off;
+            wk.op_btab = as<uint64_t>(ctx->op_btab);
+            wk.out = as<SideOut>(ctx->out);
+            wk.run_off = as<int64_t>(ctx->run_off);
+            wk.runs = as<uint32_t>(ctx->runs);
+            wk.run_len = as<int64_t>(ctx->run_len);
+            if (tm.on) {
+                // a pair of events around each walker launch (ms_walk)
+                while (ctx->walk_ev.size() < 2 * (n_walks + 1)) {
+                    hipEvent_t e = nullptr;
+                    HIP_OK(hipEventCreate(&e));
+                    ctx->walk_ev.push_back(e);
+                }
+                HIP_OK(hipEventRecord(ctx->walk_ev[2 * n_walks], xst));
+            }
+            if (op) walk_wave_kernel<true><<<(unsigned)(s1 - s0), 64, 0, xst>>>(wk);
+            else walk_wave_kernel<false><<<(unsigned)(s1 - s0), 64, 0, xst>>>(wk);
+            HIP_OK(hipGetLastError());
+            if (tm.on) HIP_OK(hipEventRecord(ctx->walk_ev[2 * n_walks++ + 1], xst));
+            return FZ_OK;
+        };
+        if (n_op > 0 && (rc = walk(0, n_op, ctx->xw, nullptr, 0, true))) return rc;
         for (int64_t b = 0; b < nb; ++b) {
             const int64_t lo = first[(size_t)b], hi = first[(size_t)b + 1];
             if (hi <= lo) continue;
             const int kb = (int)(b % nbuf);
             const hipStream_t bst = kb == 0 ? st : ctx->xs[kb - 1];
             uint8_t *wsp = as<uint8_t>(ctx->ptr_ws[kb]);
-            // class 1 (wide window) items come first in the list
-            const int64_t segs[2][2] = {{std::max(lo, n_wide), hi}, {lo, std::min(hi, n_wide)}};
+            // wide-window items come before the standard ones in the list
+            // (and one-pass ones, not executed, before both)
+            const int64_t segs[2][2] = {{std::max(lo, n_wide), hi}, {std::max(lo, n_op), std::min(hi, n_wide)}};
             for (int cls = 1; cls >= 0; --cls) {
                 const int64_t s0 = segs[cls][0], s1 = segs[cls][1];
                 if (s1 <= s0) continue;
@@ -1037,35 +1213,14 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
                 rc = cls == 0 ? launch_extend<C_STD, true>(ctx, xa, s1 - s0, xst, pk)
                               : launch_extend<C_WIDE, true>(ctx, xa, s1 - s0, xst);
                 if (rc) return rc;
-                WalkArgs wk;
-                wk.items = as<ExecItem>(ctx->items);
-                wk.begin = s0;
-                wk.end = s1;
-                wk.ptr_ws = wsp;
-                wk.ptr_base_off = b * step;
-                wk.out = as<SideOut>(ctx->out);
-                wk.run_off = as<int64_t>(ctx->run_off);
-                wk.runs = as<uint32_t>(ctx->runs);
-                wk.run_len = as<int64_t>(ctx->run_len);
-                if (tm.on) {
-                    // a pair of events around each walker launch (ms_walk)
-                    while (ctx->walk_ev.size() < 2 * (n_walks + 1)) {
-                        hipEvent_t e = nullptr;
-                        HIP_OK(hipEventCreate(&e));
-                        ctx->walk_ev.push_back(e);
-                    }
-                    HIP_OK(hipEventRecord(ctx->walk_ev[2 * n_walks], xst));
-                }
-                walk_wave_kernel<<<(unsigned)(s1 - s0), 64, 0, xst>>>(wk);
-                HIP_OK(hipGetLastError());
-                if (tm.on) HIP_OK(hipEventRecord(ctx->walk_ev[2 * n_walks++ + 1], xst));
+                if ((rc = walk(s0, s1, xst, wsp, b * step, false))) return rc;
             }
         }
         for (int k = 1; k < nbuf; ++k) {
             HIP_OK(hipEventRecord(ctx->join_ev[k - 1], ctx->xs[k - 1]));
             HIP_OK(hipStreamWaitEvent(st, ctx->join_ev[k - 1], 0));
         }
-        if (wide_apart) {
+        if (side_stream) {
             HIP_OK(hipEventRecord(ctx->wide_ev, ctx->xw));
             HIP_OK(hipStreamWaitEvent(st, ctx->wide_ev, 0));
         }
@@ -1107,6 +1262,7 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         S.executor_cells = (uint64_t)hc.exec_cells;
         S.max_band = (uint64_t)hc.max_band;
         S.n_packed = pk ? (uint64_t)nsides : 0;
+        if (onepass_ran) (void)hipEventElapsedTime(&S.ms_onepass, ctx->kev[2], ctx->kev[3]);
         for (size_t w = 0; w < n_walks; ++w) {
             float v = 0.f;
             (void)hipEventElapsedTime(&v, ctx->walk_ev[2 * w], ctx->walk_ev[2 * w + 1]);
@@ -1330,6 +1486,10 @@ static int rounds_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
                 tot.ms_main += rsst.ms_main;
                 tot.max_band = std::max(tot.max_band, rsst.max_band);
                 tot.n_packed += rsst.n_packed;
+                tot.n_onepass += rsst.n_onepass;
+                tot.onepass_cells += rsst.onepass_cells;
+                tot.onepass_bytes = std::max(tot.onepass_bytes, rsst.onepass_bytes);
+                tot.ms_onepass += rsst.ms_onepass;
             }
             rc = grow_keep(ctx, ctx->rd_cig, (size_t)(acc_words + (int64_t)words + 1) * sizeof(uint32_t),
                            (size_t)acc_words * sizeof(uint32_t), st);

@@ -135,7 +135,46 @@ __device__ __forceinline__ void load_unaligned_pk(const GlobalU8 *p, uint32_t (&
     }
 }
 
-template <int C2, bool EXEC>
+// One-pass executor state of the wave (one wave per workgroup): the pool,
+// the current arena's end and the side's block table.  Touched once per
+// block of OP_BLOCK anti-diagonals.
+struct OpState {
+    uint8_t *pool;              // the first OP_BLOCK_BYTES are a sink (see op_next_block)
+    uint64_t pool_bytes;
+    unsigned long long *used;   // bytes taken after the sink
+    uint64_t aend;              // end of the wave's current arena (0: none)
+    uint64_t *btab;             // the side's block table
+    int32_t out_of_pool;        // the side ran out of pool
+};
+__shared__ OpState op_state;
+
+__device__ __forceinline__ uint64_t uniform64(uint64_t x)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// `bytes` of pool memory at or after address cur (16-aligned), from the
+// wave's arena; a new arena when it does not fit, a direct pool carve for
+// requests above half an arena.  nullptr when the pool is exhausted.
+__device__ __forceinline__ uint8_t *op_alloc(uint64_t cur, uint64_t bytes)
+{
+    const uint64_t aend = uniform64(op_state.aend);
+    if (cur != 0 && cur + bytes <= aend) return reinterpret_cast<uint8_t *>(cur);
+    const uint64_t take = bytes > (uint64_t)OP_ARENA / 2 ? (bytes + 255) & ~(uint64_t)255 : (uint64_t)OP_ARENA;
+    unsigned long long *used = reinterpret_cast<unsigned long long *>(uniform64((uint64_t)(uintptr_t)op_state.used));
+    uint64_t off = 0;
+    if (fresh_lane_id() == 0) off = atomicAdd(used, (unsigned long long)take);
+    off = uniform64(off);
+    const uint64_t pool_bytes = uniform64(op_state.pool_bytes) - (uint64_t)OP_BLOCK_BYTES;
+    if (off > pool_bytes || take > pool_bytes - off) return nullptr;
+    const uint64_t base = uniform64((uint64_t)(uintptr_t)op_state.pool) + (uint64_t)OP_BLOCK_BYTES + off;
+    if (take == (uint64_t)OP_ARENA) op_state.aend = base + take;       // (every lane writes the same value)
+    return reinterpret_cast<uint8_t *>(base);
+}
+
+template <int C2, bool EXEC, bool ONEPASS = false>
 struct SidePk {
     static constexpr int C = 2 * C2;                 // positions per lane
     static constexpr int W = 64 * C;
@@ -143,6 +182,7 @@ struct SidePk {
     static constexpr int CPW = PAIRED ? 8 : C;       // cells per pointer word
     static constexpr int NWORD = 1;
     static constexpr int NONE_LO = 1 << 29, NONE_HI = -(1 << 29);
+    static constexpr bool STOPS = EXEC;  // the executors test d against dstop (INT_MAX: the one-pass one)
 
     // registers (packed pairs)
     uint32_t SA[C2], SB[C2], R[C2], Dn[C2];
@@ -161,6 +201,7 @@ struct SidePk {
     int dflush;
     int32_t acc_cells, acc_words, bmax;
     bool overflow;
+    int state;                  // END_* once the side stopped for another reason than its end
     uint32_t rowoff, rowcap;
     RowHdr *hdr;
     uint32_t *rows;
@@ -170,8 +211,56 @@ struct SidePk {
     int lane;
     uint32_t oe2, e2, lut_lo, lut_hi, dead2;    // packed constants (VGPR copies)
 
-    __device__ SidePk(const SideTask &task, const Scoring &s) : ydrop(s.ydrop), t(task), sc(s), lane(fresh_lane_id())
+    static constexpr int END_DEFER = 1;         // inspector: handed to the one-pass executor
+    static constexpr int END_POOL = 2;          // one-pass executor: pool exhausted
+
+    __device__ SidePk(const SideTask &task, const Scoring &s)
+        : ydrop(s.ydrop), state(0), t(task), sc(s), lane(fresh_lane_id())
     {
+    }
+
+    // Flush points where advance() hands control back to the caller.
+    static __device__ __forceinline__ bool at_checkpoint(int d)
+    {
+        if (ONEPASS) return (d & (OP_BLOCK - 1)) == 0;
+        return !EXEC && d == ONEPASS_AT;
+    }
+
+    // (inspector, at ONEPASS_AT) the side's seed is now certain to be traced
+    // and its best is still growing: it goes to the one-pass executor
+    // (defer_need is INT32_MAX when that is off)
+    __device__ __forceinline__ bool defer_now(int d) const
+    {
+        return best >= t.defer_need && d - (bi + bj) <= ONEPASS_RECENT;
+    }
+
+    // One-pass executor: close the block ending before diagonal d (its last
+    // header slot gets the block's word count) and open the block of d.
+    // When the pool is exhausted the side goes on to its end with its rows
+    // sent to the pool's sink (never read; no exit from the loop here,
+    // which would cost the sweep's registers) and is marked out of pool.
+    __device__ __forceinline__ void op_next_block(int d)
+    {
+        if (lane == 0) {
+            RowHdr h;
+            h.off = rowoff;
+            h.ibase = 0;
+            store_hdr(hdr + d, h.off, h.ibase);
+        }
+        const uint64_t cur = ((uint64_t)(uintptr_t)(rows + rowoff) + 15) & ~(uint64_t)15;
+        // (once out of pool, the rows stay in the sink: cur lies there)
+        uint8_t *blk = uniform(op_state.out_of_pool) ? nullptr : op_alloc(cur, (uint64_t)OP_BLOCK_BYTES);
+        if (!blk) {
+            blk = reinterpret_cast<uint8_t *>(uniform64((uint64_t)(uintptr_t)op_state.pool));
+            op_state.out_of_pool = 1;
+        }
+        blk = reinterpret_cast<uint8_t *>(uniform64((uint64_t)(uintptr_t)blk));
+        uint64_t *btab = reinterpret_cast<uint64_t *>(uniform64((uint64_t)(uintptr_t)op_state.btab));
+        if (lane == 0) gstore64(btab + d / OP_BLOCK, (uint64_t)(uintptr_t)blk);
+        hdr = reinterpret_cast<RowHdr *>(blk) - d;
+        rows = reinterpret_cast<uint32_t *>(blk + 8 * OP_HDRS);
+        rowoff = 0;
+        rowcap = OP_BLOCK_WORDS;
     }
 
     // lane-held values of this layout's run, formed when the run starts (not
@@ -392,10 +481,10 @@ struct SidePk {
         int rlo = min(lo1 - DELTA, lo2);
         int rhi = max(hi1 - DELTA + 1, hi2);
         bool masked = false, live = true;
-        if (((dmask - 1 - d) | rlo | (W - 1 - rhi) | (rhi - rlo) | (EXEC ? dstop - d : 0)) < 0) {
+        if (((dmask - 1 - d) | rlo | (W - 1 - rhi) | (rhi - rlo) | (STOPS ? dstop - d : 0)) < 0) {
             const int vlo = max(0, d - t.n) - od, vhi = min(t.m, d) - od;
             rlo = max(rlo, vlo);
-            rhi = min(rhi, EXEC && d > dstop ? rlo - 1 : vhi);
+            rhi = min(rhi, STOPS && d > dstop ? rlo - 1 : vhi);
             if (rlo <= rhi && (rlo < 0 || rhi > W - 1)) {
                 const int smin = floordiv(rhi - (W - 1) + C - 1, C), smax = floordiv(rlo, C);
                 if (smin > smax) {
@@ -492,15 +581,15 @@ struct SidePk {
                     RowHdr h;
                     h.off = rowoff | (CPW == 8 ? ROW_CPW8 : 0u) | ROW_PK;
                     h.ibase = rlane0 * C + od;
-                    hdr[d] = h;
+                    store_hdr(hdr + d, h.off, h.ibase);
                 }
                 if (PAIRED) {
                     // the odd lane's 16 bits above the even lane's
                     const uint32_t odd = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)word, 0xB1, 0xF, 0xF, false);
                     if (!(lane & 1) && lane >= rlane0 && lane <= lhi)
-                        rows[rowoff + ((lane - rlane0) >> 1)] = word | (odd << 16);
+                        gstore(rows + rowoff + ((lane - rlane0) >> 1), word | (odd << 16));
                 } else if (lane >= llo && lane <= lhi) {
-                    rows[rowoff + (lane - llo)] = word;
+                    gstore(rows + rowoff + (lane - llo), word);
                 }
                 rowoff += (uint32_t)nl;
             }
@@ -578,6 +667,10 @@ struct SidePk {
             if ((d & (SWITCH_EVERY - 1)) == 0) {
                 dend = d - 1;
                 flush();
+                // the caller's checkpoints (out of this loop, whose
+                // registers they would crowd): the inspector's hand-over
+                // test, the one-pass executor's block ends
+                if (at_checkpoint(d)) return d;
                 if (want_switch()) return d;
             }
         }
@@ -646,6 +739,7 @@ struct SidePk {
         dflush = o.dflush; acc_cells = 0; acc_words = 0;
         bmax = o.bmax;
         overflow = o.overflow;
+        state = 0;
         rowoff = o.rowoff; rowcap = o.rowcap; hdr = o.hdr; rows = o.rows;
         lane = fresh_lane_id();
         set_dmask();
@@ -660,14 +754,53 @@ struct SidePk {
 // wider than 232 positions and back when it narrows to 216.  The executor
 // makes the same moves at the same diagonals, so its pointer rows match the
 // inspector's sizing.
-template <bool EXEC>
+//
+// ONEPASS (with EXEC): the one-pass executor.  No end is known (dstop is
+// INT_MAX), and the rows go to blocks of OP_BLOCK anti-diagonals taken from
+// the pool as the side grows; the block table's address is left in
+// op_state.btab.  The side's last row is followed by a header holding the
+// block's word count, as at every block's end.
+template <bool EXEC, bool ONEPASS = false>
 __device__ __forceinline__ SideResult run_side_pk(const SideTask &task, const Scoring &sc, int dstop,
                                                   uint32_t *eager_lds, uint32_t *xfer, uint8_t *ptr_base,
                                                   int64_t ptr_bytes)
 {
     SideResult r;
+    int64_t nhdr = -1;
+    if constexpr (ONEPASS) {
+        // the block table (a block for every flush point the side can
+        // reach, up to anti-diagonal m + n + 1), then block 0
+        const uint64_t nblk = (uint64_t)(((int64_t)task.m + task.n + 1) / OP_BLOCK + 1);
+        uint8_t *bt = op_alloc(0, 8 * nblk);
+        uint8_t *b0 = bt ? op_alloc(((uint64_t)(uintptr_t)bt + 8 * nblk + 15) & ~(uint64_t)15, (uint64_t)OP_BLOCK_BYTES)
+                         : nullptr;
+        if (!b0) {
+            r.best = r.bi = r.bj = r.dend = r.band = 0;
+            r.cells = r.ptr_at_best = 0;
+            r.overflow = false;
+            r.state = SidePk<2, EXEC, ONEPASS>::END_POOL;
+            return r;
+        }
+        op_state.btab = reinterpret_cast<uint64_t *>(bt);      // (every lane writes the same value)
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        if (fresh_lane_id() == 0) gstore64(reinterpret_cast<uint64_t *>(bt), (uint64_t)(uintptr_t)b0);
+        ptr_base = reinterpret_cast<uint8_t *>(uniform64((uint64_t)(uintptr_t)b0));
+        ptr_bytes = 8 * OP_HDRS + 4 * (int64_t)OP_BLOCK_WORDS;
+        nhdr = OP_HDRS;
+    }
+    // the header after the side's last row: its row's end
+    auto close_rows = [&](auto &x) {
+        if constexpr (ONEPASS) {
+            if (!x.overflow && fresh_lane_id() == 0) {
+                RowHdr h;
+                h.off = x.rowoff;
+                h.ibase = 0;
+                store_hdr(x.hdr + (x.dend + 1), h.off, h.ibase);
+            }
+        }
+    };
     SideDP<3, EXEC, SUB_LUT> dn(task, sc);
-    int d = dn.start(dstop, eager_lds, ptr_base, ptr_bytes);
+    int d = dn.start(dstop, eager_lds, ptr_base, ptr_bytes, nhdr);
     // (the inspector's start runs to diagonal 33, the executor's to 1)
     while (d >= 0 && d < EAGER_ROWS + 1) {
         if (!dn.template step<1, EXEC>(d, dstop, eager_lds) || !dn.template step<0, EXEC>(d + 1, dstop, eager_lds)) {
@@ -678,23 +811,50 @@ __device__ __forceinline__ SideResult run_side_pk(const SideTask &task, const Sc
     }
     if (d < 0) {
         r.take(dn);
+        close_rows(dn);
         return r;
     }
-    SidePk<2, EXEC> p4(task, sc);
-    SidePk<3, EXEC> p6(task, sc);
+    SidePk<2, EXEC, ONEPASS> p4(task, sc);
+    SidePk<3, EXEC, ONEPASS> p6(task, sc);
     switch_layout(p4, dn, xfer, d);
+    constexpr bool CHECKPOINTS = ONEPASS || !EXEC;
+    // at a checkpoint: false to end the side (its state says why); else
+    // *stay when the layout does not change there
+    auto checkpoint = [&](auto &p, int dd, bool &stay) -> bool {
+        stay = false;
+        if (!p.at_checkpoint(dd)) return true;
+        if constexpr (!EXEC) {
+            if (p.defer_now(dd)) {
+                p.state = p.END_DEFER;
+                return false;
+            }
+        }
+        if constexpr (ONEPASS) p.op_next_block(dd);
+        stay = !p.want_switch();
+        return true;
+    };
+    auto finish = [&](auto &p) {
+        r.take(p);
+        r.state = p.state;
+        if (!p.state) close_rows(p);
+    };
     for (;;) {
-        d = p4.advance(d, dstop);
-        if (d < 0) {
-            r.take(p4);
-            return r;
-        }
+        bool stay = false;
+        do {
+            d = p4.advance(d, dstop);
+            if (d < 0 || (CHECKPOINTS && !checkpoint(p4, d, stay))) {
+                finish(p4);
+                return r;
+            }
+        } while (CHECKPOINTS && stay);
         switch_layout(p6, p4, xfer, d);
-        d = p6.advance(d, dstop);
-        if (d < 0) {
-            r.take(p6);
-            return r;
-        }
+        do {
+            d = p6.advance(d, dstop);
+            if (d < 0 || (CHECKPOINTS && !checkpoint(p6, d, stay))) {
+                finish(p6);
+                return r;
+            }
+        } while (CHECKPOINTS && stay);
         switch_layout(p4, p6, xfer, d);
     }
 }
@@ -702,15 +862,21 @@ __device__ __forceinline__ SideResult run_side_pk(const SideTask &task, const Sc
 // One wave per side; the grid covers the work list (the hardware dispatcher
 // hands waves to CUs as others retire, which balances sides of very
 // different lengths).  Register budgets of the standard kernels: the
-// inspector fits 64 VGPRs (8 waves per SIMD), the executor 72 (7 waves)
-// with byte substitution scores and 80 (6) without; more waves let a SIMD
-// pair one wave's VALU instruction with another's SALU instruction.
+// inspector and the packed executor fit 64 VGPRs (8 waves per SIMD), the
+// one-pass executor (which keeps the inspector's results and the
+// executor's rows) 72 (7 waves), the 32-bit executor 72 with byte
+// substitution scores and 80 (6) without; more waves let a SIMD pair one
+// wave's VALU instruction with another's SALU instruction.
 //
 // PK: the packed layouts (fz_packed.hpp) after the eager block; the host
 // launches it for scorings within their exact range (C = 6, SUB_LUT).
-template <int C, bool EXEC, int SUB, int WAVES, bool PK = false>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <= 8 ? (EXEC ? (PK ? 8 : SUB != SUB_WIDE ? 7 : 6) : 8) : 1))) void extend_kernel(ExtendArgs a)
+// ONEPASS (with EXEC and PK): the one-pass executor over a.list, the sides
+// the inspector deferred; it reports like the inspector and writes the rows
+// to the pool.
+template <int C, bool EXEC, int SUB, int WAVES, bool PK = false, bool ONEPASS = false>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <= 8 ? (EXEC ? (PK ? (ONEPASS ? 7 : 8) : SUB != SUB_WIDE ? 7 : 6) : 8) : 1))) void extend_kernel(ExtendArgs a)
 {
+    static_assert(!ONEPASS || (EXEC && PK && WAVES == 1), "the one-pass executor runs the packed layouts, one wave per group");
     using DP = SideDP<C, EXEC, SUB>;
     using EDP = SideDP<StartLayout<C>::value, EXEC, SUB>;     // holds the eager block
     __shared__ uint32_t eager_lds_all[WAVES][EAGER_ROWS * EDP::NEL * EDP::NWORD];
@@ -720,8 +886,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <=
     uint32_t *xfer = xfer_all[wv];
     const int idx = (int)blockIdx.x * WAVES + wv;
     if (idx >= a.nlist) return;
-    const int64_t item = EXEC ? a.exec_begin + idx : (int64_t)idx;
-    const int sid = EXEC ? a.exec[item].side : (a.list ? a.list[item] : (int)item);
+    constexpr bool TWO_PASS_EXEC = EXEC && !ONEPASS;
+    const int64_t item = TWO_PASS_EXEC ? a.exec_begin + idx : (int64_t)idx;
+    const int sid = TWO_PASS_EXEC ? a.exec[item].side : (a.list ? a.list[item] : (int)item);
     const SideTask task = a.tasks[sid];
     SideOut *o = &a.out[sid];
     if (task.m < 0) {
@@ -729,6 +896,44 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <=
             SideOut r = {};
             r.flags = SO_SKIPPED;
             *o = r;
+        }
+        return;
+    }
+    if constexpr (ONEPASS) {
+        op_state.pool = a.op_pool;              // (every lane writes the same values)
+        op_state.pool_bytes = a.op_pool_bytes;
+        op_state.used = a.op_pool_used;
+        op_state.aend = 0;
+        op_state.btab = nullptr;
+        op_state.out_of_pool = 0;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        const SideResult x = run_side_pk<true, true>(task, a.sc, 0x7fffffff, nullptr, xfer, nullptr, 0);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        const bool pool_out = x.state != 0 || uniform(op_state.out_of_pool) != 0;
+        SideOut r;
+        r.score = x.best;
+        r.ie = x.bi;
+        r.je = x.bj;
+        r.dend = x.dend;
+        r.cells = x.cells;
+        r.ptr_bytes = 0;        // (its rows are in the pool; a side given back is inspected again)
+        r.flags = x.overflow ? SO_OVERFLOW : (pool_out ? SO_DEFERRED : SO_ONEPASS);
+        r.eager_len = 0;
+        r.max_band = x.band;
+        r.pad_ = 0;
+        const uint64_t btab = uniform64((uint64_t)(uintptr_t)op_state.btab);
+        if (fresh_lane_id() == 0) {
+            *o = r;
+            a.op_btab[sid] = btab;
+            if (x.overflow) {
+                const uint32_t k = atomicAdd(a.overflow_count, 1u);
+                a.overflow_list[k] = sid;
+            } else if (pool_out) {
+                const uint32_t k = atomicAdd(a.op_fail_count, 1u);
+                a.op_fail_list[k] = sid;
+            } else {
+                atomicAdd((unsigned long long *)a.exec_cells, (unsigned long long)x.cells);
+            }
         }
         return;
     }
@@ -760,7 +965,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <=
     r.eager_len = 0;
     r.max_band = x.band;
     r.pad_ = 0;
-    if (!x.overflow && x.bi <= EAGER_EDGE && x.bj <= EAGER_EDGE) {
+    const bool deferred = x.state == SidePk<2, false>::END_DEFER;
+    if (deferred) r.flags = SO_DEFERRED;
+    if (!x.overflow && !deferred && x.bi <= EAGER_EDGE && x.bj <= EAGER_EDGE) {
         // the best cell lies in the eager block, which the start layout
         // kept (no layout change happens before diagonal 34)
         EDP e(task, a.sc);
@@ -771,7 +978,11 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <=
     }
     if (fresh_lane_id() == 0) {
         *o = r;
-        if (x.overflow) {
+        if (deferred) {
+            const uint32_t k = atomicAdd(a.defer_count, 1u);
+            a.defer_list[k] = sid;
+            atomicAdd(a.defer_diags, (unsigned long long)((int64_t)task.m + task.n + 1));
+        } else if (x.overflow) {
             const uint32_t k = atomicAdd(a.overflow_count, 1u);
             a.overflow_list[k] = sid;
         }

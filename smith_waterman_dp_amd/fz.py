@@ -12,12 +12,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfz.so")
 
 FZ_TRACEBACK, FZ_LOCAL, FZ_STATS, FZ_QUERY_RC, FZ_SEEDS_ALL, FZ_SEEDS_REUSE_INDEX = 1, 2, 4, 8, 16, 32
-FZ_ROUNDS_DOUBLING, FZ_EXACT32 = 64, 128
+FZ_ROUNDS_DOUBLING, FZ_EXACT32, FZ_TWO_PASS = 64, 128, 256
 FZ_OK, FZ_EINVAL, FZ_ENOMEM, FZ_EDEVICE = 0, -1, -2, -3
 FZ_HIT_TRACED, FZ_HIT_EAGER_LEFT, FZ_HIT_EAGER_RIGHT = 1, 2, 4
 FZ_HIT_BELOW_MIN, FZ_HIT_EBAND, FZ_HIT_ESEED, FZ_HIT_ERANGE = 8, 16, 32, 64
 FZ_HIT_COVERED, FZ_HIT_EEXEC, FZ_HIT_WIDE = 128, 256, 512
-FZ_DEBUG_SHRINK_ROWS = 1
+FZ_DEBUG_SHRINK_ROWS, FZ_DEBUG_ONEPASS_POOL = 1, 2
 FZ_YDROP_INF = 2147483647
 FZ_NOALLOC_MAX_SEEDS, FZ_NOALLOC_MAX_BASES = 65536, 4194304
 
@@ -59,10 +59,11 @@ class fz_stats(ctypes.Structure):
                 ("pointer_bytes", ctypes.c_uint64), ("n_sides", ctypes.c_uint64), ("n_eager", ctypes.c_uint64),
                 ("n_executor", ctypes.c_uint64), ("n_overflow", ctypes.c_uint64),
                 ("bin_hist", ctypes.c_uint64 * 8), ("n_batches", ctypes.c_uint64), ("max_band", ctypes.c_uint64),
-                ("n_packed", ctypes.c_uint64),
+                ("n_packed", ctypes.c_uint64), ("n_onepass", ctypes.c_uint64), ("onepass_cells", ctypes.c_uint64),
+                ("onepass_bytes", ctypes.c_uint64),
                 ("ms_pack", ctypes.c_float), ("ms_inspect", ctypes.c_float), ("ms_bin", ctypes.c_float),
                 ("ms_exec", ctypes.c_float), ("ms_walk", ctypes.c_float), ("ms_gather", ctypes.c_float),
-                ("ms_main", ctypes.c_float)]
+                ("ms_main", ctypes.c_float), ("ms_onepass", ctypes.c_float)]
 
     def as_dict(self):
         d = {f: getattr(self, f) for f, _ in self._fields_}
@@ -300,23 +301,24 @@ class Context:
             pass
 
     def extend(self, target, query, seeds, scoring, ydrop, min_traceback_score=-(1 << 62), traceback=True,
-               stream=None, want_stats=False, query_rc=False, exact32=False):
+               stream=None, want_stats=False, query_rc=False, exact32=False, two_pass=False):
         """query_rc: seeds lie on the query's reverse complement (FZ_QUERY_RC).
         exact32: keep every cell in a 32-bit lane (FZ_EXACT32); the results
-        are the same as with the packed 16-bit layouts."""
+        are the same as with the packed 16-bit layouts.  two_pass: no
+        one-pass executor (FZ_TWO_PASS); the results are the same."""
         flags = ((FZ_TRACEBACK if traceback else 0) | (FZ_QUERY_RC if query_rc else 0)
-                 | (FZ_EXACT32 if exact32 else 0))
+                 | (FZ_EXACT32 if exact32 else 0) | (FZ_TWO_PASS if two_pass else 0))
         return fz_extend_batch(self.h, target, query, seeds, scoring, ydrop, min_traceback_score, flags,
                                stream, want_stats)
 
     def extend_rounds(self, target, query, seeds, scoring, ydrop, min_traceback_score, round_size, stream=None,
-                      want_stats=False, query_rc=False, doubling=False, exact32=False):
+                      want_stats=False, query_rc=False, doubling=False, exact32=False, two_pass=False):
         """Covered-seed suppression (fz_extend_rounds): rounds of round_size
         seeds (doubling: the first round's size, each later round twice the
         one before); a seed on an alignment traced in an earlier round is not
         extended (status FZ_HIT_COVERED)."""
         flags = (FZ_TRACEBACK | (FZ_QUERY_RC if query_rc else 0) | (FZ_ROUNDS_DOUBLING if doubling else 0)
-                 | (FZ_EXACT32 if exact32 else 0))
+                 | (FZ_EXACT32 if exact32 else 0) | (FZ_TWO_PASS if two_pass else 0))
         return fz_extend_batch(self.h, target, query, seeds, scoring, ydrop, min_traceback_score, flags,
                                stream, want_stats, round_size=round_size)
 

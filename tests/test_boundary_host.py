@@ -3,6 +3,7 @@ symbol include/fz.h declares, and rejects bad calls without touching a GPU."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -34,8 +35,22 @@ def test_struct_sizes_match_header():
     assert ctypes.sizeof(fz.fz_scoring) == 20
     assert ctypes.sizeof(fz.fz_matrix) == 17 * 4           # sub[4][4] and n_score
     assert ctypes.sizeof(fz.fz_seed_stats) == 11 * 4       # eleven float phase times
-    # fz_stats: 17 uint64 counters (bin_hist holds 8), seven float times, padding to 8 bytes
-    assert ctypes.sizeof(fz.fz_stats) == 18 * 8 + 7 * 4 + 4
+    # fz_stats: 21 uint64 counters (bin_hist holds 8), eight float times
+    assert ctypes.sizeof(fz.fz_stats) == 21 * 8 + 8 * 4
+
+
+def test_struct_sizes_match_c_compiler(tmp_path):
+    # the binding's structs against the header as a C compiler lays it out
+    src = tmp_path / "sizes.c"
+    src.write_text('#include <stdio.h>\n#include "fz.h"\n'
+                   'int main(void) { printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(fz_seed), sizeof(fz_hit), '
+                   'sizeof(fz_scoring), sizeof(fz_matrix), sizeof(fz_stats), sizeof(fz_seed_stats)); return 0; }\n')
+    exe = tmp_path / "sizes"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run(["gcc", "-std=c99", "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert got == [7 * 8, 12 * 8, ctypes.sizeof(fz.fz_scoring), ctypes.sizeof(fz.fz_matrix),
+                   ctypes.sizeof(fz.fz_stats), ctypes.sizeof(fz.fz_seed_stats)]
 
 
 def test_null_context_is_rejected():

@@ -45,12 +45,15 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
 
 
-def run(ctx, w, exact32, ydrop=None, scoring=None, traceback=True):
+def run(ctx, w, exact32, ydrop=None, scoring=None, traceback=True, two_pass=True):
+    """(two-pass by default: these cases compare the packed executor's rows
+    and counts with the 32-bit one's)"""
     yd = w["ydrop"] if ydrop is None else ydrop
     sc = scoring or w["scoring"]
-    log("call extend exact32=%d: %d seeds, ydrop %d, scoring %s" % (exact32, len(w["seeds"]), yd, sc))
+    log("call extend exact32=%d two_pass=%d: %d seeds, ydrop %d, scoring %s" % (exact32, two_pass, len(w["seeds"]),
+                                                                             yd, sc))
     hits, cig, st = ctx.extend(dev(w["target"]), dev(w["query"]), dev(w["seeds"]), sc, yd, traceback=traceback,
-                               want_stats=True, exact32=exact32)
+                               want_stats=True, exact32=exact32, two_pass=two_pass)
     torch.cuda.synchronize()
     log("call done")
     return hits.cpu().numpy(), cig.cpu().numpy().view(np.uint32), st

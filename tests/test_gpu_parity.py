@@ -55,7 +55,8 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
 
 
-def run_gpu(ctx, w, seeds=None, local=False, ydrop=None, min_tb=None, traceback=True, scoring=None):
+def run_gpu(ctx, w, seeds=None, local=False, ydrop=None, min_tb=None, traceback=True, scoring=None,
+            two_pass=False):
     seeds = w["seeds"] if seeds is None else seeds
     sc = scoring or w["scoring"]
     T, Q, S = dev(w["target"]), dev(w["query"]), dev(seeds)
@@ -67,7 +68,8 @@ def run_gpu(ctx, w, seeds=None, local=False, ydrop=None, min_tb=None, traceback=
     else:
         yd = w["ydrop"] if ydrop is None else ydrop
         mt = -(1 << 62) if min_tb is None else min_tb
-        hits, cig, st = ctx.extend(T, Q, S, sc, yd, mt, traceback=traceback, want_stats=True, query_rc=rc)
+        hits, cig, st = ctx.extend(T, Q, S, sc, yd, mt, traceback=traceback, want_stats=True, query_rc=rc,
+                                   two_pass=two_pass)
     torch.cuda.synchronize()
     log("call done")
     return hits.cpu().numpy(), cig.cpu().numpy().view(np.uint32), st
