@@ -159,6 +159,7 @@ struct fz_ctx {
     hipEvent_t fork_ev = nullptr, join_ev[EXEC_STREAMS - 1] = {};
     hipStream_t xw = nullptr;           // the wide-window executor and walker, beside the batches
     hipEvent_t wide_ev = nullptr;
+    hipEvent_t op_ev = nullptr;         // the one-pass sides' walks joined
     hipEvent_t ev[12] = {};
     hipEvent_t kev[4] = {};             // brackets the dominant kernel, then the one-pass executor
 };
@@ -724,6 +725,7 @@ int fz_create(fz_ctx **out, int device, uint64_t workspace_bytes)
     bool ok = hipEventCreateWithFlags(&ctx->fork_ev, hipEventDisableTiming) == hipSuccess;
     for (auto &e : ctx->join_ev) ok = ok && hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
     ok = ok && hipEventCreateWithFlags(&ctx->wide_ev, hipEventDisableTiming) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&ctx->op_ev, hipEventDisableTiming) == hipSuccess;
     // default priority, no implicit ordering with the null stream
     for (auto &x : ctx->xs) ok = ok && hipStreamCreateWithFlags(&x, hipStreamNonBlocking) == hipSuccess;
     ok = ok && hipStreamCreateWithFlags(&ctx->xw, hipStreamNonBlocking) == hipSuccess;
@@ -766,6 +768,7 @@ void fz_destroy(fz_ctx *ctx)
         if (x) (void)hipStreamDestroy(x);
     if (ctx->xw) (void)hipStreamDestroy(ctx->xw);
     if (ctx->wide_ev) (void)hipEventDestroy(ctx->wide_ev);
+    if (ctx->op_ev) (void)hipEventDestroy(ctx->op_ev);
     if (ctx->fork_ev) (void)hipEventDestroy(ctx->fork_ev);
     for (auto &e : ctx->join_ev)
         if (e) (void)hipEventDestroy(e);
@@ -1006,6 +1009,26 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     HIP_OK(hipEventRecord(ctx->kev[1], st));
     if ((rc = read_counters())) return rc;
     if (hc.err & 1u) return fail(ctx, FZ_EINVAL, "%s", bad_byte_msg(sc));
+    // wide retry (the 1024-position window, a few long latency-bound waves)
+    // of the overflow list [first, first + count)
+    auto wide_retry = [&](uint32_t first, uint32_t count, hipStream_t ws) -> int {
+        ExtendArgs wa = ea;
+        wa.list = as<int32_t>(ctx->ovl0) + first;
+        wa.nlist = (int32_t)count;
+        wa.overflow_list = as<int32_t>(ctx->ovl1);
+        wa.overflow_count = &dc->overflow_count[1];
+        wa.result_flags = SO_WIDE_FLAG;
+        return launch_extend<C_WIDE, false>(ctx, wa, wa.nlist, ws);
+    };
+    // the inspector's overflow sides go to the wide retry beside the
+    // one-pass executor; those of the one-pass executor (and of sides it
+    // gives back) after it
+    const uint32_t n_ovl_first = hc.defer_count > 0 ? hc.overflow_count[0] : 0;
+    if (n_ovl_first > 0) {
+        HIP_OK(hipEventRecord(ctx->fork_ev, st));
+        HIP_OK(hipStreamWaitEvent(ctx->xw, ctx->fork_ev, 0));
+        if ((rc = wide_retry(0, n_ovl_first, ctx->xw))) return rc;
+    }
     bool onepass_ran = false;
     if (hc.defer_count > 0) {
         // ---- one-pass executor over the deferred sides
@@ -1033,15 +1056,11 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         }
     }
     S.n_overflow = hc.overflow_count[0];
-    if (hc.overflow_count[0] > 0) {
-        ExtendArgs wa = ea;
-        wa.list = as<int32_t>(ctx->ovl0);
-        wa.nlist = (int32_t)hc.overflow_count[0];
-        wa.overflow_list = as<int32_t>(ctx->ovl1);
-        wa.overflow_count = &dc->overflow_count[1];
-        wa.result_flags = SO_WIDE_FLAG;
-        rc = launch_extend<C_WIDE, false>(ctx, wa, wa.nlist, st);
-        if (rc) return rc;
+    if (hc.overflow_count[0] > n_ovl_first && (rc = wide_retry(n_ovl_first, hc.overflow_count[0] - n_ovl_first, st)))
+        return rc;
+    if (n_ovl_first > 0) {
+        HIP_OK(hipEventRecord(ctx->wide_ev, ctx->xw));
+        HIP_OK(hipStreamWaitEvent(st, ctx->wide_ev, 0));
     }
     tm.mark();
 
@@ -1155,13 +1174,18 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         // no workspace is reused (one batch per stream), the wide-window
         // items (a few hundred long, low-occupancy waves) run on a stream of
         // their own beside the batches, in their batch's workspace region.
-        // The one-pass sides' walks go first on that stream.
         const bool wide_apart = nb <= nbuf && n_wide > n_op;
-        const bool side_stream = wide_apart || n_op > 0;
-        if (nbuf > 1 || side_stream) {
+        // the one-pass sides' walks: on an executor stream that no batch
+        // uses, else beside the wide-window items (streams share the
+        // device's few hardware queues, so no stream is added for them)
+        const bool op_own = nbuf < EXEC_STREAMS;         // an executor stream without a batch
+        const hipStream_t xop = op_own ? ctx->xs[std::max(nbuf, 1) - 1] : ctx->xw;
+        const bool use_xw = wide_apart || (n_op > 0 && !op_own);
+        if (nbuf > 1 || use_xw || n_op > 0) {
             HIP_OK(hipEventRecord(ctx->fork_ev, st));
             for (int k = 1; k < nbuf; ++k) HIP_OK(hipStreamWaitEvent(ctx->xs[k - 1], ctx->fork_ev, 0));
-            if (side_stream) HIP_OK(hipStreamWaitEvent(ctx->xw, ctx->fork_ev, 0));
+            if (use_xw) HIP_OK(hipStreamWaitEvent(ctx->xw, ctx->fork_ev, 0));
+            if (n_op > 0 && op_own) HIP_OK(hipStreamWaitEvent(xop, ctx->fork_ev, 0));
         }
         auto walk = [&](int64_t s0, int64_t s1, hipStream_t xst, uint8_t *wsp, int64_t base_off, bool op) -> int {
             WalkArgs wk;
@@ -1190,7 +1214,7 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
             if (tm.on) HIP_OK(hipEventRecord(ctx->walk_ev[2 * n_walks++ + 1], xst));
             return FZ_OK;
         };
-        if (n_op > 0 && (rc = walk(0, n_op, ctx->xw, nullptr, 0, true))) return rc;
+        if (n_op > 0 && (rc = walk(0, n_op, xop, nullptr, 0, true))) return rc;
         for (int64_t b = 0; b < nb; ++b) {
             const int64_t lo = first[(size_t)b], hi = first[(size_t)b + 1];
             if (hi <= lo) continue;
@@ -1220,9 +1244,13 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
             HIP_OK(hipEventRecord(ctx->join_ev[k - 1], ctx->xs[k - 1]));
             HIP_OK(hipStreamWaitEvent(st, ctx->join_ev[k - 1], 0));
         }
-        if (side_stream) {
+        if (use_xw) {
             HIP_OK(hipEventRecord(ctx->wide_ev, ctx->xw));
             HIP_OK(hipStreamWaitEvent(st, ctx->wide_ev, 0));
+        }
+        if (n_op > 0 && op_own) {
+            HIP_OK(hipEventRecord(ctx->op_ev, xop));
+            HIP_OK(hipStreamWaitEvent(st, ctx->op_ev, 0));
         }
     }
     tm.mark();
