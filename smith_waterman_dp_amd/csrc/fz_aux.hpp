@@ -243,6 +243,9 @@ __global__ void combine_kernel(CombineArgs a)
                     if (sd[q]->flags & SO_EAGER) {
                         tr[q] = 1;
                         h.status |= q == 0 ? FZ_HIT_EAGER_LEFT : FZ_HIT_EAGER_RIGHT;
+                    } else if (sd[q]->flags & SO_WALKED) {
+                        tr[q] = 3;      // walked already, runs in the one-pass buffer
+                        longest = max(longest, (int64_t)max(sd[q]->ie, sd[q]->je));
                     } else {
                         tr[q] = 2;
                         const int64_t len = max(sd[q]->ie, sd[q]->je);
@@ -273,7 +276,7 @@ __global__ void combine_kernel(CombineArgs a)
     for (int q = 0; q < 2; ++q) {
         const SideOut &o = q == 0 ? L : R;
         a.side_trace[2 * k + q] = tr[q];
-        a.run_cap[2 * k + q] = tr[q] ? (int64_t)o.ie + o.je + 1 : 0;
+        a.run_cap[2 * k + q] = (tr[q] == 1 || tr[q] == 2) ? (int64_t)o.ie + o.je + 1 : 0;
     }
     a.hits[k] = h;
 }
@@ -395,6 +398,47 @@ __global__ void batch_assign_kernel(ExecItem *items, int64_t n, int64_t step, in
     for (int64_t q = bp + 1; q <= b; ++q) batch_first[q] = k;
 }
 
+// Walk items of the one-pass sides in done[0, n) (walked before the pool is
+// used again): the best cell's anti-diagonal, the side's run capacity
+// (ie + je + 1, into ptr_bytes, scanned into ptr_off), SO_WALKED set.
+__global__ void op_items_kernel(const int32_t *done, int64_t n, SideOut *out, ExecItem *items)
+{
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= n) return;
+    const int32_t s = done[k];
+    SideOut o = out[s];
+    ExecItem it;
+    it.side = s;
+    it.dstar = o.ie + o.je;
+    it.ptr_off = 0;
+    it.ptr_bytes = (int64_t)o.ie + o.je + 1;
+    it.batch = 0;
+    items[k] = it;
+    out[s].flags = o.flags | SO_WALKED;
+}
+
+// The walked sides' run counts (a walk that failed counts 0) into the
+// items' batch field, to be scanned into compact offsets.
+__global__ void op_run_count_kernel(ExecItem *items, int64_t n, const int64_t *run_len)
+{
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k < n) items[k].batch = max(run_len[items[k].side], (int64_t)0);
+}
+
+// Copy each walked side's runs from the round's scratch (at its item's
+// ptr_off, capacity ie + je + 1) to the one-pass runs buffer, packed (at
+// base + the scanned count, kept in the item's ptr_bytes field).
+__global__ void op_run_pack_kernel(const ExecItem *items, int64_t n, const uint32_t *scratch, uint32_t *runs,
+                                   int64_t base, int64_t *op_run_off)
+{
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= n) return;
+    const ExecItem it = items[k];
+    const int64_t dst = base + it.ptr_bytes;
+    for (int64_t q = 0; q < it.batch; ++q) runs[dst + q] = scratch[it.ptr_off + q];
+    op_run_off[it.side] = dst;
+}
+
 // Sides the one-pass executor gave back (pool exhausted): the inspector
 // takes them again and keeps them.
 __global__ void undefer_kernel(const int32_t *list, int64_t n, SideTask *tasks)
@@ -428,6 +472,7 @@ struct WalkArgs {
     const uint8_t *ptr_ws;
     int64_t ptr_base_off;
     const uint64_t *op_btab;    // one-pass sides (OP): each side's block table
+    int32_t runs_by_item;       // a side's runs at runs + its item's ptr_off (else runs + run_off[side])
     const SideOut *out;
     const int64_t *run_off;
     uint32_t *runs;
@@ -487,7 +532,7 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
     const RowHdr *hdr = reinterpret_cast<const RowHdr *>(base);
     const uint32_t *rows = OP ? nullptr : reinterpret_cast<const uint32_t *>(base + 8 * ((int64_t)it.dstar + 1));
     const uint64_t *btab = OP ? reinterpret_cast<const uint64_t *>(a.op_btab[it.side]) : nullptr;
-    uint32_t *runs = a.runs + a.run_off[it.side];
+    uint32_t *runs = a.runs + (a.runs_by_item ? it.ptr_off : a.run_off[it.side]);
     const uint32_t total_rows = OP ? OP_BLOCK_WORDS : (uint32_t)((it.ptr_bytes - 8 * ((int64_t)it.dstar + 1)) / 4);
 
     // states: 0 = S; 1 = arrived in I (continue if the cell's PTR_EXT_I
@@ -741,6 +786,8 @@ struct AssembleArgs {
     const int64_t *run_off;
     const int64_t *run_len;
     const uint32_t *runs;
+    const int64_t *op_run_off;  // SO_WALKED sides: their runs at op_runs + op_run_off[side]
+    const uint32_t *op_runs;
     fz_hit *hits;
     int64_t *cig_len;           // count pass output / write pass input (offsets after scan)
     uint32_t *cigar;
@@ -777,8 +824,11 @@ __global__ void assemble_kernel(AssembleArgs a)
         }
         return;
     }
-    const uint32_t *lr = a.runs + a.run_off[2 * k];
-    const uint32_t *rr = a.runs + a.run_off[2 * k + 1];
+    auto runs_of = [&](int64_t sd) -> const uint32_t * {
+        return (a.out[sd].flags & SO_WALKED) ? a.op_runs + a.op_run_off[sd] : a.runs + a.run_off[sd];
+    };
+    const uint32_t *lr = runs_of(2 * k);
+    const uint32_t *rr = runs_of(2 * k + 1);
     if (!WRITE) {
         a.cig_len[k] = assemble_one<false>(lr, nl, a.seeds[k].seed_len, rr, nr, nullptr);
     } else {

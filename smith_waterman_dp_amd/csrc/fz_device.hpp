@@ -107,10 +107,13 @@ struct SideTask {
 
 // SO_DEFERRED: the inspector stopped the side at ONEPASS_AT for the one-pass
 // executor (a transient state); SO_ONEPASS: the one-pass executor extended
-// it and wrote its complete pointer rows (walked from its block table).
+// it and wrote its complete pointer rows (walked from its block table);
+// SO_WALKED: ... and it was walked at once, its runs in the one-pass runs
+// buffer (an earlier round of a batch whose one-pass rows did not all fit
+// the pool at once).
 enum : int32_t {
     SO_OVERFLOW = 1, SO_EAGER = 2, SO_SKIPPED = 4, SO_EXEC_MISMATCH = 8, SO_WIDE_FLAG = 16,
-    SO_DEFERRED = 32, SO_ONEPASS = 64
+    SO_DEFERRED = 32, SO_ONEPASS = 64, SO_WALKED = 128
 };
 
 struct SideOut {

@@ -61,6 +61,8 @@ struct ExtendArgs {
     uint64_t *op_btab;
     int32_t *op_fail_list;
     uint32_t *op_fail_count;
+    int32_t *op_done_list;      // ... and the sides it finished
+    uint32_t *op_done_count;
     Scoring sc;
 };
 

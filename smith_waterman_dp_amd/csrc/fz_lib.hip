@@ -56,10 +56,16 @@ struct Counters {
     int64_t exec_cells;
     int64_t totals[4];
     int64_t max_band;
-    uint32_t defer_count, op_fail_count;    // one-pass executor: sides handed over, given back
+    uint32_t defer_count;                   // one-pass executor: sides handed over
     uint64_t defer_diags;                   // the deferred sides' anti-diagonals (m + n + 1 each)
-    uint64_t op_pool_used;
     int64_t op_cells;
+    int64_t op_runs_total;                  // run capacity of a round's walked sides
+    // per one-pass round (cleared before each): sides given back, sides
+    // finished, pool bytes taken
+    struct {
+        uint32_t fail, done;
+        uint64_t pool_used;
+    } op_round;
 };
 
 // One wave per workgroup for the wave-per-side kernels: sides differ in
@@ -140,6 +146,11 @@ struct fz_ctx {
     // one-pass executor: deferred sides, sides given back, block tables (by
     // side), the pool of row blocks
     DevBuf defer_list, op_fail, op_btab, op_pool;
+    // one-pass rounds: the other round's list of sides given back, the
+    // finished sides, their walk items, the walks' scratch (a run per move
+    // at most), and the runs of sides walked before the pool was used again,
+    // packed (by side: where they start)
+    DevBuf op_fail2, op_done, op_items, op_runs_tmp, op_runs, op_run_off;
     // seed stage: target keys and positions (two of each for the sort), query
     // keys, join ranges and counts, hits (two for the sort), run flags and
     // ranks, and the seeds of the last fz_find_seeds
@@ -756,7 +767,8 @@ void fz_destroy(fz_ctx *ctx)
                       &ctx->sk_out, &ctx->rd_keep, &ctx->rd_pos, &ctx->rd_seeds, &ctx->rd_hits, &ctx->rd_cnt,
                       &ctx->rd_off, &ctx->rd_cig, &ctx->sg_key, &ctx->sg_key2, &ctx->sg_end, &ctx->sg_end2,
                       &ctx->sg_v, &ctx->sg_max, &ctx->rs_cnt, &ctx->ps_tmp, &ctx->defer_list, &ctx->op_fail,
-                      &ctx->op_btab, &ctx->op_pool};
+                      &ctx->op_btab, &ctx->op_pool, &ctx->op_fail2, &ctx->op_done, &ctx->op_items,
+                      &ctx->op_runs_tmp, &ctx->op_runs, &ctx->op_run_off};
     for (auto &x : ctx->xs)
         if (x) (void)hipStreamSynchronize(x);
     if (ctx->xw) (void)hipStreamSynchronize(ctx->xw);
@@ -805,22 +817,21 @@ int fz_debug_set(fz_ctx *ctx, int what, int64_t value)
     return fail(ctx, FZ_EINVAL, "unknown debug setting or value out of range");
 }
 
-// The one-pass executor over the inspector's deferred sides (n of them in
-// ctx->defer_list); *given_back when it could not run at all (no pool).
-// Its pool is sized from the deferred sides' windows
-// (anti-diagonals times a 256-position row with its header, plus an arena
-// and a block table each), at most 7/10 of the free device memory (this
-// context's pointer workspaces counted as free, and released when the pool
-// must grow) and 3/5 of the device.  Sides that outgrow it are given back
-// (the caller re-runs them in the inspector); with no pool at all every
-// side is given back.
-static int run_onepass(fz_ctx *ctx, const ExtendArgs &ea, int64_t n, uint64_t diags, int64_t nsides,
-                       void *counters, hipStream_t st, bool *given_back)
+static int grow_keep(fz_ctx *ctx, DevBuf &b, size_t bytes, size_t keep, hipStream_t st);
+
+// The one-pass executor's pool, sized for n deferred sides whose windows
+// hold `diags` anti-diagonals in all (each side m + n + 1): a 256-position
+// row with its header per anti-diagonal, plus an arena and a block table
+// per side; at most 7/10 of the free device memory (this context's pointer
+// workspaces counted as free, and released when the pool must grow), 3/5
+// of the device, and the context's pointer-memory cap.  *bytes is the
+// pool's usable size, 0 when there is none (too little memory: the deferred
+// sides then go back to the inspector).
+static int prepare_onepass_pool(fz_ctx *ctx, int64_t n, uint64_t diags, int64_t nsides, hipStream_t st,
+                                uint64_t *bytes)
 {
-    *given_back = false;
-    Counters *dc = static_cast<Counters *>(counters);
+    *bytes = 0;
     ENSURE(ctx->op_btab, nsides * sizeof(uint64_t));
-    ENSURE(ctx->op_fail, n * sizeof(int32_t));
     uint64_t want = 0;
     if (ctx->dbg_op_pool > 0) {
         want = (uint64_t)ctx->dbg_op_pool;
@@ -865,26 +876,31 @@ static int run_onepass(fz_ctx *ctx, const ExtendArgs &ea, int64_t n, uint64_t di
         }
     }
     const uint64_t pool_bytes = ctx->op_pool.p ? std::min<uint64_t>(want, ctx->op_pool.cap) : 0;
-    if (pool_bytes < (uint64_t)(OP_BLOCK_BYTES + OP_ARENA)) {
-        // (the pool's sink and one arena at least)
-        *given_back = true;
-        return FZ_OK;
-    }
+    // (the pool's sink and one arena at least)
+    *bytes = pool_bytes >= (uint64_t)(OP_BLOCK_BYTES + OP_ARENA) ? pool_bytes : 0;
+    return FZ_OK;
+}
+
+// One round of the one-pass executor over list[0, n): sides it finishes go
+// to `done`, sides the pool could not hold to `fail` (counts in
+// Counters::op_round, cleared by the caller).
+static int launch_onepass_round(fz_ctx *ctx, const ExtendArgs &ea, const int32_t *list, int64_t n,
+                                uint64_t pool_bytes, int32_t *fail, int32_t *done, void *counters, hipStream_t st)
+{
+    Counters *dc = static_cast<Counters *>(counters);
     ExtendArgs oa = ea;
-    oa.list = as<int32_t>(ctx->defer_list);
+    oa.list = list;
     oa.nlist = (int32_t)n;
     oa.exec_cells = &dc->op_cells;
     oa.op_pool = as<uint8_t>(ctx->op_pool);
     oa.op_pool_bytes = pool_bytes;
-    oa.op_pool_used = reinterpret_cast<unsigned long long *>(&dc->op_pool_used);
+    oa.op_pool_used = reinterpret_cast<unsigned long long *>(&dc->op_round.pool_used);
     oa.op_btab = as<uint64_t>(ctx->op_btab);
-    oa.op_fail_list = as<int32_t>(ctx->op_fail);
-    oa.op_fail_count = &dc->op_fail_count;
-    HIP_OK(hipEventRecord(ctx->kev[2], st));
-    int rc = launch_onepass(ctx, oa, n, st);
-    if (rc) return rc;
-    HIP_OK(hipEventRecord(ctx->kev[3], st));
-    return FZ_OK;
+    oa.op_fail_list = fail;
+    oa.op_fail_count = &dc->op_round.fail;
+    oa.op_done_list = done;
+    oa.op_done_count = &dc->op_round.done;
+    return launch_onepass(ctx, oa, n, st);
 }
 
 static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const uint8_t *query, uint64_t qlen,
@@ -1031,20 +1047,95 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     }
     bool onepass_ran = false;
     if (hc.defer_count > 0) {
-        // ---- one-pass executor over the deferred sides
-        bool all_back = false;
-        rc = run_onepass(ctx, ea, (int64_t)hc.defer_count, hc.defer_diags, nsides, dc, st, &all_back);
+        // ---- one-pass executor over the deferred sides, in rounds: when the
+        // pool cannot hold all their rows at once, the sides a round
+        // finished are walked at once and the pool serves the next round
+        // (the sides that did not fit); the last round's sides are walked
+        // beside the two-pass executor.  A round that finishes no side
+        // gives the rest back to the inspector.
+        uint64_t pool_bytes = 0;
+        rc = prepare_onepass_pool(ctx, (int64_t)hc.defer_count, hc.defer_diags, nsides, st, &pool_bytes);
         if (rc) return rc;
-        onepass_ran = !all_back;
-        if ((rc = read_counters())) return rc;
-        const uint32_t n_back = all_back ? hc.defer_count : hc.op_fail_count;
-        S.n_onepass = (uint64_t)(hc.defer_count - n_back);
+        ENSURE(ctx->op_fail, nsides * sizeof(int32_t));
+        ENSURE(ctx->op_fail2, nsides * sizeof(int32_t));
+        ENSURE(ctx->op_done, nsides * sizeof(int32_t));
+        ENSURE(ctx->run_len, nsides * sizeof(int64_t));
+        const int32_t *L = as<int32_t>(ctx->defer_list);
+        uint32_t nL = hc.defer_count;
+        const int32_t *back = nullptr;
+        uint32_t n_back = 0;
+        if (pool_bytes == 0) {
+            back = L;
+            n_back = nL;
+            nL = 0;
+        }
+        int64_t runs_base = 0;
+        for (int fb = 0; nL > 0; fb ^= 1) {
+            rc = zero(ctx, &dc->op_round, sizeof dc->op_round, st);
+            if (rc) return rc;
+            int32_t *fl = fb ? as<int32_t>(ctx->op_fail2) : as<int32_t>(ctx->op_fail);
+            if (!onepass_ran) HIP_OK(hipEventRecord(ctx->kev[2], st));
+            rc = launch_onepass_round(ctx, ea, L, nL, pool_bytes, fl, as<int32_t>(ctx->op_done), dc, st);
+            if (rc) return rc;
+            onepass_ran = true;
+            if ((rc = read_counters())) return rc;
+            const uint32_t nd = hc.op_round.done, nf = hc.op_round.fail;
+            S.n_onepass += nd;
+            S.onepass_bytes += std::min<uint64_t>(hc.op_round.pool_used, pool_bytes);
+            if (nd == 0) {
+                back = fl;
+                n_back = nf;
+                break;
+            }
+            if (nf == 0) break;
+            // the pool serves the next round: walk this round's sides now
+            ENSURE(ctx->op_items, (int64_t)nd * sizeof(ExecItem));
+            ExecItem *items = as<ExecItem>(ctx->op_items);
+            op_items_kernel<<<blocks_for(nd, 256), 256, 0, st>>>(as<int32_t>(ctx->op_done), (int64_t)nd,
+                                                                 as<SideOut>(ctx->out), items);
+            HIP_OK(hipGetLastError());
+            const int64_t stride = sizeof(ExecItem) / sizeof(int64_t);
+            rc = scan(ctx, reinterpret_cast<const int64_t *>(&items->ptr_bytes), stride, nd,
+                      reinterpret_cast<int64_t *>(&items->ptr_off), stride, &dc->op_runs_total, st);
+            if (rc) return rc;
+            if ((rc = read_counters())) return rc;
+            ENSURE(ctx->op_runs_tmp, std::max<int64_t>(hc.op_runs_total, 1) * sizeof(uint32_t));
+            WalkArgs wk = {};
+            wk.items = items;
+            wk.begin = 0;
+            wk.end = nd;
+            wk.op_btab = as<uint64_t>(ctx->op_btab);
+            wk.runs_by_item = 1;
+            wk.out = as<SideOut>(ctx->out);
+            wk.runs = as<uint32_t>(ctx->op_runs_tmp);
+            wk.run_len = as<int64_t>(ctx->run_len);
+            walk_wave_kernel<true><<<nd, 64, 0, st>>>(wk);
+            HIP_OK(hipGetLastError());
+            // pack the runs (a walk writes far fewer than its capacity)
+            op_run_count_kernel<<<blocks_for(nd, 256), 256, 0, st>>>(items, (int64_t)nd, as<int64_t>(ctx->run_len));
+            HIP_OK(hipGetLastError());
+            rc = scan(ctx, reinterpret_cast<const int64_t *>(&items->batch), stride, nd,
+                      reinterpret_cast<int64_t *>(&items->ptr_bytes), stride, &dc->op_runs_total, st);
+            if (rc) return rc;
+            if ((rc = read_counters())) return rc;
+            const int64_t packed = hc.op_runs_total;
+            rc = grow_keep(ctx, ctx->op_runs, (size_t)std::max<int64_t>(runs_base + packed, 1) * sizeof(uint32_t),
+                           (size_t)runs_base * sizeof(uint32_t), st);
+            if (rc) return rc;
+            ENSURE(ctx->op_run_off, nsides * sizeof(int64_t));
+            op_run_pack_kernel<<<blocks_for(nd, 256), 256, 0, st>>>(items, (int64_t)nd, as<uint32_t>(ctx->op_runs_tmp),
+                                                                    as<uint32_t>(ctx->op_runs), runs_base,
+                                                                    as<int64_t>(ctx->op_run_off));
+            HIP_OK(hipGetLastError());
+            runs_base += packed;
+            L = fl;
+            nL = nf;
+        }
+        if (onepass_ran) HIP_OK(hipEventRecord(ctx->kev[3], st));
         S.onepass_cells = (uint64_t)hc.op_cells;
-        S.onepass_bytes = hc.op_pool_used;
         if (n_back > 0) {
-            // the pool ran out: the inspector takes those sides back and
-            // keeps them (the two-pass executor traces them)
-            int32_t *back = all_back ? as<int32_t>(ctx->defer_list) : as<int32_t>(ctx->op_fail);
+            // the pool held none of them: the inspector takes those sides
+            // back and keeps them (the two-pass executor traces them)
             undefer_kernel<<<blocks_for(n_back, 256), 256, 0, st>>>(back, (int64_t)n_back, as<SideTask>(ctx->tasks));
             HIP_OK(hipGetLastError());
             ExtendArgs ra = ea;
@@ -1188,7 +1279,7 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
             if (n_op > 0 && op_own) HIP_OK(hipStreamWaitEvent(xop, ctx->fork_ev, 0));
         }
         auto walk = [&](int64_t s0, int64_t s1, hipStream_t xst, uint8_t *wsp, int64_t base_off, bool op) -> int {
-            WalkArgs wk;
+            WalkArgs wk = {};
             wk.items = as<ExecItem>(ctx->items);
             wk.begin = s0;
             wk.end = s1;
@@ -1257,7 +1348,9 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
 
     // ---- gather CIGARs
     ENSURE(ctx->cig, n * sizeof(int64_t));
-    AssembleArgs aa;
+    AssembleArgs aa = {};
+    aa.op_run_off = as<int64_t>(ctx->op_run_off);
+    aa.op_runs = as<uint32_t>(ctx->op_runs);
     aa.seeds = seeds;
     aa.out = as<SideOut>(ctx->out);
     aa.n = n;

@@ -144,6 +144,7 @@ struct OpState {
     unsigned long long *used;   // bytes taken after the sink
     uint64_t aend;              // end of the wave's current arena (0: none)
     uint64_t *btab;             // the side's block table
+    uint64_t admit;             // no side starts once `used` is past this
     int32_t out_of_pool;        // the side ran out of pool
 };
 __shared__ OpState op_state;
@@ -158,7 +159,9 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t x)
 // `bytes` of pool memory at or after address cur (16-aligned), from the
 // wave's arena; a new arena when it does not fit, a direct pool carve for
 // requests above half an arena.  nullptr when the pool is exhausted.
-__device__ __forceinline__ uint8_t *op_alloc(uint64_t cur, uint64_t bytes)
+// With `limit`, the carve fails also when the pool had `limit` bytes or more
+// taken before it (admission of a new side, see run_side_pk).
+__device__ __forceinline__ uint8_t *op_alloc(uint64_t cur, uint64_t bytes, uint64_t limit = ~(uint64_t)0)
 {
     const uint64_t aend = uniform64(op_state.aend);
     if (cur != 0 && cur + bytes <= aend) return reinterpret_cast<uint8_t *>(cur);
@@ -168,7 +171,7 @@ __device__ __forceinline__ uint8_t *op_alloc(uint64_t cur, uint64_t bytes)
     if (fresh_lane_id() == 0) off = atomicAdd(used, (unsigned long long)take);
     off = uniform64(off);
     const uint64_t pool_bytes = uniform64(op_state.pool_bytes) - (uint64_t)OP_BLOCK_BYTES;
-    if (off > pool_bytes || take > pool_bytes - off) return nullptr;
+    if (off > pool_bytes || take > pool_bytes - off || off >= limit) return nullptr;
     const uint64_t base = uniform64((uint64_t)(uintptr_t)op_state.pool) + (uint64_t)OP_BLOCK_BYTES + off;
     if (take == (uint64_t)OP_ARENA) op_state.aend = base + take;       // (every lane writes the same value)
     return reinterpret_cast<uint8_t *>(base);
@@ -236,9 +239,8 @@ struct SidePk {
 
     // One-pass executor: close the block ending before diagonal d (its last
     // header slot gets the block's word count) and open the block of d.
-    // When the pool is exhausted the side goes on to its end with its rows
-    // sent to the pool's sink (never read; no exit from the loop here,
-    // which would cost the sweep's registers) and is marked out of pool.
+    // When the pool is exhausted the side's rows go to the pool's sink
+    // (never read) and it is marked out of pool; the caller ends it.
     __device__ __forceinline__ void op_next_block(int d)
     {
         if (lane == 0) {
@@ -771,7 +773,12 @@ __device__ __forceinline__ SideResult run_side_pk(const SideTask &task, const Sc
         // the block table (a block for every flush point the side can
         // reach, up to anti-diagonal m + n + 1), then block 0
         const uint64_t nblk = (uint64_t)(((int64_t)task.m + task.n + 1) / OP_BLOCK + 1);
-        uint8_t *bt = op_alloc(0, 8 * nblk);
+        // admission: a side starts only if the pool had less than its
+        // admission mark taken before the side's first carve (taken in the
+        // same atomic step, so sides that start together are counted one
+        // after the other), so that the sides already running have room to
+        // finish: a side that runs out midway was swept for nothing
+        uint8_t *bt = op_alloc(0, 8 * nblk, uniform64(op_state.admit));
         uint8_t *b0 = bt ? op_alloc(((uint64_t)(uintptr_t)bt + 8 * nblk + 15) & ~(uint64_t)15, (uint64_t)OP_BLOCK_BYTES)
                          : nullptr;
         if (!b0) {
@@ -829,7 +836,12 @@ __device__ __forceinline__ SideResult run_side_pk(const SideTask &task, const Sc
                 return false;
             }
         }
-        if constexpr (ONEPASS) p.op_next_block(dd);
+        if constexpr (ONEPASS) {
+            p.op_next_block(dd);
+            // out of pool: the side ends at the next diagonal (its stop
+            // diagonal; no exit from the sweep here) and is given back
+            if (uniform(op_state.out_of_pool)) dstop = dd - 1;
+        }
         stay = !p.want_switch();
         return true;
     };
@@ -905,6 +917,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <=
         op_state.used = a.op_pool_used;
         op_state.aend = 0;
         op_state.btab = nullptr;
+        op_state.admit = a.op_pool_bytes / 10 * 9;
         op_state.out_of_pool = 0;
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         const SideResult x = run_side_pk<true, true>(task, a.sc, 0x7fffffff, nullptr, xfer, nullptr, 0);
@@ -933,6 +946,8 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <=
                 a.op_fail_list[k] = sid;
             } else {
                 atomicAdd((unsigned long long *)a.exec_cells, (unsigned long long)x.cells);
+                const uint32_t k = atomicAdd(a.op_done_count, 1u);
+                a.op_done_list[k] = sid;
             }
         }
         return;

@@ -292,12 +292,13 @@ def test_wide_band_and_overflow(ctx):
 
 
 def test_pointer_workspace_batches(ctx):
-    """A tiny pointer workspace forces many executor batches; results equal."""
+    """A tiny pointer workspace forces many executor batches; results equal.
+    (Two-pass: the cap would otherwise serve most sides in one-pass rounds.)"""
     w = W.executor_heavy(n_pairs=60, len_min=300, len_max=3000, seed=4)
     ref = run_gpu(ctx, w)
     fz.fz_set_pointer_workspace(ctx.h, 4 << 20)
     try:
-        gh, gc, st = run_gpu(ctx, w)
+        gh, gc, st = run_gpu(ctx, w, two_pass=True)
     finally:
         fz.fz_set_pointer_workspace(ctx.h, 0)
     assert st["n_batches"] > 1
@@ -314,7 +315,7 @@ def test_workspace_cap_at_create():
     c1 = fz.Context(0, workspace_bytes=4 << 20)
     try:
         ref = run_gpu(c0, w)
-        gh, gc, st = run_gpu(c1, w)
+        gh, gc, st = run_gpu(c1, w, two_pass=True)
     finally:
         c0.close()
         c1.close()
