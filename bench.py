@@ -54,15 +54,33 @@ VALU_PEAK_OPS_PK16 = 2 * VALU_PEAK_OPS
 OPS_PER_CELL = {"extend": 13, "local": 12}
 
 
-# HBM traffic of one inspector launch on the 1M-seed skewed batch, from two
-# rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) scaled by what the same
-# counters read for a plain 1 GiB device copy in the same run (FETCH_SIZE
-# reads 0.5 GiB for it, WRITE_SIZE 1.0 GiB).  Valid only for the kernel
-# sources it was taken on (hash of fz_extend.hpp, fz_device.hpp and
-# fz_packed.hpp); reported as null otherwise.
-TRAFFIC_SRC_HASH = "6a2de3bcf1998d63"
-TRAFFIC_FETCH_BYTES = 5.449e6 * 1024 / 0.5
-TRAFFIC_WRITE_BYTES = 3.436e6 * 1024 / 1.0
+def extension_kernels(cells, onepass_cells, inspector_ms, onepass_ms, peak):
+    """Rooflines of the two kernels that sweep the extension's cells: the
+    inspector (the cells of every side it finished: all but the one-pass
+    sides') and the one-pass executor (its sides' cells, each swept once with
+    its pointers).  Returns (dominant, [both]); a kernel that did not run
+    (0 ms) is left out."""
+    ops = OPS_PER_CELL["extend"]
+    ks = []
+    for name, c, ms in (("extend_kernel (inspector)", cells - onepass_cells, inspector_ms),
+                        ("extend_kernel (one-pass executor)", onepass_cells, onepass_ms)):
+        if ms > 0 and c > 0:
+            ach = ops * c / (ms / 1e3) / 1e12
+            ks.append({"kernel": name, "cells": int(c), "ms": round(ms, 3), "achieved": round(ach, 3),
+                       "frac": round(ach / peak, 4)})
+    dom = max(ks, key=lambda k: k["ms"]) if ks else None
+    return dom, ks
+
+
+# HBM traffic of one launch of each extension kernel on the 1M-seed skewed
+# batch, from two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE, KiB)
+# scaled by what the same counters read for a plain 1 GiB device copy in the
+# same run (FETCH_SIZE reads 0.5 GiB for it, WRITE_SIZE 1.0 GiB).  Valid only
+# for the kernel sources it was taken on (hash of fz_extend.hpp,
+# fz_device.hpp and fz_packed.hpp); reported as null otherwise.
+TRAFFIC_SRC_HASH = "754075208a90a29f"
+TRAFFIC = {"extend_kernel (inspector)": (4.503e6 * 1024 / 0.5, 5.837e6 * 1024 / 1.0),
+           "extend_kernel (one-pass executor)": (3.763e6 * 1024 / 0.5, 1.689e8 * 1024 / 1.0)}
 
 
 # The same for one join_count_kernel launch of the seed stage on the 20 Mbp
@@ -333,10 +351,11 @@ def bench_pipeline(a):
         print("[bench] warmup %d done" % k, file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    res, main_ms = None, []
+    res, main_ms, op_ms = None, [], []
     for k in range(steps):
         res = step()
         main_ms.append(sum(st["ms_main"] for _, _, st in res))
+        op_ms.append(sum(st["ms_onepass"] for _, _, st in res))
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms_per_step = dt / steps * 1e3
@@ -348,9 +367,10 @@ def bench_pipeline(a):
         per_strand.append({"seeds": int(n), "covered": int(((hh[:, 1] & fz.FZ_HIT_COVERED) != 0).sum()),
                            "traced": int(((hh[:, 1] & fz.FZ_HIT_TRACED) != 0).sum())})
     kern_s = float(np.mean(main_ms)) / 1e3
-    achieved = OPS_PER_CELL["extend"] * cells / kern_s / 1e12
     packed = all(int(st["n_packed"]) > 0 for _, _, st in res)
     peak = (VALU_PEAK_OPS_PK16 if packed else VALU_PEAK_OPS) / 1e12
+    op_cells = sum(int(st["onepass_cells"]) for _, _, st in res)
+    dom, kernels = extension_kernels(cells, op_cells, kern_s * 1e3, float(np.mean(op_ms)), peak)
     bases = int(w["target"].size + w["query"].size)
     out = {"metric": "whole-pair alignment (seed stage + covered-seed rounds, both strands) on a 20 Mbp "
                      "chromosome pair, 1 MI355X",
@@ -362,9 +382,9 @@ def bench_pipeline(a):
                       "round_doubling": bool(a.round_doubling), "strands_run": a.strands,
                       "min_traceback_score": 3000, "cells_per_step": cells, "strands": per_strand,
                       "inspector_ms": round(kern_s * 1e3, 3)},
-           "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(peak, 3), "unit": "TOP/s",
-                        "frac": round(achieved / peak, 4), "traffic": None,
-                        "kernel": "extend_kernel (inspector, all rounds)", "ops_per_cell": OPS_PER_CELL["extend"]}}
+           "roofline": {"bound": "alu", "achieved": dom["achieved"], "peak": round(peak, 3), "unit": "TOP/s",
+                        "frac": dom["frac"], "traffic": None, "kernel": dom["kernel"] + ", all rounds",
+                        "ops_per_cell": OPS_PER_CELL["extend"], "kernels": kernels}}
     if not a.no_cpu:
         print("[bench] CPU oracle sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_pipeline_baseline(w, a.cpu_seconds, a.round_size, a.round_doubling)
@@ -455,7 +475,7 @@ def main():
         step()
         print("[bench] warmup %d done" % k, file=sys.stderr, flush=True)
     torch.cuda.synchronize()
-    main_ms, step_ms = [], []
+    main_ms, step_ms, op_ms = [], [], []
     t0 = time.perf_counter()
     hits = None
     st = None
@@ -465,6 +485,7 @@ def main():
         torch.cuda.synchronize()
         step_ms.append((time.perf_counter() - ts) * 1e3)
         main_ms.append(st["ms_main"])
+        op_ms.append(0.0 if local else st["ms_onepass"])
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     call_ms = None if local or rounds else call_overhead_ms(ctx, T, Q, S, w, min_tb)
@@ -484,15 +505,24 @@ def main():
     gcups = cells / (ms_per_step / 1e3) / 1e9
     ops = OPS_PER_CELL["local" if local else "extend"]
     kern_s = float(np.median(main_ms)) / 1e3
-    achieved = ops * cells / kern_s / 1e12
     # the extension's cells run in packed 16-bit layouts when the scoring
     # allows it (every side after its first 34 anti-diagonals): their peak
     # is the packed rate
     packed = (not local) and int(st["n_packed"]) > 0
     peak = (VALU_PEAK_OPS_PK16 if packed else VALU_PEAK_OPS) / 1e12
+    if local:
+        dom = {"kernel": "local_kernel", "cells": cells, "ms": round(kern_s * 1e3, 3),
+               "achieved": round(ops * cells / kern_s / 1e12, 3)}
+        dom["frac"] = round(dom["achieved"] / peak, 4)
+        kernels = [dom]
+    else:
+        dom, kernels = extension_kernels(cells, int(st["onepass_cells"]), kern_s * 1e3, float(np.median(op_ms)), peak)
     traffic = None
     if a.workload == "skewed" and kernel_src_hash() == TRAFFIC_SRC_HASH:
-        traffic = measured_traffic(TRAFFIC_FETCH_BYTES, TRAFFIC_WRITE_BYTES, kern_s)
+        for k in kernels:
+            if k["kernel"] in TRAFFIC:
+                k["traffic"] = measured_traffic(*TRAFFIC[k["kernel"]], k["ms"] / 1e3)
+        traffic = dom.get("traffic")
     cfg = {"workload": a.workload, "records": n, "target_bp": int(w["target"].size), "query_bp": int(w["query"].size),
            "cells_per_step": cells, "scoring": w["scoring"], "ydrop": None if local else w["ydrop"],
            "min_traceback_score": w.get("min_tb"), "main_kernel_ms": round(kern_s * 1e3, 3),
@@ -528,17 +558,17 @@ def main():
            "value": round(gcups, 3), "unit": "GCUPS", "n_gpus": 1, "steps": steps, "warmup": a.warmup,
            "ms_per_step": round(ms_per_step, 3), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "int16x2" if packed else "int32", "data": "synthetic", "config": cfg,
-           "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(peak, 3), "unit": "TOP/s",
-                        "frac": round(achieved / peak, 4), "traffic": traffic,
-                        "kernel": "local_kernel" if local else "extend_kernel (inspector)",
-                        "ops_per_cell": ops,
+           "roofline": {"bound": "alu", "achieved": dom["achieved"], "peak": round(peak, 3), "unit": "TOP/s",
+                        "frac": dom["frac"], "traffic": traffic, "kernel": dom["kernel"],
+                        "ops_per_cell": ops, "kernels": kernels,
                         # the whole call against the same peak: ops_per_cell x GCUPS
                         "end_to_end": {"achieved": round(ops * gcups / 1e3, 3),
-                                       "frac": round(ops * gcups / 1e3 / peak, 4)}}}
+                                       "frac": round(ops * gcups / 1e3 / peak, 4),
+                                       "frac_of_int32_peak": round(ops * gcups / 1e3 / (VALU_PEAK_OPS / 1e12), 4)}}}
     if packed:
         # for comparison with 32-bit builds: the same figure against the
         # int32 lane rate
-        out["roofline"]["frac_of_int32_peak"] = round(achieved / (VALU_PEAK_OPS / 1e12), 4)
+        out["roofline"]["frac_of_int32_peak"] = round(dom["achieved"] / (VALU_PEAK_OPS / 1e12), 4)
         out["roofline"]["arith"] = "packed int16 pairs after anti-diagonal 33, int32 before"
     probe = measured_valu_peak(packed)
     if probe is not None:
