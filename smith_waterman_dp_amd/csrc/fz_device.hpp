@@ -99,13 +99,13 @@ struct SideTask {
     int32_t m, n;               // m < 0: skip (invalid seed)
     int32_t seed, side;         // side 0 = left, 1 = right
     // The inspector hands the side to the one-pass executor when, at
-    // anti-diagonal ONEPASS_AT, its best score is at least this (its seed is
+    // anti-diagonal ONEPASS_AT (or AT2, AT3), its best score is at least this (its seed is
     // then traced whatever the other side scores) and still growing;
     // INT32_MAX: never.
     int32_t defer_need, pad_;
 };
 
-// SO_DEFERRED: the inspector stopped the side at ONEPASS_AT for the one-pass
+// SO_DEFERRED: the inspector stopped the side at a hand-over test for the one-pass
 // executor (a transient state); SO_ONEPASS: the one-pass executor extended
 // it and wrote its complete pointer rows (walked from its block table);
 // SO_WALKED: ... and it was walked at once, its runs in the one-pass runs
@@ -162,7 +162,13 @@ constexpr int64_t MAX_SIDE_LEN = (int64_t)1 << 28;
 // OP_ROW_WORDS words each, offsets relative to the block's first row word.
 // A side's block table (one 64-bit address per block) and its blocks are
 // carved out of per-wave arenas of OP_ARENA bytes taken from one pool.
-constexpr int ONEPASS_AT = 256;             // a multiple of 8 (a flush point of the packed layouts)
+// Hand-over tests at anti-diagonals 256, 1024 and 4096 (flush points of the
+// packed layouts): a long side whose best stalls for a while near 256 and
+// grows again is still handed over later, at the cost of the anti-diagonals
+// the inspector swept before.
+constexpr int ONEPASS_AT = 256;
+constexpr int ONEPASS_AT2 = 1024;
+constexpr int ONEPASS_AT3 = 4096;
 constexpr int ONEPASS_RECENT = 64;          // best found at most this many anti-diagonals before
 constexpr int OP_BLOCK = 64;                // anti-diagonals per block (a power of two, a multiple of 8)
 constexpr int OP_HDRS = OP_BLOCK + 1;

@@ -376,6 +376,20 @@ int launch_extend(fz_ctx *ctx, const ExtendArgs &a, int64_t nwork, hipStream_t s
     return FZ_OK;
 }
 
+// The packed two-pass executor over sides of the shortest length bin: four
+// waves (sides) per workgroup.  These sides are short and alike, so a group
+// is not held long by one of them, and a quarter of the workgroups keeps
+// the dispatcher, which short one-wave groups outrun, from bounding the
+// launch.
+int launch_exec_short(fz_ctx *ctx, const ExtendArgs &a, int64_t nwork, hipStream_t st)
+{
+    if (nwork <= 0) return FZ_OK;
+    constexpr int G = 4;
+    extend_kernel<C_STD, true, SUB_LUT, G, true><<<(unsigned)((nwork + G - 1) / G), 64 * G, 0, st>>>(a);
+    HIP_OK(hipGetLastError());
+    return FZ_OK;
+}
+
 // The one-pass executor over a.list (one wave per side, like the others).
 int launch_onepass(fz_ctx *ctx, const ExtendArgs &a, int64_t nwork, hipStream_t st)
 {
@@ -1186,10 +1200,11 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     // and slow, so they overlap everything after them), then the standard
     // ones, each class longest bins first; items [0, n_op) are one-pass,
     // [n_op, n_wide) wide
-    int64_t n_exec = 0, n_op = 0, n_wide = 0;
+    int64_t n_exec = 0, n_op = 0, n_wide = 0, n_short = 0;
     for (int cls = EXEC_CLASSES - 1; cls >= 0; --cls)
         for (int b = NBINS - 1; b >= 0; --b) {
             base[cls * NBINS + b] = (uint32_t)n_exec;
+            if (cls == EXEC_CLASS_STD && b == 0) n_short = n_exec;   // the shortest standard bin from here
             n_exec += hc.bin_count[cls * NBINS + b];
             if (cls == EXEC_CLASS_ONEPASS) n_op = n_exec;
             if (cls == EXEC_CLASS_WIDE) n_wide = n_exec;
@@ -1325,8 +1340,19 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
                 xa.nlist = (int32_t)(s1 - s0);
                 xa.ptr_ws = wsp;
                 xa.ptr_base_off = b * step;
-                rc = cls == 0 ? launch_extend<C_STD, true>(ctx, xa, s1 - s0, xst, pk)
-                              : launch_extend<C_WIDE, true>(ctx, xa, s1 - s0, xst);
+                if (cls == 0 && pk && s1 > n_short) {
+                    // the shortest bin's sides in groups of four
+                    const int64_t m = std::max(s0, n_short);
+                    xa.nlist = (int32_t)(m - s0);
+                    if ((rc = launch_extend<C_STD, true>(ctx, xa, m - s0, xst, pk))) return rc;
+                    ExtendArgs sa = xa;
+                    sa.exec_begin = m;
+                    sa.nlist = (int32_t)(s1 - m);
+                    rc = launch_exec_short(ctx, sa, s1 - m, xst);
+                } else {
+                    rc = cls == 0 ? launch_extend<C_STD, true>(ctx, xa, s1 - s0, xst, pk)
+                                  : launch_extend<C_WIDE, true>(ctx, xa, s1 - s0, xst);
+                }
                 if (rc) return rc;
                 if ((rc = walk(s0, s1, xst, wsp, b * step, false))) return rc;
             }

@@ -226,10 +226,10 @@ struct SidePk {
     static __device__ __forceinline__ bool at_checkpoint(int d)
     {
         if (ONEPASS) return (d & (OP_BLOCK - 1)) == 0;
-        return !EXEC && d == ONEPASS_AT;
+        return !EXEC && (d == ONEPASS_AT || d == ONEPASS_AT2 || d == ONEPASS_AT3);
     }
 
-    // (inspector, at ONEPASS_AT) the side's seed is now certain to be traced
+    // (inspector, at a hand-over test) the side's seed is now certain to be traced
     // and its best is still growing: it goes to the one-pass executor
     // (defer_need is INT32_MAX when that is off)
     __device__ __forceinline__ bool defer_now(int d) const
