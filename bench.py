@@ -486,6 +486,9 @@ def main():
         step_ms.append((time.perf_counter() - ts) * 1e3)
         main_ms.append(st["ms_main"])
         op_ms.append(0.0 if local else st["ms_onepass"])
+        print("[bench] step %d: %.1f ms (dominant kernel %.1f ms%s)" % (
+            k, step_ms[-1], st["ms_main"], "" if local else ", one-pass %.1f ms, exec %.1f ms" % (
+                st["ms_onepass"], st["ms_exec"])), file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     call_ms = None if local or rounds else call_overhead_ms(ctx, T, Q, S, w, min_tb)

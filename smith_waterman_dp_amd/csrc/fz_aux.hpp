@@ -522,6 +522,8 @@ template <bool OP>
 __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
 {
     constexpr int WPR = WALK_CHUNK / 6 + 2;              // words staged per row (at most)
+    constexpr int WPR4 = (WPR + 3) / 4;                  // 16-byte loads per row
+    static_assert(16 * WPR4 <= WALK_PAD + 4, "the row loads must stay within a pointer area's pad");
     __shared__ uint32_t wl[WALK_CHUNK][WPR];
     const int lane = lane_id();
     const int64_t k = a.begin + (int64_t)blockIdx.x;
@@ -531,7 +533,8 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
     const uint8_t *base = OP ? nullptr : a.ptr_ws + (it.ptr_off - a.ptr_base_off);
     const RowHdr *hdr = reinterpret_cast<const RowHdr *>(base);
     const uint32_t *rows = OP ? nullptr : reinterpret_cast<const uint32_t *>(base + 8 * ((int64_t)it.dstar + 1));
-    const uint64_t *btab = OP ? reinterpret_cast<const uint64_t *>(a.op_btab[it.side]) : nullptr;
+    typedef __attribute__((address_space(1))) const uint64_t GlobalU64;
+    GlobalU64 *btab = OP ? reinterpret_cast<GlobalU64 *>(a.op_btab[it.side]) : nullptr;
     uint32_t *runs = a.runs + (a.runs_by_item ? it.ptr_off : a.run_off[it.side]);
     const uint32_t total_rows = OP ? OP_BLOCK_WORDS : (uint32_t)((it.ptr_bytes - 8 * ((int64_t)it.dstar + 1)) / 4);
 
@@ -572,14 +575,34 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
         // (packed rows hold PTR_DIAG and PTR_FROM_I inverted)
         return ((wl[r][q] >> row_shift(p, cpw8, pk)) & 0xFu) ^ (pk ? (PTR_DIAG | PTR_FROM_I) : 0u);
     };
+    // one-pass blocks: lane k < 8 holds the address of block pf_b0 + k,
+    // loaded one chunk ahead (a chunk's rows lie in at most three blocks)
+    uint64_t pf = 0;
+    int pf_b0 = -(1 << 30);
     while (!bad && !(st == 0 && i == 0 && j == 0)) {
         const int d = i + j;
         const int dlo = max(0, d - (WALK_CHUNK - 1));
         int rib[2] = {0, 0}, rw0[2] = {0, 0}, rnw[2] = {0, 0};
+        uint64_t cur = 0;
+        int cur_b0 = 0;
+        if constexpr (OP) {
+            const int b0 = dlo / OP_BLOCK, bmax = it.dstar / OP_BLOCK;
+            if (b0 < pf_b0 || d / OP_BLOCK > pf_b0 + 7) {
+                // (the first chunk, or a walk that left the prefetched range)
+                pf = (lane < 8 && b0 + lane <= bmax) ? btab[b0 + lane] : 0;
+                pf_b0 = b0;
+            }
+            cur = pf;
+            cur_b0 = pf_b0;
+            // the next chunk ends below dlo and starts at or above dlo - 128
+            const int nb0 = max(0, dlo - WALK_CHUNK) / OP_BLOCK;
+            pf = (lane < 8 && nb0 + lane <= bmax) ? btab[nb0 + lane] : 0;
+            pf_b0 = nb0;
+        }
         {
             // both rows' headers, then every word load of both rows, then
-            // the LDS stores: two memory round trips per chunk (three with
-            // one-pass blocks: block address, headers, words)
+            // the LDS stores: two memory round trips per chunk (one-pass
+            // blocks: the block addresses come from the chunk before)
             RowHdr h[2];
             uint32_t rend[2];
             const uint32_t *rb[2] = {rows, rows};
@@ -592,11 +615,16 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
                     // the block's headers hold one more slot, the block's
                     // word count, so the next header is the row's end also
                     // for the block's last row (and the side's)
-                    const uint8_t *blk = reinterpret_cast<const uint8_t *>(btab[dr / OP_BLOCK]);
-                    const RowHdr *bh = reinterpret_cast<const RowHdr *>(blk);
+                    const int src = dr / OP_BLOCK - cur_b0;      // 0..2
+                    const uint32_t alo = (uint32_t)__shfl((int)(uint32_t)cur, src);
+                    const uint32_t ahi = (uint32_t)__shfl((int)(uint32_t)(cur >> 32), src);
+                    const uint64_t blk = ((uint64_t)ahi << 32) | alo;
+                    GlobalU64 *bh = reinterpret_cast<GlobalU64 *>(blk);
                     const int q = dr & (OP_BLOCK - 1);
-                    h[h2] = bh[q];
-                    rend[h2] = min(bh[q + 1].off & ROW_OFF_MASK, total_rows);
+                    const uint64_t h0 = bh[q], h1 = bh[q + 1];
+                    h[h2].off = (uint32_t)h0;
+                    h[h2].ibase = (int32_t)(h0 >> 32);
+                    rend[h2] = min((uint32_t)h1 & ROW_OFF_MASK, total_rows);
                     rb[h2] = reinterpret_cast<const uint32_t *>(blk + 8 * OP_HDRS);
                 } else {
                     h[h2] = hdr[dr];
@@ -606,7 +634,7 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
                     rend[h2] = min(dr < it.dstar ? next_off : total_rows, total_rows);
                 }
             }
-            uint32_t v[2][WPR];
+            uint32_t v[2][WPR4 * 4];
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 const int dr = dlo + h2 * WALK_LANES + lane;
@@ -623,12 +651,19 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
                 // ibase biased by 2^29 (rows' ibase lies within +-2^29: sides
                 // are at most MAX_SIDE_LEN long), the format flags above it
                 rib[h2] = (int)((uint32_t)(h[h2].ibase + (1 << 29)) | (h[h2].off & (ROW_CPW8 | ROW_PK)));
+                // 16-byte loads from the window's first word (the rows'
+                // first word when the row has none in the window), all
+                // issued before any is used: they reach at most 4 WPR4 - 1
+                // words past a row's last word, which every pointer area
+                // has after it (WALK_PAD)
+                const uint32_t w0 = rw0[h2] < rnw[h2] ? off + (uint32_t)rw0[h2] : 0u;
+                const GlobalU8 *src = reinterpret_cast<const GlobalU8 *>(reinterpret_cast<uintptr_t>(rb[h2] + w0));
 #pragma unroll
-                for (int q = 0; q < WPR; ++q) {
-                    // every load in bounds (the side's first word when the
-                    // row is empty), all issued before any is used
-                    const int w = min(rw0[h2] + q, rnw[h2] - 1);
-                    v[h2][q] = rb[h2][rnw[h2] > 0 ? off + (uint32_t)w : 0u];
+                for (int g = 0; g < WPR4; ++g) {
+                    uint32_t t[4];
+                    load_unaligned<4>(src + 16 * g, t);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[h2][4 * g + e] = t[e];
                 }
             }
 #pragma unroll

@@ -177,6 +177,11 @@ constexpr int64_t OP_BLOCK_BYTES = ((8 * OP_HDRS + 4 * OP_BLOCK * OP_ROW_WORDS) 
 constexpr int64_t OP_ARENA = (int64_t)256 << 10;
 constexpr uint32_t OP_BLOCK_WORDS = OP_BLOCK * OP_ROW_WORDS;
 
+// Bytes kept readable after every area of pointer rows (the pool, the
+// executor's workspaces): the traceback walker loads rows in 16-byte groups
+// that may run past a row's last word.
+constexpr int64_t WALK_PAD = 256;
+
 // Entries per array of the LDS hand-over between layouts (S of two
 // diagonals and the two gap states of the union of the last two hulls,
 // which is at most 256 positions wide when a side changes layout).

@@ -854,7 +854,9 @@ static int prepare_onepass_pool(fz_ctx *ctx, int64_t n, uint64_t diags, int64_t 
         HIP_OK(hipMemGetInfo(&fr, &tot));
         uint64_t avail = (uint64_t)fr + ctx->op_pool.cap;
         for (const auto &b : ctx->ptr_ws) avail += b.cap;
-        const uint64_t cap = std::min<uint64_t>(avail / 10 * 7, (uint64_t)tot / 5 * 3);
+        // three quarters of what is available: a pool that runs short
+        // costs a round (a walk and the kernel's tail) per refill
+        const uint64_t cap = std::min<uint64_t>(avail / 4 * 3, (uint64_t)tot / 4 * 3);
         const uint64_t need = diags * (8 + 4 * 32) + (uint64_t)n * (uint64_t)(OP_ARENA + 8192) + ((uint64_t)64 << 20);
         want = std::min(need, cap);
         // a pointer-memory cap set on the context bounds the pool too
@@ -889,7 +891,7 @@ static int prepare_onepass_pool(fz_ctx *ctx, int64_t n, uint64_t diags, int64_t 
             ctx->op_pool.p = nullptr;
         }
     }
-    const uint64_t pool_bytes = ctx->op_pool.p ? std::min<uint64_t>(want, ctx->op_pool.cap) : 0;
+    const uint64_t pool_bytes = ctx->op_pool.p ? std::min<uint64_t>(want, ctx->op_pool.cap - WALK_PAD) : 0;
     // (the pool's sink and one arena at least)
     *bytes = pool_bytes >= (uint64_t)(OP_BLOCK_BYTES + OP_ARENA) ? pool_bytes : 0;
     return FZ_OK;
@@ -1260,7 +1262,7 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         const int64_t step = std::max<int64_t>(1, ws - max_item);
         const int64_t nb = (total_ptr + step - 1) / step;
         const int nbuf = (int)std::min<int64_t>(nb, EXEC_STREAMS);
-        for (int k = 0; k < nbuf; ++k) ENSURE(ctx->ptr_ws[k], ws);
+        for (int k = 0; k < nbuf; ++k) ENSURE(ctx->ptr_ws[k], ws + WALK_PAD);
         ENSURE(ctx->batch_first, (nb + 1) * sizeof(int64_t));
         fill_i64_kernel<<<blocks_for(nb + 1, 256), 256, 0, st>>>(as<int64_t>(ctx->batch_first), nb + 1, n_exec);
         HIP_OK(hipGetLastError());
