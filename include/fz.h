@@ -396,9 +396,12 @@ int fz_find_seeds(fz_ctx *ctx,
  * goes to the one-pass executor).
  * FZ_DEBUG_ONEPASS_POOL: the one-pass executor's pool is `value` bytes, so
  * that sides run out of it and go back to the inspector; 0 turns the
- * one-pass executor off, -1 restores the library's sizing.  Returns FZ_OK,
- * or FZ_EINVAL for an unknown `what` or a value out of range. */
-enum { FZ_DEBUG_SHRINK_ROWS = 1, FZ_DEBUG_ONEPASS_POOL = 2 };
+ * one-pass executor off, -1 restores the library's sizing.
+ * FZ_DEBUG_ONEPASS_ORDER: 1 (the default) launches the one-pass executor's
+ * sides longest first by a predicted length, 0 in the order the inspector
+ * handed them over (results are the same either way).  Returns FZ_OK, or
+ * FZ_EINVAL for an unknown `what` or a value out of range. */
+enum { FZ_DEBUG_SHRINK_ROWS = 1, FZ_DEBUG_ONEPASS_POOL = 2, FZ_DEBUG_ONEPASS_ORDER = 3 };
 int fz_debug_set(fz_ctx *ctx, int what, int64_t value);
 
 /* Copy the first n seeds of the last successful fz_find_seeds to dst

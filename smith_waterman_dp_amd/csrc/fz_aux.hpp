@@ -447,6 +447,151 @@ __global__ void undefer_kernel(const int32_t *list, int64_t n, SideTask *tasks)
     if (k < n) tasks[list[k]].defer_need = INT32_MAX;
 }
 
+// ------------------------------------------- one-pass launch order --
+// The one-pass executor's waves are latency-bound: a side of tens of
+// thousands of anti-diagonals takes about as long alone on the machine as
+// among others, so one started late ends the kernel long after the rest.
+// Its sides go longest first, by a predicted length: how far homology runs
+// along the side's diagonal.  The prediction follows the diagonal in steps
+// of OP_TRACK_STEP bases, comparing windows of OP_TRACK_LEN bases of A with
+// B: four windows a quarter step apart at offsets within 8 of the diagonal
+// found so far, else two at offsets within OP_TRACK_WIDE (clusters of indels
+// move the diagonal by tens of bases now and then); a window with
+// OP_TRACK_HIT (OP_TRACK_HIT_WIDE) or more equal bases at some offset is
+// homology there (the offset becomes the diagonal).  OP_TRACK_MISS steps in a row without homology end it (an
+// alignment under a y-drop of thousands bridges shorter unrelated
+// stretches; a long side predicted short costs more than the reverse), and
+// so does the window's end.  The key is the predicted length in units of
+// 4 steps.  Only the order of the sides depends on it, not any result.
+constexpr int OP_TRACK_STEP = 256;
+constexpr int OP_TRACK_LEN = 32;
+constexpr int OP_TRACK_HIT = 17;            // 53% (random sequence: 25%), kept low: diverged stretches
+                                            // still extend an alignment
+constexpr int OP_TRACK_HIT_WIDE = 19;       // (8 times the offsets: fewer chance hits)
+constexpr int OP_TRACK_MISS = 3;
+constexpr int OP_TRACK_WIDE = 128;
+constexpr int OP_TRACK_WIDE0 = 320;
+constexpr int OP_TRACK_MAX = 64;            // steps (16 kb: longer sides all go first, early enough
+                                            // that even the longest windows end with the rest)
+constexpr int OP_KEYS = 64;
+
+// Equal bases of a[0 .. OP_TRACK_LEN - 1] (A, ascending) and b[0], b[-1],
+// .., b[-(OP_TRACK_LEN - 1)] (B, descending addresses), with 16-byte loads.
+__device__ __forceinline__ int window_matches(const GlobalU8 *a, const GlobalU8 *b)
+{
+    constexpr int NW = OP_TRACK_LEN / 4;
+    uint32_t va[NW], vb[NW];
+#pragma unroll
+    for (int h = 0; h < NW / 4; ++h) {
+        load_unaligned<4>(a + 16 * h, *reinterpret_cast<uint32_t(*)[4]>(&va[4 * h]));
+        load_unaligned<4>(b - (OP_TRACK_LEN - 1) + 16 * h, *reinterpret_cast<uint32_t(*)[4]>(&vb[4 * h]));
+    }
+    int cnt = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        // B's dword NW - 1 - w holds positions 4w + 3 .. 4w in memory order
+        const uint32_t x = va[w] ^ __builtin_amdgcn_perm(0u, vb[NW - 1 - w], 0x00010203u);
+        const uint32_t z = ~(((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;     // a byte's top bit: it is 0
+        cnt += __builtin_popcount(z);
+    }
+    return cnt;
+}
+
+// One wave per side, OP_KEY_WAVES sides per workgroup (tiny workgroups
+// would cap the resident waves below what hides the loads' latency).
+constexpr int OP_KEY_WAVES = 4;
+__global__ __launch_bounds__(64 * OP_KEY_WAVES) void op_key_kernel(const int32_t *__restrict__ list, int64_t n,
+                                                                   const SideTask *__restrict__ tasks,
+                                                                   uint8_t *__restrict__ key,
+                                                                   uint32_t *__restrict__ hist)
+{
+    const int64_t k = (int64_t)blockIdx.x * OP_KEY_WAVES + uniform((int)(threadIdx.x / 64));
+    if (k >= n) return;
+    const int lane = lane_id();
+    const SideTask t = tasks[list[k]];
+    // base i of the side's A at A[i], base j of its B at B[-j] (1-based)
+    const GlobalU8 *A = reinterpret_cast<const GlobalU8 *>(reinterpret_cast<uintptr_t>(t.A + t.abase));
+    const GlobalU8 *B = reinterpret_cast<const GlobalU8 *>(reinterpret_cast<uintptr_t>(t.B + t.bbase));
+    const int lim = min(t.m, t.n);
+    const int g = lane >> 4, o = (lane & 15) - 8;
+    // windows at i = x .. x + LEN - 1 and j = x + delta .. x + delta + LEN
+    // - 1: in [1, lim] when x + LEN - 1 + |delta| <= lim and x + delta >= 1
+    auto count = [&](int x, int delta) -> int {
+        return x + delta >= 1 ? window_matches(A + x, B - (x + delta)) : 0;
+    };
+    int center = 0, steps = 0, miss = 0;
+    for (int s = 1; s <= OP_TRACK_MAX; ++s) {
+        const int xs = OP_TRACK_STEP * s;
+        constexpr int Q = OP_TRACK_STEP / 4;
+        // (the first step searches wider: the alignment may have opened a gap
+        // of a few hundred bases near the seed)
+        const int wide = s == 1 ? OP_TRACK_WIDE0 : OP_TRACK_WIDE;
+        if (xs + 3 * Q + OP_TRACK_LEN + abs(center) + wide > lim) {
+            steps = s;                  // the window's end
+            break;
+        }
+        int delta = center + o;
+        int c = count(xs + Q * g, delta);
+        int best = c >= OP_TRACK_HIT ? c : 0, bdelta = delta;
+        if (ballot(best > 0) == 0) {
+            for (int d0 = -wide; d0 < wide; d0 += 64) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    delta = center + d0 + lane;
+                    c = count(xs + 2 * Q * h, delta);
+                    if (c >= OP_TRACK_HIT_WIDE && c > best) {
+                        best = c;
+                        bdelta = delta;
+                    }
+                }
+            }
+        }
+        if (ballot(best > 0)) {
+            // the offset of the most equal bases
+            const int top = wave_max(best);
+            center = __builtin_amdgcn_readlane(bdelta, ctz64(ballot(best == top)));
+            steps = s;
+            miss = 0;
+        } else if (++miss == OP_TRACK_MISS) {
+            break;
+        }
+    }
+    if (lane == 0) {
+        const int kk = min(OP_KEYS - 1, steps >> 2);
+        key[k] = (uint8_t)kk;
+        atomicAdd(&hist[kk], 1u);
+    }
+}
+
+// list[k] to out in descending key order (hist: the keys' counts; cur:
+// zeroed cursors; the order within a key is arbitrary).  Blocks of 256
+// count their keys in LDS and take one range per key.
+__global__ __launch_bounds__(256) void op_order_kernel(const int32_t *__restrict__ list, int64_t n,
+                                                       const uint8_t *__restrict__ key,
+                                                       const uint32_t *__restrict__ hist, uint32_t *__restrict__ cur,
+                                                       int32_t *__restrict__ out)
+{
+    __shared__ uint32_t lcnt[OP_KEYS], lbase[OP_KEYS];
+    const int tid = (int)threadIdx.x;
+    if (tid < OP_KEYS) lcnt[tid] = 0;
+    __syncthreads();
+    const int64_t k = (int64_t)blockIdx.x * 256 + tid;
+    int kk = -1;
+    uint32_t lpos = 0;
+    if (k < n) {
+        kk = key[k];
+        lpos = atomicAdd(&lcnt[kk], 1u);
+    }
+    __syncthreads();
+    if (tid < OP_KEYS) {
+        uint32_t base = 0;
+        for (int b = OP_KEYS - 1; b > tid; --b) base += hist[b];
+        lbase[tid] = lcnt[tid] ? base + atomicAdd(&cur[tid], lcnt[tid]) : 0u;
+    }
+    __syncthreads();
+    if (kk >= 0) out[lbase[kk] + lpos] = list[k];
+}
+
 __global__ void fill_i64_kernel(int64_t *p, int64_t n, int64_t v)
 {
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;

@@ -66,6 +66,8 @@ struct Counters {
         uint32_t fail, done;
         uint64_t pool_used;
     } op_round;
+    uint32_t op_key_hist[OP_KEYS];          // one-pass launch order: keys' counts, then cursors
+    uint32_t op_key_cur[OP_KEYS];
 };
 
 // One wave per workgroup for the wave-per-side kernels: sides differ in
@@ -135,6 +137,7 @@ struct fz_ctx {
     uint64_t ptr_cap = 0;               // 0 = default
     int64_t dbg_shrink_rows = 0;        // fz_debug_set(FZ_DEBUG_SHRINK_ROWS)
     int64_t dbg_op_pool = -1;           // fz_debug_set(FZ_DEBUG_ONEPASS_POOL): pool bytes (-1: sized by the library)
+    int64_t dbg_op_order = 1;           // fz_debug_set(FZ_DEBUG_ONEPASS_ORDER): predicted longest first (0: as deferred)
     std::vector<hipEvent_t> walk_ev;    // brackets of the walker launches (FZ_STATS)
     uint64_t last_words = 0;            // CIGAR words of the last successful call
     DevBuf Tf, Tr, Qf, Qr;
@@ -145,7 +148,7 @@ struct fz_ctx {
     DevBuf ptr_ws[EXEC_STREAMS];        // one pointer workspace per executor stream
     // one-pass executor: deferred sides, sides given back, block tables (by
     // side), the pool of row blocks
-    DevBuf defer_list, op_fail, op_btab, op_pool;
+    DevBuf defer_list, op_fail, op_btab, op_pool, op_key, op_order;
     // one-pass rounds: the other round's list of sides given back, the
     // finished sides, their walk items, the walks' scratch (a run per move
     // at most), and the runs of sides walked before the pool was used again,
@@ -782,7 +785,7 @@ void fz_destroy(fz_ctx *ctx)
                       &ctx->rd_off, &ctx->rd_cig, &ctx->sg_key, &ctx->sg_key2, &ctx->sg_end, &ctx->sg_end2,
                       &ctx->sg_v, &ctx->sg_max, &ctx->rs_cnt, &ctx->ps_tmp, &ctx->defer_list, &ctx->op_fail,
                       &ctx->op_btab, &ctx->op_pool, &ctx->op_fail2, &ctx->op_done, &ctx->op_items,
-                      &ctx->op_runs_tmp, &ctx->op_runs, &ctx->op_run_off};
+                      &ctx->op_runs_tmp, &ctx->op_runs, &ctx->op_run_off, &ctx->op_key, &ctx->op_order};
     for (auto &x : ctx->xs)
         if (x) (void)hipStreamSynchronize(x);
     if (ctx->xw) (void)hipStreamSynchronize(ctx->xw);
@@ -828,6 +831,10 @@ int fz_debug_set(fz_ctx *ctx, int what, int64_t value)
         ctx->dbg_op_pool = value;
         return FZ_OK;
     }
+    if (what == FZ_DEBUG_ONEPASS_ORDER && (value == 0 || value == 1)) {
+        ctx->dbg_op_order = value;
+        return FZ_OK;
+    }
     return fail(ctx, FZ_EINVAL, "unknown debug setting or value out of range");
 }
 
@@ -836,8 +843,8 @@ static int grow_keep(fz_ctx *ctx, DevBuf &b, size_t bytes, size_t keep, hipStrea
 // The one-pass executor's pool, sized for n deferred sides whose windows
 // hold `diags` anti-diagonals in all (each side m + n + 1): a 256-position
 // row with its header per anti-diagonal, plus an arena and a block table
-// per side; at most 7/10 of the free device memory (this context's pointer
-// workspaces counted as free, and released when the pool must grow), 3/5
+// per side; at most 3/4 of the free device memory (this context's pointer
+// workspaces counted as free, and released when the pool must grow), 3/4
 // of the device, and the context's pointer-memory cap.  *bytes is the
 // pool's usable size, 0 when there is none (too little memory: the deferred
 // sides then go back to the inspector).
@@ -1078,6 +1085,21 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         ENSURE(ctx->run_len, nsides * sizeof(int64_t));
         const int32_t *L = as<int32_t>(ctx->defer_list);
         uint32_t nL = hc.defer_count;
+        if (nL > 1 && ctx->dbg_op_order) {
+            // longest sides first (predicted)
+            ENSURE(ctx->op_key, (int64_t)nL);
+            ENSURE(ctx->op_order, (int64_t)nL * sizeof(int32_t));
+            rc = zero(ctx, dc->op_key_hist, 2 * OP_KEYS * sizeof(uint32_t), st);
+            if (rc) return rc;
+            op_key_kernel<<<blocks_for(nL, OP_KEY_WAVES), 64 * OP_KEY_WAVES, 0, st>>>(
+                L, (int64_t)nL, as<SideTask>(ctx->tasks), as<uint8_t>(ctx->op_key), dc->op_key_hist);
+            HIP_OK(hipGetLastError());
+            op_order_kernel<<<blocks_for(nL, 256), 256, 0, st>>>(L, (int64_t)nL, as<uint8_t>(ctx->op_key),
+                                                                 dc->op_key_hist, dc->op_key_cur,
+                                                                 as<int32_t>(ctx->op_order));
+            HIP_OK(hipGetLastError());
+            L = as<int32_t>(ctx->op_order);
+        }
         const int32_t *back = nullptr;
         uint32_t n_back = 0;
         if (pool_bytes == 0) {

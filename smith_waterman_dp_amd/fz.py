@@ -17,7 +17,7 @@ FZ_OK, FZ_EINVAL, FZ_ENOMEM, FZ_EDEVICE = 0, -1, -2, -3
 FZ_HIT_TRACED, FZ_HIT_EAGER_LEFT, FZ_HIT_EAGER_RIGHT = 1, 2, 4
 FZ_HIT_BELOW_MIN, FZ_HIT_EBAND, FZ_HIT_ESEED, FZ_HIT_ERANGE = 8, 16, 32, 64
 FZ_HIT_COVERED, FZ_HIT_EEXEC, FZ_HIT_WIDE = 128, 256, 512
-FZ_DEBUG_SHRINK_ROWS, FZ_DEBUG_ONEPASS_POOL = 1, 2
+FZ_DEBUG_SHRINK_ROWS, FZ_DEBUG_ONEPASS_POOL, FZ_DEBUG_ONEPASS_ORDER = 1, 2, 3
 FZ_YDROP_INF = 2147483647
 FZ_NOALLOC_MAX_SEEDS, FZ_NOALLOC_MAX_BASES = 65536, 4194304
 

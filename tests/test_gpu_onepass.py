@@ -153,6 +153,19 @@ def test_onepass_pool_off(ctx, heavy):
     same(a, b, "pool off")
 
 
+def test_onepass_launch_order(ctx, heavy):
+    """The one-pass sides go longest first by a predicted length; in the
+    order the inspector handed them over the results are the same."""
+    a = run(ctx, heavy, False, label="order predicted")
+    fz.fz_debug_set(ctx.h, fz.FZ_DEBUG_ONEPASS_ORDER, 0)
+    try:
+        b = run(ctx, heavy, False, label="order as handed over")
+    finally:
+        fz.fz_debug_set(ctx.h, fz.FZ_DEBUG_ONEPASS_ORDER, 1)
+    assert a[2]["n_onepass"] == b[2]["n_onepass"] > 0
+    same(a, b, "launch order")
+
+
 def test_onepass_under_workspace_cap(ctx, heavy):
     """A 4 MiB pointer-memory cap bounds the pool too (many rounds), the
     same results."""
