@@ -57,6 +57,8 @@ struct SeedInfo {
     int64_t seed_score;
     int64_t status;
 };
+// (the wide retry reads seed_score through ExtendArgs::info as int64 pairs)
+static_assert(sizeof(SeedInfo) == 16 && offsetof(SeedInfo, seed_score) == 0, "SeedInfo layout");
 
 // T16f .. Q16r: the 16-bit copies of the packed layouts (may be null when
 // they are not used).
@@ -134,10 +136,11 @@ __device__ __forceinline__ int exec_class(int32_t flags)
     return (flags & SO_ONEPASS) ? EXEC_CLASS_ONEPASS : (flags & SO_WIDE_FLAG) ? EXEC_CLASS_WIDE : EXEC_CLASS_STD;
 }
 
+constexpr int SHORT_BIN_LEN = 512;          // the shortest executor bin: sides of at most this length
 __device__ __forceinline__ int bin_of(int64_t len)
 {
     int b = 0;
-    int64_t edge = 512;
+    int64_t edge = SHORT_BIN_LEN;
     while (len > edge && b < NBINS - 1) {
         edge *= 4;
         ++b;
@@ -208,6 +211,7 @@ __global__ void combine_kernel(CombineArgs a)
     h.bin = -1;
     int tr[2] = {0, 0};
     int bkey[2] = {0, 0};
+    bool binned[2] = {false, false};
     uint64_t pmax = 0, bmax = 0;
     fz_seed s = {};
     SeedInfo in = {0, 0};
@@ -251,8 +255,9 @@ __global__ void combine_kernel(CombineArgs a)
                         const int64_t len = max(sd[q]->ie, sd[q]->je);
                         const int cls = exec_class(sd[q]->flags);
                         bkey[q] = cls * NBINS + bin_of(len);
-                        // (one-pass sides have their rows already)
-                        if (cls != EXEC_CLASS_ONEPASS) pmax = max(pmax, (uint64_t)sd[q]->ptr_bytes);
+                        binned[q] = !(sd[q]->flags & SO_EARLY);     // (early sides: walked from their own list)
+                        // (one-pass and early sides have their rows already)
+                        if (cls != EXEC_CLASS_ONEPASS && binned[q]) pmax = max(pmax, (uint64_t)sd[q]->ptr_bytes);
                         longest = max(longest, len);
                     }
                 }
@@ -271,7 +276,7 @@ __global__ void combine_kernel(CombineArgs a)
         if (cmax) atomicMax((unsigned long long *)a.max_ptr, (unsigned long long)cmax);
         if (wmax) atomicMax((unsigned long long *)a.max_band, (unsigned long long)wmax);
     }
-    for (int q = 0; q < 2; ++q) (void)wave_grouped_inc(a.bin_count, bkey[q], tr[q] == 2);
+    for (int q = 0; q < 2; ++q) (void)wave_grouped_inc(a.bin_count, bkey[q], tr[q] == 2 && binned[q]);
     if (!valid) return;
     for (int q = 0; q < 2; ++q) {
         const SideOut &o = q == 0 ? L : R;
@@ -289,11 +294,12 @@ __global__ void bin_scatter_kernel(int64_t nsides, const int32_t *side_trace, co
                                    int64_t shrink_words)
 {
     const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const bool active = s < nsides && side_trace[s] == 2;
+    bool active = s < nsides && side_trace[s] == 2;
     SideOut o = {};
     int b = 0;
     if (active) {
         o = out[s];
+        active = !(o.flags & SO_EARLY);         // (as the combine counted)
         b = exec_class(o.flags) * NBINS + bin_of(max(o.ie, o.je));
     }
     const uint32_t r = wave_grouped_inc(bin_fill, b, active);     // every lane of the wave
@@ -437,6 +443,37 @@ __global__ void op_run_pack_kernel(const ExecItem *items, int64_t n, const uint3
     const int64_t dst = base + it.ptr_bytes;
     for (int64_t q = 0; q < it.batch; ++q) runs[dst + q] = scratch[it.ptr_off + q];
     op_run_off[it.side] = dst;
+}
+
+// Traced sides the inspector finished that are longer than the shortest
+// executor bin join the one-pass executor's list: there they are swept once
+// more with their rows among the other one-pass sides, longest first,
+// instead of as two-pass executor waves that end a batch alone, and walked
+// with them.  A seed with a deferred side is certain to be traced; one whose
+// sides both finished is traced when its score passes min_tb (as the
+// combine decides).  Seeds with an overflowed side (its wide retry still to
+// come) are left to the two-pass path.
+__global__ void onepass_pick_kernel(int64_t n, const SeedInfo *__restrict__ info, SideOut *__restrict__ out,
+                                    const SideTask *__restrict__ tasks, int64_t min_tb, int32_t min_len,
+                                    int32_t *__restrict__ defer_list, uint32_t *__restrict__ defer_count,
+                                    unsigned long long *__restrict__ defer_diags)
+{
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= n || info[k].status) return;
+    const SideOut L = out[2 * k], R = out[2 * k + 1];
+    if ((L.flags | R.flags) & (SO_OVERFLOW | SO_SKIPPED)) return;
+    const bool traced = ((L.flags | R.flags) & SO_DEFERRED) ||
+                        (int64_t)L.score + info[k].seed_score + R.score > min_tb;
+    if (!traced) return;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const SideOut &o = q ? R : L;
+        if ((o.flags & (SO_DEFERRED | SO_EAGER)) || max(o.ie, o.je) <= min_len) continue;
+        const int64_t sid = 2 * k + q;
+        out[sid].flags = SO_DEFERRED;
+        defer_list[atomicAdd(defer_count, 1u)] = (int32_t)sid;
+        atomicAdd(defer_diags, (unsigned long long)((int64_t)tasks[sid].m + tasks[sid].n + 1));
+    }
 }
 
 // Sides the one-pass executor gave back (pool exhausted): the inspector
@@ -622,6 +659,7 @@ struct WalkArgs {
     const int64_t *run_off;
     uint32_t *runs;
     int64_t *run_len;
+    const int32_t *side_trace;  // (early list) items whose side is not traced through the executor are skipped
 };
 
 __device__ __forceinline__ void rle_push(uint32_t *runs, int64_t &n, uint32_t &cur_op, uint32_t &cur_len, uint32_t op)
@@ -674,6 +712,7 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
     const int64_t k = a.begin + (int64_t)blockIdx.x;
     if (k >= a.end) return;
     const ExecItem it = a.items[k];
+    if (a.side_trace && a.side_trace[it.side] != 2) return;
     const SideOut o = a.out[it.side];
     const uint8_t *base = OP ? nullptr : a.ptr_ws + (it.ptr_off - a.ptr_base_off);
     const RowHdr *hdr = reinterpret_cast<const RowHdr *>(base);

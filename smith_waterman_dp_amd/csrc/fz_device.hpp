@@ -111,9 +111,12 @@ struct SideTask {
 // SO_WALKED: ... and it was walked at once, its runs in the one-pass runs
 // buffer (an earlier round of a batch whose one-pass rows did not all fit
 // the pool at once).
+// SO_EARLY: a side of the wide retry that the retry's wave also traced (its
+// rows in the early workspace, an item of the early list); it is only
+// walked with the other executor sides.
 enum : int32_t {
     SO_OVERFLOW = 1, SO_EAGER = 2, SO_SKIPPED = 4, SO_EXEC_MISMATCH = 8, SO_WIDE_FLAG = 16,
-    SO_DEFERRED = 32, SO_ONEPASS = 64, SO_WALKED = 128
+    SO_DEFERRED = 32, SO_ONEPASS = 64, SO_WALKED = 128, SO_EARLY = 256
 };
 
 struct SideOut {

@@ -63,6 +63,16 @@ struct ExtendArgs {
     uint32_t *op_fail_count;
     int32_t *op_done_list;      // ... and the sides it finished
     uint32_t *op_done_count;
+    // the wide retry beside the one-pass executor: a side whose seed is then
+    // certain to be traced gets its rows in the same wave (SO_EARLY), in the
+    // early workspace (early_bytes taken of early_cap), listed in early_items
+    uint8_t *early_ws;
+    uint64_t early_cap;
+    unsigned long long *early_bytes;
+    ExecItem *early_items;
+    uint32_t *early_count;
+    const void *info;           // the seeds' SeedInfo (seed scores)
+    int64_t min_tb;
     Scoring sc;
 };
 

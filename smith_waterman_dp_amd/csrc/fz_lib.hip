@@ -68,6 +68,10 @@ struct Counters {
     } op_round;
     uint32_t op_key_hist[OP_KEYS];          // one-pass launch order: keys' counts, then cursors
     uint32_t op_key_cur[OP_KEYS];
+    struct {
+        uint32_t count, pad;                // the wide retry's sides traced beside the one-pass executor
+        uint64_t bytes;                     // their rows' workspace
+    } early;
 };
 
 // One wave per workgroup for the wave-per-side kernels: sides differ in
@@ -148,7 +152,7 @@ struct fz_ctx {
     DevBuf ptr_ws[EXEC_STREAMS];        // one pointer workspace per executor stream
     // one-pass executor: deferred sides, sides given back, block tables (by
     // side), the pool of row blocks
-    DevBuf defer_list, op_fail, op_btab, op_pool, op_key, op_order;
+    DevBuf defer_list, op_fail, op_btab, op_pool, op_key, op_order, early_items, early_ws;
     // one-pass rounds: the other round's list of sides given back, the
     // finished sides, their walk items, the walks' scratch (a run per move
     // at most), and the runs of sides walked before the pool was used again,
@@ -785,7 +789,8 @@ void fz_destroy(fz_ctx *ctx)
                       &ctx->rd_off, &ctx->rd_cig, &ctx->sg_key, &ctx->sg_key2, &ctx->sg_end, &ctx->sg_end2,
                       &ctx->sg_v, &ctx->sg_max, &ctx->rs_cnt, &ctx->ps_tmp, &ctx->defer_list, &ctx->op_fail,
                       &ctx->op_btab, &ctx->op_pool, &ctx->op_fail2, &ctx->op_done, &ctx->op_items,
-                      &ctx->op_runs_tmp, &ctx->op_runs, &ctx->op_run_off, &ctx->op_key, &ctx->op_order};
+                      &ctx->op_runs_tmp, &ctx->op_runs, &ctx->op_run_off, &ctx->op_key, &ctx->op_order,
+                      &ctx->early_items, &ctx->early_ws};
     for (auto &x : ctx->xs)
         if (x) (void)hipStreamSynchronize(x);
     if (ctx->xw) (void)hipStreamSynchronize(ctx->xw);
@@ -1046,17 +1051,41 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     rc = launch_extend<C_STD, false>(ctx, ea, nsides, st, pk);
     if (rc) return rc;
     HIP_OK(hipEventRecord(ctx->kev[1], st));
+    if (defer_on) {
+        onepass_pick_kernel<<<blocks_for(n, 256), 256, 0, st>>>(
+            n, as<SeedInfo>(ctx->info), as<SideOut>(ctx->out), as<SideTask>(ctx->tasks), min_tb, SHORT_BIN_LEN,
+            as<int32_t>(ctx->defer_list), &dc->defer_count, reinterpret_cast<unsigned long long *>(&dc->defer_diags));
+        HIP_OK(hipGetLastError());
+    }
     if ((rc = read_counters())) return rc;
     if (hc.err & 1u) return fail(ctx, FZ_EINVAL, "%s", bad_byte_msg(sc));
     // wide retry (the 1024-position window, a few long latency-bound waves)
     // of the overflow list [first, first + count)
-    auto wide_retry = [&](uint32_t first, uint32_t count, hipStream_t ws) -> int {
+    auto wide_retry = [&](uint32_t first, uint32_t count, hipStream_t ws, bool early) -> int {
         ExtendArgs wa = ea;
         wa.list = as<int32_t>(ctx->ovl0) + first;
         wa.nlist = (int32_t)count;
         wa.overflow_list = as<int32_t>(ctx->ovl1);
         wa.overflow_count = &dc->overflow_count[1];
         wa.result_flags = SO_WIDE_FLAG;
+        if (early && (flags & FZ_TRACEBACK)) {
+            // beside the one-pass executor: sides certain to be traced are
+            // traced in the retry's own wave (a handful of long waves that
+            // would otherwise end the executor phase alone)
+            size_t fr = 0, tot = 0;
+            HIP_OK(hipMemGetInfo(&fr, &tot));
+            uint64_t cap = std::min<uint64_t>((uint64_t)2 << 30, (uint64_t)fr / 16);
+            if (ctx->ptr_cap) cap = std::min<uint64_t>(cap, ctx->ptr_cap);     // (a pointer-memory cap bounds it too)
+            ENSURE(ctx->early_items, (int64_t)count * sizeof(ExecItem));
+            ENSURE(ctx->early_ws, (int64_t)cap + WALK_PAD);
+            wa.early_ws = as<uint8_t>(ctx->early_ws);
+            wa.early_cap = std::min<uint64_t>(cap, ctx->early_ws.cap - WALK_PAD);
+            wa.early_bytes = reinterpret_cast<unsigned long long *>(&dc->early.bytes);
+            wa.early_items = as<ExecItem>(ctx->early_items);
+            wa.early_count = &dc->early.count;
+            wa.info = as<SeedInfo>(ctx->info);
+            wa.min_tb = min_tb;
+        }
         return launch_extend<C_WIDE, false>(ctx, wa, wa.nlist, ws);
     };
     // the inspector's overflow sides go to the wide retry beside the
@@ -1066,9 +1095,10 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     if (n_ovl_first > 0) {
         HIP_OK(hipEventRecord(ctx->fork_ev, st));
         HIP_OK(hipStreamWaitEvent(ctx->xw, ctx->fork_ev, 0));
-        if ((rc = wide_retry(0, n_ovl_first, ctx->xw))) return rc;
+        if ((rc = wide_retry(0, n_ovl_first, ctx->xw, true))) return rc;
     }
     bool onepass_ran = false;
+    int64_t n_early = 0;                // the wide retry's sides traced beside the one-pass executor
     if (hc.defer_count > 0) {
         // ---- one-pass executor over the deferred sides, in rounds: when the
         // pool cannot hold all their rows at once, the sides a round
@@ -1185,7 +1215,8 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         }
     }
     S.n_overflow = hc.overflow_count[0];
-    if (hc.overflow_count[0] > n_ovl_first && (rc = wide_retry(n_ovl_first, hc.overflow_count[0] - n_ovl_first, st)))
+    if (hc.overflow_count[0] > n_ovl_first &&
+        (rc = wide_retry(n_ovl_first, hc.overflow_count[0] - n_ovl_first, st, false)))
         return rc;
     if (n_ovl_first > 0) {
         HIP_OK(hipEventRecord(ctx->wide_ev, ctx->xw));
@@ -1256,6 +1287,26 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
                                                                as<int64_t>(ctx->run_len));
     HIP_OK(hipGetLastError());
     tm.mark();
+
+    // the early list's traced sides (their rows written by the wide retry
+    // beside the one-pass executor; the stream joined the retry's after it)
+    n_early = (int64_t)hc.early.count;
+    if (n_early > 0) {
+        WalkArgs wk = {};
+        wk.items = as<ExecItem>(ctx->early_items);
+        wk.begin = 0;
+        wk.end = n_early;
+        wk.ptr_ws = as<uint8_t>(ctx->early_ws);
+        wk.ptr_base_off = 0;
+        wk.out = as<SideOut>(ctx->out);
+        wk.run_off = as<int64_t>(ctx->run_off);
+        wk.runs = as<uint32_t>(ctx->runs);
+        wk.run_len = as<int64_t>(ctx->run_len);
+        wk.side_trace = as<int32_t>(ctx->side_trace);
+        walk_wave_kernel<false><<<(unsigned)n_early, 64, 0, st>>>(wk);
+        HIP_OK(hipGetLastError());
+        S.n_executor += (uint64_t)n_early;
+    }
 
     // ---- execute + walk, in batches
     size_t n_walks = 0;

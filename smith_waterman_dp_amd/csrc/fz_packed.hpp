@@ -889,6 +889,11 @@ template <int C, bool EXEC, int SUB, int WAVES, bool PK = false, bool ONEPASS = 
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <= 8 ? (EXEC ? (PK ? (ONEPASS ? 7 : 8) : SUB != SUB_WIDE ? 7 : 6) : 8) : 1))) void extend_kernel(ExtendArgs a)
 {
     static_assert(!ONEPASS || (EXEC && PK && WAVES == 1), "the one-pass executor runs the packed layouts, one wave per group");
+    // The 1024-position kernels (the wide retry and its executor) run a
+    // handful of long latency-bound waves beside the one-pass executor's
+    // thousands: they take the SIMD's issue first, else each would get an
+    // eighth of it and end long after the one-pass sides.
+    if constexpr (C > 8) __builtin_amdgcn_s_setprio(3);
     using DP = SideDP<C, EXEC, SUB>;
     using EDP = SideDP<StartLayout<C>::value, EXEC, SUB>;     // holds the eager block
     __shared__ uint32_t eager_lds_all[WAVES][EAGER_ROWS * EDP::NEL * EDP::NWORD];
@@ -990,6 +995,43 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <=
         e.bj = x.bj;
         r.flags |= SO_EAGER;
         r.eager_len = e.eager_walk(eager_lds, a.eager_ops + (int64_t)sid * EAGER_OPS);
+    }
+    if constexpr (C > 8 && !EXEC) {
+        // (the wide retry beside the one-pass executor) a side whose seed is
+        // now certain to be traced is traced at once: the executor sweeps it
+        // again to its best cell in this wave, into the early workspace.  The
+        // other side is final unless it is in this retry too (then the side
+        // waits for the executor phase); a torn read of it only changes
+        // which path traces the side, the walk takes traced sides only.
+        if (a.early_items && !x.overflow && !(r.flags & SO_EAGER)) {
+            const SideOut p = a.out[sid ^ 1];
+            const int64_t seed_score = reinterpret_cast<const int64_t *>(a.info)[2 * (sid >> 1)];
+            bool traced = (p.flags & SO_DEFERRED) != 0;
+            if (!traced && !(p.flags & (SO_OVERFLOW | SO_SKIPPED)))
+                traced = (int64_t)x.best + seed_score + p.score > a.min_tb;
+            if (traced) {
+                const uint64_t need = ((uint64_t)x.ptr_at_best + 15) & ~(uint64_t)15;
+                uint64_t off = 0;
+                if (fresh_lane_id() == 0) off = atomicAdd(a.early_bytes, (unsigned long long)need);
+                off = uniform64(off);
+                if (off + need <= a.early_cap) {
+                    const SideResult e = run_side<C, true, SUB>(task, a.sc, x.bi + x.bj, nullptr, xfer,
+                                                                a.early_ws + off, x.ptr_at_best);
+                    r.flags |= SO_EARLY;
+                    if (e.overflow || e.best != x.best || e.bi != x.bi) r.flags |= SO_EXEC_MISMATCH;
+                    if (fresh_lane_id() == 0) {
+                        atomicAdd((unsigned long long *)a.exec_cells, (unsigned long long)e.cells);
+                        ExecItem it;
+                        it.side = sid;
+                        it.dstar = x.bi + x.bj;
+                        it.ptr_off = (int64_t)off;
+                        it.ptr_bytes = x.ptr_at_best;
+                        it.batch = 0;
+                        a.early_items[atomicAdd(a.early_count, 1u)] = it;
+                    }
+                }
+            }
+        }
     }
     if (fresh_lane_id() == 0) {
         *o = r;
