@@ -543,6 +543,7 @@ def main():
         cfg["onepass_sides"] = int(st["n_onepass"])
         cfg["onepass_cells"] = int(st["onepass_cells"])
         cfg["onepass_pool_bytes"] = int(st["onepass_bytes"])
+        cfg["tail_walked_sides"] = int(st["n_tail_walked"])
         cfg["phase_ms"] = {k[3:]: round(float(st[k]), 1) for k in
                            ("ms_pack", "ms_inspect", "ms_onepass", "ms_bin", "ms_exec", "ms_walk", "ms_gather")}
         cfg["max_band"] = int(st["max_band"])

@@ -122,6 +122,8 @@ typedef struct {
                                     * count them */
     uint64_t onepass_cells;        /* their canonical cells (all of them, best to band's end too) */
     uint64_t onepass_bytes;        /* pool bytes their row blocks, block tables and arenas took */
+    uint64_t n_tail_walked;        /* one-pass sides walked while the one-pass executor still ran
+                                    * (FZ_DEBUG_TAIL_WALK) */
     float ms_pack, ms_inspect, ms_bin, ms_exec, ms_walk, ms_gather;
                                    /* phase spans between HIP events on the call's stream;
                                     * ms_inspect includes the one-pass executor; ms_walk is the
@@ -399,9 +401,16 @@ int fz_find_seeds(fz_ctx *ctx,
  * one-pass executor off, -1 restores the library's sizing.
  * FZ_DEBUG_ONEPASS_ORDER: 1 (the default) launches the one-pass executor's
  * sides longest first by a predicted length, 0 in the order the inspector
- * handed them over (results are the same either way).  Returns FZ_OK, or
- * FZ_EINVAL for an unknown `what` or a value out of range. */
-enum { FZ_DEBUG_SHRINK_ROWS = 1, FZ_DEBUG_ONEPASS_POOL = 2, FZ_DEBUG_ONEPASS_ORDER = 3 };
+ * handed them over (results are the same either way).
+ * FZ_DEBUG_TAIL_WALK: 1 (the default) walks the one-pass sides that have
+ * finished while the one-pass executor's last waves still run (the tail
+ * walk), 0 walks every one-pass side after it, 2 runs the tail walk after
+ * the executor (so that it takes every side whose runs fit), a larger value
+ * runs it after the executor with at most `value` run words for all sides
+ * (the rest fall back to the later walk); results are the same in every
+ * case.  Returns FZ_OK, or FZ_EINVAL for an unknown `what` or a value out
+ * of range. */
+enum { FZ_DEBUG_SHRINK_ROWS = 1, FZ_DEBUG_ONEPASS_POOL = 2, FZ_DEBUG_ONEPASS_ORDER = 3, FZ_DEBUG_TAIL_WALK = 4 };
 int fz_debug_set(fz_ctx *ctx, int what, int64_t value);
 
 /* Copy the first n seeds of the last successful fz_find_seeds to dst

@@ -417,7 +417,8 @@ __global__ void op_items_kernel(const int32_t *done, int64_t n, SideOut *out, Ex
     it.side = s;
     it.dstar = o.ie + o.je;
     it.ptr_off = 0;
-    it.ptr_bytes = (int64_t)o.ie + o.je + 1;
+    // (a tail-walked side has its runs already: no scratch)
+    it.ptr_bytes = (o.flags & SO_TAIL) ? 0 : (int64_t)o.ie + o.je + 1;
     it.batch = 0;
     items[k] = it;
     out[s].flags = o.flags | SO_WALKED;
@@ -432,17 +433,22 @@ __global__ void op_run_count_kernel(ExecItem *items, int64_t n, const int64_t *r
 }
 
 // Copy each walked side's runs from the round's scratch (at its item's
-// ptr_off, capacity ie + je + 1) to the one-pass runs buffer, packed (at
-// base + the scanned count, kept in the item's ptr_bytes field).
-__global__ void op_run_pack_kernel(const ExecItem *items, int64_t n, const uint32_t *scratch, uint32_t *runs,
-                                   int64_t base, int64_t *op_run_off)
+// ptr_off, capacity ie + je + 1), or from the tail buffer for a side the tail
+// walk took (at op_run_off), to the one-pass runs buffer, packed (at base +
+// the scanned count, kept in the item's ptr_bytes field).
+__global__ void op_run_pack_kernel(const ExecItem *items, int64_t n, const uint32_t *scratch,
+                                   const uint32_t *tail_runs, SideOut *out, uint32_t *runs, int64_t base,
+                                   int64_t *op_run_off)
 {
     const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= n) return;
     const ExecItem it = items[k];
     const int64_t dst = base + it.ptr_bytes;
-    for (int64_t q = 0; q < it.batch; ++q) runs[dst + q] = scratch[it.ptr_off + q];
+    const int32_t fl = out[it.side].flags;
+    const uint32_t *src = (fl & SO_TAIL) ? tail_runs + op_run_off[it.side] : scratch + it.ptr_off;
+    for (int64_t q = 0; q < it.batch; ++q) runs[dst + q] = src[q];
     op_run_off[it.side] = dst;
+    if (fl & SO_TAIL) out[it.side].flags = fl & ~SO_TAIL;
 }
 
 // Traced sides the inspector finished that are longer than the shortest
@@ -655,12 +661,29 @@ struct WalkArgs {
     int64_t ptr_base_off;
     const uint64_t *op_btab;    // one-pass sides (OP): each side's block table
     int32_t runs_by_item;       // a side's runs at runs + its item's ptr_off (else runs + run_off[side])
-    const SideOut *out;
+    SideOut *out;
     const int64_t *run_off;
     uint32_t *runs;
     int64_t *run_len;
     const int32_t *side_trace;  // (early list) items whose side is not traced through the executor are skipped
+    // Tail walk (OP, tail_list set): wave k takes one-pass list entry
+    // tail_list[k] if tail_fin[k] already says its side finished, takes
+    // TAIL_RUNS(ie + je) run words of the tail buffer (runs, tail_cap words,
+    // tail_used taken), and on success records run_len, op_run_off and
+    // SO_TAIL.  A side it skips, cannot fit or cannot finish is walked later
+    // as before.  The other OP walks skip SO_TAIL sides.
+    const int32_t *tail_list;
+    const uint32_t *tail_fin;
+    unsigned long long *tail_used;
+    uint64_t tail_cap;
+    int64_t *op_run_off;
+    uint32_t *tail_sides;       // sides the tail walk finished (stats)
 };
+
+// Run words a tail walk may write for a side whose best cell is on
+// anti-diagonal dstar: a CIGAR with more runs (a gap every 32 moves or so)
+// is left to the walk after the executor, which has room for one run per move.
+__device__ __forceinline__ int64_t TAIL_RUNS(int64_t dstar) { return min(dstar + 1, dstar / 32 + 256); }
 
 __device__ __forceinline__ void rle_push(uint32_t *runs, int64_t &n, uint32_t &cur_op, uint32_t &cur_len, uint32_t op)
 {
@@ -711,15 +734,36 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
     const int lane = lane_id();
     const int64_t k = a.begin + (int64_t)blockIdx.x;
     if (k >= a.end) return;
-    const ExecItem it = a.items[k];
-    if (a.side_trace && a.side_trace[it.side] != 2) return;
-    const SideOut o = a.out[it.side];
+    const bool tail = OP && a.tail_list != nullptr;
+    ExecItem it = {};
+    SideOut o;
+    int64_t cap = INT64_MAX;        // run words this walk may write
+    uint64_t slot = 0;
+    if (tail) {
+        // (acquire: the executor wave's rows and result, written back past
+        // its XCD's L2 before the flag, are read past this one's)
+        const uint32_t fin = __hip_atomic_load(a.tail_fin + k, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+        if (uniform((int)fin) != 1) return;
+        it.side = a.tail_list[k];
+        o = a.out[it.side];
+        if (o.flags & (SO_EXEC_MISMATCH | SO_TAIL)) return;
+        it.dstar = o.ie + o.je;
+        cap = TAIL_RUNS(it.dstar);
+        if (lane == 0) slot = atomicAdd(a.tail_used, (unsigned long long)cap);
+        slot = uniform64(slot);
+        if (slot > a.tail_cap || (uint64_t)cap > a.tail_cap - slot) return;
+    } else {
+        it = a.items[k];
+        if (a.side_trace && a.side_trace[it.side] != 2) return;
+        o = a.out[it.side];
+        if (OP && (o.flags & SO_TAIL)) return;      // (walked by the tail walk)
+    }
     const uint8_t *base = OP ? nullptr : a.ptr_ws + (it.ptr_off - a.ptr_base_off);
     const RowHdr *hdr = reinterpret_cast<const RowHdr *>(base);
     const uint32_t *rows = OP ? nullptr : reinterpret_cast<const uint32_t *>(base + 8 * ((int64_t)it.dstar + 1));
     typedef __attribute__((address_space(1))) const uint64_t GlobalU64;
     GlobalU64 *btab = OP ? reinterpret_cast<GlobalU64 *>(a.op_btab[it.side]) : nullptr;
-    uint32_t *runs = a.runs + (a.runs_by_item ? it.ptr_off : a.run_off[it.side]);
+    uint32_t *runs = a.runs + (tail ? (int64_t)slot : a.runs_by_item ? it.ptr_off : a.run_off[it.side]);
     const uint32_t total_rows = OP ? OP_BLOCK_WORDS : (uint32_t)((it.ptr_bytes - 8 * ((int64_t)it.dstar + 1)) / 4);
 
     // states: 0 = S; 1 = arrived in I (continue if the cell's PTR_EXT_I
@@ -740,7 +784,7 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
             clen += cnt;
             return;
         }
-        if (clen && lane == 0) runs[n] = (clen << 4) | cop;
+        if (clen && lane == 0 && n < cap) runs[n] = (clen << 4) | cop;
         if (clen) ++n;
         cop = op;
         clen = cnt;
@@ -938,9 +982,21 @@ __global__ __launch_bounds__(64) void walk_wave_kernel(WalkArgs a)
         }
         __syncthreads();
     }
-    if (clen && lane == 0) runs[n] = (clen << 4) | cop;
+    if (clen && lane == 0 && n < cap) runs[n] = (clen << 4) | cop;
     if (clen) ++n;
-    if (lane == 0) a.run_len[it.side] = (!bad && i == 0 && j == 0 && st == 0) ? n : -1;
+    const bool ok = !bad && i == 0 && j == 0 && st == 0;
+    if (tail) {
+        // (a side that did not fit its run words or did not reach the
+        // origin is walked again after the executor, which reports it)
+        if (ok && n <= cap && lane == 0) {
+            a.run_len[it.side] = n;
+            a.op_run_off[it.side] = (int64_t)slot;
+            atomicOr(&a.out[it.side].flags, SO_TAIL);
+            atomicAdd(a.tail_sides, 1u);
+        }
+        return;
+    }
+    if (lane == 0) a.run_len[it.side] = ok ? n : -1;
 }
 
 // Eager sides: op bytes (end-first) -> run words (end-first).
@@ -1007,6 +1063,7 @@ struct AssembleArgs {
     const uint32_t *runs;
     const int64_t *op_run_off;  // SO_WALKED sides: their runs at op_runs + op_run_off[side]
     const uint32_t *op_runs;
+    const uint32_t *tail_runs;  // SO_TAIL sides: at tail_runs + op_run_off[side]
     fz_hit *hits;
     int64_t *cig_len;           // count pass output / write pass input (offsets after scan)
     uint32_t *cigar;
@@ -1044,7 +1101,9 @@ __global__ void assemble_kernel(AssembleArgs a)
         return;
     }
     auto runs_of = [&](int64_t sd) -> const uint32_t * {
-        return (a.out[sd].flags & SO_WALKED) ? a.op_runs + a.op_run_off[sd] : a.runs + a.run_off[sd];
+        const int32_t fl = a.out[sd].flags;
+        return (fl & SO_TAIL) ? a.tail_runs + a.op_run_off[sd]
+               : (fl & SO_WALKED) ? a.op_runs + a.op_run_off[sd] : a.runs + a.run_off[sd];
     };
     const uint32_t *lr = runs_of(2 * k);
     const uint32_t *rr = runs_of(2 * k + 1);

@@ -114,9 +114,12 @@ struct SideTask {
 // SO_EARLY: a side of the wide retry that the retry's wave also traced (its
 // rows in the early workspace, an item of the early list); it is only
 // walked with the other executor sides.
+// SO_TAIL: a one-pass side walked while the one-pass executor still ran
+// (the tail walk); its runs are in the tail buffer at op_run_off[side]
+// until a round's packing moves them to the one-pass runs buffer.
 enum : int32_t {
     SO_OVERFLOW = 1, SO_EAGER = 2, SO_SKIPPED = 4, SO_EXEC_MISMATCH = 8, SO_WIDE_FLAG = 16,
-    SO_DEFERRED = 32, SO_ONEPASS = 64, SO_WALKED = 128, SO_EARLY = 256
+    SO_DEFERRED = 32, SO_ONEPASS = 64, SO_WALKED = 128, SO_EARLY = 256, SO_TAIL = 512
 };
 
 struct SideOut {
@@ -310,6 +313,12 @@ __device__ __forceinline__ int wave_max(int v)
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint64_t uniform64(uint64_t x)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
 
 __device__ __forceinline__ int ctz64(uint64_t x) { return __builtin_ctzll(x); }
 __device__ __forceinline__ int hibit64(uint64_t x) { return 63 - __builtin_clzll(x); }

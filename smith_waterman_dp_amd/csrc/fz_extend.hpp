@@ -63,6 +63,9 @@ struct ExtendArgs {
     uint32_t *op_fail_count;
     int32_t *op_done_list;      // ... and the sides it finished
     uint32_t *op_done_count;
+    uint32_t *op_fin;           // (nullable) by list index: 1 once the side finished, its rows
+                                // and result visible on every XCD (agent-scope release)
+    uint32_t *op_last_started;  // (nullable, host memory) 1 once the list's last wave started
     // the wide retry beside the one-pass executor: a side whose seed is then
     // certain to be traced gets its rows in the same wave (SO_EARLY), in the
     // early workspace (early_bytes taken of early_cap), listed in early_items

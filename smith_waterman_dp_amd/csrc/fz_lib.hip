@@ -23,6 +23,8 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <thread>
+#include <chrono>
 #include <string>
 #include <vector>
 
@@ -72,6 +74,10 @@ struct Counters {
         uint32_t count, pad;                // the wide retry's sides traced beside the one-pass executor
         uint64_t bytes;                     // their rows' workspace
     } early;
+    struct {
+        uint64_t used;                      // tail walk: run words taken of the tail buffer (per round)
+        uint32_t sides, pad;                // one-pass sides it walked (per call)
+    } tail;
 };
 
 // One wave per workgroup for the wave-per-side kernels: sides differ in
@@ -141,6 +147,8 @@ struct fz_ctx {
     uint64_t ptr_cap = 0;               // 0 = default
     int64_t dbg_shrink_rows = 0;        // fz_debug_set(FZ_DEBUG_SHRINK_ROWS)
     int64_t dbg_op_pool = -1;           // fz_debug_set(FZ_DEBUG_ONEPASS_POOL): pool bytes (-1: sized by the library)
+    int64_t dbg_tail = 1;               // fz_debug_set(FZ_DEBUG_TAIL_WALK): 0 off, 1 beside the executor,
+                                        // 2 after it, more: after it within that many run words
     int64_t dbg_op_order = 1;           // fz_debug_set(FZ_DEBUG_ONEPASS_ORDER): predicted longest first (0: as deferred)
     std::vector<hipEvent_t> walk_ev;    // brackets of the walker launches (FZ_STATS)
     uint64_t last_words = 0;            // CIGAR words of the last successful call
@@ -158,6 +166,8 @@ struct fz_ctx {
     // at most), and the runs of sides walked before the pool was used again,
     // packed (by side: where they start)
     DevBuf op_fail2, op_done, op_items, op_runs_tmp, op_runs, op_run_off;
+    // tail walk: finished flags by list index, the runs of the sides it walked
+    DevBuf op_fin, tail_runs;
     // seed stage: target keys and positions (two of each for the sort), query
     // keys, join ranges and counts, hits (two for the sort), run flags and
     // ranks, and the seeds of the last fz_find_seeds
@@ -178,6 +188,9 @@ struct fz_ctx {
     hipStream_t xw = nullptr;           // the wide-window executor and walker, beside the batches
     hipEvent_t wide_ev = nullptr;
     hipEvent_t op_ev = nullptr;         // the one-pass sides' walks joined
+    hipEvent_t tail_ev[2] = {};         // a one-pass round's list ready; its tail walk done
+    hipEvent_t op_end_ev = nullptr;     // a one-pass round's executor done
+    uint32_t *op_started = nullptr;     // (coherent pinned host memory) the round's last executor wave started
     hipEvent_t ev[12] = {};
     hipEvent_t kev[4] = {};             // brackets the dominant kernel, then the one-pass executor
 };
@@ -758,6 +771,9 @@ int fz_create(fz_ctx **out, int device, uint64_t workspace_bytes)
     for (auto &e : ctx->join_ev) ok = ok && hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
     ok = ok && hipEventCreateWithFlags(&ctx->wide_ev, hipEventDisableTiming) == hipSuccess;
     ok = ok && hipEventCreateWithFlags(&ctx->op_ev, hipEventDisableTiming) == hipSuccess;
+    for (auto &e : ctx->tail_ev) ok = ok && hipEventCreateWithFlags(&e, hipEventDisableTiming) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&ctx->op_end_ev, hipEventDisableTiming) == hipSuccess;
+    ok = ok && hipHostMalloc((void **)&ctx->op_started, 256, hipHostMallocCoherent) == hipSuccess;
     // default priority, no implicit ordering with the null stream
     for (auto &x : ctx->xs) ok = ok && hipStreamCreateWithFlags(&x, hipStreamNonBlocking) == hipSuccess;
     ok = ok && hipStreamCreateWithFlags(&ctx->xw, hipStreamNonBlocking) == hipSuccess;
@@ -790,7 +806,7 @@ void fz_destroy(fz_ctx *ctx)
                       &ctx->sg_v, &ctx->sg_max, &ctx->rs_cnt, &ctx->ps_tmp, &ctx->defer_list, &ctx->op_fail,
                       &ctx->op_btab, &ctx->op_pool, &ctx->op_fail2, &ctx->op_done, &ctx->op_items,
                       &ctx->op_runs_tmp, &ctx->op_runs, &ctx->op_run_off, &ctx->op_key, &ctx->op_order,
-                      &ctx->early_items, &ctx->early_ws};
+                      &ctx->early_items, &ctx->early_ws, &ctx->op_fin, &ctx->tail_runs};
     for (auto &x : ctx->xs)
         if (x) (void)hipStreamSynchronize(x);
     if (ctx->xw) (void)hipStreamSynchronize(ctx->xw);
@@ -803,6 +819,10 @@ void fz_destroy(fz_ctx *ctx)
     if (ctx->xw) (void)hipStreamDestroy(ctx->xw);
     if (ctx->wide_ev) (void)hipEventDestroy(ctx->wide_ev);
     if (ctx->op_ev) (void)hipEventDestroy(ctx->op_ev);
+    for (auto &e : ctx->tail_ev)
+        if (e) (void)hipEventDestroy(e);
+    if (ctx->op_end_ev) (void)hipEventDestroy(ctx->op_end_ev);
+    if (ctx->op_started) (void)hipHostFree(ctx->op_started);
     if (ctx->fork_ev) (void)hipEventDestroy(ctx->fork_ev);
     for (auto &e : ctx->join_ev)
         if (e) (void)hipEventDestroy(e);
@@ -838,6 +858,10 @@ int fz_debug_set(fz_ctx *ctx, int what, int64_t value)
     }
     if (what == FZ_DEBUG_ONEPASS_ORDER && (value == 0 || value == 1)) {
         ctx->dbg_op_order = value;
+        return FZ_OK;
+    }
+    if (what == FZ_DEBUG_TAIL_WALK && value >= 0 && value <= ((int64_t)1 << 40)) {
+        ctx->dbg_tail = value;
         return FZ_OK;
     }
     return fail(ctx, FZ_EINVAL, "unknown debug setting or value out of range");
@@ -913,7 +937,8 @@ static int prepare_onepass_pool(fz_ctx *ctx, int64_t n, uint64_t diags, int64_t 
 // to `done`, sides the pool could not hold to `fail` (counts in
 // Counters::op_round, cleared by the caller).
 static int launch_onepass_round(fz_ctx *ctx, const ExtendArgs &ea, const int32_t *list, int64_t n,
-                                uint64_t pool_bytes, int32_t *fail, int32_t *done, void *counters, hipStream_t st)
+                                uint64_t pool_bytes, int32_t *fail, int32_t *done, uint32_t *fin,
+                                uint32_t *last_started, void *counters, hipStream_t st)
 {
     Counters *dc = static_cast<Counters *>(counters);
     ExtendArgs oa = ea;
@@ -928,6 +953,8 @@ static int launch_onepass_round(fz_ctx *ctx, const ExtendArgs &ea, const int32_t
     oa.op_fail_count = &dc->op_round.fail;
     oa.op_done_list = done;
     oa.op_done_count = &dc->op_round.done;
+    oa.op_fin = fin;
+    oa.op_last_started = last_started;
     return launch_onepass(ctx, oa, n, st);
 }
 
@@ -1098,6 +1125,7 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         if ((rc = wide_retry(0, n_ovl_first, ctx->xw, true))) return rc;
     }
     bool onepass_ran = false;
+    bool tail_ran = false;              // a tail walk beside the one-pass executor (tail_ev[1] its end)
     int64_t n_early = 0;                // the wide retry's sides traced beside the one-pass executor
     if (hc.defer_count > 0) {
         // ---- one-pass executor over the deferred sides, in rounds: when the
@@ -1106,6 +1134,30 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
         // (the sides that did not fit); the last round's sides are walked
         // beside the two-pass executor.  A round that finishes no side
         // gives the rest back to the inspector.
+        // Tail walk: the one-pass executor's last waves run for tens of
+        // milliseconds after its last dispatch, with most of the machine
+        // idle.  A walk launched beside it (on an executor stream no one
+        // uses yet) takes the sides that have finished by the time its wave
+        // runs, into a run buffer of its own (1/64 of the free memory, at
+        // most 1 GiB, taken once per context, before the pool).
+        const bool tail_on = ctx->dbg_tail != 0;
+        if (tail_on) {
+            if (!ctx->tail_runs.p) {
+                size_t fr = 0, tot = 0;
+                HIP_OK(hipMemGetInfo(&fr, &tot));
+                ENSURE(ctx->tail_runs, std::max<uint64_t>(std::min<uint64_t>((uint64_t)fr / 64, (uint64_t)1 << 30), 4096));
+            }
+            ENSURE(ctx->op_fin, nsides * sizeof(uint32_t));
+            ENSURE(ctx->op_run_off, nsides * sizeof(int64_t));
+            rc = zero(ctx, &dc->tail, sizeof dc->tail, st);
+            if (rc) return rc;
+        }
+        // (test settings: after the executor on the caller's stream, where
+        // every finished side is taken, within a given number of run words)
+        const uint64_t tail_cap = ctx->dbg_tail > 2 ? std::min<uint64_t>(ctx->tail_runs.cap / sizeof(uint32_t),
+                                                                          (uint64_t)ctx->dbg_tail)
+                                                    : ctx->tail_runs.cap / sizeof(uint32_t);
+        const hipStream_t ts = ctx->dbg_tail >= 2 ? st : ctx->xs[0];
         uint64_t pool_bytes = 0;
         rc = prepare_onepass_pool(ctx, (int64_t)hc.defer_count, hc.defer_diags, nsides, st, &pool_bytes);
         if (rc) return rc;
@@ -1142,10 +1194,59 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
             rc = zero(ctx, &dc->op_round, sizeof dc->op_round, st);
             if (rc) return rc;
             int32_t *fl = fb ? as<int32_t>(ctx->op_fail2) : as<int32_t>(ctx->op_fail);
+            if (tail_on) {
+                rc = zero(ctx, ctx->op_fin.p, (size_t)nL * sizeof(uint32_t), st);
+                if (rc) return rc;
+                HIP_OK(hipEventRecord(ctx->tail_ev[0], st));
+            }
             if (!onepass_ran) HIP_OK(hipEventRecord(ctx->kev[2], st));
-            rc = launch_onepass_round(ctx, ea, L, nL, pool_bytes, fl, as<int32_t>(ctx->op_done), dc, st);
+            const bool tail_beside = tail_on && ts != st;
+            uint32_t *started_dev = nullptr;
+            if (tail_beside) {
+                __atomic_store_n(ctx->op_started, 0u, __ATOMIC_RELEASE);
+                HIP_OK(hipHostGetDevicePointer((void **)&started_dev, ctx->op_started, 0));
+            }
+            rc = launch_onepass_round(ctx, ea, L, nL, pool_bytes, fl, as<int32_t>(ctx->op_done),
+                                      tail_on ? as<uint32_t>(ctx->op_fin) : nullptr, started_dev, dc, st);
             if (rc) return rc;
             onepass_ran = true;
+            if (tail_beside) {
+                // hold the tail walk back until the executor's last wave has
+                // started (or the executor has ended): launched earlier, its
+                // waves would take slots from executor waves not yet started
+                HIP_OK(hipEventRecord(ctx->op_end_ev, st));
+                while (__atomic_load_n(ctx->op_started, __ATOMIC_ACQUIRE) == 0) {
+                    const hipError_t q = hipEventQuery(ctx->op_end_ev);
+                    if (q != hipErrorNotReady) {
+                        HIP_OK(q);
+                        break;
+                    }
+                    std::this_thread::sleep_for(std::chrono::microseconds(200));
+                }
+            }
+            if (tail_on) {
+                // (after the executor in host order: the device dispatches it
+                // once the executor's grid is dispatched, or its waves find
+                // few sides finished)
+                HIP_OK(hipStreamWaitEvent(ts, ctx->tail_ev[0], 0));
+                WalkArgs wk = {};
+                wk.begin = 0;
+                wk.end = nL;
+                wk.op_btab = as<uint64_t>(ctx->op_btab);
+                wk.out = as<SideOut>(ctx->out);
+                wk.runs = as<uint32_t>(ctx->tail_runs);
+                wk.run_len = as<int64_t>(ctx->run_len);
+                wk.tail_list = L;
+                wk.tail_fin = as<uint32_t>(ctx->op_fin);
+                wk.tail_used = reinterpret_cast<unsigned long long *>(&dc->tail.used);
+                wk.tail_cap = tail_cap;
+                wk.op_run_off = as<int64_t>(ctx->op_run_off);
+                wk.tail_sides = &dc->tail.sides;
+                walk_wave_kernel<true><<<nL, 64, 0, ts>>>(wk);
+                HIP_OK(hipGetLastError());
+                HIP_OK(hipEventRecord(ctx->tail_ev[1], ts));
+                tail_ran = true;
+            }
             if ((rc = read_counters())) return rc;
             const uint32_t nd = hc.op_round.done, nf = hc.op_round.fail;
             S.n_onepass += nd;
@@ -1157,6 +1258,8 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
             }
             if (nf == 0) break;
             // the pool serves the next round: walk this round's sides now
+            // (those the tail walk took have their runs already)
+            if (tail_on) HIP_OK(hipStreamWaitEvent(st, ctx->tail_ev[1], 0));
             ENSURE(ctx->op_items, (int64_t)nd * sizeof(ExecItem));
             ExecItem *items = as<ExecItem>(ctx->op_items);
             op_items_kernel<<<blocks_for(nd, 256), 256, 0, st>>>(as<int32_t>(ctx->op_done), (int64_t)nd,
@@ -1191,11 +1294,14 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
                            (size_t)runs_base * sizeof(uint32_t), st);
             if (rc) return rc;
             ENSURE(ctx->op_run_off, nsides * sizeof(int64_t));
-            op_run_pack_kernel<<<blocks_for(nd, 256), 256, 0, st>>>(items, (int64_t)nd, as<uint32_t>(ctx->op_runs_tmp),
-                                                                    as<uint32_t>(ctx->op_runs), runs_base,
-                                                                    as<int64_t>(ctx->op_run_off));
+            op_run_pack_kernel<<<blocks_for(nd, 256), 256, 0, st>>>(
+                items, (int64_t)nd, as<uint32_t>(ctx->op_runs_tmp), as<uint32_t>(ctx->tail_runs),
+                as<SideOut>(ctx->out), as<uint32_t>(ctx->op_runs), runs_base, as<int64_t>(ctx->op_run_off));
             HIP_OK(hipGetLastError());
             runs_base += packed;
+            // (the tail buffer's runs are packed: the next round's tail walk
+            // starts it over)
+            if (tail_on && (rc = zero(ctx, &dc->tail.used, sizeof dc->tail.used, st))) return rc;
             L = fl;
             nL = nf;
         }
@@ -1395,6 +1501,7 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
             if (tm.on) HIP_OK(hipEventRecord(ctx->walk_ev[2 * n_walks++ + 1], xst));
             return FZ_OK;
         };
+        if (n_op > 0 && tail_ran) HIP_OK(hipStreamWaitEvent(xop, ctx->tail_ev[1], 0));
         if (n_op > 0 && (rc = walk(0, n_op, xop, nullptr, 0, true))) return rc;
         for (int64_t b = 0; b < nb; ++b) {
             const int64_t lo = first[(size_t)b], hi = first[(size_t)b + 1];
@@ -1448,10 +1555,12 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     tm.mark();
 
     // ---- gather CIGARs
+    if (tail_ran) HIP_OK(hipStreamWaitEvent(st, ctx->tail_ev[1], 0));
     ENSURE(ctx->cig, n * sizeof(int64_t));
     AssembleArgs aa = {};
     aa.op_run_off = as<int64_t>(ctx->op_run_off);
     aa.op_runs = as<uint32_t>(ctx->op_runs);
+    aa.tail_runs = as<uint32_t>(ctx->tail_runs);
     aa.seeds = seeds;
     aa.out = as<SideOut>(ctx->out);
     aa.n = n;
@@ -1468,6 +1577,7 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
     if (rc) return rc;
     if ((rc = read_counters())) return rc;
     const int64_t total_words = hc.totals[2];
+    S.n_tail_walked = tail_ran ? hc.tail.sides : 0;
     ENSURE(ctx->cigar, std::max<int64_t>(total_words, 1) * sizeof(uint32_t));
     aa.cigar = as<uint32_t>(ctx->cigar);
     assemble_kernel<true><<<blocks_for(n, 256), 256, 0, st>>>(aa);

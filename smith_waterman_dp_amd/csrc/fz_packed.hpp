@@ -149,13 +149,6 @@ struct OpState {
 };
 __shared__ OpState op_state;
 
-__device__ __forceinline__ uint64_t uniform64(uint64_t x)
-{
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32));
-    return ((uint64_t)hi << 32) | lo;
-}
-
 // `bytes` of pool memory at or after address cur (16-aligned), from the
 // wave's arena; a new arena when it does not fit, a direct pool carve for
 // requests above half an arena.  nullptr when the pool is exhausted.
@@ -903,6 +896,13 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <=
     uint32_t *xfer = xfer_all[wv];
     const int idx = (int)blockIdx.x * WAVES + wv;
     if (idx >= a.nlist) return;
+    if constexpr (ONEPASS) {
+        // (workgroups start in index order: the host launches the tail walk
+        // once the grid's last wave runs, so that the walk's waves never
+        // hold slots that executor waves still wait for)
+        if (a.op_last_started && idx == a.nlist - 1 && fresh_lane_id() == 0)
+            __hip_atomic_store(a.op_last_started, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
     constexpr bool TWO_PASS_EXEC = EXEC && !ONEPASS;
     const int64_t item = TWO_PASS_EXEC ? a.exec_begin + idx : (int64_t)idx;
     const int sid = TWO_PASS_EXEC ? a.exec[item].side : (a.list ? a.list[item] : (int)item);
@@ -954,6 +954,13 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <=
                 const uint32_t k = atomicAdd(a.op_done_count, 1u);
                 a.op_done_list[k] = sid;
             }
+        }
+        if (a.op_fin && !x.overflow && !pool_out) {
+            // publish the finished side to the tail walk: every lane's row,
+            // header and block-table stores and lane 0's result are written
+            // back past this XCD's L2 before the flag
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            if (fresh_lane_id() == 0) __hip_atomic_store(a.op_fin + idx, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         return;
     }

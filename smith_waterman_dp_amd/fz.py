@@ -17,7 +17,7 @@ FZ_OK, FZ_EINVAL, FZ_ENOMEM, FZ_EDEVICE = 0, -1, -2, -3
 FZ_HIT_TRACED, FZ_HIT_EAGER_LEFT, FZ_HIT_EAGER_RIGHT = 1, 2, 4
 FZ_HIT_BELOW_MIN, FZ_HIT_EBAND, FZ_HIT_ESEED, FZ_HIT_ERANGE = 8, 16, 32, 64
 FZ_HIT_COVERED, FZ_HIT_EEXEC, FZ_HIT_WIDE = 128, 256, 512
-FZ_DEBUG_SHRINK_ROWS, FZ_DEBUG_ONEPASS_POOL, FZ_DEBUG_ONEPASS_ORDER = 1, 2, 3
+FZ_DEBUG_SHRINK_ROWS, FZ_DEBUG_ONEPASS_POOL, FZ_DEBUG_ONEPASS_ORDER, FZ_DEBUG_TAIL_WALK = 1, 2, 3, 4
 FZ_YDROP_INF = 2147483647
 FZ_NOALLOC_MAX_SEEDS, FZ_NOALLOC_MAX_BASES = 65536, 4194304
 
@@ -60,7 +60,7 @@ class fz_stats(ctypes.Structure):
                 ("n_executor", ctypes.c_uint64), ("n_overflow", ctypes.c_uint64),
                 ("bin_hist", ctypes.c_uint64 * 8), ("n_batches", ctypes.c_uint64), ("max_band", ctypes.c_uint64),
                 ("n_packed", ctypes.c_uint64), ("n_onepass", ctypes.c_uint64), ("onepass_cells", ctypes.c_uint64),
-                ("onepass_bytes", ctypes.c_uint64),
+                ("onepass_bytes", ctypes.c_uint64), ("n_tail_walked", ctypes.c_uint64),
                 ("ms_pack", ctypes.c_float), ("ms_inspect", ctypes.c_float), ("ms_bin", ctypes.c_float),
                 ("ms_exec", ctypes.c_float), ("ms_walk", ctypes.c_float), ("ms_gather", ctypes.c_float),
                 ("ms_main", ctypes.c_float), ("ms_onepass", ctypes.c_float)]

@@ -35,8 +35,8 @@ def test_struct_sizes_match_header():
     assert ctypes.sizeof(fz.fz_scoring) == 20
     assert ctypes.sizeof(fz.fz_matrix) == 17 * 4           # sub[4][4] and n_score
     assert ctypes.sizeof(fz.fz_seed_stats) == 11 * 4       # eleven float phase times
-    # fz_stats: 21 uint64 counters (bin_hist holds 8), eight float times
-    assert ctypes.sizeof(fz.fz_stats) == 21 * 8 + 8 * 4
+    # fz_stats: 22 uint64 counters (bin_hist holds 8), eight float times
+    assert ctypes.sizeof(fz.fz_stats) == 22 * 8 + 8 * 4
 
 
 def test_struct_sizes_match_c_compiler(tmp_path):

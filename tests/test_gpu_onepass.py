@@ -166,6 +166,54 @@ def test_onepass_launch_order(ctx, heavy):
     same(a, b, "launch order")
 
 
+def tail_mode(ctx, mode):
+    fz.fz_debug_set(ctx.h, fz.FZ_DEBUG_TAIL_WALK, mode)
+
+
+@pytest.mark.parametrize("mode", [0, 2, 3000])
+def test_onepass_tail_walk(ctx, heavy, mode):
+    """The tail walk (one-pass sides walked while the one-pass executor's
+    last waves still run) changes no result: off, after the executor (every
+    side whose runs fit is walked there), and after it within 3,000 run words
+    (a few sides fit, the rest fall back to the walk after the executor)."""
+    ref = run(ctx, heavy, False, label="tail default")
+    assert ref[2]["n_tail_walked"] <= ref[2]["n_onepass"]
+    tail_mode(ctx, mode)
+    try:
+        a = run(ctx, heavy, False, label="tail mode %d" % mode)
+    finally:
+        tail_mode(ctx, 1)
+    log("tail mode %d: %d of %d one-pass sides walked in the tail" % (mode, a[2]["n_tail_walked"], a[2]["n_onepass"]))
+    if mode == 0:
+        assert a[2]["n_tail_walked"] == 0
+    elif mode == 2:
+        assert a[2]["n_tail_walked"] >= 0.9 * a[2]["n_onepass"]
+    else:
+        assert 0 < a[2]["n_tail_walked"] < a[2]["n_onepass"]
+    same(a, ref, "tail mode %d" % mode)
+    if mode == 2:
+        against_oracle(heavy, a, label="tail after the executor")
+
+
+def test_onepass_tail_walk_pool_rounds(ctx, heavy):
+    """Pool rounds with the tail walk taking every finished side: each
+    round's tail-walked runs are packed with the round's other walked sides
+    before the next round reuses the tail buffer."""
+    ref = run(ctx, heavy, True, label="tail rounds ref")
+    full = run(ctx, heavy, False, label="tail rounds default")
+    pool = max(full[2]["onepass_bytes"] // 2, 1 << 20)
+    fz.fz_debug_set(ctx.h, fz.FZ_DEBUG_ONEPASS_POOL, pool)
+    tail_mode(ctx, 2)
+    try:
+        a = run(ctx, heavy, False, label="tail rounds, pool %d" % pool)
+    finally:
+        tail_mode(ctx, 1)
+        fz.fz_debug_set(ctx.h, fz.FZ_DEBUG_ONEPASS_POOL, -1)
+    assert a[2]["onepass_bytes"] > pool        # (more than one round)
+    assert a[2]["n_tail_walked"] > a[2]["n_onepass"] // 2
+    same(a, ref, "tail rounds")
+
+
 def test_onepass_under_workspace_cap(ctx, heavy):
     """A 4 MiB pointer-memory cap bounds the pool too (many rounds), the
     same results."""
