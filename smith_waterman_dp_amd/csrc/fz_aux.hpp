@@ -680,6 +680,23 @@ struct WalkArgs {
     uint32_t *tail_sides;       // sides the tail walk finished (stats)
 };
 
+// Before the tail walk: sets the flag that one-pass waves ending from now on
+// read (they then write back their own L2), waits until it is acknowledged,
+// then writes back the L2 of the XCD it runs on; launched with
+// TAIL_FLUSH_GROUPS single-wave groups, which the dispatcher spreads over
+// every XCD.  Sides that ended before the flag was set are then readable by
+// the walk, which starts after this kernel has ended.
+constexpr int TAIL_FLUSH_GROUPS = 64;
+__global__ void tail_flush_kernel(uint32_t *flushed)
+{
+    if (threadIdx.x == 0) __hip_atomic_store(flushed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // Run words a tail walk may write for a side whose best cell is on
 // anti-diagonal dstar: a CIGAR with more runs (a gap every 32 moves or so)
 // is left to the walk after the executor, which has room for one run per move.

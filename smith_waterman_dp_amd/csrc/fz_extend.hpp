@@ -66,6 +66,7 @@ struct ExtendArgs {
     uint32_t *op_fin;           // (nullable) by list index: 1 once the side finished, its rows
                                 // and result visible on every XCD (agent-scope release)
     uint32_t *op_last_started;  // (nullable, host memory) 1 once the list's last wave started
+    const uint32_t *op_flushed; // 1 once the tail walk's flush began (tail_flush_kernel)
     // the wide retry beside the one-pass executor: a side whose seed is then
     // certain to be traced gets its rows in the same wave (SO_EARLY), in the
     // early workspace (early_bytes taken of early_cap), listed in early_items

@@ -76,7 +76,8 @@ struct Counters {
     } early;
     struct {
         uint64_t used;                      // tail walk: run words taken of the tail buffer (per round)
-        uint32_t sides, pad;                // one-pass sides it walked (per call)
+        uint32_t sides;                     // one-pass sides it walked (per call)
+        uint32_t flushed;                   // the round's tail flush began (tail_flush_kernel)
     } tail;
 };
 
@@ -955,6 +956,7 @@ static int launch_onepass_round(fz_ctx *ctx, const ExtendArgs &ea, const int32_t
     oa.op_done_count = &dc->op_round.done;
     oa.op_fin = fin;
     oa.op_last_started = last_started;
+    oa.op_flushed = &dc->tail.flushed;
     return launch_onepass(ctx, oa, n, st);
 }
 
@@ -1197,6 +1199,8 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
             if (tail_on) {
                 rc = zero(ctx, ctx->op_fin.p, (size_t)nL * sizeof(uint32_t), st);
                 if (rc) return rc;
+                rc = zero(ctx, &dc->tail.flushed, sizeof dc->tail.flushed, st);
+                if (rc) return rc;
                 HIP_OK(hipEventRecord(ctx->tail_ev[0], st));
             }
             if (!onepass_ran) HIP_OK(hipEventRecord(ctx->kev[2], st));
@@ -1229,6 +1233,8 @@ static int extend_impl(fz_ctx *ctx, const uint8_t *target, uint64_t tlen, const 
                 // once the executor's grid is dispatched, or its waves find
                 // few sides finished)
                 HIP_OK(hipStreamWaitEvent(ts, ctx->tail_ev[0], 0));
+                tail_flush_kernel<<<TAIL_FLUSH_GROUPS, 64, 0, ts>>>(&dc->tail.flushed);
+                HIP_OK(hipGetLastError());
                 WalkArgs wk = {};
                 wk.begin = 0;
                 wk.end = nL;

@@ -956,10 +956,26 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(C <=
             }
         }
         if (a.op_fin && !x.overflow && !pool_out) {
-            // publish the finished side to the tail walk: every lane's row,
-            // header and block-table stores and lane 0's result are written
-            // back past this XCD's L2 before the flag
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            // Publish the finished side to the tail walk: its rows, headers,
+            // block table and result must be written back past this XCD's L2
+            // before the walk reads them.  Every store of the wave is first
+            // acknowledged by the L2; a side that then finds the flush not
+            // begun leaves the write-back to tail_flush_kernel, which sets
+            // its flag before writing back every XCD's L2 and runs before the
+            // walk; a side that finds it begun writes back its own L2.
+            // (the signal fences keep the compiler from moving memory
+            // operations across the wait, the load and the flag store)
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_waitcnt(0);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            const uint32_t flushed = __hip_atomic_load(a.op_flushed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (uniform((int)flushed) != 0) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                // (the write-back done before the flag: the compiler's own
+                // wait after it is dropped when no store is outstanding)
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
             if (fresh_lane_id() == 0) __hip_atomic_store(a.op_fin + idx, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         return;
