@@ -78,9 +78,9 @@ def extension_kernels(cells, onepass_cells, inspector_ms, onepass_ms, peak):
 # same run (FETCH_SIZE reads 0.5 GiB for it, WRITE_SIZE 1.0 GiB).  Valid only
 # for the kernel sources it was taken on (hash of fz_extend.hpp,
 # fz_device.hpp and fz_packed.hpp); reported as null otherwise.
-TRAFFIC_SRC_HASH = "5cc2a528df2a95b4"
-TRAFFIC = {"extend_kernel (inspector)": (4.680e6 * 1024 / 0.5, 7.593e6 * 1024 / 1.0),
-           "extend_kernel (one-pass executor)": (3.958e6 * 1024 / 0.5, 1.752e8 * 1024 / 1.0)}
+TRAFFIC_SRC_HASH = "1269baeb08c0dd35"
+TRAFFIC = {"extend_kernel (inspector)": (4.681e6 * 1024 / 0.5, 7.593e6 * 1024 / 1.0),
+           "extend_kernel (one-pass executor)": (3.756e6 * 1024 / 0.5, 1.676e8 * 1024 / 1.0)}
 
 
 # The same for one join_count_kernel launch of the seed stage on the 20 Mbp
